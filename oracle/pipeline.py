@@ -1,0 +1,59 @@
+"""Oracle end-to-end helpers: build the quantizer from seeds, compress into a paged cache.
+
+Composition only; the arithmetic lives in codebook, rotation, quantize and
+attention. Keys get MSE codes plus QJL signs, values MSE codes only
+("FlashQuant" page, "使用方式": MSE mode for values, inner-product mode for
+keys). K and V of one layer share the rotation (a reading: the pages do not
+say).
+"""
+import numpy as np
+
+from . import codebook, paged, quantize, rotation
+
+HAAR = 0
+WHT = 1
+
+
+def build(bits, head_dim, rot=HAAR, rot_seed=1, qjl_seed=2, qjl_dim=None):
+    """All stored parameters of one layer's quantizer.
+
+    Returns levels32, boundaries32, pi (fp32 operator as float64), signs (WHT
+    only, else None), s (fp32 QJL matrix as float64, m x d).
+    """
+    lev, bnd = codebook.scaled_codebook(bits, head_dim)
+    m = head_dim if qjl_dim is None else qjl_dim
+    if rot == HAAR:
+        pi = rotation.stored(rotation.haar_rotation(rot_seed, head_dim))
+        sg = None
+    else:
+        sg = rotation.wht_signs(rot_seed, head_dim)
+        pi = rotation.stored(rotation.wht_matrix(sg))
+    s = rotation.stored(rotation.qjl_matrix(qjl_seed, m, head_dim))
+    return {"bits": bits, "d": head_dim, "rot": rot, "levels": lev, "boundaries": bnd,
+            "pi": pi, "signs": sg, "s": s, "m": m}
+
+
+def encode_keys(x, q):
+    return quantize.encode(x, q["pi"], q["levels"], q["boundaries"], q["bits"], s=q["s"])
+
+
+def encode_values(x, q):
+    return quantize.encode(x, q["pi"], q["levels"], q["boundaries"], q["bits"])
+
+
+def compress(cache, k, v, slot_mapping, q, with_qjl=True):
+    """Encode k, v ([T, Hkv, d]) and store them at slot_mapping ([T]).
+
+    Returns the per-head encodings (list over heads of (k_enc, v_enc)) so that
+    tests can look at y, p and the codes directly.
+    """
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    T, Hkv, d = k.shape
+    encs = []
+    for h in range(Hkv):
+        ke = encode_keys(k[:, h], q) if with_qjl else encode_values(k[:, h], q)
+        ve = encode_values(v[:, h], q)
+        paged.write(cache, slot_mapping, h, ke, ve)
+        encs.append((ke, ve))
+    return encs
