@@ -1,0 +1,208 @@
+/*
+ * fq.h -- C ABI of libfq: TurboQuant KV-cache compression and decode attention
+ * over the compressed, paged cache, for AMD Instinct MI355X (gfx950).
+ *
+ * The method: "FlashQuant ... KV缓存压缩方案" (zingnex.cn), section
+ * "TurboQuant" (normalise, rotate, Lloyd-Max quantize, pack + fp32 norm),
+ * section "QJL" (residual-sign correction of key inner products) and section
+ * "架构设计" (codebook / quantizer / packing / rotation core; compress and
+ * split-K paged decode kernels); "TurboQuant : compresser le KV-cache"
+ * (patricehuetz.fr), "Couche 1" (randomized Walsh-Hadamard), "Couche 3"
+ * (packing), "Couche 4" (fp32 norms).
+ *
+ * Conventions for every entry point:
+ *  - Returns an fq_status; never throws, never aborts. Arguments are checked on
+ *    the host before any device work; a failed check launches nothing.
+ *  - Memory is owned by the caller. "device" pointers are HIP device memory on
+ *    the current device; "host" pointers are ordinary host memory. The library
+ *    allocates nothing and keeps no state between calls.
+ *  - Device work is enqueued on `stream` (a hipStream_t; NULL = the default
+ *    stream) and is asynchronous; results are ready when the stream is.
+ *  - Reductions run in a fixed order (no float atomics): the same inputs give
+ *    bit-identical outputs run to run.
+ *  - Supported shapes: head_dim = 128, bits in {2, 4}, 16-token blocks,
+ *    qjl_dim in {0, 128}, 1 <= num_q_heads / num_kv_heads <= 16. Others return
+ *    FQ_ERR_UNSUPPORTED.
+ *  - Out-of-range slot ids or block-table entries are not detected on the
+ *    device: the caller guarantees 0 <= slot < num_blocks * 16 (or slot < 0 to
+ *    skip) and 0 <= block_tables[b][i] < num_blocks for i < ceil(seq_lens[b]/16).
+ */
+#ifndef FQ_H
+#define FQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum fq_status {
+  FQ_OK = 0,
+  FQ_ERR_INVALID_ARG = 1,  /* null / misaligned pointer, negative size, bad enum */
+  FQ_ERR_UNSUPPORTED = 2,  /* valid but outside the supported shapes above */
+  FQ_ERR_WORKSPACE = 3,    /* workspace missing or smaller than fq_decode_workspace_size */
+  FQ_ERR_HIP = 4           /* the HIP runtime reported an error at launch */
+} fq_status;
+
+typedef enum fq_rotation { FQ_ROT_HAAR = 0, FQ_ROT_WHT = 1 } fq_rotation;
+typedef enum fq_dtype { FQ_F32 = 0, FQ_BF16 = 1 } fq_dtype;
+
+/* Human-readable name of a status code (static string). */
+const char* fq_status_string(int status);
+
+/* Library version as an integer (major * 10000 + minor * 100 + patch). */
+int fq_version(void);
+
+/*
+ * fq_build_codebook -- host, synchronous. Builds the parameters of one layer's
+ * quantizer ("FlashQuant" page, "TurboQuant" steps 2-3 and "QJL").
+ *
+ *  bits       2 or 4: 2^bits Lloyd-Max levels for N(0,1), iterated to the
+ *             float64 fixed point (largest level change < 1e-15) from the cell
+ *             quantiles, made exactly antisymmetric, then scaled by 1/sqrt(d).
+ *  head_dim   d = 128.
+ *  rotation   FQ_ROT_HAAR: G with i.i.d. N(0,1) entries from stream rot_seed,
+ *             Householder QR G = QR, Pi = Q diag(sign(diag R)) (Haar).
+ *             FQ_ROT_WHT: signs s_j = +-1 from stream rot_seed,
+ *             Pi = H diag(s) / sqrt(d), H the Sylvester Hadamard matrix.
+ *  qjl_dim    m, rows of the QJL matrix S (0 = none, else 128); S has i.i.d.
+ *             N(0,1) entries from stream qjl_seed.
+ *  Streams: SplitMix64 (output i = mix64(seed + (i+1) * 0x9E3779B97F4A7C15)),
+ *  uniform = ((out >> 11) + 0.5) * 2^-53, Box-Muller pairs (cos, sin);
+ *  matrix entry (i, j) is stream element i*d + j; sign j = top bit of output j.
+ *
+ * Outputs (host, caller-allocated, fp32, each rounded once from float64):
+ *  levels          [2^bits]          ascending, already scaled by 1/sqrt(d)
+ *  boundaries      [2^bits - 1]      midpoints of adjacent levels, scaled
+ *  rotation_matrix [d * d] row-major, y = Pi u  (both rotation kinds; may be NULL)
+ *  rotation_t      [d * d] row-major Pi^T, the same numbers transposed (may be NULL)
+ *  wht_signs       [d]               +-1 (FQ_ROT_WHT; may be NULL)
+ *  qjl_matrix      [qjl_dim * d]     row-major S (may be NULL)
+ * Errors: FQ_ERR_INVALID_ARG for null levels/boundaries or a bad enum;
+ * FQ_ERR_UNSUPPORTED for other bits / head_dim / qjl_dim.
+ */
+fq_status fq_build_codebook(int bits, int head_dim, int rotation, uint64_t rot_seed,
+                            uint64_t qjl_seed, int qjl_dim, float* levels, float* boundaries,
+                            float* rotation_matrix, float* rotation_t, float* wht_signs,
+                            float* qjl_matrix);
+
+/* One layer's quantizer parameters, all device pointers (fp32, as built above). */
+typedef struct fq_quantizer {
+  int32_t bits;                 /* 2 or 4 */
+  int32_t head_dim;             /* 128 */
+  int32_t rotation;             /* fq_rotation */
+  int32_t qjl_dim;              /* 0 or 128 */
+  const float* levels;          /* [2^bits] */
+  const float* boundaries;      /* [2^bits - 1] */
+  const float* rotation_matrix; /* [d][d] row-major Pi; required for both kinds */
+  const float* rotation_t;      /* [d][d] row-major Pi^T; required for both kinds */
+  const float* wht_signs;       /* [d]; required for FQ_ROT_WHT */
+  const float* qjl_matrix;      /* [qjl_dim][d] row-major; required when qjl_dim > 0 */
+} fq_quantizer;
+
+/*
+ * The paged compressed cache of one layer (device pointers, 16-byte aligned).
+ * Token slot = block * 16 + offset. Per field:
+ *   k_codes [num_blocks][Hkv][16][d*bits/8] u8   index of coordinate 2k in the low
+ *                                                nibble of byte k (4-bit); coordinate
+ *                                                4k+i in bits 2i..2i+1 (2-bit)
+ *   k_norm  [num_blocks][Hkv][16]           f32  ||k||
+ *   k_qjl   [num_blocks][Hkv][16][m/8]      u8   bit i of byte j = [p_{8j+i} >= 0]
+ *   k_gamma [num_blocks][Hkv][16]           f32  ||k - k_mse||
+ *   v_codes, v_norm                              as k_codes, k_norm
+ * k_qjl / k_gamma are used only when qjl_dim > 0 (keys in inner-product mode).
+ */
+typedef struct fq_cache {
+  int32_t num_blocks;
+  int32_t block_size;   /* 16 */
+  int32_t num_kv_heads;
+  int32_t head_dim;     /* 128 */
+  int32_t bits;         /* must equal the quantizer's */
+  int32_t qjl_dim;      /* 0 (MSE-only keys) or the quantizer's qjl_dim */
+  uint8_t* k_codes;
+  float* k_norm;
+  uint8_t* k_qjl;
+  float* k_gamma;
+  uint8_t* v_codes;
+  float* v_norm;
+} fq_cache;
+
+/*
+ * fq_compress -- encode K and V vectors into the paged cache ("FlashQuant"
+ * page, "TurboQuant" steps 1-4 and "QJL"; "架构设计": fused
+ * normalise + rotate + quantize + pack).
+ *
+ * For each token t < num_tokens and KV head h with slot_mapping[t] >= 0:
+ *   n = ||x||, u = x / n (0 when n = 0), y = Pi u,
+ *   idx_j = #{i : boundary_i < y_j} (decided in fp32), codes packed as above,
+ *   norm = n (fp32); for keys when qjl_dim > 0 also
+ *   r = y - level[idx], gamma = n ||r||, p = S r, bit_i = [p_i >= 0].
+ * Values use the MSE encoding only.
+ *
+ *  k, v          device, element (t, h, j) at t*token_stride + h*head_stride + j,
+ *                dtype FQ_F32 or FQ_BF16; either may be NULL to skip that side.
+ *                Every vector must start on a 16-byte boundary (base pointer and
+ *                both strides, in bytes, multiples of 16).
+ *  num_tokens    >= 0 (0 is a no-op).
+ *  slot_mapping  device int64 [num_tokens]; negative = skip the token.
+ *  debug_y       optional device fp32 [2][num_tokens][Hkv][d]: y of K (index 0)
+ *                and V (index 1) as the kernel computed them; rows of skipped
+ *                tokens and of a NULL side are not written.
+ *  debug_p       optional device fp32 [num_tokens][Hkv][qjl_dim]: p of the keys.
+ * Errors: FQ_ERR_INVALID_ARG, FQ_ERR_UNSUPPORTED, FQ_ERR_HIP.
+ */
+fq_status fq_compress(void* stream, const fq_quantizer* quant, const fq_cache* cache,
+                      const void* k, const void* v, int dtype, int64_t num_tokens,
+                      int64_t token_stride, int64_t head_stride, const int64_t* slot_mapping,
+                      float* debug_y, float* debug_p);
+
+/*
+ * Split count the decode chooses when called with num_splits = 0: enough
+ * (batch, KV head, split) work-groups to fill the GPU, each covering at least
+ * 256 tokens, at most 64 splits. Host only.
+ */
+int fq_decode_auto_splits(int batch, int num_kv_heads, int max_seq_len);
+
+/*
+ * Bytes of device workspace fq_decode_attention needs for these sizes
+ * (num_splits = 0 means the automatic choice for max_seq_len). Host only.
+ */
+fq_status fq_decode_workspace_size(int batch, int num_q_heads, int num_kv_heads, int head_dim,
+                                   int qjl_dim, int max_seq_len, int num_splits, size_t* bytes);
+
+/*
+ * fq_decode_attention -- one decode step of attention read straight from the
+ * compressed, paged cache ("FlashQuant" page, "架构设计": paged split-K decode;
+ * "QJL": corrected inner product).
+ *
+ * For every sequence b and query head h (KV head h / (num_q_heads / Hkv)):
+ *   q~ = Pi q, q_s = S q~ (once per head),
+ *   s_t = scale * ( n_t <q~, level[idx_t]> + gamma_t sqrt(pi/2)/m <q_s, 2 sigma_t - 1> )
+ *         for t < seq_lens[b] (the QJL term only when qjl_dim > 0),
+ *   o_rot = sum_t softmax(s)_t * nv_t * level[idxv_t]  (rotated frame),
+ *   out = Pi^T o_rot.
+ * The context is cut into num_splits chunks of whole 16-token blocks; each
+ * chunk keeps a running max / sum / weighted sum, merged by log-sum-exp.
+ *
+ *  q             device [batch][num_q_heads][d], FQ_F32 or FQ_BF16.
+ *  block_tables  device int32 [batch][max_blocks_per_seq].
+ *  seq_lens      device int32 [batch]; each in [0, max_seq_len]; 0 gives out = 0.
+ *  max_seq_len   host bound on seq_lens, <= max_blocks_per_seq * 16.
+ *  num_splits    0 = automatic, else 1..64.
+ *  scale         softmax scale (1/sqrt(d) in the method).
+ *  workspace     device, >= fq_decode_workspace_size bytes, 256-byte aligned.
+ *  out           device fp32 [batch][num_q_heads][d].
+ * Errors: FQ_ERR_INVALID_ARG, FQ_ERR_UNSUPPORTED, FQ_ERR_WORKSPACE, FQ_ERR_HIP.
+ */
+fq_status fq_decode_attention(void* stream, const fq_quantizer* quant, const fq_cache* cache,
+                              const void* q, int q_dtype, int batch, int num_q_heads,
+                              const int32_t* block_tables, int max_blocks_per_seq,
+                              const int32_t* seq_lens, int max_seq_len, int num_splits,
+                              float scale, void* workspace, size_t workspace_bytes, float* out);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FQ_H */

@@ -1,0 +1,175 @@
+// C-ABI entry points: host-side argument checks, then the HIP launchers.
+#include <cstdint>
+
+#include "fq.h"
+#include "fq_internal.h"
+
+namespace {
+
+inline bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+fq_status check_quantizer(const fq_quantizer* q) {
+  if (!q) return FQ_ERR_INVALID_ARG;
+  if (q->rotation != FQ_ROT_HAAR && q->rotation != FQ_ROT_WHT) return FQ_ERR_INVALID_ARG;
+  if (q->bits != 2 && q->bits != 4) return FQ_ERR_UNSUPPORTED;
+  if (q->head_dim != FQ_HEAD_DIM) return FQ_ERR_UNSUPPORTED;
+  if (q->qjl_dim != 0 && q->qjl_dim != FQ_HEAD_DIM) return FQ_ERR_UNSUPPORTED;
+  if (!q->levels || !q->boundaries || !q->rotation_matrix || !q->rotation_t)
+    return FQ_ERR_INVALID_ARG;
+  if (q->rotation == FQ_ROT_WHT && !q->wht_signs) return FQ_ERR_INVALID_ARG;
+  if (q->qjl_dim > 0 && !q->qjl_matrix) return FQ_ERR_INVALID_ARG;
+  if (!aligned(q->levels, 4) || !aligned(q->boundaries, 4) || !aligned(q->rotation_matrix, 16) ||
+      !aligned(q->rotation_t, 16))
+    return FQ_ERR_INVALID_ARG;
+  if (q->qjl_dim > 0 && !aligned(q->qjl_matrix, 16)) return FQ_ERR_INVALID_ARG;
+  return FQ_OK;
+}
+
+fq_status check_cache(const fq_cache* c, const fq_quantizer* q) {
+  if (!c) return FQ_ERR_INVALID_ARG;
+  if (c->num_blocks < 0 || c->num_kv_heads <= 0) return FQ_ERR_INVALID_ARG;
+  if (c->block_size != FQ_BLOCK || c->head_dim != FQ_HEAD_DIM) return FQ_ERR_UNSUPPORTED;
+  if (c->bits != q->bits) return FQ_ERR_INVALID_ARG;
+  if (c->qjl_dim != 0 && c->qjl_dim != q->qjl_dim) return FQ_ERR_INVALID_ARG;
+  if (!c->k_codes || !c->k_norm || !c->v_codes || !c->v_norm) return FQ_ERR_INVALID_ARG;
+  if (!aligned(c->k_codes, 16) || !aligned(c->v_codes, 16) || !aligned(c->k_norm, 16) ||
+      !aligned(c->v_norm, 16))
+    return FQ_ERR_INVALID_ARG;
+  if (c->qjl_dim > 0) {
+    if (!c->k_qjl || !c->k_gamma) return FQ_ERR_INVALID_ARG;
+    if (!aligned(c->k_qjl, 16) || !aligned(c->k_gamma, 16)) return FQ_ERR_INVALID_ARG;
+  }
+  return FQ_OK;
+}
+
+}  // namespace
+
+namespace fq {
+
+DecodeWorkspace decode_workspace(int batch, int num_q_heads, int head_dim, int qjl_dim,
+                                 int num_splits) {
+  auto up = [](size_t x) { return (x + 255) & ~static_cast<size_t>(255); };
+  const size_t bh = static_cast<size_t>(batch) * num_q_heads;
+  DecodeWorkspace w{};
+  size_t off = 0;
+  w.qrot = off;
+  off += up(bh * head_dim * sizeof(float));
+  w.qs = off;
+  off += up(bh * (qjl_dim > 0 ? qjl_dim : 1) * sizeof(float));
+  w.part_o = off;
+  off += up(bh * num_splits * head_dim * sizeof(float));
+  w.part_ml = off;
+  off += up(bh * num_splits * 2 * sizeof(float));
+  w.total = off;
+  return w;
+}
+
+int auto_splits(int batch, int num_kv_heads, int max_seq_len) {
+  const int target_groups = 512;  // 2 work-groups per CU on 256 CUs
+  int groups = batch * num_kv_heads;
+  int s = groups >= target_groups ? 1 : (target_groups + groups - 1) / groups;
+  int by_len = max_seq_len / 256;
+  if (by_len < 1) by_len = 1;
+  if (s > by_len) s = by_len;
+  if (s > FQ_MAX_SPLITS) s = FQ_MAX_SPLITS;
+  if (s < 1) s = 1;
+  return s;
+}
+
+}  // namespace fq
+
+extern "C" {
+
+const char* fq_status_string(int status) {
+  switch (status) {
+    case FQ_OK: return "FQ_OK";
+    case FQ_ERR_INVALID_ARG: return "FQ_ERR_INVALID_ARG";
+    case FQ_ERR_UNSUPPORTED: return "FQ_ERR_UNSUPPORTED";
+    case FQ_ERR_WORKSPACE: return "FQ_ERR_WORKSPACE";
+    case FQ_ERR_HIP: return "FQ_ERR_HIP";
+    default: return "FQ_ERR_UNKNOWN";
+  }
+}
+
+int fq_version(void) { return FQ_VERSION; }
+
+fq_status fq_compress(void* stream, const fq_quantizer* quant, const fq_cache* cache,
+                      const void* k, const void* v, int dtype, int64_t num_tokens,
+                      int64_t token_stride, int64_t head_stride, const int64_t* slot_mapping,
+                      float* debug_y, float* debug_p) {
+  fq_status st = check_quantizer(quant);
+  if (st != FQ_OK) return st;
+  st = check_cache(cache, quant);
+  if (st != FQ_OK) return st;
+  if (dtype != FQ_F32 && dtype != FQ_BF16) return FQ_ERR_INVALID_ARG;
+  if (num_tokens < 0 || token_stride < 0 || head_stride < 0) return FQ_ERR_INVALID_ARG;
+  if (num_tokens == 0 || (!k && !v)) return FQ_OK;
+  if (!slot_mapping || !aligned(slot_mapping, 8)) return FQ_ERR_INVALID_ARG;
+  const uintptr_t ea = dtype == FQ_F32 ? 4 : 2;
+  // every vector starts on a 16-byte boundary so the kernel can use 16-byte loads
+  const uintptr_t va = 16;
+  for (const void* p : {k, v}) {
+    if (!p) continue;
+    if (!aligned(p, va)) return FQ_ERR_INVALID_ARG;
+  }
+  if ((token_stride * ea) % va != 0 || (head_stride * ea) % va != 0) return FQ_ERR_INVALID_ARG;
+  if (num_tokens > 1 && token_stride == 0) return FQ_ERR_INVALID_ARG;
+  if (cache->num_kv_heads > 1 && head_stride == 0) return FQ_ERR_INVALID_ARG;
+  if (debug_y && !aligned(debug_y, 16)) return FQ_ERR_INVALID_ARG;
+  if (debug_p && !aligned(debug_p, 16)) return FQ_ERR_INVALID_ARG;
+  if (num_tokens * cache->num_kv_heads > (int64_t{1} << 31) - 1) return FQ_ERR_UNSUPPORTED;
+  int e = fq::launch_compress(stream, *quant, *cache, k, v, dtype, num_tokens, token_stride,
+                              head_stride, slot_mapping, debug_y, debug_p);
+  return e == 0 ? FQ_OK : FQ_ERR_HIP;
+}
+
+int fq_decode_auto_splits(int batch, int num_kv_heads, int max_seq_len) {
+  if (batch <= 0 || num_kv_heads <= 0 || max_seq_len < 0) return 1;
+  return fq::auto_splits(batch, num_kv_heads, max_seq_len);
+}
+
+fq_status fq_decode_workspace_size(int batch, int num_q_heads, int num_kv_heads, int head_dim,
+                                   int qjl_dim, int max_seq_len, int num_splits, size_t* bytes) {
+  if (!bytes) return FQ_ERR_INVALID_ARG;
+  if (batch < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || max_seq_len < 0 || num_splits < 0)
+    return FQ_ERR_INVALID_ARG;
+  if (head_dim != FQ_HEAD_DIM || (qjl_dim != 0 && qjl_dim != FQ_HEAD_DIM))
+    return FQ_ERR_UNSUPPORTED;
+  if (num_splits > FQ_MAX_SPLITS) return FQ_ERR_UNSUPPORTED;
+  int s = num_splits == 0 ? fq::auto_splits(batch, num_kv_heads, max_seq_len) : num_splits;
+  *bytes = fq::decode_workspace(batch, num_q_heads, head_dim, qjl_dim, s).total;
+  return FQ_OK;
+}
+
+fq_status fq_decode_attention(void* stream, const fq_quantizer* quant, const fq_cache* cache,
+                              const void* q, int q_dtype, int batch, int num_q_heads,
+                              const int32_t* block_tables, int max_blocks_per_seq,
+                              const int32_t* seq_lens, int max_seq_len, int num_splits,
+                              float scale, void* workspace, size_t workspace_bytes, float* out) {
+  fq_status st = check_quantizer(quant);
+  if (st != FQ_OK) return st;
+  st = check_cache(cache, quant);
+  if (st != FQ_OK) return st;
+  if (q_dtype != FQ_F32 && q_dtype != FQ_BF16) return FQ_ERR_INVALID_ARG;
+  if (batch < 0 || num_q_heads <= 0 || max_blocks_per_seq < 0 || max_seq_len < 0 ||
+      num_splits < 0)
+    return FQ_ERR_INVALID_ARG;
+  if (num_q_heads % cache->num_kv_heads != 0) return FQ_ERR_INVALID_ARG;
+  if (num_q_heads / cache->num_kv_heads > FQ_MAX_GROUP) return FQ_ERR_UNSUPPORTED;
+  if (num_splits > FQ_MAX_SPLITS) return FQ_ERR_UNSUPPORTED;
+  if (static_cast<int64_t>(max_seq_len) > static_cast<int64_t>(max_blocks_per_seq) * FQ_BLOCK)
+    return FQ_ERR_INVALID_ARG;
+  if (batch == 0) return FQ_OK;
+  if (!q || !block_tables || !seq_lens || !out) return FQ_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(block_tables, 4) || !aligned(seq_lens, 4) || !aligned(out, 16))
+    return FQ_ERR_INVALID_ARG;
+  const int s = num_splits == 0 ? fq::auto_splits(batch, cache->num_kv_heads, max_seq_len)
+                                : num_splits;
+  const size_t need = fq::decode_workspace(batch, num_q_heads, FQ_HEAD_DIM, quant->qjl_dim, s).total;
+  if (!workspace || workspace_bytes < need || !aligned(workspace, 256)) return FQ_ERR_WORKSPACE;
+  int e = fq::launch_decode(stream, *quant, *cache, q, q_dtype, batch, num_q_heads, block_tables,
+                            max_blocks_per_seq, seq_lens, max_seq_len, s, scale, workspace, out);
+  return e == 0 ? FQ_OK : FQ_ERR_HIP;
+}
+
+}  // extern "C"

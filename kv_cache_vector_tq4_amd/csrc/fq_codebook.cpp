@@ -1,0 +1,176 @@
+// Host-side builder of a layer's quantizer: Lloyd-Max codebook, rotation,
+// QJL matrix. "FlashQuant" page, "TurboQuant" steps 2-3 (Haar rotation,
+// Gaussian Lloyd-Max with closed-form centroids) and "QJL" (Gaussian
+// projection S); "TurboQuant" blog, "Couche 1" (randomized Walsh-Hadamard).
+// Everything is computed in double and rounded once to fp32 on output.
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <vector>
+
+#include "fq.h"
+#include "fq_internal.h"
+
+namespace {
+
+// SplitMix64 (Steele, Lea & Flood 2014), addressed by counter: output i of
+// the stream started at `seed`.
+inline uint64_t splitmix64_at(uint64_t seed, uint64_t i) {
+  uint64_t z = seed + (i + 1) * 0x9E3779B97F4A7C15ull;
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
+}
+
+inline double uniform_at(uint64_t seed, uint64_t i) {
+  return (static_cast<double>(splitmix64_at(seed, i) >> 11) + 0.5) * 0x1.0p-53;
+}
+
+// n standard normals by Box-Muller; pair p uses uniforms 2p and 2p+1.
+void gaussians(uint64_t seed, size_t n, double* out) {
+  const double two_pi = 6.283185307179586476925286766559;
+  for (size_t p = 0; 2 * p < n; ++p) {
+    double u1 = uniform_at(seed, 2 * p), u2 = uniform_at(seed, 2 * p + 1);
+    double r = std::sqrt(-2.0 * std::log(u1));
+    out[2 * p] = r * std::cos(two_pi * u2);
+    if (2 * p + 1 < n) out[2 * p + 1] = r * std::sin(two_pi * u2);
+  }
+}
+
+double npdf(double x) { return std::isinf(x) ? 0.0 : std::exp(-0.5 * x * x) * 0.39894228040143267794; }
+
+// P(a < Z <= b), evaluated on the side of zero where it does not cancel.
+double nmass(double a, double b) {
+  const double r2 = 0.70710678118654752440;
+  if (a >= 0) return 0.5 * std::erfc(a * r2) - 0.5 * std::erfc(b * r2);
+  return 0.5 * std::erfc(-b * r2) - 0.5 * std::erfc(-a * r2);
+}
+
+// Phi^{-1}(p) by bisection on the CDF (only the starting point of Lloyd).
+double nquantile(double p) {
+  double lo = -40.0, hi = 40.0;
+  for (int i = 0; i < 200; ++i) {
+    double mid = 0.5 * (lo + hi);
+    double cdf = 0.5 * std::erfc(-mid * 0.70710678118654752440);
+    if (cdf < p) lo = mid; else hi = mid;
+  }
+  return 0.5 * (lo + hi);
+}
+
+void lloyd_max(int bits, std::vector<double>& lev, std::vector<double>& bnd) {
+  const int L = 1 << bits;
+  lev.resize(L);
+  bnd.resize(L - 1);
+  for (int i = 0; i < L; ++i) lev[i] = nquantile((i + 0.5) / L);
+  std::vector<double> nl(L);
+  for (int it = 0; it < 200000; ++it) {
+    for (int i = 0; i + 1 < L; ++i) bnd[i] = 0.5 * (lev[i] + lev[i + 1]);
+    double delta = 0;
+    for (int i = 0; i < L; ++i) {
+      double a = i == 0 ? -INFINITY : bnd[i - 1];
+      double b = i == L - 1 ? INFINITY : bnd[i];
+      nl[i] = (npdf(a) - npdf(b)) / nmass(a, b);
+      delta = std::fmax(delta, std::fabs(nl[i] - lev[i]));
+    }
+    lev = nl;
+    if (delta < 1e-15) break;
+  }
+  std::vector<double> sym(L);
+  for (int i = 0; i < L; ++i) sym[i] = 0.5 * (lev[i] - lev[L - 1 - i]);
+  lev = sym;
+  for (int i = 0; i + 1 < L; ++i) bnd[i] = 0.5 * (lev[i] + lev[i + 1]);
+}
+
+// Haar orthogonal matrix: Householder QR of a Gaussian matrix, Q with the
+// columns' signs flipped so that diag(R) > 0. a: d x d row-major, overwritten.
+void haar_from_gaussian(int d, std::vector<double>& a, std::vector<double>& q) {
+  std::vector<double> vs(static_cast<size_t>(d) * d, 0.0);  // Householder vectors, row k
+  std::vector<double> rdiag(d);
+  for (int k = 0; k < d; ++k) {
+    double norm2 = 0;
+    for (int i = k; i < d; ++i) norm2 += a[i * d + k] * a[i * d + k];
+    double nrm = std::sqrt(norm2);
+    double x0 = a[k * d + k];
+    double alpha = x0 >= 0 ? -nrm : nrm;
+    double* v = &vs[static_cast<size_t>(k) * d];
+    for (int i = k; i < d; ++i) v[i] = a[i * d + k];
+    v[k] -= alpha;
+    double vn2 = 0;
+    for (int i = k; i < d; ++i) vn2 += v[i] * v[i];
+    rdiag[k] = alpha;
+    if (vn2 == 0) continue;
+    double inv = 1.0 / std::sqrt(vn2);
+    for (int i = k; i < d; ++i) v[i] *= inv;
+    for (int j = k; j < d; ++j) {
+      double dot = 0;
+      for (int i = k; i < d; ++i) dot += v[i] * a[i * d + j];
+      for (int i = k; i < d; ++i) a[i * d + j] -= 2.0 * dot * v[i];
+    }
+  }
+  // Q = H_0 H_1 ... H_{d-1}: apply the reflectors to I in reverse order.
+  q.assign(static_cast<size_t>(d) * d, 0.0);
+  for (int i = 0; i < d; ++i) q[i * d + i] = 1.0;
+  for (int k = d - 1; k >= 0; --k) {
+    const double* v = &vs[static_cast<size_t>(k) * d];
+    for (int j = 0; j < d; ++j) {
+      double dot = 0;
+      for (int i = k; i < d; ++i) dot += v[i] * q[i * d + j];
+      for (int i = k; i < d; ++i) q[i * d + j] -= 2.0 * dot * v[i];
+    }
+  }
+  for (int j = 0; j < d; ++j)
+    if (rdiag[j] < 0)
+      for (int i = 0; i < d; ++i) q[i * d + j] = -q[i * d + j];
+}
+
+}  // namespace
+
+extern "C" fq_status fq_build_codebook(int bits, int head_dim, int rotation, uint64_t rot_seed,
+                                       uint64_t qjl_seed, int qjl_dim, float* levels,
+                                       float* boundaries, float* rotation_matrix,
+                                       float* rotation_t, float* wht_signs, float* qjl_matrix) {
+  if (!levels || !boundaries) return FQ_ERR_INVALID_ARG;
+  if (rotation != FQ_ROT_HAAR && rotation != FQ_ROT_WHT) return FQ_ERR_INVALID_ARG;
+  if (bits != 2 && bits != 4) return FQ_ERR_UNSUPPORTED;
+  if (head_dim != FQ_HEAD_DIM) return FQ_ERR_UNSUPPORTED;
+  if (qjl_dim != 0 && qjl_dim != FQ_HEAD_DIM) return FQ_ERR_UNSUPPORTED;
+  const int d = head_dim;
+  const double inv_sqrt_d = 1.0 / std::sqrt(static_cast<double>(d));
+
+  std::vector<double> lev, bnd;
+  lloyd_max(bits, lev, bnd);
+  for (size_t i = 0; i < lev.size(); ++i) levels[i] = static_cast<float>(lev[i] * inv_sqrt_d);
+  for (size_t i = 0; i < bnd.size(); ++i) boundaries[i] = static_cast<float>(bnd[i] * inv_sqrt_d);
+
+  std::vector<double> pi(static_cast<size_t>(d) * d);
+  if (rotation == FQ_ROT_HAAR) {
+    if (rotation_matrix || rotation_t) {
+      std::vector<double> g(static_cast<size_t>(d) * d);
+      gaussians(rot_seed, g.size(), g.data());
+      haar_from_gaussian(d, g, pi);
+    }
+  } else {
+    std::vector<double> s(d);
+    for (int j = 0; j < d; ++j) s[j] = (splitmix64_at(rot_seed, j) >> 63) ? -1.0 : 1.0;
+    if (wht_signs)
+      for (int j = 0; j < d; ++j) wht_signs[j] = static_cast<float>(s[j]);
+    // Pi[i][j] = H[i][j] s_j / sqrt(d); Sylvester H[i][j] = (-1)^popcount(i & j).
+    for (int i = 0; i < d; ++i)
+      for (int j = 0; j < d; ++j) {
+        double h = (__builtin_popcount(static_cast<unsigned>(i & j)) & 1) ? -1.0 : 1.0;
+        pi[i * d + j] = h * s[j] * inv_sqrt_d;
+      }
+  }
+  for (int i = 0; i < d; ++i)
+    for (int j = 0; j < d; ++j) {
+      if (rotation_matrix) rotation_matrix[i * d + j] = static_cast<float>(pi[i * d + j]);
+      if (rotation_t) rotation_t[j * d + i] = static_cast<float>(pi[i * d + j]);
+    }
+
+  if (qjl_dim > 0 && qjl_matrix) {
+    std::vector<double> s(static_cast<size_t>(qjl_dim) * d);
+    gaussians(qjl_seed, s.size(), s.data());
+    for (size_t i = 0; i < s.size(); ++i) qjl_matrix[i] = static_cast<float>(s[i]);
+  }
+  return FQ_OK;
+}

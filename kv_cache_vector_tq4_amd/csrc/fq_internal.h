@@ -1,0 +1,41 @@
+// Internal declarations shared by the C-ABI layer and the HIP launchers.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+
+#include "fq.h"
+
+#define FQ_HEAD_DIM 128
+#define FQ_BLOCK 16
+#define FQ_MAX_GROUP 16
+#define FQ_MAX_SPLITS 64
+#define FQ_VERSION 100
+
+namespace fq {
+
+// Workspace carve-up of fq_decode_attention (offsets in bytes, 256-aligned).
+struct DecodeWorkspace {
+  size_t qrot;    // f32 [B][Hq][d]        rotated queries
+  size_t qs;      // f32 [B][Hq][m]        S q~ (when qjl_dim > 0)
+  size_t part_o;  // f32 [B][Hq][splits][d] unnormalised o_rot per split
+  size_t part_ml; // f32 [B][Hq][splits][2] running max and sum per split
+  size_t total;
+};
+
+DecodeWorkspace decode_workspace(int batch, int num_q_heads, int head_dim, int qjl_dim,
+                                 int num_splits);
+int auto_splits(int batch, int num_kv_heads, int max_seq_len);
+
+// Launchers: arguments already validated; return hipSuccess or the launch error.
+int launch_compress(void* stream, const fq_quantizer& q, const fq_cache& c, const void* k,
+                    const void* v, int dtype, int64_t num_tokens, int64_t token_stride,
+                    int64_t head_stride, const int64_t* slot_mapping, float* debug_y,
+                    float* debug_p);
+
+int launch_decode(void* stream, const fq_quantizer& q, const fq_cache& c, const void* qv,
+                  int q_dtype, int batch, int num_q_heads, const int32_t* block_tables,
+                  int max_blocks_per_seq, const int32_t* seq_lens, int max_seq_len,
+                  int num_splits, float scale, void* workspace, float* out);
+
+}  // namespace fq

@@ -1,0 +1,257 @@
+"""Python binding of libfq (ctypes): argument marshalling only.
+
+Every step of the method runs inside libfq (host builder or HIP kernels).
+PyTorch supplies device memory and the stream. The binding refuses to run
+without the built library: there is no fallback path.
+"""
+import ctypes
+import math
+import os
+
+import numpy as np
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libfq.so")
+
+FQ_OK, FQ_ERR_INVALID_ARG, FQ_ERR_UNSUPPORTED, FQ_ERR_WORKSPACE, FQ_ERR_HIP = range(5)
+ROT_HAAR, ROT_WHT = 0, 1
+F32, BF16 = 0, 1
+BLOCK = 16
+
+_lib = None
+
+
+class FQError(RuntimeError):
+    def __init__(self, status, what):
+        self.status = status
+        super().__init__("%s failed: %s" % (what, status_string(status)))
+
+
+class QuantizerT(ctypes.Structure):
+    _fields_ = [
+        ("bits", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("rotation", ctypes.c_int32),
+        ("qjl_dim", ctypes.c_int32),
+        ("levels", ctypes.c_void_p),
+        ("boundaries", ctypes.c_void_p),
+        ("rotation_matrix", ctypes.c_void_p),
+        ("rotation_t", ctypes.c_void_p),
+        ("wht_signs", ctypes.c_void_p),
+        ("qjl_matrix", ctypes.c_void_p),
+    ]
+
+
+class CacheT(ctypes.Structure):
+    _fields_ = [
+        ("num_blocks", ctypes.c_int32),
+        ("block_size", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("bits", ctypes.c_int32),
+        ("qjl_dim", ctypes.c_int32),
+        ("k_codes", ctypes.c_void_p),
+        ("k_norm", ctypes.c_void_p),
+        ("k_qjl", ctypes.c_void_p),
+        ("k_gamma", ctypes.c_void_p),
+        ("v_codes", ctypes.c_void_p),
+        ("v_norm", ctypes.c_void_p),
+    ]
+
+
+EXPORTS = {
+    "fq_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "fq_version": (ctypes.c_int, []),
+    "fq_build_codebook": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_uint64,
+                                         ctypes.c_uint64, ctypes.c_int] + [ctypes.c_void_p] * 6),
+    "fq_compress": (ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(QuantizerT), ctypes.POINTER(CacheT),
+                                   ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int64,
+                                   ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p,
+                                   ctypes.c_void_p]),
+    "fq_decode_auto_splits": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, ctypes.c_int]),
+    "fq_decode_workspace_size": (ctypes.c_int, [ctypes.c_int] * 7 + [ctypes.POINTER(ctypes.c_size_t)]),
+    "fq_decode_attention": (ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(QuantizerT), ctypes.POINTER(CacheT),
+                                           ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                           ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_int,
+                                           ctypes.c_int, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t,
+                                           ctypes.c_void_p]),
+}
+
+
+def lib():
+    """The loaded libfq; raises if the HIP library has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError("libfq.so is not built (run `python -m kv_cache_vector_tq4_amd.build`)")
+        h = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in EXPORTS.items():
+            f = getattr(h, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = h
+    return _lib
+
+
+def status_string(status):
+    return lib().fq_status_string(int(status)).decode()
+
+
+def _check(status, what):
+    if status != FQ_OK:
+        raise FQError(status, what)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    import torch
+
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def build_codebook(bits=4, head_dim=128, rotation=ROT_HAAR, rot_seed=1, qjl_seed=2, qjl_dim=128):
+    """Host arrays of one layer's quantizer, built by libfq (fq_build_codebook)."""
+    L = 1 << bits
+    out = {
+        "levels": np.zeros(L, np.float32),
+        "boundaries": np.zeros(L - 1, np.float32),
+        "rotation_matrix": np.zeros((head_dim, head_dim), np.float32),
+        "rotation_t": np.zeros((head_dim, head_dim), np.float32),
+        "wht_signs": np.zeros(head_dim, np.float32),
+        "qjl_matrix": np.zeros((max(qjl_dim, 1), head_dim), np.float32),
+    }
+    p = lambda a: a.ctypes.data_as(ctypes.c_void_p)
+    st = lib().fq_build_codebook(bits, head_dim, rotation, rot_seed, qjl_seed, qjl_dim,
+                                 p(out["levels"]), p(out["boundaries"]), p(out["rotation_matrix"]),
+                                 p(out["rotation_t"]), p(out["wht_signs"]),
+                                 p(out["qjl_matrix"]) if qjl_dim else None)
+    _check(st, "fq_build_codebook")
+    out.update(bits=bits, head_dim=head_dim, rotation=rotation, qjl_dim=qjl_dim)
+    return out
+
+
+class Quantizer:
+    """Device copy of a layer's quantizer parameters plus the C struct pointing at them."""
+
+    def __init__(self, bits=4, head_dim=128, rotation=ROT_HAAR, rot_seed=1, qjl_seed=2, qjl_dim=128,
+                 device="cuda"):
+        import torch
+
+        self.host = build_codebook(bits, head_dim, rotation, rot_seed, qjl_seed, qjl_dim)
+        self.bits, self.head_dim, self.rotation, self.qjl_dim = bits, head_dim, rotation, qjl_dim
+        self.dev = {k: torch.from_numpy(np.ascontiguousarray(self.host[k])).to(device)
+                    for k in ("levels", "boundaries", "rotation_matrix", "rotation_t", "wht_signs", "qjl_matrix")}
+        d = self.dev
+        self.struct = QuantizerT(bits, head_dim, rotation, qjl_dim, d["levels"].data_ptr(),
+                                 d["boundaries"].data_ptr(), d["rotation_matrix"].data_ptr(),
+                                 d["rotation_t"].data_ptr(), d["wht_signs"].data_ptr(),
+                                 d["qjl_matrix"].data_ptr() if qjl_dim else None)
+
+
+class PagedCache:
+    """A layer's paged compressed cache in device memory (torch tensors) plus its C struct."""
+
+    def __init__(self, num_blocks, num_kv_heads, head_dim=128, bits=4, qjl_dim=128, device="cuda"):
+        import torch
+
+        cb = head_dim * bits // 8
+        self.num_blocks, self.num_kv_heads, self.head_dim = num_blocks, num_kv_heads, head_dim
+        self.bits, self.qjl_dim = bits, qjl_dim
+        z = lambda *shape, dt: torch.zeros(shape, dtype=dt, device=device)
+        self.k_codes = z(num_blocks, num_kv_heads, BLOCK, cb, dt=torch.uint8)
+        self.k_norm = z(num_blocks, num_kv_heads, BLOCK, dt=torch.float32)
+        self.v_codes = z(num_blocks, num_kv_heads, BLOCK, cb, dt=torch.uint8)
+        self.v_norm = z(num_blocks, num_kv_heads, BLOCK, dt=torch.float32)
+        if qjl_dim:
+            self.k_qjl = z(num_blocks, num_kv_heads, BLOCK, qjl_dim // 8, dt=torch.uint8)
+            self.k_gamma = z(num_blocks, num_kv_heads, BLOCK, dt=torch.float32)
+        else:
+            self.k_qjl = self.k_gamma = None
+        self.struct = CacheT(num_blocks, BLOCK, num_kv_heads, head_dim, bits, qjl_dim,
+                             self.k_codes.data_ptr(), self.k_norm.data_ptr(),
+                             self.k_qjl.data_ptr() if qjl_dim else None,
+                             self.k_gamma.data_ptr() if qjl_dim else None,
+                             self.v_codes.data_ptr(), self.v_norm.data_ptr())
+
+    def fields(self):
+        out = {"k_codes": self.k_codes, "k_norm": self.k_norm, "v_codes": self.v_codes, "v_norm": self.v_norm}
+        if self.qjl_dim:
+            out.update(k_qjl=self.k_qjl, k_gamma=self.k_gamma)
+        return out
+
+    def bytes_per_token_head(self):
+        cb = self.head_dim * self.bits // 8
+        return 2 * (cb + 4) + ((self.qjl_dim // 8 + 4) if self.qjl_dim else 0)
+
+
+def _dtype_code(t):
+    import torch
+
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype == torch.float32:
+        return F32
+    raise TypeError("K/V/q must be float32 or bfloat16, got %s" % t.dtype)
+
+
+def compress(quant, cache, k, v, slot_mapping, debug=False, stream=None):
+    """fq_compress: K, V [T, Hkv, d] (innermost contiguous), slot_mapping int64 [T].
+
+    Returns (debug_y [2, T, Hkv, d], debug_p [T, Hkv, m]) when debug, else None.
+    """
+    import torch
+
+    src = k if k is not None else v
+    T = src.shape[0]
+    for x in (k, v):
+        if x is not None:
+            assert x.shape[1:] == (cache.num_kv_heads, cache.head_dim) and x.stride(2) == 1
+            assert x.dtype == src.dtype and x.stride() == src.stride()
+    assert slot_mapping.dtype == torch.int64 and slot_mapping.numel() == T and slot_mapping.is_contiguous()
+    dy = dp = None
+    if debug:
+        dy = torch.zeros((2, T, cache.num_kv_heads, cache.head_dim), dtype=torch.float32, device=src.device)
+        dp = torch.zeros((T, cache.num_kv_heads, max(quant.qjl_dim, 1)), dtype=torch.float32, device=src.device)
+    st = lib().fq_compress(_stream(stream), ctypes.byref(quant.struct), ctypes.byref(cache.struct),
+                           _ptr(k), _ptr(v), _dtype_code(src), T, src.stride(0), src.stride(1),
+                           _ptr(slot_mapping), _ptr(dy), _ptr(dp))
+    _check(st, "fq_compress")
+    return (dy, dp) if debug else None
+
+
+def auto_splits(batch, num_kv_heads, max_seq_len):
+    return int(lib().fq_decode_auto_splits(batch, num_kv_heads, max_seq_len))
+
+
+def workspace_bytes(batch, num_q_heads, num_kv_heads, head_dim, qjl_dim, max_seq_len, num_splits=0):
+    n = ctypes.c_size_t(0)
+    st = lib().fq_decode_workspace_size(batch, num_q_heads, num_kv_heads, head_dim, qjl_dim, max_seq_len,
+                                        num_splits, ctypes.byref(n))
+    _check(st, "fq_decode_workspace_size")
+    return int(n.value)
+
+
+def decode(quant, cache, q, block_tables, seq_lens, max_seq_len, num_splits=0, scale=None, workspace=None,
+           out=None, stream=None):
+    """fq_decode_attention: q [B, Hq, d] -> out fp32 [B, Hq, d]."""
+    import torch
+
+    B, Hq, d = q.shape
+    assert q.is_contiguous() and block_tables.dtype == torch.int32 and seq_lens.dtype == torch.int32
+    assert block_tables.is_contiguous() and seq_lens.is_contiguous()
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    need = workspace_bytes(B, Hq, cache.num_kv_heads, d, quant.qjl_dim, max_seq_len, num_splits)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    if out is None:
+        out = torch.empty((B, Hq, d), dtype=torch.float32, device=q.device)
+    st = lib().fq_decode_attention(_stream(stream), ctypes.byref(quant.struct), ctypes.byref(cache.struct),
+                                   _ptr(q), _dtype_code(q), B, Hq, _ptr(block_tables), block_tables.shape[1],
+                                   _ptr(seq_lens), int(max_seq_len), int(num_splits), float(scale),
+                                   _ptr(workspace), workspace.numel() * workspace.element_size(), _ptr(out))
+    _check(st, "fq_decode_attention")
+    return out

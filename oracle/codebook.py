@@ -9,8 +9,8 @@ the centroid update has a closed form. Section "架构设计" lists the codebook
 Readings taken where the pages are silent or disagree:
 * distribution: N(0, 1) levels scaled by 1/sqrt(d) (the blog's spherical-Beta
   codebook is not used);
-* the codebook is the Lloyd fixed point (iterate until the largest level change
-  is below 1e-13), not a fixed iteration count;
+* the codebook is the Lloyd fixed point in float64 (iterate until the largest
+  level change is below 1e-15, a few ulps), not a fixed iteration count;
 * levels are made exactly antisymmetric (l[L-1-i] = -l[i]) so the middle
   boundary is exactly 0;
 * stored values: level_i = fp32(l_i / sqrt(d)), boundary_i = fp32(b_i / sqrt(d)),
@@ -37,7 +37,7 @@ def _mass(a, b):
     return np.where(upper, ndtr(-a) - ndtr(-b), ndtr(b) - ndtr(a))
 
 
-def lloyd_max_gaussian(bits: int, tol: float = 1e-13, max_iter: int = 200000):
+def lloyd_max_gaussian(bits: int, tol: float = 1e-15, max_iter: int = 200000):
     """Fixed point of the Lloyd iteration for N(0,1) with 2**bits cells (float64).
 
     Returns (levels, boundaries, iterations, residual), levels ascending,

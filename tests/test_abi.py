@@ -1,0 +1,143 @@
+"""CPU tests of the C-ABI library: it loads, exports every declared entry point,
+its host-side builder matches the oracle, and argument checks return their
+status codes without touching a device."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from kv_cache_vector_tq4_amd import fq
+from oracle import pipeline
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    names = set()
+    for fn in os.listdir(os.path.join(ROOT, "include")):
+        if fn.endswith(".h"):
+            text = open(os.path.join(ROOT, "include", fn)).read()
+            text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+            names |= set(re.findall(r"\b(fq_[a-z0-9_]+)\s*\(", text))
+    return names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = fq.lib()
+    declared = _declared()
+    assert {"fq_build_codebook", "fq_compress", "fq_decode_attention"} <= declared
+    for name in declared:
+        assert hasattr(lib, name), name
+    assert set(fq.EXPORTS) == declared
+
+
+def test_status_strings():
+    assert fq.status_string(0) == "FQ_OK"
+    assert fq.status_string(3) == "FQ_ERR_WORKSPACE"
+    assert fq.status_string(99) == "FQ_ERR_UNKNOWN"
+
+
+@pytest.mark.parametrize("bits", [2, 4])
+@pytest.mark.parametrize("rot", [fq.ROT_HAAR, fq.ROT_WHT])
+def test_builder_matches_oracle(bits, rot):
+    lib_cb = fq.build_codebook(bits, 128, rot, rot_seed=11, qjl_seed=12, qjl_dim=128)
+    ora = pipeline.build(bits, 128, rot=rot, rot_seed=11, qjl_seed=12)
+    assert np.array_equal(lib_cb["levels"], ora["levels"])
+    assert np.array_equal(lib_cb["boundaries"], ora["boundaries"])
+    pi = lib_cb["rotation_matrix"].astype(np.float64)
+    assert np.max(np.abs(pi - ora["pi"])) <= 1e-6
+    assert np.array_equal(lib_cb["rotation_t"], lib_cb["rotation_matrix"].T)
+    assert np.array_equal(lib_cb["qjl_matrix"].astype(np.float64), ora["s"])
+    if rot == fq.ROT_WHT:
+        assert np.array_equal(lib_cb["wht_signs"].astype(np.float64), ora["signs"])
+        assert np.array_equal(pi, ora["pi"])
+
+
+def test_builder_haar_matches_oracle_bitwise_mostly():
+    """Householder in C++ vs LAPACK: after rounding to fp32 nearly every entry is equal."""
+    lib_cb = fq.build_codebook(4, 128, fq.ROT_HAAR, rot_seed=1, qjl_seed=2)
+    ora = pipeline.build(4, 128)
+    diff = lib_cb["rotation_matrix"] != ora["pi"].astype(np.float32)
+    assert diff.mean() < 1e-3
+
+
+def test_builder_errors():
+    L = fq.lib()
+    buf = np.zeros(128 * 128, np.float32)
+    p = buf.ctypes.data_as(ctypes.c_void_p)
+    assert L.fq_build_codebook(3, 128, 0, 1, 2, 128, p, p, None, None, None, None) == fq.FQ_ERR_UNSUPPORTED
+    assert L.fq_build_codebook(4, 64, 0, 1, 2, 128, p, p, None, None, None, None) == fq.FQ_ERR_UNSUPPORTED
+    assert L.fq_build_codebook(4, 128, 5, 1, 2, 128, p, p, None, None, None, None) == fq.FQ_ERR_INVALID_ARG
+    assert L.fq_build_codebook(4, 128, 0, 1, 2, 128, None, p, None, None, None, None) == fq.FQ_ERR_INVALID_ARG
+    assert L.fq_build_codebook(4, 128, 0, 1, 2, 64, p, p, None, None, None, None) == fq.FQ_ERR_UNSUPPORTED
+
+
+def _fake_structs(bits=4, qjl=128, hkv=2):
+    """Structs whose pointers are aligned host addresses: only argument checks may see them."""
+    store = np.zeros(1 << 16, np.float32)
+    base = (store.ctypes.data + 255) & ~255
+    qz = fq.QuantizerT(bits, 128, fq.ROT_HAAR, qjl, base, base, base, base, base, base)
+    cz = fq.CacheT(4, 16, hkv, 128, bits, qjl, base, base, base, base, base, base)
+    return store, base, qz, cz
+
+
+def test_compress_argument_checks():
+    L = fq.lib()
+    store, base, qz, cz = _fake_structs()
+    call = lambda q, c, **kw: L.fq_compress(None, ctypes.byref(q) if q else None, ctypes.byref(c) if c else None,
+                                            kw.get("k", base), kw.get("v", base), kw.get("dt", fq.BF16),
+                                            kw.get("n", 4), kw.get("ts", 256), kw.get("hs", 128),
+                                            kw.get("slots", base), None, None)
+    assert call(None, cz) == fq.FQ_ERR_INVALID_ARG
+    assert call(qz, None) == fq.FQ_ERR_INVALID_ARG
+    assert call(qz, cz, dt=7) == fq.FQ_ERR_INVALID_ARG
+    assert call(qz, cz, n=-1) == fq.FQ_ERR_INVALID_ARG
+    assert call(qz, cz, n=0) == fq.FQ_OK                      # empty input is a no-op
+    assert call(qz, cz, k=None, v=None) == fq.FQ_OK
+    assert call(qz, cz, slots=None) == fq.FQ_ERR_INVALID_ARG
+    assert call(qz, cz, k=base + 2) == fq.FQ_ERR_INVALID_ARG  # vectors must be 16-byte aligned
+    assert call(qz, cz, hs=4) == fq.FQ_ERR_INVALID_ARG        # 8-byte head stride
+    qb = fq.QuantizerT(3, 128, 0, 128, base, base, base, base, base, base)
+    assert call(qb, cz) == fq.FQ_ERR_UNSUPPORTED
+    cb = fq.CacheT(4, 8, 2, 128, 4, 128, base, base, base, base, base, base)
+    assert call(qz, cb) == fq.FQ_ERR_UNSUPPORTED              # block size must be 16
+    cm = fq.CacheT(4, 16, 2, 128, 2, 128, base, base, base, base, base, base)
+    assert call(qz, cm) == fq.FQ_ERR_INVALID_ARG              # bits differ from the quantizer's
+    cn = fq.CacheT(4, 16, 2, 128, 4, 128, base, base, None, base, base, base)
+    assert call(qz, cn) == fq.FQ_ERR_INVALID_ARG              # QJL keys need k_qjl
+    qn = fq.QuantizerT(4, 128, 0, 128, base, base, base, None, base, base)
+    assert call(qn, cz) == fq.FQ_ERR_INVALID_ARG              # Pi^T required
+
+
+def test_decode_argument_checks_and_workspace():
+    L = fq.lib()
+    store, base, qz, cz = _fake_structs(hkv=2)
+    n = fq.workspace_bytes(3, 8, 2, 128, 128, 1000, 4)
+    assert n >= 3 * 8 * 128 * 4 * 2 + 3 * 8 * 4 * (128 + 2) * 4
+    assert fq.workspace_bytes(3, 8, 2, 128, 128, 1000, 0) == fq.workspace_bytes(
+        3, 8, 2, 128, 128, 1000, fq.auto_splits(3, 2, 1000))
+
+    def call(**kw):
+        return L.fq_decode_attention(None, ctypes.byref(qz), ctypes.byref(cz), kw.get("q", base), fq.F32,
+                                     kw.get("B", 3), kw.get("hq", 8), base, kw.get("mb", 63), base,
+                                     kw.get("ms", 1000), kw.get("ns", 4), 0.088, kw.get("ws", base),
+                                     kw.get("wb", n), kw.get("out", base))
+    assert call(hq=7) == fq.FQ_ERR_INVALID_ARG       # Hq not a multiple of Hkv
+    assert call(hq=2 * 17) == fq.FQ_ERR_UNSUPPORTED  # group of 17 query heads
+    assert call(ns=65) == fq.FQ_ERR_UNSUPPORTED
+    assert call(ms=63 * 16 + 1) == fq.FQ_ERR_INVALID_ARG
+    assert call(out=None) == fq.FQ_ERR_INVALID_ARG
+    assert call(wb=n - 1) == fq.FQ_ERR_WORKSPACE
+    assert call(ws=None) == fq.FQ_ERR_WORKSPACE
+    assert call(ws=base + 16) == fq.FQ_ERR_WORKSPACE  # 256-byte alignment
+    assert call(B=0) == fq.FQ_OK
+
+
+def test_auto_splits():
+    assert fq.auto_splits(1, 8, 4096) == 16
+    assert fq.auto_splits(1, 8, 32768) == 64
+    assert fq.auto_splits(32, 8, 4096) == 2
+    assert fq.auto_splits(64, 8, 4096) == 1
+    assert fq.auto_splits(1, 1, 100) == 1

@@ -1,0 +1,107 @@
+"""GPU parity of fq_compress against the oracle (through the C ABI)."""
+import numpy as np
+import pytest
+
+from kv_cache_vector_tq4_amd import fq, synth
+from tests import parity
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(w, inp, rot=fq.ROT_HAAR, qjl=128, rot_seed=1, qjl_seed=2):
+    t = parity.torch_inputs(inp, w.dtype)
+    qz = fq.Quantizer(w.bits, 128, rot, rot_seed, qjl_seed, 128)
+    cache = fq.PagedCache(inp["num_blocks"], w.num_kv_heads, 128, w.bits, qjl)
+    dy, dp = fq.compress(qz, cache, t["k"], t["v"], t["slots"], debug=True)
+    oq = parity.oracle_quantizer(w.bits, rot=rot, rot_seed=rot_seed, qjl_seed=qjl_seed)
+    return qz, cache, dy, dp, oq, t
+
+
+@pytest.mark.parametrize("bits", [4, 2])
+@pytest.mark.parametrize("rot", [fq.ROT_HAAR, fq.ROT_WHT])
+def test_compress_tiny_f32(gpu_lib, bits, rot):
+    w = synth.workload(0, bits=bits)
+    inp = synth.layer_inputs(w)
+    qz, cache, dy, dp, oq, _ = _run(w, inp, rot=rot)
+    c = parity.check_compress(inp, oq, cache, dy, dp)
+    print("near-tie mismatches", c)
+
+
+@pytest.mark.parametrize("bits", [4, 2])
+def test_compress_ragged_bf16_several_tiles(gpu_lib, bits):
+    """Ragged lengths (not multiples of 16 or 64), skipped slots, GQA shapes, bf16."""
+    w, inp = parity.small_workload(3, 8, 4, [1, 77, 300], 320, bits=bits, seed=31)
+    qz, cache, dy, dp, oq, _ = _run(w, inp)
+    c = parity.check_compress(inp, oq, cache, dy, dp)
+    print("near-tie mismatches", c)
+    # slots of tokens past each sequence's length were never written
+    host = parity.cache_to_host(cache)
+    used = np.zeros(inp["num_blocks"] * 16, bool)
+    used[inp["slot_mapping"][inp["slot_mapping"] >= 0]] = True
+    unused = ~used.reshape(-1, 16)
+    assert np.all(host["k_norm"].transpose(0, 2, 1)[unused] == 0)
+    assert np.all(host["v_codes"].transpose(0, 2, 1, 3)[unused] == 0)
+
+
+def test_compress_mse_only_keys(gpu_lib):
+    w, inp = parity.small_workload(1, 4, 2, [100], 112, seed=3)
+    qz, cache, dy, dp, oq, _ = _run(w, inp, qjl=0)
+    assert cache.k_qjl is None
+    parity.check_compress(inp, oq, cache, dy, None)
+
+
+def test_compress_zero_and_extreme_vectors(gpu_lib):
+    """n = 0 gives y = 0 (all codes = #{boundaries < 0}); a huge-norm and a one-hot vector."""
+    import torch
+
+    w, inp = parity.small_workload(1, 2, 2, [16], 16, dtype="f32", seed=5)
+    inp["k"][0, 0, 0] = 0.0
+    inp["v"][0, 1, 1] = 0.0
+    inp["k"][0, 2, 1] = 0.0
+    inp["k"][0, 2, 1, 5] = 3.0
+    inp["v"][0, 3, 0] *= 1e6
+    qz, cache, dy, dp, oq, _ = _run(w, inp)
+    parity.check_compress(inp, oq, cache, dy, dp)
+    host = parity.cache_to_host(cache)
+    s0 = inp["slot_mapping"][0]
+    assert host["k_norm"][s0 // 16, 0, s0 % 16] == 0
+    assert np.all(host["k_codes"][s0 // 16, 0, s0 % 16] == 0x77)
+    assert host["k_gamma"][s0 // 16, 0, s0 % 16] == 0
+
+
+def test_compress_strided_input(gpu_lib):
+    """K and V may be views with token / head strides (e.g. slices of a fused QKV buffer)."""
+    import torch
+
+    w, inp = parity.small_workload(1, 8, 2, [50], 64, seed=9)
+    t = parity.torch_inputs(inp, "bf16")
+    fused = torch.zeros((t["k"].shape[0], 3, 2, 128), dtype=torch.bfloat16, device="cuda")
+    fused[:, 1] = t["k"]
+    fused[:, 2] = t["v"]
+    qz = fq.Quantizer(4, 128, fq.ROT_HAAR, 1, 2, 128)
+    cache = fq.PagedCache(inp["num_blocks"], 2, 128, 4, 128)
+    dy, dp = fq.compress(qz, cache, fused[:, 1], fused[:, 2], t["slots"], debug=True)
+    oq = parity.oracle_quantizer(4)
+    parity.check_compress(inp, oq, cache, dy, dp)
+
+
+def test_compress_is_deterministic(gpu_lib):
+    w, inp = parity.small_workload(2, 8, 2, [200, 130], 208, seed=13)
+    outs = []
+    for _ in range(2):
+        qz, cache, dy, dp, oq, _ = _run(w, inp)
+        outs.append(parity.cache_to_host(cache))
+    for name in outs[0]:
+        assert np.array_equal(outs[0][name], outs[1][name]), name
+
+
+def test_compress_full_size_8b_layer_sampled(gpu_lib):
+    """Whole 4096-token context of the 8B-shaped layer (8 KV heads, bf16) in one launch;
+    sampled tokens of every head compared with the oracle."""
+    w = synth.workload(1)
+    inp = synth.layer_inputs(w)
+    qz, cache, dy, dp, oq, _ = _run(w, inp)
+    rs = np.random.default_rng(0)
+    tok = np.sort(rs.choice(4096, size=256, replace=False))
+    c = parity.check_compress(inp, oq, cache, dy, dp, tokens=tok)
+    print("near-tie mismatches", c)

@@ -1,0 +1,103 @@
+"""GPU parity of fq_decode_attention against the oracle (through the C ABI).
+
+The GPU decodes the oracle's own compressed bytes, so the comparison isolates
+the decode arithmetic; tolerance 1e-3 max-abs on the fp32 outputs."""
+import numpy as np
+import pytest
+import torch
+
+from kv_cache_vector_tq4_amd import fq, synth
+from tests import parity
+
+pytestmark = pytest.mark.gpu
+
+
+def _decode_case(w, inp, rot=fq.ROT_HAAR, with_qjl=True, num_splits=0, seqs=None):
+    t = parity.torch_inputs(inp, w.dtype)
+    oq = parity.oracle_quantizer(w.bits, rot=rot)
+    qz = fq.Quantizer(w.bits, 128, rot, 1, 2, 128)
+    host = parity.oracle_cache(inp, oq, with_qjl=with_qjl, seqs=seqs)
+    cache = fq.PagedCache(inp["num_blocks"], w.num_kv_heads, 128, w.bits, 128 if with_qjl else 0)
+    parity.upload_cache(host, cache)
+    out = fq.decode(qz, cache, t["q"], t["bt"], t["lens"], max(w.seq_lens), num_splits=num_splits)
+    torch.cuda.synchronize()
+    ref = parity.oracle_decode(inp, host, oq, with_qjl=with_qjl, seqs=seqs)
+    return out.cpu().numpy(), ref, (qz, cache, t, oq, host)
+
+
+@pytest.mark.parametrize("bits", [4, 2])
+@pytest.mark.parametrize("rot", [fq.ROT_HAAR, fq.ROT_WHT])
+def test_decode_tiny(gpu_lib, bits, rot):
+    w = synth.workload(0, bits=bits)
+    inp = synth.layer_inputs(w)
+    out, ref, _ = _decode_case(w, inp, rot=rot)
+    err = np.max(np.abs(out - ref))
+    print("max-abs", err, "cos vs exact", parity.cosine(out, parity.exact(inp)))
+    assert err <= parity.DECODE_TOL
+
+
+@pytest.mark.parametrize("G", [1, 4, 8, 16])
+def test_decode_groups_ragged(gpu_lib, G):
+    w, inp = parity.small_workload(3, 2 * G, 2, [5, 333, 1000], 1008, seed=G)
+    out, ref, _ = _decode_case(w, inp, num_splits=3)
+    assert np.max(np.abs(out - ref)) <= parity.DECODE_TOL
+
+
+def test_decode_mse_only_keys(gpu_lib):
+    w, inp = parity.small_workload(2, 8, 2, [700, 64], 704, seed=41)
+    out, ref, _ = _decode_case(w, inp, with_qjl=False)
+    assert np.max(np.abs(out - ref)) <= parity.DECODE_TOL
+
+
+def test_decode_empty_and_single_token(gpu_lib):
+    w, inp = parity.small_workload(3, 4, 2, [0, 1, 17], 32, seed=43)
+    out, ref, _ = _decode_case(w, inp, num_splits=2)
+    assert np.all(out[0] == 0)
+    assert np.max(np.abs(out - ref)) <= parity.DECODE_TOL
+
+
+def test_decode_split_invariance_and_determinism(gpu_lib):
+    w, inp = parity.small_workload(2, 16, 4, [1500, 999], 1504, seed=47)
+    base, ref, (qz, cache, t, oq, host) = _decode_case(w, inp, num_splits=1)
+    assert np.max(np.abs(base - ref)) <= parity.DECODE_TOL
+    for s in (2, 4, 7, 64, 0):
+        o = fq.decode(qz, cache, t["q"], t["bt"], t["lens"], 1500, num_splits=s).cpu().numpy()
+        assert np.max(np.abs(o - base)) <= 1e-5, s
+        o2 = fq.decode(qz, cache, t["q"], t["bt"], t["lens"], 1500, num_splits=s).cpu().numpy()
+        assert np.array_equal(o, o2), s
+
+
+def test_decode_block_permutation_is_bit_identical(gpu_lib):
+    w, inp = parity.small_workload(1, 8, 2, [400], 400, seed=53)
+    out, ref, (qz, cache, t, oq, host) = _decode_case(w, inp, num_splits=4)
+    nb = inp["num_blocks"]
+    perm = np.random.default_rng(1).permutation(nb)
+    moved = {n: np.empty_like(a) for n, a in host.items()}
+    for n, a in host.items():
+        moved[n][perm] = a
+    cache2 = fq.PagedCache(nb, 2, 128, 4, 128)
+    parity.upload_cache(moved, cache2)
+    bt2 = torch.from_numpy(perm[inp["block_tables"]].astype(np.int32)).cuda()
+    o2 = fq.decode(qz, cache2, t["q"], bt2, t["lens"], 400, num_splits=4).cpu().numpy()
+    assert np.array_equal(out, o2)
+
+
+def test_decode_full_size_b32_sampled(gpu_lib):
+    """The batch-32 8B-shaped layer (lengths 3072..4096, 4 splits) in the launch configuration
+    the benchmark times; the oracle writes and checks three of the 32 sequences."""
+    w = synth.workload(2)
+    inp = synth.layer_inputs(w)
+    seqs = [0, 13, 31]
+    t = parity.torch_inputs(inp, "bf16")
+    oq = parity.oracle_quantizer(4)
+    qz = fq.Quantizer(4, 128, fq.ROT_HAAR, 1, 2, 128)
+    cache = fq.PagedCache(inp["num_blocks"], 8, 128, 4, 128)
+    fq.compress(qz, cache, t["k"], t["v"], t["slots"])
+    host = parity.oracle_cache(inp, oq, seqs=seqs)
+    blocks = np.concatenate([inp["block_tables"][b] for b in seqs])
+    parity.upload_cache(host, cache, blocks=blocks)
+    out = fq.decode(qz, cache, t["q"], t["bt"], t["lens"], 4096, num_splits=4).cpu().numpy()
+    ref = parity.oracle_decode(inp, host, oq, seqs=seqs)
+    err = np.max(np.abs(out[seqs] - ref))
+    print("max-abs", err, "cos vs exact", parity.cosine(out[seqs], parity.exact(inp, seqs)))
+    assert err <= parity.DECODE_TOL
