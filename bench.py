@@ -1,0 +1,223 @@
+"""Benchmark of the compressed-KV hot path on one MI355X.
+
+Workload (default): Llama-3-8B-shaped attention, 32 layers, batch 32, context
+lengths uniform in [3072, 4096], 32 query / 8 KV heads, head_dim 128, TQ4 keys
+(4-bit Lloyd-Max + 1-bit QJL) and values (4-bit), 16-token pages with random
+non-contiguous block tables, 4 decode splits. Every layer has its own
+compressed cache (5.2 GB in all, far beyond the 256 MB last-level cache), filled
+by compressing the whole synthetic context before timing.
+
+One step = one decode step of the whole 32-layer stack: per layer, fq_compress of
+the newest token's K and V (written into its slot) and fq_decode_attention of
+the 32 sequences over their compressed pages. value = batch / step time
+(decode tokens/s). Inputs are resident in HBM before the timed region.
+
+Also reported: the prefill compress rate (Mvectors/s) measured while filling
+the caches, the roofline of the dominant kernel (the decode) and the CPU oracle
+timed on a bounded sample of the same work.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--layers 32] [--no-cpu]
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "compressed-KV decode tokens/s & HBM GB/s (8B-shape, 4K ctx); compress Mvec/s"
+HBM_PEAK_GBS = 8000.0
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--layers", type=int, default=32)
+    p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    p.add_argument("--cpu-seconds", type=float, default=12.0)
+    return p.parse_args()
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def cpu_baseline(w, layer_seed, budget_s):
+    """The oracle (unchanged) on a bounded sample: whole sequences of one layer, each
+    one compress of the new token + decode over the oracle's own compressed pages."""
+    import threadpoolctl
+
+    from kv_cache_vector_tq4_amd import synth
+    from oracle import attention, paged, pipeline
+
+    oq = pipeline.build(4, 128)
+    inp = synth.layer_inputs(synth.Workload("cpu-sample", 1, w.num_q_heads, w.num_kv_heads, 128,
+                                            [w.seq_lens[0]], w.capacity_tokens), data_seed=layer_seed)
+    L = int(inp["seq_lens"][0])
+    cache = paged.empty_cache(inp["num_blocks"], w.num_kv_heads, 128, 4, qjl_dim=128)
+    pipeline.compress(cache, inp["k"][0, :L], inp["v"][0, :L], inp["slot_mapping"][:L], oq)
+    info = threadpoolctl.threadpool_info()
+    cores = max([i.get("num_threads", 1) for i in info] + [1])
+    n = 0
+    t0 = time.perf_counter()
+    while True:
+        pipeline.compress(cache, inp["k"][0, L - 1:L], inp["v"][0, L - 1:L], inp["slot_mapping"][L - 1:L], oq)
+        attention.decode_rotated(inp["q"], cache, inp["block_tables"], inp["seq_lens"], oq["levels"],
+                                 oq["pi"], oq["s"], 4)
+        n += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    per_seq_layer = dt / n
+    return {
+        "value": 1.0 / (per_seq_layer * w.layers),
+        "unit": "tokens/s",
+        "cores": cores,
+        "kind": "oracle",
+        "sample": "%d x (compress 1 new token + decode 1 sequence of %d tokens, 32 q / 8 kv heads, one layer) "
+                  "in %.1f s; tokens/s = 1 / (seconds per sequence-layer x %d layers)" % (n, L, dt, w.layers),
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from kv_cache_vector_tq4_amd import fq, synth
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = "cuda"
+    w = synth.workload(2)
+    w.layers = args.layers
+    B, Hq, Hkv, d = w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim
+    lens = np.asarray(w.seq_lens, np.int32)
+    max_len = int(lens.max())
+    splits = w.num_splits
+
+    qz = fq.Quantizer(4, d, fq.ROT_HAAR, 1, 2, 128, device=dev)
+    bt_np, nblocks = synth.block_tables(1234, w.seq_lens, w.capacity_tokens)
+    bt = torch.from_numpy(bt_np).to(dev)
+    lens_t = torch.from_numpy(lens).to(dev)
+    slots_np = np.concatenate([synth.slot_mapping_for(bt_np[b], int(lens[b])) for b in range(B)])
+    slots_all = torch.from_numpy(slots_np).to(dev)
+    new_slots = torch.from_numpy(np.array([synth.slot_mapping_for(bt_np[b], int(lens[b]))[-1]
+                                           for b in range(B)], np.int64)).to(dev)
+    ntok = int(lens.sum())
+
+    stream = torch.cuda.current_stream()
+    caches, qs, knew, vnew = [], [], [], []
+    comp_ms = []
+    log("filling %d layer caches (%d tokens x %d heads each)..." % (w.layers, ntok, Hkv))
+    for layer in range(w.layers):
+        cache = fq.PagedCache(nblocks, Hkv, d, 4, 128, device=dev)
+        k, v = synth.kv_device(5000 + layer, ntok, Hkv, d, device=dev)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        fq.compress(qz, cache, k, v, slots_all)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        comp_ms.append(e0.elapsed_time(e1))
+        g = torch.Generator(device=dev)
+        g.manual_seed(9000 + layer)
+        qs.append(torch.randn((B, Hq, d), generator=g, device=dev).to(torch.bfloat16))
+        knew.append(k[-B:].contiguous())
+        vnew.append(v[-B:].contiguous())
+        caches.append(cache)
+        del k, v
+    torch.cuda.synchronize()
+    ws_bytes = fq.workspace_bytes(B, Hq, Hkv, d, 128, max_len, splits)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    outs = [torch.empty((B, Hq, d), dtype=torch.float32, device=dev) for _ in range(w.layers)]
+
+    ev = []  # (start, end) events around each decode call in the timed steps
+
+    def step(record):
+        for layer in range(w.layers):
+            fq.compress(qz, caches[layer], knew[layer], vnew[layer], new_slots)
+            if record:
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+            fq.decode(qz, caches[layer], qs[layer], bt, lens_t, max_len, num_splits=splits, workspace=ws,
+                      out=outs[layer])
+            if record:
+                e1.record(stream)
+                ev.append((e0, e1))
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    log("timing %d steps..." % args.steps)
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(True)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_per_step = elapsed * 1000.0 / args.steps
+    dec_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+
+    bpt = caches[0].bytes_per_token_head()  # 156 B at 4 bits with QJL keys
+    dec_bytes = ntok * Hkv * bpt
+    achieved = dec_bytes / (dec_ms * 1e-3) / 1e9
+    comp_vec = 2 * ntok * Hkv
+    comp_med_ms = float(np.median(comp_ms[1:] if len(comp_ms) > 1 else comp_ms))
+    comp_bytes = ntok * Hkv * (2 * d * 2) + ntok * 8 + ntok * Hkv * bpt
+    result = {
+        "metric": METRIC,
+        "value": B / (ms_per_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": "llama3-8b-shape attention stack: %d layers x (compress new token + decode), batch %d, "
+                        "ctx U[3072,4096] (sum %d), 32 q / 8 kv heads, d 128, TQ4 K(MSE+QJL)+V, 16-token pages, "
+                        "%d splits" % (w.layers, B, ntok, splits),
+            "layers": w.layers, "batch": B, "context_tokens": ntok, "num_splits": splits,
+            "cache_bytes_per_layer": dec_bytes, "bytes_per_token_head": bpt,
+        },
+        "roofline": {
+            "kernel": "fq_decode_attention (rotate_queries + split_attention + merge_unrotate)",
+            "bound": "hbm",
+            "achieved": achieved,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBS,
+            "traffic": None,
+            "algorithmic_bytes_per_launch": dec_bytes,
+            "avg_launch_ms": dec_ms,
+        },
+        "compress": {
+            "mvec_per_s": comp_vec / (comp_med_ms * 1e-3) / 1e6,
+            "vectors_per_launch": comp_vec,
+            "avg_launch_ms": comp_med_ms,
+            "achieved_gbs": comp_bytes / (comp_med_ms * 1e-3) / 1e9,
+            "frac_hbm": comp_bytes / (comp_med_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "algorithmic_bytes_per_launch": comp_bytes,
+        },
+    }
+    if not args.no_cpu:
+        log("timing the CPU oracle (~%.0f s)..." % args.cpu_seconds)
+        result["cpu_baseline"] = cpu_baseline(w, 77, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -143,3 +143,18 @@ def layer_inputs(w: Workload, layer: int = 0, data_seed: int = None):
         "num_blocks": nb,
         "slot_mapping": slots.reshape(-1),
     }
+
+
+def kv_device(seed: int, tokens: int, num_kv_heads: int, d: int, device="cuda", dtype="bf16"):
+    """Device-side K, V [tokens, Hkv, d] with the same recipe (torch generator on the device)."""
+    import torch
+
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    s = torch.exp(0.5 * torch.randn((num_kv_heads, d), generator=g, device=device))
+    out_idx = torch.argsort(torch.rand((num_kv_heads, d), generator=g, device=device), dim=1)[:, :4]
+    s.scatter_(1, out_idx, s.gather(1, out_idx) * 10.0)
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    k = (torch.randn((tokens, num_kv_heads, d), generator=g, device=device) * s[None]).to(tdt)
+    v = torch.randn((tokens, num_kv_heads, d), generator=g, device=device).to(tdt)
+    return k, v
