@@ -17,6 +17,8 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <cstdlib>
+#include <cstring>
 
 #include "fq_internal.h"
 
@@ -276,6 +278,313 @@ __global__ void __launch_bounds__(256) split_attention_kernel(DecodeArgs a) {
   }
 }
 
+// ---------------------------------------------------------------- kernel 2 (MFMA)
+// Split attention on the matrix cores, for 4-bit codes.
+//
+// One work-group of 4 waves per (split, KV head, sequence); the waves take the
+// split's 16-token pages round-robin, each with its own running max / sum /
+// rotated-frame accumulator, merged in LDS at the end.
+//
+// Per page and wave:
+//  scores  C[token][head] (16 x 16) = K^[16 x 128] q~[128 x 16] on
+//          v_mfma_f32_16x16x32_f16, A = dequantized codes, B = rotated queries
+//          (G heads, padded to 16 with zeros). Every fp32 operand is split into
+//          fp16 hi + lo and three products (hi*hi + lo*hi + hi*lo) are summed,
+//          which keeps ~22 significant bits; the QJL signs are exact +-1 in fp16
+//          and take two products (q_s hi, lo).
+//  values  C[head][dim] += P[head][16 tokens] V^[16 tokens x 16 dims] on
+//          v_mfma_f32_16x16x16_f16 for 8 dim tiles, again with hi/lo splits.
+// The score accumulator layout (lane = head, 4 tokens) is exactly the A layout
+// of the value product, so the probabilities never leave the registers.
+// Codes are dequantized through LDS tables indexed by a code byte (two 4-bit
+// codes -> fp16 hi pair and lo pair), replicated 16 times so that 16 lanes with
+// different bytes hit different banks. Levels are scaled by 2^8 and each query
+// head by a power of two before the split so that no lo part is subnormal.
+// Lane l: g = l / 16 (k-group / token quad), n = l % 16 (token / head / dim group).
+typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef float f4 __attribute__((ext_vector_type(4)));
+
+constexpr int LEV_SHIFT = 8;        // levels are stored x 2^8 in the tables
+constexpr int TAB_COPIES = 16;
+constexpr int SGN_COPIES = 8;
+
+__device__ __forceinline__ uint32_t h2bits(_Float16 a, _Float16 b) {
+  return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, a)) |
+         (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, b)) << 16);
+}
+
+__device__ __forceinline__ void split_f16(float x, _Float16& hi, _Float16& lo) {
+  hi = static_cast<_Float16>(x);
+  lo = static_cast<_Float16>(x - static_cast<float>(hi));
+}
+
+__device__ __forceinline__ h8 as_h8(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+  uint4 u = make_uint4(a, b, c, d);
+  return __builtin_bit_cast(h8, u);
+}
+
+__device__ __forceinline__ h4 as_h4(uint32_t a, uint32_t b) {
+  uint2 u = make_uint2(a, b);
+  return __builtin_bit_cast(h4, u);
+}
+
+__device__ __forceinline__ f4 mfma32(h8 a, h8 b, f4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f4 mfma16(h4 a, h4 b, f4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
+}
+
+struct PageData {
+  uint4 kc;       // 16 code bytes: dims 32g .. 32g+31 of token n
+  uint32_t sg;    // 32 QJL bits: projections 32g .. 32g+31 of token n
+  float4 kn, gm, vn;  // norms / gamma of tokens 4g .. 4g+3
+  uint32_t vc[4]; // code dword n (dims 8n .. 8n+7) of tokens 4g+e
+};
+
+__device__ __forceinline__ void load_page(const DecodeArgs& a, int64_t rec0, int g, int n, PageData& d) {
+  d.kc = *reinterpret_cast<const uint4*>(a.k_codes + (rec0 + n) * 64 + 16 * g);
+  d.kn = *reinterpret_cast<const float4*>(a.k_norm + rec0 + 4 * g);
+  if (a.qjl_on) {  // keys without QJL fields have no k_qjl / k_gamma arrays
+    d.sg = *reinterpret_cast<const uint32_t*>(a.k_qjl + (rec0 + n) * 16 + 4 * g);
+    d.gm = *reinterpret_cast<const float4*>(a.k_gamma + rec0 + 4 * g);
+  } else {
+    d.sg = 0;
+    d.gm = make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  d.vn = *reinterpret_cast<const float4*>(a.v_norm + rec0 + 4 * g);
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+    d.vc[e] = *reinterpret_cast<const uint32_t*>(a.v_codes + (rec0 + 4 * g + e) * 64 + 4 * n);
+}
+
+__global__ void __launch_bounds__(256, 2) split_mfma4_kernel(DecodeArgs a) {
+  __shared__ uint2 s_tab[256 * TAB_COPIES];     // 32 KB: byte -> (hi pair, lo pair)
+  __shared__ uint4 s_sgn[256 * SGN_COPIES];     // 32 KB: byte -> 8 x fp16 +-1
+  const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 4, n = lane & 15;
+  const int G = a.group;
+
+  // ---- tables
+  {
+    const int e = tid;  // one byte value per thread
+    const float c0 = a.levels[e & 15] * static_cast<float>(1 << LEV_SHIFT);
+    const float c1 = a.levels[e >> 4] * static_cast<float>(1 << LEV_SHIFT);
+    _Float16 h0, l0, h1, l1;
+    split_f16(c0, h0, l0);
+    split_f16(c1, h1, l1);
+    const uint2 ent = make_uint2(h2bits(h0, h1), h2bits(l0, l1));
+#pragma unroll
+    for (int c = 0; c < TAB_COPIES; ++c) s_tab[e * TAB_COPIES + c] = ent;
+    uint32_t w[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const uint32_t lo = ((e >> (2 * k)) & 1) ? 0x3C00u : 0xBC00u;
+      const uint32_t hi = ((e >> (2 * k + 1)) & 1) ? 0x3C00u : 0xBC00u;
+      w[k] = lo | (hi << 16);
+    }
+    const uint4 sgn = make_uint4(w[0], w[1], w[2], w[3]);
+#pragma unroll
+    for (int c = 0; c < SGN_COPIES; ++c) s_sgn[e * SGN_COPIES + c] = sgn;
+  }
+
+  // ---- query operands (B of the score products): head n, dims 32g + 8s + e
+  h8 qh[4], ql[4], sh[4], sl[4];
+  float qscale, sscale;
+  {
+    float qv[32], sv[32];
+    const bool live = n < G;
+    const int64_t row = (static_cast<int64_t>(b) * a.hq + kvh * G + (live ? n : 0)) * D + 32 * g;
+    float mq = 0.f, ms = 0.f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      qv[i] = live ? a.qrot[row + i] : 0.f;
+      sv[i] = (live && a.qjl_on) ? a.qs[row + i] : 0.f;
+      mq = fmaxf(mq, fabsf(qv[i]));
+      ms = fmaxf(ms, fabsf(sv[i]));
+    }
+    mq = fmaxf(mq, __shfl_xor(mq, 16));
+    mq = fmaxf(mq, __shfl_xor(mq, 32));
+    ms = fmaxf(ms, __shfl_xor(ms, 16));
+    ms = fmaxf(ms, __shfl_xor(ms, 32));
+    int ex;
+    frexpf(mq, &ex);
+    qscale = mq > 0.f ? ldexpf(1.f, 8 - ex) : 1.f;  // max |q~| * qscale in [128, 256)
+    frexpf(ms, &ex);
+    sscale = ms > 0.f ? ldexpf(1.f, 8 - ex) : 1.f;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      uint32_t hw[4], lw[4], shw[4], slw[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        _Float16 h0, l0, h1, l1;
+        split_f16(qv[8 * s + 2 * k] * qscale, h0, l0);
+        split_f16(qv[8 * s + 2 * k + 1] * qscale, h1, l1);
+        hw[k] = h2bits(h0, h1);
+        lw[k] = h2bits(l0, l1);
+        split_f16(sv[8 * s + 2 * k] * sscale, h0, l0);
+        split_f16(sv[8 * s + 2 * k + 1] * sscale, h1, l1);
+        shw[k] = h2bits(h0, h1);
+        slw[k] = h2bits(l0, l1);
+      }
+      qh[s] = as_h8(hw[0], hw[1], hw[2], hw[3]);
+      ql[s] = as_h8(lw[0], lw[1], lw[2], lw[3]);
+      sh[s] = as_h8(shw[0], shw[1], shw[2], shw[3]);
+      sl[s] = as_h8(slw[0], slw[1], slw[2], slw[3]);
+    }
+  }
+  // score = kn * accK * kmul + gamma * accQ * smul
+  const float kmul = a.scale / (qscale * static_cast<float>(1 << LEV_SHIFT));
+  const float smul = a.scale * QJL_C / sscale;
+  __syncthreads();
+
+  const int len = a.seq_lens[b];
+  const int t0 = split * a.chunk;
+  const int t1 = min(len, t0 + a.chunk);
+  const int npages = t1 > t0 ? (t1 - t0 + FQ_BLOCK - 1) / FQ_BLOCK : 0;
+  const int32_t* bt = a.block_tables + static_cast<int64_t>(b) * a.max_blocks + t0 / FQ_BLOCK;
+  const int tc = lane & (TAB_COPIES - 1);
+  const int sc8 = lane & (SGN_COPIES - 1);
+
+  float m_run = -INFINITY, l_run = 0.f;
+  f4 acc_o[8];
+#pragma unroll
+  for (int t = 0; t < 8; ++t) acc_o[t] = f4{0.f, 0.f, 0.f, 0.f};
+
+  PageData cur, nxt;
+  int p = wave;
+  if (p < npages) load_page(a, (static_cast<int64_t>(bt[p]) * a.hkv + kvh) * FQ_BLOCK, g, n, cur);
+  for (; p < npages; p += 4) {
+    if (p + 4 < npages) load_page(a, (static_cast<int64_t>(bt[p + 4]) * a.hkv + kvh) * FQ_BLOCK, g, n, nxt);
+
+    // ---- scores
+    f4 accK = {0.f, 0.f, 0.f, 0.f}, accQ = {0.f, 0.f, 0.f, 0.f};
+    const uint32_t kw[4] = {cur.kc.x, cur.kc.y, cur.kc.z, cur.kc.w};
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      uint2 e0 = s_tab[((kw[s] >> 0) & 0xFF) * TAB_COPIES + tc];
+      uint2 e1 = s_tab[((kw[s] >> 8) & 0xFF) * TAB_COPIES + tc];
+      uint2 e2 = s_tab[((kw[s] >> 16) & 0xFF) * TAB_COPIES + tc];
+      uint2 e3 = s_tab[((kw[s] >> 24) & 0xFF) * TAB_COPIES + tc];
+      const h8 ah = as_h8(e0.x, e1.x, e2.x, e3.x);
+      const h8 al = as_h8(e0.y, e1.y, e2.y, e3.y);
+      accK = mfma32(ah, qh[s], accK);
+      accK = mfma32(ah, ql[s], accK);
+      accK = mfma32(al, qh[s], accK);
+      // Unconditional: without QJL fields the q_s operands and signs are zero, so
+      // accQ stays 0. Keeping the score block free of branches keeps every MFMA
+      // result separated from its first vector-ALU read by straight-line code.
+      const uint4 sg = s_sgn[((cur.sg >> (8 * s)) & 0xFF) * SGN_COPIES + sc8];
+      const h8 as = __builtin_bit_cast(h8, sg);
+      accQ = mfma32(as, sh[s], accQ);
+      accQ = mfma32(as, sl[s], accQ);
+    }
+    const int tbase = t0 + p * FQ_BLOCK + 4 * g;
+    float sc[4];
+    const float knv[4] = {cur.kn.x, cur.kn.y, cur.kn.z, cur.kn.w};
+    const float gmv[4] = {cur.gm.x, cur.gm.y, cur.gm.z, cur.gm.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float v = fmaf(gmv[e] * accQ[e], smul, knv[e] * accK[e] * kmul);
+      sc[e] = (tbase + e < t1) ? v : -INFINITY;
+    }
+
+    // ---- online softmax (lane owns head n, tokens 4g..4g+3)
+    float mx = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_new = fmaxf(m_run, mx);
+    if (__any(m_new > m_run)) {
+      const float alpha = m_run == -INFINITY ? 0.f : __expf(m_run - m_new);
+      l_run *= alpha;
+      // o rows are heads 4g + e: fetch their alpha from lane 4g + e
+      float al[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) al[e] = __shfl(alpha, 4 * g + e);
+#pragma unroll
+      for (int t = 0; t < 8; ++t)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc_o[t][e] *= al[e];
+      m_run = m_new;
+    }
+    const float vnv[4] = {cur.vn.x, cur.vn.y, cur.vn.z, cur.vn.w};
+    uint32_t ph[2], pl[2];
+#pragma unroll
+    for (int e = 0; e < 4; e += 2) {
+      const float p0 = __expf(sc[e] - m_run), p1 = __expf(sc[e + 1] - m_run);
+      l_run += p0 + p1;
+      _Float16 h0, l0, h1, l1;
+      split_f16(p0 * vnv[e], h0, l0);
+      split_f16(p1 * vnv[e + 1], h1, l1);
+      ph[e / 2] = h2bits(h0, h1);
+      pl[e / 2] = h2bits(l0, l1);
+    }
+    const h4 Ph = as_h4(ph[0], ph[1]), Pl = as_h4(pl[0], pl[1]);
+
+    // ---- values: tokens (4g+0, 4g+1) and (4g+2, 4g+3) paired per code byte
+    const uint32_t x01 = (cur.vc[0] & 0x0F0F0F0Fu) | ((cur.vc[1] & 0x0F0F0F0Fu) << 4);
+    const uint32_t y01 = ((cur.vc[0] >> 4) & 0x0F0F0F0Fu) | (cur.vc[1] & 0xF0F0F0F0u);
+    const uint32_t x23 = (cur.vc[2] & 0x0F0F0F0Fu) | ((cur.vc[3] & 0x0F0F0F0Fu) << 4);
+    const uint32_t y23 = ((cur.vc[2] >> 4) & 0x0F0F0F0Fu) | (cur.vc[3] & 0xF0F0F0F0u);
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const uint32_t u01 = (t & 1) ? y01 : x01;
+      const uint32_t u23 = (t & 1) ? y23 : x23;
+      const int sh8 = 8 * (t >> 1);
+      const uint2 e01 = s_tab[((u01 >> sh8) & 0xFF) * TAB_COPIES + tc];
+      const uint2 e23 = s_tab[((u23 >> sh8) & 0xFF) * TAB_COPIES + tc];
+      const h4 bh = as_h4(e01.x, e23.x), bl = as_h4(e01.y, e23.y);
+      acc_o[t] = mfma16(Ph, bh, acc_o[t]);
+      acc_o[t] = mfma16(Pl, bh, acc_o[t]);
+      acc_o[t] = mfma16(Ph, bl, acc_o[t]);
+    }
+    if (p + 4 < npages) cur = nxt;
+  }
+
+  // ---- merge the 4 waves in LDS, then write this split's partials
+  l_run += __shfl_xor(l_run, 16);
+  l_run += __shfl_xor(l_run, 32);
+  __syncthreads();  // tables are dead from here on; reuse s_tab as scratch
+  float* s_o = reinterpret_cast<float*>(s_tab);             // [4 waves][16 heads][128]
+  float* s_ml = reinterpret_cast<float*>(s_sgn);            // [4 waves][16 heads][2]
+  if (g == 0) {
+    s_ml[(wave * 16 + n) * 2] = m_run;
+    s_ml[(wave * 16 + n) * 2 + 1] = l_run;
+  }
+  const float unscale = 1.0f / static_cast<float>(1 << LEV_SHIFT);
+#pragma unroll
+  for (int t = 0; t < 8; ++t)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) s_o[(wave * 16 + 4 * g + e) * D + 8 * n + t] = acc_o[t][e] * unscale;
+  __syncthreads();
+  for (int idx = tid; idx < G * D; idx += blockDim.x) {
+    const int h = idx / D, j = idx % D;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < 4; ++w)
+      if (s_ml[(w * 16 + h) * 2 + 1] > 0.f) M = fmaxf(M, s_ml[(w * 16 + h) * 2]);
+    float o = 0.f, L = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float lw = s_ml[(w * 16 + h) * 2 + 1];
+      if (lw > 0.f) {
+        const float f = __expf(s_ml[(w * 16 + h) * 2] - M);
+        o = fmaf(s_o[(w * 16 + h) * D + j], f, o);
+        L = fmaf(lw, f, L);
+      }
+    }
+    const int64_t base = (static_cast<int64_t>(b) * a.hq + kvh * G + h) * a.splits + split;
+    a.part_o[base * D + j] = o;
+    if (j == 0) {
+      a.part_ml[base * 2] = M;
+      a.part_ml[base * 2 + 1] = L;
+    }
+  }
+}
+
 // ---------------------------------------------------------------- kernel 3
 __global__ void __launch_bounds__(D) merge_unrotate_kernel(DecodeArgs a) {
   __shared__ float s_o[D];
@@ -356,7 +665,11 @@ int launch_decode(void* stream, const fq_quantizer& q, const fq_cache& c, const 
   else
     hipLaunchKernelGGL(rotate_queries_kernel<FQ_F32>, dim3((nvec + 15) / 16), dim3(256), 0, st, a);
   dim3 grid(num_splits, c.num_kv_heads, batch);
-  if (q.bits == 4)
+  const char* impl = std::getenv("FQ_DECODE_KERNEL");
+  const bool valu = impl && std::strcmp(impl, "valu") == 0;
+  if (q.bits == 4 && !valu)
+    hipLaunchKernelGGL(split_mfma4_kernel, grid, dim3(256), 0, st, a);
+  else if (q.bits == 4)
     hipLaunchKernelGGL(split_attention_kernel<4>, grid, dim3(256), 0, st, a);
   else
     hipLaunchKernelGGL(split_attention_kernel<2>, grid, dim3(256), 0, st, a);

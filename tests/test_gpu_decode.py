@@ -101,3 +101,16 @@ def test_decode_full_size_b32_sampled(gpu_lib):
     err = np.max(np.abs(out[seqs] - ref))
     print("max-abs", err, "cos vs exact", parity.cosine(out[seqs], parity.exact(inp, seqs)))
     assert err <= parity.DECODE_TOL
+
+
+def test_decode_vector_alu_kernel_matches_matrix_core_kernel(gpu_lib, monkeypatch):
+    """The 4-bit decode has a matrix-core split kernel (default) and a vector-ALU one
+    (FQ_DECODE_KERNEL=valu); both must match the oracle."""
+    w, inp = parity.small_workload(2, 32, 8, [2000, 777], 2000, seed=59)
+    out_m, ref, (qz, cache, t, oq, host) = _decode_case(w, inp, num_splits=3)
+    monkeypatch.setenv("FQ_DECODE_KERNEL", "valu")
+    out_v = fq.decode(qz, cache, t["q"], t["bt"], t["lens"], 2000, num_splits=3).cpu().numpy()
+    monkeypatch.delenv("FQ_DECODE_KERNEL")
+    assert np.max(np.abs(out_m - ref)) <= parity.DECODE_TOL
+    assert np.max(np.abs(out_v - ref)) <= parity.DECODE_TOL
+    assert np.max(np.abs(out_m - out_v)) <= 1e-4
