@@ -42,6 +42,7 @@ def parse():
     p.add_argument("--layers", type=int, default=32)
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
+    p.add_argument("--no-graph", action="store_true", help="time eager launches instead of a HIP graph")
     return p.parse_args()
 
 
@@ -158,13 +159,48 @@ def main():
     for _ in range(args.warmup):
         step(False)
     torch.cuda.synchronize()
-    log("timing %d steps..." % args.steps)
+
+    graph = None
+    graph_check = None
+    if not args.no_graph:
+        # The step is launch-bound (5 launches per layer): capture it once, replay it.
+        ref = [o.clone() for o in outs]
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(side):
+            with torch.cuda.graph(graph, stream=side):
+                step(False)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        for _ in range(3):  # replays with eager work and syncs between them match eager output
+            for o in outs:
+                o.zero_()
+            graph.replay()
+            torch.cuda.synchronize()
+            graph_check = max(float((o - r).abs().max()) for o, r in zip(outs, ref))
+            assert graph_check == 0.0, "graph replay differs from eager: %g" % graph_check
+
+    log("timing %d steps (%s)..." % (args.steps, "graph replay" if graph else "eager"))
+    torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        step(True)
+        if graph is not None:
+            graph.replay()
+        else:
+            step(False)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     ms_per_step = elapsed * 1000.0 / args.steps
+
+    # per-launch durations of the dominant kernel: HIP events around each decode call,
+    # on the stream the library launches on, over K eager steps
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    for _ in range(args.steps):
+        step(True)
+    torch.cuda.synchronize()
+    ms_eager = (time.perf_counter() - t1) * 1000.0 / args.steps
     dec_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
 
     bpt = caches[0].bytes_per_token_head()  # 156 B at 4 bits with QJL keys
@@ -181,6 +217,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": ms_per_step,
+        "timing": {"mode": "hip graph replay" if graph is not None else "eager", "ms_per_step_eager": ms_eager,
+                   "graph_vs_eager_max_abs": graph_check},
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,

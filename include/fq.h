@@ -99,7 +99,29 @@ typedef struct fq_quantizer {
   const float* rotation_t;      /* [d][d] row-major Pi^T; required for both kinds */
   const float* wht_signs;       /* [d]; required for FQ_ROT_WHT */
   const float* qjl_matrix;      /* [qjl_dim][d] row-major; required when qjl_dim > 0 */
+  const void* mfma_operands;    /* optional: FQ_MFMA_OPERAND_BYTES from fq_pack_mfma_operands,
+                                   16-byte aligned; NULL = the kernels derive them */
 } fq_quantizer;
+
+/* Size in bytes of the prepared matrix-core operands of one quantizer. */
+#define FQ_MFMA_OPERAND_BYTES 131072
+
+/*
+ * fq_pack_mfma_operands -- host, synchronous. Lays out Pi (as bf16 hi + lo) and S
+ * (as fp16 hi + lo; zeros when qjl_matrix is NULL) in the fragment order the
+ * compress kernels feed to the matrix cores, so that no kernel launch has to
+ * derive them. Pure re-encoding of the two fp32 matrices (round to nearest even;
+ * lo = round(x - hi)); the result is the same the kernels compute for themselves.
+ *  rotation_matrix  host fp32 [d][d] row-major Pi
+ *  qjl_matrix       host fp32 [d][d] row-major S, or NULL
+ *  head_dim         128
+ *  out              host buffer of FQ_MFMA_OPERAND_BYTES bytes (caller copies it to
+ *                   the device and sets fq_quantizer.mfma_operands)
+ * Errors: FQ_ERR_INVALID_ARG (NULL rotation / out, out_bytes too small),
+ * FQ_ERR_UNSUPPORTED (head_dim != 128).
+ */
+fq_status fq_pack_mfma_operands(const float* rotation_matrix, const float* qjl_matrix, int head_dim,
+                                void* out, size_t out_bytes);
 
 /*
  * The paged compressed cache of one layer (device pointers, 16-byte aligned).

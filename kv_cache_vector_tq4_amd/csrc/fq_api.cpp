@@ -22,6 +22,7 @@ fq_status check_quantizer(const fq_quantizer* q) {
       !aligned(q->rotation_t, 16))
     return FQ_ERR_INVALID_ARG;
   if (q->qjl_dim > 0 && !aligned(q->qjl_matrix, 16)) return FQ_ERR_INVALID_ARG;
+  if (q->mfma_operands && !aligned(q->mfma_operands, 16)) return FQ_ERR_INVALID_ARG;
   return FQ_OK;
 }
 

@@ -174,3 +174,71 @@ extern "C" fq_status fq_build_codebook(int bits, int head_dim, int rotation, uin
   }
   return FQ_OK;
 }
+
+namespace {
+
+// Round-to-nearest-even bf16 of a finite fp32 value, as bits.
+inline uint32_t bf16_bits_rne(float x) {
+  uint32_t u;
+  std::memcpy(&u, &x, 4);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+inline float bf16_to_float(uint32_t b) {
+  const uint32_t u = b << 16;
+  float f;
+  std::memcpy(&f, &u, 4);
+  return f;
+}
+
+inline uint32_t f16_bits(float x) {
+  const _Float16 h = static_cast<_Float16>(x);
+  uint16_t b;
+  std::memcpy(&b, &h, 2);
+  return b;
+}
+
+// Accumulator row r of row tile T of the 32x32 matrix-core products holds this
+// rotated coordinate (lane half h = (r / 4) % 2 owns coordinates 64h .. 64h+63).
+inline int perm_row(int T, int r) { return 64 * ((r >> 2) & 1) + 16 * T + 4 * (r >> 3) + (r & 3); }
+
+}  // namespace
+
+extern "C" fq_status fq_pack_mfma_operands(const float* rotation_matrix, const float* qjl_matrix,
+                                           int head_dim, void* out, size_t out_bytes) {
+  if (!rotation_matrix || !out || out_bytes < FQ_MFMA_OPERAND_BYTES) return FQ_ERR_INVALID_ARG;
+  if (head_dim != FQ_HEAD_DIM) return FQ_ERR_UNSUPPORTED;
+  const int d = head_dim;
+  uint32_t* o = static_cast<uint32_t*>(out);  // 4 matrices x 32 fragments x 64 lanes x 4 dwords
+  const int per_matrix = 32 * 64 * 4;
+  for (int f = 0; f < 32; ++f) {
+    const int T = f >> 3, s = f & 7;
+    for (int l = 0; l < 64; ++l) {
+      const int row = perm_row(T, l & 31);
+      const int col = 64 * (l >> 5) + 8 * s;
+      for (int q = 0; q < 4; ++q) {
+        uint32_t ph = 0, pl = 0, sh = 0, sl = 0;
+        for (int half = 0; half < 2; ++half) {
+          const int e = 2 * q + half;
+          const float x = rotation_matrix[row * d + col + e];
+          const uint32_t hb = bf16_bits_rne(x);
+          const uint32_t lb = bf16_bits_rne(x - bf16_to_float(hb));
+          ph |= hb << (16 * half);
+          pl |= lb << (16 * half);
+          if (qjl_matrix) {
+            const float y = qjl_matrix[row * d + col + e];
+            const _Float16 yh = static_cast<_Float16>(y);
+            sh |= f16_bits(y) << (16 * half);
+            sl |= f16_bits(y - static_cast<float>(yh)) << (16 * half);
+          }
+        }
+        const int idx = (f * 64 + l) * 4 + q;
+        o[0 * per_matrix + idx] = ph;
+        o[1 * per_matrix + idx] = pl;
+        o[2 * per_matrix + idx] = sh;
+        o[3 * per_matrix + idx] = sl;
+      }
+    }
+  }
+  return FQ_OK;
+}

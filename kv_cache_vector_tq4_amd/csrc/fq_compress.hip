@@ -15,6 +15,8 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <cstdlib>
+#include <cstring>
 
 #include "fq_internal.h"
 
@@ -37,6 +39,8 @@ struct CompressArgs {
   const float* levels;
   const float* bnd;
   const float* pit;     // Pi^T, row-major: row k = column k of Pi
+  const float* pi_rows; // Pi, row-major
+  const void* mfma_ops; // prepared fragments (optional)
   const float* signs;   // WHT signs
   const float* smat;    // S, row-major [m][d]
   const int64_t* slots;
@@ -201,6 +205,359 @@ __global__ void __launch_bounds__(64) compress_lane_kernel(CompressArgs a) {
                  static_cast<uint32_t>(hi), static_cast<uint32_t>(hi >> 32));
 }
 
+// ------------------------------------------------------------------ MFMA tiles
+// Matrix-core compress: 32 vectors per wave, v_mfma_f32_32x32x16_{bf16,f16}.
+//
+// Rotation: Y^T (128 x 32) = Pi (128 x 128) X^T (128 x 32), A = Pi fragments from
+// LDS (bf16 hi + lo: 16 significant bits, y error ~1e-6), B = the vectors
+// themselves (bf16 inputs are exact; fp32 inputs are split into hi + lo).
+// The rows of Pi are fed in a permuted order so that accumulator register vv of
+// row tile T in lane (h, v) is coordinate 64h + 16T + vv of vector v: every lane
+// holds 64 consecutive coordinates of one vector, which makes the norm, the
+// boundary search, the nibble packing and the QJL sign packing lane-local, and
+// makes the lane's residuals directly the B operand of the QJL product
+// p^T = S r^T (S in fp16 hi + lo, r in fp16 hi + lo, three products).
+// Boundary search: a 256-cell table over the boundary range; each cell holds
+// the number of boundaries certainly below it and the single boundary that may
+// lie within half a cell of it, so idx = count + [b < y] with one exact fp32
+// compare.
+typedef __bf16 b8 __attribute__((ext_vector_type(8)));
+typedef _Float16 hh8 __attribute__((ext_vector_type(8)));
+typedef float f16v __attribute__((ext_vector_type(16)));
+
+constexpr int CT_WAVES = 8;          // waves per work-group
+constexpr int CT_VEC = 32;           // vectors per wave tile
+constexpr int QT_CELLS = 256;
+
+struct QCell {
+  uint32_t count;
+  float b;
+  float c_lo;
+  float c_hi;
+};
+
+__device__ __forceinline__ int perm_row(int T, int r) {
+  // accumulator row r of row tile T -> rotated coordinate
+  return 64 * ((r >> 2) & 1) + 16 * T + 4 * (r >> 3) + (r & 3);
+}
+
+__device__ __forceinline__ uint32_t bf16_rne(float x) {
+  const uint32_t u = __float_as_uint(x);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+__device__ __forceinline__ void split_bf16(float x, uint32_t& hi, uint32_t& lo) {
+  hi = bf16_rne(x);
+  lo = bf16_rne(x - __uint_as_float(hi << 16));
+}
+
+__device__ __forceinline__ void split_f16b(float x, uint32_t& hi, uint32_t& lo) {
+  const _Float16 h = static_cast<_Float16>(x);
+  const _Float16 l = static_cast<_Float16>(x - static_cast<float>(h));
+  hi = __builtin_bit_cast(uint16_t, h);
+  lo = __builtin_bit_cast(uint16_t, l);
+}
+
+// Fragment layout (shared by the LDS copy, the global operand buffer and the
+// host packer): matrix M in {Pi hi, Pi lo, S hi, S lo} is 32 fragments f = T * 8 + s
+// of 64 lanes x 16 bytes; lane (r = l % 32, hk = l / 32) of fragment (T, s) holds
+// M[perm_row(T, r)][64 hk + 8 s + e], e = 0..7 (bf16 for Pi, fp16 for S).
+constexpr int FRAG_U4 = 32 * 64;  // uint4 per matrix (32 KB)
+
+// One wave compresses one tile of 32 vectors of one kind. fpi -> Pi hi / lo
+// fragments (2 * FRAG_U4 uint4), fsm -> S hi / lo fragments (keys only).
+template <int BITS, int DT, bool KEY>
+__device__ __forceinline__ void compress_tile(const CompressArgs& a, int kind, int64_t tile, int lane,
+                                              const uint4* __restrict__ fpi, const uint4* __restrict__ fsm,
+                                              const QCell* __restrict__ qt, float inv_w, float off) {
+  const int v = lane & 31, h = lane >> 5;
+  const int64_t nvec = a.ntok * a.hkv;
+  const int esz = DT == FQ_BF16 ? 2 : 4;
+  const uint8_t* src = static_cast<const uint8_t*>(a.src[kind]);
+  const int64_t vid = tile * CT_VEC + v;
+  const bool valid = vid < nvec;
+  const int64_t t = valid ? vid / a.hkv : 0;
+  const int hd = valid ? static_cast<int>(vid - t * a.hkv) : 0;
+  const int64_t slot = valid ? a.slots[t] : -1;
+  const uint8_t* base = src + ((t * a.tstride + hd * a.hstride) * esz) + 64 * h * esz;
+
+  // ---- load 64 coordinates (64h .. 64h+63) of vector v; B fragments per k-step
+  b8 xb[8];
+  b8 xl[DT == FQ_BF16 ? 1 : 8];
+  float ss = 0.f;
+  if constexpr (DT == FQ_BF16) {
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      uint4 u = valid ? reinterpret_cast<const uint4*>(base)[s] : make_uint4(0, 0, 0, 0);
+      const uint32_t w4[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float lo = __uint_as_float(w4[q] << 16), hi = __uint_as_float(w4[q] & 0xffff0000u);
+        ss = fmaf(lo, lo, ss);
+        ss = fmaf(hi, hi, ss);
+      }
+      xb[s] = __builtin_bit_cast(b8, u);
+    }
+  } else {
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      float4 f0 = valid ? reinterpret_cast<const float4*>(base)[2 * s] : make_float4(0, 0, 0, 0);
+      float4 f1 = valid ? reinterpret_cast<const float4*>(base)[2 * s + 1] : make_float4(0, 0, 0, 0);
+      const float xs[8] = {f0.x, f0.y, f0.z, f0.w, f1.x, f1.y, f1.z, f1.w};
+      uint32_t hi[8], lo[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        ss = fmaf(xs[e], xs[e], ss);
+        split_bf16(xs[e], hi[e], lo[e]);
+      }
+      xb[s] = __builtin_bit_cast(b8, make_uint4(hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16), hi[4] | (hi[5] << 16), hi[6] | (hi[7] << 16)));
+      xl[s] = __builtin_bit_cast(b8, make_uint4(lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16), lo[4] | (lo[5] << 16), lo[6] | (lo[7] << 16)));
+    }
+  }
+  ss += __shfl_xor(ss, 32);
+  const float n = sqrtf(ss);
+  const float inv = n > 0.f ? 1.0f / n : 0.f;
+
+  // ---- rotation on the matrix cores
+  f16v acc[4];
+#pragma unroll
+  for (int T = 0; T < 4; ++T) acc[T] = f16v{};
+#pragma unroll
+  for (int s = 0; s < 8; ++s) {
+    __builtin_amdgcn_sched_barrier(0);  // keep fragment loads next to their products
+#pragma unroll
+    for (int T = 0; T < 4; ++T) {
+      const b8 ah = __builtin_bit_cast(b8, fpi[(T * 8 + s) * 64 + lane]);
+      const b8 al = __builtin_bit_cast(b8, fpi[(32 + T * 8 + s) * 64 + lane]);
+      acc[T] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, xb[s], acc[T], 0, 0, 0);
+      acc[T] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, xb[s], acc[T], 0, 0, 0);
+      if constexpr (DT != FQ_BF16) acc[T] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, xl[s], acc[T], 0, 0, 0);
+    }
+  }
+  // acc[T][vv] = (Pi x)[64h + 16T + vv]
+#pragma unroll
+  for (int T = 0; T < 4; ++T)
+#pragma unroll
+    for (int vv = 0; vv < 16; ++vv) acc[T][vv] *= inv;
+
+  const int64_t rec = ((slot >> 4) * a.hkv + hd) * FQ_BLOCK + (slot & 15);
+  const bool store = slot >= 0;
+  if (a.dbg_y && store) {
+    float4* dy = reinterpret_cast<float4*>(a.dbg_y + ((kind * a.ntok + t) * a.hkv + hd) * D + 64 * h);
+#pragma unroll
+    for (int T = 0; T < 4; ++T)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        dy[4 * T + q] = make_float4(acc[T][4 * q], acc[T][4 * q + 1], acc[T][4 * q + 2], acc[T][4 * q + 3]);
+  }
+
+  // ---- boundary search and packing; keys keep r = y - level[idx] in acc
+  constexpr int PER = 32 / BITS;
+  uint32_t words[64 / PER];
+#pragma unroll
+  for (int w = 0; w < 64 / PER; ++w) words[w] = 0;
+#pragma unroll
+  for (int T = 0; T < 4; ++T) {
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int vv = 0; vv < 16; ++vv) {
+      const int rel = 16 * T + vv;
+      const float y = acc[T][vv];
+      int c = static_cast<int>(floorf(fmaf(y, inv_w, off)));
+      c = min(max(c, 0), QT_CELLS - 1);
+      const QCell q = qt[c];
+      const bool gt = q.b < y;
+      const uint32_t idx = q.count + (gt ? 1u : 0u);
+      words[rel / PER] |= idx << (BITS * (rel % PER));
+      if constexpr (KEY) acc[T][vv] = y - (gt ? q.c_hi : q.c_lo);
+    }
+  }
+  if (store) {
+    uint4* cd = reinterpret_cast<uint4*>(a.codes[kind] + rec * (D * BITS / 8) + 64 * h * BITS / 8);
+#pragma unroll
+    for (int w = 0; w < 64 / PER; w += 4) cd[w / 4] = make_uint4(words[w], words[w + 1], words[w + 2], words[w + 3]);
+    if (h == 0) a.norm[kind][rec] = n;
+  }
+
+  if constexpr (KEY) {
+    if (!a.qjl_on) return;
+    float rr = 0.f;
+#pragma unroll
+    for (int T = 0; T < 4; ++T)
+#pragma unroll
+      for (int vv = 0; vv < 16; ++vv) rr = fmaf(acc[T][vv], acc[T][vv], rr);
+    rr += __shfl_xor(rr, 32);
+    // B fragments of r, converted per k-step: step s covers coordinates
+    // 64h + 8s + e = acc[s/2][8(s%2) + e]
+    f16v pacc[4];
+#pragma unroll
+    for (int T = 0; T < 4; ++T) pacc[T] = f16v{};
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      __builtin_amdgcn_sched_barrier(0);
+      uint32_t hi[8], lo[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) split_f16b(acc[s >> 1][8 * (s & 1) + e], hi[e], lo[e]);
+      const hh8 rh = __builtin_bit_cast(hh8, make_uint4(hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16), hi[4] | (hi[5] << 16), hi[6] | (hi[7] << 16)));
+      const hh8 rl = __builtin_bit_cast(hh8, make_uint4(lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16), lo[4] | (lo[5] << 16), lo[6] | (lo[7] << 16)));
+#pragma unroll
+      for (int T = 0; T < 4; ++T) {
+        const hh8 ah = __builtin_bit_cast(hh8, fsm[(T * 8 + s) * 64 + lane]);
+        const hh8 al = __builtin_bit_cast(hh8, fsm[(32 + T * 8 + s) * 64 + lane]);
+        pacc[T] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah, rh, pacc[T], 0, 0, 0);
+        pacc[T] = __builtin_amdgcn_mfma_f32_32x32x16_f16(al, rh, pacc[T], 0, 0, 0);
+        pacc[T] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah, rl, pacc[T], 0, 0, 0);
+      }
+    }
+    // pacc[T][vv] = p[64h + 16T + vv]
+    uint32_t sg[2] = {0u, 0u};
+#pragma unroll
+    for (int T = 0; T < 4; ++T)
+#pragma unroll
+      for (int vv = 0; vv < 16; ++vv) {
+        const int rel = 16 * T + vv;
+        sg[rel >> 5] |= (pacc[T][vv] >= 0.f ? 1u : 0u) << (rel & 31);
+      }
+    if (store) {
+      *reinterpret_cast<uint2*>(a.qjl + rec * (D / 8) + 8 * h) = make_uint2(sg[0], sg[1]);
+      if (h == 0) a.gamma[rec] = n * sqrtf(rr);
+      if (a.dbg_p) {
+        float4* dp = reinterpret_cast<float4*>(a.dbg_p + (t * a.hkv + hd) * D + 64 * h);
+#pragma unroll
+        for (int T = 0; T < 4; ++T)
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            dp[4 * T + q] = make_float4(pacc[T][4 * q], pacc[T][4 * q + 1], pacc[T][4 * q + 2], pacc[T][4 * q + 3]);
+      }
+    }
+  }
+}
+
+// Quantization cells and codebook staging; callers synchronize afterwards.
+template <int BITS>
+__device__ __forceinline__ void build_qtable(const CompressArgs& a, QCell* s_qt, float* s_qmap, float* s_bl,
+                                             int tid, int nthreads) {
+  constexpr int L = 1 << BITS;
+  if (tid < L - 1) s_bl[tid] = a.bnd[tid];
+  if (tid >= 32 && tid < 32 + L) s_bl[16 + tid - 32] = a.levels[tid - 32];
+  __syncthreads();
+  const float b0 = s_bl[0], bm = s_bl[L - 2];
+  const float w = (bm - b0) / static_cast<float>(QT_CELLS - 8);
+  const float inv_w = 1.0f / w;
+  const float off = -(b0 - 4.0f * w) * inv_w;  // position of y: y * inv_w + off
+  if (tid == 0) {
+    s_qmap[0] = inv_w;
+    s_qmap[1] = off;
+  }
+  for (int cell = tid; cell < QT_CELLS; cell += nthreads) {
+    const float c = static_cast<float>(cell);
+    uint32_t cnt = 0;
+    float bb = INFINITY;
+#pragma unroll
+    for (int i = 0; i < L - 1; ++i) {
+      const float pos = fmaf(s_bl[i], inv_w, off);
+      if (pos < c - 0.5f) ++cnt;
+      else if (pos < c + 1.5f) bb = s_bl[i];
+    }
+    s_qt[cell] = QCell{cnt, bb, s_bl[16 + cnt], s_bl[16 + (cnt + 1 < L ? cnt + 1 : cnt)]};
+  }
+}
+
+__device__ __forceinline__ uint4 pack8(const uint32_t (&u)[8]) {
+  return make_uint4(u[0] | (u[1] << 16), u[2] | (u[3] << 16), u[4] | (u[5] << 16), u[6] | (u[7] << 16));
+}
+
+// Large inputs: work-groups of 8 waves loop over tiles with the fragments in LDS
+// (copied from the prepared operand buffer, or built from the fp32 matrices).
+template <int BITS, int DT, bool KEY>
+__global__ void __launch_bounds__(CT_WAVES * 64) compress_mfma_kernel(CompressArgs a, int kind) {
+  __shared__ uint4 s_pi[2 * FRAG_U4];                       // Pi fragments, bf16 hi / lo (64 KB)
+  __shared__ uint4 s_sm[KEY ? 2 * FRAG_U4 : 1];             // S fragments, fp16 hi / lo (64 KB, keys)
+  __shared__ QCell s_qt[QT_CELLS];
+  __shared__ float s_qmap[2];
+  __shared__ float s_bl[32];                                // boundaries [0, 15), levels at [16, 32)
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if (a.mfma_ops) {
+    const uint4* ops = static_cast<const uint4*>(a.mfma_ops);
+    for (int i = tid; i < 2 * FRAG_U4; i += blockDim.x) s_pi[i] = ops[i];
+    if constexpr (KEY)
+      for (int i = tid; i < 2 * FRAG_U4; i += blockDim.x) s_sm[i] = ops[2 * FRAG_U4 + i];
+  } else {
+    for (int idx = tid; idx < FRAG_U4; idx += blockDim.x) {
+      const int f = idx >> 6, l = idx & 63;
+      const int T = f >> 3, s = f & 7, r = l & 31, hk = l >> 5;
+      const int row = perm_row(T, r);
+      const int col = 64 * hk + 8 * s;
+      const float4* src = reinterpret_cast<const float4*>(a.pi_rows + row * D + col);
+      const float4 x0 = src[0], x1 = src[1];
+      const float xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+      uint32_t hi[8], lo[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) split_bf16(xs[e], hi[e], lo[e]);
+      s_pi[idx] = pack8(hi);
+      s_pi[FRAG_U4 + idx] = pack8(lo);
+      if constexpr (KEY) {
+        const float4* ss = reinterpret_cast<const float4*>(a.smat + row * D + col);
+        const float4 y0 = ss[0], y1 = ss[1];
+        const float ys[8] = {y0.x, y0.y, y0.z, y0.w, y1.x, y1.y, y1.z, y1.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) split_f16b(ys[e], hi[e], lo[e]);
+        s_sm[idx] = pack8(hi);
+        s_sm[FRAG_U4 + idx] = pack8(lo);
+      }
+    }
+  }
+  build_qtable<BITS>(a, s_qt, s_qmap, s_bl, tid, blockDim.x);
+  __syncthreads();
+  const float inv_w = s_qmap[0], off = s_qmap[1];
+  const int64_t nvec = a.ntok * a.hkv;
+  const int64_t ntiles = (nvec + CT_VEC - 1) / CT_VEC;
+  for (int64_t tile = static_cast<int64_t>(blockIdx.x) * CT_WAVES + wave; tile < ntiles;
+       tile += static_cast<int64_t>(gridDim.x) * CT_WAVES)
+    compress_tile<BITS, DT, KEY>(a, kind, tile, lane, s_pi, s_sm, s_qt, inv_w, off);
+}
+
+// Small inputs (e.g. the new token of every sequence in a decode step): one wave
+// per tile and per kind, fragments read straight from the prepared operand
+// buffer, so no work-group pays for filling 128 KB of LDS.
+template <int BITS, int DT>
+__global__ void __launch_bounds__(64) compress_direct_kernel(CompressArgs a) {
+  __shared__ QCell s_qt[QT_CELLS];
+  __shared__ float s_qmap[2];
+  __shared__ float s_bl[32];
+  const int tid = threadIdx.x;
+  build_qtable<BITS>(a, s_qt, s_qmap, s_bl, tid, 64);
+  __syncthreads();
+  const int kind = blockIdx.y;
+  if (!a.src[kind]) return;
+  const uint4* ops = static_cast<const uint4*>(a.mfma_ops);
+  if (kind == 0)
+    compress_tile<BITS, DT, true>(a, 0, blockIdx.x, tid, ops, ops + 2 * FRAG_U4, s_qt, s_qmap[0], s_qmap[1]);
+  else
+    compress_tile<BITS, DT, false>(a, 1, blockIdx.x, tid, ops, ops, s_qt, s_qmap[0], s_qmap[1]);
+}
+
+template <int BITS, int DT>
+int launch_mfma(hipStream_t st, const CompressArgs& a) {
+  const int64_t nvec = a.ntok * a.hkv;
+  const int64_t tiles = (nvec + CT_VEC - 1) / CT_VEC;
+  if (a.mfma_ops && tiles <= 1024) {
+    hipLaunchKernelGGL((compress_direct_kernel<BITS, DT>), dim3(static_cast<unsigned>(tiles), 2), dim3(64), 0, st, a);
+    return static_cast<int>(hipGetLastError());
+  }
+  const int64_t want = (tiles + CT_WAVES - 1) / CT_WAVES;
+  if (a.src[0]) {
+    const unsigned g = static_cast<unsigned>(want < 256 ? want : 256);
+    hipLaunchKernelGGL((compress_mfma_kernel<BITS, DT, true>), dim3(g), dim3(CT_WAVES * 64), 0, st, a, 0);
+  }
+  if (a.src[1]) {
+    const unsigned g = static_cast<unsigned>(want < 512 ? want : 512);
+    hipLaunchKernelGGL((compress_mfma_kernel<BITS, DT, false>), dim3(g), dim3(CT_WAVES * 64), 0, st, a, 1);
+  }
+  return static_cast<int>(hipGetLastError());
+}
+
 template <int BITS, int DT, bool WHT>
 int launch_lane(hipStream_t st, const CompressArgs& a) {
   const int64_t nvec = a.ntok * a.hkv;
@@ -227,6 +584,8 @@ int launch_compress(void* stream, const fq_quantizer& q, const fq_cache& c, cons
   a.levels = q.levels;
   a.bnd = q.boundaries;
   a.pit = q.rotation_t;
+  a.pi_rows = q.rotation_matrix;
+  a.mfma_ops = q.mfma_operands;
   a.signs = q.wht_signs;
   a.smat = q.qjl_matrix;
   a.slots = slot_mapping;
@@ -240,6 +599,12 @@ int launch_compress(void* stream, const fq_quantizer& q, const fq_cache& c, cons
   hipStream_t st = static_cast<hipStream_t>(stream);
   const bool wht = q.rotation == FQ_ROT_WHT;
   const bool bf = dtype == FQ_BF16;
+  const char* impl = std::getenv("FQ_COMPRESS_KERNEL");
+  const bool lane_impl = impl && std::strcmp(impl, "lane") == 0;
+  if (!lane_impl) {
+    if (q.bits == 4) return bf ? launch_mfma<4, FQ_BF16>(st, a) : launch_mfma<4, FQ_F32>(st, a);
+    return bf ? launch_mfma<2, FQ_BF16>(st, a) : launch_mfma<2, FQ_F32>(st, a);
+  }
   if (q.bits == 4) {
     if (bf) return wht ? launch_lane<4, FQ_BF16, true>(st, a) : launch_lane<4, FQ_BF16, false>(st, a);
     return wht ? launch_lane<4, FQ_F32, true>(st, a) : launch_lane<4, FQ_F32, false>(st, a);

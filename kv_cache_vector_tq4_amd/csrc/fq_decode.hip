@@ -84,6 +84,7 @@ __global__ void __launch_bounds__(256) rotate_queries_kernel(DecodeArgs a) {
   float acc[NV / 2];
 #pragma unroll
   for (int i = 0; i < NV / 2; ++i) acc[i] = 0.f;
+#pragma unroll 16
   for (int k = 0; k < D; ++k) {
     const float w = a.pit[k * D + j];
 #pragma unroll
@@ -102,6 +103,7 @@ __global__ void __launch_bounds__(256) rotate_queries_kernel(DecodeArgs a) {
   // q_s[i] = sum_j S[i][j] q~[j]; thread j plays the role of row i = j.
 #pragma unroll
   for (int i = 0; i < NV / 2; ++i) acc[i] = 0.f;
+#pragma unroll 8
   for (int k = 0; k < D; k += 4) {
     const float4 w = reinterpret_cast<const float4*>(a.smat + j * D + k)[0];
 #pragma unroll
@@ -329,6 +331,10 @@ __device__ __forceinline__ h4 as_h4(uint32_t a, uint32_t b) {
   return __builtin_bit_cast(h4, u);
 }
 
+__device__ __forceinline__ uint32_t tab_at(const uint32_t* t, uint32_t byte_off) {
+  return *reinterpret_cast<const uint32_t*>(reinterpret_cast<const uint8_t*>(t) + byte_off);
+}
+
 __device__ __forceinline__ f4 mfma32(h8 a, h8 b, f4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
@@ -361,7 +367,12 @@ __device__ __forceinline__ void load_page(const DecodeArgs& a, int64_t rec0, int
 }
 
 __global__ void __launch_bounds__(256, 2) split_mfma4_kernel(DecodeArgs a) {
-  __shared__ uint2 s_tab[256 * TAB_COPIES];     // 32 KB: byte -> (hi pair, lo pair)
+  // byte -> fp16 hi pair / lo pair, 16 copies each. The lo table sits one dword off
+  // a 256-byte multiple from the hi table so that a hi and a lo lookup cannot be
+  // fused into one paired read (which would have to be split again with moves).
+  __shared__ uint32_t s_tab[2 * 256 * TAB_COPIES + 1];
+  uint32_t* const s_thi = s_tab;
+  uint32_t* const s_tlo = s_tab + 256 * TAB_COPIES + 1;
   __shared__ uint4 s_sgn[256 * SGN_COPIES];     // 32 KB: byte -> 8 x fp16 +-1
   const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -376,9 +387,12 @@ __global__ void __launch_bounds__(256, 2) split_mfma4_kernel(DecodeArgs a) {
     _Float16 h0, l0, h1, l1;
     split_f16(c0, h0, l0);
     split_f16(c1, h1, l1);
-    const uint2 ent = make_uint2(h2bits(h0, h1), h2bits(l0, l1));
+    const uint32_t eh = h2bits(h0, h1), el = h2bits(l0, l1);
 #pragma unroll
-    for (int c = 0; c < TAB_COPIES; ++c) s_tab[e * TAB_COPIES + c] = ent;
+    for (int c = 0; c < TAB_COPIES; ++c) {
+      s_thi[e * TAB_COPIES + c] = eh;
+      s_tlo[e * TAB_COPIES + c] = el;
+    }
     uint32_t w[4];
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
@@ -447,6 +461,7 @@ __global__ void __launch_bounds__(256, 2) split_mfma4_kernel(DecodeArgs a) {
   const int npages = t1 > t0 ? (t1 - t0 + FQ_BLOCK - 1) / FQ_BLOCK : 0;
   const int32_t* bt = a.block_tables + static_cast<int64_t>(b) * a.max_blocks + t0 / FQ_BLOCK;
   const int tc = lane & (TAB_COPIES - 1);
+  const uint32_t tc4 = static_cast<uint32_t>(tc) * 4u;
   const int sc8 = lane & (SGN_COPIES - 1);
 
   float m_run = -INFINITY, l_run = 0.f;
@@ -454,38 +469,37 @@ __global__ void __launch_bounds__(256, 2) split_mfma4_kernel(DecodeArgs a) {
 #pragma unroll
   for (int t = 0; t < 8; ++t) acc_o[t] = f4{0.f, 0.f, 0.f, 0.f};
 
-  PageData cur, nxt;
-  int p = wave;
-  if (p < npages) load_page(a, (static_cast<int64_t>(bt[p]) * a.hkv + kvh) * FQ_BLOCK, g, n, cur);
-  for (; p < npages; p += 4) {
-    if (p + 4 < npages) load_page(a, (static_cast<int64_t>(bt[p + 4]) * a.hkv + kvh) * FQ_BLOCK, g, n, nxt);
-
+  // One 16-token page per wave at a time; two more pages of the same wave are in
+  // flight (a three-stage register ring, unrolled so that no stage is copied).
+  auto page_rec = [&](int pg) { return (static_cast<int64_t>(bt[pg]) * a.hkv + kvh) * FQ_BLOCK; };
+  auto process = [&](const PageData& d, int p) {
     // ---- scores
     f4 accK = {0.f, 0.f, 0.f, 0.f}, accQ = {0.f, 0.f, 0.f, 0.f};
-    const uint32_t kw[4] = {cur.kc.x, cur.kc.y, cur.kc.z, cur.kc.w};
+    const uint32_t kw[4] = {d.kc.x, d.kc.y, d.kc.z, d.kc.w};
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      uint2 e0 = s_tab[((kw[s] >> 0) & 0xFF) * TAB_COPIES + tc];
-      uint2 e1 = s_tab[((kw[s] >> 8) & 0xFF) * TAB_COPIES + tc];
-      uint2 e2 = s_tab[((kw[s] >> 16) & 0xFF) * TAB_COPIES + tc];
-      uint2 e3 = s_tab[((kw[s] >> 24) & 0xFF) * TAB_COPIES + tc];
-      const h8 ah = as_h8(e0.x, e1.x, e2.x, e3.x);
-      const h8 al = as_h8(e0.y, e1.y, e2.y, e3.y);
+      // byte offsets into a table: code byte * 64 + copy * 4
+      const uint32_t o0 = ((kw[s] << 6) & 0x3FC0u) | tc4;
+      const uint32_t o1 = ((kw[s] >> 2) & 0x3FC0u) | tc4;
+      const uint32_t o2 = ((kw[s] >> 10) & 0x3FC0u) | tc4;
+      const uint32_t o3 = ((kw[s] >> 18) & 0x3FC0u) | tc4;
+      const h8 ah = as_h8(tab_at(s_thi, o0), tab_at(s_thi, o1), tab_at(s_thi, o2), tab_at(s_thi, o3));
+      const h8 al = as_h8(tab_at(s_tlo, o0), tab_at(s_tlo, o1), tab_at(s_tlo, o2), tab_at(s_tlo, o3));
       accK = mfma32(ah, qh[s], accK);
       accK = mfma32(ah, ql[s], accK);
       accK = mfma32(al, qh[s], accK);
       // Unconditional: without QJL fields the q_s operands and signs are zero, so
       // accQ stays 0. Keeping the score block free of branches keeps every MFMA
       // result separated from its first vector-ALU read by straight-line code.
-      const uint4 sg = s_sgn[((cur.sg >> (8 * s)) & 0xFF) * SGN_COPIES + sc8];
+      const uint4 sg = s_sgn[((d.sg >> (8 * s)) & 0xFF) * SGN_COPIES + sc8];
       const h8 as = __builtin_bit_cast(h8, sg);
       accQ = mfma32(as, sh[s], accQ);
       accQ = mfma32(as, sl[s], accQ);
     }
     const int tbase = t0 + p * FQ_BLOCK + 4 * g;
     float sc[4];
-    const float knv[4] = {cur.kn.x, cur.kn.y, cur.kn.z, cur.kn.w};
-    const float gmv[4] = {cur.gm.x, cur.gm.y, cur.gm.z, cur.gm.w};
+    const float knv[4] = {d.kn.x, d.kn.y, d.kn.z, d.kn.w};
+    const float gmv[4] = {d.gm.x, d.gm.y, d.gm.z, d.gm.w};
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const float v = fmaf(gmv[e] * accQ[e], smul, knv[e] * accK[e] * kmul);
@@ -510,7 +524,7 @@ __global__ void __launch_bounds__(256, 2) split_mfma4_kernel(DecodeArgs a) {
         for (int e = 0; e < 4; ++e) acc_o[t][e] *= al[e];
       m_run = m_new;
     }
-    const float vnv[4] = {cur.vn.x, cur.vn.y, cur.vn.z, cur.vn.w};
+    const float vnv[4] = {d.vn.x, d.vn.y, d.vn.z, d.vn.w};
     uint32_t ph[2], pl[2];
 #pragma unroll
     for (int e = 0; e < 4; e += 2) {
@@ -525,30 +539,44 @@ __global__ void __launch_bounds__(256, 2) split_mfma4_kernel(DecodeArgs a) {
     const h4 Ph = as_h4(ph[0], ph[1]), Pl = as_h4(pl[0], pl[1]);
 
     // ---- values: tokens (4g+0, 4g+1) and (4g+2, 4g+3) paired per code byte
-    const uint32_t x01 = (cur.vc[0] & 0x0F0F0F0Fu) | ((cur.vc[1] & 0x0F0F0F0Fu) << 4);
-    const uint32_t y01 = ((cur.vc[0] >> 4) & 0x0F0F0F0Fu) | (cur.vc[1] & 0xF0F0F0F0u);
-    const uint32_t x23 = (cur.vc[2] & 0x0F0F0F0Fu) | ((cur.vc[3] & 0x0F0F0F0Fu) << 4);
-    const uint32_t y23 = ((cur.vc[2] >> 4) & 0x0F0F0F0Fu) | (cur.vc[3] & 0xF0F0F0F0u);
+    const uint32_t x01 = (d.vc[0] & 0x0F0F0F0Fu) | ((d.vc[1] & 0x0F0F0F0Fu) << 4);
+    const uint32_t y01 = ((d.vc[0] >> 4) & 0x0F0F0F0Fu) | (d.vc[1] & 0xF0F0F0F0u);
+    const uint32_t x23 = (d.vc[2] & 0x0F0F0F0Fu) | ((d.vc[3] & 0x0F0F0F0Fu) << 4);
+    const uint32_t y23 = ((d.vc[2] >> 4) & 0x0F0F0F0Fu) | (d.vc[3] & 0xF0F0F0F0u);
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
       const uint32_t u01 = (t & 1) ? y01 : x01;
       const uint32_t u23 = (t & 1) ? y23 : x23;
       const int sh8 = 8 * (t >> 1);
-      const uint2 e01 = s_tab[((u01 >> sh8) & 0xFF) * TAB_COPIES + tc];
-      const uint2 e23 = s_tab[((u23 >> sh8) & 0xFF) * TAB_COPIES + tc];
-      const h4 bh = as_h4(e01.x, e23.x), bl = as_h4(e01.y, e23.y);
+      const uint32_t o01 = (((u01 >> sh8) << 6) & 0x3FC0u) | tc4;
+      const uint32_t o23 = (((u23 >> sh8) << 6) & 0x3FC0u) | tc4;
+      const h4 bh = as_h4(tab_at(s_thi, o01), tab_at(s_thi, o23));
+      const h4 bl = as_h4(tab_at(s_tlo, o01), tab_at(s_tlo, o23));
       acc_o[t] = mfma16(Ph, bh, acc_o[t]);
       acc_o[t] = mfma16(Pl, bh, acc_o[t]);
       acc_o[t] = mfma16(Ph, bl, acc_o[t]);
     }
-    if (p + 4 < npages) cur = nxt;
+  };
+  PageData A, B, C;
+  const int p0 = wave;
+  if (p0 < npages) load_page(a, page_rec(p0), g, n, A);
+  if (p0 + 4 < npages) load_page(a, page_rec(p0 + 4), g, n, B);
+  for (int p = p0; p < npages; p += 12) {
+    if (p + 8 < npages) load_page(a, page_rec(p + 8), g, n, C);
+    process(A, p);
+    if (p + 4 >= npages) break;
+    if (p + 12 < npages) load_page(a, page_rec(p + 12), g, n, A);
+    process(B, p + 4);
+    if (p + 8 >= npages) break;
+    if (p + 16 < npages) load_page(a, page_rec(p + 16), g, n, B);
+    process(C, p + 8);
   }
 
   // ---- merge the 4 waves in LDS, then write this split's partials
   l_run += __shfl_xor(l_run, 16);
   l_run += __shfl_xor(l_run, 32);
-  __syncthreads();  // tables are dead from here on; reuse s_tab as scratch
-  float* s_o = reinterpret_cast<float*>(s_tab);             // [4 waves][16 heads][128]
+  __syncthreads();  // tables are dead from here on; reuse them as scratch
+  float* s_o = reinterpret_cast<float*>(s_tab);             // [4 waves][16 heads][128] over both tables
   float* s_ml = reinterpret_cast<float*>(s_sgn);            // [4 waves][16 heads][2]
   if (g == 0) {
     s_ml[(wave * 16 + n) * 2] = m_run;
@@ -592,16 +620,21 @@ __global__ void __launch_bounds__(D) merge_unrotate_kernel(DecodeArgs a) {
   __shared__ float s_inv;
   const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
   const int64_t base = (static_cast<int64_t>(b) * a.hq + h) * a.splits;
+  __shared__ float s_m[FQ_MAX_SPLITS], s_l[FQ_MAX_SPLITS];
+  if (tid < a.splits) {
+    s_m[tid] = a.part_ml[(base + tid) * 2];
+    s_l[tid] = a.part_ml[(base + tid) * 2 + 1];
+  }
+  __syncthreads();
   if (tid == 0) {
     float M = -INFINITY;
     for (int s = 0; s < a.splits; ++s)
-      if (a.part_ml[(base + s) * 2 + 1] > 0.f) M = fmaxf(M, a.part_ml[(base + s) * 2]);
+      if (s_l[s] > 0.f) M = fmaxf(M, s_m[s]);
     float Ls = 0.f;
     for (int s = 0; s < a.splits; ++s) {
-      const float l = a.part_ml[(base + s) * 2 + 1];
-      const float w = l > 0.f ? __expf(a.part_ml[(base + s) * 2] - M) : 0.f;
+      const float w = s_l[s] > 0.f ? __expf(s_m[s] - M) : 0.f;
       s_w[s] = w;
-      Ls += l * w;
+      Ls += s_l[s] * w;
     }
     s_inv = Ls > 0.f ? 1.f / Ls : 0.f;
   }
@@ -615,6 +648,7 @@ __global__ void __launch_bounds__(D) merge_unrotate_kernel(DecodeArgs a) {
   __syncthreads();
   // out_k = sum_j Pi[j][k] O_j (row j of Pi read coalesced over k)
   float r = 0.f;
+#pragma unroll 16
   for (int jj = 0; jj < D; ++jj) r = fmaf(a.pi[jj * D + tid], s_o[jj], r);
   a.out[(static_cast<int64_t>(b) * a.hq + h) * D + tid] = r;
 }

@@ -39,7 +39,11 @@ class QuantizerT(ctypes.Structure):
         ("rotation_t", ctypes.c_void_p),
         ("wht_signs", ctypes.c_void_p),
         ("qjl_matrix", ctypes.c_void_p),
+        ("mfma_operands", ctypes.c_void_p),
     ]
+
+
+MFMA_OPERAND_BYTES = 131072
 
 
 class CacheT(ctypes.Structure):
@@ -68,6 +72,8 @@ EXPORTS = {
                                    ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int64,
                                    ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p,
                                    ctypes.c_void_p]),
+    "fq_pack_mfma_operands": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p,
+                                             ctypes.c_size_t]),
     "fq_decode_auto_splits": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, ctypes.c_int]),
     "fq_decode_workspace_size": (ctypes.c_int, [ctypes.c_int] * 7 + [ctypes.POINTER(ctypes.c_size_t)]),
     "fq_decode_attention": (ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(QuantizerT), ctypes.POINTER(CacheT),
@@ -134,22 +140,42 @@ def build_codebook(bits=4, head_dim=128, rotation=ROT_HAAR, rot_seed=1, qjl_seed
     return out
 
 
+def pack_mfma_operands(rotation_matrix, qjl_matrix=None):
+    """Host bytes of the prepared matrix-core operands (fq_pack_mfma_operands)."""
+    out = np.zeros(MFMA_OPERAND_BYTES, np.uint8)
+    r = np.ascontiguousarray(rotation_matrix, np.float32)
+    sq = None if qjl_matrix is None else np.ascontiguousarray(qjl_matrix, np.float32)
+    st = lib().fq_pack_mfma_operands(r.ctypes.data_as(ctypes.c_void_p),
+                                     None if sq is None else sq.ctypes.data_as(ctypes.c_void_p),
+                                     r.shape[0], out.ctypes.data_as(ctypes.c_void_p), out.nbytes)
+    _check(st, "fq_pack_mfma_operands")
+    return out
+
+
 class Quantizer:
-    """Device copy of a layer's quantizer parameters plus the C struct pointing at them."""
+    """Device copy of a layer's quantizer parameters plus the C struct pointing at them.
+
+    prepared=True also uploads the packed matrix-core operands (fq_pack_mfma_operands);
+    with prepared=False the kernels derive them from the fp32 matrices themselves.
+    """
 
     def __init__(self, bits=4, head_dim=128, rotation=ROT_HAAR, rot_seed=1, qjl_seed=2, qjl_dim=128,
-                 device="cuda"):
+                 device="cuda", prepared=True):
         import torch
 
         self.host = build_codebook(bits, head_dim, rotation, rot_seed, qjl_seed, qjl_dim)
         self.bits, self.head_dim, self.rotation, self.qjl_dim = bits, head_dim, rotation, qjl_dim
-        self.dev = {k: torch.from_numpy(np.ascontiguousarray(self.host[k])).to(device)
-                    for k in ("levels", "boundaries", "rotation_matrix", "rotation_t", "wht_signs", "qjl_matrix")}
+        keys = ("levels", "boundaries", "rotation_matrix", "rotation_t", "wht_signs", "qjl_matrix")
+        self.dev = {k: torch.from_numpy(np.ascontiguousarray(self.host[k])).to(device) for k in keys}
+        if prepared:
+            ops = pack_mfma_operands(self.host["rotation_matrix"], self.host["qjl_matrix"] if qjl_dim else None)
+            self.dev["mfma_operands"] = torch.from_numpy(ops).to(device)
         d = self.dev
         self.struct = QuantizerT(bits, head_dim, rotation, qjl_dim, d["levels"].data_ptr(),
                                  d["boundaries"].data_ptr(), d["rotation_matrix"].data_ptr(),
                                  d["rotation_t"].data_ptr(), d["wht_signs"].data_ptr(),
-                                 d["qjl_matrix"].data_ptr() if qjl_dim else None)
+                                 d["qjl_matrix"].data_ptr() if qjl_dim else None,
+                                 d["mfma_operands"].data_ptr() if prepared else None)
 
 
 class PagedCache:

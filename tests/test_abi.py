@@ -78,7 +78,7 @@ def _fake_structs(bits=4, qjl=128, hkv=2):
     """Structs whose pointers are aligned host addresses: only argument checks may see them."""
     store = np.zeros(1 << 16, np.float32)
     base = (store.ctypes.data + 255) & ~255
-    qz = fq.QuantizerT(bits, 128, fq.ROT_HAAR, qjl, base, base, base, base, base, base)
+    qz = fq.QuantizerT(bits, 128, fq.ROT_HAAR, qjl, base, base, base, base, base, base, None)
     cz = fq.CacheT(4, 16, hkv, 128, bits, qjl, base, base, base, base, base, base)
     return store, base, qz, cz
 
@@ -99,7 +99,7 @@ def test_compress_argument_checks():
     assert call(qz, cz, slots=None) == fq.FQ_ERR_INVALID_ARG
     assert call(qz, cz, k=base + 2) == fq.FQ_ERR_INVALID_ARG  # vectors must be 16-byte aligned
     assert call(qz, cz, hs=4) == fq.FQ_ERR_INVALID_ARG        # 8-byte head stride
-    qb = fq.QuantizerT(3, 128, 0, 128, base, base, base, base, base, base)
+    qb = fq.QuantizerT(3, 128, 0, 128, base, base, base, base, base, base, None)
     assert call(qb, cz) == fq.FQ_ERR_UNSUPPORTED
     cb = fq.CacheT(4, 8, 2, 128, 4, 128, base, base, base, base, base, base)
     assert call(qz, cb) == fq.FQ_ERR_UNSUPPORTED              # block size must be 16
@@ -107,8 +107,10 @@ def test_compress_argument_checks():
     assert call(qz, cm) == fq.FQ_ERR_INVALID_ARG              # bits differ from the quantizer's
     cn = fq.CacheT(4, 16, 2, 128, 4, 128, base, base, None, base, base, base)
     assert call(qz, cn) == fq.FQ_ERR_INVALID_ARG              # QJL keys need k_qjl
-    qn = fq.QuantizerT(4, 128, 0, 128, base, base, base, None, base, base)
+    qn = fq.QuantizerT(4, 128, 0, 128, base, base, base, None, base, base, None)
     assert call(qn, cz) == fq.FQ_ERR_INVALID_ARG              # Pi^T required
+    qm = fq.QuantizerT(4, 128, 0, 128, base, base, base, base, base, base, base + 8)
+    assert call(qm, cz) == fq.FQ_ERR_INVALID_ARG              # operand buffer must be 16-byte aligned
 
 
 def test_decode_argument_checks_and_workspace():
@@ -141,3 +143,41 @@ def test_auto_splits():
     assert fq.auto_splits(32, 8, 4096) == 2
     assert fq.auto_splits(64, 8, 4096) == 1
     assert fq.auto_splits(1, 1, 100) == 1
+
+
+def _perm_row(T, r):
+    return 64 * ((r >> 2) & 1) + 16 * T + 4 * (r >> 3) + (r & 3)
+
+
+def test_pack_mfma_operands_layout():
+    """The packed operands are Pi in bf16 hi + lo and S in fp16 hi + lo (round to nearest
+    even), in the fragment order documented in the header; checked entry by entry."""
+    cb = fq.build_codebook(4, 128, fq.ROT_HAAR, 1, 2, 128)
+    pi, sm = cb["rotation_matrix"], cb["qjl_matrix"]
+    raw = fq.pack_mfma_operands(pi, sm).view(np.uint16).reshape(4, 32, 64, 8)
+
+    def bf16_rne(x):
+        u = np.asarray(x, np.float32).view(np.uint32).astype(np.uint64)
+        return (((u + 0x7FFF + ((u >> 16) & 1)) >> 16) & 0xFFFF).astype(np.uint16)
+
+    def bf16_val(b):
+        return (b.astype(np.uint32) << 16).view(np.float32)
+
+    for f in (0, 7, 13, 31):
+        T, s = f >> 3, f & 7
+        for l in (0, 5, 31, 32, 63):
+            row = _perm_row(T, l & 31)
+            col = 64 * (l >> 5) + 8 * s
+            x = pi[row, col:col + 8]
+            hi = bf16_rne(x)
+            lo = bf16_rne(x - bf16_val(hi))
+            assert np.array_equal(raw[0, f, l], hi) and np.array_equal(raw[1, f, l], lo)
+            y = sm[row, col:col + 8]
+            yh = y.astype(np.float16)
+            yl = (y - yh.astype(np.float32)).astype(np.float16)
+            assert np.array_equal(raw[2, f, l], yh.view(np.uint16))
+            assert np.array_equal(raw[3, f, l], yl.view(np.uint16))
+    # every coordinate appears exactly once per fragment column set
+    rows = sorted(_perm_row(T, r) for T in range(4) for r in range(32) if (r >> 2) & 1 == 0)
+    assert rows == list(range(64))
+    assert fq.lib().fq_pack_mfma_operands(None, None, 128, None, 0) == fq.FQ_ERR_INVALID_ARG

@@ -8,9 +8,9 @@ from tests import parity
 pytestmark = pytest.mark.gpu
 
 
-def _run(w, inp, rot=fq.ROT_HAAR, qjl=128, rot_seed=1, qjl_seed=2):
+def _run(w, inp, rot=fq.ROT_HAAR, qjl=128, rot_seed=1, qjl_seed=2, prepared=True):
     t = parity.torch_inputs(inp, w.dtype)
-    qz = fq.Quantizer(w.bits, 128, rot, rot_seed, qjl_seed, 128)
+    qz = fq.Quantizer(w.bits, 128, rot, rot_seed, qjl_seed, 128, prepared=prepared)
     cache = fq.PagedCache(inp["num_blocks"], w.num_kv_heads, 128, w.bits, qjl)
     dy, dp = fq.compress(qz, cache, t["k"], t["v"], t["slots"], debug=True)
     oq = parity.oracle_quantizer(w.bits, rot=rot, rot_seed=rot_seed, qjl_seed=qjl_seed)
@@ -105,3 +105,24 @@ def test_compress_full_size_8b_layer_sampled(gpu_lib):
     tok = np.sort(rs.choice(4096, size=256, replace=False))
     c = parity.check_compress(inp, oq, cache, dy, dp, tokens=tok)
     print("near-tie mismatches", c)
+
+
+def test_compress_lane_kernel_matches_matrix_core_kernel(gpu_lib, monkeypatch):
+    """fq_compress has a matrix-core tile kernel (default) and a lane-per-vector kernel
+    (FQ_COMPRESS_KERNEL=lane); both must meet the parity bar on the same inputs."""
+    w, inp = parity.small_workload(2, 8, 4, [300, 45], 304, seed=61)
+    for impl in ("lane", None):
+        if impl:
+            monkeypatch.setenv("FQ_COMPRESS_KERNEL", impl)
+        else:
+            monkeypatch.delenv("FQ_COMPRESS_KERNEL", raising=False)
+        qz, cache, dy, dp, oq, _ = _run(w, inp)
+        parity.check_compress(inp, oq, cache, dy, dp)
+
+
+@pytest.mark.parametrize("bits", [4, 2])
+def test_compress_kernels_derive_operands_without_prepared_buffer(gpu_lib, bits):
+    """Without the packed operand buffer the tile kernel builds the fragments in LDS."""
+    w, inp = parity.small_workload(2, 8, 4, [300, 45], 304, bits=bits, seed=67)
+    qz, cache, dy, dp, oq, _ = _run(w, inp, prepared=False)
+    parity.check_compress(inp, oq, cache, dy, dp)

@@ -92,7 +92,11 @@ def test_decode_full_size_b32_sampled(gpu_lib):
     oq = parity.oracle_quantizer(4)
     qz = fq.Quantizer(4, 128, fq.ROT_HAAR, 1, 2, 128)
     cache = fq.PagedCache(inp["num_blocks"], 8, 128, 4, 128)
-    fq.compress(qz, cache, t["k"], t["v"], t["slots"])
+    dy, dp = fq.compress(qz, cache, t["k"], t["v"], t["slots"], debug=True)  # many-tile LDS path
+    rs = np.random.default_rng(3)
+    tok = np.sort(rs.choice(parity.valid_tokens(inp)[0], size=192, replace=False))
+    print("compress near-tie mismatches", parity.check_compress(inp, oq, cache, dy, dp, tokens=tok))
+    del dy, dp
     host = parity.oracle_cache(inp, oq, seqs=seqs)
     blocks = np.concatenate([inp["block_tables"][b] for b in seqs])
     parity.upload_cache(host, cache, blocks=blocks)
