@@ -31,6 +31,25 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "compressed-KV decode tokens/s & HBM GB/s (8B-shape, 4K ctx); compress Mvec/s"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_call_traffic.json")
+DECODE_SRC = os.path.join(ROOT, "kv_cache_vector_tq4_amd", "csrc", "fq_decode.hip")
+
+
+def measured_traffic():
+    """HBM bytes per decode call from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE
+    summary, or None when the decode source has changed since it was measured."""
+    import hashlib
+
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+        with open(DECODE_SRC, "rb") as f:
+            sha = hashlib.sha256(f.read()).hexdigest()
+    except (OSError, ValueError):
+        return None
+    if rec.get("decode_source_sha256") != sha:
+        return None
+    return rec.get("bytes_per_launch")
 HBM_PEAK_GBS = 8000.0
 
 
@@ -43,6 +62,8 @@ def parse():
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--no-graph", action="store_true", help="time eager launches instead of a HIP graph")
+    p.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
+                   help="only run a plain device-to-device copy of BYTES (for scaling HBM byte counters)")
     return p.parse_args()
 
 
@@ -100,6 +121,15 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = "cuda"
+    if args.calibrate_copy:
+        n = args.calibrate_copy // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes_read": 4 * n, "calibrate_copy_bytes_written": 4 * n, "launches": 3}))
+        return
     w = synth.workload(2)
     w.layers = args.layers
     B, Hq, Hkv, d = w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim
@@ -238,7 +268,7 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBS,
-            "traffic": None,
+            "traffic": measured_traffic(),
             "algorithmic_bytes_per_launch": dec_bytes,
             "avg_launch_ms": dec_ms,
         },

@@ -266,7 +266,7 @@ constexpr int FRAG_U4 = 32 * 64;  // uint4 per matrix (32 KB)
 
 // One wave compresses one tile of 32 vectors of one kind. fpi -> Pi hi / lo
 // fragments (2 * FRAG_U4 uint4), fsm -> S hi / lo fragments (keys only).
-template <int BITS, int DT, bool KEY>
+template <int BITS, int DT, bool KEY, bool FRAG_GLOBAL = false>
 __device__ __forceinline__ void compress_tile(const CompressArgs& a, int kind, int64_t tile, int lane,
                                               const uint4* __restrict__ fpi, const uint4* __restrict__ fsm,
                                               const QCell* __restrict__ qt, float inv_w, float off) {
@@ -324,7 +324,7 @@ __device__ __forceinline__ void compress_tile(const CompressArgs& a, int kind, i
   for (int T = 0; T < 4; ++T) acc[T] = f16v{};
 #pragma unroll
   for (int s = 0; s < 8; ++s) {
-    __builtin_amdgcn_sched_barrier(0);  // keep fragment loads next to their products
+    if constexpr (!FRAG_GLOBAL) __builtin_amdgcn_sched_barrier(0);  // LDS fragments: load next to use
 #pragma unroll
     for (int T = 0; T < 4; ++T) {
       const b8 ah = __builtin_bit_cast(b8, fpi[(T * 8 + s) * 64 + lane]);
@@ -358,7 +358,7 @@ __device__ __forceinline__ void compress_tile(const CompressArgs& a, int kind, i
   for (int w = 0; w < 64 / PER; ++w) words[w] = 0;
 #pragma unroll
   for (int T = 0; T < 4; ++T) {
-    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (!FRAG_GLOBAL) __builtin_amdgcn_sched_barrier(0);  // LDS fragments: load next to use
 #pragma unroll
     for (int vv = 0; vv < 16; ++vv) {
       const int rel = 16 * T + vv;
@@ -394,7 +394,7 @@ __device__ __forceinline__ void compress_tile(const CompressArgs& a, int kind, i
     for (int T = 0; T < 4; ++T) pacc[T] = f16v{};
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
-      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (!FRAG_GLOBAL) __builtin_amdgcn_sched_barrier(0);  // LDS fragments: load next to use
       uint32_t hi[8], lo[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) split_f16b(acc[s >> 1][8 * (s & 1) + e], hi[e], lo[e]);
@@ -469,8 +469,12 @@ __device__ __forceinline__ uint4 pack8(const uint32_t (&u)[8]) {
 
 // Large inputs: work-groups of 8 waves loop over tiles with the fragments in LDS
 // (copied from the prepared operand buffer, or built from the fp32 matrices).
+// Keys run 4 waves per work-group (their 128 KB of fragments allow one work-group
+// per CU anyway), which leaves each wave enough registers for the QJL product;
+// values run 8.
 template <int BITS, int DT, bool KEY>
-__global__ void __launch_bounds__(CT_WAVES * 64) compress_mfma_kernel(CompressArgs a, int kind) {
+__global__ void __launch_bounds__((KEY ? 4 : CT_WAVES) * 64) compress_mfma_kernel(CompressArgs a, int kind) {
+  constexpr int WAVES = KEY ? 4 : CT_WAVES;
   __shared__ uint4 s_pi[2 * FRAG_U4];                       // Pi fragments, bf16 hi / lo (64 KB)
   __shared__ uint4 s_sm[KEY ? 2 * FRAG_U4 : 1];             // S fragments, fp16 hi / lo (64 KB, keys)
   __shared__ QCell s_qt[QT_CELLS];
@@ -513,8 +517,8 @@ __global__ void __launch_bounds__(CT_WAVES * 64) compress_mfma_kernel(CompressAr
   const float inv_w = s_qmap[0], off = s_qmap[1];
   const int64_t nvec = a.ntok * a.hkv;
   const int64_t ntiles = (nvec + CT_VEC - 1) / CT_VEC;
-  for (int64_t tile = static_cast<int64_t>(blockIdx.x) * CT_WAVES + wave; tile < ntiles;
-       tile += static_cast<int64_t>(gridDim.x) * CT_WAVES)
+  for (int64_t tile = static_cast<int64_t>(blockIdx.x) * WAVES + wave; tile < ntiles;
+       tile += static_cast<int64_t>(gridDim.x) * WAVES)
     compress_tile<BITS, DT, KEY>(a, kind, tile, lane, s_pi, s_sm, s_qt, inv_w, off);
 }
 
@@ -533,9 +537,9 @@ __global__ void __launch_bounds__(64) compress_direct_kernel(CompressArgs a) {
   if (!a.src[kind]) return;
   const uint4* ops = static_cast<const uint4*>(a.mfma_ops);
   if (kind == 0)
-    compress_tile<BITS, DT, true>(a, 0, blockIdx.x, tid, ops, ops + 2 * FRAG_U4, s_qt, s_qmap[0], s_qmap[1]);
+    compress_tile<BITS, DT, true, true>(a, 0, blockIdx.x, tid, ops, ops + 2 * FRAG_U4, s_qt, s_qmap[0], s_qmap[1]);
   else
-    compress_tile<BITS, DT, false>(a, 1, blockIdx.x, tid, ops, ops, s_qt, s_qmap[0], s_qmap[1]);
+    compress_tile<BITS, DT, false, true>(a, 1, blockIdx.x, tid, ops, ops, s_qt, s_qmap[0], s_qmap[1]);
 }
 
 template <int BITS, int DT>
@@ -546,12 +550,13 @@ int launch_mfma(hipStream_t st, const CompressArgs& a) {
     hipLaunchKernelGGL((compress_direct_kernel<BITS, DT>), dim3(static_cast<unsigned>(tiles), 2), dim3(64), 0, st, a);
     return static_cast<int>(hipGetLastError());
   }
-  const int64_t want = (tiles + CT_WAVES - 1) / CT_WAVES;
   if (a.src[0]) {
+    const int64_t want = (tiles + 3) / 4;
     const unsigned g = static_cast<unsigned>(want < 256 ? want : 256);
-    hipLaunchKernelGGL((compress_mfma_kernel<BITS, DT, true>), dim3(g), dim3(CT_WAVES * 64), 0, st, a, 0);
+    hipLaunchKernelGGL((compress_mfma_kernel<BITS, DT, true>), dim3(g), dim3(4 * 64), 0, st, a, 0);
   }
   if (a.src[1]) {
+    const int64_t want = (tiles + CT_WAVES - 1) / CT_WAVES;
     const unsigned g = static_cast<unsigned>(want < 512 ? want : 512);
     hipLaunchKernelGGL((compress_mfma_kernel<BITS, DT, false>), dim3(g), dim3(CT_WAVES * 64), 0, st, a, 1);
   }

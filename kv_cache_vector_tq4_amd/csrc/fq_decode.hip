@@ -58,15 +58,20 @@ struct DecodeArgs {
 };
 
 // ---------------------------------------------------------------- kernel 1
+// Four query vectors per 128-thread work-group: thread j computes coordinate j of
+// q~ = Pi q (reading column j of Pi as row j of Pi^T, coalesced over j) and then
+// q_s[j] = sum_k S[j][k] q~[k] from the staged q~.
+constexpr int RQ_NV = 4;
+
 template <int DT>
-__global__ void __launch_bounds__(256) rotate_queries_kernel(DecodeArgs a) {
-  constexpr int NV = 16;  // query vectors per work-group
-  __shared__ float s_q[NV][D];
-  __shared__ float s_r[NV][D];
+__global__ void __launch_bounds__(D) rotate_queries_kernel(DecodeArgs a) {
+  __shared__ float s_q[RQ_NV][D];
+  __shared__ float s_r[RQ_NV][D];
   const int nvec = a.batch * a.hq;
-  const int v0 = blockIdx.x * NV;
-  for (int e = threadIdx.x; e < NV * D; e += blockDim.x) {
-    const int v = e / D, j = e % D;
+  const int v0 = blockIdx.x * RQ_NV;
+  const int j = threadIdx.x;
+#pragma unroll
+  for (int v = 0; v < RQ_NV; ++v) {
     float x = 0.f;
     if (v0 + v < nvec) {
       const int64_t off = static_cast<int64_t>(v0 + v) * D + j;
@@ -78,46 +83,37 @@ __global__ void __launch_bounds__(256) rotate_queries_kernel(DecodeArgs a) {
     s_q[v][j] = x;
   }
   __syncthreads();
-  const int j = threadIdx.x % D;
-  const int half = threadIdx.x / D;
-  // q~_v[j] = sum_k Pi[j][k] q_v[k] = sum_k Pi^T[k][j] q_v[k] (coalesced over j)
-  float acc[NV / 2];
+  float acc[RQ_NV];
 #pragma unroll
-  for (int i = 0; i < NV / 2; ++i) acc[i] = 0.f;
+  for (int v = 0; v < RQ_NV; ++v) acc[v] = 0.f;
 #pragma unroll 16
   for (int k = 0; k < D; ++k) {
     const float w = a.pit[k * D + j];
 #pragma unroll
-    for (int i = 0; i < NV / 2; ++i) acc[i] = fmaf(w, s_q[half + 2 * i][k], acc[i]);
+    for (int v = 0; v < RQ_NV; ++v) acc[v] = fmaf(w, s_q[v][k], acc[v]);
   }
 #pragma unroll
-  for (int i = 0; i < NV / 2; ++i) s_r[half + 2 * i][j] = acc[i];
-  __syncthreads();
-#pragma unroll
-  for (int i = 0; i < NV / 2; ++i) {
-    const int v = v0 + half + 2 * i;
-    if (v >= nvec) continue;
-    a.qrot[static_cast<int64_t>(v) * D + j] = acc[i];
+  for (int v = 0; v < RQ_NV; ++v) {
+    s_r[v][j] = acc[v];
+    if (v0 + v < nvec) a.qrot[static_cast<int64_t>(v0 + v) * D + j] = acc[v];
   }
   if (!a.qjl_on) return;
-  // q_s[i] = sum_j S[i][j] q~[j]; thread j plays the role of row i = j.
+  __syncthreads();
 #pragma unroll
-  for (int i = 0; i < NV / 2; ++i) acc[i] = 0.f;
+  for (int v = 0; v < RQ_NV; ++v) acc[v] = 0.f;
+  const float4* srow = reinterpret_cast<const float4*>(a.smat + j * D);
 #pragma unroll 8
-  for (int k = 0; k < D; k += 4) {
-    const float4 w = reinterpret_cast<const float4*>(a.smat + j * D + k)[0];
+  for (int k4 = 0; k4 < D / 4; ++k4) {
+    const float4 w = srow[k4];
 #pragma unroll
-    for (int i = 0; i < NV / 2; ++i) {
-      const float* r = s_r[half + 2 * i];
-      acc[i] = fmaf(w.x, r[k], fmaf(w.y, r[k + 1], fmaf(w.z, r[k + 2], fmaf(w.w, r[k + 3], acc[i]))));
+    for (int v = 0; v < RQ_NV; ++v) {
+      const float* r = &s_r[v][4 * k4];
+      acc[v] = fmaf(w.x, r[0], fmaf(w.y, r[1], fmaf(w.z, r[2], fmaf(w.w, r[3], acc[v]))));
     }
   }
 #pragma unroll
-  for (int i = 0; i < NV / 2; ++i) {
-    const int v = v0 + half + 2 * i;
-    if (v >= nvec) continue;
-    a.qs[static_cast<int64_t>(v) * D + j] = acc[i];
-  }
+  for (int v = 0; v < RQ_NV; ++v)
+    if (v0 + v < nvec) a.qs[static_cast<int64_t>(v0 + v) * D + j] = acc[v];
 }
 
 // ---------------------------------------------------------------- kernel 2
@@ -614,41 +610,44 @@ __global__ void __launch_bounds__(256, 2) split_mfma4_kernel(DecodeArgs a) {
 }
 
 // ---------------------------------------------------------------- kernel 3
+// One work-group per (query head, sequence): log-sum-exp merge of the splits in
+// split order, then o = Pi^T O (row j of Pi read coalesced over the output
+// coordinate). Many small work-groups keep enough loads in flight.
 __global__ void __launch_bounds__(D) merge_unrotate_kernel(DecodeArgs a) {
   __shared__ float s_o[D];
-  __shared__ float s_w[FQ_MAX_SPLITS];
+  __shared__ float s_m[FQ_MAX_SPLITS], s_l[FQ_MAX_SPLITS], s_w[FQ_MAX_SPLITS];
   __shared__ float s_inv;
   const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
-  const int64_t base = (static_cast<int64_t>(b) * a.hq + h) * a.splits;
-  __shared__ float s_m[FQ_MAX_SPLITS], s_l[FQ_MAX_SPLITS];
-  if (tid < a.splits) {
+  const int S = a.splits;
+  const int64_t base = (static_cast<int64_t>(b) * a.hq + h) * S;
+  if (tid < S) {
     s_m[tid] = a.part_ml[(base + tid) * 2];
     s_l[tid] = a.part_ml[(base + tid) * 2 + 1];
   }
   __syncthreads();
   if (tid == 0) {
     float M = -INFINITY;
-    for (int s = 0; s < a.splits; ++s)
-      if (s_l[s] > 0.f) M = fmaxf(M, s_m[s]);
+    for (int sp = 0; sp < S; ++sp)
+      if (s_l[sp] > 0.f) M = fmaxf(M, s_m[sp]);
     float Ls = 0.f;
-    for (int s = 0; s < a.splits; ++s) {
-      const float w = s_l[s] > 0.f ? __expf(s_m[s] - M) : 0.f;
-      s_w[s] = w;
-      Ls += s_l[s] * w;
+    for (int sp = 0; sp < S; ++sp) {
+      const float w = s_l[sp] > 0.f ? __expf(s_m[sp] - M) : 0.f;
+      s_w[sp] = w;
+      Ls += s_l[sp] * w;
     }
     s_inv = Ls > 0.f ? 1.f / Ls : 0.f;
   }
   __syncthreads();
   float acc = 0.f;
-  for (int s = 0; s < a.splits; ++s) {
-    const float w = s_w[s];
-    if (w != 0.f) acc = fmaf(a.part_o[(base + s) * D + tid], w, acc);
+  for (int sp = 0; sp < S; ++sp) {
+    const float w = s_w[sp];
+    const float o = a.part_o[(base + sp) * D + tid];
+    acc = fmaf(o, w, acc);
   }
   s_o[tid] = acc * s_inv;
   __syncthreads();
-  // out_k = sum_j Pi[j][k] O_j (row j of Pi read coalesced over k)
   float r = 0.f;
-#pragma unroll 16
+#pragma unroll 32
   for (int jj = 0; jj < D; ++jj) r = fmaf(a.pi[jj * D + tid], s_o[jj], r);
   a.out[(static_cast<int64_t>(b) * a.hq + h) * D + tid] = r;
 }
@@ -694,10 +693,11 @@ int launch_decode(void* stream, const fq_quantizer& q, const fq_cache& c, const 
   hipStream_t st = static_cast<hipStream_t>(stream);
 
   const int nvec = batch * num_q_heads;
+  const unsigned rq_groups = static_cast<unsigned>((nvec + RQ_NV - 1) / RQ_NV);
   if (q_dtype == FQ_BF16)
-    hipLaunchKernelGGL(rotate_queries_kernel<FQ_BF16>, dim3((nvec + 15) / 16), dim3(256), 0, st, a);
+    hipLaunchKernelGGL(rotate_queries_kernel<FQ_BF16>, dim3(rq_groups), dim3(D), 0, st, a);
   else
-    hipLaunchKernelGGL(rotate_queries_kernel<FQ_F32>, dim3((nvec + 15) / 16), dim3(256), 0, st, a);
+    hipLaunchKernelGGL(rotate_queries_kernel<FQ_F32>, dim3(rq_groups), dim3(D), 0, st, a);
   dim3 grid(num_splits, c.num_kv_heads, batch);
   const char* impl = std::getenv("FQ_DECODE_KERNEL");
   const bool valu = impl && std::strcmp(impl, "valu") == 0;
