@@ -62,6 +62,7 @@ def parse():
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--no-graph", action="store_true", help="time eager launches instead of a HIP graph")
+    p.add_argument("--no-extra", action="store_true", help="skip the other workloads' measurements")
     p.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                    help="only run a plain device-to-device copy of BYTES (for scaling HBM byte counters)")
     return p.parse_args()
@@ -106,6 +107,87 @@ def cpu_baseline(w, layer_seed, budget_s):
         "sample": "%d x (compress 1 new token + decode 1 sequence of %d tokens, 32 q / 8 kv heads, one layer) "
                   "in %.1f s; tokens/s = 1 / (seconds per sequence-layer x %d layers)" % (n, L, dt, w.layers),
     }
+
+
+def _events_ms(fn, reps, stream):
+    """Mean duration (ms) of fn() from HIP events recorded on the library's stream."""
+    import torch
+
+    out = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        fn()
+        e1.record(stream)
+        out.append((e0, e1))
+    torch.cuda.synchronize()
+    return float(np.mean([a.elapsed_time(b) for a, b in out]))
+
+
+def decode_layer_measure(index, bits, rot, replicas, reps, stream):
+    """One decode layer of a workload, rotating through distinct cache replicas so that
+    the reads come from HBM (replicas x cache bytes > the 256 MB last-level cache)."""
+    import torch
+
+    from kv_cache_vector_tq4_amd import fq, synth
+
+    w = synth.workload(index, bits=bits)
+    B, Hq, Hkv, d = w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim
+    lens = np.asarray(w.seq_lens, np.int32)
+    bt_np, nblocks = synth.block_tables(77 + index, w.seq_lens, w.capacity_tokens)
+    slots = torch.from_numpy(np.concatenate([synth.slot_mapping_for(bt_np[b], int(lens[b]))
+                                             for b in range(B)])).cuda()
+    qz = fq.Quantizer(bits, d, rot, 1, 2, 128)
+    caches = []
+    for r in range(replicas):
+        c = fq.PagedCache(nblocks, Hkv, d, bits, 128)
+        k, v = synth.kv_device(6000 + 17 * index + r, int(lens.sum()), Hkv, d)
+        fq.compress(qz, c, k, v, slots)
+        del k, v
+        caches.append(c)
+    bt = torch.from_numpy(bt_np).cuda()
+    lt = torch.from_numpy(lens).cuda()
+    q = torch.randn((B, Hq, d), device="cuda").to(torch.bfloat16)
+    ws = torch.empty(fq.workspace_bytes(B, Hq, Hkv, d, 128, int(lens.max())), dtype=torch.uint8, device="cuda")
+    out = torch.empty((B, Hq, d), dtype=torch.float32, device="cuda")
+    it = iter(range(10 ** 9))
+
+    def call():
+        fq.decode(qz, caches[next(it) % replicas], q, bt, lt, int(lens.max()), workspace=ws, out=out)
+
+    for _ in range(3):
+        call()
+    ms = _events_ms(call, reps, stream)
+    nbytes = int(lens.sum()) * Hkv * caches[0].bytes_per_token_head()
+    return {"workload": w.name, "bits": bits, "rotation": "wht" if rot else "haar",
+            "splits": fq.auto_splits(B, Hkv, int(lens.max())), "decode_ms": ms,
+            "achieved_gbs": nbytes / (ms * 1e-3) / 1e9, "frac_hbm": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "algorithmic_bytes": nbytes, "cache_replicas": replicas}
+
+
+def stream_compress_measure(bits, layers, stream):
+    """The 80-layer 70B-shaped prefill stream: every layer's 8 x 32768 K and V vectors
+    (bf16, generated on the device) compressed with that layer's quantizer."""
+    import torch
+
+    from kv_cache_vector_tq4_amd import fq, synth
+
+    T, Hkv, d = 32768, 8, 128
+    slots = torch.arange(T, dtype=torch.int64, device="cuda")
+    cache = fq.PagedCache(T // 16, Hkv, d, bits, 128)
+    total_ms = 0.0
+    for layer in range(layers):
+        qz = fq.Quantizer(bits, d, fq.ROT_HAAR, 1 + layer, 2 + layer, 128)
+        k, v = synth.kv_device(7000 + layer, T, Hkv, d)
+        total_ms += _events_ms(lambda: fq.compress(qz, cache, k, v, slots), 1, stream)
+        del k, v
+    nvec = 2 * layers * T * Hkv
+    out_b = cache.bytes_per_token_head() * T * Hkv * layers
+    in_b = 2 * layers * T * Hkv * d * 2 + layers * T * 8
+    return {"layers": layers, "bits": bits, "vectors": nvec, "ms": total_ms,
+            "mvec_per_s": nvec / (total_ms * 1e-3) / 1e6,
+            "achieved_gbs": (in_b + out_b) / (total_ms * 1e-3) / 1e9,
+            "frac_hbm": (in_b + out_b) / (total_ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
 
 
 def main():
@@ -281,6 +363,17 @@ def main():
             "algorithmic_bytes_per_launch": comp_bytes,
         },
     }
+    if not args.no_extra:
+        del caches, knew, vnew, qs, outs
+        torch.cuda.empty_cache()
+        log("other workloads: 70B-shape 32K decode, 80-layer compress stream, batch-4 2-bit decode...")
+        extra = {}
+        extra["llama70b_b1_ctx32k_haar"] = decode_layer_measure(3, 4, fq.ROT_HAAR, 8, 20, stream)
+        extra["llama70b_b1_ctx32k_wht"] = decode_layer_measure(3, 4, fq.ROT_WHT, 8, 20, stream)
+        extra["stream_80layer_compress_4bit"] = stream_compress_measure(4, 80, stream)
+        extra["stream_80layer_compress_2bit"] = stream_compress_measure(2, 80, stream)
+        extra["b4_ctx32k_decode_2bit"] = decode_layer_measure(4, 2, fq.ROT_HAAR, 4, 10, stream)
+        result["other_workloads"] = extra
     if not args.no_cpu:
         log("timing the CPU oracle (~%.0f s)..." % args.cpu_seconds)
         result["cpu_baseline"] = cpu_baseline(w, 77, args.cpu_seconds)

@@ -118,3 +118,30 @@ def test_decode_vector_alu_kernel_matches_matrix_core_kernel(gpu_lib, monkeypatc
     assert np.max(np.abs(out_m - ref)) <= parity.DECODE_TOL
     assert np.max(np.abs(out_v - ref)) <= parity.DECODE_TOL
     assert np.max(np.abs(out_m - out_v)) <= 1e-4
+
+
+@pytest.mark.parametrize("rot", [fq.ROT_HAAR, fq.ROT_WHT])
+def test_llama70b_layer_ctx32k_full_size(gpu_lib, rot):
+    """70B-shaped layer, one sequence of 32768 tokens, 64 query / 8 KV heads (GQA 8),
+    automatic split count; dense Haar and randomized Walsh-Hadamard rotations. The oracle
+    compresses the whole context (the GPU decodes the oracle's bytes); 256 sampled
+    tokens of the GPU's own compression of the same context are checked too."""
+    w = synth.workload(3)
+    inp = synth.layer_inputs(w)
+    t = parity.torch_inputs(inp, "bf16")
+    oq = parity.oracle_quantizer(4, rot=rot)
+    qz = fq.Quantizer(4, 128, rot, 1, 2, 128)
+    cache = fq.PagedCache(inp["num_blocks"], 8, 128, 4, 128)
+    dy, dp = fq.compress(qz, cache, t["k"], t["v"], t["slots"], debug=True)
+    tok = np.sort(np.random.default_rng(5).choice(32768, size=256, replace=False))
+    print("compress near-tie mismatches", parity.check_compress(inp, oq, cache, dy, dp, tokens=tok))
+    del dy, dp
+    host = parity.oracle_cache(inp, oq)
+    parity.upload_cache(host, cache)
+    splits = fq.auto_splits(1, 8, 32768)
+    out = fq.decode(qz, cache, t["q"], t["bt"], t["lens"], 32768).cpu().numpy()
+    ref = parity.oracle_decode(inp, host, oq)
+    err = np.max(np.abs(out - ref))
+    print("splits", splits, "max-abs", err, "cos vs exact", parity.cosine(out, parity.exact(inp)))
+    assert splits == 64
+    assert err <= parity.DECODE_TOL
