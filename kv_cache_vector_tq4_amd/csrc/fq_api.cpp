@@ -47,8 +47,8 @@ fq_status check_cache(const fq_cache* c, const fq_quantizer* q) {
 
 namespace fq {
 
-DecodeWorkspace decode_workspace(int batch, int num_q_heads, int head_dim, int qjl_dim,
-                                 int num_splits) {
+DecodeWorkspace decode_workspace(int batch, int num_q_heads, int num_kv_heads, int head_dim,
+                                 int qjl_dim, int num_splits) {
   auto up = [](size_t x) { return (x + 255) & ~static_cast<size_t>(255); };
   const size_t bh = static_cast<size_t>(batch) * num_q_heads;
   DecodeWorkspace w{};
@@ -61,6 +61,8 @@ DecodeWorkspace decode_workspace(int batch, int num_q_heads, int head_dim, int q
   off += up(bh * num_splits * head_dim * sizeof(float));
   w.part_ml = off;
   off += up(bh * num_splits * 2 * sizeof(float));
+  w.qops = off;
+  off += up(static_cast<size_t>(batch) * num_kv_heads * FQ_QOPS * 64 * 16);
   w.total = off;
   return w;
 }
@@ -138,7 +140,7 @@ fq_status fq_decode_workspace_size(int batch, int num_q_heads, int num_kv_heads,
     return FQ_ERR_UNSUPPORTED;
   if (num_splits > FQ_MAX_SPLITS) return FQ_ERR_UNSUPPORTED;
   int s = num_splits == 0 ? fq::auto_splits(batch, num_kv_heads, max_seq_len) : num_splits;
-  *bytes = fq::decode_workspace(batch, num_q_heads, head_dim, qjl_dim, s).total;
+  *bytes = fq::decode_workspace(batch, num_q_heads, num_kv_heads, head_dim, qjl_dim, s).total;
   return FQ_OK;
 }
 
@@ -166,7 +168,9 @@ fq_status fq_decode_attention(void* stream, const fq_quantizer* quant, const fq_
     return FQ_ERR_INVALID_ARG;
   const int s = num_splits == 0 ? fq::auto_splits(batch, cache->num_kv_heads, max_seq_len)
                                 : num_splits;
-  const size_t need = fq::decode_workspace(batch, num_q_heads, FQ_HEAD_DIM, quant->qjl_dim, s).total;
+  const size_t need =
+      fq::decode_workspace(batch, num_q_heads, cache->num_kv_heads, FQ_HEAD_DIM, quant->qjl_dim, s)
+          .total;
   if (!workspace || workspace_bytes < need || !aligned(workspace, 256)) return FQ_ERR_WORKSPACE;
   int e = fq::launch_decode(stream, *quant, *cache, q, q_dtype, batch, num_q_heads, block_tables,
                             max_blocks_per_seq, seq_lens, max_seq_len, s, scale, workspace, out);

@@ -52,68 +52,217 @@ struct DecodeArgs {
   float* qs;       // [B][Hq][m]
   float* part_o;   // [B][Hq][S][d]
   float* part_ml;  // [B][Hq][S][2]
+  uint4* qops;     // [B][Hkv][FQ_QOPS][64]
   float* out;      // [B][Hq][d]
   int batch, hq, hkv, group, splits, chunk, max_blocks, qjl_on;
   float scale;
 };
 
-// ---------------------------------------------------------------- kernel 1
-// Four query vectors per 128-thread work-group: thread j computes coordinate j of
-// q~ = Pi q (reading column j of Pi as row j of Pi^T, coalesced over j) and then
-// q_s[j] = sum_k S[j][k] q~[k] from the staged q~.
-constexpr int RQ_NV = 4;
+// fp16 helpers shared by the matrix-core kernels.
+typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef float f4 __attribute__((ext_vector_type(4)));
 
-template <int DT>
-__global__ void __launch_bounds__(D) rotate_queries_kernel(DecodeArgs a) {
-  __shared__ float s_q[RQ_NV][D];
-  __shared__ float s_r[RQ_NV][D];
-  const int nvec = a.batch * a.hq;
-  const int v0 = blockIdx.x * RQ_NV;
-  const int j = threadIdx.x;
+constexpr int LEV_SHIFT = 8;        // levels are stored x 2^8 in the tables
+constexpr int TAB_COPIES = 16;
+constexpr int SGN_COPIES = 8;
+
+__device__ __forceinline__ uint32_t h2bits(_Float16 a, _Float16 b) {
+  return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, a)) |
+         (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, b)) << 16);
+}
+
+__device__ __forceinline__ void split_f16(float x, _Float16& hi, _Float16& lo) {
+  hi = static_cast<_Float16>(x);
+  lo = static_cast<_Float16>(x - static_cast<float>(hi));
+}
+
+__device__ __forceinline__ h8 as_h8(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+  uint4 u = make_uint4(a, b, c, d);
+  return __builtin_bit_cast(h8, u);
+}
+
+__device__ __forceinline__ h4 as_h4(uint32_t a, uint32_t b) {
+  uint2 u = make_uint2(a, b);
+  return __builtin_bit_cast(h4, u);
+}
+
+__device__ __forceinline__ uint32_t tab_at(const uint32_t* t, uint32_t byte_off) {
+  return *reinterpret_cast<const uint32_t*>(reinterpret_cast<const uint8_t*>(t) + byte_off);
+}
+
+__device__ __forceinline__ f4 mfma32(h8 a, h8 b, f4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f4 mfma16(h4 a, h4 b, f4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
+}
+
+// ---------------------------------------------------------------- kernel 1
+// One work-group per (KV head, sequence); thread j owns coordinate j of the G
+// query heads of that KV head:
+//   q~[h][j]  = sum_k Pi[j][k] q[h][k]     (row j of Pi)
+//   q_s[h][j] = sum_k S[j][k] q~[h][k]     (row j of S)
+// stored as [b][query head][j]. With SLOTS > 0 it also writes the per-lane
+// operands of the packed split kernel (see packed_decode4_kernel): fp16 hi / lo
+// splits of q~ and q_s arranged in the matrix-core B layout, and the per-lane
+// score factor.
+constexpr float QJL_R = 256.0f * QJL_C;  // 2^8 (level scale) x sqrt(pi/2) / m
+constexpr float LOG2E_F = 1.4426950408889634f;
+
+__device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
-  for (int v = 0; v < RQ_NV; ++v) {
-    float x = 0.f;
-    if (v0 + v < nvec) {
-      const int64_t off = static_cast<int64_t>(v0 + v) * D + j;
-      if constexpr (DT == FQ_BF16)
-        x = __uint_as_float(static_cast<uint32_t>(static_cast<const uint16_t*>(a.q)[off]) << 16);
-      else
-        x = static_cast<const float*>(a.q)[off];
+  for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
+  return v;
+}
+
+constexpr int PQ_THREADS = 512;  // thread = (coordinate j, k-quarter kq)
+
+// Row j of a 128 x 128 fp32 matrix restricted to k = 32 kq .. 32 kq + 31: eight
+// float4, all requested together at kernel start.
+__device__ __forceinline__ void row_quarter_load(const float* m, int j, int kq, float4 (&x)[8]) {
+  const float4* src = reinterpret_cast<const float4*>(m) + j * (D / 4) + 8 * kq;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) x[i] = src[i];
+}
+
+// s_part[kq][h][j] = sum over k in quarter kq of row[k] vec[h][k], for h < G; then
+// out[h][j] = sum over the four quarters (threads of quarter kq finish heads
+// kq, kq + 4, ...).
+template <int GM>
+__device__ __forceinline__ void quarter_dot(const float4 (&row)[8], const float (*vec)[D], int j, int kq,
+                                            int G, float (*s_part)[FQ_MAX_GROUP][D]) {
+#pragma unroll
+  for (int h = 0; h < GM; ++h) {
+    if (h < G) {
+      float acc = 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float4 x = *reinterpret_cast<const float4*>(&vec[h][32 * kq + 4 * i]);
+        acc = fmaf(row[i].x, x.x, fmaf(row[i].y, x.y, fmaf(row[i].z, x.z, fmaf(row[i].w, x.w, acc))));
+      }
+      s_part[kq][h][j] = acc;
     }
-    s_q[v][j] = x;
+  }
+}
+
+template <int DT, int SLOTS>
+__global__ void __launch_bounds__(PQ_THREADS) prepare_queries_kernel(DecodeArgs a) {
+  __shared__ __align__(16) float s_q[FQ_MAX_GROUP][D];
+  __shared__ __align__(16) float s_r[FQ_MAX_GROUP][D];
+  __shared__ __align__(16) float s_s[FQ_MAX_GROUP][D];
+  __shared__ __align__(16) float s_part[4][FQ_MAX_GROUP][D];
+  __shared__ float s_mx[2][FQ_MAX_GROUP][2];  // [q~, q_s][head][row half]
+  const int kvh = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  const int j = tid & (D - 1);
+  const int kq = __builtin_amdgcn_readfirstlane(tid >> 7);
+  const int G = a.group;
+  const bool qjl = a.qjl_on != 0;
+  const int64_t row0 = (static_cast<int64_t>(b) * a.hq + kvh * G) * D;
+  float4 pr[8], sr[8];
+  row_quarter_load(a.pi, j, kq, pr);
+  row_quarter_load(qjl ? a.smat : a.pi, j, kq, sr);  // S is unused without QJL fields
+  for (int h = kq; h < G; h += 4) {
+    const int64_t off = row0 + h * D + j;
+    if constexpr (DT == FQ_BF16)
+      s_q[h][j] = __uint_as_float(static_cast<uint32_t>(static_cast<const uint16_t*>(a.q)[off]) << 16);
+    else
+      s_q[h][j] = static_cast<const float*>(a.q)[off];
   }
   __syncthreads();
-  float acc[RQ_NV];
-#pragma unroll
-  for (int v = 0; v < RQ_NV; ++v) acc[v] = 0.f;
-#pragma unroll 16
-  for (int k = 0; k < D; ++k) {
-    const float w = a.pit[k * D + j];
-#pragma unroll
-    for (int v = 0; v < RQ_NV; ++v) acc[v] = fmaf(w, s_q[v][k], acc[v]);
-  }
-#pragma unroll
-  for (int v = 0; v < RQ_NV; ++v) {
-    s_r[v][j] = acc[v];
-    if (v0 + v < nvec) a.qrot[static_cast<int64_t>(v0 + v) * D + j] = acc[v];
-  }
-  if (!a.qjl_on) return;
+  auto dot = [&](const float4 (&row)[8], const float (*vec)[D]) {
+    if (G <= 4) quarter_dot<4>(row, vec, j, kq, G, s_part);
+    else if (G <= 8) quarter_dot<8>(row, vec, j, kq, G, s_part);
+    else quarter_dot<16>(row, vec, j, kq, G, s_part);
+  };
+  dot(pr, s_q);  // q~[h][j] = sum_k Pi[j][k] q[h][k]
   __syncthreads();
-#pragma unroll
-  for (int v = 0; v < RQ_NV; ++v) acc[v] = 0.f;
-  const float4* srow = reinterpret_cast<const float4*>(a.smat + j * D);
-#pragma unroll 8
-  for (int k4 = 0; k4 < D / 4; ++k4) {
-    const float4 w = srow[k4];
-#pragma unroll
-    for (int v = 0; v < RQ_NV; ++v) {
-      const float* r = &s_r[v][4 * k4];
-      acc[v] = fmaf(w.x, r[0], fmaf(w.y, r[1], fmaf(w.z, r[2], fmaf(w.w, r[3], acc[v]))));
+  for (int h = kq; h < G; h += 4) {
+    const float v = (s_part[0][h][j] + s_part[1][h][j]) + (s_part[2][h][j] + s_part[3][h][j]);
+    s_r[h][j] = v;
+    a.qrot[row0 + h * D + j] = v;
+  }
+  __syncthreads();
+  if (qjl) {
+    dot(sr, s_r);  // q_s[h][j] = sum_k S[j][k] q~[h][k]
+    __syncthreads();
+  }
+  for (int h = kq; h < G; h += 4) {
+    float v = 0.f;
+    if (qjl) {
+      v = (s_part[0][h][j] + s_part[1][h][j]) + (s_part[2][h][j] + s_part[3][h][j]);
+      a.qs[row0 + h * D + j] = v;
+    }
+    s_s[h][j] = v;
+  }
+  __syncthreads();
+  if constexpr (SLOTS == 0) return;
+  // ---- per-head maxima (each wave holds 64 coordinates of the heads of its quarter)
+  for (int h = kq; h < G; h += 4) {
+    const float mr = wave_max(fabsf(s_r[h][j]));
+    const float ms = wave_max(fabsf(s_s[h][j]));
+    if ((j & 63) == 0) {
+      s_mx[0][h][j >> 6] = mr;
+      s_mx[1][h][j >> 6] = ms;
     }
   }
+  __syncthreads();
+  uint4* ops = a.qops + (static_cast<int64_t>(b) * a.hkv + kvh) * (FQ_QOPS * 64);
+  for (int idx = tid; idx < FQ_QOPS * 64; idx += PQ_THREADS) {
+    const int op = idx >> 6, l = idx & 63;
+    constexpr int SL = SLOTS > 0 ? SLOTS : 1;
+    const int g = l >> 4, n = l & 15, h = n / SL, s = n % SL;
+    uint4 u = make_uint4(0u, 0u, 0u, 0u);
+    if (h < G) {
+      // One power of two per head puts max |q~| in [128, 256); q_s takes that power
+      // times QJL_R so that both accumulators share the score factor, lowered if
+      // q_s would exceed 2^15.
+      const float mq = fmaxf(s_mx[0][h][0], s_mx[0][h][1]);
+      const float msv = fmaxf(s_mx[1][h][0], s_mx[1][h][1]);
+      int ex = 0, e_use = 0, eq = 0, es = 0;
+      if (mq > 0.f) { frexpf(mq, &ex); eq = 8 - ex; }
+      if (msv > 0.f) { frexpf(msv * QJL_R, &ex); es = 15 - ex; }
+      e_use = mq > 0.f ? (msv > 0.f ? min(eq, es) : eq) : (msv > 0.f ? es : 0);
+      const float qscale = ldexpf(1.f, e_use), sscale = qscale * QJL_R;
+      auto split_pair = [](float x0, float x1, uint32_t& hi, uint32_t& lo) {
+        _Float16 h0, l0, h1, l1;
+        split_f16(x0, h0, l0);
+        split_f16(x1, h1, l1);
+        hi = h2bits(h0, h1);
+        lo = h2bits(l0, l1);
+      };
+      auto signs8 = [&](int i, bool want_lo) {  // q_s entries 32g + 8i .. +7
+        uint32_t w[4];
 #pragma unroll
-  for (int v = 0; v < RQ_NV; ++v)
-    if (v0 + v < nvec) a.qs[static_cast<int64_t>(v0 + v) * D + j] = acc[v];
+        for (int k = 0; k < 4; ++k) {
+          uint32_t hi, lo;
+          split_pair(s_s[h][32 * g + 8 * i + 2 * k] * sscale, s_s[h][32 * g + 8 * i + 2 * k + 1] * sscale,
+                     hi, lo);
+          w[k] = want_lo ? lo : hi;
+        }
+        return make_uint4(w[0], w[1], w[2], w[3]);
+      };
+      if (op < 8) {
+        const int i = op;
+        if (s < 2) {  // q~ entries 32g + 4i .. +3
+          uint32_t h01, l01, h23, l23;
+          const float* r = &s_r[h][32 * g + 4 * i];
+          split_pair(r[0] * qscale, r[1] * qscale, h01, l01);
+          split_pair(r[2] * qscale, r[3] * qscale, h23, l23);
+          u = s == 0 ? make_uint4(h01, h01, h23, h23) : make_uint4(l01, 0u, l23, 0u);
+        } else if (i < 4) {  // SLOTS 4 only: sign operands share these registers
+          u = signs8(i, s == 3);
+        }
+      } else if (op < 12) {
+        if (SLOTS == 2) u = signs8(op - 8, s == 1);
+      } else {
+        const float cfac = a.scale * LOG2E_F / (qscale * 256.0f);
+        u = make_uint4(__float_as_uint(cfac), 0u, 0u, 0u);
+      }
+    }
+    ops[idx] = u;
+  }
 }
 
 // ---------------------------------------------------------------- kernel 2
@@ -299,46 +448,6 @@ __global__ void __launch_bounds__(256) split_attention_kernel(DecodeArgs a) {
 // different bytes hit different banks. Levels are scaled by 2^8 and each query
 // head by a power of two before the split so that no lo part is subnormal.
 // Lane l: g = l / 16 (k-group / token quad), n = l % 16 (token / head / dim group).
-typedef _Float16 h4 __attribute__((ext_vector_type(4)));
-typedef _Float16 h8 __attribute__((ext_vector_type(8)));
-typedef float f4 __attribute__((ext_vector_type(4)));
-
-constexpr int LEV_SHIFT = 8;        // levels are stored x 2^8 in the tables
-constexpr int TAB_COPIES = 16;
-constexpr int SGN_COPIES = 8;
-
-__device__ __forceinline__ uint32_t h2bits(_Float16 a, _Float16 b) {
-  return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, a)) |
-         (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, b)) << 16);
-}
-
-__device__ __forceinline__ void split_f16(float x, _Float16& hi, _Float16& lo) {
-  hi = static_cast<_Float16>(x);
-  lo = static_cast<_Float16>(x - static_cast<float>(hi));
-}
-
-__device__ __forceinline__ h8 as_h8(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
-  uint4 u = make_uint4(a, b, c, d);
-  return __builtin_bit_cast(h8, u);
-}
-
-__device__ __forceinline__ h4 as_h4(uint32_t a, uint32_t b) {
-  uint2 u = make_uint2(a, b);
-  return __builtin_bit_cast(h4, u);
-}
-
-__device__ __forceinline__ uint32_t tab_at(const uint32_t* t, uint32_t byte_off) {
-  return *reinterpret_cast<const uint32_t*>(reinterpret_cast<const uint8_t*>(t) + byte_off);
-}
-
-__device__ __forceinline__ f4 mfma32(h8 a, h8 b, f4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
-}
-
-__device__ __forceinline__ f4 mfma16(h4 a, h4 b, f4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
-}
-
 struct PageData {
   uint4 kc;       // 16 code bytes: dims 32g .. 32g+31 of token n
   uint32_t sg;    // 32 QJL bits: projections 32g .. 32g+31 of token n
@@ -609,47 +718,460 @@ __global__ void __launch_bounds__(256, 2) split_mfma4_kernel(DecodeArgs a) {
   }
 }
 
-// ---------------------------------------------------------------- kernel 3
-// One work-group per (query head, sequence): log-sum-exp merge of the splits in
-// split order, then o = Pi^T O (row j of Pi read coalesced over the output
-// coordinate). Many small work-groups keep enough loads in flight.
-__global__ void __launch_bounds__(D) merge_unrotate_kernel(DecodeArgs a) {
-  __shared__ float s_o[D];
-  __shared__ float s_m[FQ_MAX_SPLITS], s_l[FQ_MAX_SPLITS], s_w[FQ_MAX_SPLITS];
-  __shared__ float s_inv;
-  const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
-  const int S = a.splits;
-  const int64_t base = (static_cast<int64_t>(b) * a.hq + h) * S;
-  if (tid < S) {
-    s_m[tid] = a.part_ml[(base + tid) * 2];
-    s_l[tid] = a.part_ml[(base + tid) * 2 + 1];
+// ---------------------------------------------------------------- kernel 2 (MFMA, packed)
+// Split attention on the matrix cores, 4-bit codes, group size G <= 8.
+//
+// One work-group of WAVES waves per (split, KV head, sequence); waves take the
+// split's 16-token pages round-robin and are merged in LDS at the end.
+//
+// Scores are computed transposed, C[(query head, slot)][token], so that one lane
+// ends up holding whole scores: lane (g, n) (g = lane / 16, n = lane % 16) holds
+// rows 4g .. 4g+3 of column n, i.e. every slot of its head(s) for token n.
+//   SLOTS = 4 (G <= 4): row 4h + s, lane (g, n) serves head g.
+//     codes   B = [hi | lo] of the dequantized keys, interleaved along K;
+//             A: slot 0 = q~ hi against both parts, slot 1 = q~ lo against the
+//             hi part, so slot 0 + slot 1 = (k^hi + k^lo) q~hi + k^hi q~lo.
+//     signs   B = exact +-1, A: slot 2 = q_s hi, slot 3 = q_s lo.
+//     Both products read the same A registers (the unused slots of one are the
+//     operands of the other) and write different accumulators.
+//   SLOTS = 2 (G <= 8): row 2h + s, lane (g, n) serves heads 2g and 2g + 1;
+//     slots 0 / 1 as above for the codes and a separate operand set for the
+//     signs (slot 0 = q_s hi, slot 1 = q_s lo).
+// The value product C[(head, slot)][dim] += P[(head, slot)][(token, part)]
+// V^[(token, part)][dim] runs on 16x16x32 with K = 16 tokens x {hi, lo}: row
+// slot 0 carries P hi against both parts of V^, row slot 1 carries P lo against
+// the hi part (rows of other slots are zero). P goes from the score layout
+// (lane = head x token) to the operand layout (lane = head-slot x token quad)
+// by four lane permutes.
+//
+// Dequantization reads one 8-byte LDS entry per code byte (hi pair, lo pair of
+// the two codes' levels x 2^8). The table holds 32 copies of each entry, copy =
+// lane % 32, with a 256-byte stride per byte value, so lane offsets are built by
+// one byte permute and a wave's 64 lookups never share a bank. QJL signs use a
+// 16-entry nibble table (4 x fp16 +-1) laid out the same way.
+//
+// Scores are kept in log2 units (log2 e folded into the per-head factor); the
+// running max is only moved when a page's max exceeds it by more than 8, so
+// probabilities stay below 2^8 and fp16-splittable.
+// Work-group shape per slot layout: waves, register-ring depth, waves per SIMD.
+constexpr int PK4_WAVES = 4, PK4_RING = 3, PK4_OCC = 2;  // SLOTS 4
+constexpr int PK2_WAVES = 8, PK2_RING = 2, PK2_OCC = 4;  // SLOTS 2
+constexpr int PK_SIGN_BASE = 0;       // 16 x 32 x 8 B
+constexpr int PK_CODE_BASE = 4096;    // 256 x 32 x 8 B
+constexpr int PK_STAGE_BASE = 69632;  // 256 x 8 B staging for the table build
+constexpr int PK_QOPS_BASE = 71680;   // 8 x 64 lanes x 16 B code-product operands
+constexpr int PK_LDS_BYTES = PK_QOPS_BASE + 8 * 64 * 16;
+constexpr float PK_TAU = 8.0f;
+
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u(uint32_t x) {
+  return static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(x), CTRL, 0xF, 0xF, true));
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+  return __uint_as_float(dpp_u<CTRL>(__float_as_uint(x)));
+}
+constexpr int DPP_XOR1 = 0xB1;    // quad_perm [1, 0, 3, 2]
+constexpr int DPP_XOR2 = 0x4E;    // quad_perm [2, 3, 0, 1]
+constexpr int DPP_ROR4 = 0x124;   // rotate right by 4 within a row of 16 lanes
+constexpr int DPP_ROR8 = 0x128;   // rotate right by 8 within a row of 16 lanes
+
+// Maximum / sum over the 16 lanes of a row.
+__device__ __forceinline__ float row_max(float x) {
+  x = fmaxf(x, dpp_f<DPP_XOR1>(x));
+  x = fmaxf(x, dpp_f<DPP_XOR2>(x));
+  x = fmaxf(x, dpp_f<DPP_ROR4>(x));
+  return fmaxf(x, dpp_f<DPP_ROR8>(x));
+}
+__device__ __forceinline__ float row_sum(float x) {
+  x += dpp_f<DPP_XOR1>(x);
+  x += dpp_f<DPP_XOR2>(x);
+  x += dpp_f<DPP_ROR4>(x);
+  return x + dpp_f<DPP_ROR8>(x);
+}
+
+// Byte b of w placed in byte 1 of the result, byte 0 of c in byte 0, zeros above:
+// (byte of w) * 256 + c for c < 256.
+__device__ __forceinline__ uint32_t tab_off(uint32_t w, uint32_t c, int b) {
+  return __builtin_amdgcn_perm(w, c, 0x0C0C0400u + (static_cast<uint32_t>(b) << 8));
+}
+
+__device__ __forceinline__ uint2 lds_u2(const uint8_t* base, uint32_t off) {
+  return *reinterpret_cast<const uint2*>(base + off);
+}
+
+__device__ __forceinline__ h8 h8_of(uint2 a, uint2 b) { return as_h8(a.x, a.y, b.x, b.y); }
+
+struct PkPage {
+  uint4 kc;        // code bytes 16g .. 16g+15 of token n (dims 32g .. 32g+31)
+  uint32_t sg;     // sign bytes 4g .. 4g+3 of token n (projections 32g .. 32g+31)
+  float kn, gm, vn;  // key norm, gamma, value norm of token n
+  uint32_t vc[4];  // value code dword n (dims 8n .. 8n+7) of tokens 4g+e
+};
+
+// Per-lane byte offsets of a page's fields (constant over pages).
+struct PkLane {
+  uint32_t kc, sg, vc;
+};
+
+// Loads one page; rec0 = first record of the page (wave-uniform), so every
+// address is a uniform base plus a fixed 32-bit lane offset.
+__device__ __forceinline__ void pk_load(const DecodeArgs& a, int64_t rec0, int n, const PkLane& o,
+                                        const float* gptr, const uint8_t* sgn_base, PkPage& d) {
+  d.kc = *reinterpret_cast<const uint4*>(a.k_codes + rec0 * 64 + o.kc);
+  d.sg = *reinterpret_cast<const uint32_t*>(sgn_base + rec0 * 16 + o.sg);
+  d.kn = a.k_norm[rec0 + n];
+  d.gm = gptr[rec0 + n];
+  d.vn = a.v_norm[rec0 + n];
+  const uint8_t* vcb = a.v_codes + rec0 * 64 + o.vc;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) d.vc[e] = *reinterpret_cast<const uint32_t*>(vcb + 64 * e);
+}
+
+template <int SLOTS, int WAVES, int RING, int OCC>
+__global__ void __launch_bounds__(WAVES * 64, OCC) packed_decode4_kernel(DecodeArgs a) {
+  __shared__ __align__(16) uint8_t s_lds[PK_LDS_BYTES];
+  const uint8_t* const s_code = s_lds + PK_CODE_BASE;
+  const uint8_t* const s_sign = s_lds + PK_SIGN_BASE;
+  constexpr int HL = 4 / SLOTS;  // heads per lane in the score layout (1 or 2)
+  const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 4, n = lane & 15;
+  const int s = n % SLOTS;  // operand-layout slot of this lane
+  const int G = a.group;
+
+  const int t0 = split * a.chunk;
+  const int p0 = wave;
+  // The first 64 block numbers of this wave are requested together with the
+  // sequence length (columns clamped to the table row).
+  const int32_t* btrow = a.block_tables + static_cast<int64_t>(b) * a.max_blocks;
+  int bt_cur = a.max_blocks > 0 ? btrow[min(t0 / FQ_BLOCK + p0 + lane * WAVES, a.max_blocks - 1)] : 0;
+  const int len = a.seq_lens[b];
+  const int t1 = min(len, t0 + a.chunk);
+  const int npages = t1 > t0 ? (t1 - t0 + FQ_BLOCK - 1) / FQ_BLOCK : 0;
+  const int32_t* bt = btrow + t0 / FQ_BLOCK;
+  const bool qjl = a.qjl_on != 0;
+  // Without QJL fields the sign operands are zero; their loads read other, valid
+  // arrays of the page instead.
+  const uint8_t* const sgn_base = qjl ? a.k_qjl : a.k_codes;
+  const float* const gptr = qjl ? a.k_gamma : a.k_norm;
+  // This wave's pages are p0 + i * WAVES, i < my_pages, taken in chunks of 64 whose
+  // block numbers are held one per lane; a page's record then comes from a lane
+  // read. Every load of the page loop is unconditional (prefetch indices are
+  // clamped to the chunk's last page), so each wait covers exactly the page it
+  // needs and not the prefetches behind it.
+  const int my_pages = p0 < npages ? (npages - 1 - p0) / WAVES + 1 : 0;
+  auto bt_chunk = [&](int c0) {
+    const int cn = min(64, my_pages - c0);
+    return bt[p0 + (c0 + min(lane, cn - 1)) * WAVES];
+  };
+  auto rec_of = [&](int vblk, int i) {
+    const int blk = __builtin_amdgcn_readlane(vblk, i);
+    return (static_cast<int64_t>(blk) * a.hkv + kvh) * FQ_BLOCK;
+  };
+  PkLane lo;
+  lo.kc = static_cast<uint32_t>(n * 64 + 16 * g);
+  lo.sg = static_cast<uint32_t>(n * 16 + 4 * g);
+  lo.vc = static_cast<uint32_t>(4 * g * 64 + 4 * n);
+
+  // ---- the wave's first two pages are requested before any set-up work
+  PkPage ring[RING];
+  if (my_pages > 0) {
+#pragma unroll
+    for (int k = 0; k < RING - 1; ++k)
+      pk_load(a, rec_of(bt_cur, min(k, min(64, my_pages) - 1)), n, lo, gptr, sgn_base, ring[k]);
   }
-  __syncthreads();
-  if (tid == 0) {
-    float M = -INFINITY;
-    for (int sp = 0; sp < S; ++sp)
-      if (s_l[sp] > 0.f) M = fmaxf(M, s_m[sp]);
-    float Ls = 0.f;
-    for (int sp = 0; sp < S; ++sp) {
-      const float w = s_l[sp] > 0.f ? __expf(s_m[sp] - M) : 0.f;
-      s_w[sp] = w;
-      Ls += s_l[sp] * w;
+
+  // ---- query operands, prepared per lane by the query kernel. The code-product
+  // operands (shared by every wave) are read from LDS at each step.
+  h8 qs[4];  // SLOTS 2: sign-product A operands
+  float cf[HL];  // score factor of this lane's head(s) in the score layout
+  const uint4* const ops = a.qops + (static_cast<int64_t>(b) * a.hkv + kvh) * (FQ_QOPS * 64);
+  // operand idx / 64 of lane idx % 64 goes to LDS entry idx
+  for (int idx = tid; idx < 8 * 64; idx += WAVES * 64)
+    reinterpret_cast<uint4*>(s_lds + PK_QOPS_BASE)[idx] = ops[idx];
+  {
+    if constexpr (SLOTS == 2) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) qs[i] = __builtin_bit_cast(h8, ops[(8 + i) * 64 + lane]);
     }
-    s_inv = Ls > 0.f ? 1.f / Ls : 0.f;
+    // the factor of head h sits in operand 12 of lane h * SLOTS
+#pragma unroll
+    for (int k = 0; k < HL; ++k) cf[k] = __uint_as_float(ops[12 * 64 + (HL * g + k) * SLOTS].x);
+  }
+
+  // ---- tables: stage the 256 entries once, then fan out 32 conflict-free copies
+  {
+    uint2* stage = reinterpret_cast<uint2*>(s_lds + PK_STAGE_BASE);
+    if (tid < 256) {
+      const float c0 = a.levels[tid & 15] * static_cast<float>(1 << LEV_SHIFT);
+      const float c1 = a.levels[tid >> 4] * static_cast<float>(1 << LEV_SHIFT);
+      _Float16 h0, l0, h1, l1;
+      split_f16(c0, h0, l0);
+      split_f16(c1, h1, l1);
+      stage[tid] = make_uint2(h2bits(h0, h1), h2bits(l0, l1));
+    }
+    for (int idx = tid; idx < 16 * 32; idx += WAVES * 64) {
+      const int nib = idx >> 5;
+      uint32_t w[2];
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const uint32_t lo16 = ((nib >> (2 * k)) & 1) ? 0x3C00u : 0xBC00u;
+        const uint32_t hi16 = ((nib >> (2 * k + 1)) & 1) ? 0x3C00u : 0xBC00u;
+        w[k] = lo16 | (hi16 << 16);
+      }
+      *reinterpret_cast<uint2*>(s_lds + PK_SIGN_BASE + idx * 8) = make_uint2(w[0], w[1]);
+    }
+    __syncthreads();
+    // 8192 entries; four per thread and round, reads issued before writes
+    constexpr int NT = WAVES * 64;
+    for (int base = 0; base < 256 * 32; base += 4 * NT) {
+      uint2 v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int idx = base + u * NT + tid;
+        if (idx < 256 * 32) v[u] = stage[idx >> 5];
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int idx = base + u * NT + tid;
+        if (idx < 256 * 32) *reinterpret_cast<uint2*>(s_lds + PK_CODE_BASE + idx * 8) = v[u];
+      }
+    }
+  }
+
+  const h8* const s_qm = reinterpret_cast<const h8*>(s_lds + PK_QOPS_BASE) + lane;
+  // ---- per-lane constants
+  const uint32_t copy8 = static_cast<uint32_t>(lane & 31) * 8u;
+  const uint32_t m_le1 = s <= 1 ? 0xFFFFFFFFu : 0u;
+  const uint32_t m_eq0 = s == 0 ? 0xFFFFFFFFu : 0u;
+  // P operand: slot 0 takes the hi halves of the packed (hi, lo) pairs, slot 1
+  // the lo halves.
+  const uint32_t psel = s == 0 ? 0x05040100u : 0x07060302u;
+  // P operand of lane (g, n): head n / SLOTS, tokens 4g .. 4g+3, which the score
+  // layout keeps in lanes 16 (head / HL) + 4g + r (register head % HL), r < 4.
+  const int src_lane = 16 * ((n / SLOTS) / HL) + 4 * g;
+  const bool src_k1 = HL == 2 && ((n / SLOTS) & 1) != 0;
+
+  float m_run[HL], l_run[HL];
+#pragma unroll
+  for (int k = 0; k < HL; ++k) {
+    m_run[k] = -INFINITY;
+    l_run[k] = 0.f;
+  }
+  f4 acc_o[8];
+#pragma unroll
+  for (int t = 0; t < 8; ++t) acc_o[t] = f4{0.f, 0.f, 0.f, 0.f};
+  __syncthreads();
+
+  auto process = [&](const PkPage& d, int p) {
+    // ---- scores: C[(head, slot)][token]
+    f4 accM = {0.f, 0.f, 0.f, 0.f}, accQ = {0.f, 0.f, 0.f, 0.f};
+    const uint32_t kw[4] = {d.kc.x, d.kc.y, d.kc.z, d.kc.w};
+    const uint32_t sgl = d.sg & 0x0F0F0F0Fu, sgh = (d.sg >> 4) & 0x0F0F0F0Fu;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint2 e0 = lds_u2(s_code, tab_off(kw[i >> 1], copy8, (2 * i) & 3));
+      const uint2 e1 = lds_u2(s_code, tab_off(kw[i >> 1], copy8, (2 * i + 1) & 3));
+      const h8 qmi = s_qm[i * 64];
+      accM = mfma32(qmi, h8_of(e0, e1), accM);
+      if (i < 4) {
+        const uint2 z0 = lds_u2(s_sign, tab_off(sgl, copy8, i));
+        const uint2 z1 = lds_u2(s_sign, tab_off(sgh, copy8, i));
+        if constexpr (SLOTS == 4) accQ = mfma32(qmi, h8_of(z0, z1), accQ);
+        else accQ = mfma32(qs[i], h8_of(z0, z1), accQ);
+      }
+    }
+    // pair bytes (token 4g, 4g+1) and (4g+2, 4g+3) per dimension 8n + t
+    const uint32_t x01 = (d.vc[0] & 0x0F0F0F0Fu) | ((d.vc[1] << 4) & 0xF0F0F0F0u);
+    const uint32_t z01 = ((d.vc[0] >> 4) & 0x0F0F0F0Fu) | (d.vc[1] & 0xF0F0F0F0u);
+    const uint32_t x23 = (d.vc[2] & 0x0F0F0F0Fu) | ((d.vc[3] << 4) & 0xF0F0F0F0u);
+    const uint32_t z23 = ((d.vc[2] >> 4) & 0x0F0F0F0Fu) | (d.vc[3] & 0xF0F0F0F0u);
+    const bool valid = t0 + p * FQ_BLOCK + n < t1;
+    float sc[HL];
+    if constexpr (SLOTS == 4) {
+      sc[0] = fmaf(accQ[2] + accQ[3], d.gm, (accM[0] + accM[1]) * d.kn) * cf[0];
+    } else {
+      sc[0] = fmaf(accQ[0] + accQ[1], d.gm, (accM[0] + accM[1]) * d.kn) * cf[0];
+      sc[1] = fmaf(accQ[2] + accQ[3], d.gm, (accM[2] + accM[3]) * d.kn) * cf[1];
+    }
+    // ---- online softmax: the 16 lanes of row g hold one head's 16 tokens. The
+    // running max only has to be within PK_TAU of the true one, so the page max
+    // is formed only when some score exceeds it by more than that.
+    bool grow = false;
+#pragma unroll
+    for (int k = 0; k < HL; ++k) {
+      sc[k] = valid ? sc[k] : -INFINITY;
+      grow = grow || (sc[k] > m_run[k] + PK_TAU);
+    }
+    if (__any(grow)) {
+      float al[HL];
+#pragma unroll
+      for (int k = 0; k < HL; ++k) {
+        const float m_new = fmaxf(m_run[k], row_max(sc[k]));
+        al[k] = __builtin_amdgcn_exp2f(m_run[k] - m_new);  // 0 while m_run = -inf
+        l_run[k] *= al[k];
+        m_run[k] = m_new;
+      }
+      // acc_o rows 4g .. 4g+3 are (head HL g + k, slot) pairs
+      const f4 av = HL == 1 ? f4{al[0], al[0], al[0], al[0]} : f4{al[0], al[0], al[HL - 1], al[HL - 1]};
+#pragma unroll
+      for (int t = 0; t < 8; ++t) acc_o[t] *= av;
+    }
+    uint32_t xp[HL];  // (hi, lo) fp16 pair of p * value norm, per head of this lane
+#pragma unroll
+    for (int k = 0; k < HL; ++k) {
+      const float pr = __builtin_amdgcn_exp2f(sc[k] - m_run[k]);
+      l_run[k] += pr;
+      const float pv = valid ? pr * d.vn : 0.f;
+      _Float16 ph, pl;
+      split_f16(pv, ph, pl);
+      xp[k] = h2bits(ph, pl);
+    }
+    // to the operand layout: (hi, lo) pairs of tokens 4g .. 4g+3 for head n / SLOTS
+    uint32_t y[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int addr = (src_lane + r) * 4;
+      y[r] = static_cast<uint32_t>(__builtin_amdgcn_ds_bpermute(addr, static_cast<int>(xp[0])));
+      if constexpr (HL == 2) {
+        const uint32_t y1 = static_cast<uint32_t>(__builtin_amdgcn_ds_bpermute(addr, static_cast<int>(xp[HL - 1])));
+        y[r] = src_k1 ? y1 : y[r];
+      }
+    }
+    const uint32_t y01 = __builtin_amdgcn_perm(y[1], y[0], psel);
+    const uint32_t y23 = __builtin_amdgcn_perm(y[3], y[2], psel);
+    const h8 ap = as_h8(y01 & m_le1, y01 & m_eq0, y23 & m_le1, y23 & m_eq0);
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const uint32_t w01 = (t & 1) ? z01 : x01, w23 = (t & 1) ? z23 : x23;
+      const uint2 e01 = lds_u2(s_code, tab_off(w01, copy8, t >> 1));
+      const uint2 e23 = lds_u2(s_code, tab_off(w23, copy8, t >> 1));
+      acc_o[t] = mfma32(ap, h8_of(e01, e23), acc_o[t]);
+    }
+  };
+
+  // One page per wave at a time with RING - 1 more of the same wave in flight (a
+  // register ring, unrolled so that no stage is copied).
+  for (int c0 = 0; c0 < my_pages; c0 += 64) {
+    const int cn = min(64, my_pages - c0);
+    if (c0 > 0) {
+      bt_cur = bt_chunk(c0);
+#pragma unroll
+      for (int k = 0; k < RING - 1; ++k) pk_load(a, rec_of(bt_cur, min(k, cn - 1)), n, lo, gptr, sgn_base, ring[k]);
+    }
+    for (int i = 0; i < cn; i += RING) {
+#pragma unroll
+      for (int k = 0; k < RING; ++k) {
+        const int ik = i + k;
+        pk_load(a, rec_of(bt_cur, min(ik + RING - 1, cn - 1)), n, lo, gptr, sgn_base, ring[(k + RING - 1) % RING]);
+        if (ik < cn) process(ring[k], p0 + (c0 + ik) * WAVES);
+      }
+    }
+  }
+
+  // ---- per-wave totals, then merge the waves in LDS
+#pragma unroll
+  for (int k = 0; k < HL; ++k) l_run[k] = row_sum(l_run[k]);
+  __syncthreads();  // tables are dead from here on
+  constexpr int HP = 4 * HL;  // heads per wave
+  float* s_o = reinterpret_cast<float*>(s_lds);                    // [WAVES][HP][128]
+  float* s_ml = reinterpret_cast<float*>(s_lds) + WAVES * HP * D;  // [WAVES][HP][2]
+  if (n == 0) {
+#pragma unroll
+    for (int k = 0; k < HL; ++k) {
+      s_ml[(wave * HP + HL * g + k) * 2] = m_run[k];
+      s_ml[(wave * HP + HL * g + k) * 2 + 1] = l_run[k];
+    }
+  }
+  const float unscale = 1.0f / static_cast<float>(1 << LEV_SHIFT);
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+#pragma unroll
+    for (int k = 0; k < HL; ++k)
+      s_o[(wave * HP + HL * g + k) * D + 8 * n + t] = (acc_o[t][2 * k] + acc_o[t][2 * k + 1]) * unscale;
   }
   __syncthreads();
-  float acc = 0.f;
-  for (int sp = 0; sp < S; ++sp) {
-    const float w = s_w[sp];
-    const float o = a.part_o[(base + sp) * D + tid];
-    acc = fmaf(o, w, acc);
+  constexpr float LN2 = 0.6931471805599453f;
+  for (int idx = tid; idx < G * D; idx += WAVES * 64) {
+    const int hh = idx / D, j = idx % D;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < WAVES; ++w)
+      if (s_ml[(w * HP + hh) * 2 + 1] > 0.f) M = fmaxf(M, s_ml[(w * HP + hh) * 2]);
+    float o = 0.f, L = 0.f;
+#pragma unroll
+    for (int w = 0; w < WAVES; ++w) {
+      const float lw = s_ml[(w * HP + hh) * 2 + 1];
+      if (lw > 0.f) {
+        const float f = exp2f(s_ml[(w * HP + hh) * 2] - M);
+        o = fmaf(s_o[(w * HP + hh) * D + j], f, o);
+        L = fmaf(lw, f, L);
+      }
+    }
+    const int64_t base = (static_cast<int64_t>(b) * a.hq + kvh * G + hh) * a.splits + split;
+    a.part_o[base * D + j] = o;
+    if (j == 0) {
+      a.part_ml[base * 2] = M * LN2;  // natural-log units for the merge
+      a.part_ml[base * 2 + 1] = L;
+    }
   }
-  s_o[tid] = acc * s_inv;
+}
+
+// ---------------------------------------------------------------- kernel 3
+// One work-group per (KV head, sequence):
+//  1. wave w takes heads w, w + 8: lane sp holds split sp's (max, sum), and the
+//     log-sum-exp weights exp(m_sp - M) and 1 / sum_sp l_sp w_sp go to LDS;
+//  2. thread (j, kq) adds up coordinate j of splits sp = kq, kq + 4, ... for every
+//     head (all loads of a head issued together), the four quarters are summed;
+//  3. o = Pi^T O, each thread holding a quarter of row j of Pi^T (loaded first).
+__global__ void __launch_bounds__(PQ_THREADS) merge_unrotate_kernel(DecodeArgs a) {
+  __shared__ __align__(16) float s_o[FQ_MAX_GROUP][D];
+  __shared__ __align__(16) float s_part[4][FQ_MAX_GROUP][D];
+  __shared__ float s_w[FQ_MAX_GROUP][FQ_MAX_SPLITS];
+  __shared__ float s_inv[FQ_MAX_GROUP];
+  const int kvh = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  const int j = tid & (D - 1);
+  const int kq = __builtin_amdgcn_readfirstlane(tid >> 7);
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int G = a.group, S = a.splits;
+  float4 tr[8];
+  row_quarter_load(a.pit, j, kq, tr);
+  const int64_t head0 = static_cast<int64_t>(b) * a.hq + kvh * G;
+  for (int h = wv; h < G; h += PQ_THREADS / 64) {
+    float m = -INFINITY, l = 0.f;
+    if (lane < S) {
+      const float2 x = reinterpret_cast<const float2*>(a.part_ml)[(head0 + h) * S + lane];
+      m = x.x;
+      l = x.y;
+    }
+    const float M = wave_max(l > 0.f ? m : -INFINITY);
+    const float w = (lane < S && l > 0.f) ? __expf(m - M) : 0.f;
+    float L = l * w;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) L += __shfl_xor(L, off);
+    if (lane < S) s_w[h][lane] = w;
+    if (lane == 0) s_inv[h] = L > 0.f ? 1.f / L : 0.f;
+  }
   __syncthreads();
-  float r = 0.f;
-#pragma unroll 32
-  for (int jj = 0; jj < D; ++jj) r = fmaf(a.pi[jj * D + tid], s_o[jj], r);
-  a.out[(static_cast<int64_t>(b) * a.hq + h) * D + tid] = r;
+  for (int h = 0; h < G; ++h) {
+    const float* po = a.part_o + (head0 + h) * S * D + j;
+    float acc = 0.f;
+#pragma unroll 16
+    for (int sp = kq; sp < S; sp += 4) acc = fmaf(po[sp * D], s_w[h][sp], acc);
+    s_part[kq][h][j] = acc;
+  }
+  __syncthreads();
+  for (int h = kq; h < G; h += 4)
+    s_o[h][j] = ((s_part[0][h][j] + s_part[1][h][j]) + (s_part[2][h][j] + s_part[3][h][j])) * s_inv[h];
+  __syncthreads();
+  if (G <= 4) quarter_dot<4>(tr, s_o, j, kq, G, s_part);  // o[h][j] = sum_k Pi^T[j][k] o_rot[h][k]
+  else if (G <= 8) quarter_dot<8>(tr, s_o, j, kq, G, s_part);
+  else quarter_dot<16>(tr, s_o, j, kq, G, s_part);
+  __syncthreads();
+  for (int h = kq; h < G; h += 4)
+    a.out[(head0 + h) * D + j] = (s_part[0][h][j] + s_part[1][h][j]) + (s_part[2][h][j] + s_part[3][h][j]);
 }
 
 }  // namespace
@@ -658,7 +1180,8 @@ int launch_decode(void* stream, const fq_quantizer& q, const fq_cache& c, const 
                   int q_dtype, int batch, int num_q_heads, const int32_t* block_tables,
                   int max_blocks_per_seq, const int32_t* seq_lens, int max_seq_len,
                   int num_splits, float scale, void* workspace, float* out) {
-  const DecodeWorkspace ws = decode_workspace(batch, num_q_heads, D, q.qjl_dim, num_splits);
+  const DecodeWorkspace ws =
+      decode_workspace(batch, num_q_heads, c.num_kv_heads, D, q.qjl_dim, num_splits);
   uint8_t* wb = static_cast<uint8_t*>(workspace);
   DecodeArgs a{};
   a.q = qv;
@@ -678,6 +1201,7 @@ int launch_decode(void* stream, const fq_quantizer& q, const fq_cache& c, const 
   a.qs = reinterpret_cast<float*>(wb + ws.qs);
   a.part_o = reinterpret_cast<float*>(wb + ws.part_o);
   a.part_ml = reinterpret_cast<float*>(wb + ws.part_ml);
+  a.qops = reinterpret_cast<uint4*>(wb + ws.qops);
   a.out = out;
   a.batch = batch;
   a.hq = num_q_heads;
@@ -692,22 +1216,35 @@ int launch_decode(void* stream, const fq_quantizer& q, const fq_cache& c, const 
   a.scale = scale;
   hipStream_t st = static_cast<hipStream_t>(stream);
 
-  const int nvec = batch * num_q_heads;
-  const unsigned rq_groups = static_cast<unsigned>((nvec + RQ_NV - 1) / RQ_NV);
-  if (q_dtype == FQ_BF16)
-    hipLaunchKernelGGL(rotate_queries_kernel<FQ_BF16>, dim3(rq_groups), dim3(D), 0, st, a);
-  else
-    hipLaunchKernelGGL(rotate_queries_kernel<FQ_F32>, dim3(rq_groups), dim3(D), 0, st, a);
-  dim3 grid(num_splits, c.num_kv_heads, batch);
+  // Split kernel: packed matrix-core kernel for 4-bit codes and groups of up to 8
+  // query heads; the earlier matrix-core kernel for larger groups; the vector-ALU
+  // kernel for 2-bit codes (or on request).
   const char* impl = std::getenv("FQ_DECODE_KERNEL");
   const bool valu = impl && std::strcmp(impl, "valu") == 0;
-  if (q.bits == 4 && !valu)
+  const bool v1 = impl && std::strcmp(impl, "mfma_v1") == 0;
+  const int slots = (q.bits == 4 && !valu && !v1) ? (a.group <= 4 ? 4 : a.group <= 8 ? 2 : 0) : 0;
+  const dim3 pgrid(c.num_kv_heads, batch);
+  if (q_dtype == FQ_BF16) {
+    if (slots == 4) hipLaunchKernelGGL((prepare_queries_kernel<FQ_BF16, 4>), pgrid, dim3(PQ_THREADS), 0, st, a);
+    else if (slots == 2) hipLaunchKernelGGL((prepare_queries_kernel<FQ_BF16, 2>), pgrid, dim3(PQ_THREADS), 0, st, a);
+    else hipLaunchKernelGGL((prepare_queries_kernel<FQ_BF16, 0>), pgrid, dim3(PQ_THREADS), 0, st, a);
+  } else {
+    if (slots == 4) hipLaunchKernelGGL((prepare_queries_kernel<FQ_F32, 4>), pgrid, dim3(PQ_THREADS), 0, st, a);
+    else if (slots == 2) hipLaunchKernelGGL((prepare_queries_kernel<FQ_F32, 2>), pgrid, dim3(PQ_THREADS), 0, st, a);
+    else hipLaunchKernelGGL((prepare_queries_kernel<FQ_F32, 0>), pgrid, dim3(PQ_THREADS), 0, st, a);
+  }
+  dim3 grid(num_splits, c.num_kv_heads, batch);
+  if (slots == 4)
+    hipLaunchKernelGGL((packed_decode4_kernel<4, PK4_WAVES, PK4_RING, PK4_OCC>), grid, dim3(PK4_WAVES * 64), 0, st, a);
+  else if (slots == 2)
+    hipLaunchKernelGGL((packed_decode4_kernel<2, PK2_WAVES, PK2_RING, PK2_OCC>), grid, dim3(PK2_WAVES * 64), 0, st, a);
+  else if (q.bits == 4 && !valu)
     hipLaunchKernelGGL(split_mfma4_kernel, grid, dim3(256), 0, st, a);
   else if (q.bits == 4)
     hipLaunchKernelGGL(split_attention_kernel<4>, grid, dim3(256), 0, st, a);
   else
     hipLaunchKernelGGL(split_attention_kernel<2>, grid, dim3(256), 0, st, a);
-  hipLaunchKernelGGL(merge_unrotate_kernel, dim3(num_q_heads, batch), dim3(D), 0, st, a);
+  hipLaunchKernelGGL(merge_unrotate_kernel, pgrid, dim3(PQ_THREADS), 0, st, a);
   return static_cast<int>(hipGetLastError());
 }
 

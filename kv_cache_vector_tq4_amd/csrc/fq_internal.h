@@ -20,11 +20,16 @@ struct DecodeWorkspace {
   size_t qs;      // f32 [B][Hq][m]        S q~ (when qjl_dim > 0)
   size_t part_o;  // f32 [B][Hq][splits][d] unnormalised o_rot per split
   size_t part_ml; // f32 [B][Hq][splits][2] running max and sum per split
+  size_t qops;    // [B][Hkv][FQ_QOPS][64 lanes] x 16 B: per-lane matrix-core query operands
   size_t total;
 };
 
-DecodeWorkspace decode_workspace(int batch, int num_q_heads, int head_dim, int qjl_dim,
-                                 int num_splits);
+// Query operands per (sequence, KV head): 8 code-product B registers, 4 sign-product
+// B registers and one register holding the per-lane score factor.
+#define FQ_QOPS 13
+
+DecodeWorkspace decode_workspace(int batch, int num_q_heads, int num_kv_heads, int head_dim,
+                                 int qjl_dim, int num_splits);
 int auto_splits(int batch, int num_kv_heads, int max_seq_len);
 
 // Launchers: arguments already validated; return hipSuccess or the launch error.
