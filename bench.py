@@ -3,7 +3,9 @@
 Workload (default): Llama-3-8B-shaped attention, 32 layers, batch 32, context
 lengths uniform in [3072, 4096], 32 query / 8 KV heads, head_dim 128, TQ4 keys
 (4-bit Lloyd-Max + 1-bit QJL) and values (4-bit), 16-token pages with random
-non-contiguous block tables, 4 decode splits. Every layer has its own
+non-contiguous block tables. The decode split count is the library's choice
+(one round of work-groups: 2 splits at this shape; --splits 4 runs the pages'
+4-way split instead). Every layer has its own
 compressed cache (5.2 GB in all, far beyond the 256 MB last-level cache), filled
 by compressing the whole synthetic context before timing.
 
@@ -16,7 +18,7 @@ Also reported: the prefill compress rate (Mvectors/s) measured while filling
 the caches, the roofline of the dominant kernel (the decode) and the CPU oracle
 timed on a bounded sample of the same work.
 
-    python bench.py [--steps K] [--warmup W] [--gpus 1] [--layers 32] [--no-cpu]
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--layers 32] [--splits S] [--no-cpu]
 """
 import argparse
 import json
@@ -59,6 +61,8 @@ def parse():
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--layers", type=int, default=32)
+    p.add_argument("--splits", type=int, default=0,
+                   help="decode splits per (sequence, KV head); 0 = the library's choice")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--no-graph", action="store_true", help="time eager launches instead of a HIP graph")
@@ -217,7 +221,7 @@ def main():
     B, Hq, Hkv, d = w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim
     lens = np.asarray(w.seq_lens, np.int32)
     max_len = int(lens.max())
-    splits = w.num_splits
+    splits = args.splits if args.splits > 0 else fq.auto_splits(B, Hkv, max_len)
 
     qz = fq.Quantizer(4, d, fq.ROT_HAAR, 1, 2, 128, device=dev)
     bt_np, nblocks = synth.block_tables(1234, w.seq_lens, w.capacity_tokens)
@@ -305,15 +309,43 @@ def main():
     elapsed = time.perf_counter() - t0
     ms_per_step = elapsed * 1000.0 / args.steps
 
-    # per-launch durations of the dominant kernel: HIP events around each decode call,
-    # on the stream the library launches on, over K eager steps
+    # per-launch durations of the dominant call: HIP events around each decode call,
+    # on the stream the library launches on, over K eager steps (includes the host's
+    # launch gaps between the call's kernels) ...
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     for _ in range(args.steps):
         step(True)
     torch.cuda.synchronize()
     ms_eager = (time.perf_counter() - t1) * 1000.0 / args.steps
-    dec_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    dec_ms_eager = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    # ... and from HIP events around replays of a graph holding only the layers' decode
+    # calls (device time of the call as the stack runs it)
+    dec_ms = dec_ms_eager
+    if graph is not None:
+        def decodes():
+            for layer in range(w.layers):
+                fq.decode(qz, caches[layer], qs[layer], bt, lens_t, max_len, num_splits=splits, workspace=ws,
+                          out=outs[layer])
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        dgraph = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(side):
+            with torch.cuda.graph(dgraph, stream=side):
+                decodes()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        dgraph.replay()
+        torch.cuda.synchronize()
+        pairs = []
+        for _ in range(args.steps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            dgraph.replay()
+            e1.record(stream)
+            pairs.append((e0, e1))
+        torch.cuda.synchronize()
+        dec_ms = float(np.mean([a.elapsed_time(b) for a, b in pairs])) / w.layers
 
     bpt = caches[0].bytes_per_token_head()  # 156 B at 4 bits with QJL keys
     dec_bytes = ntok * Hkv * bpt
@@ -344,7 +376,7 @@ def main():
             "cache_bytes_per_layer": dec_bytes, "bytes_per_token_head": bpt,
         },
         "roofline": {
-            "kernel": "fq_decode_attention (rotate_queries + split_attention + merge_unrotate)",
+            "kernel": "fq_decode_attention (prepare_queries + packed split attention + merge_unrotate)",
             "bound": "hbm",
             "achieved": achieved,
             "peak": HBM_PEAK_GBS,
@@ -353,6 +385,9 @@ def main():
             "traffic": measured_traffic(),
             "algorithmic_bytes_per_launch": dec_bytes,
             "avg_launch_ms": dec_ms,
+            "timing": "HIP events around graph replays of the %d layers' decode calls" % w.layers
+                      if graph is not None else "HIP events around eager decode calls",
+            "avg_launch_ms_eager": dec_ms_eager,
         },
         "compress": {
             "mvec_per_s": comp_vec / (comp_med_ms * 1e-3) / 1e6,

@@ -542,12 +542,187 @@ __global__ void __launch_bounds__(64) compress_direct_kernel(CompressArgs a) {
     compress_tile<BITS, DT, false, true>(a, 1, blockIdx.x, tid, ops, ops, s_qt, s_qmap[0], s_qmap[1]);
 }
 
+// One 32-vector tile per work-group of 4 waves, wave T producing output rows
+// 64h + 16T .. +15 of each lane's vectors (row tile T of compress_tile): a
+// quarter of the products and of the fragment reads per wave, for inputs too
+// small to fill the GPU with one wave per tile. The residual's fp16 hi / lo
+// fragments and |r|^2 partial sums cross the waves through LDS for the QJL
+// product.
+template <int BITS, int DT, bool KEY>
+__device__ __forceinline__ void compress_quarter(const CompressArgs& a, int kind, int64_t tile, int lane, int T,
+                                                 const uint4* __restrict__ fpi, const uint4* __restrict__ fsm,
+                                                 const QCell* __restrict__ qt, float inv_w, float off,
+                                                 uint4* s_rh, uint4* s_rl, float* s_rr) {
+  const int v = lane & 31, h = lane >> 5;
+  const int64_t nvec = a.ntok * a.hkv;
+  const int esz = DT == FQ_BF16 ? 2 : 4;
+  const uint8_t* src = static_cast<const uint8_t*>(a.src[kind]);
+  const int64_t vid = tile * CT_VEC + v;
+  const bool valid = vid < nvec;
+  const int64_t t = valid ? vid / a.hkv : 0;
+  const int hd = valid ? static_cast<int>(vid - t * a.hkv) : 0;
+  const int64_t slot = valid ? a.slots[t] : -1;
+  const uint8_t* base = src + ((t * a.tstride + hd * a.hstride) * esz) + 64 * h * esz;
+
+  b8 xb[8];
+  b8 xl[DT == FQ_BF16 ? 1 : 8];
+  float ss = 0.f;
+  if constexpr (DT == FQ_BF16) {
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      uint4 u = valid ? reinterpret_cast<const uint4*>(base)[s] : make_uint4(0, 0, 0, 0);
+      const uint32_t w4[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float lo = __uint_as_float(w4[q] << 16), hi = __uint_as_float(w4[q] & 0xffff0000u);
+        ss = fmaf(lo, lo, ss);
+        ss = fmaf(hi, hi, ss);
+      }
+      xb[s] = __builtin_bit_cast(b8, u);
+    }
+  } else {
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      float4 f0 = valid ? reinterpret_cast<const float4*>(base)[2 * s] : make_float4(0, 0, 0, 0);
+      float4 f1 = valid ? reinterpret_cast<const float4*>(base)[2 * s + 1] : make_float4(0, 0, 0, 0);
+      const float xs[8] = {f0.x, f0.y, f0.z, f0.w, f1.x, f1.y, f1.z, f1.w};
+      uint32_t hi[8], lo[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        ss = fmaf(xs[e], xs[e], ss);
+        split_bf16(xs[e], hi[e], lo[e]);
+      }
+      xb[s] = __builtin_bit_cast(b8, make_uint4(hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16), hi[4] | (hi[5] << 16), hi[6] | (hi[7] << 16)));
+      xl[s] = __builtin_bit_cast(b8, make_uint4(lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16), lo[4] | (lo[5] << 16), lo[6] | (lo[7] << 16)));
+    }
+  }
+  ss += __shfl_xor(ss, 32);
+  const float n = sqrtf(ss);
+  const float inv = n > 0.f ? 1.0f / n : 0.f;
+
+  // ---- row tile T of the rotation
+  f16v acc = f16v{};
+#pragma unroll
+  for (int s = 0; s < 8; ++s) {
+    const b8 ah = __builtin_bit_cast(b8, fpi[(T * 8 + s) * 64 + lane]);
+    const b8 al = __builtin_bit_cast(b8, fpi[(32 + T * 8 + s) * 64 + lane]);
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, xb[s], acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, xb[s], acc, 0, 0, 0);
+    if constexpr (DT != FQ_BF16) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, xl[s], acc, 0, 0, 0);
+  }
+  // acc[vv] = (Pi x / |x|)[64h + 16T + vv]
+#pragma unroll
+  for (int vv = 0; vv < 16; ++vv) acc[vv] *= inv;
+
+  const int64_t rec = ((slot >> 4) * a.hkv + hd) * FQ_BLOCK + (slot & 15);
+  const bool store = slot >= 0;
+  if (a.dbg_y && store) {
+    float4* dy = reinterpret_cast<float4*>(a.dbg_y + ((kind * a.ntok + t) * a.hkv + hd) * D + 64 * h + 16 * T);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) dy[q] = make_float4(acc[4 * q], acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]);
+  }
+
+  // ---- boundary search and packing of the 16 coordinates; keys keep the residual
+  constexpr int PER = 32 / BITS;
+  constexpr int NW = 16 / PER;  // code words per lane and row tile
+  uint32_t words[NW];
+#pragma unroll
+  for (int w = 0; w < NW; ++w) words[w] = 0;
+#pragma unroll
+  for (int vv = 0; vv < 16; ++vv) {
+    const float y = acc[vv];
+    int c = static_cast<int>(floorf(fmaf(y, inv_w, off)));
+    c = min(max(c, 0), QT_CELLS - 1);
+    const QCell q = qt[c];
+    const bool gt = q.b < y;
+    const uint32_t idx = q.count + (gt ? 1u : 0u);
+    words[vv / PER] |= idx << (BITS * (vv % PER));
+    if constexpr (KEY) acc[vv] = y - (gt ? q.c_hi : q.c_lo);
+  }
+  if (store) {
+    uint8_t* cd = a.codes[kind] + rec * (D * BITS / 8) + (64 * h + 16 * T) * BITS / 8;
+    if constexpr (NW == 2) *reinterpret_cast<uint2*>(cd) = make_uint2(words[0], words[1]);
+    else *reinterpret_cast<uint32_t*>(cd) = words[0];
+    if (h == 0 && T == 0) a.norm[kind][rec] = n;
+  }
+
+  if constexpr (KEY) {
+    if (!a.qjl_on) return;  // uniform over the work-group
+    float rr = 0.f;
+#pragma unroll
+    for (int vv = 0; vv < 16; ++vv) rr = fmaf(acc[vv], acc[vv], rr);
+    s_rr[T * 64 + lane] = rr;
+    // k-steps 2T and 2T + 1 of the QJL product cover coordinates 64h + 8s + e
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      uint32_t hi[8], lo[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) split_f16b(acc[8 * q + e], hi[e], lo[e]);
+      s_rh[(2 * T + q) * 64 + lane] = make_uint4(hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16), hi[4] | (hi[5] << 16), hi[6] | (hi[7] << 16));
+      s_rl[(2 * T + q) * 64 + lane] = make_uint4(lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16), lo[4] | (lo[5] << 16), lo[6] | (lo[7] << 16));
+    }
+    __syncthreads();
+    f16v pacc = f16v{};
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      const hh8 rh = __builtin_bit_cast(hh8, s_rh[s * 64 + lane]);
+      const hh8 rl = __builtin_bit_cast(hh8, s_rl[s * 64 + lane]);
+      const hh8 ah = __builtin_bit_cast(hh8, fsm[(T * 8 + s) * 64 + lane]);
+      const hh8 al = __builtin_bit_cast(hh8, fsm[(32 + T * 8 + s) * 64 + lane]);
+      pacc = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah, rh, pacc, 0, 0, 0);
+      pacc = __builtin_amdgcn_mfma_f32_32x32x16_f16(al, rh, pacc, 0, 0, 0);
+      pacc = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah, rl, pacc, 0, 0, 0);
+    }
+    // pacc[vv] = p[64h + 16T + vv]
+    uint32_t sg = 0u;
+#pragma unroll
+    for (int vv = 0; vv < 16; ++vv) sg |= (pacc[vv] >= 0.f ? 1u : 0u) << vv;
+    float rr_all = (s_rr[lane] + s_rr[64 + lane]) + (s_rr[128 + lane] + s_rr[192 + lane]);
+    rr_all += __shfl_xor(rr_all, 32);
+    if (store) {
+      *reinterpret_cast<uint16_t*>(a.qjl + rec * (D / 8) + 8 * h + 2 * T) = static_cast<uint16_t>(sg);
+      if (h == 0 && T == 0) a.gamma[rec] = n * sqrtf(rr_all);
+      if (a.dbg_p) {
+        float4* dp = reinterpret_cast<float4*>(a.dbg_p + (t * a.hkv + hd) * D + 64 * h + 16 * T);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) dp[q] = make_float4(pacc[4 * q], pacc[4 * q + 1], pacc[4 * q + 2], pacc[4 * q + 3]);
+      }
+    }
+  }
+}
+
+template <int BITS, int DT>
+__global__ void __launch_bounds__(256) compress_split_kernel(CompressArgs a) {
+  __shared__ QCell s_qt[QT_CELLS];
+  __shared__ float s_qmap[2];
+  __shared__ float s_bl[32];
+  __shared__ uint4 s_rh[8 * 64], s_rl[8 * 64];
+  __shared__ float s_rr[4 * 64];
+  const int tid = threadIdx.x;
+  build_qtable<BITS>(a, s_qt, s_qmap, s_bl, tid, 256);
+  __syncthreads();
+  const int kind = blockIdx.y;
+  if (!a.src[kind]) return;  // uniform over the work-group
+  const uint4* ops = static_cast<const uint4*>(a.mfma_ops);
+  const int T = __builtin_amdgcn_readfirstlane(tid >> 6);
+  if (kind == 0)
+    compress_quarter<BITS, DT, true>(a, 0, blockIdx.x, tid & 63, T, ops, ops + 2 * FRAG_U4, s_qt, s_qmap[0],
+                                     s_qmap[1], s_rh, s_rl, s_rr);
+  else
+    compress_quarter<BITS, DT, false>(a, 1, blockIdx.x, tid & 63, T, ops, ops, s_qt, s_qmap[0], s_qmap[1], s_rh,
+                                      s_rl, s_rr);
+}
+
 template <int BITS, int DT>
 int launch_mfma(hipStream_t st, const CompressArgs& a) {
   const int64_t nvec = a.ntok * a.hkv;
   const int64_t tiles = (nvec + CT_VEC - 1) / CT_VEC;
   if (a.mfma_ops && tiles <= 1024) {
-    hipLaunchKernelGGL((compress_direct_kernel<BITS, DT>), dim3(static_cast<unsigned>(tiles), 2), dim3(64), 0, st, a);
+    const char* impl = std::getenv("FQ_COMPRESS_KERNEL");
+    if (impl && std::strcmp(impl, "direct") == 0)
+      hipLaunchKernelGGL((compress_direct_kernel<BITS, DT>), dim3(static_cast<unsigned>(tiles), 2), dim3(64), 0, st, a);
+    else
+      hipLaunchKernelGGL((compress_split_kernel<BITS, DT>), dim3(static_cast<unsigned>(tiles), 2), dim3(256), 0, st, a);
     return static_cast<int>(hipGetLastError());
   }
   if (a.src[0]) {

@@ -54,7 +54,7 @@ struct DecodeArgs {
   float* part_ml;  // [B][Hq][S][2]
   uint4* qops;     // [B][Hkv][FQ_QOPS][64]
   float* out;      // [B][Hq][d]
-  int batch, hq, hkv, group, splits, chunk, max_blocks, qjl_on;
+  int batch, hq, hkv, group, splits, chunk, max_blocks, qjl_on, q_bf16;
   float scale;
 };
 
@@ -115,6 +115,64 @@ __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
   return v;
+}
+
+// Matrix-core query operand op (0 .. FQ_QOPS-1) of lane l of the packed split
+// kernel, from q~ (r) and q_s (sq) of the G query heads (rows of D floats) and
+// their per-head maxima |q~| (mq) and |q_s| (ms).
+//   op 0..7   code-product operand of k-step op; op 0..3 also the sign-product
+//             operand when SLOTS = 4 (slots 2 / 3);
+//   op 8..11  SLOTS = 2: sign-product operand of k-step op - 8;
+//   op 12     the score factor of the lane's head in .x.
+// One power of two per head puts max |q~| in [128, 256); q_s takes that power
+// times QJL_R so that both accumulators share the score factor, lowered if q_s
+// would exceed 2^15.
+template <int SLOTS>
+__device__ uint4 query_operand(int op, int l, int G, const float* r, const float* sq, const float* mq,
+                               const float* ms, float scale) {
+  const int g = l >> 4, n = l & 15, h = n / SLOTS, s = n % SLOTS;
+  uint4 u = make_uint4(0u, 0u, 0u, 0u);
+  if (h >= G) return u;
+  int ex = 0, eq = 0, es = 0;
+  const float mqh = mq[h], msh = ms[h];
+  if (mqh > 0.f) { frexpf(mqh, &ex); eq = 8 - ex; }
+  if (msh > 0.f) { frexpf(msh * QJL_R, &ex); es = 15 - ex; }
+  const int e_use = mqh > 0.f ? (msh > 0.f ? min(eq, es) : eq) : (msh > 0.f ? es : 0);
+  const float qscale = ldexpf(1.f, e_use), sscale = qscale * QJL_R;
+  auto split_pair = [](float x0, float x1, uint32_t& hi, uint32_t& lo) {
+    _Float16 h0, l0, h1, l1;
+    split_f16(x0, h0, l0);
+    split_f16(x1, h1, l1);
+    hi = h2bits(h0, h1);
+    lo = h2bits(l0, l1);
+  };
+  auto signs8 = [&](int i, bool want_lo) {  // q_s entries 32g + 8i .. +7
+    uint32_t w[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      uint32_t hi, lo;
+      const float* x = sq + h * D + 32 * g + 8 * i + 2 * k;
+      split_pair(x[0] * sscale, x[1] * sscale, hi, lo);
+      w[k] = want_lo ? lo : hi;
+    }
+    return make_uint4(w[0], w[1], w[2], w[3]);
+  };
+  if (op < 8) {
+    if (s < 2) {  // q~ entries 32g + 4 op .. +3
+      uint32_t h01, l01, h23, l23;
+      const float* x = r + h * D + 32 * g + 4 * op;
+      split_pair(x[0] * qscale, x[1] * qscale, h01, l01);
+      split_pair(x[2] * qscale, x[3] * qscale, h23, l23);
+      u = s == 0 ? make_uint4(h01, h01, h23, h23) : make_uint4(l01, 0u, l23, 0u);
+    } else if (op < 4) {
+      u = signs8(op, s == 3);
+    }
+  } else if (op < 12) {
+    if (SLOTS == 2) u = signs8(op - 8, s == 1);
+  } else {
+    u = make_uint4(__float_as_uint(scale * LOG2E_F / (qscale * 256.0f)), 0u, 0u, 0u);
+  }
+  return u;
 }
 
 constexpr int PQ_THREADS = 512;  // thread = (coordinate j, k-quarter kq)
@@ -208,61 +266,16 @@ __global__ void __launch_bounds__(PQ_THREADS) prepare_queries_kernel(DecodeArgs 
     }
   }
   __syncthreads();
-  uint4* ops = a.qops + (static_cast<int64_t>(b) * a.hkv + kvh) * (FQ_QOPS * 64);
-  for (int idx = tid; idx < FQ_QOPS * 64; idx += PQ_THREADS) {
-    const int op = idx >> 6, l = idx & 63;
-    constexpr int SL = SLOTS > 0 ? SLOTS : 1;
-    const int g = l >> 4, n = l & 15, h = n / SL, s = n % SL;
-    uint4 u = make_uint4(0u, 0u, 0u, 0u);
-    if (h < G) {
-      // One power of two per head puts max |q~| in [128, 256); q_s takes that power
-      // times QJL_R so that both accumulators share the score factor, lowered if
-      // q_s would exceed 2^15.
-      const float mq = fmaxf(s_mx[0][h][0], s_mx[0][h][1]);
-      const float msv = fmaxf(s_mx[1][h][0], s_mx[1][h][1]);
-      int ex = 0, e_use = 0, eq = 0, es = 0;
-      if (mq > 0.f) { frexpf(mq, &ex); eq = 8 - ex; }
-      if (msv > 0.f) { frexpf(msv * QJL_R, &ex); es = 15 - ex; }
-      e_use = mq > 0.f ? (msv > 0.f ? min(eq, es) : eq) : (msv > 0.f ? es : 0);
-      const float qscale = ldexpf(1.f, e_use), sscale = qscale * QJL_R;
-      auto split_pair = [](float x0, float x1, uint32_t& hi, uint32_t& lo) {
-        _Float16 h0, l0, h1, l1;
-        split_f16(x0, h0, l0);
-        split_f16(x1, h1, l1);
-        hi = h2bits(h0, h1);
-        lo = h2bits(l0, l1);
-      };
-      auto signs8 = [&](int i, bool want_lo) {  // q_s entries 32g + 8i .. +7
-        uint32_t w[4];
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          uint32_t hi, lo;
-          split_pair(s_s[h][32 * g + 8 * i + 2 * k] * sscale, s_s[h][32 * g + 8 * i + 2 * k + 1] * sscale,
-                     hi, lo);
-          w[k] = want_lo ? lo : hi;
-        }
-        return make_uint4(w[0], w[1], w[2], w[3]);
-      };
-      if (op < 8) {
-        const int i = op;
-        if (s < 2) {  // q~ entries 32g + 4i .. +3
-          uint32_t h01, l01, h23, l23;
-          const float* r = &s_r[h][32 * g + 4 * i];
-          split_pair(r[0] * qscale, r[1] * qscale, h01, l01);
-          split_pair(r[2] * qscale, r[3] * qscale, h23, l23);
-          u = s == 0 ? make_uint4(h01, h01, h23, h23) : make_uint4(l01, 0u, l23, 0u);
-        } else if (i < 4) {  // SLOTS 4 only: sign operands share these registers
-          u = signs8(i, s == 3);
-        }
-      } else if (op < 12) {
-        if (SLOTS == 2) u = signs8(op - 8, s == 1);
-      } else {
-        const float cfac = a.scale * LOG2E_F / (qscale * 256.0f);
-        u = make_uint4(__float_as_uint(cfac), 0u, 0u, 0u);
-      }
-    }
-    ops[idx] = u;
+  __shared__ float s_mq[FQ_MAX_GROUP], s_ms[FQ_MAX_GROUP];
+  if (tid < G) {
+    s_mq[tid] = fmaxf(s_mx[0][tid][0], s_mx[0][tid][1]);
+    s_ms[tid] = fmaxf(s_mx[1][tid][0], s_mx[1][tid][1]);
   }
+  __syncthreads();
+  uint4* ops = a.qops + (static_cast<int64_t>(b) * a.hkv + kvh) * (FQ_QOPS * 64);
+  constexpr int SL = SLOTS > 0 ? SLOTS : 1;
+  for (int idx = tid; idx < FQ_QOPS * 64; idx += PQ_THREADS)
+    ops[idx] = query_operand<SL>(idx >> 6, idx & 63, G, &s_r[0][0], &s_s[0][0], s_mq, s_ms, a.scale);
 }
 
 // ---------------------------------------------------------------- kernel 2
@@ -887,11 +900,10 @@ __global__ void __launch_bounds__(WAVES * 64, OCC) packed_decode4_kernel(DecodeA
   // operands (shared by every wave) are read from LDS at each step.
   h8 qs[4];  // SLOTS 2: sign-product A operands
   float cf[HL];  // score factor of this lane's head(s) in the score layout
-  const uint4* const ops = a.qops + (static_cast<int64_t>(b) * a.hkv + kvh) * (FQ_QOPS * 64);
-  // operand idx / 64 of lane idx % 64 goes to LDS entry idx
-  for (int idx = tid; idx < 8 * 64; idx += WAVES * 64)
-    reinterpret_cast<uint4*>(s_lds + PK_QOPS_BASE)[idx] = ops[idx];
   {
+    const uint4* const ops = a.qops + (static_cast<int64_t>(b) * a.hkv + kvh) * (FQ_QOPS * 64);
+    for (int idx = tid; idx < 8 * 64; idx += WAVES * 64)
+      reinterpret_cast<uint4*>(s_lds + PK_QOPS_BASE)[idx] = ops[idx];
     if constexpr (SLOTS == 2) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) qs[i] = __builtin_bit_cast(h8, ops[(8 + i) * 64 + lane]);
@@ -1213,6 +1225,7 @@ int launch_decode(void* stream, const fq_quantizer& q, const fq_cache& c, const 
   if (a.chunk == 0) a.chunk = FQ_BLOCK;
   a.max_blocks = max_blocks_per_seq;
   a.qjl_on = c.qjl_dim > 0 ? 1 : 0;
+  a.q_bf16 = q_dtype == FQ_BF16 ? 1 : 0;
   a.scale = scale;
   hipStream_t st = static_cast<hipStream_t>(stream);
 
