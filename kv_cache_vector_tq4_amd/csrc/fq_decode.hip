@@ -177,19 +177,17 @@ __device__ uint4 query_operand(int op, int l, int G, const float* r, const float
 
 constexpr int PQ_THREADS = 512;  // thread = (coordinate j, k-quarter kq)
 
-// Row j of a 128 x 128 fp32 matrix restricted to k = 32 kq .. 32 kq + 31: eight
-// float4, all requested together at kernel start.
-__device__ __forceinline__ void row_quarter_load(const float* m, int j, int kq, float4 (&x)[8]) {
-  const float4* src = reinterpret_cast<const float4*>(m) + j * (D / 4) + 8 * kq;
+// Column j of a 128 x 128 fp32 row-major matrix M restricted to rows 32 kq ..
+// 32 kq + 31 (x[i] = M[32 kq + i][j]): 32 loads, each of which reads 256
+// contiguous bytes across the 64 lanes of a wave.
+__device__ __forceinline__ void col_quarter_load(const float* m, int j, int kq, float (&x)[32]) {
 #pragma unroll
-  for (int i = 0; i < 8; ++i) x[i] = src[i];
+  for (int i = 0; i < 32; ++i) x[i] = m[(32 * kq + i) * D + j];
 }
 
-// s_part[kq][h][j] = sum over k in quarter kq of row[k] vec[h][k], for h < G; then
-// out[h][j] = sum over the four quarters (threads of quarter kq finish heads
-// kq, kq + 4, ...).
+// s_part[kq][h][j] = sum over i < 32 of col[i] vec[h][32 kq + i], for h < G
 template <int GM>
-__device__ __forceinline__ void quarter_dot(const float4 (&row)[8], const float (*vec)[D], int j, int kq,
+__device__ __forceinline__ void quarter_dot(const float (&col)[32], const float (*vec)[D], int j, int kq,
                                             int G, float (*s_part)[FQ_MAX_GROUP][D]) {
 #pragma unroll
   for (int h = 0; h < GM; ++h) {
@@ -198,12 +196,102 @@ __device__ __forceinline__ void quarter_dot(const float4 (&row)[8], const float 
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const float4 x = *reinterpret_cast<const float4*>(&vec[h][32 * kq + 4 * i]);
-        acc = fmaf(row[i].x, x.x, fmaf(row[i].y, x.y, fmaf(row[i].z, x.z, fmaf(row[i].w, x.w, acc))));
+        acc = fmaf(col[4 * i], x.x, fmaf(col[4 * i + 1], x.y, fmaf(col[4 * i + 2], x.z, fmaf(col[4 * i + 3], x.w, acc))));
       }
       s_part[kq][h][j] = acc;
     }
   }
 }
+
+// KP-way versions of the above (rows kp * D/KP .. of column j).
+template <int KP>
+__device__ __forceinline__ void col_part_load(const float* m, int j, int kp, float (&x)[D / KP]) {
+#pragma unroll
+  for (int i = 0; i < D / KP; ++i) x[i] = m[(kp * (D / KP) + i) * D + j];
+}
+template <int GM, int KP>
+__device__ __forceinline__ void part_dot(const float (&col)[D / KP], const float* vec, int j, int kp, int G,
+                                         float* s_part) {
+#pragma unroll
+  for (int h = 0; h < GM; ++h) {
+    if (h < G) {
+      float acc = 0.f;
+#pragma unroll
+      for (int i = 0; i < D / KP / 4; ++i) {
+        const float4 x = *reinterpret_cast<const float4*>(vec + h * D + kp * (D / KP) + 4 * i);
+        acc = fmaf(col[4 * i], x.x, fmaf(col[4 * i + 1], x.y, fmaf(col[4 * i + 2], x.z, fmaf(col[4 * i + 3], x.w, acc))));
+      }
+      s_part[(kp * FQ_MAX_GROUP + h) * D + j] = acc;
+    }
+  }
+}
+
+// Log-sum-exp merge of the splits of one (KV head, sequence) and the output
+// rotation, by a work-group of NT threads (thread = (coordinate j, k-part kp)),
+// with lds >= (17 + NT / D * 16) * D + 16 * FQ_MAX_SPLITS + 16 floats:
+//  1. wave w takes heads w, w + NT/64: lane sp holds split sp's (max, sum); the
+//     weights exp(m_sp - M) and 1 / sum_sp l_sp w_sp go to LDS;
+//  2. thread (j, kp) adds up coordinate j of splits sp = kp, kp + KP, ... for every
+//     head; the parts are summed;
+//  3. o = Pi^T O = sum_k Pi[k][j] o_rot[k], column j of Pi loaded first.
+template <int NT>
+__device__ __forceinline__ void merge_group(const DecodeArgs& a, int kvh, int b, int tid, float* lds) {
+  constexpr int KP = NT / D;
+  float* const s_o = lds;                                       // [16][D]
+  float* const s_part = s_o + FQ_MAX_GROUP * D;                 // [KP][16][D]
+  float* const s_w = s_part + KP * FQ_MAX_GROUP * D;            // [16][FQ_MAX_SPLITS]
+  float* const s_inv = s_w + FQ_MAX_GROUP * FQ_MAX_SPLITS;      // [16]
+  const int j = tid & (D - 1);
+  const int kp = __builtin_amdgcn_readfirstlane(tid / D);
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int G = a.group, S = a.splits;
+  float pc[D / KP];
+  col_part_load<KP>(a.pi, j, kp, pc);
+  const int64_t head0 = static_cast<int64_t>(b) * a.hq + kvh * G;
+  for (int h = wv; h < G; h += NT / 64) {
+    float m = -INFINITY, l = 0.f;
+    if (lane < S) {
+      const float2 x = reinterpret_cast<const float2*>(a.part_ml)[(head0 + h) * S + lane];
+      m = x.x;
+      l = x.y;
+    }
+    const float M = wave_max(l > 0.f ? m : -INFINITY);
+    const float w = (lane < S && l > 0.f) ? __expf(m - M) : 0.f;
+    float L = l * w;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) L += __shfl_xor(L, off);
+    if (lane < S) s_w[h * FQ_MAX_SPLITS + lane] = w;
+    if (lane == 0) s_inv[h] = L > 0.f ? 1.f / L : 0.f;
+  }
+  __syncthreads();
+  for (int h = 0; h < G; ++h) {
+    const float* po = a.part_o + (head0 + h) * S * D + j;
+    float acc = 0.f;
+#pragma unroll 16
+    for (int sp = kp; sp < S; sp += KP) acc = fmaf(po[sp * D], s_w[h * FQ_MAX_SPLITS + sp], acc);
+    s_part[(kp * FQ_MAX_GROUP + h) * D + j] = acc;
+  }
+  __syncthreads();
+  for (int h = kp; h < G; h += KP) {
+    float v = 0.f;
+#pragma unroll
+    for (int k = 0; k < KP; ++k) v += s_part[(k * FQ_MAX_GROUP + h) * D + j];
+    s_o[h * D + j] = v * s_inv[h];
+  }
+  __syncthreads();
+  if (G <= 4) part_dot<4, KP>(pc, s_o, j, kp, G, s_part);
+  else if (G <= 8) part_dot<8, KP>(pc, s_o, j, kp, G, s_part);
+  else part_dot<16, KP>(pc, s_o, j, kp, G, s_part);
+  __syncthreads();
+  for (int h = kp; h < G; h += KP) {
+    float v = 0.f;
+#pragma unroll
+    for (int k = 0; k < KP; ++k) v += s_part[(k * FQ_MAX_GROUP + h) * D + j];
+    a.out[(head0 + h) * D + j] = v;
+  }
+}
+
+constexpr int ST_STRIDE = D + 1;  // transposed matrix in LDS: [k][j], padded rows
 
 template <int DT, int SLOTS>
 __global__ void __launch_bounds__(PQ_THREADS) prepare_queries_kernel(DecodeArgs a) {
@@ -211,6 +299,7 @@ __global__ void __launch_bounds__(PQ_THREADS) prepare_queries_kernel(DecodeArgs 
   __shared__ __align__(16) float s_r[FQ_MAX_GROUP][D];
   __shared__ __align__(16) float s_s[FQ_MAX_GROUP][D];
   __shared__ __align__(16) float s_part[4][FQ_MAX_GROUP][D];
+  __shared__ float s_st[D * ST_STRIDE];       // S transposed: s_st[k * ST_STRIDE + j] = S[j][k]
   __shared__ float s_mx[2][FQ_MAX_GROUP][2];  // [q~, q_s][head][row half]
   const int kvh = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
   const int j = tid & (D - 1);
@@ -218,9 +307,16 @@ __global__ void __launch_bounds__(PQ_THREADS) prepare_queries_kernel(DecodeArgs 
   const int G = a.group;
   const bool qjl = a.qjl_on != 0;
   const int64_t row0 = (static_cast<int64_t>(b) * a.hq + kvh * G) * D;
-  float4 pr[8], sr[8];
-  row_quarter_load(a.pi, j, kq, pr);
-  row_quarter_load(qjl ? a.smat : a.pi, j, kq, sr);  // S is unused without QJL fields
+  // q~[h][j] = sum_k Pi[j][k] q[h][k] = sum_k Pi^T[k][j] q[h][k]: column j of Pi^T
+  float pc[32];
+  col_quarter_load(a.pit, j, kq, pc);
+  // S arrives in one coalesced pass (float4 number tid + 512 i) and is transposed in LDS
+  float4 sv[8];
+  {
+    const float4* src = reinterpret_cast<const float4*>(qjl ? a.smat : a.pit);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) sv[i] = src[tid + PQ_THREADS * i];
+  }
   for (int h = kq; h < G; h += 4) {
     const int64_t off = row0 + h * D + j;
     if constexpr (DT == FQ_BF16)
@@ -228,13 +324,22 @@ __global__ void __launch_bounds__(PQ_THREADS) prepare_queries_kernel(DecodeArgs 
     else
       s_q[h][j] = static_cast<const float*>(a.q)[off];
   }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int f = tid + PQ_THREADS * i;  // S[r][4c .. 4c+3]
+    const int r = f >> 5, c4 = 4 * (f & 31);
+    s_st[(c4 + 0) * ST_STRIDE + r] = sv[i].x;
+    s_st[(c4 + 1) * ST_STRIDE + r] = sv[i].y;
+    s_st[(c4 + 2) * ST_STRIDE + r] = sv[i].z;
+    s_st[(c4 + 3) * ST_STRIDE + r] = sv[i].w;
+  }
   __syncthreads();
-  auto dot = [&](const float4 (&row)[8], const float (*vec)[D]) {
-    if (G <= 4) quarter_dot<4>(row, vec, j, kq, G, s_part);
-    else if (G <= 8) quarter_dot<8>(row, vec, j, kq, G, s_part);
-    else quarter_dot<16>(row, vec, j, kq, G, s_part);
+  auto dot = [&](const float (&col)[32], const float (*vec)[D]) {
+    if (G <= 4) quarter_dot<4>(col, vec, j, kq, G, s_part);
+    else if (G <= 8) quarter_dot<8>(col, vec, j, kq, G, s_part);
+    else quarter_dot<16>(col, vec, j, kq, G, s_part);
   };
-  dot(pr, s_q);  // q~[h][j] = sum_k Pi[j][k] q[h][k]
+  dot(pc, s_q);
   __syncthreads();
   for (int h = kq; h < G; h += 4) {
     const float v = (s_part[0][h][j] + s_part[1][h][j]) + (s_part[2][h][j] + s_part[3][h][j]);
@@ -243,7 +348,10 @@ __global__ void __launch_bounds__(PQ_THREADS) prepare_queries_kernel(DecodeArgs 
   }
   __syncthreads();
   if (qjl) {
-    dot(sr, s_r);  // q_s[h][j] = sum_k S[j][k] q~[h][k]
+    float sc[32];  // S[j][32 kq + i]
+#pragma unroll
+    for (int i = 0; i < 32; ++i) sc[i] = s_st[(32 * kq + i) * ST_STRIDE + j];
+    dot(sc, s_r);  // q_s[h][j] = sum_k S[j][k] q~[h][k]
     __syncthreads();
   }
   for (int h = kq; h < G; h += 4) {
@@ -1132,58 +1240,10 @@ __global__ void __launch_bounds__(WAVES * 64, OCC) packed_decode4_kernel(DecodeA
 }
 
 // ---------------------------------------------------------------- kernel 3
-// One work-group per (KV head, sequence):
-//  1. wave w takes heads w, w + 8: lane sp holds split sp's (max, sum), and the
-//     log-sum-exp weights exp(m_sp - M) and 1 / sum_sp l_sp w_sp go to LDS;
-//  2. thread (j, kq) adds up coordinate j of splits sp = kq, kq + 4, ... for every
-//     head (all loads of a head issued together), the four quarters are summed;
-//  3. o = Pi^T O, each thread holding a quarter of row j of Pi^T (loaded first).
+// One work-group per (KV head, sequence): merge_group over its splits.
 __global__ void __launch_bounds__(PQ_THREADS) merge_unrotate_kernel(DecodeArgs a) {
-  __shared__ __align__(16) float s_o[FQ_MAX_GROUP][D];
-  __shared__ __align__(16) float s_part[4][FQ_MAX_GROUP][D];
-  __shared__ float s_w[FQ_MAX_GROUP][FQ_MAX_SPLITS];
-  __shared__ float s_inv[FQ_MAX_GROUP];
-  const int kvh = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
-  const int j = tid & (D - 1);
-  const int kq = __builtin_amdgcn_readfirstlane(tid >> 7);
-  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
-  const int G = a.group, S = a.splits;
-  float4 tr[8];
-  row_quarter_load(a.pit, j, kq, tr);
-  const int64_t head0 = static_cast<int64_t>(b) * a.hq + kvh * G;
-  for (int h = wv; h < G; h += PQ_THREADS / 64) {
-    float m = -INFINITY, l = 0.f;
-    if (lane < S) {
-      const float2 x = reinterpret_cast<const float2*>(a.part_ml)[(head0 + h) * S + lane];
-      m = x.x;
-      l = x.y;
-    }
-    const float M = wave_max(l > 0.f ? m : -INFINITY);
-    const float w = (lane < S && l > 0.f) ? __expf(m - M) : 0.f;
-    float L = l * w;
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) L += __shfl_xor(L, off);
-    if (lane < S) s_w[h][lane] = w;
-    if (lane == 0) s_inv[h] = L > 0.f ? 1.f / L : 0.f;
-  }
-  __syncthreads();
-  for (int h = 0; h < G; ++h) {
-    const float* po = a.part_o + (head0 + h) * S * D + j;
-    float acc = 0.f;
-#pragma unroll 16
-    for (int sp = kq; sp < S; sp += 4) acc = fmaf(po[sp * D], s_w[h][sp], acc);
-    s_part[kq][h][j] = acc;
-  }
-  __syncthreads();
-  for (int h = kq; h < G; h += 4)
-    s_o[h][j] = ((s_part[0][h][j] + s_part[1][h][j]) + (s_part[2][h][j] + s_part[3][h][j])) * s_inv[h];
-  __syncthreads();
-  if (G <= 4) quarter_dot<4>(tr, s_o, j, kq, G, s_part);  // o[h][j] = sum_k Pi^T[j][k] o_rot[h][k]
-  else if (G <= 8) quarter_dot<8>(tr, s_o, j, kq, G, s_part);
-  else quarter_dot<16>(tr, s_o, j, kq, G, s_part);
-  __syncthreads();
-  for (int h = kq; h < G; h += 4)
-    a.out[(head0 + h) * D + j] = (s_part[0][h][j] + s_part[1][h][j]) + (s_part[2][h][j] + s_part[3][h][j]);
+  __shared__ __align__(16) float s_m[(17 + PQ_THREADS / D * 16) * D + 16 * FQ_MAX_SPLITS + 16];
+  merge_group<PQ_THREADS>(a, blockIdx.x, blockIdx.y, threadIdx.x, s_m);
 }
 
 }  // namespace
