@@ -105,7 +105,7 @@ __device__ __forceinline__ f4 mfma16(h4 a, h4 b, f4 c) {
 //   q~[h][j]  = sum_k Pi[j][k] q[h][k]     (row j of Pi)
 //   q_s[h][j] = sum_k S[j][k] q~[h][k]     (row j of S)
 // stored as [b][query head][j]. With SLOTS > 0 it also writes the per-lane
-// operands of the packed split kernel (see packed_decode4_kernel): fp16 hi / lo
+// operands of the packed split kernel (see packed_decode_kernel): fp16 hi / lo
 // splits of q~ and q_s arranged in the matrix-core B layout, and the per-lane
 // score factor.
 constexpr float QJL_R = 256.0f * QJL_C;  // 2^8 (level scale) x sqrt(pi/2) / m
@@ -865,11 +865,17 @@ __global__ void __launch_bounds__(256, 2) split_mfma4_kernel(DecodeArgs a) {
 // (lane = head x token) to the operand layout (lane = head-slot x token quad)
 // by four lane permutes.
 //
-// Dequantization reads one 8-byte LDS entry per code byte (hi pair, lo pair of
-// the two codes' levels x 2^8). The table holds 32 copies of each entry, copy =
-// lane % 32, with a 256-byte stride per byte value, so lane offsets are built by
-// one byte permute and a wave's 64 lookups never share a bank. QJL signs use a
-// 16-entry nibble table (4 x fp16 +-1) laid out the same way.
+// Dequantization of 4-bit codes reads one 8-byte LDS entry per code byte (hi
+// pair, lo pair of the two codes' levels x 2^8). The table holds 32 copies of
+// each entry, copy = lane % 32, with a 256-byte stride per byte value, so lane
+// offsets are built by one byte permute and a wave's 64 lookups never share a
+// bank. QJL signs use a 16-entry nibble table (4 x fp16 +-1) laid out the same
+// way. 2-bit codes: one 16-byte entry per byte (four codes f0..f3 as f0 f1 hi,
+// f0 f1 lo, f2 f3 hi, f2 f3 lo), 16 copies (copy = lane % 16): a key byte holds
+// dims 4k .. 4k+3, so a lookup is one whole B operand of the score product in the
+// 4-bit order; value bytes are regrouped in registers so that one byte holds the
+// codes of one dimension for tokens (4g, 4g+2, 4g+1, 4g+3), and the P operand
+// takes its tokens in that order.
 //
 // Scores are kept in log2 units (log2 e folded into the per-head factor); the
 // running max is only moved when a page's max exceeds it by more than 8, so
@@ -878,10 +884,10 @@ __global__ void __launch_bounds__(256, 2) split_mfma4_kernel(DecodeArgs a) {
 constexpr int PK4_WAVES = 4, PK4_RING = 3, PK4_OCC = 2;  // SLOTS 4
 constexpr int PK2_WAVES = 8, PK2_RING = 2, PK2_OCC = 4;  // SLOTS 2
 constexpr int PK_SIGN_BASE = 0;       // 16 x 32 x 8 B
-constexpr int PK_CODE_BASE = 4096;    // 256 x 32 x 8 B
-constexpr int PK_STAGE_BASE = 69632;  // 256 x 8 B staging for the table build
-constexpr int PK_QOPS_BASE = 71680;   // 8 x 64 lanes x 16 B code-product operands
-constexpr int PK_LDS_BYTES = PK_QOPS_BASE + 8 * 64 * 16;
+constexpr int PK_CODE_BASE = 4096;    // 256 x 32 x 8 B (4-bit) or 256 x 16 x 16 B (2-bit)
+constexpr int PK_STAGE_BASE = 69632;  // 256 x 16 B staging for the table build
+constexpr int PK_QOPS_BASE = 73728;   // 8 x 64 lanes x 16 B code-product operands
+constexpr int PK_LDS_BYTES = PK_QOPS_BASE + 8 * 64 * 16;  // 80 KB: two work-groups per CU
 constexpr float PK_TAU = 8.0f;
 
 template <int CTRL>
@@ -921,13 +927,18 @@ __device__ __forceinline__ uint2 lds_u2(const uint8_t* base, uint32_t off) {
   return *reinterpret_cast<const uint2*>(base + off);
 }
 
+__device__ __forceinline__ uint4 lds_u4(const uint8_t* base, uint32_t off) {
+  return *reinterpret_cast<const uint4*>(base + off);
+}
+
 __device__ __forceinline__ h8 h8_of(uint2 a, uint2 b) { return as_h8(a.x, a.y, b.x, b.y); }
 
+template <int BITS>
 struct PkPage {
-  uint4 kc;        // code bytes 16g .. 16g+15 of token n (dims 32g .. 32g+31)
-  uint32_t sg;     // sign bytes 4g .. 4g+3 of token n (projections 32g .. 32g+31)
-  float kn, gm, vn;  // key norm, gamma, value norm of token n
-  uint32_t vc[4];  // value code dword n (dims 8n .. 8n+7) of tokens 4g+e
+  uint32_t kc[BITS];  // code dwords of token n covering dims 32g .. 32g+31
+  uint32_t sg;        // sign bytes 4g .. 4g+3 of token n (projections 32g .. 32g+31)
+  float kn, gm, vn;   // key norm, gamma, value norm of token n
+  uint32_t vc[4];     // value codes of dims 8n .. 8n+7 of tokens 4g+e (4-bit: a dword, 2-bit: 16 bits)
 };
 
 // Per-lane byte offsets of a page's fields (constant over pages).
@@ -937,20 +948,37 @@ struct PkLane {
 
 // Loads one page; rec0 = first record of the page (wave-uniform), so every
 // address is a uniform base plus a fixed 32-bit lane offset.
+template <int BITS>
 __device__ __forceinline__ void pk_load(const DecodeArgs& a, int64_t rec0, int n, const PkLane& o,
-                                        const float* gptr, const uint8_t* sgn_base, PkPage& d) {
-  d.kc = *reinterpret_cast<const uint4*>(a.k_codes + rec0 * 64 + o.kc);
+                                        const float* gptr, const uint8_t* sgn_base, PkPage<BITS>& d) {
+  constexpr int CB = D * BITS / 8;  // code bytes per vector
+  if constexpr (BITS == 4) {
+    const uint4 k = *reinterpret_cast<const uint4*>(a.k_codes + rec0 * CB + o.kc);
+    d.kc[0] = k.x;
+    d.kc[1] = k.y;
+    d.kc[2] = k.z;
+    d.kc[3] = k.w;
+  } else {
+    const uint2 k = *reinterpret_cast<const uint2*>(a.k_codes + rec0 * CB + o.kc);
+    d.kc[0] = k.x;
+    d.kc[1] = k.y;
+  }
   d.sg = *reinterpret_cast<const uint32_t*>(sgn_base + rec0 * 16 + o.sg);
   d.kn = a.k_norm[rec0 + n];
   d.gm = gptr[rec0 + n];
   d.vn = a.v_norm[rec0 + n];
-  const uint8_t* vcb = a.v_codes + rec0 * 64 + o.vc;
+  const uint8_t* vcb = a.v_codes + rec0 * CB + o.vc;
 #pragma unroll
-  for (int e = 0; e < 4; ++e) d.vc[e] = *reinterpret_cast<const uint32_t*>(vcb + 64 * e);
+  for (int e = 0; e < 4; ++e) {
+    if constexpr (BITS == 4) d.vc[e] = *reinterpret_cast<const uint32_t*>(vcb + CB * e);
+    else d.vc[e] = *reinterpret_cast<const uint16_t*>(vcb + CB * e);
+  }
 }
 
-template <int SLOTS, int WAVES, int RING, int OCC>
-__global__ void __launch_bounds__(WAVES * 64, OCC) packed_decode4_kernel(DecodeArgs a) {
+template <int BITS, int SLOTS, int WAVES, int RING, int OCC>
+__global__ void __launch_bounds__(WAVES * 64, OCC) packed_decode_kernel(DecodeArgs a) {
+  static_assert(BITS == 4 || BITS == 2, "4- or 2-bit codes");
+  constexpr int CB = D * BITS / 8;  // code bytes per vector
   __shared__ __align__(16) uint8_t s_lds[PK_LDS_BYTES];
   const uint8_t* const s_code = s_lds + PK_CODE_BASE;
   const uint8_t* const s_sign = s_lds + PK_SIGN_BASE;
@@ -992,12 +1020,12 @@ __global__ void __launch_bounds__(WAVES * 64, OCC) packed_decode4_kernel(DecodeA
     return (static_cast<int64_t>(blk) * a.hkv + kvh) * FQ_BLOCK;
   };
   PkLane lo;
-  lo.kc = static_cast<uint32_t>(n * 64 + 16 * g);
+  lo.kc = static_cast<uint32_t>(n * CB + 4 * BITS * g);
   lo.sg = static_cast<uint32_t>(n * 16 + 4 * g);
-  lo.vc = static_cast<uint32_t>(4 * g * 64 + 4 * n);
+  lo.vc = static_cast<uint32_t>(4 * g * CB + BITS * n);
 
   // ---- the wave's first two pages are requested before any set-up work
-  PkPage ring[RING];
+  PkPage<BITS> ring[RING];
   if (my_pages > 0) {
 #pragma unroll
     for (int k = 0; k < RING - 1; ++k)
@@ -1021,16 +1049,27 @@ __global__ void __launch_bounds__(WAVES * 64, OCC) packed_decode4_kernel(DecodeA
     for (int k = 0; k < HL; ++k) cf[k] = __uint_as_float(ops[12 * 64 + (HL * g + k) * SLOTS].x);
   }
 
-  // ---- tables: stage the 256 entries once, then fan out 32 conflict-free copies
+  // ---- tables: stage the 256 entries once, then fan out conflict-free copies
   {
     uint2* stage = reinterpret_cast<uint2*>(s_lds + PK_STAGE_BASE);
+    uint4* stage4 = reinterpret_cast<uint4*>(s_lds + PK_STAGE_BASE);
     if (tid < 256) {
-      const float c0 = a.levels[tid & 15] * static_cast<float>(1 << LEV_SHIFT);
-      const float c1 = a.levels[tid >> 4] * static_cast<float>(1 << LEV_SHIFT);
-      _Float16 h0, l0, h1, l1;
-      split_f16(c0, h0, l0);
-      split_f16(c1, h1, l1);
-      stage[tid] = make_uint2(h2bits(h0, h1), h2bits(l0, l1));
+      if constexpr (BITS == 4) {
+        const float c0 = a.levels[tid & 15] * static_cast<float>(1 << LEV_SHIFT);
+        const float c1 = a.levels[tid >> 4] * static_cast<float>(1 << LEV_SHIFT);
+        _Float16 h0, l0, h1, l1;
+        split_f16(c0, h0, l0);
+        split_f16(c1, h1, l1);
+        stage[tid] = make_uint2(h2bits(h0, h1), h2bits(l0, l1));
+      } else {
+        constexpr float SC = static_cast<float>(1 << LEV_SHIFT);
+        _Float16 h0, l0, h1, l1, h2, l2, h3, l3;
+        split_f16(a.levels[tid & 3] * SC, h0, l0);
+        split_f16(a.levels[(tid >> 2) & 3] * SC, h1, l1);
+        split_f16(a.levels[(tid >> 4) & 3] * SC, h2, l2);
+        split_f16(a.levels[tid >> 6] * SC, h3, l3);
+        stage4[tid] = make_uint4(h2bits(h0, h1), h2bits(l0, l1), h2bits(h2, h3), h2bits(l2, l3));
+      }
     }
     for (int idx = tid; idx < 16 * 32; idx += WAVES * 64) {
       const int nib = idx >> 5;
@@ -1044,26 +1083,28 @@ __global__ void __launch_bounds__(WAVES * 64, OCC) packed_decode4_kernel(DecodeA
       *reinterpret_cast<uint2*>(s_lds + PK_SIGN_BASE + idx * 8) = make_uint2(w[0], w[1]);
     }
     __syncthreads();
-    // 8192 entries; four per thread and round, reads issued before writes
+    // 8192 (4096) entries; four per thread and round, reads issued before writes
     constexpr int NT = WAVES * 64;
-    for (int base = 0; base < 256 * 32; base += 4 * NT) {
-      uint2 v[4];
+    static_assert((256 * 16) % (4 * NT) == 0, "whole rounds");
+    if constexpr (BITS == 4) {
+      for (int base = 0; base < 256 * 32; base += 4 * NT) {
+        uint2 v[4];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int idx = base + u * NT + tid;
-        if (idx < 256 * 32) v[u] = stage[idx >> 5];
-      }
+        for (int u = 0; u < 4; ++u) v[u] = stage[(base + u * NT + tid) >> 5];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int idx = base + u * NT + tid;
-        if (idx < 256 * 32) *reinterpret_cast<uint2*>(s_lds + PK_CODE_BASE + idx * 8) = v[u];
+        for (int u = 0; u < 4; ++u) *reinterpret_cast<uint2*>(s_lds + PK_CODE_BASE + (base + u * NT + tid) * 8) = v[u];
       }
+    } else {
+#pragma unroll
+      for (int idx = tid; idx < 256 * 16; idx += NT)
+        *reinterpret_cast<uint4*>(s_lds + PK_CODE_BASE + idx * 16) = stage4[idx >> 4];
     }
   }
 
   const h8* const s_qm = reinterpret_cast<const h8*>(s_lds + PK_QOPS_BASE) + lane;
   // ---- per-lane constants
   const uint32_t copy8 = static_cast<uint32_t>(lane & 31) * 8u;
+  const uint32_t copy16 = static_cast<uint32_t>(lane & 15) * 16u;
   const uint32_t m_le1 = s <= 1 ? 0xFFFFFFFFu : 0u;
   const uint32_t m_eq0 = s == 0 ? 0xFFFFFFFFu : 0u;
   // P operand: slot 0 takes the hi halves of the packed (hi, lo) pairs, slot 1
@@ -1085,17 +1126,23 @@ __global__ void __launch_bounds__(WAVES * 64, OCC) packed_decode4_kernel(DecodeA
   for (int t = 0; t < 8; ++t) acc_o[t] = f4{0.f, 0.f, 0.f, 0.f};
   __syncthreads();
 
-  auto process = [&](const PkPage& d, int p) {
-    // ---- scores: C[(head, slot)][token]
+  auto process = [&](const PkPage<BITS>& d, int p) {
+    // ---- scores: C[(head, slot)][token]; product i covers dims 32g + 4i .. 4i+3
     f4 accM = {0.f, 0.f, 0.f, 0.f}, accQ = {0.f, 0.f, 0.f, 0.f};
-    const uint32_t kw[4] = {d.kc.x, d.kc.y, d.kc.z, d.kc.w};
     const uint32_t sgl = d.sg & 0x0F0F0F0Fu, sgh = (d.sg >> 4) & 0x0F0F0F0Fu;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const uint2 e0 = lds_u2(s_code, tab_off(kw[i >> 1], copy8, (2 * i) & 3));
-      const uint2 e1 = lds_u2(s_code, tab_off(kw[i >> 1], copy8, (2 * i + 1) & 3));
+      h8 kop;
+      if constexpr (BITS == 4) {
+        const uint2 e0 = lds_u2(s_code, tab_off(d.kc[i >> 1], copy8, (2 * i) & 3));
+        const uint2 e1 = lds_u2(s_code, tab_off(d.kc[i >> 1], copy8, (2 * i + 1) & 3));
+        kop = h8_of(e0, e1);
+      } else {
+        const uint4 e = lds_u4(s_code, tab_off(d.kc[i >> 2], copy16, i & 3));
+        kop = as_h8(e.x, e.y, e.z, e.w);
+      }
       const h8 qmi = s_qm[i * 64];
-      accM = mfma32(qmi, h8_of(e0, e1), accM);
+      accM = mfma32(qmi, kop, accM);
       if (i < 4) {
         const uint2 z0 = lds_u2(s_sign, tab_off(sgl, copy8, i));
         const uint2 z1 = lds_u2(s_sign, tab_off(sgh, copy8, i));
@@ -1103,11 +1150,25 @@ __global__ void __launch_bounds__(WAVES * 64, OCC) packed_decode4_kernel(DecodeA
         else accQ = mfma32(qs[i], h8_of(z0, z1), accQ);
       }
     }
-    // pair bytes (token 4g, 4g+1) and (4g+2, 4g+3) per dimension 8n + t
-    const uint32_t x01 = (d.vc[0] & 0x0F0F0F0Fu) | ((d.vc[1] << 4) & 0xF0F0F0F0u);
-    const uint32_t z01 = ((d.vc[0] >> 4) & 0x0F0F0F0Fu) | (d.vc[1] & 0xF0F0F0F0u);
-    const uint32_t x23 = (d.vc[2] & 0x0F0F0F0Fu) | ((d.vc[3] << 4) & 0xF0F0F0F0u);
-    const uint32_t z23 = ((d.vc[2] >> 4) & 0x0F0F0F0Fu) | (d.vc[3] & 0xF0F0F0F0u);
+    // 4-bit: pair bytes (token 4g, 4g+1) and (4g+2, 4g+3) per dimension 8n + t.
+    // 2-bit: bytes of 2-bit fields (4g, 4g+2, 4g+1, 4g+3) per dimension, byte k
+    // of r1 = dims 8n + {0, 4, 1, 5}, of r2 = dims 8n + {2, 6, 3, 7}.
+    uint32_t x01 = 0, z01 = 0, x23 = 0, z23 = 0, r1 = 0, r2 = 0;
+    if constexpr (BITS == 4) {
+      x01 = (d.vc[0] & 0x0F0F0F0Fu) | ((d.vc[1] << 4) & 0xF0F0F0F0u);
+      z01 = ((d.vc[0] >> 4) & 0x0F0F0F0Fu) | (d.vc[1] & 0xF0F0F0F0u);
+      x23 = (d.vc[2] & 0x0F0F0F0Fu) | ((d.vc[3] << 4) & 0xF0F0F0F0u);
+      z23 = ((d.vc[2] >> 4) & 0x0F0F0F0Fu) | (d.vc[3] & 0xF0F0F0F0u);
+    } else {
+      // nibble j: (token a, token b) fields of dim 2j (even) or 2j + 1 (odd)
+      const uint32_t n02e = (d.vc[0] & 0x3333u) | ((d.vc[2] << 2) & 0xCCCCu);
+      const uint32_t n02o = ((d.vc[0] >> 2) & 0x3333u) | (d.vc[2] & 0xCCCCu);
+      const uint32_t n13e = (d.vc[1] & 0x3333u) | ((d.vc[3] << 2) & 0xCCCCu);
+      const uint32_t n13o = ((d.vc[1] >> 2) & 0x3333u) | (d.vc[3] & 0xCCCCu);
+      const uint32_t ee = n02e | (n02o << 16), ff = n13e | (n13o << 16);
+      r1 = (ee & 0x0F0F0F0Fu) | ((ff << 4) & 0xF0F0F0F0u);
+      r2 = ((ee >> 4) & 0x0F0F0F0Fu) | (ff & 0xF0F0F0F0u);
+    }
     const bool valid = t0 + p * FQ_BLOCK + n < t1;
     float sc[HL];
     if constexpr (SLOTS == 4) {
@@ -1160,15 +1221,24 @@ __global__ void __launch_bounds__(WAVES * 64, OCC) packed_decode4_kernel(DecodeA
         y[r] = src_k1 ? y1 : y[r];
       }
     }
-    const uint32_t y01 = __builtin_amdgcn_perm(y[1], y[0], psel);
-    const uint32_t y23 = __builtin_amdgcn_perm(y[3], y[2], psel);
+    // token order of the value operand: 4-bit (0, 1, 2, 3), 2-bit (0, 2, 1, 3)
+    constexpr int TA = BITS == 4 ? 1 : 2, TB = BITS == 4 ? 2 : 1;
+    const uint32_t y01 = __builtin_amdgcn_perm(y[TA], y[0], psel);
+    const uint32_t y23 = __builtin_amdgcn_perm(y[3], y[TB], psel);
     const h8 ap = as_h8(y01 & m_le1, y01 & m_eq0, y23 & m_le1, y23 & m_eq0);
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
-      const uint32_t w01 = (t & 1) ? z01 : x01, w23 = (t & 1) ? z23 : x23;
-      const uint2 e01 = lds_u2(s_code, tab_off(w01, copy8, t >> 1));
-      const uint2 e23 = lds_u2(s_code, tab_off(w23, copy8, t >> 1));
-      acc_o[t] = mfma32(ap, h8_of(e01, e23), acc_o[t]);
+      h8 vop;
+      if constexpr (BITS == 4) {
+        const uint32_t w01 = (t & 1) ? z01 : x01, w23 = (t & 1) ? z23 : x23;
+        const uint2 e01 = lds_u2(s_code, tab_off(w01, copy8, t >> 1));
+        const uint2 e23 = lds_u2(s_code, tab_off(w23, copy8, t >> 1));
+        vop = h8_of(e01, e23);
+      } else {
+        const uint4 e = lds_u4(s_code, tab_off(t < 4 ? r1 : r2, copy16, t & 3));
+        vop = as_h8(e.x, e.y, e.z, e.w);
+      }
+      acc_o[t] = mfma32(ap, vop, acc_o[t]);
     }
   };
 
@@ -1208,9 +1278,10 @@ __global__ void __launch_bounds__(WAVES * 64, OCC) packed_decode4_kernel(DecodeA
   const float unscale = 1.0f / static_cast<float>(1 << LEV_SHIFT);
 #pragma unroll
   for (int t = 0; t < 8; ++t) {
+    const int dim = 8 * n + (BITS == 4 ? t : (t >> 1) + 4 * (t & 1));  // 2-bit: r1, r2 byte order
 #pragma unroll
     for (int k = 0; k < HL; ++k)
-      s_o[(wave * HP + HL * g + k) * D + 8 * n + t] = (acc_o[t][2 * k] + acc_o[t][2 * k + 1]) * unscale;
+      s_o[(wave * HP + HL * g + k) * D + dim] = (acc_o[t][2 * k] + acc_o[t][2 * k + 1]) * unscale;
   }
   __syncthreads();
   constexpr float LN2 = 0.6931471805599453f;
@@ -1289,13 +1360,13 @@ int launch_decode(void* stream, const fq_quantizer& q, const fq_cache& c, const 
   a.scale = scale;
   hipStream_t st = static_cast<hipStream_t>(stream);
 
-  // Split kernel: packed matrix-core kernel for 4-bit codes and groups of up to 8
-  // query heads; the earlier matrix-core kernel for larger groups; the vector-ALU
-  // kernel for 2-bit codes (or on request).
+  // Split kernel: packed matrix-core kernel for groups of up to 8 query heads; for
+  // larger groups the earlier matrix-core kernel (4-bit) or the vector-ALU kernel
+  // (2-bit, or any width on request).
   const char* impl = std::getenv("FQ_DECODE_KERNEL");
   const bool valu = impl && std::strcmp(impl, "valu") == 0;
   const bool v1 = impl && std::strcmp(impl, "mfma_v1") == 0;
-  const int slots = (q.bits == 4 && !valu && !v1) ? (a.group <= 4 ? 4 : a.group <= 8 ? 2 : 0) : 0;
+  const int slots = (!valu && !v1) ? (a.group <= 4 ? 4 : a.group <= 8 ? 2 : 0) : 0;
   const dim3 pgrid(c.num_kv_heads, batch);
   if (q_dtype == FQ_BF16) {
     if (slots == 4) hipLaunchKernelGGL((prepare_queries_kernel<FQ_BF16, 4>), pgrid, dim3(PQ_THREADS), 0, st, a);
@@ -1307,10 +1378,14 @@ int launch_decode(void* stream, const fq_quantizer& q, const fq_cache& c, const 
     else hipLaunchKernelGGL((prepare_queries_kernel<FQ_F32, 0>), pgrid, dim3(PQ_THREADS), 0, st, a);
   }
   dim3 grid(num_splits, c.num_kv_heads, batch);
-  if (slots == 4)
-    hipLaunchKernelGGL((packed_decode4_kernel<4, PK4_WAVES, PK4_RING, PK4_OCC>), grid, dim3(PK4_WAVES * 64), 0, st, a);
+  if (slots == 4 && q.bits == 4)
+    hipLaunchKernelGGL((packed_decode_kernel<4, 4, PK4_WAVES, PK4_RING, PK4_OCC>), grid, dim3(PK4_WAVES * 64), 0, st, a);
+  else if (slots == 2 && q.bits == 4)
+    hipLaunchKernelGGL((packed_decode_kernel<4, 2, PK2_WAVES, PK2_RING, PK2_OCC>), grid, dim3(PK2_WAVES * 64), 0, st, a);
+  else if (slots == 4)
+    hipLaunchKernelGGL((packed_decode_kernel<2, 4, PK4_WAVES, PK4_RING, PK4_OCC>), grid, dim3(PK4_WAVES * 64), 0, st, a);
   else if (slots == 2)
-    hipLaunchKernelGGL((packed_decode4_kernel<2, PK2_WAVES, PK2_RING, PK2_OCC>), grid, dim3(PK2_WAVES * 64), 0, st, a);
+    hipLaunchKernelGGL((packed_decode_kernel<2, 2, PK2_WAVES, PK2_RING, PK2_OCC>), grid, dim3(PK2_WAVES * 64), 0, st, a);
   else if (q.bits == 4 && !valu)
     hipLaunchKernelGGL(split_mfma4_kernel, grid, dim3(256), 0, st, a);
   else if (q.bits == 4)

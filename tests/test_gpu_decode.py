@@ -36,15 +36,17 @@ def test_decode_tiny(gpu_lib, bits, rot):
     assert err <= parity.DECODE_TOL
 
 
+@pytest.mark.parametrize("bits", [4, 2])
 @pytest.mark.parametrize("G", [1, 4, 8, 16])
-def test_decode_groups_ragged(gpu_lib, G):
-    w, inp = parity.small_workload(3, 2 * G, 2, [5, 333, 1000], 1008, seed=G)
+def test_decode_groups_ragged(gpu_lib, G, bits):
+    w, inp = parity.small_workload(3, 2 * G, 2, [5, 333, 1000], 1008, bits=bits, seed=G)
     out, ref, _ = _decode_case(w, inp, num_splits=3)
     assert np.max(np.abs(out - ref)) <= parity.DECODE_TOL
 
 
-def test_decode_mse_only_keys(gpu_lib):
-    w, inp = parity.small_workload(2, 8, 2, [700, 64], 704, seed=41)
+@pytest.mark.parametrize("bits", [4, 2])
+def test_decode_mse_only_keys(gpu_lib, bits):
+    w, inp = parity.small_workload(2, 8, 2, [700, 64], 704, bits=bits, seed=41)
     out, ref, _ = _decode_case(w, inp, with_qjl=False)
     assert np.max(np.abs(out - ref)) <= parity.DECODE_TOL
 
@@ -107,10 +109,12 @@ def test_decode_full_size_b32_sampled(gpu_lib):
     assert err <= parity.DECODE_TOL
 
 
-def test_decode_vector_alu_kernel_matches_matrix_core_kernel(gpu_lib, monkeypatch):
-    """The 4-bit decode has a matrix-core split kernel (default) and a vector-ALU one
+@pytest.mark.parametrize("bits", [4, 2])
+@pytest.mark.parametrize("G", [4, 8])
+def test_decode_vector_alu_kernel_matches_matrix_core_kernel(gpu_lib, monkeypatch, bits, G):
+    """The decode has matrix-core split kernels (default) and a vector-ALU one
     (FQ_DECODE_KERNEL=valu); both must match the oracle."""
-    w, inp = parity.small_workload(2, 32, 8, [2000, 777], 2000, seed=59)
+    w, inp = parity.small_workload(2, 8 * G, 8, [2000, 777], 2000, bits=bits, seed=59)
     out_m, ref, (qz, cache, t, oq, host) = _decode_case(w, inp, num_splits=3)
     monkeypatch.setenv("FQ_DECODE_KERNEL", "valu")
     out_v = fq.decode(qz, cache, t["q"], t["bt"], t["lens"], 2000, num_splits=3).cpu().numpy()
