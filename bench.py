@@ -4,8 +4,8 @@ Workload (default): Llama-3-8B-shaped attention, 32 layers, batch 32, context
 lengths uniform in [3072, 4096], 32 query / 8 KV heads, head_dim 128, TQ4 keys
 (4-bit Lloyd-Max + 1-bit QJL) and values (4-bit), 16-token pages with random
 non-contiguous block tables. The decode split count is the library's choice
-(one round of work-groups: 2 splits at this shape; --splits 4 runs the pages'
-4-way split instead). Every layer has its own
+(one split per (sequence, KV head) at this shape: the whole decode is one
+launch; --splits 4 runs the pages' 4-way split instead). Every layer has its own
 compressed cache (5.2 GB in all, far beyond the 256 MB last-level cache), filled
 by compressing the whole synthetic context before timing.
 
@@ -376,7 +376,9 @@ def main():
             "cache_bytes_per_layer": dec_bytes, "bytes_per_token_head": bpt,
         },
         "roofline": {
-            "kernel": "fq_decode_attention (prepare_queries + packed split attention + merge_unrotate)",
+            "kernel": ("fq_decode_attention (one launch: packed_decode_kernel, query preparation and output "
+                       "rotation in-kernel)" if splits == 1 else
+                       "fq_decode_attention (prepare_queries + packed split attention + merge_unrotate)"),
             "bound": "hbm",
             "achieved": achieved,
             "peak": HBM_PEAK_GBS,

@@ -79,13 +79,14 @@ int fq_version(void);
  *  rotation_t      [d * d] row-major Pi^T, the same numbers transposed (may be NULL)
  *  wht_signs       [d]               +-1 (FQ_ROT_WHT; may be NULL)
  *  qjl_matrix      [qjl_dim * d]     row-major S (may be NULL)
+ *  qjl_matrix_t    [d * qjl_dim]     row-major S^T, the same numbers transposed (may be NULL)
  * Errors: FQ_ERR_INVALID_ARG for null levels/boundaries or a bad enum;
  * FQ_ERR_UNSUPPORTED for other bits / head_dim / qjl_dim.
  */
 fq_status fq_build_codebook(int bits, int head_dim, int rotation, uint64_t rot_seed,
                             uint64_t qjl_seed, int qjl_dim, float* levels, float* boundaries,
                             float* rotation_matrix, float* rotation_t, float* wht_signs,
-                            float* qjl_matrix);
+                            float* qjl_matrix, float* qjl_matrix_t);
 
 /* One layer's quantizer parameters, all device pointers (fp32, as built above). */
 typedef struct fq_quantizer {
@@ -99,6 +100,7 @@ typedef struct fq_quantizer {
   const float* rotation_t;      /* [d][d] row-major Pi^T; required for both kinds */
   const float* wht_signs;       /* [d]; required for FQ_ROT_WHT */
   const float* qjl_matrix;      /* [qjl_dim][d] row-major; required when qjl_dim > 0 */
+  const float* qjl_matrix_t;    /* [d][qjl_dim] row-major S^T; required when qjl_dim > 0 */
   const void* mfma_operands;    /* optional: FQ_MFMA_OPERAND_BYTES from fq_pack_mfma_operands,
                                    16-byte aligned; NULL = the kernels derive them */
 } fq_quantizer;

@@ -17,11 +17,12 @@ fq_status check_quantizer(const fq_quantizer* q) {
   if (!q->levels || !q->boundaries || !q->rotation_matrix || !q->rotation_t)
     return FQ_ERR_INVALID_ARG;
   if (q->rotation == FQ_ROT_WHT && !q->wht_signs) return FQ_ERR_INVALID_ARG;
-  if (q->qjl_dim > 0 && !q->qjl_matrix) return FQ_ERR_INVALID_ARG;
+  if (q->qjl_dim > 0 && (!q->qjl_matrix || !q->qjl_matrix_t)) return FQ_ERR_INVALID_ARG;
   if (!aligned(q->levels, 4) || !aligned(q->boundaries, 4) || !aligned(q->rotation_matrix, 16) ||
       !aligned(q->rotation_t, 16))
     return FQ_ERR_INVALID_ARG;
-  if (q->qjl_dim > 0 && !aligned(q->qjl_matrix, 16)) return FQ_ERR_INVALID_ARG;
+  if (q->qjl_dim > 0 && (!aligned(q->qjl_matrix, 16) || !aligned(q->qjl_matrix_t, 16)))
+    return FQ_ERR_INVALID_ARG;
   if (q->mfma_operands && !aligned(q->mfma_operands, 16)) return FQ_ERR_INVALID_ARG;
   return FQ_OK;
 }
@@ -68,9 +69,11 @@ DecodeWorkspace decode_workspace(int batch, int num_q_heads, int num_kv_heads, i
 }
 
 int auto_splits(int batch, int num_kv_heads, int max_seq_len) {
-  const int target_groups = 512;  // 2 work-groups per CU on 256 CUs
-  int groups = batch * num_kv_heads;
-  int s = groups >= target_groups ? 1 : (target_groups + groups - 1) / groups;
+  // Once the (sequence, KV head) pairs cover the 256 CUs, one split each (the
+  // single-launch path); below that, splits for two work-groups per CU.
+  const int groups = batch * num_kv_heads;
+  if (groups >= 256) return 1;
+  int s = (512 + groups - 1) / groups;
   int by_len = max_seq_len / 256;
   if (by_len < 1) by_len = 1;
   if (s > by_len) s = by_len;

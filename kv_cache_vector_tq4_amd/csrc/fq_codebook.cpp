@@ -128,7 +128,8 @@ void haar_from_gaussian(int d, std::vector<double>& a, std::vector<double>& q) {
 extern "C" fq_status fq_build_codebook(int bits, int head_dim, int rotation, uint64_t rot_seed,
                                        uint64_t qjl_seed, int qjl_dim, float* levels,
                                        float* boundaries, float* rotation_matrix,
-                                       float* rotation_t, float* wht_signs, float* qjl_matrix) {
+                                       float* rotation_t, float* wht_signs, float* qjl_matrix,
+                                       float* qjl_matrix_t) {
   if (!levels || !boundaries) return FQ_ERR_INVALID_ARG;
   if (rotation != FQ_ROT_HAAR && rotation != FQ_ROT_WHT) return FQ_ERR_INVALID_ARG;
   if (bits != 2 && bits != 4) return FQ_ERR_UNSUPPORTED;
@@ -167,10 +168,15 @@ extern "C" fq_status fq_build_codebook(int bits, int head_dim, int rotation, uin
       if (rotation_t) rotation_t[j * d + i] = static_cast<float>(pi[i * d + j]);
     }
 
-  if (qjl_dim > 0 && qjl_matrix) {
+  if (qjl_dim > 0 && (qjl_matrix || qjl_matrix_t)) {
     std::vector<double> s(static_cast<size_t>(qjl_dim) * d);
     gaussians(qjl_seed, s.size(), s.data());
-    for (size_t i = 0; i < s.size(); ++i) qjl_matrix[i] = static_cast<float>(s[i]);
+    for (int i = 0; i < qjl_dim; ++i)
+      for (int j = 0; j < d; ++j) {
+        const float x = static_cast<float>(s[static_cast<size_t>(i) * d + j]);
+        if (qjl_matrix) qjl_matrix[i * d + j] = x;
+        if (qjl_matrix_t) qjl_matrix_t[j * qjl_dim + i] = x;
+      }
   }
   return FQ_OK;
 }

@@ -39,6 +39,7 @@ struct DecodeArgs {
   const float* pi;    // Pi row-major
   const float* pit;   // Pi^T row-major
   const float* smat;  // S row-major [m][d]
+  const float* sit;   // S^T row-major [d][m]
   const float* levels;
   const uint8_t* k_codes;
   const float* k_norm;
@@ -185,25 +186,8 @@ __device__ __forceinline__ void col_quarter_load(const float* m, int j, int kq, 
   for (int i = 0; i < 32; ++i) x[i] = m[(32 * kq + i) * D + j];
 }
 
-// s_part[kq][h][j] = sum over i < 32 of col[i] vec[h][32 kq + i], for h < G
-template <int GM>
-__device__ __forceinline__ void quarter_dot(const float (&col)[32], const float (*vec)[D], int j, int kq,
-                                            int G, float (*s_part)[FQ_MAX_GROUP][D]) {
-#pragma unroll
-  for (int h = 0; h < GM; ++h) {
-    if (h < G) {
-      float acc = 0.f;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const float4 x = *reinterpret_cast<const float4*>(&vec[h][32 * kq + 4 * i]);
-        acc = fmaf(col[4 * i], x.x, fmaf(col[4 * i + 1], x.y, fmaf(col[4 * i + 2], x.z, fmaf(col[4 * i + 3], x.w, acc))));
-      }
-      s_part[kq][h][j] = acc;
-    }
-  }
-}
-
-// KP-way versions of the above (rows kp * D/KP .. of column j).
+// KP-way version of col_quarter_load (rows kp * D/KP .. of column j) and the
+// matching partial dot products.
 template <int KP>
 __device__ __forceinline__ void col_part_load(const float* m, int j, int kp, float (&x)[D / KP]) {
 #pragma unroll
@@ -291,99 +275,121 @@ __device__ __forceinline__ void merge_group(const DecodeArgs& a, int kvh, int b,
   }
 }
 
-constexpr int ST_STRIDE = D + 1;  // transposed matrix in LDS: [k][j], padded rows
+// s_part[(kq GM + h) D + j] = sum over i < 32 of col[i] vec[h D + 32 kq + i], h < G <= GB
+template <int GB, int GM>
+__device__ __forceinline__ void quarter_dot_g(const float (&col)[32], const float* vec, int j, int kq, int G,
+                                              float* s_part) {
+#pragma unroll
+  for (int h = 0; h < GB; ++h) {
+    if (h < G) {
+      float acc = 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float4 x = *reinterpret_cast<const float4*>(vec + h * D + 32 * kq + 4 * i);
+        acc = fmaf(col[4 * i], x.x, fmaf(col[4 * i + 1], x.y, fmaf(col[4 * i + 2], x.z, fmaf(col[4 * i + 3], x.w, acc))));
+      }
+      s_part[(kq * GM + h) * D + j] = acc;
+    }
+  }
+}
 
-template <int DT, int SLOTS>
-__global__ void __launch_bounds__(PQ_THREADS) prepare_queries_kernel(DecodeArgs a) {
-  __shared__ __align__(16) float s_q[FQ_MAX_GROUP][D];
-  __shared__ __align__(16) float s_r[FQ_MAX_GROUP][D];
-  __shared__ __align__(16) float s_s[FQ_MAX_GROUP][D];
-  __shared__ __align__(16) float s_part[4][FQ_MAX_GROUP][D];
-  __shared__ float s_st[D * ST_STRIDE];       // S transposed: s_st[k * ST_STRIDE + j] = S[j][k]
-  __shared__ float s_mx[2][FQ_MAX_GROUP][2];  // [q~, q_s][head][row half]
-  const int kvh = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+template <int GM>
+__device__ __forceinline__ void quarter_dot_any(const float (&col)[32], const float* vec, int j, int kq, int G,
+                                                float* s_part) {
+  if (G <= 4) quarter_dot_g<4 < GM ? 4 : GM, GM>(col, vec, j, kq, G, s_part);
+  else if (G <= 8) quarter_dot_g<8 < GM ? 8 : GM, GM>(col, vec, j, kq, G, s_part);
+  else quarter_dot_g<GM, GM>(col, vec, j, kq, G, s_part);
+}
+
+// LDS floats used by prepare_group for groups of up to GM heads.
+template <int GM>
+constexpr int prep_lds_floats() { return 7 * GM * D + 6 * GM; }
+
+// The query work of one (KV head, sequence) by PQ_THREADS threads (thread =
+// (coordinate j, k-quarter kq)), lds = prep_lds_floats<GM>() floats:
+//   q~[h][j]  = sum_k Pi[j][k] q[h][k]     (column j of Pi^T)
+//   q_s[h][j] = sum_k S[j][k] q~[h][k]     (column j of S^T)
+// written to qrot / qs when write_vec, and with SLOTS > 0 the FQ_QOPS x 64
+// per-lane operands of the packed split kernel to ops (global memory or LDS; the
+// caller synchronizes before reading them).
+template <int DT, int SLOTS, int GM>
+__device__ __forceinline__ void prepare_group(const DecodeArgs& a, int kvh, int b, int tid, float* lds, uint4* ops,
+                                              bool write_vec) {
+  float* const s_q = lds;                    // [GM][D]
+  float* const s_r = s_q + GM * D;           // [GM][D]
+  float* const s_s = s_r + GM * D;           // [GM][D]
+  float* const s_part = s_s + GM * D;        // [4][GM][D]
+  float* const s_mx = s_part + 4 * GM * D;   // [2][GM][2]: [q~, q_s][head][row half]
+  float* const s_mq = s_mx + 4 * GM;         // [GM]
+  float* const s_ms = s_mq + GM;             // [GM]
   const int j = tid & (D - 1);
   const int kq = __builtin_amdgcn_readfirstlane(tid >> 7);
   const int G = a.group;
   const bool qjl = a.qjl_on != 0;
   const int64_t row0 = (static_cast<int64_t>(b) * a.hq + kvh * G) * D;
-  // q~[h][j] = sum_k Pi[j][k] q[h][k] = sum_k Pi^T[k][j] q[h][k]: column j of Pi^T
-  float pc[32];
+  // both matrices by columns: 32 loads each, every one 256 contiguous bytes per wave
+  float pc[32], sc[32];
   col_quarter_load(a.pit, j, kq, pc);
-  // S arrives in one coalesced pass (float4 number tid + 512 i) and is transposed in LDS
-  float4 sv[8];
-  {
-    const float4* src = reinterpret_cast<const float4*>(qjl ? a.smat : a.pit);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) sv[i] = src[tid + PQ_THREADS * i];
-  }
+  col_quarter_load(qjl ? a.sit : a.pit, j, kq, sc);
   for (int h = kq; h < G; h += 4) {
     const int64_t off = row0 + h * D + j;
     if constexpr (DT == FQ_BF16)
-      s_q[h][j] = __uint_as_float(static_cast<uint32_t>(static_cast<const uint16_t*>(a.q)[off]) << 16);
+      s_q[h * D + j] = __uint_as_float(static_cast<uint32_t>(static_cast<const uint16_t*>(a.q)[off]) << 16);
     else
-      s_q[h][j] = static_cast<const float*>(a.q)[off];
-  }
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int f = tid + PQ_THREADS * i;  // S[r][4c .. 4c+3]
-    const int r = f >> 5, c4 = 4 * (f & 31);
-    s_st[(c4 + 0) * ST_STRIDE + r] = sv[i].x;
-    s_st[(c4 + 1) * ST_STRIDE + r] = sv[i].y;
-    s_st[(c4 + 2) * ST_STRIDE + r] = sv[i].z;
-    s_st[(c4 + 3) * ST_STRIDE + r] = sv[i].w;
+      s_q[h * D + j] = static_cast<const float*>(a.q)[off];
   }
   __syncthreads();
-  auto dot = [&](const float (&col)[32], const float (*vec)[D]) {
-    if (G <= 4) quarter_dot<4>(col, vec, j, kq, G, s_part);
-    else if (G <= 8) quarter_dot<8>(col, vec, j, kq, G, s_part);
-    else quarter_dot<16>(col, vec, j, kq, G, s_part);
-  };
-  dot(pc, s_q);
+  quarter_dot_any<GM>(pc, s_q, j, kq, G, s_part);
   __syncthreads();
   for (int h = kq; h < G; h += 4) {
-    const float v = (s_part[0][h][j] + s_part[1][h][j]) + (s_part[2][h][j] + s_part[3][h][j]);
-    s_r[h][j] = v;
-    a.qrot[row0 + h * D + j] = v;
+    const float v = (s_part[(0 * GM + h) * D + j] + s_part[(1 * GM + h) * D + j]) +
+                    (s_part[(2 * GM + h) * D + j] + s_part[(3 * GM + h) * D + j]);
+    s_r[h * D + j] = v;
+    if (write_vec) a.qrot[row0 + h * D + j] = v;
   }
   __syncthreads();
   if (qjl) {
-    float sc[32];  // S[j][32 kq + i]
-#pragma unroll
-    for (int i = 0; i < 32; ++i) sc[i] = s_st[(32 * kq + i) * ST_STRIDE + j];
-    dot(sc, s_r);  // q_s[h][j] = sum_k S[j][k] q~[h][k]
+    quarter_dot_any<GM>(sc, s_r, j, kq, G, s_part);
     __syncthreads();
   }
   for (int h = kq; h < G; h += 4) {
     float v = 0.f;
     if (qjl) {
-      v = (s_part[0][h][j] + s_part[1][h][j]) + (s_part[2][h][j] + s_part[3][h][j]);
-      a.qs[row0 + h * D + j] = v;
+      v = (s_part[(0 * GM + h) * D + j] + s_part[(1 * GM + h) * D + j]) +
+          (s_part[(2 * GM + h) * D + j] + s_part[(3 * GM + h) * D + j]);
+      if (write_vec) a.qs[row0 + h * D + j] = v;
     }
-    s_s[h][j] = v;
+    s_s[h * D + j] = v;
   }
   __syncthreads();
-  if constexpr (SLOTS == 0) return;
-  // ---- per-head maxima (each wave holds 64 coordinates of the heads of its quarter)
-  for (int h = kq; h < G; h += 4) {
-    const float mr = wave_max(fabsf(s_r[h][j]));
-    const float ms = wave_max(fabsf(s_s[h][j]));
-    if ((j & 63) == 0) {
-      s_mx[0][h][j >> 6] = mr;
-      s_mx[1][h][j >> 6] = ms;
+  if constexpr (SLOTS > 0) {
+    // per-head maxima (each wave holds 64 coordinates of the heads of its quarter)
+    for (int h = kq; h < G; h += 4) {
+      const float mr = wave_max(fabsf(s_r[h * D + j]));
+      const float ms = wave_max(fabsf(s_s[h * D + j]));
+      if ((j & 63) == 0) {
+        s_mx[(0 * GM + h) * 2 + (j >> 6)] = mr;
+        s_mx[(1 * GM + h) * 2 + (j >> 6)] = ms;
+      }
     }
+    __syncthreads();
+    if (tid < G) {
+      s_mq[tid] = fmaxf(s_mx[(0 * GM + tid) * 2], s_mx[(0 * GM + tid) * 2 + 1]);
+      s_ms[tid] = fmaxf(s_mx[(1 * GM + tid) * 2], s_mx[(1 * GM + tid) * 2 + 1]);
+    }
+    __syncthreads();
+    for (int idx = tid; idx < FQ_QOPS * 64; idx += PQ_THREADS)
+      ops[idx] = query_operand<SLOTS>(idx >> 6, idx & 63, G, s_r, s_s, s_mq, s_ms, a.scale);
   }
-  __syncthreads();
-  __shared__ float s_mq[FQ_MAX_GROUP], s_ms[FQ_MAX_GROUP];
-  if (tid < G) {
-    s_mq[tid] = fmaxf(s_mx[0][tid][0], s_mx[0][tid][1]);
-    s_ms[tid] = fmaxf(s_mx[1][tid][0], s_mx[1][tid][1]);
-  }
-  __syncthreads();
-  uint4* ops = a.qops + (static_cast<int64_t>(b) * a.hkv + kvh) * (FQ_QOPS * 64);
-  constexpr int SL = SLOTS > 0 ? SLOTS : 1;
-  for (int idx = tid; idx < FQ_QOPS * 64; idx += PQ_THREADS)
-    ops[idx] = query_operand<SL>(idx >> 6, idx & 63, G, &s_r[0][0], &s_s[0][0], s_mq, s_ms, a.scale);
+}
+
+// One work-group per (KV head, sequence).
+template <int DT, int SLOTS>
+__global__ void __launch_bounds__(PQ_THREADS) prepare_queries_kernel(DecodeArgs a) {
+  __shared__ __align__(16) float s_p[prep_lds_floats<FQ_MAX_GROUP>()];
+  const int kvh = blockIdx.x, b = blockIdx.y;
+  prepare_group<DT, SLOTS, FQ_MAX_GROUP>(a, kvh, b, threadIdx.x, s_p,
+                                         a.qops + (static_cast<int64_t>(b) * a.hkv + kvh) * (FQ_QOPS * 64), true);
 }
 
 // ---------------------------------------------------------------- kernel 2
@@ -881,13 +887,19 @@ __global__ void __launch_bounds__(256, 2) split_mfma4_kernel(DecodeArgs a) {
 // running max is only moved when a page's max exceeds it by more than 8, so
 // probabilities stay below 2^8 and fp16-splittable.
 // Work-group shape per slot layout: waves, register-ring depth, waves per SIMD.
-constexpr int PK4_WAVES = 4, PK4_RING = 3, PK4_OCC = 2;  // SLOTS 4
+constexpr int PK4_WAVES = 4, PK4_RING = 2, PK4_OCC = 2;  // SLOTS 4
 constexpr int PK2_WAVES = 8, PK2_RING = 2, PK2_OCC = 4;  // SLOTS 2
+constexpr int PKF_WAVES = 8, PKF_RING = 2, PKF_OCC = 2;  // the only split (query preparation in-kernel)
 constexpr int PK_SIGN_BASE = 0;       // 16 x 32 x 8 B
 constexpr int PK_CODE_BASE = 4096;    // 256 x 32 x 8 B (4-bit) or 256 x 16 x 16 B (2-bit)
 constexpr int PK_STAGE_BASE = 69632;  // 256 x 16 B staging for the table build
 constexpr int PK_QOPS_BASE = 73728;   // 8 x 64 lanes x 16 B code-product operands
 constexpr int PK_LDS_BYTES = PK_QOPS_BASE + 8 * 64 * 16;  // 80 KB: two work-groups per CU
+// In-kernel query preparation (groups of up to 8 heads) uses the code-table area
+// before the table is built: its scratch, then the FQ_QOPS x 64 operands.
+constexpr int PK_PREP_GM = 8;
+constexpr int PK_PREP_OPS = PK_CODE_BASE + ((prep_lds_floats<PK_PREP_GM>() * 4 + 255) / 256) * 256;
+static_assert(PK_PREP_OPS + FQ_QOPS * 64 * 16 <= PK_STAGE_BASE, "query preparation fits the code-table area");
 constexpr float PK_TAU = 8.0f;
 
 template <int CTRL>
@@ -975,9 +987,15 @@ __device__ __forceinline__ void pk_load(const DecodeArgs& a, int64_t rec0, int n
   }
 }
 
-template <int BITS, int SLOTS, int WAVES, int RING, int OCC>
+// PREP < 0: one split of many, query operands from prepare_queries_kernel,
+// partial results for merge_unrotate_kernel. PREP = the query dtype: the only
+// split of its (KV head, sequence); the work-group prepares its own query
+// operands (prepare_group, in the LDS the code table takes later) and writes
+// the un-rotated output itself.
+template <int BITS, int SLOTS, int WAVES, int RING, int OCC, int PREP>
 __global__ void __launch_bounds__(WAVES * 64, OCC) packed_decode_kernel(DecodeArgs a) {
   static_assert(BITS == 4 || BITS == 2, "4- or 2-bit codes");
+  static_assert(PREP < 0 || WAVES * 64 == PQ_THREADS, "in-kernel query preparation takes PQ_THREADS threads");
   constexpr int CB = D * BITS / 8;  // code bytes per vector
   __shared__ __align__(16) uint8_t s_lds[PK_LDS_BYTES];
   const uint8_t* const s_code = s_lds + PK_CODE_BASE;
@@ -1024,7 +1042,7 @@ __global__ void __launch_bounds__(WAVES * 64, OCC) packed_decode_kernel(DecodeAr
   lo.sg = static_cast<uint32_t>(n * 16 + 4 * g);
   lo.vc = static_cast<uint32_t>(4 * g * CB + BITS * n);
 
-  // ---- the wave's first two pages are requested before any set-up work
+  // ---- the wave's first RING - 1 pages are requested before any set-up work
   PkPage<BITS> ring[RING];
   if (my_pages > 0) {
 #pragma unroll
@@ -1032,17 +1050,31 @@ __global__ void __launch_bounds__(WAVES * 64, OCC) packed_decode_kernel(DecodeAr
       pk_load(a, rec_of(bt_cur, min(k, min(64, my_pages) - 1)), n, lo, gptr, sgn_base, ring[k]);
   }
 
-  // ---- query operands, prepared per lane by the query kernel. The code-product
-  // operands (shared by every wave) are read from LDS at each step.
-  h8 qs[4];  // SLOTS 2: sign-product A operands
+  // ---- query operands, prepared per lane by the query kernel. With two heads per
+  // lane (SLOTS 2) registers are short, so the code-product operands (the same for
+  // every wave) are read from LDS at each step.
+  h8 qs[4];   // SLOTS 2: sign-product A operands
+  h8 qmr[8];  // SLOTS 4: code-product A operands, held in registers (SLOTS 2 reads them from LDS)
   float cf[HL];  // score factor of this lane's head(s) in the score layout
   {
-    const uint4* const ops = a.qops + (static_cast<int64_t>(b) * a.hkv + kvh) * (FQ_QOPS * 64);
+    const uint4* ops;
+    if constexpr (PREP >= 0) {
+      uint4* const s_ops = reinterpret_cast<uint4*>(s_lds + PK_PREP_OPS);
+      prepare_group<PREP, SLOTS, PK_PREP_GM>(a, kvh, b, tid, reinterpret_cast<float*>(s_lds + PK_CODE_BASE), s_ops,
+                                             false);
+      __syncthreads();
+      ops = s_ops;
+    } else {
+      ops = a.qops + (static_cast<int64_t>(b) * a.hkv + kvh) * (FQ_QOPS * 64);
+    }
     for (int idx = tid; idx < 8 * 64; idx += WAVES * 64)
       reinterpret_cast<uint4*>(s_lds + PK_QOPS_BASE)[idx] = ops[idx];
     if constexpr (SLOTS == 2) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) qs[i] = __builtin_bit_cast(h8, ops[(8 + i) * 64 + lane]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) qmr[i] = __builtin_bit_cast(h8, ops[i * 64 + lane]);
     }
     // the factor of head h sits in operand 12 of lane h * SLOTS
 #pragma unroll
@@ -1141,7 +1173,7 @@ __global__ void __launch_bounds__(WAVES * 64, OCC) packed_decode_kernel(DecodeAr
         const uint4 e = lds_u4(s_code, tab_off(d.kc[i >> 2], copy16, i & 3));
         kop = as_h8(e.x, e.y, e.z, e.w);
       }
-      const h8 qmi = s_qm[i * 64];
+      const h8 qmi = SLOTS == 4 ? qmr[i] : s_qm[i * 64];
       accM = mfma32(qmi, kop, accM);
       if (i < 4) {
         const uint2 z0 = lds_u2(s_sign, tab_off(sgl, copy8, i));
@@ -1284,6 +1316,41 @@ __global__ void __launch_bounds__(WAVES * 64, OCC) packed_decode_kernel(DecodeAr
       s_o[(wave * HP + HL * g + k) * D + dim] = (acc_o[t][2 * k] + acc_o[t][2 * k + 1]) * unscale;
   }
   __syncthreads();
+  if constexpr (PREP >= 0) {
+    // the only split: o_rot = O / L per head, then out = Pi^T o_rot
+    float* const s_or = s_ml + WAVES * HP * 2;  // [G][D]
+    float* const s_pp = s_or + PK_PREP_GM * D;  // [4][PK_PREP_GM][D]
+    const int jj = tid & (D - 1);
+    const int kq = __builtin_amdgcn_readfirstlane(tid >> 7);
+    float pc[32];
+    col_quarter_load(a.pi, jj, kq, pc);
+    for (int idx = tid; idx < G * D; idx += WAVES * 64) {
+      const int hh = idx / D, j = idx % D;
+      float M = -INFINITY;
+#pragma unroll
+      for (int w = 0; w < WAVES; ++w)
+        if (s_ml[(w * HP + hh) * 2 + 1] > 0.f) M = fmaxf(M, s_ml[(w * HP + hh) * 2]);
+      float o = 0.f, L = 0.f;
+#pragma unroll
+      for (int w = 0; w < WAVES; ++w) {
+        const float lw = s_ml[(w * HP + hh) * 2 + 1];
+        if (lw > 0.f) {
+          const float f = exp2f(s_ml[(w * HP + hh) * 2] - M);
+          o = fmaf(s_o[(w * HP + hh) * D + j], f, o);
+          L = fmaf(lw, f, L);
+        }
+      }
+      s_or[hh * D + j] = L > 0.f ? o / L : 0.f;
+    }
+    __syncthreads();
+    quarter_dot_any<PK_PREP_GM>(pc, s_or, jj, kq, G, s_pp);
+    __syncthreads();
+    const int64_t head0 = static_cast<int64_t>(b) * a.hq + kvh * G;
+    for (int h = kq; h < G; h += 4)
+      a.out[(head0 + h) * D + jj] = (s_pp[(0 * PK_PREP_GM + h) * D + jj] + s_pp[(1 * PK_PREP_GM + h) * D + jj]) +
+                                    (s_pp[(2 * PK_PREP_GM + h) * D + jj] + s_pp[(3 * PK_PREP_GM + h) * D + jj]);
+    return;
+  }
   constexpr float LN2 = 0.6931471805599453f;
   for (int idx = tid; idx < G * D; idx += WAVES * 64) {
     const int hh = idx / D, j = idx % D;
@@ -1331,6 +1398,7 @@ int launch_decode(void* stream, const fq_quantizer& q, const fq_cache& c, const 
   a.pi = q.rotation_matrix;
   a.pit = q.rotation_t;
   a.smat = q.qjl_matrix;
+  a.sit = q.qjl_matrix_t;
   a.levels = q.levels;
   a.k_codes = c.k_codes;
   a.k_norm = c.k_norm;
@@ -1367,6 +1435,20 @@ int launch_decode(void* stream, const fq_quantizer& q, const fq_cache& c, const 
   const bool valu = impl && std::strcmp(impl, "valu") == 0;
   const bool v1 = impl && std::strcmp(impl, "mfma_v1") == 0;
   const int slots = (!valu && !v1) ? (a.group <= 4 ? 4 : a.group <= 8 ? 2 : 0) : 0;
+  dim3 grid(num_splits, c.num_kv_heads, batch);
+  if (slots > 0 && num_splits == 1 && std::getenv("FQ_DECODE_UNFUSED") == nullptr) {
+    // one work-group per (KV head, sequence) does everything in one launch
+    const dim3 blk(PKF_WAVES * 64);
+#define FQ_FUSED(BITS, SL, DT) \
+  hipLaunchKernelGGL((packed_decode_kernel<BITS, SL, PKF_WAVES, PKF_RING, PKF_OCC, DT>), grid, blk, 0, st, a)
+    const bool bf = q_dtype == FQ_BF16;
+    if (q.bits == 4 && slots == 4) { if (bf) FQ_FUSED(4, 4, FQ_BF16); else FQ_FUSED(4, 4, FQ_F32); }
+    else if (q.bits == 4) { if (bf) FQ_FUSED(4, 2, FQ_BF16); else FQ_FUSED(4, 2, FQ_F32); }
+    else if (slots == 4) { if (bf) FQ_FUSED(2, 4, FQ_BF16); else FQ_FUSED(2, 4, FQ_F32); }
+    else { if (bf) FQ_FUSED(2, 2, FQ_BF16); else FQ_FUSED(2, 2, FQ_F32); }
+#undef FQ_FUSED
+    return static_cast<int>(hipGetLastError());
+  }
   const dim3 pgrid(c.num_kv_heads, batch);
   if (q_dtype == FQ_BF16) {
     if (slots == 4) hipLaunchKernelGGL((prepare_queries_kernel<FQ_BF16, 4>), pgrid, dim3(PQ_THREADS), 0, st, a);
@@ -1377,15 +1459,14 @@ int launch_decode(void* stream, const fq_quantizer& q, const fq_cache& c, const 
     else if (slots == 2) hipLaunchKernelGGL((prepare_queries_kernel<FQ_F32, 2>), pgrid, dim3(PQ_THREADS), 0, st, a);
     else hipLaunchKernelGGL((prepare_queries_kernel<FQ_F32, 0>), pgrid, dim3(PQ_THREADS), 0, st, a);
   }
-  dim3 grid(num_splits, c.num_kv_heads, batch);
   if (slots == 4 && q.bits == 4)
-    hipLaunchKernelGGL((packed_decode_kernel<4, 4, PK4_WAVES, PK4_RING, PK4_OCC>), grid, dim3(PK4_WAVES * 64), 0, st, a);
+    hipLaunchKernelGGL((packed_decode_kernel<4, 4, PK4_WAVES, PK4_RING, PK4_OCC, -1>), grid, dim3(PK4_WAVES * 64), 0, st, a);
   else if (slots == 2 && q.bits == 4)
-    hipLaunchKernelGGL((packed_decode_kernel<4, 2, PK2_WAVES, PK2_RING, PK2_OCC>), grid, dim3(PK2_WAVES * 64), 0, st, a);
+    hipLaunchKernelGGL((packed_decode_kernel<4, 2, PK2_WAVES, PK2_RING, PK2_OCC, -1>), grid, dim3(PK2_WAVES * 64), 0, st, a);
   else if (slots == 4)
-    hipLaunchKernelGGL((packed_decode_kernel<2, 4, PK4_WAVES, PK4_RING, PK4_OCC>), grid, dim3(PK4_WAVES * 64), 0, st, a);
+    hipLaunchKernelGGL((packed_decode_kernel<2, 4, PK4_WAVES, PK4_RING, PK4_OCC, -1>), grid, dim3(PK4_WAVES * 64), 0, st, a);
   else if (slots == 2)
-    hipLaunchKernelGGL((packed_decode_kernel<2, 2, PK2_WAVES, PK2_RING, PK2_OCC>), grid, dim3(PK2_WAVES * 64), 0, st, a);
+    hipLaunchKernelGGL((packed_decode_kernel<2, 2, PK2_WAVES, PK2_RING, PK2_OCC, -1>), grid, dim3(PK2_WAVES * 64), 0, st, a);
   else if (q.bits == 4 && !valu)
     hipLaunchKernelGGL(split_mfma4_kernel, grid, dim3(256), 0, st, a);
   else if (q.bits == 4)

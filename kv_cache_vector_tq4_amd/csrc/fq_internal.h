@@ -10,7 +10,7 @@
 #define FQ_BLOCK 16
 #define FQ_MAX_GROUP 16
 #define FQ_MAX_SPLITS 64
-#define FQ_VERSION 100
+#define FQ_VERSION 101
 
 namespace fq {
 

@@ -39,6 +39,7 @@ class QuantizerT(ctypes.Structure):
         ("rotation_t", ctypes.c_void_p),
         ("wht_signs", ctypes.c_void_p),
         ("qjl_matrix", ctypes.c_void_p),
+        ("qjl_matrix_t", ctypes.c_void_p),
         ("mfma_operands", ctypes.c_void_p),
     ]
 
@@ -67,7 +68,7 @@ EXPORTS = {
     "fq_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "fq_version": (ctypes.c_int, []),
     "fq_build_codebook": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_uint64,
-                                         ctypes.c_uint64, ctypes.c_int] + [ctypes.c_void_p] * 6),
+                                         ctypes.c_uint64, ctypes.c_int] + [ctypes.c_void_p] * 7),
     "fq_compress": (ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(QuantizerT), ctypes.POINTER(CacheT),
                                    ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int64,
                                    ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p,
@@ -129,12 +130,14 @@ def build_codebook(bits=4, head_dim=128, rotation=ROT_HAAR, rot_seed=1, qjl_seed
         "rotation_t": np.zeros((head_dim, head_dim), np.float32),
         "wht_signs": np.zeros(head_dim, np.float32),
         "qjl_matrix": np.zeros((max(qjl_dim, 1), head_dim), np.float32),
+        "qjl_matrix_t": np.zeros((head_dim, max(qjl_dim, 1)), np.float32),
     }
     p = lambda a: a.ctypes.data_as(ctypes.c_void_p)
     st = lib().fq_build_codebook(bits, head_dim, rotation, rot_seed, qjl_seed, qjl_dim,
                                  p(out["levels"]), p(out["boundaries"]), p(out["rotation_matrix"]),
                                  p(out["rotation_t"]), p(out["wht_signs"]),
-                                 p(out["qjl_matrix"]) if qjl_dim else None)
+                                 p(out["qjl_matrix"]) if qjl_dim else None,
+                                 p(out["qjl_matrix_t"]) if qjl_dim else None)
     _check(st, "fq_build_codebook")
     out.update(bits=bits, head_dim=head_dim, rotation=rotation, qjl_dim=qjl_dim)
     return out
@@ -165,7 +168,8 @@ class Quantizer:
 
         self.host = build_codebook(bits, head_dim, rotation, rot_seed, qjl_seed, qjl_dim)
         self.bits, self.head_dim, self.rotation, self.qjl_dim = bits, head_dim, rotation, qjl_dim
-        keys = ("levels", "boundaries", "rotation_matrix", "rotation_t", "wht_signs", "qjl_matrix")
+        keys = ("levels", "boundaries", "rotation_matrix", "rotation_t", "wht_signs", "qjl_matrix",
+                "qjl_matrix_t")
         self.dev = {k: torch.from_numpy(np.ascontiguousarray(self.host[k])).to(device) for k in keys}
         if prepared:
             ops = pack_mfma_operands(self.host["rotation_matrix"], self.host["qjl_matrix"] if qjl_dim else None)
@@ -175,6 +179,7 @@ class Quantizer:
                                  d["boundaries"].data_ptr(), d["rotation_matrix"].data_ptr(),
                                  d["rotation_t"].data_ptr(), d["wht_signs"].data_ptr(),
                                  d["qjl_matrix"].data_ptr() if qjl_dim else None,
+                                 d["qjl_matrix_t"].data_ptr() if qjl_dim else None,
                                  d["mfma_operands"].data_ptr() if prepared else None)
 
 

@@ -50,6 +50,7 @@ def test_builder_matches_oracle(bits, rot):
     assert np.max(np.abs(pi - ora["pi"])) <= 1e-6
     assert np.array_equal(lib_cb["rotation_t"], lib_cb["rotation_matrix"].T)
     assert np.array_equal(lib_cb["qjl_matrix"].astype(np.float64), ora["s"])
+    assert np.array_equal(lib_cb["qjl_matrix_t"], lib_cb["qjl_matrix"].T)
     if rot == fq.ROT_WHT:
         assert np.array_equal(lib_cb["wht_signs"].astype(np.float64), ora["signs"])
         assert np.array_equal(pi, ora["pi"])
@@ -67,18 +68,18 @@ def test_builder_errors():
     L = fq.lib()
     buf = np.zeros(128 * 128, np.float32)
     p = buf.ctypes.data_as(ctypes.c_void_p)
-    assert L.fq_build_codebook(3, 128, 0, 1, 2, 128, p, p, None, None, None, None) == fq.FQ_ERR_UNSUPPORTED
-    assert L.fq_build_codebook(4, 64, 0, 1, 2, 128, p, p, None, None, None, None) == fq.FQ_ERR_UNSUPPORTED
-    assert L.fq_build_codebook(4, 128, 5, 1, 2, 128, p, p, None, None, None, None) == fq.FQ_ERR_INVALID_ARG
-    assert L.fq_build_codebook(4, 128, 0, 1, 2, 128, None, p, None, None, None, None) == fq.FQ_ERR_INVALID_ARG
-    assert L.fq_build_codebook(4, 128, 0, 1, 2, 64, p, p, None, None, None, None) == fq.FQ_ERR_UNSUPPORTED
+    assert L.fq_build_codebook(3, 128, 0, 1, 2, 128, p, p, None, None, None, None, None) == fq.FQ_ERR_UNSUPPORTED
+    assert L.fq_build_codebook(4, 64, 0, 1, 2, 128, p, p, None, None, None, None, None) == fq.FQ_ERR_UNSUPPORTED
+    assert L.fq_build_codebook(4, 128, 5, 1, 2, 128, p, p, None, None, None, None, None) == fq.FQ_ERR_INVALID_ARG
+    assert L.fq_build_codebook(4, 128, 0, 1, 2, 128, None, p, None, None, None, None, None) == fq.FQ_ERR_INVALID_ARG
+    assert L.fq_build_codebook(4, 128, 0, 1, 2, 64, p, p, None, None, None, None, None) == fq.FQ_ERR_UNSUPPORTED
 
 
 def _fake_structs(bits=4, qjl=128, hkv=2):
     """Structs whose pointers are aligned host addresses: only argument checks may see them."""
     store = np.zeros(1 << 16, np.float32)
     base = (store.ctypes.data + 255) & ~255
-    qz = fq.QuantizerT(bits, 128, fq.ROT_HAAR, qjl, base, base, base, base, base, base, None)
+    qz = fq.QuantizerT(bits, 128, fq.ROT_HAAR, qjl, base, base, base, base, base, base, base, None)
     cz = fq.CacheT(4, 16, hkv, 128, bits, qjl, base, base, base, base, base, base)
     return store, base, qz, cz
 
@@ -99,7 +100,7 @@ def test_compress_argument_checks():
     assert call(qz, cz, slots=None) == fq.FQ_ERR_INVALID_ARG
     assert call(qz, cz, k=base + 2) == fq.FQ_ERR_INVALID_ARG  # vectors must be 16-byte aligned
     assert call(qz, cz, hs=4) == fq.FQ_ERR_INVALID_ARG        # 8-byte head stride
-    qb = fq.QuantizerT(3, 128, 0, 128, base, base, base, base, base, base, None)
+    qb = fq.QuantizerT(3, 128, 0, 128, base, base, base, base, base, base, base, None)
     assert call(qb, cz) == fq.FQ_ERR_UNSUPPORTED
     cb = fq.CacheT(4, 8, 2, 128, 4, 128, base, base, base, base, base, base)
     assert call(qz, cb) == fq.FQ_ERR_UNSUPPORTED              # block size must be 16
@@ -107,9 +108,11 @@ def test_compress_argument_checks():
     assert call(qz, cm) == fq.FQ_ERR_INVALID_ARG              # bits differ from the quantizer's
     cn = fq.CacheT(4, 16, 2, 128, 4, 128, base, base, None, base, base, base)
     assert call(qz, cn) == fq.FQ_ERR_INVALID_ARG              # QJL keys need k_qjl
-    qn = fq.QuantizerT(4, 128, 0, 128, base, base, base, None, base, base, None)
+    qn = fq.QuantizerT(4, 128, 0, 128, base, base, base, None, base, base, base, None)
     assert call(qn, cz) == fq.FQ_ERR_INVALID_ARG              # Pi^T required
-    qm = fq.QuantizerT(4, 128, 0, 128, base, base, base, base, base, base, base + 8)
+    qt = fq.QuantizerT(4, 128, 0, 128, base, base, base, base, base, base, None, None)
+    assert call(qt, cz) == fq.FQ_ERR_INVALID_ARG              # S^T required with QJL
+    qm = fq.QuantizerT(4, 128, 0, 128, base, base, base, base, base, base, base, base + 8)
     assert call(qm, cz) == fq.FQ_ERR_INVALID_ARG              # operand buffer must be 16-byte aligned
 
 
@@ -140,7 +143,8 @@ def test_decode_argument_checks_and_workspace():
 def test_auto_splits():
     assert fq.auto_splits(1, 8, 4096) == 16
     assert fq.auto_splits(1, 8, 32768) == 64
-    assert fq.auto_splits(32, 8, 4096) == 2
+    assert fq.auto_splits(32, 8, 4096) == 1
+    assert fq.auto_splits(16, 8, 4096) == 4
     assert fq.auto_splits(64, 8, 4096) == 1
     assert fq.auto_splits(1, 1, 100) == 1
 

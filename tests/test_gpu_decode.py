@@ -36,24 +36,27 @@ def test_decode_tiny(gpu_lib, bits, rot):
     assert err <= parity.DECODE_TOL
 
 
+@pytest.mark.parametrize("splits", [3, 1])
 @pytest.mark.parametrize("bits", [4, 2])
 @pytest.mark.parametrize("G", [1, 4, 8, 16])
-def test_decode_groups_ragged(gpu_lib, G, bits):
+def test_decode_groups_ragged(gpu_lib, G, bits, splits):
     w, inp = parity.small_workload(3, 2 * G, 2, [5, 333, 1000], 1008, bits=bits, seed=G)
-    out, ref, _ = _decode_case(w, inp, num_splits=3)
+    out, ref, _ = _decode_case(w, inp, num_splits=splits)
     assert np.max(np.abs(out - ref)) <= parity.DECODE_TOL
 
 
+@pytest.mark.parametrize("splits", [0, 1])
 @pytest.mark.parametrize("bits", [4, 2])
-def test_decode_mse_only_keys(gpu_lib, bits):
+def test_decode_mse_only_keys(gpu_lib, bits, splits):
     w, inp = parity.small_workload(2, 8, 2, [700, 64], 704, bits=bits, seed=41)
-    out, ref, _ = _decode_case(w, inp, with_qjl=False)
+    out, ref, _ = _decode_case(w, inp, with_qjl=False, num_splits=splits)
     assert np.max(np.abs(out - ref)) <= parity.DECODE_TOL
 
 
-def test_decode_empty_and_single_token(gpu_lib):
+@pytest.mark.parametrize("splits", [2, 1])
+def test_decode_empty_and_single_token(gpu_lib, splits):
     w, inp = parity.small_workload(3, 4, 2, [0, 1, 17], 32, seed=43)
-    out, ref, _ = _decode_case(w, inp, num_splits=2)
+    out, ref, _ = _decode_case(w, inp, num_splits=splits)
     assert np.all(out[0] == 0)
     assert np.max(np.abs(out - ref)) <= parity.DECODE_TOL
 
@@ -84,9 +87,11 @@ def test_decode_block_permutation_is_bit_identical(gpu_lib):
     assert np.array_equal(out, o2)
 
 
-def test_decode_full_size_b32_sampled(gpu_lib):
-    """The batch-32 8B-shaped layer (lengths 3072..4096, 4 splits) in the launch configuration
-    the benchmark times; the oracle writes and checks three of the 32 sequences."""
+@pytest.mark.parametrize("splits", [0, 4])
+def test_decode_full_size_b32_sampled(gpu_lib, splits):
+    """The batch-32 8B-shaped layer (lengths 3072..4096) in the launch configuration the
+    benchmark times (the library's split choice: one split, single launch) and with the
+    4-way split; the oracle writes and checks three of the 32 sequences."""
     w = synth.workload(2)
     inp = synth.layer_inputs(w)
     seqs = [0, 13, 31]
@@ -102,7 +107,8 @@ def test_decode_full_size_b32_sampled(gpu_lib):
     host = parity.oracle_cache(inp, oq, seqs=seqs)
     blocks = np.concatenate([inp["block_tables"][b] for b in seqs])
     parity.upload_cache(host, cache, blocks=blocks)
-    out = fq.decode(qz, cache, t["q"], t["bt"], t["lens"], 4096, num_splits=4).cpu().numpy()
+    assert fq.auto_splits(32, 8, 4096) == 1
+    out = fq.decode(qz, cache, t["q"], t["bt"], t["lens"], 4096, num_splits=splits).cpu().numpy()
     ref = parity.oracle_decode(inp, host, oq, seqs=seqs)
     err = np.max(np.abs(out[seqs] - ref))
     print("max-abs", err, "cos vs exact", parity.cosine(out[seqs], parity.exact(inp, seqs)))
