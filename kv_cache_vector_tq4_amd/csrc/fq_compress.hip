@@ -433,14 +433,11 @@ __device__ __forceinline__ void compress_tile(const CompressArgs& a, int kind, i
   }
 }
 
-// Quantization cells and codebook staging; callers synchronize afterwards.
+// Quantization cells from the codebook staged in s_bl (boundaries at [0, L-1),
+// levels at [16, 16+L)); callers synchronize afterwards.
 template <int BITS>
-__device__ __forceinline__ void build_qtable(const CompressArgs& a, QCell* s_qt, float* s_qmap, float* s_bl,
-                                             int tid, int nthreads) {
+__device__ __forceinline__ void fill_qtable(QCell* s_qt, float* s_qmap, const float* s_bl, int tid, int nthreads) {
   constexpr int L = 1 << BITS;
-  if (tid < L - 1) s_bl[tid] = a.bnd[tid];
-  if (tid >= 32 && tid < 32 + L) s_bl[16 + tid - 32] = a.levels[tid - 32];
-  __syncthreads();
   const float b0 = s_bl[0], bm = s_bl[L - 2];
   const float w = (bm - b0) / static_cast<float>(QT_CELLS - 8);
   const float inv_w = 1.0f / w;
@@ -461,6 +458,30 @@ __device__ __forceinline__ void build_qtable(const CompressArgs& a, QCell* s_qt,
     }
     s_qt[cell] = QCell{cnt, bb, s_bl[16 + cnt], s_bl[16 + (cnt + 1 < L ? cnt + 1 : cnt)]};
   }
+}
+
+// Codebook value of thread tid for s_bl (boundary tid, or level tid - 32), or 0.
+template <int BITS>
+__device__ __forceinline__ float codebook_value(const CompressArgs& a, int tid) {
+  constexpr int L = 1 << BITS;
+  if (tid < L - 1) return a.bnd[tid];
+  if (tid >= 32 && tid < 32 + L) return a.levels[tid - 32];
+  return 0.f;
+}
+template <int BITS>
+__device__ __forceinline__ void stage_codebook(float* s_bl, int tid, float x) {
+  constexpr int L = 1 << BITS;
+  if (tid < L - 1) s_bl[tid] = x;
+  if (tid >= 32 && tid < 32 + L) s_bl[16 + tid - 32] = x;
+}
+
+// Quantization cells and codebook staging; callers synchronize afterwards.
+template <int BITS>
+__device__ __forceinline__ void build_qtable(const CompressArgs& a, QCell* s_qt, float* s_qmap, float* s_bl,
+                                             int tid, int nthreads) {
+  stage_codebook<BITS>(s_bl, tid, codebook_value<BITS>(a, tid));
+  __syncthreads();
+  fill_qtable<BITS>(s_qt, s_qmap, s_bl, tid, nthreads);
 }
 
 __device__ __forceinline__ uint4 pack8(const uint32_t (&u)[8]) {
@@ -548,10 +569,10 @@ __global__ void __launch_bounds__(64) compress_direct_kernel(CompressArgs a) {
 // small to fill the GPU with one wave per tile. The residual's fp16 hi / lo
 // fragments and |r|^2 partial sums cross the waves through LDS for the QJL
 // product.
-template <int BITS, int DT, bool KEY>
+template <int BITS, int DT, bool KEY, typename TableFn>
 __device__ __forceinline__ void compress_quarter(const CompressArgs& a, int kind, int64_t tile, int lane, int T,
                                                  const uint4* __restrict__ fpi, const uint4* __restrict__ fsm,
-                                                 const QCell* __restrict__ qt, float inv_w, float off,
+                                                 const QCell* __restrict__ qt, const float* s_qmap, TableFn table,
                                                  uint4* s_rh, uint4* s_rl, float* s_rr) {
   const int v = lane & 31, h = lane >> 5;
   const int64_t nvec = a.ntok * a.hkv;
@@ -600,19 +621,32 @@ __device__ __forceinline__ void compress_quarter(const CompressArgs& a, int kind
   const float n = sqrtf(ss);
   const float inv = n > 0.f ? 1.0f / n : 0.f;
 
-  // ---- row tile T of the rotation
-  f16v acc = f16v{};
+  // QJL fragments of row tile T, requested now so that they are in registers
+  // before the residual exchange (a barrier no load moves across)
+  hh8 sfh[KEY ? 8 : 1], sfl[KEY ? 8 : 1];
+  if constexpr (KEY) {
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      sfh[s] = __builtin_bit_cast(hh8, fsm[(T * 8 + s) * 64 + lane]);
+      sfl[s] = __builtin_bit_cast(hh8, fsm[(32 + T * 8 + s) * 64 + lane]);
+    }
+  }
+  // ---- row tile T of the rotation (hi and lo products in separate chains)
+  f16v acc = f16v{}, acc2 = f16v{};
 #pragma unroll
   for (int s = 0; s < 8; ++s) {
     const b8 ah = __builtin_bit_cast(b8, fpi[(T * 8 + s) * 64 + lane]);
     const b8 al = __builtin_bit_cast(b8, fpi[(32 + T * 8 + s) * 64 + lane]);
     acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, xb[s], acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, xb[s], acc, 0, 0, 0);
-    if constexpr (DT != FQ_BF16) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, xl[s], acc, 0, 0, 0);
+    acc2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, xb[s], acc2, 0, 0, 0);
+    if constexpr (DT != FQ_BF16) acc2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, xl[s], acc2, 0, 0, 0);
   }
   // acc[vv] = (Pi x / |x|)[64h + 16T + vv]
 #pragma unroll
-  for (int vv = 0; vv < 16; ++vv) acc[vv] *= inv;
+  for (int vv = 0; vv < 16; ++vv) acc[vv] = (acc[vv] + acc2[vv]) * inv;
+  // the quantization cells are built while the products run; uniform over the work-group
+  table();
+  const float inv_w = s_qmap[0], off = s_qmap[1];
 
   const int64_t rec = ((slot >> 4) * a.hkv + hd) * FQ_BLOCK + (slot & 15);
   const bool store = slot >= 0;
@@ -662,17 +696,17 @@ __device__ __forceinline__ void compress_quarter(const CompressArgs& a, int kind
       s_rl[(2 * T + q) * 64 + lane] = make_uint4(lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16), lo[4] | (lo[5] << 16), lo[6] | (lo[7] << 16));
     }
     __syncthreads();
-    f16v pacc = f16v{};
+    f16v pacc = f16v{}, pacc2 = f16v{};
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
       const hh8 rh = __builtin_bit_cast(hh8, s_rh[s * 64 + lane]);
       const hh8 rl = __builtin_bit_cast(hh8, s_rl[s * 64 + lane]);
-      const hh8 ah = __builtin_bit_cast(hh8, fsm[(T * 8 + s) * 64 + lane]);
-      const hh8 al = __builtin_bit_cast(hh8, fsm[(32 + T * 8 + s) * 64 + lane]);
-      pacc = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah, rh, pacc, 0, 0, 0);
-      pacc = __builtin_amdgcn_mfma_f32_32x32x16_f16(al, rh, pacc, 0, 0, 0);
-      pacc = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah, rl, pacc, 0, 0, 0);
+      pacc = __builtin_amdgcn_mfma_f32_32x32x16_f16(sfh[s], rh, pacc, 0, 0, 0);
+      pacc2 = __builtin_amdgcn_mfma_f32_32x32x16_f16(sfl[s], rh, pacc2, 0, 0, 0);
+      pacc2 = __builtin_amdgcn_mfma_f32_32x32x16_f16(sfh[s], rl, pacc2, 0, 0, 0);
     }
+#pragma unroll
+    for (int vv = 0; vv < 16; ++vv) pacc[vv] += pacc2[vv];
     // pacc[vv] = p[64h + 16T + vv]
     uint32_t sg = 0u;
 #pragma unroll
@@ -699,18 +733,25 @@ __global__ void __launch_bounds__(256) compress_split_kernel(CompressArgs a) {
   __shared__ uint4 s_rh[8 * 64], s_rl[8 * 64];
   __shared__ float s_rr[4 * 64];
   const int tid = threadIdx.x;
-  build_qtable<BITS>(a, s_qt, s_qmap, s_bl, tid, 256);
-  __syncthreads();
   const int kind = blockIdx.y;
   if (!a.src[kind]) return;  // uniform over the work-group
+  // Every global load is issued up front; the quantization cells are built from
+  // the codebook after the rotation products, which do not need them.
+  const float cbv = codebook_value<BITS>(a, tid);
+  auto table = [&]() {
+    stage_codebook<BITS>(s_bl, tid, cbv);
+    __syncthreads();
+    fill_qtable<BITS>(s_qt, s_qmap, s_bl, tid, 256);
+    __syncthreads();
+  };
   const uint4* ops = static_cast<const uint4*>(a.mfma_ops);
   const int T = __builtin_amdgcn_readfirstlane(tid >> 6);
   if (kind == 0)
-    compress_quarter<BITS, DT, true>(a, 0, blockIdx.x, tid & 63, T, ops, ops + 2 * FRAG_U4, s_qt, s_qmap[0],
-                                     s_qmap[1], s_rh, s_rl, s_rr);
+    compress_quarter<BITS, DT, true>(a, 0, blockIdx.x, tid & 63, T, ops, ops + 2 * FRAG_U4, s_qt, s_qmap, table,
+                                     s_rh, s_rl, s_rr);
   else
-    compress_quarter<BITS, DT, false>(a, 1, blockIdx.x, tid & 63, T, ops, ops, s_qt, s_qmap[0], s_qmap[1], s_rh,
-                                      s_rl, s_rr);
+    compress_quarter<BITS, DT, false>(a, 1, blockIdx.x, tid & 63, T, ops, ops, s_qt, s_qmap, table, s_rh, s_rl,
+                                      s_rr);
 }
 
 template <int BITS, int DT>
