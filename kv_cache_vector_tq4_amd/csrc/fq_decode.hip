@@ -118,60 +118,79 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u(uint32_t x) {
+  return static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(x), CTRL, 0xF, 0xF, true));
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+  return __uint_as_float(dpp_u<CTRL>(__float_as_uint(x)));
+}
+constexpr int DPP_XOR1 = 0xB1;    // quad_perm [1, 0, 3, 2]
+constexpr int DPP_XOR2 = 0x4E;    // quad_perm [2, 3, 0, 1]
+constexpr int DPP_ROR4 = 0x124;   // rotate right by 4 within a row of 16 lanes
+constexpr int DPP_ROR8 = 0x128;   // rotate right by 8 within a row of 16 lanes
+
+// Maximum / sum over the 16 lanes of a row.
+__device__ __forceinline__ float row_max(float x) {
+  x = fmaxf(x, dpp_f<DPP_XOR1>(x));
+  x = fmaxf(x, dpp_f<DPP_XOR2>(x));
+  x = fmaxf(x, dpp_f<DPP_ROR4>(x));
+  return fmaxf(x, dpp_f<DPP_ROR8>(x));
+}
+__device__ __forceinline__ float row_sum(float x) {
+  x += dpp_f<DPP_XOR1>(x);
+  x += dpp_f<DPP_XOR2>(x);
+  x += dpp_f<DPP_ROR4>(x);
+  return x + dpp_f<DPP_ROR8>(x);
+}
+
+// Maximum over the 64 lanes (rows by DPP, then the four row results).
+__device__ __forceinline__ float wave_max_dpp(float x) {
+  const float r = row_max(x);
+  const float a0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(r), 0));
+  const float a1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(r), 16));
+  const float a2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(r), 32));
+  const float a3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(r), 48));
+  return fmaxf(fmaxf(a0, a1), fmaxf(a2, a3));
+}
+
+// One power of two per head puts max |q~| in [128, 256); q_s takes that power
+// times QJL_R so that both score accumulators share the score factor, lowered if
+// q_s would exceed 2^15.
+__device__ __forceinline__ float head_qscale(float mqh, float msh) {
+  int ex = 0, eq = 0, es = 0;
+  if (mqh > 0.f) { frexpf(mqh, &ex); eq = 8 - ex; }
+  if (msh > 0.f) { frexpf(msh * QJL_R, &ex); es = 15 - ex; }
+  const int e_use = mqh > 0.f ? (msh > 0.f ? min(eq, es) : eq) : (msh > 0.f ? es : 0);
+  return ldexpf(1.f, e_use);
+}
+
 // Matrix-core query operand op (0 .. FQ_QOPS-1) of lane l of the packed split
-// kernel, from q~ (r) and q_s (sq) of the G query heads (rows of D floats) and
-// their per-head maxima |q~| (mq) and |q_s| (ms).
+// kernel, gathered from the fp16 hi / lo splits of q~ x qscale (qh, ql) and of
+// q_s x qscale QJL_R (sh, sl), rows of D halves per head, and the per-head score
+// factors cf:
 //   op 0..7   code-product operand of k-step op; op 0..3 also the sign-product
 //             operand when SLOTS = 4 (slots 2 / 3);
 //   op 8..11  SLOTS = 2: sign-product operand of k-step op - 8;
 //   op 12     the score factor of the lane's head in .x.
-// One power of two per head puts max |q~| in [128, 256); q_s takes that power
-// times QJL_R so that both accumulators share the score factor, lowered if q_s
-// would exceed 2^15.
 template <int SLOTS>
-__device__ uint4 query_operand(int op, int l, int G, const float* r, const float* sq, const float* mq,
-                               const float* ms, float scale) {
+__device__ __forceinline__ uint4 query_operand(int op, int l, int G, const uint16_t* qh, const uint16_t* ql,
+                                               const uint16_t* sh, const uint16_t* sl, const float* cf) {
   const int g = l >> 4, n = l & 15, h = n / SLOTS, s = n % SLOTS;
   uint4 u = make_uint4(0u, 0u, 0u, 0u);
   if (h >= G) return u;
-  int ex = 0, eq = 0, es = 0;
-  const float mqh = mq[h], msh = ms[h];
-  if (mqh > 0.f) { frexpf(mqh, &ex); eq = 8 - ex; }
-  if (msh > 0.f) { frexpf(msh * QJL_R, &ex); es = 15 - ex; }
-  const int e_use = mqh > 0.f ? (msh > 0.f ? min(eq, es) : eq) : (msh > 0.f ? es : 0);
-  const float qscale = ldexpf(1.f, e_use), sscale = qscale * QJL_R;
-  auto split_pair = [](float x0, float x1, uint32_t& hi, uint32_t& lo) {
-    _Float16 h0, l0, h1, l1;
-    split_f16(x0, h0, l0);
-    split_f16(x1, h1, l1);
-    hi = h2bits(h0, h1);
-    lo = h2bits(l0, l1);
-  };
-  auto signs8 = [&](int i, bool want_lo) {  // q_s entries 32g + 8i .. +7
-    uint32_t w[4];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      uint32_t hi, lo;
-      const float* x = sq + h * D + 32 * g + 8 * i + 2 * k;
-      split_pair(x[0] * sscale, x[1] * sscale, hi, lo);
-      w[k] = want_lo ? lo : hi;
-    }
-    return make_uint4(w[0], w[1], w[2], w[3]);
-  };
   if (op < 8) {
-    if (s < 2) {  // q~ entries 32g + 4 op .. +3
-      uint32_t h01, l01, h23, l23;
-      const float* x = r + h * D + 32 * g + 4 * op;
-      split_pair(x[0] * qscale, x[1] * qscale, h01, l01);
-      split_pair(x[2] * qscale, x[3] * qscale, h23, l23);
-      u = s == 0 ? make_uint4(h01, h01, h23, h23) : make_uint4(l01, 0u, l23, 0u);
-    } else if (op < 4) {
-      u = signs8(op, s == 3);
+    if (s < 2) {  // q~ entries 32g + 4 op .. +3: slot 0 hi against both parts, slot 1 lo
+      const uint2 x = *reinterpret_cast<const uint2*>((s == 0 ? qh : ql) + h * D + 32 * g + 4 * op);
+      u = s == 0 ? make_uint4(x.x, x.x, x.y, x.y) : make_uint4(x.x, 0u, x.y, 0u);
+    } else if (op < 4) {  // q_s entries 32g + 8 op .. +7
+      u = *reinterpret_cast<const uint4*>((s == 3 ? sl : sh) + h * D + 32 * g + 8 * op);
     }
   } else if (op < 12) {
-    if (SLOTS == 2) u = signs8(op - 8, s == 1);
+    if (SLOTS == 2) u = *reinterpret_cast<const uint4*>((s == 1 ? sl : sh) + h * D + 32 * g + 8 * (op - 8));
   } else {
-    u = make_uint4(__float_as_uint(scale * LOG2E_F / (qscale * 256.0f)), 0u, 0u, 0u);
+    u.x = __float_as_uint(cf[h]);
   }
   return u;
 }
@@ -303,7 +322,35 @@ __device__ __forceinline__ void quarter_dot_any(const float (&col)[32], const fl
 
 // LDS floats used by prepare_group for groups of up to GM heads.
 template <int GM>
-constexpr int prep_lds_floats() { return 7 * GM * D + 6 * GM; }
+constexpr int prep_lds_floats() { return 9 * GM * D + 8 * GM; }
+
+// Global loads of prepare_group, issued ahead of the rest of the work: thread
+// (coordinate j, k-quarter kq) takes column j of Pi^T and of S^T (rows 32 kq ..)
+// and coordinate j of query heads kq, kq + 4, ...
+template <int GM>
+struct PrepIn {
+  float pc[32], sc[32];
+  float qv[GM / 4];
+};
+
+template <int DT, int GM>
+__device__ __forceinline__ void prep_issue(const DecodeArgs& a, int kvh, int b, int tid, PrepIn<GM>& in) {
+  const int j = tid & (D - 1);
+  const int kq = __builtin_amdgcn_readfirstlane(tid >> 7);
+  const int64_t row0 = (static_cast<int64_t>(b) * a.hq + kvh * a.group) * D;
+  // in the order of use: loads complete in issue order
+#pragma unroll
+  for (int i = 0; i < GM / 4; ++i) {
+    const int h = kq + 4 * i;
+    const int64_t off = row0 + (h < a.group ? h : 0) * D + j;
+    if constexpr (DT == FQ_BF16)
+      in.qv[i] = __uint_as_float(static_cast<uint32_t>(static_cast<const uint16_t*>(a.q)[off]) << 16);
+    else
+      in.qv[i] = static_cast<const float*>(a.q)[off];
+  }
+  col_quarter_load(a.pit, j, kq, in.pc);
+  col_quarter_load(a.qjl_on ? a.sit : a.pit, j, kq, in.sc);
+}
 
 // The query work of one (KV head, sequence) by PQ_THREADS threads (thread =
 // (coordinate j, k-quarter kq)), lds = prep_lds_floats<GM>() floats:
@@ -312,44 +359,44 @@ constexpr int prep_lds_floats() { return 7 * GM * D + 6 * GM; }
 // written to qrot / qs when write_vec, and with SLOTS > 0 the FQ_QOPS x 64
 // per-lane operands of the packed split kernel to ops (global memory or LDS; the
 // caller synchronizes before reading them).
-template <int DT, int SLOTS, int GM>
+template <int SLOTS, int GM>
 __device__ __forceinline__ void prepare_group(const DecodeArgs& a, int kvh, int b, int tid, float* lds, uint4* ops,
-                                              bool write_vec) {
-  float* const s_q = lds;                    // [GM][D]
-  float* const s_r = s_q + GM * D;           // [GM][D]
-  float* const s_s = s_r + GM * D;           // [GM][D]
-  float* const s_part = s_s + GM * D;        // [4][GM][D]
-  float* const s_mx = s_part + 4 * GM * D;   // [2][GM][2]: [q~, q_s][head][row half]
-  float* const s_mq = s_mx + 4 * GM;         // [GM]
-  float* const s_ms = s_mq + GM;             // [GM]
+                                              bool write_vec, const PrepIn<GM>& in) {
+  float* const s_q = lds;                   // [GM][D]
+  float* const s_r = s_q + GM * D;          // [GM][D]
+  float* const s_s = s_r + GM * D;          // [GM][D]
+  float* const s_part = s_s + GM * D;       // [4][GM][D]
+  uint16_t* const s_qh = reinterpret_cast<uint16_t*>(s_part + 4 * GM * D);  // 4 x [GM][D] halves
+  uint16_t* const s_ql = s_qh + GM * D;
+  uint16_t* const s_sh = s_ql + GM * D;
+  uint16_t* const s_sl = s_sh + GM * D;
+  float* const s_mx = s_part + 6 * GM * D;  // [2][GM][2]: [q~, q_s][head][row half]
+  float* const s_cf = s_mx + 4 * GM;        // [GM]
   const int j = tid & (D - 1);
   const int kq = __builtin_amdgcn_readfirstlane(tid >> 7);
   const int G = a.group;
   const bool qjl = a.qjl_on != 0;
   const int64_t row0 = (static_cast<int64_t>(b) * a.hq + kvh * G) * D;
-  // both matrices by columns: 32 loads each, every one 256 contiguous bytes per wave
-  float pc[32], sc[32];
-  col_quarter_load(a.pit, j, kq, pc);
-  col_quarter_load(qjl ? a.sit : a.pit, j, kq, sc);
-  for (int h = kq; h < G; h += 4) {
-    const int64_t off = row0 + h * D + j;
-    if constexpr (DT == FQ_BF16)
-      s_q[h * D + j] = __uint_as_float(static_cast<uint32_t>(static_cast<const uint16_t*>(a.q)[off]) << 16);
-    else
-      s_q[h * D + j] = static_cast<const float*>(a.q)[off];
-  }
+#pragma unroll
+  for (int i = 0; i < GM / 4; ++i)
+    if (kq + 4 * i < G) s_q[(kq + 4 * i) * D + j] = in.qv[i];
   __syncthreads();
-  quarter_dot_any<GM>(pc, s_q, j, kq, G, s_part);
+  quarter_dot_any<GM>(in.pc, s_q, j, kq, G, s_part);
   __syncthreads();
+  // q~ parts summed; the per-wave maxima of |q~| (64 coordinates of one head)
   for (int h = kq; h < G; h += 4) {
     const float v = (s_part[(0 * GM + h) * D + j] + s_part[(1 * GM + h) * D + j]) +
                     (s_part[(2 * GM + h) * D + j] + s_part[(3 * GM + h) * D + j]);
     s_r[h * D + j] = v;
     if (write_vec) a.qrot[row0 + h * D + j] = v;
+    if constexpr (SLOTS > 0) {
+      const float m = wave_max_dpp(fabsf(v));
+      if ((j & 63) == 0) s_mx[(0 * GM + h) * 2 + (j >> 6)] = m;
+    }
   }
   __syncthreads();
   if (qjl) {
-    quarter_dot_any<GM>(sc, s_r, j, kq, G, s_part);
+    quarter_dot_any<GM>(in.sc, s_r, j, kq, G, s_part);
     __syncthreads();
   }
   for (int h = kq; h < G; h += 4) {
@@ -360,26 +407,29 @@ __device__ __forceinline__ void prepare_group(const DecodeArgs& a, int kvh, int 
       if (write_vec) a.qs[row0 + h * D + j] = v;
     }
     s_s[h * D + j] = v;
-  }
-  __syncthreads();
-  if constexpr (SLOTS > 0) {
-    // per-head maxima (each wave holds 64 coordinates of the heads of its quarter)
-    for (int h = kq; h < G; h += 4) {
-      const float mr = wave_max(fabsf(s_r[h * D + j]));
-      const float ms = wave_max(fabsf(s_s[h * D + j]));
-      if ((j & 63) == 0) {
-        s_mx[(0 * GM + h) * 2 + (j >> 6)] = mr;
-        s_mx[(1 * GM + h) * 2 + (j >> 6)] = ms;
-      }
+    if constexpr (SLOTS > 0) {
+      const float m = wave_max_dpp(fabsf(v));
+      if ((j & 63) == 0) s_mx[(1 * GM + h) * 2 + (j >> 6)] = m;
     }
+  }
+  if constexpr (SLOTS > 0) {
     __syncthreads();
-    if (tid < G) {
-      s_mq[tid] = fmaxf(s_mx[(0 * GM + tid) * 2], s_mx[(0 * GM + tid) * 2 + 1]);
-      s_ms[tid] = fmaxf(s_mx[(1 * GM + tid) * 2], s_mx[(1 * GM + tid) * 2 + 1]);
+    // fp16 hi / lo splits of the scaled vectors, then the operands by gathering
+    for (int h = kq; h < G; h += 4) {
+      const float qscale = head_qscale(fmaxf(s_mx[(0 * GM + h) * 2], s_mx[(0 * GM + h) * 2 + 1]),
+                                       fmaxf(s_mx[(1 * GM + h) * 2], s_mx[(1 * GM + h) * 2 + 1]));
+      _Float16 hi, lo;
+      split_f16(s_r[h * D + j] * qscale, hi, lo);
+      s_qh[h * D + j] = __builtin_bit_cast(uint16_t, hi);
+      s_ql[h * D + j] = __builtin_bit_cast(uint16_t, lo);
+      split_f16(s_s[h * D + j] * (qscale * QJL_R), hi, lo);
+      s_sh[h * D + j] = __builtin_bit_cast(uint16_t, hi);
+      s_sl[h * D + j] = __builtin_bit_cast(uint16_t, lo);
+      if (j == 0) s_cf[h] = a.scale * LOG2E_F / (qscale * 256.0f);
     }
     __syncthreads();
     for (int idx = tid; idx < FQ_QOPS * 64; idx += PQ_THREADS)
-      ops[idx] = query_operand<SLOTS>(idx >> 6, idx & 63, G, s_r, s_s, s_mq, s_ms, a.scale);
+      ops[idx] = query_operand<SLOTS>(idx >> 6, idx & 63, G, s_qh, s_ql, s_sh, s_sl, s_cf);
   }
 }
 
@@ -388,8 +438,10 @@ template <int DT, int SLOTS>
 __global__ void __launch_bounds__(PQ_THREADS) prepare_queries_kernel(DecodeArgs a) {
   __shared__ __align__(16) float s_p[prep_lds_floats<FQ_MAX_GROUP>()];
   const int kvh = blockIdx.x, b = blockIdx.y;
-  prepare_group<DT, SLOTS, FQ_MAX_GROUP>(a, kvh, b, threadIdx.x, s_p,
-                                         a.qops + (static_cast<int64_t>(b) * a.hkv + kvh) * (FQ_QOPS * 64), true);
+  PrepIn<FQ_MAX_GROUP> in;
+  prep_issue<DT, FQ_MAX_GROUP>(a, kvh, b, threadIdx.x, in);
+  prepare_group<SLOTS, FQ_MAX_GROUP>(a, kvh, b, threadIdx.x, s_p,
+                                     a.qops + (static_cast<int64_t>(b) * a.hkv + kvh) * (FQ_QOPS * 64), true, in);
 }
 
 // ---------------------------------------------------------------- kernel 2
@@ -902,33 +954,6 @@ constexpr int PK_PREP_OPS = PK_CODE_BASE + ((prep_lds_floats<PK_PREP_GM>() * 4 +
 static_assert(PK_PREP_OPS + FQ_QOPS * 64 * 16 <= PK_STAGE_BASE, "query preparation fits the code-table area");
 constexpr float PK_TAU = 8.0f;
 
-template <int CTRL>
-__device__ __forceinline__ uint32_t dpp_u(uint32_t x) {
-  return static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(x), CTRL, 0xF, 0xF, true));
-}
-template <int CTRL>
-__device__ __forceinline__ float dpp_f(float x) {
-  return __uint_as_float(dpp_u<CTRL>(__float_as_uint(x)));
-}
-constexpr int DPP_XOR1 = 0xB1;    // quad_perm [1, 0, 3, 2]
-constexpr int DPP_XOR2 = 0x4E;    // quad_perm [2, 3, 0, 1]
-constexpr int DPP_ROR4 = 0x124;   // rotate right by 4 within a row of 16 lanes
-constexpr int DPP_ROR8 = 0x128;   // rotate right by 8 within a row of 16 lanes
-
-// Maximum / sum over the 16 lanes of a row.
-__device__ __forceinline__ float row_max(float x) {
-  x = fmaxf(x, dpp_f<DPP_XOR1>(x));
-  x = fmaxf(x, dpp_f<DPP_XOR2>(x));
-  x = fmaxf(x, dpp_f<DPP_ROR4>(x));
-  return fmaxf(x, dpp_f<DPP_ROR8>(x));
-}
-__device__ __forceinline__ float row_sum(float x) {
-  x += dpp_f<DPP_XOR1>(x);
-  x += dpp_f<DPP_XOR2>(x);
-  x += dpp_f<DPP_ROR4>(x);
-  return x + dpp_f<DPP_ROR8>(x);
-}
-
 // Byte b of w placed in byte 1 of the result, byte 0 of c in byte 0, zeros above:
 // (byte of w) * 256 + c for c < 256.
 __device__ __forceinline__ uint32_t tab_off(uint32_t w, uint32_t c, int b) {
@@ -1042,7 +1067,21 @@ __global__ void __launch_bounds__(WAVES * 64, OCC) packed_decode_kernel(DecodeAr
   lo.sg = static_cast<uint32_t>(n * 16 + 4 * g);
   lo.vc = static_cast<uint32_t>(4 * g * CB + BITS * n);
 
-  // ---- the wave's first RING - 1 pages are requested before any set-up work
+  // ---- the query loads (in-kernel preparation) and the wave's first RING - 1
+  // pages are requested before any set-up work, in the order they are needed
+  PrepIn<PK_PREP_GM> pin;
+  if constexpr (PREP >= 0) prep_issue<(PREP >= 0 ? PREP : 0), PK_PREP_GM>(a, kvh, b, tid, pin);
+  // codebook levels of the table entry this thread stages (threads < 256)
+  float lv[BITS == 4 ? 2 : 4] = {};
+  if (tid < 256) {
+    if constexpr (BITS == 4) {
+      lv[0] = a.levels[tid & 15];
+      lv[1] = a.levels[tid >> 4];
+    } else {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) lv[k] = a.levels[(tid >> (2 * k)) & 3];
+    }
+  }
   PkPage<BITS> ring[RING];
   if (my_pages > 0) {
 #pragma unroll
@@ -1060,8 +1099,8 @@ __global__ void __launch_bounds__(WAVES * 64, OCC) packed_decode_kernel(DecodeAr
     const uint4* ops;
     if constexpr (PREP >= 0) {
       uint4* const s_ops = reinterpret_cast<uint4*>(s_lds + PK_PREP_OPS);
-      prepare_group<PREP, SLOTS, PK_PREP_GM>(a, kvh, b, tid, reinterpret_cast<float*>(s_lds + PK_CODE_BASE), s_ops,
-                                             false);
+      prepare_group<SLOTS, PK_PREP_GM>(a, kvh, b, tid, reinterpret_cast<float*>(s_lds + PK_CODE_BASE), s_ops, false,
+                                       pin);
       __syncthreads();
       ops = s_ops;
     } else {
@@ -1087,8 +1126,8 @@ __global__ void __launch_bounds__(WAVES * 64, OCC) packed_decode_kernel(DecodeAr
     uint4* stage4 = reinterpret_cast<uint4*>(s_lds + PK_STAGE_BASE);
     if (tid < 256) {
       if constexpr (BITS == 4) {
-        const float c0 = a.levels[tid & 15] * static_cast<float>(1 << LEV_SHIFT);
-        const float c1 = a.levels[tid >> 4] * static_cast<float>(1 << LEV_SHIFT);
+        const float c0 = lv[0] * static_cast<float>(1 << LEV_SHIFT);
+        const float c1 = lv[1] * static_cast<float>(1 << LEV_SHIFT);
         _Float16 h0, l0, h1, l1;
         split_f16(c0, h0, l0);
         split_f16(c1, h1, l1);
@@ -1096,10 +1135,10 @@ __global__ void __launch_bounds__(WAVES * 64, OCC) packed_decode_kernel(DecodeAr
       } else {
         constexpr float SC = static_cast<float>(1 << LEV_SHIFT);
         _Float16 h0, l0, h1, l1, h2, l2, h3, l3;
-        split_f16(a.levels[tid & 3] * SC, h0, l0);
-        split_f16(a.levels[(tid >> 2) & 3] * SC, h1, l1);
-        split_f16(a.levels[(tid >> 4) & 3] * SC, h2, l2);
-        split_f16(a.levels[tid >> 6] * SC, h3, l3);
+        split_f16(lv[0] * SC, h0, l0);
+        split_f16(lv[1] * SC, h1, l1);
+        split_f16(lv[2] * SC, h2, l2);
+        split_f16(lv[3] * SC, h3, l3);
         stage4[tid] = make_uint4(h2bits(h0, h1), h2bits(l0, l1), h2bits(h2, h3), h2bits(l2, l3));
       }
     }
@@ -1128,8 +1167,8 @@ __global__ void __launch_bounds__(WAVES * 64, OCC) packed_decode_kernel(DecodeAr
       }
     } else {
 #pragma unroll
-      for (int idx = tid; idx < 256 * 16; idx += NT)
-        *reinterpret_cast<uint4*>(s_lds + PK_CODE_BASE + idx * 16) = stage4[idx >> 4];
+      for (int base = 0; base < 256 * 16; base += NT)
+        *reinterpret_cast<uint4*>(s_lds + PK_CODE_BASE + (base + tid) * 16) = stage4[(base + tid) >> 4];
     }
   }
 
@@ -1274,6 +1313,13 @@ __global__ void __launch_bounds__(WAVES * 64, OCC) packed_decode_kernel(DecodeAr
     }
   };
 
+  // The only split un-rotates its output at the end: column jj of Pi (rows 32 kq ..)
+  // is requested now and arrives during the page loop.
+  const int jj = tid & (D - 1);
+  const int kq = __builtin_amdgcn_readfirstlane(tid >> 7);
+  float pc[32];
+  if constexpr (PREP >= 0) col_quarter_load(a.pi, jj, kq, pc);
+
   // One page per wave at a time with RING - 1 more of the same wave in flight (a
   // register ring, unrolled so that no stage is copied).
   for (int c0 = 0; c0 < my_pages; c0 += 64) {
@@ -1320,10 +1366,6 @@ __global__ void __launch_bounds__(WAVES * 64, OCC) packed_decode_kernel(DecodeAr
     // the only split: o_rot = O / L per head, then out = Pi^T o_rot
     float* const s_or = s_ml + WAVES * HP * 2;  // [G][D]
     float* const s_pp = s_or + PK_PREP_GM * D;  // [4][PK_PREP_GM][D]
-    const int jj = tid & (D - 1);
-    const int kq = __builtin_amdgcn_readfirstlane(tid >> 7);
-    float pc[32];
-    col_quarter_load(a.pi, jj, kq, pc);
     for (int idx = tid; idx < G * D; idx += WAVES * 64) {
       const int hh = idx / D, j = idx % D;
       float M = -INFINITY;
