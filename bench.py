@@ -161,10 +161,25 @@ def decode_layer_measure(index, bits, rot, replicas, reps, stream):
 
     for _ in range(3):
         call()
-    ms = _events_ms(call, reps, stream)
+    ms_eager = _events_ms(call, reps, stream)
+    # device time of a call: HIP events around replays of a graph holding one call per
+    # replica (as for the stack's decode roofline; eager calls add host launch gaps)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            for r in range(replicas):
+                fq.decode(qz, caches[r], q, bt, lt, int(lens.max()), workspace=ws, out=out)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    ms = _events_ms(g.replay, max(5, reps // replicas), stream) / replicas
     nbytes = int(lens.sum()) * Hkv * caches[0].bytes_per_token_head()
     return {"workload": w.name, "bits": bits, "rotation": "wht" if rot else "haar",
-            "splits": fq.auto_splits(B, Hkv, int(lens.max())), "decode_ms": ms,
+            "splits": fq.auto_splits(B, Hkv, int(lens.max())), "decode_ms": ms, "decode_ms_eager": ms_eager,
+            "timing": "HIP events around graph replays of one call per cache replica",
             "achieved_gbs": nbytes / (ms * 1e-3) / 1e9, "frac_hbm": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
             "algorithmic_bytes": nbytes, "cache_replicas": replicas}
 

@@ -168,29 +168,28 @@ __device__ __forceinline__ float head_qscale(float mqh, float msh) {
 
 // Matrix-core query operand op (0 .. FQ_QOPS-1) of lane l of the packed split
 // kernel, gathered from the fp16 hi / lo splits of q~ x qscale (qh, ql) and of
-// q_s x qscale QJL_R (sh, sl), rows of D halves per head, and the per-head score
-// factors cf:
+// q_s x qscale QJL_R (sh, sl), the rows of D halves of the lane's head
+// (n / SLOTS), and that head's score factor cf:
 //   op 0..7   code-product operand of k-step op; op 0..3 also the sign-product
 //             operand when SLOTS = 4 (slots 2 / 3);
 //   op 8..11  SLOTS = 2: sign-product operand of k-step op - 8;
 //   op 12     the score factor of the lane's head in .x.
 template <int SLOTS>
-__device__ __forceinline__ uint4 query_operand(int op, int l, int G, const uint16_t* qh, const uint16_t* ql,
-                                               const uint16_t* sh, const uint16_t* sl, const float* cf) {
-  const int g = l >> 4, n = l & 15, h = n / SLOTS, s = n % SLOTS;
+__device__ __forceinline__ uint4 query_operand(int op, int l, const uint16_t* qh, const uint16_t* ql,
+                                               const uint16_t* sh, const uint16_t* sl, float cf) {
+  const int g = l >> 4, s = (l & 15) % SLOTS;
   uint4 u = make_uint4(0u, 0u, 0u, 0u);
-  if (h >= G) return u;
   if (op < 8) {
     if (s < 2) {  // q~ entries 32g + 4 op .. +3: slot 0 hi against both parts, slot 1 lo
-      const uint2 x = *reinterpret_cast<const uint2*>((s == 0 ? qh : ql) + h * D + 32 * g + 4 * op);
+      const uint2 x = *reinterpret_cast<const uint2*>((s == 0 ? qh : ql) + 32 * g + 4 * op);
       u = s == 0 ? make_uint4(x.x, x.x, x.y, x.y) : make_uint4(x.x, 0u, x.y, 0u);
     } else if (op < 4) {  // q_s entries 32g + 8 op .. +7
-      u = *reinterpret_cast<const uint4*>((s == 3 ? sl : sh) + h * D + 32 * g + 8 * op);
+      u = *reinterpret_cast<const uint4*>((s == 3 ? sl : sh) + 32 * g + 8 * op);
     }
   } else if (op < 12) {
-    if (SLOTS == 2) u = *reinterpret_cast<const uint4*>((s == 1 ? sl : sh) + h * D + 32 * g + 8 * (op - 8));
+    if (SLOTS == 2) u = *reinterpret_cast<const uint4*>((s == 1 ? sl : sh) + 32 * g + 8 * (op - 8));
   } else {
-    u.x = __float_as_uint(cf[h]);
+    u.x = __float_as_uint(cf);
   }
   return u;
 }
@@ -229,16 +228,17 @@ __device__ __forceinline__ void part_dot(const float (&col)[D / KP], const float
   }
 }
 
-// Log-sum-exp merge of the splits of one (KV head, sequence) and the output
-// rotation, by a work-group of NT threads (thread = (coordinate j, k-part kp)),
-// with lds >= (17 + NT / D * 16) * D + 16 * FQ_MAX_SPLITS + 16 floats:
+// Log-sum-exp merge of the splits of query heads head0 .. head0 + G - 1 (global
+// indices, G <= 16) and the output rotation, by a work-group of NT threads
+// (thread = (coordinate j, k-part kp)), with lds >= (17 + NT / D * 16) * D +
+// 16 * FQ_MAX_SPLITS + 16 floats:
 //  1. wave w takes heads w, w + NT/64: lane sp holds split sp's (max, sum); the
 //     weights exp(m_sp - M) and 1 / sum_sp l_sp w_sp go to LDS;
 //  2. thread (j, kp) adds up coordinate j of splits sp = kp, kp + KP, ... for every
 //     head; the parts are summed;
 //  3. o = Pi^T O = sum_k Pi[k][j] o_rot[k], column j of Pi loaded first.
 template <int NT>
-__device__ __forceinline__ void merge_group(const DecodeArgs& a, int kvh, int b, int tid, float* lds) {
+__device__ __forceinline__ void merge_group(const DecodeArgs& a, int64_t head0, int G, int tid, float* lds) {
   constexpr int KP = NT / D;
   float* const s_o = lds;                                       // [16][D]
   float* const s_part = s_o + FQ_MAX_GROUP * D;                 // [KP][16][D]
@@ -247,10 +247,9 @@ __device__ __forceinline__ void merge_group(const DecodeArgs& a, int kvh, int b,
   const int j = tid & (D - 1);
   const int kp = __builtin_amdgcn_readfirstlane(tid / D);
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
-  const int G = a.group, S = a.splits;
+  const int S = a.splits;
   float pc[D / KP];
   col_part_load<KP>(a.pi, j, kp, pc);
-  const int64_t head0 = static_cast<int64_t>(b) * a.hq + kvh * G;
   for (int h = wv; h < G; h += NT / 64) {
     float m = -INFINITY, l = 0.f;
     if (lane < S) {
@@ -325,8 +324,8 @@ template <int GM>
 constexpr int prep_lds_floats() { return 9 * GM * D + 8 * GM; }
 
 // Global loads of prepare_group, issued ahead of the rest of the work: thread
-// (coordinate j, k-quarter kq) takes column j of Pi^T and of S^T (rows 32 kq ..)
-// and coordinate j of query heads kq, kq + 4, ...
+// (coordinate j, k-quarter kq) takes coordinate j of query heads hb + kq,
+// hb + kq + 4, ... (< hb + hn) and column j of Pi^T and of S^T (rows 32 kq ..).
 template <int GM>
 struct PrepIn {
   float pc[32], sc[32];
@@ -334,15 +333,16 @@ struct PrepIn {
 };
 
 template <int DT, int GM>
-__device__ __forceinline__ void prep_issue(const DecodeArgs& a, int kvh, int b, int tid, PrepIn<GM>& in) {
+__device__ __forceinline__ void prep_issue(const DecodeArgs& a, int kvh, int b, int hb, int hn, int tid,
+                                           PrepIn<GM>& in) {
   const int j = tid & (D - 1);
   const int kq = __builtin_amdgcn_readfirstlane(tid >> 7);
-  const int64_t row0 = (static_cast<int64_t>(b) * a.hq + kvh * a.group) * D;
+  const int64_t row0 = (static_cast<int64_t>(b) * a.hq + kvh * a.group + hb) * D;
   // in the order of use: loads complete in issue order
 #pragma unroll
   for (int i = 0; i < GM / 4; ++i) {
     const int h = kq + 4 * i;
-    const int64_t off = row0 + (h < a.group ? h : 0) * D + j;
+    const int64_t off = row0 + (h < hn ? h : 0) * D + j;
     if constexpr (DT == FQ_BF16)
       in.qv[i] = __uint_as_float(static_cast<uint32_t>(static_cast<const uint16_t*>(a.q)[off]) << 16);
     else
@@ -352,16 +352,18 @@ __device__ __forceinline__ void prep_issue(const DecodeArgs& a, int kvh, int b, 
   col_quarter_load(a.qjl_on ? a.sit : a.pit, j, kq, in.sc);
 }
 
-// The query work of one (KV head, sequence) by PQ_THREADS threads (thread =
-// (coordinate j, k-quarter kq)), lds = prep_lds_floats<GM>() floats:
+// The query work for heads hb .. hb + hn - 1 (hn <= GM) of the group of one (KV
+// head, sequence) by PQ_THREADS threads (thread = (coordinate j, k-quarter kq)),
+// lds = prep_lds_floats<GM>() floats:
 //   q~[h][j]  = sum_k Pi[j][k] q[h][k]     (column j of Pi^T)
 //   q_s[h][j] = sum_k S[j][k] q~[h][k]     (column j of S^T)
-// written to qrot / qs when write_vec, and with SLOTS > 0 the FQ_QOPS x 64
-// per-lane operands of the packed split kernel to ops (global memory or LDS; the
-// caller synchronizes before reading them).
+// written to qrot / qs when write_vec, and with SLOTS > 0 those heads' entries
+// of the FQ_QOPS x 64 per-lane operands of the packed split kernel to ops (global
+// memory or LDS; the caller synchronizes before reading them); the range that
+// starts at head 0 also zeroes the entries of the lanes without a head.
 template <int SLOTS, int GM>
-__device__ __forceinline__ void prepare_group(const DecodeArgs& a, int kvh, int b, int tid, float* lds, uint4* ops,
-                                              bool write_vec, const PrepIn<GM>& in) {
+__device__ __forceinline__ void prepare_group(const DecodeArgs& a, int kvh, int b, int hb, int hn, int tid,
+                                              float* lds, uint4* ops, bool write_vec, const PrepIn<GM>& in) {
   float* const s_q = lds;                   // [GM][D]
   float* const s_r = s_q + GM * D;          // [GM][D]
   float* const s_s = s_r + GM * D;          // [GM][D]
@@ -374,14 +376,16 @@ __device__ __forceinline__ void prepare_group(const DecodeArgs& a, int kvh, int 
   float* const s_cf = s_mx + 4 * GM;        // [GM]
   const int j = tid & (D - 1);
   const int kq = __builtin_amdgcn_readfirstlane(tid >> 7);
-  const int G = a.group;
+  // G = heads of this range; threads beyond PQ_THREADS (larger work-groups) only
+  // take the barriers
+  const int G = tid < PQ_THREADS ? hn : 0;
   const bool qjl = a.qjl_on != 0;
-  const int64_t row0 = (static_cast<int64_t>(b) * a.hq + kvh * G) * D;
+  const int64_t row0 = (static_cast<int64_t>(b) * a.hq + kvh * a.group + hb) * D;
 #pragma unroll
   for (int i = 0; i < GM / 4; ++i)
     if (kq + 4 * i < G) s_q[(kq + 4 * i) * D + j] = in.qv[i];
   __syncthreads();
-  quarter_dot_any<GM>(in.pc, s_q, j, kq, G, s_part);
+  if (G > 0) quarter_dot_any<GM>(in.pc, s_q, j, kq, G, s_part);
   __syncthreads();
   // q~ parts summed; the per-wave maxima of |q~| (64 coordinates of one head)
   for (int h = kq; h < G; h += 4) {
@@ -396,7 +400,7 @@ __device__ __forceinline__ void prepare_group(const DecodeArgs& a, int kvh, int 
   }
   __syncthreads();
   if (qjl) {
-    quarter_dot_any<GM>(in.sc, s_r, j, kq, G, s_part);
+    if (G > 0) quarter_dot_any<GM>(in.sc, s_r, j, kq, G, s_part);
     __syncthreads();
   }
   for (int h = kq; h < G; h += 4) {
@@ -428,19 +432,29 @@ __device__ __forceinline__ void prepare_group(const DecodeArgs& a, int kvh, int 
       if (j == 0) s_cf[h] = a.scale * LOG2E_F / (qscale * 256.0f);
     }
     __syncthreads();
-    for (int idx = tid; idx < FQ_QOPS * 64; idx += PQ_THREADS)
-      ops[idx] = query_operand<SLOTS>(idx >> 6, idx & 63, G, s_qh, s_ql, s_sh, s_sl, s_cf);
+    if (G > 0)
+      for (int idx = tid; idx < FQ_QOPS * 64; idx += PQ_THREADS) {
+        const int l = idx & 63, h = (l & 15) / SLOTS - hb;  // local head of lane l
+        if (h + hb >= a.group) {
+          if (hb == 0) ops[idx] = make_uint4(0u, 0u, 0u, 0u);
+        } else if (h >= 0 && h < G) {
+          ops[idx] = query_operand<SLOTS>(idx >> 6, l, s_qh + h * D, s_ql + h * D, s_sh + h * D, s_sl + h * D, s_cf[h]);
+        }
+      }
   }
 }
 
-// One work-group per (KV head, sequence).
+// One work-group per (KV head, sequence, part of the group): the group's heads
+// are shared out over gridDim.z work-groups (all in one, or one each when there
+// are few (KV head, sequence) pairs to spread the work over).
 template <int DT, int SLOTS>
 __global__ void __launch_bounds__(PQ_THREADS) prepare_queries_kernel(DecodeArgs a) {
   __shared__ __align__(16) float s_p[prep_lds_floats<FQ_MAX_GROUP>()];
   const int kvh = blockIdx.x, b = blockIdx.y;
+  const int hn = a.group / gridDim.z, hb = blockIdx.z * hn;
   PrepIn<FQ_MAX_GROUP> in;
-  prep_issue<DT, FQ_MAX_GROUP>(a, kvh, b, threadIdx.x, in);
-  prepare_group<SLOTS, FQ_MAX_GROUP>(a, kvh, b, threadIdx.x, s_p,
+  prep_issue<DT, FQ_MAX_GROUP>(a, kvh, b, hb, hn, threadIdx.x, in);
+  prepare_group<SLOTS, FQ_MAX_GROUP>(a, kvh, b, hb, hn, threadIdx.x, s_p,
                                      a.qops + (static_cast<int64_t>(b) * a.hkv + kvh) * (FQ_QOPS * 64), true, in);
 }
 
@@ -941,7 +955,10 @@ __global__ void __launch_bounds__(256, 2) split_mfma4_kernel(DecodeArgs a) {
 // Work-group shape per slot layout: waves, register-ring depth, waves per SIMD.
 constexpr int PK4_WAVES = 4, PK4_RING = 2, PK4_OCC = 2;  // SLOTS 4
 constexpr int PK2_WAVES = 8, PK2_RING = 2, PK2_OCC = 4;  // SLOTS 2
-constexpr int PKF_WAVES = 8, PKF_RING = 2, PKF_OCC = 2;  // the only split (query preparation in-kernel)
+// the only split (query preparation in-kernel): 8 waves for 4-bit codes, 12 for
+// 2-bit (whose loop gains from a third wave per SIMD; the 4-bit loop loses)
+constexpr int PKF_RING = 2, PKF_OCC = 2;
+constexpr int pkf_waves(int bits) { return bits == 4 ? 8 : 12; }
 constexpr int PK_SIGN_BASE = 0;       // 16 x 32 x 8 B
 constexpr int PK_CODE_BASE = 4096;    // 256 x 32 x 8 B (4-bit) or 256 x 16 x 16 B (2-bit)
 constexpr int PK_STAGE_BASE = 69632;  // 256 x 16 B staging for the table build
@@ -1020,7 +1037,8 @@ __device__ __forceinline__ void pk_load(const DecodeArgs& a, int64_t rec0, int n
 template <int BITS, int SLOTS, int WAVES, int RING, int OCC, int PREP>
 __global__ void __launch_bounds__(WAVES * 64, OCC) packed_decode_kernel(DecodeArgs a) {
   static_assert(BITS == 4 || BITS == 2, "4- or 2-bit codes");
-  static_assert(PREP < 0 || WAVES * 64 == PQ_THREADS, "in-kernel query preparation takes PQ_THREADS threads");
+  static_assert(PREP < 0 || WAVES * 64 >= PQ_THREADS, "in-kernel query preparation takes PQ_THREADS threads");
+  static_assert(WAVES * 64 >= 256, "the table stage takes 256 threads");
   constexpr int CB = D * BITS / 8;  // code bytes per vector
   __shared__ __align__(16) uint8_t s_lds[PK_LDS_BYTES];
   const uint8_t* const s_code = s_lds + PK_CODE_BASE;
@@ -1070,7 +1088,9 @@ __global__ void __launch_bounds__(WAVES * 64, OCC) packed_decode_kernel(DecodeAr
   // ---- the query loads (in-kernel preparation) and the wave's first RING - 1
   // pages are requested before any set-up work, in the order they are needed
   PrepIn<PK_PREP_GM> pin;
-  if constexpr (PREP >= 0) prep_issue<(PREP >= 0 ? PREP : 0), PK_PREP_GM>(a, kvh, b, tid, pin);
+  if constexpr (PREP >= 0) {
+    if (tid < PQ_THREADS) prep_issue<(PREP >= 0 ? PREP : 0), PK_PREP_GM>(a, kvh, b, 0, G, tid, pin);
+  }
   // codebook levels of the table entry this thread stages (threads < 256)
   float lv[BITS == 4 ? 2 : 4] = {};
   if (tid < 256) {
@@ -1099,8 +1119,8 @@ __global__ void __launch_bounds__(WAVES * 64, OCC) packed_decode_kernel(DecodeAr
     const uint4* ops;
     if constexpr (PREP >= 0) {
       uint4* const s_ops = reinterpret_cast<uint4*>(s_lds + PK_PREP_OPS);
-      prepare_group<SLOTS, PK_PREP_GM>(a, kvh, b, tid, reinterpret_cast<float*>(s_lds + PK_CODE_BASE), s_ops, false,
-                                       pin);
+      prepare_group<SLOTS, PK_PREP_GM>(a, kvh, b, 0, G, tid, reinterpret_cast<float*>(s_lds + PK_CODE_BASE), s_ops,
+                                       false, pin);
       __syncthreads();
       ops = s_ops;
     } else {
@@ -1156,8 +1176,13 @@ __global__ void __launch_bounds__(WAVES * 64, OCC) packed_decode_kernel(DecodeAr
     __syncthreads();
     // 8192 (4096) entries; four per thread and round, reads issued before writes
     constexpr int NT = WAVES * 64;
-    static_assert((256 * 16) % (4 * NT) == 0, "whole rounds");
-    if constexpr (BITS == 4) {
+    if constexpr (BITS == 4 && (256 * 32) % (4 * NT) != 0) {
+      for (int idx = tid; idx < 256 * 32; idx += NT)
+        *reinterpret_cast<uint2*>(s_lds + PK_CODE_BASE + idx * 8) = stage[idx >> 5];
+    } else if constexpr (BITS == 2 && (256 * 16) % NT != 0) {
+      for (int idx = tid; idx < 256 * 16; idx += NT)
+        *reinterpret_cast<uint4*>(s_lds + PK_CODE_BASE + idx * 16) = stage4[idx >> 4];
+    } else if constexpr (BITS == 4) {
       for (int base = 0; base < 256 * 32; base += 4 * NT) {
         uint2 v[4];
 #pragma unroll
@@ -1318,7 +1343,9 @@ __global__ void __launch_bounds__(WAVES * 64, OCC) packed_decode_kernel(DecodeAr
   const int jj = tid & (D - 1);
   const int kq = __builtin_amdgcn_readfirstlane(tid >> 7);
   float pc[32];
-  if constexpr (PREP >= 0) col_quarter_load(a.pi, jj, kq, pc);
+  if constexpr (PREP >= 0) {
+    if (tid < PQ_THREADS) col_quarter_load(a.pi, jj, kq, pc);
+  }
 
   // One page per wave at a time with RING - 1 more of the same wave in flight (a
   // register ring, unrolled so that no stage is copied).
@@ -1366,6 +1393,7 @@ __global__ void __launch_bounds__(WAVES * 64, OCC) packed_decode_kernel(DecodeAr
     // the only split: o_rot = O / L per head, then out = Pi^T o_rot
     float* const s_or = s_ml + WAVES * HP * 2;  // [G][D]
     float* const s_pp = s_or + PK_PREP_GM * D;  // [4][PK_PREP_GM][D]
+    static_assert((WAVES * HP * (D + 2) + 5 * PK_PREP_GM * D) * 4 <= PK_LDS_BYTES, "epilogue fits the LDS");
     for (int idx = tid; idx < G * D; idx += WAVES * 64) {
       const int hh = idx / D, j = idx % D;
       float M = -INFINITY;
@@ -1385,12 +1413,14 @@ __global__ void __launch_bounds__(WAVES * 64, OCC) packed_decode_kernel(DecodeAr
       s_or[hh * D + j] = L > 0.f ? o / L : 0.f;
     }
     __syncthreads();
-    quarter_dot_any<PK_PREP_GM>(pc, s_or, jj, kq, G, s_pp);
+    if (tid < PQ_THREADS) quarter_dot_any<PK_PREP_GM>(pc, s_or, jj, kq, G, s_pp);
     __syncthreads();
     const int64_t head0 = static_cast<int64_t>(b) * a.hq + kvh * G;
-    for (int h = kq; h < G; h += 4)
-      a.out[(head0 + h) * D + jj] = (s_pp[(0 * PK_PREP_GM + h) * D + jj] + s_pp[(1 * PK_PREP_GM + h) * D + jj]) +
-                                    (s_pp[(2 * PK_PREP_GM + h) * D + jj] + s_pp[(3 * PK_PREP_GM + h) * D + jj]);
+    if (tid < PQ_THREADS) {
+      for (int h = kq; h < G; h += 4)
+        a.out[(head0 + h) * D + jj] = (s_pp[(0 * PK_PREP_GM + h) * D + jj] + s_pp[(1 * PK_PREP_GM + h) * D + jj]) +
+                                      (s_pp[(2 * PK_PREP_GM + h) * D + jj] + s_pp[(3 * PK_PREP_GM + h) * D + jj]);
+    }
     return;
   }
   constexpr float LN2 = 0.6931471805599453f;
@@ -1420,10 +1450,13 @@ __global__ void __launch_bounds__(WAVES * 64, OCC) packed_decode_kernel(DecodeAr
 }
 
 // ---------------------------------------------------------------- kernel 3
-// One work-group per (KV head, sequence): merge_group over its splits.
+// One work-group per (KV head, sequence, part of the group, as above): merge_group
+// of those heads' splits.
 __global__ void __launch_bounds__(PQ_THREADS) merge_unrotate_kernel(DecodeArgs a) {
   __shared__ __align__(16) float s_m[(17 + PQ_THREADS / D * 16) * D + 16 * FQ_MAX_SPLITS + 16];
-  merge_group<PQ_THREADS>(a, blockIdx.x, blockIdx.y, threadIdx.x, s_m);
+  const int hn = a.group / gridDim.z;
+  merge_group<PQ_THREADS>(a, static_cast<int64_t>(blockIdx.y) * a.hq + blockIdx.x * a.group + blockIdx.z * hn, hn,
+                          threadIdx.x, s_m);
 }
 
 }  // namespace
@@ -1480,9 +1513,9 @@ int launch_decode(void* stream, const fq_quantizer& q, const fq_cache& c, const 
   dim3 grid(num_splits, c.num_kv_heads, batch);
   if (slots > 0 && num_splits == 1 && std::getenv("FQ_DECODE_UNFUSED") == nullptr) {
     // one work-group per (KV head, sequence) does everything in one launch
-    const dim3 blk(PKF_WAVES * 64);
-#define FQ_FUSED(BITS, SL, DT) \
-  hipLaunchKernelGGL((packed_decode_kernel<BITS, SL, PKF_WAVES, PKF_RING, PKF_OCC, DT>), grid, blk, 0, st, a)
+#define FQ_FUSED(BITS, SL, DT)                                                                                \
+  hipLaunchKernelGGL((packed_decode_kernel<BITS, SL, pkf_waves(BITS), PKF_RING, PKF_OCC, DT>), grid,          \
+                     dim3(pkf_waves(BITS) * 64), 0, st, a)
     const bool bf = q_dtype == FQ_BF16;
     if (q.bits == 4 && slots == 4) { if (bf) FQ_FUSED(4, 4, FQ_BF16); else FQ_FUSED(4, 4, FQ_F32); }
     else if (q.bits == 4) { if (bf) FQ_FUSED(4, 2, FQ_BF16); else FQ_FUSED(4, 2, FQ_F32); }
@@ -1491,7 +1524,9 @@ int launch_decode(void* stream, const fq_quantizer& q, const fq_cache& c, const 
 #undef FQ_FUSED
     return static_cast<int>(hipGetLastError());
   }
-  const dim3 pgrid(c.num_kv_heads, batch);
+  // query preparation and merge: one work-group per query head when there are few
+  // (KV head, sequence) pairs, else one per pair
+  const dim3 pgrid(c.num_kv_heads, batch, batch * c.num_kv_heads >= 128 ? 1 : a.group);
   if (q_dtype == FQ_BF16) {
     if (slots == 4) hipLaunchKernelGGL((prepare_queries_kernel<FQ_BF16, 4>), pgrid, dim3(PQ_THREADS), 0, st, a);
     else if (slots == 2) hipLaunchKernelGGL((prepare_queries_kernel<FQ_BF16, 2>), pgrid, dim3(PQ_THREADS), 0, st, a);
