@@ -276,9 +276,14 @@ __device__ __forceinline__ void compress_tile(const CompressArgs& a, int kind, i
   const uint8_t* src = static_cast<const uint8_t*>(a.src[kind]);
   const int64_t vid = tile * CT_VEC + v;
   const bool valid = vid < nvec;
-  const int64_t t = valid ? vid / a.hkv : 0;
-  const int hd = valid ? static_cast<int>(vid - t * a.hkv) : 0;
-  const int64_t slot = valid ? a.slots[t] : -1;
+  // Lanes past the last vector load vector 0 (loads stay unconditional, so no wait
+  // is tied to a branch); their columns of the products are never stored.
+  const int64_t vl = valid ? vid : 0;
+  // vectors per launch < 2^31 (checked on the host): 32-bit division
+  const int64_t t = static_cast<uint32_t>(vl) / static_cast<uint32_t>(a.hkv);
+  const int hd = static_cast<int>(vl - t * a.hkv);
+  const int64_t slot_t = a.slots[t];
+  const int64_t slot = valid ? slot_t : -1;
   const uint8_t* base = src + ((t * a.tstride + hd * a.hstride) * esz) + 64 * h * esz;
 
   // ---- load 64 coordinates (64h .. 64h+63) of vector v; B fragments per k-step
@@ -288,7 +293,7 @@ __device__ __forceinline__ void compress_tile(const CompressArgs& a, int kind, i
   if constexpr (DT == FQ_BF16) {
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
-      uint4 u = valid ? reinterpret_cast<const uint4*>(base)[s] : make_uint4(0, 0, 0, 0);
+      uint4 u = reinterpret_cast<const uint4*>(base)[s];
       const uint32_t w4[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
@@ -301,8 +306,8 @@ __device__ __forceinline__ void compress_tile(const CompressArgs& a, int kind, i
   } else {
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
-      float4 f0 = valid ? reinterpret_cast<const float4*>(base)[2 * s] : make_float4(0, 0, 0, 0);
-      float4 f1 = valid ? reinterpret_cast<const float4*>(base)[2 * s + 1] : make_float4(0, 0, 0, 0);
+      float4 f0 = reinterpret_cast<const float4*>(base)[2 * s];
+      float4 f1 = reinterpret_cast<const float4*>(base)[2 * s + 1];
       const float xs[8] = {f0.x, f0.y, f0.z, f0.w, f1.x, f1.y, f1.z, f1.w};
       uint32_t hi[8], lo[8];
 #pragma unroll
@@ -451,10 +456,12 @@ __device__ __forceinline__ void fill_qtable(QCell* s_qt, float* s_qmap, const fl
     uint32_t cnt = 0;
     float bb = INFINITY;
 #pragma unroll
-    for (int i = 0; i < L - 1; ++i) {
-      const float pos = fmaf(s_bl[i], inv_w, off);
-      if (pos < c - 0.5f) ++cnt;
-      else if (pos < c + 1.5f) bb = s_bl[i];
+    for (int i = 0; i < L - 1; ++i) {  // branch-free: counts and selects
+      const float bi = s_bl[i];
+      const float pos = fmaf(bi, inv_w, off);
+      const bool below = pos < c - 0.5f;
+      cnt += below ? 1u : 0u;
+      bb = (!below && pos < c + 1.5f) ? bi : bb;
     }
     s_qt[cell] = QCell{cnt, bb, s_bl[16 + cnt], s_bl[16 + (cnt + 1 < L ? cnt + 1 : cnt)]};
   }
@@ -580,18 +587,55 @@ __device__ __forceinline__ void compress_quarter(const CompressArgs& a, int kind
   const uint8_t* src = static_cast<const uint8_t*>(a.src[kind]);
   const int64_t vid = tile * CT_VEC + v;
   const bool valid = vid < nvec;
-  const int64_t t = valid ? vid / a.hkv : 0;
-  const int hd = valid ? static_cast<int>(vid - t * a.hkv) : 0;
-  const int64_t slot = valid ? a.slots[t] : -1;
+  // Lanes past the last vector load vector 0 (loads stay unconditional, so no wait
+  // is tied to a branch); their columns of the products are never stored.
+  const int64_t vl = valid ? vid : 0;
+  // vectors per launch < 2^31 (checked on the host): 32-bit division
+  const int64_t t = static_cast<uint32_t>(vl) / static_cast<uint32_t>(a.hkv);
+  const int hd = static_cast<int>(vl - t * a.hkv);
+  const int64_t slot_t = a.slots[t];
+  const int64_t slot = valid ? slot_t : -1;
   const uint8_t* base = src + ((t * a.tstride + hd * a.hstride) * esz) + 64 * h * esz;
 
+  // raw inputs first; the quantization cells are built while they are in flight
+  // (uniform over the work-group)
+  // output pointers read from the arguments now and kept in scalar registers:
+  // scalar loads later would share a wait counter with the table lookups
+  uint8_t* codes_p = a.codes[kind];
+  float* norm_p = a.norm[kind];
+  uint8_t* qjl_p = a.qjl;
+  float* gamma_p = a.gamma;
+  float* dbg_y = a.dbg_y;
+  float* dbg_p = a.dbg_p;
+  asm volatile("" : "+s"(codes_p), "+s"(norm_p), "+s"(qjl_p), "+s"(gamma_p), "+s"(dbg_y), "+s"(dbg_p));
+  uint4 raw[DT == FQ_BF16 ? 8 : 16];
+#pragma unroll
+  for (int s = 0; s < (DT == FQ_BF16 ? 8 : 16); ++s)
+    raw[s] = reinterpret_cast<const uint4*>(base)[s];
+  // the fragments of row tile T: rotation (bf16 hi / lo) and, for keys, the QJL
+  // matrix (fp16 hi / lo), all in registers before the first barrier
+  b8 fah[8], fal[8];
+#pragma unroll
+  for (int s = 0; s < 8; ++s) {
+    fah[s] = __builtin_bit_cast(b8, fpi[(T * 8 + s) * 64 + lane]);
+    fal[s] = __builtin_bit_cast(b8, fpi[(32 + T * 8 + s) * 64 + lane]);
+  }
+  hh8 sfh[KEY ? 8 : 1], sfl[KEY ? 8 : 1];
+  if constexpr (KEY) {
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      sfh[s] = __builtin_bit_cast(hh8, fsm[(T * 8 + s) * 64 + lane]);
+      sfl[s] = __builtin_bit_cast(hh8, fsm[(32 + T * 8 + s) * 64 + lane]);
+    }
+  }
+  table();
   b8 xb[8];
   b8 xl[DT == FQ_BF16 ? 1 : 8];
   float ss = 0.f;
   if constexpr (DT == FQ_BF16) {
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
-      uint4 u = valid ? reinterpret_cast<const uint4*>(base)[s] : make_uint4(0, 0, 0, 0);
+      const uint4 u = raw[s];
       const uint32_t w4[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
@@ -604,8 +648,8 @@ __device__ __forceinline__ void compress_quarter(const CompressArgs& a, int kind
   } else {
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
-      float4 f0 = valid ? reinterpret_cast<const float4*>(base)[2 * s] : make_float4(0, 0, 0, 0);
-      float4 f1 = valid ? reinterpret_cast<const float4*>(base)[2 * s + 1] : make_float4(0, 0, 0, 0);
+      const float4 f0 = __builtin_bit_cast(float4, raw[2 * s]);
+      const float4 f1 = __builtin_bit_cast(float4, raw[2 * s + 1]);
       const float xs[8] = {f0.x, f0.y, f0.z, f0.w, f1.x, f1.y, f1.z, f1.w};
       uint32_t hi[8], lo[8];
 #pragma unroll
@@ -621,22 +665,11 @@ __device__ __forceinline__ void compress_quarter(const CompressArgs& a, int kind
   const float n = sqrtf(ss);
   const float inv = n > 0.f ? 1.0f / n : 0.f;
 
-  // QJL fragments of row tile T, requested now so that they are in registers
-  // before the residual exchange (a barrier no load moves across)
-  hh8 sfh[KEY ? 8 : 1], sfl[KEY ? 8 : 1];
-  if constexpr (KEY) {
-#pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      sfh[s] = __builtin_bit_cast(hh8, fsm[(T * 8 + s) * 64 + lane]);
-      sfl[s] = __builtin_bit_cast(hh8, fsm[(32 + T * 8 + s) * 64 + lane]);
-    }
-  }
   // ---- row tile T of the rotation (hi and lo products in separate chains)
   f16v acc = f16v{}, acc2 = f16v{};
 #pragma unroll
   for (int s = 0; s < 8; ++s) {
-    const b8 ah = __builtin_bit_cast(b8, fpi[(T * 8 + s) * 64 + lane]);
-    const b8 al = __builtin_bit_cast(b8, fpi[(32 + T * 8 + s) * 64 + lane]);
+    const b8 ah = fah[s], al = fal[s];
     acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, xb[s], acc, 0, 0, 0);
     acc2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, xb[s], acc2, 0, 0, 0);
     if constexpr (DT != FQ_BF16) acc2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, xl[s], acc2, 0, 0, 0);
@@ -644,14 +677,12 @@ __device__ __forceinline__ void compress_quarter(const CompressArgs& a, int kind
   // acc[vv] = (Pi x / |x|)[64h + 16T + vv]
 #pragma unroll
   for (int vv = 0; vv < 16; ++vv) acc[vv] = (acc[vv] + acc2[vv]) * inv;
-  // the quantization cells are built while the products run; uniform over the work-group
-  table();
   const float inv_w = s_qmap[0], off = s_qmap[1];
 
   const int64_t rec = ((slot >> 4) * a.hkv + hd) * FQ_BLOCK + (slot & 15);
   const bool store = slot >= 0;
-  if (a.dbg_y && store) {
-    float4* dy = reinterpret_cast<float4*>(a.dbg_y + ((kind * a.ntok + t) * a.hkv + hd) * D + 64 * h + 16 * T);
+  if (dbg_y && store) {
+    float4* dy = reinterpret_cast<float4*>(dbg_y + ((kind * a.ntok + t) * a.hkv + hd) * D + 64 * h + 16 * T);
 #pragma unroll
     for (int q = 0; q < 4; ++q) dy[q] = make_float4(acc[4 * q], acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]);
   }
@@ -674,10 +705,10 @@ __device__ __forceinline__ void compress_quarter(const CompressArgs& a, int kind
     if constexpr (KEY) acc[vv] = y - (gt ? q.c_hi : q.c_lo);
   }
   if (store) {
-    uint8_t* cd = a.codes[kind] + rec * (D * BITS / 8) + (64 * h + 16 * T) * BITS / 8;
+    uint8_t* cd = codes_p + rec * (D * BITS / 8) + (64 * h + 16 * T) * BITS / 8;
     if constexpr (NW == 2) *reinterpret_cast<uint2*>(cd) = make_uint2(words[0], words[1]);
     else *reinterpret_cast<uint32_t*>(cd) = words[0];
-    if (h == 0 && T == 0) a.norm[kind][rec] = n;
+    if (h == 0 && T == 0) norm_p[rec] = n;
   }
 
   if constexpr (KEY) {
@@ -714,10 +745,10 @@ __device__ __forceinline__ void compress_quarter(const CompressArgs& a, int kind
     float rr_all = (s_rr[lane] + s_rr[64 + lane]) + (s_rr[128 + lane] + s_rr[192 + lane]);
     rr_all += __shfl_xor(rr_all, 32);
     if (store) {
-      *reinterpret_cast<uint16_t*>(a.qjl + rec * (D / 8) + 8 * h + 2 * T) = static_cast<uint16_t>(sg);
-      if (h == 0 && T == 0) a.gamma[rec] = n * sqrtf(rr_all);
-      if (a.dbg_p) {
-        float4* dp = reinterpret_cast<float4*>(a.dbg_p + (t * a.hkv + hd) * D + 64 * h + 16 * T);
+      *reinterpret_cast<uint16_t*>(qjl_p + rec * (D / 8) + 8 * h + 2 * T) = static_cast<uint16_t>(sg);
+      if (h == 0 && T == 0) gamma_p[rec] = n * sqrtf(rr_all);
+      if (dbg_p) {
+        float4* dp = reinterpret_cast<float4*>(dbg_p + (t * a.hkv + hd) * D + 64 * h + 16 * T);
 #pragma unroll
         for (int q = 0; q < 4; ++q) dp[q] = make_float4(pacc[4 * q], pacc[4 * q + 1], pacc[4 * q + 2], pacc[4 * q + 3]);
       }
@@ -736,7 +767,7 @@ __global__ void __launch_bounds__(256) compress_split_kernel(CompressArgs a) {
   const int kind = blockIdx.y;
   if (!a.src[kind]) return;  // uniform over the work-group
   // Every global load is issued up front; the quantization cells are built from
-  // the codebook after the rotation products, which do not need them.
+  // the codebook while the inputs are in flight.
   const float cbv = codebook_value<BITS>(a, tid);
   auto table = [&]() {
     stage_codebook<BITS>(s_bl, tid, cbv);
