@@ -120,9 +120,11 @@ def test_compress_lane_kernel_matches_matrix_core_kernel(gpu_lib, monkeypatch):
         parity.check_compress(inp, oq, cache, dy, dp)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("bits", [4, 2])
-def test_compress_kernels_derive_operands_without_prepared_buffer(gpu_lib, bits):
-    """Without the packed operand buffer the tile kernel builds the fragments in LDS."""
-    w, inp = parity.small_workload(2, 8, 4, [300, 45], 304, bits=bits, seed=67)
+def test_compress_kernels_derive_operands_without_prepared_buffer(gpu_lib, bits, dtype):
+    """Without the packed operand buffer the multi-tile kernel (the one large inputs use)
+    builds the fragments in LDS; bf16 and fp32 inputs."""
+    w, inp = parity.small_workload(2, 8, 4, [300, 45], 304, dtype=dtype, bits=bits, seed=67)
     qz, cache, dy, dp, oq, _ = _run(w, inp, prepared=False)
     parity.check_compress(inp, oq, cache, dy, dp)
