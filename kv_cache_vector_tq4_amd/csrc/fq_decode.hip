@@ -964,6 +964,11 @@ constexpr int PK_CODE_BASE = 4096;    // 256 x 32 x 8 B (4-bit) or 256 x 16 x 16
 constexpr int PK_STAGE_BASE = 69632;  // 256 x 16 B staging for the table build
 constexpr int PK_QOPS_BASE = 73728;   // 8 x 64 lanes x 16 B code-product operands
 constexpr int PK_LDS_BYTES = PK_QOPS_BASE + 8 * 64 * 16;  // 80 KB: two work-groups per CU
+// The single-split kernel (one work-group per CU) adds a byte-indexed QJL sign
+// table: 256 entries of eight fp16 +-1, 16 copies (copy = lane % 16), so one
+// 16-byte lookup per sign byte.
+constexpr int PK_BSIGN_BASE = PK_LDS_BYTES;
+constexpr int PK_LDS_BYTES_F = PK_BSIGN_BASE + 256 * 16 * 16;
 // In-kernel query preparation (groups of up to 8 heads) uses the code-table area
 // before the table is built: its scratch, then the FQ_QOPS x 64 operands.
 constexpr int PK_PREP_GM = 8;
@@ -1006,26 +1011,42 @@ template <int BITS>
 __device__ __forceinline__ void pk_load(const DecodeArgs& a, int64_t rec0, int n, const PkLane& o,
                                         const float* gptr, const uint8_t* sgn_base, PkPage<BITS>& d) {
   constexpr int CB = D * BITS / 8;  // code bytes per vector
+  // The page's field bases are uniform: pinned in scalar registers, every load is a
+  // scalar base plus the lane's 32-bit offset (no 64-bit vector address adds).
+  typedef const __attribute__((address_space(1))) uint8_t* gb8;
+  typedef const __attribute__((address_space(1))) float* gf32;
+  gb8 kcb = (gb8)(a.k_codes + rec0 * CB);
+  gb8 sgb = (gb8)(sgn_base + rec0 * 16);
+  gf32 knb = (gf32)(a.k_norm + rec0);
+  gf32 gmb = (gf32)(gptr + rec0);
+  gf32 vnb = (gf32)(a.v_norm + rec0);
+  gb8 vcb = (gb8)(a.v_codes + rec0 * CB);
+  asm volatile("" : "+s"(kcb), "+s"(sgb), "+s"(knb), "+s"(gmb), "+s"(vnb), "+s"(vcb));
+  uint32_t okc = o.kc, osg = o.sg, ovc = o.vc;  // 32-bit lane offsets, kept so
+  asm volatile("" : "+v"(okc), "+v"(osg), "+v"(ovc));
   if constexpr (BITS == 4) {
-    const uint4 k = *reinterpret_cast<const uint4*>(a.k_codes + rec0 * CB + o.kc);
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    const u32x4 k = *reinterpret_cast<const __attribute__((address_space(1))) u32x4*>(kcb + okc);
     d.kc[0] = k.x;
     d.kc[1] = k.y;
     d.kc[2] = k.z;
     d.kc[3] = k.w;
   } else {
-    const uint2 k = *reinterpret_cast<const uint2*>(a.k_codes + rec0 * CB + o.kc);
+    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+    const u32x2 k = *reinterpret_cast<const __attribute__((address_space(1))) u32x2*>(kcb + okc);
     d.kc[0] = k.x;
     d.kc[1] = k.y;
   }
-  d.sg = *reinterpret_cast<const uint32_t*>(sgn_base + rec0 * 16 + o.sg);
-  d.kn = a.k_norm[rec0 + n];
-  d.gm = gptr[rec0 + n];
-  d.vn = a.v_norm[rec0 + n];
-  const uint8_t* vcb = a.v_codes + rec0 * CB + o.vc;
+  d.sg = *reinterpret_cast<const __attribute__((address_space(1))) uint32_t*>(sgb + osg);
+  d.kn = knb[n];
+  d.gm = gmb[n];
+  d.vn = vnb[n];
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
-    if constexpr (BITS == 4) d.vc[e] = *reinterpret_cast<const uint32_t*>(vcb + CB * e);
-    else d.vc[e] = *reinterpret_cast<const uint16_t*>(vcb + CB * e);
+    if constexpr (BITS == 4)
+      d.vc[e] = *reinterpret_cast<const __attribute__((address_space(1))) uint32_t*>(vcb + ovc + CB * e);
+    else
+      d.vc[e] = *reinterpret_cast<const __attribute__((address_space(1))) uint16_t*>(vcb + ovc + CB * e);
   }
 }
 
@@ -1040,7 +1061,9 @@ __global__ void __launch_bounds__(WAVES * 64, OCC) packed_decode_kernel(DecodeAr
   static_assert(PREP < 0 || WAVES * 64 >= PQ_THREADS, "in-kernel query preparation takes PQ_THREADS threads");
   static_assert(WAVES * 64 >= 256, "the table stage takes 256 threads");
   constexpr int CB = D * BITS / 8;  // code bytes per vector
-  __shared__ __align__(16) uint8_t s_lds[PK_LDS_BYTES];
+  constexpr bool BSIGN = PREP >= 0;  // byte-indexed sign table
+  constexpr int PRO = RING - 1;  // pages requested ahead of the loop
+  __shared__ __align__(16) uint8_t s_lds[BSIGN ? PK_LDS_BYTES_F : PK_LDS_BYTES];
   const uint8_t* const s_code = s_lds + PK_CODE_BASE;
   const uint8_t* const s_sign = s_lds + PK_SIGN_BASE;
   constexpr int HL = 4 / SLOTS;  // heads per lane in the score layout (1 or 2)
@@ -1105,7 +1128,7 @@ __global__ void __launch_bounds__(WAVES * 64, OCC) packed_decode_kernel(DecodeAr
   PkPage<BITS> ring[RING];
   if (my_pages > 0) {
 #pragma unroll
-    for (int k = 0; k < RING - 1; ++k)
+    for (int k = 0; k < PRO; ++k)
       pk_load(a, rec_of(bt_cur, min(k, min(64, my_pages) - 1)), n, lo, gptr, sgn_base, ring[k]);
   }
 
@@ -1162,6 +1185,21 @@ __global__ void __launch_bounds__(WAVES * 64, OCC) packed_decode_kernel(DecodeAr
         stage4[tid] = make_uint4(h2bits(h0, h1), h2bits(l0, l1), h2bits(h2, h3), h2bits(l2, l3));
       }
     }
+    if constexpr (BSIGN) {
+      // entry (byte x, copy c) at 256 x + 16 c: half e = bit e of x ? +1 : -1
+      for (int idx = tid; idx < 256 * 16; idx += WAVES * 64) {
+        const uint32_t x = static_cast<uint32_t>(idx) >> 4;
+        uint32_t w[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const uint32_t lo16 = ((x >> (2 * k)) & 1) ? 0x3C00u : 0xBC00u;
+          const uint32_t hi16 = ((x >> (2 * k + 1)) & 1) ? 0x3C00u : 0xBC00u;
+          w[k] = lo16 | (hi16 << 16);
+        }
+        *reinterpret_cast<uint4*>(s_lds + PK_BSIGN_BASE + idx * 16) = make_uint4(w[0], w[1], w[2], w[3]);
+      }
+    }
+    if constexpr (!BSIGN)
     for (int idx = tid; idx < 16 * 32; idx += WAVES * 64) {
       const int nib = idx >> 5;
       uint32_t w[2];
@@ -1222,7 +1260,9 @@ __global__ void __launch_bounds__(WAVES * 64, OCC) packed_decode_kernel(DecodeAr
   for (int t = 0; t < 8; ++t) acc_o[t] = f4{0.f, 0.f, 0.f, 0.f};
   __syncthreads();
 
-  auto process = [&](const PkPage<BITS>& d, int p) {
+  // ---- one page: scores (16 tokens x this lane's heads, -inf where the token is
+  // past the split or the page is a stand-in), then softmax, then the value product
+  auto score = [&](const PkPage<BITS>& d, int p, bool real, float (&sc)[HL]) {
     // ---- scores: C[(head, slot)][token]; product i covers dims 32g + 4i .. 4i+3
     f4 accM = {0.f, 0.f, 0.f, 0.f}, accQ = {0.f, 0.f, 0.f, 0.f};
     const uint32_t sgl = d.sg & 0x0F0F0F0Fu, sgh = (d.sg >> 4) & 0x0F0F0F0Fu;
@@ -1240,12 +1280,65 @@ __global__ void __launch_bounds__(WAVES * 64, OCC) packed_decode_kernel(DecodeAr
       const h8 qmi = SLOTS == 4 ? qmr[i] : s_qm[i * 64];
       accM = mfma32(qmi, kop, accM);
       if (i < 4) {
-        const uint2 z0 = lds_u2(s_sign, tab_off(sgl, copy8, i));
-        const uint2 z1 = lds_u2(s_sign, tab_off(sgh, copy8, i));
-        if constexpr (SLOTS == 4) accQ = mfma32(qmi, h8_of(z0, z1), accQ);
-        else accQ = mfma32(qs[i], h8_of(z0, z1), accQ);
+        h8 sop;  // +-1 of projections 32g + 8i .. +7 (sign byte i of the lane)
+        if constexpr (BSIGN) {
+          const uint4 z = lds_u4(s_lds + PK_BSIGN_BASE, tab_off(d.sg, copy16, i));
+          sop = as_h8(z.x, z.y, z.z, z.w);
+        } else {
+          const uint2 z0 = lds_u2(s_sign, tab_off(sgl, copy8, i));
+          const uint2 z1 = lds_u2(s_sign, tab_off(sgh, copy8, i));
+          sop = h8_of(z0, z1);
+        }
+        if constexpr (SLOTS == 4) accQ = mfma32(qmi, sop, accQ);
+        else accQ = mfma32(qs[i], sop, accQ);
       }
     }
+    const bool valid = real && t0 + p * FQ_BLOCK + n < t1;
+    if constexpr (SLOTS == 4) {
+      sc[0] = fmaf(accQ[2] + accQ[3], d.gm, (accM[0] + accM[1]) * d.kn) * cf[0];
+    } else {
+      sc[0] = fmaf(accQ[0] + accQ[1], d.gm, (accM[0] + accM[1]) * d.kn) * cf[0];
+      sc[1] = fmaf(accQ[2] + accQ[3], d.gm, (accM[2] + accM[3]) * d.kn) * cf[1];
+    }
+#pragma unroll
+    for (int k = 0; k < HL; ++k) sc[k] = valid ? sc[k] : -INFINITY;
+  };
+  // The running max only has to be within PK_TAU of the true one, so a page's max is
+  // formed only when some score exceeds it by more than that (the 16 lanes of row g
+  // hold one head's 16 tokens).
+  auto grows = [&](const float (&sc)[HL]) {
+    bool grow = false;
+#pragma unroll
+    for (int k = 0; k < HL; ++k) grow = grow || (sc[k] > m_run[k] + PK_TAU);
+    return grow;
+  };
+  auto rescale = [&](const float (&mx)[HL]) {  // mx: this lane's candidate maxima
+    float al[HL];
+#pragma unroll
+    for (int k = 0; k < HL; ++k) {
+      const float m_new = fmaxf(m_run[k], row_max(mx[k]));
+      al[k] = __builtin_amdgcn_exp2f(m_run[k] - m_new);  // 0 while m_run = -inf
+      l_run[k] *= al[k];
+      m_run[k] = m_new;
+    }
+    // acc_o rows 4g .. 4g+3 are (head HL g + k, slot) pairs
+    const f4 av = HL == 1 ? f4{al[0], al[0], al[0], al[0]} : f4{al[0], al[0], al[HL - 1], al[HL - 1]};
+#pragma unroll
+    for (int t = 0; t < 8; ++t) acc_o[t] *= av;
+  };
+  auto probs = [&](const float (&sc)[HL], float vn, uint32_t (&xp)[HL]) {
+    // (hi, lo) fp16 pair of p * value norm, per head of this lane
+#pragma unroll
+    for (int k = 0; k < HL; ++k) {
+      const bool live = sc[k] != -INFINITY;
+      const float pr = live ? __builtin_amdgcn_exp2f(sc[k] - m_run[k]) : 0.f;
+      l_run[k] += pr;
+      _Float16 ph, pl;
+      split_f16(pr * vn, ph, pl);
+      xp[k] = h2bits(ph, pl);
+    }
+  };
+  auto pv = [&](const PkPage<BITS>& d, const uint32_t (&xp)[HL]) {
     // 4-bit: pair bytes (token 4g, 4g+1) and (4g+2, 4g+3) per dimension 8n + t.
     // 2-bit: bytes of 2-bit fields (4g, 4g+2, 4g+1, 4g+3) per dimension, byte k
     // of r1 = dims 8n + {0, 4, 1, 5}, of r2 = dims 8n + {2, 6, 3, 7}.
@@ -1264,47 +1357,6 @@ __global__ void __launch_bounds__(WAVES * 64, OCC) packed_decode_kernel(DecodeAr
       const uint32_t ee = n02e | (n02o << 16), ff = n13e | (n13o << 16);
       r1 = (ee & 0x0F0F0F0Fu) | ((ff << 4) & 0xF0F0F0F0u);
       r2 = ((ee >> 4) & 0x0F0F0F0Fu) | (ff & 0xF0F0F0F0u);
-    }
-    const bool valid = t0 + p * FQ_BLOCK + n < t1;
-    float sc[HL];
-    if constexpr (SLOTS == 4) {
-      sc[0] = fmaf(accQ[2] + accQ[3], d.gm, (accM[0] + accM[1]) * d.kn) * cf[0];
-    } else {
-      sc[0] = fmaf(accQ[0] + accQ[1], d.gm, (accM[0] + accM[1]) * d.kn) * cf[0];
-      sc[1] = fmaf(accQ[2] + accQ[3], d.gm, (accM[2] + accM[3]) * d.kn) * cf[1];
-    }
-    // ---- online softmax: the 16 lanes of row g hold one head's 16 tokens. The
-    // running max only has to be within PK_TAU of the true one, so the page max
-    // is formed only when some score exceeds it by more than that.
-    bool grow = false;
-#pragma unroll
-    for (int k = 0; k < HL; ++k) {
-      sc[k] = valid ? sc[k] : -INFINITY;
-      grow = grow || (sc[k] > m_run[k] + PK_TAU);
-    }
-    if (__any(grow)) {
-      float al[HL];
-#pragma unroll
-      for (int k = 0; k < HL; ++k) {
-        const float m_new = fmaxf(m_run[k], row_max(sc[k]));
-        al[k] = __builtin_amdgcn_exp2f(m_run[k] - m_new);  // 0 while m_run = -inf
-        l_run[k] *= al[k];
-        m_run[k] = m_new;
-      }
-      // acc_o rows 4g .. 4g+3 are (head HL g + k, slot) pairs
-      const f4 av = HL == 1 ? f4{al[0], al[0], al[0], al[0]} : f4{al[0], al[0], al[HL - 1], al[HL - 1]};
-#pragma unroll
-      for (int t = 0; t < 8; ++t) acc_o[t] *= av;
-    }
-    uint32_t xp[HL];  // (hi, lo) fp16 pair of p * value norm, per head of this lane
-#pragma unroll
-    for (int k = 0; k < HL; ++k) {
-      const float pr = __builtin_amdgcn_exp2f(sc[k] - m_run[k]);
-      l_run[k] += pr;
-      const float pv = valid ? pr * d.vn : 0.f;
-      _Float16 ph, pl;
-      split_f16(pv, ph, pl);
-      xp[k] = h2bits(ph, pl);
     }
     // to the operand layout: (hi, lo) pairs of tokens 4g .. 4g+3 for head n / SLOTS
     uint32_t y[4];
@@ -1337,6 +1389,16 @@ __global__ void __launch_bounds__(WAVES * 64, OCC) packed_decode_kernel(DecodeAr
       acc_o[t] = mfma32(ap, vop, acc_o[t]);
     }
   };
+  auto process = [&](const PkPage<BITS>& d, int p) {
+    float sc[HL];
+    score(d, p, true, sc);
+    if (__any(grows(sc))) rescale(sc);
+    uint32_t xp[HL];
+    probs(sc, d.vn, xp);
+    pv(d, xp);
+  };
+
+
 
   // The only split un-rotates its output at the end: column jj of Pi (rows 32 kq ..)
   // is requested now and arrives during the page loop.
@@ -1354,7 +1416,7 @@ __global__ void __launch_bounds__(WAVES * 64, OCC) packed_decode_kernel(DecodeAr
     if (c0 > 0) {
       bt_cur = bt_chunk(c0);
 #pragma unroll
-      for (int k = 0; k < RING - 1; ++k) pk_load(a, rec_of(bt_cur, min(k, cn - 1)), n, lo, gptr, sgn_base, ring[k]);
+      for (int k = 0; k < PRO; ++k) pk_load(a, rec_of(bt_cur, min(k, cn - 1)), n, lo, gptr, sgn_base, ring[k]);
     }
     for (int i = 0; i < cn; i += RING) {
 #pragma unroll
