@@ -53,6 +53,25 @@ def measured_traffic():
         return None
     return rec.get("bytes_per_launch")
 HBM_PEAK_GBS = 8000.0
+MFMA_FILE = os.path.join(ROOT, "profiles", "compress_mfma_util.json")
+COMPRESS_SRC = os.path.join(ROOT, "kv_cache_vector_tq4_amd", "csrc", "fq_compress.hip")
+
+
+def measured_mfma_util():
+    """Matrix-core utilisation of the prefill compress kernels from the committed
+    rocprofv3 counter summary, or None when the compress source has changed since."""
+    import hashlib
+
+    try:
+        with open(MFMA_FILE) as f:
+            rec = json.load(f)
+        with open(COMPRESS_SRC, "rb") as f:
+            sha = hashlib.sha256(f.read()).hexdigest()
+    except (OSError, ValueError):
+        return None
+    if rec.get("compress_source_sha256") != sha:
+        return None
+    return rec.get("kernels")
 
 
 def parse():
@@ -182,6 +201,50 @@ def decode_layer_measure(index, bits, rot, replicas, reps, stream):
             "timing": "HIP events around graph replays of one call per cache replica",
             "achieved_gbs": nbytes / (ms * 1e-3) / 1e9, "frac_hbm": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
             "algorithmic_bytes": nbytes, "cache_replicas": replicas}
+
+
+def compress_layer_measure(index, rot, reps, stream):
+    """Prefill compress of one layer's whole context (K and V) of a workload."""
+    import torch
+
+    from kv_cache_vector_tq4_amd import fq, synth
+
+    w = synth.workload(index)
+    Hkv, d = w.num_kv_heads, w.head_dim
+    T = int(np.sum(w.seq_lens))
+    qz = fq.Quantizer(4, d, rot, 1, 2, 128)
+    cache = fq.PagedCache((T + 15) // 16, Hkv, d, 4, 128)
+    slots = torch.arange(T, dtype=torch.int64, device="cuda")
+    k, v = synth.kv_device(8000 + index, T, Hkv, d)
+    fq.compress(qz, cache, k, v, slots)
+    ms = _events_ms(lambda: fq.compress(qz, cache, k, v, slots), reps, stream)
+    nvec = 2 * T * Hkv
+    nbytes = nvec * d * 2 + T * 8 + T * Hkv * cache.bytes_per_token_head()
+    return {"workload": w.name, "rotation": "wht" if rot else "haar", "vectors": nvec, "ms": ms,
+            "mvec_per_s": nvec / (ms * 1e-3) / 1e6, "achieved_gbs": nbytes / (ms * 1e-3) / 1e9,
+            "frac_hbm": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+
+
+def attention_cosines(q, k, v, lens, kv_rows, out, seqs):
+    """Cosine of the decode outputs against exact softmax attention over the
+    uncompressed (bf16) K and V, per (sequence, query head), for sampled sequences.
+    Reference arithmetic in fp32 with torch (measurement only)."""
+    import torch
+
+    Hq, d = q.shape[1], q.shape[2]
+    Hkv = k.shape[1]
+    G = Hq // Hkv
+    cos = []
+    for b in seqs:
+        kb, vb = kv_rows(b)  # [len][Hkv][d] float32
+        qb = q[b].float().view(Hkv, G, d)
+        s = torch.matmul(qb, kb.permute(1, 2, 0).contiguous()) / np.sqrt(d)  # [Hkv][G][len]
+        o = torch.matmul(torch.softmax(s, dim=-1), vb.permute(1, 0, 2).contiguous())  # [Hkv][G][d]
+        ref = o.reshape(Hq, d)
+        got = out[b]
+        cos.append(torch.nn.functional.cosine_similarity(ref, got, dim=-1).cpu().numpy())
+    c = np.concatenate(cos)
+    return {"mean": float(c.mean()), "min": float(c.min()), "pairs": int(c.size)}
 
 
 def stream_compress_measure(bits, layers, stream):
@@ -362,6 +425,21 @@ def main():
         torch.cuda.synchronize()
         dec_ms = float(np.mean([a.elapsed_time(b) for a, b in pairs])) / w.layers
 
+    # accuracy: layer 0's outputs against exact attention over its uncompressed K / V
+    # (the newest token of sequence b holds knew[0][b] / vnew[0][b], written by the step)
+    k0, v0 = synth.kv_device(5000, ntok, Hkv, d, device=dev)
+    offs = np.concatenate([[0], np.cumsum(lens)])
+
+    def kv_rows(b):
+        kb = k0[offs[b]:offs[b + 1]].float().clone()
+        vb = v0[offs[b]:offs[b + 1]].float().clone()
+        kb[-1] = knew[0][b].float()
+        vb[-1] = vnew[0][b].float()
+        return kb, vb
+
+    accuracy = attention_cosines(qs[0], k0, v0, lens, kv_rows, outs[0], [0, 7, 15, 31])
+    del k0, v0
+
     bpt = caches[0].bytes_per_token_head()  # 156 B at 4 bits with QJL keys
     dec_bytes = ntok * Hkv * bpt
     achieved = dec_bytes / (dec_ms * 1e-3) / 1e9
@@ -413,18 +491,25 @@ def main():
             "achieved_gbs": comp_bytes / (comp_med_ms * 1e-3) / 1e9,
             "frac_hbm": comp_bytes / (comp_med_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
             "algorithmic_bytes_per_launch": comp_bytes,
+            "mfma_util": measured_mfma_util(),
         },
+        "accuracy": dict(accuracy, what="cosine of decode outputs vs exact fp32 softmax attention over the "
+                         "uncompressed bf16 K/V, layer 0, sequences 0 / 7 / 15 / 31, all 32 query heads"),
     }
     if not args.no_extra:
         del caches, knew, vnew, qs, outs
         torch.cuda.empty_cache()
-        log("other workloads: 70B-shape 32K decode, 80-layer compress stream, batch-4 2-bit decode...")
+        log("other workloads: 70B-shape 32K decode and compress, 80-layer compress stream, batch-4 2-bit "
+            "decode, batch-1 8B decode...")
         extra = {}
         extra["llama70b_b1_ctx32k_haar"] = decode_layer_measure(3, 4, fq.ROT_HAAR, 8, 20, stream)
         extra["llama70b_b1_ctx32k_wht"] = decode_layer_measure(3, 4, fq.ROT_WHT, 8, 20, stream)
         extra["stream_80layer_compress_4bit"] = stream_compress_measure(4, 80, stream)
         extra["stream_80layer_compress_2bit"] = stream_compress_measure(2, 80, stream)
         extra["b4_ctx32k_decode_2bit"] = decode_layer_measure(4, 2, fq.ROT_HAAR, 4, 10, stream)
+        extra["llama8b_b1_ctx4k"] = decode_layer_measure(1, 4, fq.ROT_HAAR, 32, 64, stream)
+        extra["llama70b_b1_ctx32k_compress_haar"] = compress_layer_measure(3, fq.ROT_HAAR, 10, stream)
+        extra["llama70b_b1_ctx32k_compress_wht"] = compress_layer_measure(3, fq.ROT_WHT, 10, stream)
         result["other_workloads"] = extra
     if not args.no_cpu:
         log("timing the CPU oracle (~%.0f s)..." % args.cpu_seconds)
