@@ -9,16 +9,19 @@ launch; --splits 4 runs the pages' 4-way split instead). Every layer has its own
 compressed cache (5.2 GB in all, far beyond the 256 MB last-level cache), filled
 by compressing the whole synthetic context before timing.
 
-One step = one decode step of the whole 32-layer stack: per layer, fq_compress of
-the newest token's K and V (written into its slot) and fq_decode_attention of
-the 32 sequences over their compressed pages. value = batch / step time
-(decode tokens/s). Inputs are resident in HBM before the timed region.
+One step = one decode step of the whole 32-layer stack: per layer, the newest
+token's K and V compressed into its slot and the attention of the 32 sequences
+over their compressed pages, as fq_decode_step does it (its two halves are
+enqueued as fq_step_prepare: append + query preparation, and fq_step_attend: the
+attention, so that HIP events can bracket the attention launch). --separate
+runs fq_compress + fq_decode_attention per layer instead. value = batch / step
+time (decode tokens/s). Inputs are resident in HBM before the timed region.
 
 Also reported: the prefill compress rate (Mvectors/s) measured while filling
-the caches, the roofline of the dominant kernel (the decode) and the CPU oracle
-timed on a bounded sample of the same work.
+the caches, the roofline of the dominant kernel (the attention launch) and the
+CPU oracle timed on a bounded sample of the same work.
 
-    python bench.py [--steps K] [--warmup W] [--gpus 1] [--layers 32] [--splits S] [--no-cpu]
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--layers 32] [--splits S] [--separate] [--no-cpu]
 """
 import argparse
 import json
@@ -85,6 +88,8 @@ def parse():
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--no-graph", action="store_true", help="time eager launches instead of a HIP graph")
+    p.add_argument("--separate", action="store_true",
+                   help="per layer fq_compress of the newest tokens, then fq_decode_attention")
     p.add_argument("--no-extra", action="store_true", help="skip the other workloads' measurements")
     p.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                    help="only run a plain device-to-device copy of BYTES (for scaling HBM byte counters)")
@@ -333,19 +338,35 @@ def main():
         del k, v
     torch.cuda.synchronize()
     ws_bytes = fq.workspace_bytes(B, Hq, Hkv, d, 128, max_len, splits)
-    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    # one workspace per layer: each keeps its layer's prepared queries, so the
+    # attention launches can also be replayed on their own
+    wss = [torch.empty(ws_bytes, dtype=torch.uint8, device=dev) for _ in range(w.layers)]
     outs = [torch.empty((B, Hq, d), dtype=torch.float32, device=dev) for _ in range(w.layers)]
 
-    ev = []  # (start, end) events around each decode call in the timed steps
+    ev = []  # (start, end) events around each attention launch in the timed steps
+
+    def attend(layer):
+        if args.separate:
+            fq.decode(qz, caches[layer], qs[layer], bt, lens_t, max_len, num_splits=splits, workspace=wss[layer],
+                      out=outs[layer])
+        else:
+            fq.step_attend(qz, caches[layer], B, Hq, bt, lens_t, max_len, wss[layer], num_splits=splits,
+                           out=outs[layer])
+
+    def prepare(layer):
+        if args.separate:
+            fq.compress(qz, caches[layer], knew[layer], vnew[layer], new_slots)
+        else:
+            fq.step_prepare(qz, caches[layer], knew[layer], vnew[layer], new_slots, qs[layer], max_len,
+                            wss[layer], num_splits=splits)
 
     def step(record):
         for layer in range(w.layers):
-            fq.compress(qz, caches[layer], knew[layer], vnew[layer], new_slots)
+            prepare(layer)
             if record:
                 e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                 e0.record(stream)
-            fq.decode(qz, caches[layer], qs[layer], bt, lens_t, max_len, num_splits=splits, workspace=ws,
-                      out=outs[layer])
+            attend(layer)
             if record:
                 e1.record(stream)
                 ev.append((e0, e1))
@@ -357,7 +378,7 @@ def main():
     graph = None
     graph_check = None
     if not args.no_graph:
-        # The step is launch-bound (5 launches per layer): capture it once, replay it.
+        # The step is launch-bound (two launches per layer): capture it once, replay it.
         ref = [o.clone() for o in outs]
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())
@@ -397,33 +418,38 @@ def main():
     torch.cuda.synchronize()
     ms_eager = (time.perf_counter() - t1) * 1000.0 / args.steps
     dec_ms_eager = float(np.mean([a.elapsed_time(b) for a, b in ev]))
-    # ... and from HIP events around replays of a graph holding only the layers' decode
-    # calls (device time of the call as the stack runs it)
+    # ... and from HIP events around replays of a graph holding only the layers'
+    # attention launches (device time of the launch as the stack runs it), and one
+    # holding only the preparation launches
     dec_ms = dec_ms_eager
+    prep_ms = None
     if graph is not None:
-        def decodes():
-            for layer in range(w.layers):
-                fq.decode(qz, caches[layer], qs[layer], bt, lens_t, max_len, num_splits=splits, workspace=ws,
-                          out=outs[layer])
-        side = torch.cuda.Stream()
-        side.wait_stream(torch.cuda.current_stream())
-        dgraph = torch.cuda.CUDAGraph()
-        with torch.cuda.stream(side):
-            with torch.cuda.graph(dgraph, stream=side):
-                decodes()
-        torch.cuda.current_stream().wait_stream(side)
-        torch.cuda.synchronize()
-        dgraph.replay()
-        torch.cuda.synchronize()
-        pairs = []
-        for _ in range(args.steps):
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            dgraph.replay()
-            e1.record(stream)
-            pairs.append((e0, e1))
-        torch.cuda.synchronize()
-        dec_ms = float(np.mean([a.elapsed_time(b) for a, b in pairs])) / w.layers
+        def graph_ms(fn):
+            side = torch.cuda.Stream()
+            side.wait_stream(torch.cuda.current_stream())
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.stream(side):
+                with torch.cuda.graph(g, stream=side):
+                    for layer in range(w.layers):
+                        fn(layer)
+            torch.cuda.current_stream().wait_stream(side)
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            pairs = []
+            for _ in range(args.steps):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                g.replay()
+                e1.record(stream)
+                pairs.append((e0, e1))
+            torch.cuda.synchronize()
+            return float(np.mean([a.elapsed_time(b) for a, b in pairs])) / w.layers
+
+        ref = [o.clone() for o in outs]
+        dec_ms = graph_ms(attend)
+        assert all(torch.equal(o, r) for o, r in zip(outs, ref)), "attention replays differ from the step"
+        prep_ms = graph_ms(prepare)
 
     # accuracy: layer 0's outputs against exact attention over its uncompressed K / V
     # (the newest token of sequence b holds knew[0][b] / vnew[0][b], written by the step)
@@ -462,16 +488,21 @@ def main():
         "dtype": "f32",
         "data": "synthetic",
         "config": {
-            "workload": "llama3-8b-shape attention stack: %d layers x (compress new token + decode), batch %d, "
+            "workload": "llama3-8b-shape attention stack: %d layers x (compress new token + decode%s), batch %d, "
                         "ctx U[3072,4096] (sum %d), 32 q / 8 kv heads, d 128, TQ4 K(MSE+QJL)+V, 16-token pages, "
-                        "%d splits" % (w.layers, B, ntok, splits),
+                        "%d splits" % (w.layers, ": fq_compress, fq_decode_attention" if args.separate else
+                                       ": fq_decode_step", B, ntok, splits),
             "layers": w.layers, "batch": B, "context_tokens": ntok, "num_splits": splits,
             "cache_bytes_per_layer": dec_bytes, "bytes_per_token_head": bpt,
         },
         "roofline": {
             "kernel": ("fq_decode_attention (one launch: packed_decode_kernel, query preparation and output "
-                       "rotation in-kernel)" if splits == 1 else
-                       "fq_decode_attention (prepare_queries + packed split attention + merge_unrotate)"),
+                       "rotation in-kernel)" if args.separate and splits == 1 else
+                       "fq_decode_attention (prepare_queries + packed split attention + merge_unrotate)"
+                       if args.separate else
+                       "fq_step_attend (one launch: packed_decode_kernel, queries prepared by fq_step_prepare, "
+                       "output rotation in-kernel)" if splits == 1 else
+                       "fq_step_attend (packed split attention + merge_unrotate)"),
             "bound": "hbm",
             "achieved": achieved,
             "peak": HBM_PEAK_GBS,
@@ -480,9 +511,16 @@ def main():
             "traffic": measured_traffic(),
             "algorithmic_bytes_per_launch": dec_bytes,
             "avg_launch_ms": dec_ms,
-            "timing": "HIP events around graph replays of the %d layers' decode calls" % w.layers
-                      if graph is not None else "HIP events around eager decode calls",
+            "timing": "HIP events around graph replays of the %d layers' attention calls" % w.layers
+                      if graph is not None else "HIP events around eager attention calls",
             "avg_launch_ms_eager": dec_ms_eager,
+        },
+        "step_parts": {
+            "prepare_ms": prep_ms,
+            "prepare": ("fq_compress of the newest 32 x 8 K and V" if args.separate else
+                        "fq_step_prepare: newest 32 x 8 K and V compressed + queries prepared (one launch)"),
+            "attend_ms": dec_ms,
+            "timing": "HIP events around graph replays of the %d layers' calls of each part" % w.layers,
         },
         "compress": {
             "mvec_per_s": comp_vec / (comp_med_ms * 1e-3) / 1e6,

@@ -225,6 +225,69 @@ fq_status fq_decode_attention(void* stream, const fq_quantizer* quant, const fq_
                               const int32_t* seq_lens, int max_seq_len, int num_splits,
                               float scale, void* workspace, size_t workspace_bytes, float* out);
 
+/*
+ * fq_decode_step -- one decode step of one layer: the newest K / V token of every
+ * sequence is compressed into its slot, then the attention of fq_decode_attention
+ * reads the cache ("FlashQuant" page, "架构设计": compress and paged decode
+ * kernels; "TurboQuant" steps 1-4 and "QJL" for the new token). The result is
+ * that of fq_compress(k_new, v_new, num_tokens = batch, slot_mapping) followed
+ * by fq_decode_attention on the same stream, except that the new token's y and p
+ * are computed by fp32 FMAs against the fp32 Pi and S (fq_compress uses split
+ * matrix-core products), so a coordinate within rounding of a boundary (or a p
+ * within rounding of 0) may be decided differently; debug_y / debug_p expose
+ * the values the codes were decided from.
+ *
+ * Two launches: query preparation together with the compression of the new
+ * tokens, then the attention (plus a merge launch when num_splits > 1).
+ *
+ *  k_new, v_new  device, element (b, h, j) of sequence b's newest token at
+ *                b * token_stride + h * head_stride + j, dtype kv_dtype (FQ_F32 or
+ *                FQ_BF16); both required, each vector on a 16-byte boundary.
+ *  slot_mapping  device int64 [batch]: the slot of sequence b's newest token
+ *                (normally block_tables[b][(seq_lens[b]-1)/16] * 16 + (seq_lens[b]-1)
+ *                % 16, so that the attention covers it); negative = not stored.
+ *  debug_y       optional device fp32 [2][batch][Hkv][d], as in fq_compress.
+ *  debug_p       optional device fp32 [batch][Hkv][qjl_dim], as in fq_compress.
+ *  All other arguments, the workspace size and the output as fq_decode_attention.
+ * Errors: as fq_decode_attention, plus FQ_ERR_INVALID_ARG for the append inputs.
+ */
+fq_status fq_decode_step(void* stream, const fq_quantizer* quant, const fq_cache* cache,
+                         const void* k_new, const void* v_new, int kv_dtype, int64_t token_stride,
+                         int64_t head_stride, const int64_t* slot_mapping, const void* q,
+                         int q_dtype, int batch, int num_q_heads, const int32_t* block_tables,
+                         int max_blocks_per_seq, const int32_t* seq_lens, int max_seq_len,
+                         int num_splits, float scale, void* workspace, size_t workspace_bytes,
+                         float* out, float* debug_y, float* debug_p);
+
+/*
+ * fq_step_prepare / fq_step_attend -- the two halves of fq_decode_step, for callers
+ * that enqueue them separately (to overlap other work between them, or to time
+ * the attention on its own). fq_step_prepare compresses the newest tokens into
+ * the cache and writes the prepared queries (q~, q_s and their matrix-core
+ * operands, with the score scale folded in) into the workspace; fq_step_attend
+ * then runs the attention from that workspace. Calling fq_step_prepare and then
+ * fq_step_attend on one stream, with the same quant, cache, batch, num_q_heads,
+ * max_seq_len, num_splits, scale and workspace, is fq_decode_step. The workspace
+ * holds the prepared queries in between: nothing else may write it, and
+ * fq_step_attend may be repeated (same output) while it is unchanged.
+ *
+ *  fq_step_prepare  arguments as fq_decode_step (no block tables, lengths or
+ *                   output; max_seq_len and num_splits only fix the split count
+ *                   and the workspace size).
+ *  fq_step_attend   arguments as fq_decode_attention without q.
+ * Errors: as fq_decode_step.
+ */
+fq_status fq_step_prepare(void* stream, const fq_quantizer* quant, const fq_cache* cache,
+                          const void* k_new, const void* v_new, int kv_dtype, int64_t token_stride,
+                          int64_t head_stride, const int64_t* slot_mapping, const void* q,
+                          int q_dtype, int batch, int num_q_heads, int max_seq_len, int num_splits,
+                          float scale, void* workspace, size_t workspace_bytes, float* debug_y,
+                          float* debug_p);
+fq_status fq_step_attend(void* stream, const fq_quantizer* quant, const fq_cache* cache, int batch,
+                         int num_q_heads, const int32_t* block_tables, int max_blocks_per_seq,
+                         const int32_t* seq_lens, int max_seq_len, int num_splits, float scale,
+                         void* workspace, size_t workspace_bytes, float* out);
+
 #ifdef __cplusplus
 }
 #endif

@@ -147,27 +147,36 @@ fq_status fq_decode_workspace_size(int batch, int num_q_heads, int num_kv_heads,
   return FQ_OK;
 }
 
-fq_status fq_decode_attention(void* stream, const fq_quantizer* quant, const fq_cache* cache,
-                              const void* q, int q_dtype, int batch, int num_q_heads,
-                              const int32_t* block_tables, int max_blocks_per_seq,
-                              const int32_t* seq_lens, int max_seq_len, int num_splits,
-                              float scale, void* workspace, size_t workspace_bytes, float* out) {
+}  // extern "C"
+
+namespace {
+
+fq_status decode_checked(void* stream, const fq_quantizer* quant, const fq_cache* cache,
+                         const void* q, int q_dtype, int batch, int num_q_heads,
+                         const int32_t* block_tables, int max_blocks_per_seq,
+                         const int32_t* seq_lens, int max_seq_len, int num_splits, float scale,
+                         void* workspace, size_t workspace_bytes, float* out,
+                         const fq::AppendIn* app, int phase) {
   fq_status st = check_quantizer(quant);
   if (st != FQ_OK) return st;
   st = check_cache(cache, quant);
   if (st != FQ_OK) return st;
-  if (q_dtype != FQ_F32 && q_dtype != FQ_BF16) return FQ_ERR_INVALID_ARG;
+  const bool queries = phase != fq::DECODE_ATTEND;  // reads q
+  const bool attends = phase != fq::DECODE_PREPARE;  // reads the cache pages, writes out
+  if (queries && q_dtype != FQ_F32 && q_dtype != FQ_BF16) return FQ_ERR_INVALID_ARG;
   if (batch < 0 || num_q_heads <= 0 || max_blocks_per_seq < 0 || max_seq_len < 0 ||
       num_splits < 0)
     return FQ_ERR_INVALID_ARG;
   if (num_q_heads % cache->num_kv_heads != 0) return FQ_ERR_INVALID_ARG;
   if (num_q_heads / cache->num_kv_heads > FQ_MAX_GROUP) return FQ_ERR_UNSUPPORTED;
   if (num_splits > FQ_MAX_SPLITS) return FQ_ERR_UNSUPPORTED;
-  if (static_cast<int64_t>(max_seq_len) > static_cast<int64_t>(max_blocks_per_seq) * FQ_BLOCK)
+  if (attends &&
+      static_cast<int64_t>(max_seq_len) > static_cast<int64_t>(max_blocks_per_seq) * FQ_BLOCK)
     return FQ_ERR_INVALID_ARG;
   if (batch == 0) return FQ_OK;
-  if (!q || !block_tables || !seq_lens || !out) return FQ_ERR_INVALID_ARG;
-  if (!aligned(q, 16) || !aligned(block_tables, 4) || !aligned(seq_lens, 4) || !aligned(out, 16))
+  if (queries && (!q || !aligned(q, 16))) return FQ_ERR_INVALID_ARG;
+  if (attends && (!block_tables || !seq_lens || !out)) return FQ_ERR_INVALID_ARG;
+  if (attends && (!aligned(block_tables, 4) || !aligned(seq_lens, 4) || !aligned(out, 16)))
     return FQ_ERR_INVALID_ARG;
   const int s = num_splits == 0 ? fq::auto_splits(batch, cache->num_kv_heads, max_seq_len)
                                 : num_splits;
@@ -175,9 +184,76 @@ fq_status fq_decode_attention(void* stream, const fq_quantizer* quant, const fq_
       fq::decode_workspace(batch, num_q_heads, cache->num_kv_heads, FQ_HEAD_DIM, quant->qjl_dim, s)
           .total;
   if (!workspace || workspace_bytes < need || !aligned(workspace, 256)) return FQ_ERR_WORKSPACE;
+  if (app) {
+    if (app->dtype != FQ_F32 && app->dtype != FQ_BF16) return FQ_ERR_INVALID_ARG;
+    if (!app->k || !app->v || !app->slot_mapping || !aligned(app->slot_mapping, 8))
+      return FQ_ERR_INVALID_ARG;
+    if (app->token_stride < 0 || app->head_stride < 0) return FQ_ERR_INVALID_ARG;
+    const uintptr_t ea = app->dtype == FQ_F32 ? 4 : 2;
+    if (!aligned(app->k, 16) || !aligned(app->v, 16)) return FQ_ERR_INVALID_ARG;
+    if ((app->token_stride * ea) % 16 != 0 || (app->head_stride * ea) % 16 != 0)
+      return FQ_ERR_INVALID_ARG;
+    if (batch > 1 && app->token_stride == 0) return FQ_ERR_INVALID_ARG;
+    if (cache->num_kv_heads > 1 && app->head_stride == 0) return FQ_ERR_INVALID_ARG;
+    if (app->debug_y && !aligned(app->debug_y, 16)) return FQ_ERR_INVALID_ARG;
+    if (app->debug_p && !aligned(app->debug_p, 16)) return FQ_ERR_INVALID_ARG;
+  }
   int e = fq::launch_decode(stream, *quant, *cache, q, q_dtype, batch, num_q_heads, block_tables,
-                            max_blocks_per_seq, seq_lens, max_seq_len, s, scale, workspace, out);
+                            max_blocks_per_seq, seq_lens, max_seq_len, s, scale, workspace, out,
+                            app, phase);
   return e == 0 ? FQ_OK : FQ_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+fq_status fq_decode_attention(void* stream, const fq_quantizer* quant, const fq_cache* cache,
+                              const void* q, int q_dtype, int batch, int num_q_heads,
+                              const int32_t* block_tables, int max_blocks_per_seq,
+                              const int32_t* seq_lens, int max_seq_len, int num_splits,
+                              float scale, void* workspace, size_t workspace_bytes, float* out) {
+  return decode_checked(stream, quant, cache, q, q_dtype, batch, num_q_heads, block_tables,
+                        max_blocks_per_seq, seq_lens, max_seq_len, num_splits, scale, workspace,
+                        workspace_bytes, out, nullptr, fq::DECODE_ALL);
+}
+
+fq_status fq_decode_step(void* stream, const fq_quantizer* quant, const fq_cache* cache,
+                         const void* k_new, const void* v_new, int kv_dtype, int64_t token_stride,
+                         int64_t head_stride, const int64_t* slot_mapping, const void* q,
+                         int q_dtype, int batch, int num_q_heads, const int32_t* block_tables,
+                         int max_blocks_per_seq, const int32_t* seq_lens, int max_seq_len,
+                         int num_splits, float scale, void* workspace, size_t workspace_bytes,
+                         float* out, float* debug_y, float* debug_p) {
+  const fq::AppendIn app{k_new, v_new, kv_dtype, token_stride, head_stride, slot_mapping,
+                         debug_y, debug_p};
+  return decode_checked(stream, quant, cache, q, q_dtype, batch, num_q_heads, block_tables,
+                        max_blocks_per_seq, seq_lens, max_seq_len, num_splits, scale, workspace,
+                        workspace_bytes, out, &app, fq::DECODE_ALL);
+}
+
+fq_status fq_step_prepare(void* stream, const fq_quantizer* quant, const fq_cache* cache,
+                          const void* k_new, const void* v_new, int kv_dtype, int64_t token_stride,
+                          int64_t head_stride, const int64_t* slot_mapping, const void* q,
+                          int q_dtype, int batch, int num_q_heads, int max_seq_len, int num_splits,
+                          float scale, void* workspace, size_t workspace_bytes, float* debug_y,
+                          float* debug_p) {
+  const fq::AppendIn app{k_new, v_new, kv_dtype, token_stride, head_stride, slot_mapping,
+                         debug_y, debug_p};
+  // the page loop's bound on max_seq_len does not apply: pass a table wide enough
+  const int mb = (max_seq_len + FQ_BLOCK - 1) / FQ_BLOCK;
+  return decode_checked(stream, quant, cache, q, q_dtype, batch, num_q_heads, nullptr, mb,
+                        nullptr, max_seq_len, num_splits, scale, workspace, workspace_bytes,
+                        nullptr, &app, fq::DECODE_PREPARE);
+}
+
+fq_status fq_step_attend(void* stream, const fq_quantizer* quant, const fq_cache* cache, int batch,
+                         int num_q_heads, const int32_t* block_tables, int max_blocks_per_seq,
+                         const int32_t* seq_lens, int max_seq_len, int num_splits, float scale,
+                         void* workspace, size_t workspace_bytes, float* out) {
+  return decode_checked(stream, quant, cache, nullptr, FQ_F32, batch, num_q_heads, block_tables,
+                        max_blocks_per_seq, seq_lens, max_seq_len, num_splits, scale, workspace,
+                        workspace_bytes, out, nullptr, fq::DECODE_ATTEND);
 }
 
 }  // extern "C"

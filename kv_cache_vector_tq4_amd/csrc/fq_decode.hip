@@ -55,6 +55,16 @@ struct DecodeArgs {
   float* part_ml;  // [B][Hq][S][2]
   uint4* qops;     // [B][Hkv][FQ_QOPS][64]
   float* out;      // [B][Hq][d]
+  // the newest token of every sequence, compressed into its slot before the
+  // decode reads the cache (append_group); unused otherwise
+  const void* knew;       // K / V element (b, h, j) at b * kv_tstride + h * kv_hstride + j
+  const void* vnew;
+  const int64_t* slots;   // [B] slot of sequence b's newest token, < 0 = not stored
+  const float* bnd;       // codebook boundaries
+  float* dbg_y;           // optional [2][B][Hkv][d]
+  float* dbg_p;           // optional [B][Hkv][m]
+  int64_t kv_tstride, kv_hstride;
+  int kv_bf16, bits;
   int batch, hq, hkv, group, splits, chunk, max_blocks, qjl_on, q_bf16;
   float scale;
 };
@@ -153,6 +163,16 @@ __device__ __forceinline__ float wave_max_dpp(float x) {
   const float a2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(r), 32));
   const float a3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(r), 48));
   return fmaxf(fmaxf(a0, a1), fmaxf(a2, a3));
+}
+
+// Sum over the 64 lanes, in a fixed order (rows by DPP, then the four row sums).
+__device__ __forceinline__ float wave_sum_dpp(float x) {
+  const float r = row_sum(x);
+  const float a0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(r), 0));
+  const float a1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(r), 16));
+  const float a2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(r), 32));
+  const float a3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(r), 48));
+  return (a0 + a1) + (a2 + a3);
 }
 
 // One power of two per head puts max |q~| in [128, 256); q_s takes that power
@@ -444,14 +464,117 @@ __device__ __forceinline__ void prepare_group(const DecodeArgs& a, int kvh, int 
   }
 }
 
+// LDS floats used by append_group.
+constexpr int APPEND_LDS_FLOATS = 11 * D + 8;
+static_assert(APPEND_LDS_FLOATS <= prep_lds_floats<FQ_MAX_GROUP>(), "append fits the preparation LDS");
+
+// The newest token of sequence b, KV head kvh, compressed into its slot as
+// fq_compress does it ("FlashQuant" page, "TurboQuant" steps 1-4 and "QJL"), by
+// PQ_THREADS threads (thread = (coordinate j, k-quarter kq)), in fp32 against the
+// fp32 Pi and S:
+//   n = ||x||, y = (Pi x) / n (0 when n = 0), idx_j = #{i : boundary_i < y_j},
+//   codes and n stored; keys also r = y - level[idx], gamma = n ||r||, p = S r,
+//   bit j = [p_j >= 0].
+// Nothing is stored when the slot is negative.
+template <int BITS, int KDT>
+__device__ __forceinline__ void append_group(const DecodeArgs& a, int kvh, int b, int tid, float* lds) {
+  constexpr int L = 1 << BITS;
+  constexpr int PER = 32 / BITS;      // codes per 32-bit word
+  constexpr int CB = D * BITS / 8;    // code bytes per vector
+  float* const s_x = lds;             // [2][D] raw K, V
+  float* const s_part = s_x + 2 * D;  // [4][2][D] quarter sums
+  float* const s_r = s_part + 8 * D;  // [D] key residual
+  float* const s_sum = s_r + D;       // [6]: ||k||^2, ||v||^2, ||r||^2, per half
+  const int j = tid & (D - 1);
+  const int kq = __builtin_amdgcn_readfirstlane(tid >> 7);
+  const int lane = tid & 63;
+  const bool qjl = a.qjl_on != 0;
+  // loads first: coordinate j of K (kq 0) or V (kq 1), then columns of Pi^T, S^T
+  float x = 0.f;
+  if (kq < 2) {
+    const int64_t off = static_cast<int64_t>(b) * a.kv_tstride + static_cast<int64_t>(kvh) * a.kv_hstride + j;
+    const void* src = kq == 0 ? a.knew : a.vnew;
+    if constexpr (KDT == FQ_BF16)
+      x = __uint_as_float(static_cast<uint32_t>(static_cast<const uint16_t*>(src)[off]) << 16);
+    else
+      x = static_cast<const float*>(src)[off];
+  }
+  float pc[32], sc[32];
+  col_quarter_load(a.pit, j, kq, pc);
+  col_quarter_load(qjl ? a.sit : a.pit, j, kq, sc);
+  const int64_t slot = a.slots[b];
+  const int64_t rec = ((slot >> 4) * a.hkv + kvh) * FQ_BLOCK + (slot & 15);
+  if (kq < 2) {
+    s_x[kq * D + j] = x;
+    const float ss = wave_sum_dpp(x * x);
+    if (lane == 0) s_sum[2 * kq + (j >> 6)] = ss;
+  }
+  __syncthreads();
+  quarter_dot_g<2, 2>(pc, s_x, j, kq, 2, s_part);
+  __syncthreads();
+  const float nk = sqrtf(s_sum[0] + s_sum[1]);
+  if (kq < 2) {
+    const int h = kq;  // 0: K, 1: V
+    const float n = h == 0 ? nk : sqrtf(s_sum[2] + s_sum[3]);
+    const float inv = n > 0.f ? 1.0f / n : 0.f;
+    const float y = ((s_part[(0 * 2 + h) * D + j] + s_part[(1 * 2 + h) * D + j]) +
+                     (s_part[(2 * 2 + h) * D + j] + s_part[(3 * 2 + h) * D + j])) * inv;
+    const cptr bq = uniform_ptr(a.bnd);
+    uint32_t idx = 0;
+#pragma unroll
+    for (int i = 0; i < L - 1; ++i) idx += bq[i] < y ? 1u : 0u;
+    // word j / PER of the packed codes gathered in its first lane
+    uint32_t w = idx << (BITS * (j % PER));
+#pragma unroll
+    for (int m = 1; m < PER; m <<= 1) w |= static_cast<uint32_t>(__shfl_xor(static_cast<int>(w), m));
+    if (slot >= 0) {
+      if (a.dbg_y) a.dbg_y[((static_cast<int64_t>(h) * a.batch + b) * a.hkv + kvh) * D + j] = y;
+      uint8_t* const codes = const_cast<uint8_t*>(h == 0 ? a.k_codes : a.v_codes);
+      if (j % PER == 0) *reinterpret_cast<uint32_t*>(codes + rec * CB + 4 * (j / PER)) = w;
+      if (j == 0) const_cast<float*>(h == 0 ? a.k_norm : a.v_norm)[rec] = n;
+    }
+    if (h == 0 && qjl) {
+      const float r = y - a.levels[idx];
+      s_r[j] = r;
+      const float rr = wave_sum_dpp(r * r);
+      if (lane == 0) s_sum[4 + (j >> 6)] = rr;
+    }
+  }
+  if (!qjl) return;  // uniform over the work-group
+  __syncthreads();
+  quarter_dot_g<1, 1>(sc, s_r, j, kq, 1, s_part);
+  __syncthreads();
+  if (kq == 0) {
+    const float p = (s_part[0 * D + j] + s_part[1 * D + j]) + (s_part[2 * D + j] + s_part[3 * D + j]);
+    // bit i of sign byte t = [p_{8t+i} >= 0]: the wave's ballot, lane order
+    const uint64_t sg = __ballot(p >= 0.f);
+    if (slot >= 0) {
+      if (a.dbg_p) a.dbg_p[(static_cast<int64_t>(b) * a.hkv + kvh) * D + j] = p;
+      if (lane == 0) *reinterpret_cast<uint64_t*>(const_cast<uint8_t*>(a.k_qjl) + rec * (D / 8) + 8 * (j >> 6)) = sg;
+      if (j == 0) const_cast<float*>(a.k_gamma)[rec] = nk * sqrtf(s_sum[4] + s_sum[5]);
+    }
+  }
+}
+
 // One work-group per (KV head, sequence, part of the group): the group's heads
-// are shared out over gridDim.z work-groups (all in one, or one each when there
-// are few (KV head, sequence) pairs to spread the work over).
-template <int DT, int SLOTS>
+// are shared out over the first gridDim.z - APPEND work-groups (all in one, or one
+// each when there are few (KV head, sequence) pairs to spread the work over);
+// with APPEND the last one compresses the newest K / V token of the pair.
+template <int DT, int SLOTS, int APPEND>
 __global__ void __launch_bounds__(PQ_THREADS) prepare_queries_kernel(DecodeArgs a) {
   __shared__ __align__(16) float s_p[prep_lds_floats<FQ_MAX_GROUP>()];
   const int kvh = blockIdx.x, b = blockIdx.y;
-  const int hn = a.group / gridDim.z, hb = blockIdx.z * hn;
+  if (APPEND && static_cast<int>(blockIdx.z) == static_cast<int>(gridDim.z) - 1) {
+    if (a.bits == 4) {
+      if (a.kv_bf16) append_group<4, FQ_BF16>(a, kvh, b, threadIdx.x, s_p);
+      else append_group<4, FQ_F32>(a, kvh, b, threadIdx.x, s_p);
+    } else {
+      if (a.kv_bf16) append_group<2, FQ_BF16>(a, kvh, b, threadIdx.x, s_p);
+      else append_group<2, FQ_F32>(a, kvh, b, threadIdx.x, s_p);
+    }
+    return;
+  }
+  const int hn = a.group / (static_cast<int>(gridDim.z) - APPEND), hb = blockIdx.z * hn;
   PrepIn<FQ_MAX_GROUP> in;
   prep_issue<DT, FQ_MAX_GROUP>(a, kvh, b, hb, hn, threadIdx.x, in);
   prepare_group<SLOTS, FQ_MAX_GROUP>(a, kvh, b, hb, hn, threadIdx.x, s_p,
@@ -1050,24 +1173,46 @@ __device__ __forceinline__ void pk_load(const DecodeArgs& a, int64_t rec0, int n
   }
 }
 
-// PREP < 0: one split of many, query operands from prepare_queries_kernel,
-// partial results for merge_unrotate_kernel. PREP = the query dtype: the only
-// split of its (KV head, sequence); the work-group prepares its own query
-// operands (prepare_group, in the LDS the code table takes later) and writes
-// the un-rotated output itself.
+// (KV head, sequence) of a work-group of a one-split grid (1, Hkv, B). Work-groups
+// go to the 8 XCDs round-robin by linear id, each XCD with its own L2; this order
+// puts KV heads 2k and 2k+1 of a sequence on the same XCD, one right after the
+// other, so the 128-byte lines they share (the two heads' 64-byte runs of key
+// norms, gammas and value norms per page) come from HBM once and then from that
+// L2. Identity when Hkv is odd or Hkv * B is not a multiple of 16.
+__device__ __forceinline__ void xcd_pair_map(int hkv, int batch, int& kvh, int& b) {
+  const int n = hkv * batch;
+  if ((hkv & 1) != 0 || (n & 15) != 0) return;
+  const int lin = static_cast<int>(blockIdx.y) + hkv * static_cast<int>(blockIdx.z);
+  const int x = lin & 7, s = lin >> 3;      // XCD, position on it
+  const int pair = (s >> 1) * 8 + x;        // (sequence, head pair), round-robin over XCDs
+  const int hp = hkv >> 1;
+  b = pair / hp;
+  kvh = 2 * (pair - b * hp) + (s & 1);
+}
+
+// PREP = -1: one split of many, query operands from prepare_queries_kernel,
+// partial results for merge_unrotate_kernel. PREP = -2: the only split of its
+// (KV head, sequence), query operands from prepare_queries_kernel; the
+// work-group normalizes and un-rotates its output itself. PREP = the query
+// dtype (>= 0): as -2, and the work-group prepares its own query operands too
+// (prepare_group, in the LDS the code table takes later).
 template <int BITS, int SLOTS, int WAVES, int RING, int OCC, int PREP>
 __global__ void __launch_bounds__(WAVES * 64, OCC) packed_decode_kernel(DecodeArgs a) {
   static_assert(BITS == 4 || BITS == 2, "4- or 2-bit codes");
-  static_assert(PREP < 0 || WAVES * 64 >= PQ_THREADS, "in-kernel query preparation takes PQ_THREADS threads");
+  constexpr bool INPREP = PREP >= 0;  // query operands prepared in-kernel
+  constexpr bool ONLY = PREP != -1;   // the only split: output finished in-kernel
+  static_assert(!ONLY || WAVES * 64 >= PQ_THREADS, "in-kernel query work takes PQ_THREADS threads");
   static_assert(WAVES * 64 >= 256, "the table stage takes 256 threads");
   constexpr int CB = D * BITS / 8;  // code bytes per vector
-  constexpr bool BSIGN = PREP >= 0;  // byte-indexed sign table
+  constexpr bool BSIGN = ONLY;  // byte-indexed sign table (one work-group per CU)
   constexpr int PRO = RING - 1;  // pages requested ahead of the loop
   __shared__ __align__(16) uint8_t s_lds[BSIGN ? PK_LDS_BYTES_F : PK_LDS_BYTES];
   const uint8_t* const s_code = s_lds + PK_CODE_BASE;
   const uint8_t* const s_sign = s_lds + PK_SIGN_BASE;
   constexpr int HL = 4 / SLOTS;  // heads per lane in the score layout (1 or 2)
-  const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+  const int split = blockIdx.x;
+  int kvh = blockIdx.y, b = blockIdx.z;
+  if constexpr (ONLY) xcd_pair_map(a.hkv, a.batch, kvh, b);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, n = lane & 15;
@@ -1111,7 +1256,7 @@ __global__ void __launch_bounds__(WAVES * 64, OCC) packed_decode_kernel(DecodeAr
   // ---- the query loads (in-kernel preparation) and the wave's first RING - 1
   // pages are requested before any set-up work, in the order they are needed
   PrepIn<PK_PREP_GM> pin;
-  if constexpr (PREP >= 0) {
+  if constexpr (INPREP) {
     if (tid < PQ_THREADS) prep_issue<(PREP >= 0 ? PREP : 0), PK_PREP_GM>(a, kvh, b, 0, G, tid, pin);
   }
   // codebook levels of the table entry this thread stages (threads < 256)
@@ -1140,7 +1285,7 @@ __global__ void __launch_bounds__(WAVES * 64, OCC) packed_decode_kernel(DecodeAr
   float cf[HL];  // score factor of this lane's head(s) in the score layout
   {
     const uint4* ops;
-    if constexpr (PREP >= 0) {
+    if constexpr (INPREP) {
       uint4* const s_ops = reinterpret_cast<uint4*>(s_lds + PK_PREP_OPS);
       prepare_group<SLOTS, PK_PREP_GM>(a, kvh, b, 0, G, tid, reinterpret_cast<float*>(s_lds + PK_CODE_BASE), s_ops,
                                        false, pin);
@@ -1405,7 +1550,7 @@ __global__ void __launch_bounds__(WAVES * 64, OCC) packed_decode_kernel(DecodeAr
   const int jj = tid & (D - 1);
   const int kq = __builtin_amdgcn_readfirstlane(tid >> 7);
   float pc[32];
-  if constexpr (PREP >= 0) {
+  if constexpr (ONLY) {
     if (tid < PQ_THREADS) col_quarter_load(a.pi, jj, kq, pc);
   }
 
@@ -1451,7 +1596,7 @@ __global__ void __launch_bounds__(WAVES * 64, OCC) packed_decode_kernel(DecodeAr
       s_o[(wave * HP + HL * g + k) * D + dim] = (acc_o[t][2 * k] + acc_o[t][2 * k + 1]) * unscale;
   }
   __syncthreads();
-  if constexpr (PREP >= 0) {
+  if constexpr (ONLY) {
     // the only split: o_rot = O / L per head, then out = Pi^T o_rot
     float* const s_or = s_ml + WAVES * HP * 2;  // [G][D]
     float* const s_pp = s_or + PK_PREP_GM * D;  // [4][PK_PREP_GM][D]
@@ -1526,7 +1671,8 @@ __global__ void __launch_bounds__(PQ_THREADS) merge_unrotate_kernel(DecodeArgs a
 int launch_decode(void* stream, const fq_quantizer& q, const fq_cache& c, const void* qv,
                   int q_dtype, int batch, int num_q_heads, const int32_t* block_tables,
                   int max_blocks_per_seq, const int32_t* seq_lens, int max_seq_len,
-                  int num_splits, float scale, void* workspace, float* out) {
+                  int num_splits, float scale, void* workspace, float* out,
+                  const AppendIn* app, int phase) {
   const DecodeWorkspace ws =
       decode_workspace(batch, num_q_heads, c.num_kv_heads, D, q.qjl_dim, num_splits);
   uint8_t* wb = static_cast<uint8_t*>(workspace);
@@ -1563,6 +1709,18 @@ int launch_decode(void* stream, const fq_quantizer& q, const fq_cache& c, const 
   a.qjl_on = c.qjl_dim > 0 ? 1 : 0;
   a.q_bf16 = q_dtype == FQ_BF16 ? 1 : 0;
   a.scale = scale;
+  a.bits = q.bits;
+  a.bnd = q.boundaries;
+  if (app) {
+    a.knew = app->k;
+    a.vnew = app->v;
+    a.slots = app->slot_mapping;
+    a.dbg_y = app->debug_y;
+    a.dbg_p = app->debug_p;
+    a.kv_tstride = app->token_stride;
+    a.kv_hstride = app->head_stride;
+    a.kv_bf16 = app->dtype == FQ_BF16 ? 1 : 0;
+  }
   hipStream_t st = static_cast<hipStream_t>(stream);
 
   // Split kernel: packed matrix-core kernel for groups of up to 8 query heads; for
@@ -1573,7 +1731,8 @@ int launch_decode(void* stream, const fq_quantizer& q, const fq_cache& c, const 
   const bool v1 = impl && std::strcmp(impl, "mfma_v1") == 0;
   const int slots = (!valu && !v1) ? (a.group <= 4 ? 4 : a.group <= 8 ? 2 : 0) : 0;
   dim3 grid(num_splits, c.num_kv_heads, batch);
-  if (slots > 0 && num_splits == 1 && std::getenv("FQ_DECODE_UNFUSED") == nullptr) {
+  const bool only = slots > 0 && num_splits == 1 && std::getenv("FQ_DECODE_UNFUSED") == nullptr;
+  if (only && !app && phase == DECODE_ALL) {
     // one work-group per (KV head, sequence) does everything in one launch
 #define FQ_FUSED(BITS, SL, DT)                                                                                \
   hipLaunchKernelGGL((packed_decode_kernel<BITS, SL, pkf_waves(BITS), PKF_RING, PKF_OCC, DT>), grid,          \
@@ -1587,16 +1746,39 @@ int launch_decode(void* stream, const fq_quantizer& q, const fq_cache& c, const 
     return static_cast<int>(hipGetLastError());
   }
   // query preparation and merge: one work-group per query head when there are few
-  // (KV head, sequence) pairs, else one per pair
+  // (KV head, sequence) pairs, else one per pair; one more per pair appends its
+  // newest token
   const dim3 pgrid(c.num_kv_heads, batch, batch * c.num_kv_heads >= 128 ? 1 : a.group);
+  const dim3 agrid(pgrid.x, pgrid.y, pgrid.z + (app ? 1 : 0));
+  if (phase != DECODE_ATTEND) {
+#define FQ_PREP(DT, SL)                                                                                  \
+  do {                                                                                                   \
+    if (app) hipLaunchKernelGGL((prepare_queries_kernel<DT, SL, 1>), agrid, dim3(PQ_THREADS), 0, st, a); \
+    else hipLaunchKernelGGL((prepare_queries_kernel<DT, SL, 0>), pgrid, dim3(PQ_THREADS), 0, st, a);     \
+  } while (0)
   if (q_dtype == FQ_BF16) {
-    if (slots == 4) hipLaunchKernelGGL((prepare_queries_kernel<FQ_BF16, 4>), pgrid, dim3(PQ_THREADS), 0, st, a);
-    else if (slots == 2) hipLaunchKernelGGL((prepare_queries_kernel<FQ_BF16, 2>), pgrid, dim3(PQ_THREADS), 0, st, a);
-    else hipLaunchKernelGGL((prepare_queries_kernel<FQ_BF16, 0>), pgrid, dim3(PQ_THREADS), 0, st, a);
+    if (slots == 4) FQ_PREP(FQ_BF16, 4);
+    else if (slots == 2) FQ_PREP(FQ_BF16, 2);
+    else FQ_PREP(FQ_BF16, 0);
   } else {
-    if (slots == 4) hipLaunchKernelGGL((prepare_queries_kernel<FQ_F32, 4>), pgrid, dim3(PQ_THREADS), 0, st, a);
-    else if (slots == 2) hipLaunchKernelGGL((prepare_queries_kernel<FQ_F32, 2>), pgrid, dim3(PQ_THREADS), 0, st, a);
-    else hipLaunchKernelGGL((prepare_queries_kernel<FQ_F32, 0>), pgrid, dim3(PQ_THREADS), 0, st, a);
+    if (slots == 4) FQ_PREP(FQ_F32, 4);
+    else if (slots == 2) FQ_PREP(FQ_F32, 2);
+    else FQ_PREP(FQ_F32, 0);
+  }
+#undef FQ_PREP
+  }
+  if (phase == DECODE_PREPARE) return static_cast<int>(hipGetLastError());
+  if (only) {
+    // the only split, query operands from the preparation launch
+#define FQ_ONLY(BITS, SL)                                                                                       \
+  hipLaunchKernelGGL((packed_decode_kernel<BITS, SL, pkf_waves(BITS), PKF_RING, PKF_OCC, -2>), grid,            \
+                     dim3(pkf_waves(BITS) * 64), 0, st, a)
+    if (q.bits == 4 && slots == 4) FQ_ONLY(4, 4);
+    else if (q.bits == 4) FQ_ONLY(4, 2);
+    else if (slots == 4) FQ_ONLY(2, 4);
+    else FQ_ONLY(2, 2);
+#undef FQ_ONLY
+    return static_cast<int>(hipGetLastError());
   }
   if (slots == 4 && q.bits == 4)
     hipLaunchKernelGGL((packed_decode_kernel<4, 4, PK4_WAVES, PK4_RING, PK4_OCC, -1>), grid, dim3(PK4_WAVES * 64), 0, st, a);

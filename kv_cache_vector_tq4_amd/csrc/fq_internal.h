@@ -10,7 +10,7 @@
 #define FQ_BLOCK 16
 #define FQ_MAX_GROUP 16
 #define FQ_MAX_SPLITS 64
-#define FQ_VERSION 101
+#define FQ_VERSION 102
 
 namespace fq {
 
@@ -38,9 +38,28 @@ int launch_compress(void* stream, const fq_quantizer& q, const fq_cache& c, cons
                     int64_t head_stride, const int64_t* slot_mapping, float* debug_y,
                     float* debug_p);
 
+// The newest K / V token of every sequence, compressed into the cache by the
+// decode step before the attention reads it.
+struct AppendIn {
+  const void* k;
+  const void* v;
+  int dtype;
+  int64_t token_stride, head_stride;
+  const int64_t* slot_mapping;  // [batch]
+  float* debug_y;
+  float* debug_p;
+};
+
+// Which launches of a decode call to enqueue: all of them, only the query
+// preparation (with the append, if any) into the workspace, or only the attention
+// from a workspace prepared earlier on the same stream.
+enum DecodePhase { DECODE_ALL = 0, DECODE_PREPARE = 1, DECODE_ATTEND = 2 };
+
+// app == nullptr: decode only; else append the newest tokens first (same stream).
 int launch_decode(void* stream, const fq_quantizer& q, const fq_cache& c, const void* qv,
                   int q_dtype, int batch, int num_q_heads, const int32_t* block_tables,
                   int max_blocks_per_seq, const int32_t* seq_lens, int max_seq_len,
-                  int num_splits, float scale, void* workspace, float* out);
+                  int num_splits, float scale, void* workspace, float* out,
+                  const AppendIn* app, int phase);
 
 }  // namespace fq

@@ -82,6 +82,21 @@ EXPORTS = {
                                            ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_int,
                                            ctypes.c_int, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t,
                                            ctypes.c_void_p]),
+    "fq_decode_step": (ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(QuantizerT), ctypes.POINTER(CacheT),
+                                      ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int64,
+                                      ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
+                                      ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p,
+                                      ctypes.c_int, ctypes.c_int, ctypes.c_float, ctypes.c_void_p,
+                                      ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
+    "fq_step_prepare": (ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(QuantizerT), ctypes.POINTER(CacheT),
+                                       ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int64,
+                                       ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
+                                       ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_float,
+                                       ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p]),
+    "fq_step_attend": (ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(QuantizerT), ctypes.POINTER(CacheT),
+                                      ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p,
+                                      ctypes.c_int, ctypes.c_int, ctypes.c_float, ctypes.c_void_p,
+                                      ctypes.c_size_t, ctypes.c_void_p]),
 }
 
 
@@ -285,4 +300,84 @@ def decode(quant, cache, q, block_tables, seq_lens, max_seq_len, num_splits=0, s
                                    _ptr(seq_lens), int(max_seq_len), int(num_splits), float(scale),
                                    _ptr(workspace), workspace.numel() * workspace.element_size(), _ptr(out))
     _check(st, "fq_decode_attention")
+    return out
+
+
+def decode_step(quant, cache, k_new, v_new, slot_mapping, q, block_tables, seq_lens, max_seq_len, num_splits=0,
+                scale=None, workspace=None, out=None, debug=False, stream=None):
+    """fq_decode_step: compress k_new / v_new [B, Hkv, d] into slot_mapping [B], then decode q [B, Hq, d].
+
+    Returns out fp32 [B, Hq, d], or (out, debug_y [2, B, Hkv, d], debug_p [B, Hkv, m]) when debug.
+    """
+    import torch
+
+    B, Hq, d = q.shape
+    assert q.is_contiguous() and block_tables.dtype == torch.int32 and seq_lens.dtype == torch.int32
+    assert block_tables.is_contiguous() and seq_lens.is_contiguous()
+    for x in (k_new, v_new):
+        assert x.shape == (B, cache.num_kv_heads, d) and x.stride(2) == 1
+        assert x.dtype == k_new.dtype and x.stride() == k_new.stride()
+    assert slot_mapping.dtype == torch.int64 and slot_mapping.numel() == B and slot_mapping.is_contiguous()
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    need = workspace_bytes(B, Hq, cache.num_kv_heads, d, quant.qjl_dim, max_seq_len, num_splits)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    if out is None:
+        out = torch.empty((B, Hq, d), dtype=torch.float32, device=q.device)
+    dy = dp = None
+    if debug:
+        dy = torch.zeros((2, B, cache.num_kv_heads, d), dtype=torch.float32, device=q.device)
+        dp = torch.zeros((B, cache.num_kv_heads, max(quant.qjl_dim, 1)), dtype=torch.float32, device=q.device)
+    st = lib().fq_decode_step(_stream(stream), ctypes.byref(quant.struct), ctypes.byref(cache.struct),
+                              _ptr(k_new), _ptr(v_new), _dtype_code(k_new), k_new.stride(0), k_new.stride(1),
+                              _ptr(slot_mapping), _ptr(q), _dtype_code(q), B, Hq, _ptr(block_tables),
+                              block_tables.shape[1], _ptr(seq_lens), int(max_seq_len), int(num_splits),
+                              float(scale), _ptr(workspace), workspace.numel() * workspace.element_size(),
+                              _ptr(out), _ptr(dy), _ptr(dp))
+    _check(st, "fq_decode_step")
+    return (out, dy, dp) if debug else out
+
+
+def step_prepare(quant, cache, k_new, v_new, slot_mapping, q, max_seq_len, workspace, num_splits=0, scale=None,
+                 debug=False, stream=None):
+    """fq_step_prepare: append k_new / v_new [B, Hkv, d] at slot_mapping [B] and prepare q [B, Hq, d] into
+    workspace. Returns (debug_y, debug_p) when debug, else None."""
+    import torch
+
+    B, Hq, d = q.shape
+    assert q.is_contiguous()
+    for x in (k_new, v_new):
+        assert x.shape == (B, cache.num_kv_heads, d) and x.stride(2) == 1
+        assert x.dtype == k_new.dtype and x.stride() == k_new.stride()
+    assert slot_mapping.dtype == torch.int64 and slot_mapping.numel() == B and slot_mapping.is_contiguous()
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    dy = dp = None
+    if debug:
+        dy = torch.zeros((2, B, cache.num_kv_heads, d), dtype=torch.float32, device=q.device)
+        dp = torch.zeros((B, cache.num_kv_heads, max(quant.qjl_dim, 1)), dtype=torch.float32, device=q.device)
+    st = lib().fq_step_prepare(_stream(stream), ctypes.byref(quant.struct), ctypes.byref(cache.struct),
+                               _ptr(k_new), _ptr(v_new), _dtype_code(k_new), k_new.stride(0), k_new.stride(1),
+                               _ptr(slot_mapping), _ptr(q), _dtype_code(q), B, Hq, int(max_seq_len),
+                               int(num_splits), float(scale), _ptr(workspace),
+                               workspace.numel() * workspace.element_size(), _ptr(dy), _ptr(dp))
+    _check(st, "fq_step_prepare")
+    return (dy, dp) if debug else None
+
+
+def step_attend(quant, cache, batch, num_q_heads, block_tables, seq_lens, max_seq_len, workspace, num_splits=0,
+                scale=None, out=None, stream=None):
+    """fq_step_attend: the attention from a workspace prepared by step_prepare -> out fp32 [B, Hq, d]."""
+    import torch
+
+    d = cache.head_dim
+    assert block_tables.dtype == torch.int32 and seq_lens.dtype == torch.int32
+    assert block_tables.is_contiguous() and seq_lens.is_contiguous()
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    if out is None:
+        out = torch.empty((batch, num_q_heads, d), dtype=torch.float32, device=block_tables.device)
+    st = lib().fq_step_attend(_stream(stream), ctypes.byref(quant.struct), ctypes.byref(cache.struct), batch,
+                              num_q_heads, _ptr(block_tables), block_tables.shape[1], _ptr(seq_lens),
+                              int(max_seq_len), int(num_splits), float(scale), _ptr(workspace),
+                              workspace.numel() * workspace.element_size(), _ptr(out))
+    _check(st, "fq_step_attend")
     return out
