@@ -577,8 +577,10 @@ __global__ void __launch_bounds__(PQ_THREADS) prepare_queries_kernel(DecodeArgs 
   const int hn = a.group / (static_cast<int>(gridDim.z) - APPEND), hb = blockIdx.z * hn;
   PrepIn<FQ_MAX_GROUP> in;
   prep_issue<DT, FQ_MAX_GROUP>(a, kvh, b, hb, hn, threadIdx.x, in);
+  // q~ and q_s as fp32 rows only for the kernels that read them (groups of 16)
   prepare_group<SLOTS, FQ_MAX_GROUP>(a, kvh, b, hb, hn, threadIdx.x, s_p,
-                                     a.qops + (static_cast<int64_t>(b) * a.hkv + kvh) * (FQ_QOPS * 64), true, in);
+                                     a.qops + (static_cast<int64_t>(b) * a.hkv + kvh) * (FQ_QOPS * 64), SLOTS == 0,
+                                     in);
 }
 
 // ---------------------------------------------------------------- kernel 2
@@ -1270,32 +1272,25 @@ __global__ void __launch_bounds__(WAVES * 64, OCC) packed_decode_kernel(DecodeAr
       for (int k = 0; k < 4; ++k) lv[k] = a.levels[(tid >> (2 * k)) & 3];
     }
   }
-  PkPage<BITS> ring[RING];
-  if (my_pages > 0) {
-#pragma unroll
-    for (int k = 0; k < PRO; ++k)
-      pk_load(a, rec_of(bt_cur, min(k, min(64, my_pages) - 1)), n, lo, gptr, sgn_base, ring[k]);
-  }
-
-  // ---- query operands, prepared per lane by the query kernel. With two heads per
-  // lane (SLOTS 2) registers are short, so the code-product operands (the same for
-  // every wave) are read from LDS at each step.
+  // ---- query operands. With two heads per lane (SLOTS 2) registers are short, so
+  // the code-product operands (the same for every wave) are read from LDS at each
+  // step. Prepared by the query launch, they are requested before the pages (loads
+  // complete in issue order, so waiting for them then waits for nothing else);
+  // prepared in-kernel, they are read from LDS below.
   h8 qs[4];   // SLOTS 2: sign-product A operands
   h8 qmr[8];  // SLOTS 4: code-product A operands, held in registers (SLOTS 2 reads them from LDS)
   float cf[HL];  // score factor of this lane's head(s) in the score layout
-  {
-    const uint4* ops;
-    if constexpr (INPREP) {
-      uint4* const s_ops = reinterpret_cast<uint4*>(s_lds + PK_PREP_OPS);
-      prepare_group<SLOTS, PK_PREP_GM>(a, kvh, b, 0, G, tid, reinterpret_cast<float*>(s_lds + PK_CODE_BASE), s_ops,
-                                       false, pin);
-      __syncthreads();
-      ops = s_ops;
-    } else {
-      ops = a.qops + (static_cast<int64_t>(b) * a.hkv + kvh) * (FQ_QOPS * 64);
+  constexpr int NT = WAVES * 64;
+  constexpr int QC = (8 * 64 + NT - 1) / NT;  // code-product operands copied to LDS per thread
+  uint4 qcp[QC];
+  auto operands = [&](const uint4* ops, bool copy_now) {
+#pragma unroll
+    for (int k = 0; k < QC; ++k) qcp[k] = ops[min(tid + k * NT, 8 * 64 - 1)];
+    if (copy_now) {
+#pragma unroll
+      for (int k = 0; k < QC; ++k)
+        if (tid + k * NT < 8 * 64) reinterpret_cast<uint4*>(s_lds + PK_QOPS_BASE)[tid + k * NT] = qcp[k];
     }
-    for (int idx = tid; idx < 8 * 64; idx += WAVES * 64)
-      reinterpret_cast<uint4*>(s_lds + PK_QOPS_BASE)[idx] = ops[idx];
     if constexpr (SLOTS == 2) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) qs[i] = __builtin_bit_cast(h8, ops[(8 + i) * 64 + lane]);
@@ -1306,6 +1301,43 @@ __global__ void __launch_bounds__(WAVES * 64, OCC) packed_decode_kernel(DecodeAr
     // the factor of head h sits in operand 12 of lane h * SLOTS
 #pragma unroll
     for (int k = 0; k < HL; ++k) cf[k] = __uint_as_float(ops[12 * 64 + (HL * g + k) * SLOTS].x);
+  };
+  if constexpr (!INPREP) operands(a.qops + (static_cast<int64_t>(b) * a.hkv + kvh) * (FQ_QOPS * 64), false);
+
+  PkPage<BITS> ring[RING];
+  if (my_pages > 0) {
+#pragma unroll
+    for (int k = 0; k < PRO; ++k)
+      pk_load(a, rec_of(bt_cur, min(k, min(64, my_pages) - 1)), n, lo, gptr, sgn_base, ring[k]);
+  }
+
+  // the byte-indexed sign table needs no input: built while the loads are in flight
+  // (its LDS is not the one in-kernel query preparation uses)
+  if constexpr (BSIGN) {
+    // entry (byte x, copy c) at 256 x + 16 c: half e = bit e of x ? +1 : -1
+    for (int idx = tid; idx < 256 * 16; idx += WAVES * 64) {
+      const uint32_t x = static_cast<uint32_t>(idx) >> 4;
+      uint32_t w[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const uint32_t lo16 = ((x >> (2 * k)) & 1) ? 0x3C00u : 0xBC00u;
+        const uint32_t hi16 = ((x >> (2 * k + 1)) & 1) ? 0x3C00u : 0xBC00u;
+        w[k] = lo16 | (hi16 << 16);
+      }
+      *reinterpret_cast<uint4*>(s_lds + PK_BSIGN_BASE + idx * 16) = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+  }
+
+  if constexpr (INPREP) {
+    uint4* const s_ops = reinterpret_cast<uint4*>(s_lds + PK_PREP_OPS);
+    prepare_group<SLOTS, PK_PREP_GM>(a, kvh, b, 0, G, tid, reinterpret_cast<float*>(s_lds + PK_CODE_BASE), s_ops,
+                                     false, pin);
+    __syncthreads();
+    operands(s_ops, true);
+  } else {
+#pragma unroll
+    for (int k = 0; k < QC; ++k)
+      if (tid + k * NT < 8 * 64) reinterpret_cast<uint4*>(s_lds + PK_QOPS_BASE)[tid + k * NT] = qcp[k];
   }
 
   // ---- tables: stage the 256 entries once, then fan out conflict-free copies
@@ -1330,20 +1362,6 @@ __global__ void __launch_bounds__(WAVES * 64, OCC) packed_decode_kernel(DecodeAr
         stage4[tid] = make_uint4(h2bits(h0, h1), h2bits(l0, l1), h2bits(h2, h3), h2bits(l2, l3));
       }
     }
-    if constexpr (BSIGN) {
-      // entry (byte x, copy c) at 256 x + 16 c: half e = bit e of x ? +1 : -1
-      for (int idx = tid; idx < 256 * 16; idx += WAVES * 64) {
-        const uint32_t x = static_cast<uint32_t>(idx) >> 4;
-        uint32_t w[4];
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const uint32_t lo16 = ((x >> (2 * k)) & 1) ? 0x3C00u : 0xBC00u;
-          const uint32_t hi16 = ((x >> (2 * k + 1)) & 1) ? 0x3C00u : 0xBC00u;
-          w[k] = lo16 | (hi16 << 16);
-        }
-        *reinterpret_cast<uint4*>(s_lds + PK_BSIGN_BASE + idx * 16) = make_uint4(w[0], w[1], w[2], w[3]);
-      }
-    }
     if constexpr (!BSIGN)
     for (int idx = tid; idx < 16 * 32; idx += WAVES * 64) {
       const int nib = idx >> 5;
@@ -1358,7 +1376,6 @@ __global__ void __launch_bounds__(WAVES * 64, OCC) packed_decode_kernel(DecodeAr
     }
     __syncthreads();
     // 8192 (4096) entries; four per thread and round, reads issued before writes
-    constexpr int NT = WAVES * 64;
     if constexpr (BITS == 4 && (256 * 32) % (4 * NT) != 0) {
       for (int idx = tid; idx < 256 * 32; idx += NT)
         *reinterpret_cast<uint2*>(s_lds + PK_CODE_BASE + idx * 8) = stage[idx >> 5];
