@@ -11,17 +11,18 @@ by compressing the whole synthetic context before timing.
 
 One step = one decode step of the whole 32-layer stack: per layer, the newest
 token's K and V compressed into its slot and the attention of the 32 sequences
-over their compressed pages, as fq_decode_step does it (its two halves are
-enqueued as fq_step_prepare: append + query preparation, and fq_step_attend: the
-attention, so that HIP events can bracket the attention launch). --separate
-runs fq_compress + fq_decode_attention per layer instead. value = batch / step
-time (decode tokens/s). Inputs are resident in HBM before the timed region.
+over their compressed pages: fq_decode_step, one launch per layer at this shape.
+--split-step enqueues its two halves instead (fq_step_prepare: append + query
+preparation; fq_step_attend: the attention), --separate runs fq_compress +
+fq_decode_attention per layer. value = batch / step time (decode tokens/s).
+Inputs are resident in HBM before the timed region.
 
 Also reported: the prefill compress rate (Mvectors/s) measured while filling
 the caches, the roofline of the dominant kernel (the attention launch) and the
 CPU oracle timed on a bounded sample of the same work.
 
-    python bench.py [--steps K] [--warmup W] [--gpus 1] [--layers 32] [--splits S] [--separate] [--no-cpu]
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--layers 32] [--splits S]
+                    [--split-step | --separate] [--no-cpu]
 """
 import argparse
 import json
@@ -40,9 +41,10 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_call_traffic.json")
 DECODE_SRC = os.path.join(ROOT, "kv_cache_vector_tq4_amd", "csrc", "fq_decode.hip")
 
 
-def measured_traffic():
-    """HBM bytes per decode call from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE
-    summary, or None when the decode source has changed since it was measured."""
+def measured_traffic(mode):
+    """HBM bytes per timed launch from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE
+    summary, or None when the decode source has changed since it was measured or it
+    was measured for another step form."""
     import hashlib
 
     try:
@@ -52,7 +54,7 @@ def measured_traffic():
             sha = hashlib.sha256(f.read()).hexdigest()
     except (OSError, ValueError):
         return None
-    if rec.get("decode_source_sha256") != sha:
+    if rec.get("decode_source_sha256") != sha or rec.get("bench_mode") != mode:
         return None
     return rec.get("bytes_per_launch")
 HBM_PEAK_GBS = 8000.0
@@ -90,6 +92,8 @@ def parse():
     p.add_argument("--no-graph", action="store_true", help="time eager launches instead of a HIP graph")
     p.add_argument("--separate", action="store_true",
                    help="per layer fq_compress of the newest tokens, then fq_decode_attention")
+    p.add_argument("--split-step", action="store_true",
+                   help="per layer fq_step_prepare, then fq_step_attend (the two halves of fq_decode_step)")
     p.add_argument("--no-extra", action="store_true", help="skip the other workloads' measurements")
     p.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                    help="only run a plain device-to-device copy of BYTES (for scaling HBM byte counters)")
@@ -343,20 +347,24 @@ def main():
     wss = [torch.empty(ws_bytes, dtype=torch.uint8, device=dev) for _ in range(w.layers)]
     outs = [torch.empty((B, Hq, d), dtype=torch.float32, device=dev) for _ in range(w.layers)]
 
-    ev = []  # (start, end) events around each attention launch in the timed steps
+    ev = []  # (start, end) events around each timed call (the attention part) in the timed steps
+    mode = "separate" if args.separate else "split" if args.split_step else "step"
 
     def attend(layer):
-        if args.separate:
+        if mode == "separate":
             fq.decode(qz, caches[layer], qs[layer], bt, lens_t, max_len, num_splits=splits, workspace=wss[layer],
                       out=outs[layer])
-        else:
+        elif mode == "split":
             fq.step_attend(qz, caches[layer], B, Hq, bt, lens_t, max_len, wss[layer], num_splits=splits,
                            out=outs[layer])
+        else:
+            fq.decode_step(qz, caches[layer], knew[layer], vnew[layer], new_slots, qs[layer], bt, lens_t, max_len,
+                           num_splits=splits, workspace=wss[layer], out=outs[layer])
 
     def prepare(layer):
-        if args.separate:
+        if mode == "separate":
             fq.compress(qz, caches[layer], knew[layer], vnew[layer], new_slots)
-        else:
+        elif mode == "split":
             fq.step_prepare(qz, caches[layer], knew[layer], vnew[layer], new_slots, qs[layer], max_len,
                             wss[layer], num_splits=splits)
 
@@ -449,7 +457,8 @@ def main():
         ref = [o.clone() for o in outs]
         dec_ms = graph_ms(attend)
         assert all(torch.equal(o, r) for o, r in zip(outs, ref)), "attention replays differ from the step"
-        prep_ms = graph_ms(prepare)
+        if mode != "step":
+            prep_ms = graph_ms(prepare)
 
     # accuracy: layer 0's outputs against exact attention over its uncompressed K / V
     # (the newest token of sequence b holds knew[0][b] / vnew[0][b], written by the step)
@@ -468,7 +477,11 @@ def main():
 
     bpt = caches[0].bytes_per_token_head()  # 156 B at 4 bits with QJL keys
     dec_bytes = ntok * Hkv * bpt
-    achieved = dec_bytes / (dec_ms * 1e-3) / 1e9
+    # the timed launch reads the layer's cache; in the one-launch step it also reads
+    # the newest bf16 K and V (2 x 256 B per sequence and KV head) and writes their
+    # records (bpt bytes each)
+    launch_bytes = dec_bytes + (B * Hkv * (2 * d * 2 + bpt) if mode == "step" else 0)
+    achieved = launch_bytes / (dec_ms * 1e-3) / 1e9
     comp_vec = 2 * ntok * Hkv
     comp_med_ms = float(np.median(comp_ms[1:] if len(comp_ms) > 1 else comp_ms))
     comp_bytes = ntok * Hkv * (2 * d * 2) + ntok * 8 + ntok * Hkv * bpt
@@ -488,36 +501,42 @@ def main():
         "dtype": "f32",
         "data": "synthetic",
         "config": {
-            "workload": "llama3-8b-shape attention stack: %d layers x (compress new token + decode%s), batch %d, "
+            "workload": "llama3-8b-shape attention stack: %d layers x (compress new token + decode: %s), batch %d, "
                         "ctx U[3072,4096] (sum %d), 32 q / 8 kv heads, d 128, TQ4 K(MSE+QJL)+V, 16-token pages, "
-                        "%d splits" % (w.layers, ": fq_compress, fq_decode_attention" if args.separate else
-                                       ": fq_decode_step", B, ntok, splits),
+                        "%d splits" % (w.layers, {"separate": "fq_compress, fq_decode_attention",
+                                                  "split": "fq_step_prepare, fq_step_attend",
+                                                  "step": "fq_decode_step"}[mode], B, ntok, splits),
             "layers": w.layers, "batch": B, "context_tokens": ntok, "num_splits": splits,
             "cache_bytes_per_layer": dec_bytes, "bytes_per_token_head": bpt,
         },
         "roofline": {
-            "kernel": ("fq_decode_attention (one launch: packed_decode_kernel, query preparation and output "
-                       "rotation in-kernel)" if args.separate and splits == 1 else
-                       "fq_decode_attention (prepare_queries + packed split attention + merge_unrotate)"
-                       if args.separate else
-                       "fq_step_attend (one launch: packed_decode_kernel, queries prepared by fq_step_prepare, "
-                       "output rotation in-kernel)" if splits == 1 else
-                       "fq_step_attend (packed split attention + merge_unrotate)"),
+            "kernel": {
+                ("separate", True): "fq_decode_attention (one launch: packed_decode_kernel, query preparation and "
+                                    "output rotation in-kernel)",
+                ("separate", False): "fq_decode_attention (prepare_queries + packed split attention + merge_unrotate)",
+                ("split", True): "fq_step_attend (one launch: packed_decode_kernel, queries prepared by "
+                                 "fq_step_prepare, output rotation in-kernel)",
+                ("split", False): "fq_step_attend (packed split attention + merge_unrotate)",
+                ("step", True): "fq_decode_step (one launch: packed_decode_kernel appending the newest K/V token, "
+                                "preparing the queries and rotating the output in-kernel)",
+                ("step", False): "fq_decode_step (prepare_queries with the append + packed split attention + "
+                                 "merge_unrotate)"}[(mode, splits == 1)],
             "bound": "hbm",
             "achieved": achieved,
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBS,
-            "traffic": measured_traffic(),
-            "algorithmic_bytes_per_launch": dec_bytes,
+            "traffic": measured_traffic(mode),
+            "algorithmic_bytes_per_launch": launch_bytes,
             "avg_launch_ms": dec_ms,
-            "timing": "HIP events around graph replays of the %d layers' attention calls" % w.layers
-                      if graph is not None else "HIP events around eager attention calls",
+            "timing": "HIP events around graph replays of the %d layers' %s calls" % (
+                w.layers, "fq_decode_step" if mode == "step" else "attention")
+                      if graph is not None else "HIP events around eager calls",
             "avg_launch_ms_eager": dec_ms_eager,
         },
-        "step_parts": {
+        "step_parts": None if mode == "step" else {
             "prepare_ms": prep_ms,
-            "prepare": ("fq_compress of the newest 32 x 8 K and V" if args.separate else
+            "prepare": ("fq_compress of the newest 32 x 8 K and V" if mode == "separate" else
                         "fq_step_prepare: newest 32 x 8 K and V compressed + queries prepared (one launch)"),
             "attend_ms": dec_ms,
             "timing": "HIP events around graph replays of the %d layers' calls of each part" % w.layers,

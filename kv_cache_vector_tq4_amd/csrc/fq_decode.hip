@@ -56,7 +56,7 @@ struct DecodeArgs {
   uint4* qops;     // [B][Hkv][FQ_QOPS][64]
   float* out;      // [B][Hq][d]
   // the newest token of every sequence, compressed into its slot before the
-  // decode reads the cache (append_group); unused otherwise
+  // decode reads the cache (prepare_group with APP); unused otherwise
   const void* knew;       // K / V element (b, h, j) at b * kv_tstride + h * kv_hstride + j
   const void* vnew;
   const int64_t* slots;   // [B] slot of sequence b's newest token, < 0 = not stored
@@ -345,14 +345,16 @@ constexpr int prep_lds_floats() { return 9 * GM * D + 8 * GM; }
 
 // Global loads of prepare_group, issued ahead of the rest of the work: thread
 // (coordinate j, k-quarter kq) takes coordinate j of query heads hb + kq,
-// hb + kq + 4, ... (< hb + hn) and column j of Pi^T and of S^T (rows 32 kq ..).
+// hb + kq + 4, ... (< hb + hn), with APP coordinate j of the sequence's newest K
+// (kq 0) or V (kq 1) vector, and column j of Pi^T and of S^T (rows 32 kq ..).
 template <int GM>
 struct PrepIn {
   float pc[32], sc[32];
   float qv[GM / 4];
+  float xv;  // newest K / V coordinate (APP)
 };
 
-template <int DT, int GM>
+template <int DT, int GM, bool APP>
 __device__ __forceinline__ void prep_issue(const DecodeArgs& a, int kvh, int b, int hb, int hn, int tid,
                                            PrepIn<GM>& in) {
   const int j = tid & (D - 1);
@@ -368,22 +370,39 @@ __device__ __forceinline__ void prep_issue(const DecodeArgs& a, int kvh, int b, 
     else
       in.qv[i] = static_cast<const float*>(a.q)[off];
   }
+  in.xv = 0.f;
+  if constexpr (APP) {
+    if (kq < 2) {
+      const int64_t off = static_cast<int64_t>(b) * a.kv_tstride + static_cast<int64_t>(kvh) * a.kv_hstride + j;
+      const void* src = kq == 0 ? a.knew : a.vnew;
+      in.xv = a.kv_bf16 ? __uint_as_float(static_cast<uint32_t>(static_cast<const uint16_t*>(src)[off]) << 16)
+                        : static_cast<const float*>(src)[off];
+    }
+  }
   col_quarter_load(a.pit, j, kq, in.pc);
   col_quarter_load(a.qjl_on ? a.sit : a.pit, j, kq, in.sc);
 }
 
-// The query work for heads hb .. hb + hn - 1 (hn <= GM) of the group of one (KV
-// head, sequence) by PQ_THREADS threads (thread = (coordinate j, k-quarter kq)),
-// lds = prep_lds_floats<GM>() floats:
+// The query work for heads hb .. hb + hn - 1 of the group of one (KV head,
+// sequence) by PQ_THREADS threads (thread = (coordinate j, k-quarter kq)),
+// lds = prep_lds_floats<GM>() floats, hn + 2 <= GM:
 //   q~[h][j]  = sum_k Pi[j][k] q[h][k]     (column j of Pi^T)
 //   q_s[h][j] = sum_k S[j][k] q~[h][k]     (column j of S^T)
 // written to qrot / qs when write_vec, and with SLOTS > 0 those heads' entries
 // of the FQ_QOPS x 64 per-lane operands of the packed split kernel to ops (global
 // memory or LDS; the caller synchronizes before reading them); the range that
 // starts at head 0 also zeroes the entries of the lanes without a head.
-template <int SLOTS, int GM>
+//
+// With APP the same products also compress the sequence's newest K and V vectors
+// into their slot, as fq_compress does it ("FlashQuant" page, "TurboQuant" steps
+// 1-4 and "QJL"), in fp32 against the fp32 Pi and S: rows hn (K) and hn + 1 (V) of
+// the Pi product give y = (Pi x) / n (0 when n = 0), idx_j = #{i : boundary_i <
+// y_j}; the key residual r = y - level[idx] is row hn of the S product, p = S r,
+// bit j = [p_j >= 0], gamma = n ||r||. Nothing is stored when the slot is negative.
+template <int SLOTS, int GM, bool APP>
 __device__ __forceinline__ void prepare_group(const DecodeArgs& a, int kvh, int b, int hb, int hn, int tid,
                                               float* lds, uint4* ops, bool write_vec, const PrepIn<GM>& in) {
+  static_assert(!APP || GM >= 3, "room for the appended rows");
   float* const s_q = lds;                   // [GM][D]
   float* const s_r = s_q + GM * D;          // [GM][D]
   float* const s_s = s_r + GM * D;          // [GM][D]
@@ -394,18 +413,33 @@ __device__ __forceinline__ void prepare_group(const DecodeArgs& a, int kvh, int 
   uint16_t* const s_sl = s_sh + GM * D;
   float* const s_mx = s_part + 6 * GM * D;  // [2][GM][2]: [q~, q_s][head][row half]
   float* const s_cf = s_mx + 4 * GM;        // [GM]
+  float* const s_nrm = s_cf + GM;           // [6]: ||k||^2, ||v||^2, ||r||^2 per row half
   const int j = tid & (D - 1);
   const int kq = __builtin_amdgcn_readfirstlane(tid >> 7);
+  const int lane = tid & 63;
   // G = heads of this range; threads beyond PQ_THREADS (larger work-groups) only
   // take the barriers
-  const int G = tid < PQ_THREADS ? hn : 0;
+  const bool mine = tid < PQ_THREADS;
+  const int G = mine ? hn : 0;
   const bool qjl = a.qjl_on != 0;
+  const int r1 = mine ? hn + (APP ? 2 : 0) : 0;          // rows of the Pi product
+  const int r2 = mine ? hn + (APP && qjl ? 1 : 0) : 0;   // rows of the S product
   const int64_t row0 = (static_cast<int64_t>(b) * a.hq + kvh * a.group + hb) * D;
+  int64_t slot = -1, rec = 0;
+  if constexpr (APP) {
+    slot = a.slots[b];
+    rec = ((slot >> 4) * a.hkv + kvh) * FQ_BLOCK + (slot & 15);
+  }
 #pragma unroll
   for (int i = 0; i < GM / 4; ++i)
     if (kq + 4 * i < G) s_q[(kq + 4 * i) * D + j] = in.qv[i];
+  if (APP && mine && kq < 2) {
+    s_q[(hn + kq) * D + j] = in.xv;
+    const float ss = wave_sum_dpp(in.xv * in.xv);
+    if (lane == 0) s_nrm[2 * kq + (j >> 6)] = ss;
+  }
   __syncthreads();
-  if (G > 0) quarter_dot_any<GM>(in.pc, s_q, j, kq, G, s_part);
+  if (r1 > 0) quarter_dot_any<GM>(in.pc, s_q, j, kq, r1, s_part);
   __syncthreads();
   // q~ parts summed; the per-wave maxima of |q~| (64 coordinates of one head)
   for (int h = kq; h < G; h += 4) {
@@ -418,9 +452,44 @@ __device__ __forceinline__ void prepare_group(const DecodeArgs& a, int kvh, int 
       if ((j & 63) == 0) s_mx[(0 * GM + h) * 2 + (j >> 6)] = m;
     }
   }
+  const float nk = APP ? sqrtf(s_nrm[0] + s_nrm[1]) : 0.f;
+  if (APP && mine && kq < 2) {
+    const int r = hn + kq;  // row: 0 K, 1 V
+    const float n = kq == 0 ? nk : sqrtf(s_nrm[2] + s_nrm[3]);
+    const float inv = n > 0.f ? 1.0f / n : 0.f;
+    const float y = ((s_part[(0 * GM + r) * D + j] + s_part[(1 * GM + r) * D + j]) +
+                     (s_part[(2 * GM + r) * D + j] + s_part[(3 * GM + r) * D + j])) * inv;
+    const cptr bq = uniform_ptr(a.bnd);
+    const int nb = (1 << a.bits) - 1;
+    uint32_t idx = 0;
+#pragma unroll
+    for (int i = 0; i < 15; ++i) {
+      const float bi = bq[i < nb ? i : nb - 1];  // reads stay inside the nb boundaries
+      if (i < nb) idx += bi < y ? 1u : 0u;
+    }
+    // 32-bit word j / per of the packed codes gathered in its first lane
+    const int per = 32 / a.bits;
+    uint32_t w = idx << (a.bits * (j % per));
+#pragma unroll
+    for (int m = 1; m < 16; m <<= 1)
+      if (m < per) w |= static_cast<uint32_t>(__shfl_xor(static_cast<int>(w), m));
+    if (slot >= 0) {
+      if (a.dbg_y) a.dbg_y[((static_cast<int64_t>(kq) * a.batch + b) * a.hkv + kvh) * D + j] = y;
+      const int cb = D * a.bits / 8;  // code bytes per vector
+      uint8_t* const codes = const_cast<uint8_t*>(kq == 0 ? a.k_codes : a.v_codes);
+      if (j % per == 0) *reinterpret_cast<uint32_t*>(codes + rec * cb + 4 * (j / per)) = w;
+      if (j == 0) const_cast<float*>(kq == 0 ? a.k_norm : a.v_norm)[rec] = n;
+    }
+    if (kq == 0 && qjl) {
+      const float res = y - a.levels[idx];
+      s_r[hn * D + j] = res;
+      const float rr = wave_sum_dpp(res * res);
+      if (lane == 0) s_nrm[4 + (j >> 6)] = rr;
+    }
+  }
   __syncthreads();
   if (qjl) {
-    if (G > 0) quarter_dot_any<GM>(in.sc, s_r, j, kq, G, s_part);
+    if (r2 > 0) quarter_dot_any<GM>(in.sc, s_r, j, kq, r2, s_part);
     __syncthreads();
   }
   for (int h = kq; h < G; h += 4) {
@@ -434,6 +503,18 @@ __device__ __forceinline__ void prepare_group(const DecodeArgs& a, int kvh, int 
     if constexpr (SLOTS > 0) {
       const float m = wave_max_dpp(fabsf(v));
       if ((j & 63) == 0) s_mx[(1 * GM + h) * 2 + (j >> 6)] = m;
+    }
+  }
+  if (APP && qjl && mine && kq == 0) {
+    const int r = hn;
+    const float p = (s_part[(0 * GM + r) * D + j] + s_part[(1 * GM + r) * D + j]) +
+                    (s_part[(2 * GM + r) * D + j] + s_part[(3 * GM + r) * D + j]);
+    // bit i of sign byte t = [p_{8t+i} >= 0]: the wave's ballot, lane order
+    const uint64_t sg = __ballot(p >= 0.f);
+    if (slot >= 0) {
+      if (a.dbg_p) a.dbg_p[(static_cast<int64_t>(b) * a.hkv + kvh) * D + j] = p;
+      if (lane == 0) *reinterpret_cast<uint64_t*>(const_cast<uint8_t*>(a.k_qjl) + rec * (D / 8) + 8 * (j >> 6)) = sg;
+      if (j == 0) const_cast<float*>(a.k_gamma)[rec] = nk * sqrtf(s_nrm[4] + s_nrm[5]);
     }
   }
   if constexpr (SLOTS > 0) {
@@ -464,123 +545,26 @@ __device__ __forceinline__ void prepare_group(const DecodeArgs& a, int kvh, int 
   }
 }
 
-// LDS floats used by append_group.
-constexpr int APPEND_LDS_FLOATS = 11 * D + 8;
-static_assert(APPEND_LDS_FLOATS <= prep_lds_floats<FQ_MAX_GROUP>(), "append fits the preparation LDS");
-
-// The newest token of sequence b, KV head kvh, compressed into its slot as
-// fq_compress does it ("FlashQuant" page, "TurboQuant" steps 1-4 and "QJL"), by
-// PQ_THREADS threads (thread = (coordinate j, k-quarter kq)), in fp32 against the
-// fp32 Pi and S:
-//   n = ||x||, y = (Pi x) / n (0 when n = 0), idx_j = #{i : boundary_i < y_j},
-//   codes and n stored; keys also r = y - level[idx], gamma = n ||r||, p = S r,
-//   bit j = [p_j >= 0].
-// Nothing is stored when the slot is negative.
-template <int BITS, int KDT>
-__device__ __forceinline__ void append_group(const DecodeArgs& a, int kvh, int b, int tid, float* lds) {
-  constexpr int L = 1 << BITS;
-  constexpr int PER = 32 / BITS;      // codes per 32-bit word
-  constexpr int CB = D * BITS / 8;    // code bytes per vector
-  float* const s_x = lds;             // [2][D] raw K, V
-  float* const s_part = s_x + 2 * D;  // [4][2][D] quarter sums
-  float* const s_r = s_part + 8 * D;  // [D] key residual
-  float* const s_sum = s_r + D;       // [6]: ||k||^2, ||v||^2, ||r||^2, per half
-  const int j = tid & (D - 1);
-  const int kq = __builtin_amdgcn_readfirstlane(tid >> 7);
-  const int lane = tid & 63;
-  const bool qjl = a.qjl_on != 0;
-  // loads first: coordinate j of K (kq 0) or V (kq 1), then columns of Pi^T, S^T
-  float x = 0.f;
-  if (kq < 2) {
-    const int64_t off = static_cast<int64_t>(b) * a.kv_tstride + static_cast<int64_t>(kvh) * a.kv_hstride + j;
-    const void* src = kq == 0 ? a.knew : a.vnew;
-    if constexpr (KDT == FQ_BF16)
-      x = __uint_as_float(static_cast<uint32_t>(static_cast<const uint16_t*>(src)[off]) << 16);
-    else
-      x = static_cast<const float*>(src)[off];
-  }
-  float pc[32], sc[32];
-  col_quarter_load(a.pit, j, kq, pc);
-  col_quarter_load(qjl ? a.sit : a.pit, j, kq, sc);
-  const int64_t slot = a.slots[b];
-  const int64_t rec = ((slot >> 4) * a.hkv + kvh) * FQ_BLOCK + (slot & 15);
-  if (kq < 2) {
-    s_x[kq * D + j] = x;
-    const float ss = wave_sum_dpp(x * x);
-    if (lane == 0) s_sum[2 * kq + (j >> 6)] = ss;
-  }
-  __syncthreads();
-  quarter_dot_g<2, 2>(pc, s_x, j, kq, 2, s_part);
-  __syncthreads();
-  const float nk = sqrtf(s_sum[0] + s_sum[1]);
-  if (kq < 2) {
-    const int h = kq;  // 0: K, 1: V
-    const float n = h == 0 ? nk : sqrtf(s_sum[2] + s_sum[3]);
-    const float inv = n > 0.f ? 1.0f / n : 0.f;
-    const float y = ((s_part[(0 * 2 + h) * D + j] + s_part[(1 * 2 + h) * D + j]) +
-                     (s_part[(2 * 2 + h) * D + j] + s_part[(3 * 2 + h) * D + j])) * inv;
-    const cptr bq = uniform_ptr(a.bnd);
-    uint32_t idx = 0;
-#pragma unroll
-    for (int i = 0; i < L - 1; ++i) idx += bq[i] < y ? 1u : 0u;
-    // word j / PER of the packed codes gathered in its first lane
-    uint32_t w = idx << (BITS * (j % PER));
-#pragma unroll
-    for (int m = 1; m < PER; m <<= 1) w |= static_cast<uint32_t>(__shfl_xor(static_cast<int>(w), m));
-    if (slot >= 0) {
-      if (a.dbg_y) a.dbg_y[((static_cast<int64_t>(h) * a.batch + b) * a.hkv + kvh) * D + j] = y;
-      uint8_t* const codes = const_cast<uint8_t*>(h == 0 ? a.k_codes : a.v_codes);
-      if (j % PER == 0) *reinterpret_cast<uint32_t*>(codes + rec * CB + 4 * (j / PER)) = w;
-      if (j == 0) const_cast<float*>(h == 0 ? a.k_norm : a.v_norm)[rec] = n;
-    }
-    if (h == 0 && qjl) {
-      const float r = y - a.levels[idx];
-      s_r[j] = r;
-      const float rr = wave_sum_dpp(r * r);
-      if (lane == 0) s_sum[4 + (j >> 6)] = rr;
-    }
-  }
-  if (!qjl) return;  // uniform over the work-group
-  __syncthreads();
-  quarter_dot_g<1, 1>(sc, s_r, j, kq, 1, s_part);
-  __syncthreads();
-  if (kq == 0) {
-    const float p = (s_part[0 * D + j] + s_part[1 * D + j]) + (s_part[2 * D + j] + s_part[3 * D + j]);
-    // bit i of sign byte t = [p_{8t+i} >= 0]: the wave's ballot, lane order
-    const uint64_t sg = __ballot(p >= 0.f);
-    if (slot >= 0) {
-      if (a.dbg_p) a.dbg_p[(static_cast<int64_t>(b) * a.hkv + kvh) * D + j] = p;
-      if (lane == 0) *reinterpret_cast<uint64_t*>(const_cast<uint8_t*>(a.k_qjl) + rec * (D / 8) + 8 * (j >> 6)) = sg;
-      if (j == 0) const_cast<float*>(a.k_gamma)[rec] = nk * sqrtf(s_sum[4] + s_sum[5]);
-    }
-  }
-}
-
 // One work-group per (KV head, sequence, part of the group): the group's heads
-// are shared out over the first gridDim.z - APPEND work-groups (all in one, or one
-// each when there are few (KV head, sequence) pairs to spread the work over);
-// with APPEND the last one compresses the newest K / V token of the pair.
+// are shared out over gridDim.z work-groups (all in one, or one each when there
+// are few (KV head, sequence) pairs to spread the work over); with APPEND the
+// first one also compresses the pair's newest K / V token.
 template <int DT, int SLOTS, int APPEND>
 __global__ void __launch_bounds__(PQ_THREADS) prepare_queries_kernel(DecodeArgs a) {
-  __shared__ __align__(16) float s_p[prep_lds_floats<FQ_MAX_GROUP>()];
+  constexpr int GM = FQ_MAX_GROUP + (APPEND ? 2 : 0);
+  __shared__ __align__(16) float s_p[prep_lds_floats<GM>()];
   const int kvh = blockIdx.x, b = blockIdx.y;
-  if (APPEND && static_cast<int>(blockIdx.z) == static_cast<int>(gridDim.z) - 1) {
-    if (a.bits == 4) {
-      if (a.kv_bf16) append_group<4, FQ_BF16>(a, kvh, b, threadIdx.x, s_p);
-      else append_group<4, FQ_F32>(a, kvh, b, threadIdx.x, s_p);
-    } else {
-      if (a.kv_bf16) append_group<2, FQ_BF16>(a, kvh, b, threadIdx.x, s_p);
-      else append_group<2, FQ_F32>(a, kvh, b, threadIdx.x, s_p);
-    }
-    return;
-  }
-  const int hn = a.group / (static_cast<int>(gridDim.z) - APPEND), hb = blockIdx.z * hn;
-  PrepIn<FQ_MAX_GROUP> in;
-  prep_issue<DT, FQ_MAX_GROUP>(a, kvh, b, hb, hn, threadIdx.x, in);
+  const int hn = a.group / gridDim.z, hb = blockIdx.z * hn;
+  uint4* const ops = a.qops + (static_cast<int64_t>(b) * a.hkv + kvh) * (FQ_QOPS * 64);
   // q~ and q_s as fp32 rows only for the kernels that read them (groups of 16)
-  prepare_group<SLOTS, FQ_MAX_GROUP>(a, kvh, b, hb, hn, threadIdx.x, s_p,
-                                     a.qops + (static_cast<int64_t>(b) * a.hkv + kvh) * (FQ_QOPS * 64), SLOTS == 0,
-                                     in);
+  PrepIn<GM> in;
+  if (APPEND && blockIdx.z == 0) {
+    prep_issue<DT, GM, true>(a, kvh, b, hb, hn, threadIdx.x, in);
+    prepare_group<SLOTS, GM, true>(a, kvh, b, hb, hn, threadIdx.x, s_p, ops, SLOTS == 0, in);
+  } else {
+    prep_issue<DT, GM, false>(a, kvh, b, hb, hn, threadIdx.x, in);
+    prepare_group<SLOTS, GM, false>(a, kvh, b, hb, hn, threadIdx.x, s_p, ops, SLOTS == 0, in);
+  }
 }
 
 // ---------------------------------------------------------------- kernel 2
@@ -1084,6 +1068,15 @@ constexpr int PK2_WAVES = 8, PK2_RING = 2, PK2_OCC = 4;  // SLOTS 2
 // 2-bit (whose loop gains from a third wave per SIMD; the 4-bit loop loses)
 constexpr int PKF_RING = 2, PKF_OCC = 2;
 constexpr int pkf_waves(int bits) { return bits == 4 ? 8 : 12; }
+// Static page order of a work-group. A SIMD issues its oldest wave first, so wave
+// class c = wave / 4 (the SIMD's waves in age order) pages faster the lower c:
+// 0.88 / 1.02 / 1.22 us per page for the three classes of the single-split 2-bit
+// work-group (phase stamps, batch-32 layer). There class c takes WMIN + (classes
+// - 1 - c) pages per round (7 : 6 : 5), in slots interleaved over the round, so
+// that its waves end together (2 % faster). In the 4-bit one (two classes) the
+// younger wave speeds up once the older is done, and plain round-robin (WMIN = 0)
+// is as fast. The order is fixed, so the reduction order is too.
+constexpr int pk_wmin(int bits, bool only) { return only && bits == 2 ? 5 : 0; }
 constexpr int PK_SIGN_BASE = 0;       // 16 x 32 x 8 B
 constexpr int PK_CODE_BASE = 4096;    // 256 x 32 x 8 B (4-bit) or 256 x 16 x 16 B (2-bit)
 constexpr int PK_STAGE_BASE = 69632;  // 256 x 16 B staging for the table build
@@ -1096,7 +1089,7 @@ constexpr int PK_BSIGN_BASE = PK_LDS_BYTES;
 constexpr int PK_LDS_BYTES_F = PK_BSIGN_BASE + 256 * 16 * 16;
 // In-kernel query preparation (groups of up to 8 heads) uses the code-table area
 // before the table is built: its scratch, then the FQ_QOPS x 64 operands.
-constexpr int PK_PREP_GM = 8;
+constexpr int PK_PREP_GM = 10;  // up to 8 heads and, when appending, the new K and V
 constexpr int PK_PREP_OPS = PK_CODE_BASE + ((prep_lds_floats<PK_PREP_GM>() * 4 + 255) / 256) * 256;
 static_assert(PK_PREP_OPS + FQ_QOPS * 64 * 16 <= PK_STAGE_BASE, "query preparation fits the code-table area");
 constexpr float PK_TAU = 8.0f;
@@ -1198,12 +1191,13 @@ __device__ __forceinline__ void xcd_pair_map(int hkv, int batch, int& kvh, int& 
 // work-group normalizes and un-rotates its output itself. PREP = the query
 // dtype (>= 0): as -2, and the work-group prepares its own query operands too
 // (prepare_group, in the LDS the code table takes later).
-template <int BITS, int SLOTS, int WAVES, int RING, int OCC, int PREP>
+template <int BITS, int SLOTS, int WAVES, int RING, int OCC, int PREP, bool APP = false>
 __global__ void __launch_bounds__(WAVES * 64, OCC) packed_decode_kernel(DecodeArgs a) {
   static_assert(BITS == 4 || BITS == 2, "4- or 2-bit codes");
   constexpr bool INPREP = PREP >= 0;  // query operands prepared in-kernel
   constexpr bool ONLY = PREP != -1;   // the only split: output finished in-kernel
   static_assert(!ONLY || WAVES * 64 >= PQ_THREADS, "in-kernel query work takes PQ_THREADS threads");
+  static_assert(!APP || INPREP, "the append runs in the in-kernel query preparation");
   static_assert(WAVES * 64 >= 256, "the table stage takes 256 threads");
   constexpr int CB = D * BITS / 8;  // code bytes per vector
   constexpr bool BSIGN = ONLY;  // byte-indexed sign table (one work-group per CU)
@@ -1222,11 +1216,24 @@ __global__ void __launch_bounds__(WAVES * 64, OCC) packed_decode_kernel(DecodeAr
   const int G = a.group;
 
   const int t0 = split * a.chunk;
-  const int p0 = wave;
+  // This wave's i-th page of the split: rounds of RL pages in 4-page slots (one page
+  // per SIMD); the wave takes page sub of wt slots per round.
+  constexpr int NCLS = WAVES / 4, WMIN = pk_wmin(BITS, ONLY);
+  constexpr int RL = WMIN == 0 ? WAVES : 4 * (NCLS * WMIN + NCLS * (NCLS - 1) / 2);
+  const int cls = wave >> 2, sub = wave & 3;
+  const int wt = WMIN == 0 ? 1 : WMIN + (NCLS - 1 - cls);
+  auto slot_of = [&](int j) {  // slot of the wave's j-th page of a round
+    const int e = j - WMIN;
+    return WMIN == 0 ? cls : j < WMIN ? NCLS * j + cls : NCLS * WMIN + e * (NCLS - 1) - e * (e - 1) / 2 + cls;
+  };
+  auto page_of = [&](int i) {
+    const int r = i / wt;
+    return r * RL + 4 * slot_of(i - r * wt) + sub;
+  };
   // The first 64 block numbers of this wave are requested together with the
   // sequence length (columns clamped to the table row).
   const int32_t* btrow = a.block_tables + static_cast<int64_t>(b) * a.max_blocks;
-  int bt_cur = a.max_blocks > 0 ? btrow[min(t0 / FQ_BLOCK + p0 + lane * WAVES, a.max_blocks - 1)] : 0;
+  int bt_cur = a.max_blocks > 0 ? btrow[min(t0 / FQ_BLOCK + page_of(lane), a.max_blocks - 1)] : 0;
   const int len = a.seq_lens[b];
   const int t1 = min(len, t0 + a.chunk);
   const int npages = t1 > t0 ? (t1 - t0 + FQ_BLOCK - 1) / FQ_BLOCK : 0;
@@ -1236,16 +1243,16 @@ __global__ void __launch_bounds__(WAVES * 64, OCC) packed_decode_kernel(DecodeAr
   // arrays of the page instead.
   const uint8_t* const sgn_base = qjl ? a.k_qjl : a.k_codes;
   const float* const gptr = qjl ? a.k_gamma : a.k_norm;
-  // This wave's pages are p0 + i * WAVES, i < my_pages, taken in chunks of 64 whose
-  // block numbers are held one per lane; a page's record then comes from a lane
-  // read. Every load of the page loop is unconditional (prefetch indices are
-  // clamped to the chunk's last page), so each wait covers exactly the page it
-  // needs and not the prefetches behind it.
-  const int my_pages = p0 < npages ? (npages - 1 - p0) / WAVES + 1 : 0;
-  auto bt_chunk = [&](int c0) {
-    const int cn = min(64, my_pages - c0);
-    return bt[p0 + (c0 + min(lane, cn - 1)) * WAVES];
-  };
+  // This wave's pages are page_of(i), i < my_pages, taken in chunks of 64 whose
+  // block numbers (and page indices) are held one per lane; a page's record then
+  // comes from a lane read. Every load of the page loop is unconditional (prefetch
+  // indices are clamped to the chunk's last page), so each wait covers exactly the
+  // page it needs and not the prefetches behind it.
+  const int nround = npages / RL, rem = npages - nround * RL;
+  int my_pages = nround * wt;
+  for (int j = 0; j < wt; ++j) my_pages += 4 * slot_of(j) + sub < rem ? 1 : 0;
+  int pg_cur = page_of(lane);
+  auto chunk_lane = [&](int c0) { return c0 + min(lane, min(64, my_pages - c0) - 1); };
   auto rec_of = [&](int vblk, int i) {
     const int blk = __builtin_amdgcn_readlane(vblk, i);
     return (static_cast<int64_t>(blk) * a.hkv + kvh) * FQ_BLOCK;
@@ -1259,7 +1266,7 @@ __global__ void __launch_bounds__(WAVES * 64, OCC) packed_decode_kernel(DecodeAr
   // pages are requested before any set-up work, in the order they are needed
   PrepIn<PK_PREP_GM> pin;
   if constexpr (INPREP) {
-    if (tid < PQ_THREADS) prep_issue<(PREP >= 0 ? PREP : 0), PK_PREP_GM>(a, kvh, b, 0, G, tid, pin);
+    if (tid < PQ_THREADS) prep_issue<(PREP >= 0 ? PREP : 0), PK_PREP_GM, APP>(a, kvh, b, 0, G, tid, pin);
   }
   // codebook levels of the table entry this thread stages (threads < 256)
   float lv[BITS == 4 ? 2 : 4] = {};
@@ -1274,8 +1281,9 @@ __global__ void __launch_bounds__(WAVES * 64, OCC) packed_decode_kernel(DecodeAr
   }
   // ---- query operands. With two heads per lane (SLOTS 2) registers are short, so
   // the code-product operands (the same for every wave) are read from LDS at each
-  // step. Prepared by the query launch, they are requested before the pages (loads
-  // complete in issue order, so waiting for them then waits for nothing else);
+  // step. Prepared by the query launch, the only split requests them before the
+  // pages (loads complete in issue order, so waiting for them then waits for
+  // nothing else; the split kernels, at 128 registers, request them after);
   // prepared in-kernel, they are read from LDS below.
   h8 qs[4];   // SLOTS 2: sign-product A operands
   h8 qmr[8];  // SLOTS 4: code-product A operands, held in registers (SLOTS 2 reads them from LDS)
@@ -1284,12 +1292,11 @@ __global__ void __launch_bounds__(WAVES * 64, OCC) packed_decode_kernel(DecodeAr
   constexpr int QC = (8 * 64 + NT - 1) / NT;  // code-product operands copied to LDS per thread
   uint4 qcp[QC];
   auto operands = [&](const uint4* ops, bool copy_now) {
-#pragma unroll
-    for (int k = 0; k < QC; ++k) qcp[k] = ops[min(tid + k * NT, 8 * 64 - 1)];
     if (copy_now) {
+      for (int idx = tid; idx < 8 * 64; idx += NT) reinterpret_cast<uint4*>(s_lds + PK_QOPS_BASE)[idx] = ops[idx];
+    } else {
 #pragma unroll
-      for (int k = 0; k < QC; ++k)
-        if (tid + k * NT < 8 * 64) reinterpret_cast<uint4*>(s_lds + PK_QOPS_BASE)[tid + k * NT] = qcp[k];
+      for (int k = 0; k < QC; ++k) qcp[k] = ops[min(tid + k * NT, 8 * 64 - 1)];
     }
     if constexpr (SLOTS == 2) {
 #pragma unroll
@@ -1302,7 +1309,8 @@ __global__ void __launch_bounds__(WAVES * 64, OCC) packed_decode_kernel(DecodeAr
 #pragma unroll
     for (int k = 0; k < HL; ++k) cf[k] = __uint_as_float(ops[12 * 64 + (HL * g + k) * SLOTS].x);
   };
-  if constexpr (!INPREP) operands(a.qops + (static_cast<int64_t>(b) * a.hkv + kvh) * (FQ_QOPS * 64), false);
+  const uint4* const gops = a.qops + (static_cast<int64_t>(b) * a.hkv + kvh) * (FQ_QOPS * 64);
+  if constexpr (!INPREP && ONLY) operands(gops, false);
 
   PkPage<BITS> ring[RING];
   if (my_pages > 0) {
@@ -1330,14 +1338,25 @@ __global__ void __launch_bounds__(WAVES * 64, OCC) packed_decode_kernel(DecodeAr
 
   if constexpr (INPREP) {
     uint4* const s_ops = reinterpret_cast<uint4*>(s_lds + PK_PREP_OPS);
-    prepare_group<SLOTS, PK_PREP_GM>(a, kvh, b, 0, G, tid, reinterpret_cast<float*>(s_lds + PK_CODE_BASE), s_ops,
-                                     false, pin);
+    prepare_group<SLOTS, PK_PREP_GM, APP>(a, kvh, b, 0, G, tid, reinterpret_cast<float*>(s_lds + PK_CODE_BASE),
+                                          s_ops, false, pin);
     __syncthreads();
     operands(s_ops, true);
-  } else {
+    if constexpr (APP) {
+      // A page requested before the append wrote the new token's record is
+      // requested again (the barrier above made those stores visible).
+      const int64_t nslot = a.slots[b];
+#pragma unroll
+      for (int k = 0; k < PRO; ++k)
+        if (k < my_pages && nslot >= 0 && __builtin_amdgcn_readlane(bt_cur, k) == static_cast<int>(nslot >> 4))
+          pk_load(a, rec_of(bt_cur, k), n, lo, gptr, sgn_base, ring[k]);
+    }
+  } else if constexpr (ONLY) {
 #pragma unroll
     for (int k = 0; k < QC; ++k)
       if (tid + k * NT < 8 * 64) reinterpret_cast<uint4*>(s_lds + PK_QOPS_BASE)[tid + k * NT] = qcp[k];
+  } else {
+    operands(gops, true);
   }
 
   // ---- tables: stage the 256 entries once, then fan out conflict-free copies
@@ -1576,7 +1595,8 @@ __global__ void __launch_bounds__(WAVES * 64, OCC) packed_decode_kernel(DecodeAr
   for (int c0 = 0; c0 < my_pages; c0 += 64) {
     const int cn = min(64, my_pages - c0);
     if (c0 > 0) {
-      bt_cur = bt_chunk(c0);
+      pg_cur = page_of(chunk_lane(c0));
+      bt_cur = bt[pg_cur];
 #pragma unroll
       for (int k = 0; k < PRO; ++k) pk_load(a, rec_of(bt_cur, min(k, cn - 1)), n, lo, gptr, sgn_base, ring[k]);
     }
@@ -1585,7 +1605,7 @@ __global__ void __launch_bounds__(WAVES * 64, OCC) packed_decode_kernel(DecodeAr
       for (int k = 0; k < RING; ++k) {
         const int ik = i + k;
         pk_load(a, rec_of(bt_cur, min(ik + RING - 1, cn - 1)), n, lo, gptr, sgn_base, ring[(k + RING - 1) % RING]);
-        if (ik < cn) process(ring[k], p0 + (c0 + ik) * WAVES);
+        if (ik < cn) process(ring[k], __builtin_amdgcn_readlane(pg_cur, ik));
       }
     }
   }
@@ -1749,11 +1769,18 @@ int launch_decode(void* stream, const fq_quantizer& q, const fq_cache& c, const 
   const int slots = (!valu && !v1) ? (a.group <= 4 ? 4 : a.group <= 8 ? 2 : 0) : 0;
   dim3 grid(num_splits, c.num_kv_heads, batch);
   const bool only = slots > 0 && num_splits == 1 && std::getenv("FQ_DECODE_UNFUSED") == nullptr;
-  if (only && !app && phase == DECODE_ALL) {
+  if (only && phase == DECODE_ALL) {
     // one work-group per (KV head, sequence) does everything in one launch
-#define FQ_FUSED(BITS, SL, DT)                                                                                \
-  hipLaunchKernelGGL((packed_decode_kernel<BITS, SL, pkf_waves(BITS), PKF_RING, PKF_OCC, DT>), grid,          \
-                     dim3(pkf_waves(BITS) * 64), 0, st, a)
+    // (appending the newest token first, when asked)
+#define FQ_FUSED(BITS, SL, DT)                                                                                   \
+  do {                                                                                                           \
+    if (app)                                                                                                     \
+      hipLaunchKernelGGL((packed_decode_kernel<BITS, SL, pkf_waves(BITS), PKF_RING, PKF_OCC, DT, true>), grid,   \
+                         dim3(pkf_waves(BITS) * 64), 0, st, a);                                                  \
+    else                                                                                                         \
+      hipLaunchKernelGGL((packed_decode_kernel<BITS, SL, pkf_waves(BITS), PKF_RING, PKF_OCC, DT, false>), grid,  \
+                         dim3(pkf_waves(BITS) * 64), 0, st, a);                                                  \
+  } while (0)
     const bool bf = q_dtype == FQ_BF16;
     if (q.bits == 4 && slots == 4) { if (bf) FQ_FUSED(4, 4, FQ_BF16); else FQ_FUSED(4, 4, FQ_F32); }
     else if (q.bits == 4) { if (bf) FQ_FUSED(4, 2, FQ_BF16); else FQ_FUSED(4, 2, FQ_F32); }
@@ -1763,14 +1790,13 @@ int launch_decode(void* stream, const fq_quantizer& q, const fq_cache& c, const 
     return static_cast<int>(hipGetLastError());
   }
   // query preparation and merge: one work-group per query head when there are few
-  // (KV head, sequence) pairs, else one per pair; one more per pair appends its
+  // (KV head, sequence) pairs, else one per pair; the pair's first one appends its
   // newest token
   const dim3 pgrid(c.num_kv_heads, batch, batch * c.num_kv_heads >= 128 ? 1 : a.group);
-  const dim3 agrid(pgrid.x, pgrid.y, pgrid.z + (app ? 1 : 0));
   if (phase != DECODE_ATTEND) {
 #define FQ_PREP(DT, SL)                                                                                  \
   do {                                                                                                   \
-    if (app) hipLaunchKernelGGL((prepare_queries_kernel<DT, SL, 1>), agrid, dim3(PQ_THREADS), 0, st, a); \
+    if (app) hipLaunchKernelGGL((prepare_queries_kernel<DT, SL, 1>), pgrid, dim3(PQ_THREADS), 0, st, a); \
     else hipLaunchKernelGGL((prepare_queries_kernel<DT, SL, 0>), pgrid, dim3(PQ_THREADS), 0, st, a);     \
   } while (0)
   if (q_dtype == FQ_BF16) {
