@@ -1,17 +1,20 @@
-// fq_compress on gfx950: one 128-d K or V vector per lane.
+// fq_compress on gfx950: 128-d K and V vectors into the paged cache.
 //
 // "FlashQuant" page, "TurboQuant" steps 1-4 (norm, rotation, Lloyd-Max
 // quantization, packing + fp32 norm) and "QJL" (residual signs for keys);
 // "TurboQuant" blog, "Couche 1" (randomized Walsh-Hadamard).
 //
-// Each lane owns one vector, so the norm, the 15 boundary compares, the
-// nibble packing and the QJL sign packing are all lane-local (no cross-lane
-// traffic). The dense rotation is an outer product over k: the lane streams
-// its input 8 coordinates at a time and adds x_k * (column k of Pi) into 128
-// accumulators; column k of Pi is row k of Pi^T, a wave-uniform 512-byte row
-// read through the scalar cache, so every FMA takes one operand from an SGPR.
-// The QJL projection p = S r is 128 row dot products with r held in registers.
-// The Walsh-Hadamard variant runs its 7 butterfly stages in registers.
+// Kernels:
+//  * compress_mfma_kernel (large inputs) / compress_split_kernel (up to 1024 tiles):
+//    32 vectors per wave tile; the rotation Y^T = Pi X^T and the QJL projection
+//    P^T = S R^T run on the matrix cores (Pi as bf16 hi + lo, S and the residual as
+//    fp16 hi + lo), with Pi's rows fed in an order that leaves 64 consecutive
+//    coordinates of one vector in each lane, so the norm, the boundary search, the
+//    packing, gamma and the sign packing are lane-local.
+//  * compress_direct_kernel, compress_lane_kernel (FQ_COMPRESS_KERNEL=direct /
+//    lane): one wave per tile straight from the prepared fragments, and one
+//    vector per lane on the vector ALU (dense rotation as an outer product over
+//    rows of Pi^T from the scalar cache, or the Walsh-Hadamard butterflies).
 #include <hip/hip_runtime.h>
 
 #include <cstdint>

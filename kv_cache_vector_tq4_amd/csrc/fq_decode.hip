@@ -1,19 +1,23 @@
-// fq_decode_attention on gfx950: paged split-K decode over the compressed cache.
+// fq_decode_attention / fq_decode_step on gfx950: paged decode attention read
+// straight from the compressed cache.
 //
 // "FlashQuant" page, "架构设计" (paged decode with split-K FlashDecoding over
-// the compressed pages) and "QJL" (corrected key inner product).
+// the compressed pages) and "QJL" (corrected key inner product); "TurboQuant"
+// steps 1-4 for the newest token a decode step appends.
 //
-// Three launches per call:
-//  1. rotate_queries: q~ = Pi q and q_s = S q~ for every (sequence, query head),
-//     stored in the workspace as [b][query head][coordinate]; a query head's row
-//     is read wave-uniformly through the scalar cache by kernel 2.
-//  2. split_attention: one work-group per (split, KV head, sequence) covering all
-//     G query heads of that KV head. Tokens are scored one per lane straight from
-//     the packed codes (level lookup in LDS, q~ / q_s from the scalar cache),
-//     softmax statistics are kept online per 256-token sub-chunk, and values are
-//     accumulated in the rotated frame, one coordinate per lane.
-//  3. merge_unrotate: log-sum-exp merge of the splits in split order, then
-//     o = Pi^T o_rot once per query head.
+// Kernels:
+//  * packed_decode_kernel: one work-group per (split, KV head, sequence) covering
+//    all G <= 8 query heads of the KV head; scores and value products on the
+//    matrix cores from the packed codes (dequantized through LDS tables), online
+//    softmax in log2 units, values accumulated in the rotated frame. When each
+//    (sequence, KV head) is one split it also prepares its queries (q~ = Pi q,
+//    q_s = S q~), optionally compresses the newest K and V into the cache first,
+//    and writes o = Pi^T o_rot itself: one launch per call.
+//  * prepare_queries_kernel: the query preparation (and the append) for the split
+//    path and for fq_step_prepare; merge_unrotate_kernel: log-sum-exp merge of the
+//    splits in split order, then o = Pi^T o_rot.
+//  * split_mfma4_kernel / split_attention_kernel: groups of 16 query heads (4-bit
+//    matrix-core / vector ALU), and the vector-ALU cross-check.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
