@@ -234,6 +234,27 @@ def compress_layer_measure(index, rot, reps, stream):
             "frac_hbm": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
 
 
+def decompress_measure(qz, cache, slots, reps, stream):
+    """fq_decompress of a layer's whole context (K and V, bf16 out), timed with events."""
+    import torch
+
+    from kv_cache_vector_tq4_amd import fq
+
+    T, Hkv, d = slots.numel(), cache.num_kv_heads, cache.head_dim
+    ko = torch.empty((T, Hkv, d), dtype=torch.bfloat16, device=slots.device)
+    vo = torch.empty_like(ko)
+    fq.decompress(qz, cache, slots, k_out=ko, v_out=vo)
+    ms = _events_ms(lambda: fq.decompress(qz, cache, slots, k_out=ko, v_out=vo), reps, stream)
+    nvec = 2 * int((slots >= 0).sum().item()) * Hkv
+    nbytes = nvec * (d * cache.bits // 8 + 4 + 2 * d) + 8 * T
+    del ko, vo
+    return {"what": "fq_decompress of one layer's context, K and V, bf16 out (MSE reconstruction n Pi^T c)",
+            "vectors": nvec, "ms": ms, "mvec_per_s": nvec / (ms * 1e-3) / 1e6,
+            "algorithmic_bytes": nbytes, "achieved_gbs": nbytes / (ms * 1e-3) / 1e9,
+            "frac_hbm": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "bytes_per_vector": "codes %d + norm 4 in, %d out" % (d * cache.bits // 8, 2 * d)}
+
+
 def attention_cosines(q, k, v, lens, kv_rows, out, seqs):
     """Cosine of the decode outputs against exact softmax attention over the
     uncompressed (bf16) K and V, per (sequence, query head), for sampled sequences.
@@ -341,6 +362,7 @@ def main():
         caches.append(cache)
         del k, v
     torch.cuda.synchronize()
+    decomp = decompress_measure(qz, caches[0], slots_all, 5, stream)
     ws_bytes = fq.workspace_bytes(B, Hq, Hkv, d, 128, max_len, splits)
     # one workspace per layer: each keeps its layer's prepared queries, so the
     # attention launches can also be replayed on their own
@@ -550,6 +572,7 @@ def main():
             "algorithmic_bytes_per_launch": comp_bytes,
             "mfma_util": measured_mfma_util(),
         },
+        "decompress": decomp,
         "accuracy": dict(accuracy, what="cosine of decode outputs vs exact fp32 softmax attention over the "
                          "uncompressed bf16 K/V, layer 0, sequences 0 / 7 / 15 / 31, all 32 query heads"),
     }

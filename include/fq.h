@@ -182,6 +182,28 @@ fq_status fq_compress(void* stream, const fq_quantizer* quant, const fq_cache* c
                       float* debug_y, float* debug_p);
 
 /*
+ * fq_decompress -- rebuild dense K and V vectors from the paged cache ("FlashQuant"
+ * page, "架构设计": the decompress kernel; "TurboQuant" steps 2-4 read backwards).
+ *
+ * For each token t < num_tokens with slot_mapping[t] >= 0 and KV head h:
+ *   x_hat = n * Pi^T level[idx]   (the MSE reconstruction of the stored vector;
+ *   for keys the QJL bits, which correct inner products with the key, are not applied)
+ * written at t * token_stride + h * head_stride + j (j < d) of k_out / v_out.
+ *
+ *  slot_mapping  device int64 [num_tokens]; negative = that token's rows are not written.
+ *  out_dtype     FQ_F32 or FQ_BF16 (rounded to nearest even).
+ *  k_out, v_out  device; either may be NULL to skip that side. Every vector starts
+ *                on a 16-byte boundary (base pointers and both strides, in bytes,
+ *                multiples of 16).
+ * The products run on the matrix cores with Pi and n * level split into bf16 hi + lo
+ * (about 16 significant bits): fp32 outputs are within 1e-5 * n of the exact value.
+ * Errors: FQ_ERR_INVALID_ARG, FQ_ERR_UNSUPPORTED, FQ_ERR_HIP.
+ */
+fq_status fq_decompress(void* stream, const fq_quantizer* quant, const fq_cache* cache,
+                        const int64_t* slot_mapping, int64_t num_tokens, int out_dtype, void* k_out,
+                        void* v_out, int64_t token_stride, int64_t head_stride);
+
+/*
  * Split count the decode chooses when called with num_splits = 0: enough
  * (batch, KV head, split) work-groups to fill the GPU, each covering at least
  * 256 tokens, at most 64 splits. Host only.

@@ -129,6 +129,30 @@ fq_status fq_compress(void* stream, const fq_quantizer* quant, const fq_cache* c
   return e == 0 ? FQ_OK : FQ_ERR_HIP;
 }
 
+fq_status fq_decompress(void* stream, const fq_quantizer* quant, const fq_cache* cache,
+                        const int64_t* slot_mapping, int64_t num_tokens, int out_dtype, void* k_out,
+                        void* v_out, int64_t token_stride, int64_t head_stride) {
+  fq_status st = check_quantizer(quant);
+  if (st != FQ_OK) return st;
+  st = check_cache(cache, quant);
+  if (st != FQ_OK) return st;
+  if (out_dtype != FQ_F32 && out_dtype != FQ_BF16) return FQ_ERR_INVALID_ARG;
+  if (num_tokens < 0 || token_stride < 0 || head_stride < 0) return FQ_ERR_INVALID_ARG;
+  if (num_tokens == 0 || (!k_out && !v_out)) return FQ_OK;
+  if (!slot_mapping || !aligned(slot_mapping, 8)) return FQ_ERR_INVALID_ARG;
+  // every output vector starts on a 16-byte boundary (16-byte stores)
+  const int64_t ea = out_dtype == FQ_F32 ? 4 : 2;
+  for (const void* p : {static_cast<const void*>(k_out), static_cast<const void*>(v_out)})
+    if (p && !aligned(p, 16)) return FQ_ERR_INVALID_ARG;
+  if ((token_stride * ea) % 16 != 0 || (head_stride * ea) % 16 != 0) return FQ_ERR_INVALID_ARG;
+  if (num_tokens > 1 && token_stride == 0) return FQ_ERR_INVALID_ARG;
+  if (cache->num_kv_heads > 1 && head_stride == 0) return FQ_ERR_INVALID_ARG;
+  if (num_tokens * cache->num_kv_heads > (int64_t{1} << 31) - 1) return FQ_ERR_UNSUPPORTED;
+  int e = fq::launch_decompress(stream, *quant, *cache, slot_mapping, num_tokens, out_dtype, k_out, v_out,
+                                token_stride, head_stride);
+  return e == 0 ? FQ_OK : FQ_ERR_HIP;
+}
+
 int fq_decode_auto_splits(int batch, int num_kv_heads, int max_seq_len) {
   if (batch <= 0 || num_kv_heads <= 0 || max_seq_len < 0) return 1;
   return fq::auto_splits(batch, num_kv_heads, max_seq_len);

@@ -62,4 +62,8 @@ int launch_decode(void* stream, const fq_quantizer& q, const fq_cache& c, const 
                   int num_splits, float scale, void* workspace, float* out,
                   const AppendIn* app, int phase);
 
+int launch_decompress(void* stream, const fq_quantizer& q, const fq_cache& c, const int64_t* slot_mapping,
+                      int64_t num_tokens, int out_dtype, void* k_out, void* v_out, int64_t token_stride,
+                      int64_t head_stride);
+
 }  // namespace fq

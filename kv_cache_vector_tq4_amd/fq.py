@@ -88,6 +88,9 @@ EXPORTS = {
                                       ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p,
                                       ctypes.c_int, ctypes.c_int, ctypes.c_float, ctypes.c_void_p,
                                       ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
+    "fq_decompress": (ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(QuantizerT), ctypes.POINTER(CacheT),
+                                     ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+                                     ctypes.c_int64, ctypes.c_int64]),
     "fq_step_prepare": (ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(QuantizerT), ctypes.POINTER(CacheT),
                                        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int64,
                                        ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
@@ -381,3 +384,29 @@ def step_attend(quant, cache, batch, num_q_heads, block_tables, seq_lens, max_se
                               workspace.numel() * workspace.element_size(), _ptr(out))
     _check(st, "fq_step_attend")
     return out
+
+
+def decompress(quant, cache, slot_mapping, dtype=None, k_out=None, v_out=None, which="kv", stream=None):
+    """fq_decompress: the MSE reconstructions of the tokens at slot_mapping [T] as [T, Hkv, d] tensors.
+
+    Returns (k_hat, v_hat); a side not in `which` is None. dtype: torch.float32 (default) or bfloat16.
+    """
+    import torch
+
+    T = slot_mapping.numel()
+    assert slot_mapping.dtype == torch.int64 and slot_mapping.is_contiguous()
+    dtype = torch.float32 if dtype is None else dtype
+    shape = (T, cache.num_kv_heads, cache.head_dim)
+    if "k" in which and k_out is None:
+        k_out = torch.empty(shape, dtype=dtype, device=slot_mapping.device)
+    if "v" in which and v_out is None:
+        v_out = torch.empty(shape, dtype=dtype, device=slot_mapping.device)
+    ref = k_out if k_out is not None else v_out
+    for x in (k_out, v_out):
+        if x is not None:
+            assert x.shape == shape and x.stride(2) == 1 and x.dtype == ref.dtype and x.stride() == ref.stride()
+    st = lib().fq_decompress(_stream(stream), ctypes.byref(quant.struct), ctypes.byref(cache.struct),
+                             _ptr(slot_mapping), T, _dtype_code(ref), _ptr(k_out), _ptr(v_out), ref.stride(0),
+                             ref.stride(1))
+    _check(st, "fq_decompress")
+    return k_out, v_out

@@ -1,0 +1,127 @@
+"""GPU parity of fq_decompress against the oracle's reconstruction (through the C ABI).
+
+The oracle's compressed bytes are uploaded and rebuilt by the GPU; the reference is
+oracle.quantize.reconstruct (x_hat = n Pi^T level[idx], float64) of the same bytes.
+Tolerances (from the arithmetic: Pi and n level split into bf16 hi + lo, three
+products, fp32 accumulate): fp32 output within 1e-5 n per vector; bf16 output within
+one bf16 rounding (2^-8 relative to the vector's largest coordinate) more.
+"""
+import numpy as np
+import pytest
+import torch
+
+from kv_cache_vector_tq4_amd import fq, synth
+from oracle import quantize
+from tests import parity
+
+pytestmark = pytest.mark.gpu
+
+
+def _oracle_rebuild(host, slots, oq, name):
+    """[T, Hkv, d] float64 reconstructions of the records at slots (rows of skipped slots: nan)."""
+    Hkv = host[name + "_norm"].shape[1]
+    out = np.full((len(slots), Hkv, 128), np.nan)
+    for t, s in enumerate(slots):
+        if s < 0:
+            continue
+        blk, off = s // 16, s % 16
+        idx = quantize.unpack_codes(host[name + "_codes"][blk, :, off], oq["bits"], 128)
+        out[t] = quantize.reconstruct(host[name + "_norm"][blk, :, off], idx, oq["levels"], oq["pi"])
+    return out
+
+
+def _check(gpu, ref, norms, bf16):
+    g = gpu.float().cpu().numpy().astype(np.float64)
+    live = ~np.isnan(ref[:, 0, 0])
+    err = np.abs(g[live] - ref[live])
+    tol = 1e-5 * norms[live][..., None]
+    if bf16:
+        tol = tol + 2.0 ** -8 * np.max(np.abs(ref[live]), axis=2, keepdims=True)
+    worst = float(np.max(err / tol)) if err.size else 0.0
+    assert worst <= 1.0, worst
+    return worst
+
+
+def _norms(host, slots, name):
+    Hkv = host[name + "_norm"].shape[1]
+    n = np.zeros((len(slots), Hkv))
+    for t, s in enumerate(slots):
+        if s >= 0:
+            n[t] = host[name + "_norm"][s // 16, :, s % 16]
+    return n
+
+
+@pytest.mark.parametrize("out", ["f32", "bf16"])
+@pytest.mark.parametrize("bits", [4, 2])
+@pytest.mark.parametrize("rot", [fq.ROT_HAAR, fq.ROT_WHT])
+def test_decompress_matches_oracle(gpu_lib, bits, rot, out):
+    w, inp = parity.small_workload(3, 6, 3, [5, 333, 100], 336, bits=bits, seed=31)
+    oq = parity.oracle_quantizer(bits, rot=rot)
+    qz = fq.Quantizer(bits, 128, rot, 1, 2, 128)
+    host = parity.oracle_cache(inp, oq)
+    cache = fq.PagedCache(inp["num_blocks"], 3, 128, bits, 128)
+    parity.upload_cache(host, cache)
+    slots = inp["slot_mapping"]  # [B * cap], -1 past each sequence's end
+    st = torch.from_numpy(slots).cuda()
+    dt = torch.bfloat16 if out == "bf16" else torch.float32
+    sentinel = 7.0
+    ko = torch.full((len(slots), 3, 128), sentinel, dtype=dt, device="cuda")
+    vo = torch.full_like(ko, sentinel)
+    fq.decompress(qz, cache, st, k_out=ko, v_out=vo)
+    torch.cuda.synchronize()
+    for name, g in (("k", ko), ("v", vo)):
+        ref = _oracle_rebuild(host, slots, oq, name)
+        print(name, "worst err / tol", _check(g, ref, _norms(host, slots, name), out == "bf16"))
+        # rows of skipped tokens are not written
+        assert torch.all(g[torch.from_numpy(slots < 0).cuda()] == sentinel)
+
+
+def test_decompress_strided_one_side_and_round_trip(gpu_lib):
+    """Outputs as views into wider rows; V only; the rebuilt vectors of GPU-compressed
+    inputs are close to the inputs (cosine >= 0.98, the 4-bit reconstruction the
+    pages claim at >= 0.95)."""
+    w, inp = parity.small_workload(2, 8, 2, [77, 200], 208, seed=37)
+    t = parity.torch_inputs(inp, "bf16")
+    oq = parity.oracle_quantizer(4)
+    qz = fq.Quantizer(4, 128, fq.ROT_HAAR, 1, 2, 128)
+    cache = fq.PagedCache(inp["num_blocks"], 2, 128, 4, 128)
+    fq.compress(qz, cache, t["k"], t["v"], t["slots"])
+    T = t["slots"].numel()
+    wide = torch.zeros((T, 3, 128), dtype=torch.float32, device="cuda")  # head stride 128, token stride 384
+    view = wide[:, :2, :]
+    k_hat, v_hat = fq.decompress(qz, cache, t["slots"], v_out=view, which="v")
+    assert k_hat is None
+    torch.cuda.synchronize()
+    host = parity.cache_to_host(cache)
+    slots = inp["slot_mapping"]
+    ref = _oracle_rebuild(host, slots, oq, "v")
+    _check(view, ref, _norms(host, slots, "v"), False)
+    assert torch.all(wide[:, 2, :] == 0)
+    live = torch.from_numpy(slots >= 0).cuda()
+    x = t["v"].float()[live]
+    xh = view[live]
+    cos = torch.nn.functional.cosine_similarity(x.reshape(-1, 128), xh.reshape(-1, 128), dim=1)
+    print("round-trip cosine min %.4f mean %.4f" % (cos.min().item(), cos.mean().item()))
+    assert cos.min().item() >= 0.98
+
+
+def test_decompress_full_size_b32_sampled(gpu_lib):
+    """The batch-32 8B-shaped layer (115 833 tokens x 8 heads, K and V, bf16 output) in
+    the configuration the benchmark times; 512 sampled tokens against the oracle's
+    reconstruction of the GPU-written bytes."""
+    w = synth.workload(2)
+    inp = synth.layer_inputs(w)
+    t = parity.torch_inputs(inp, "bf16")
+    oq = parity.oracle_quantizer(4)
+    qz = fq.Quantizer(4, 128, fq.ROT_HAAR, 1, 2, 128)
+    cache = fq.PagedCache(inp["num_blocks"], 8, 128, 4, 128)
+    fq.compress(qz, cache, t["k"], t["v"], t["slots"])
+    ko, vo = fq.decompress(qz, cache, t["slots"], dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    host = parity.cache_to_host(cache)
+    rs = np.random.default_rng(5)
+    tok = np.sort(rs.choice(len(inp["slot_mapping"]), size=512, replace=False))
+    slots = inp["slot_mapping"][tok]
+    for name, g in (("k", ko), ("v", vo)):
+        ref = _oracle_rebuild(host, slots, oq, name)
+        print(name, "worst err / tol", _check(g[torch.from_numpy(tok).cuda()], ref, _norms(host, slots, name), True))
