@@ -235,7 +235,7 @@ def compress_layer_measure(index, rot, reps, stream):
 
 
 def decompress_measure(qz, cache, slots, reps, stream):
-    """fq_decompress of a layer's whole context (K and V, bf16 out), timed with events."""
+    """fq_decompress of a layer's stored tokens (K and V, bf16 out), timed with events."""
     import torch
 
     from kv_cache_vector_tq4_amd import fq
@@ -248,7 +248,7 @@ def decompress_measure(qz, cache, slots, reps, stream):
     nvec = 2 * int((slots >= 0).sum().item()) * Hkv
     nbytes = nvec * (d * cache.bits // 8 + 4 + 2 * d) + 8 * T
     del ko, vo
-    return {"what": "fq_decompress of one layer's context, K and V, bf16 out (MSE reconstruction n Pi^T c)",
+    return {"what": "fq_decompress of one layer's stored tokens, K and V, bf16 out (MSE reconstruction n Pi^T c)",
             "vectors": nvec, "ms": ms, "mvec_per_s": nvec / (ms * 1e-3) / 1e6,
             "algorithmic_bytes": nbytes, "achieved_gbs": nbytes / (ms * 1e-3) / 1e9,
             "frac_hbm": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
@@ -362,7 +362,7 @@ def main():
         caches.append(cache)
         del k, v
     torch.cuda.synchronize()
-    decomp = decompress_measure(qz, caches[0], slots_all, 5, stream)
+    decomp = decompress_measure(qz, caches[0], slots_all[slots_all >= 0].contiguous(), 5, stream)
     ws_bytes = fq.workspace_bytes(B, Hq, Hkv, d, 128, max_len, splits)
     # one workspace per layer: each keeps its layer's prepared queries, so the
     # attention launches can also be replayed on their own

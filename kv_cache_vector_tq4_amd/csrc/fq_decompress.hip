@@ -17,6 +17,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <type_traits>
 
 #include "fq_internal.h"
 
@@ -27,10 +28,12 @@ constexpr int D = FQ_HEAD_DIM;
 constexpr int DQ_WAVES = 4;           // waves per work-group (two work-groups per CU)
 constexpr int DQ_VEC = 32;            // vectors per wave tile
 constexpr int DQ_FRAG = 8 * 4 * 64;   // A fragments: 8 k-steps x 4 row tiles x 64 lanes (16 B each)
-constexpr int DQ_COPIES = 4;          // copies of the level table (copy = lane % 4)
+constexpr int DQ_STAGE = 2048;        // bytes of LDS per wave for re-ordering its stores
 
 typedef __bf16 b8 __attribute__((ext_vector_type(8)));
 typedef float f16v __attribute__((ext_vector_type(16)));
+typedef uint32_t u4v __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(1))) u4v g_u4v;  // in global memory (not flat)
 
 struct DecompressArgs {
   const uint8_t* codes[2];  // K, V code arrays of the cache
@@ -42,6 +45,10 @@ struct DecompressArgs {
   int64_t ntok, tstride, hstride;
   int hkv, out_bf16;
 };
+
+// Target of the stores for vectors that have nothing to write (past the end, or a
+// token without a slot): one 512-byte row per vector of a tile, contents never read.
+__device__ uint4 g_dq_sink[DQ_VEC * 32];
 
 // x = hi + lo with hi, lo bf16 (round to nearest even), as the bit patterns.
 __device__ __forceinline__ void split_bf16x(float x, uint16_t& hi, uint16_t& lo) {
@@ -55,30 +62,32 @@ __device__ __forceinline__ uint32_t pack2(uint16_t a, uint16_t b) {
   return static_cast<uint32_t>(a) | (static_cast<uint32_t>(b) << 16);
 }
 
-// D row rho of row tile T holds output coordinate 64 h + 16 T + 4 j + k, where
+// D row rho of row tile T holds output coordinate 32 T + 16 h + 4 j + k, where
 // rho = 8 j + 4 h + k (the 32x32 accumulator layout: register 4 j + k of lane i is
-// row 8 j + 4 (i / 32) + k).
+// row 8 j + 4 (i / 32) + k): lane (vector, h) holds coordinates 32 T + 16 h .. + 15.
 __device__ __forceinline__ int out_coord(int T, int rho) {
-  return 64 * ((rho >> 2) & 1) + 16 * T + 4 * (rho >> 3) + (rho & 3);
+  return 32 * T + 16 * ((rho >> 2) & 1) + 4 * (rho >> 3) + (rho & 3);
 }
 
 // One work-group stages Pi^T's A fragments, then its waves take 32-vector tiles of
 // one kind (blockIdx.y: 0 K, 1 V) in a grid-stride loop.
-template <int BITS>
+template <int BITS, bool OBF16>
 __global__ void __launch_bounds__(DQ_WAVES * 64, 2) decompress_kernel(DecompressArgs a) {
   // level table entry of code byte x: 4-bit (hi c0 | hi c1, lo c0 | lo c1), 8 B;
   // 2-bit (hi c0 | hi c1, hi c2 | hi c3, lo c0 | lo c1, lo c2 | lo c3), 16 B; the
-  // byte's codes c0.. in coordinate order; at (x * DQ_COPIES + copy) * EB
+  // byte's codes c0.. in coordinate order; at (x * COPIES + copy) * EB (copy = lane % COPIES)
   constexpr int EB = BITS == 4 ? 8 : 16;
+  constexpr int COPIES = BITS == 4 ? 4 : 2;  // 8 KB either way: 80 KB of LDS per work-group
   __shared__ uint4 s_fh[DQ_FRAG], s_fl[DQ_FRAG];  // Pi^T fragments, bf16 hi / lo (64 KB)
-  __shared__ __align__(16) uint8_t s_tab[256 * DQ_COPIES * EB];
+  __shared__ __align__(16) uint8_t s_tab[256 * COPIES * EB];
+  __shared__ __align__(16) uint8_t s_stage[DQ_WAVES * DQ_STAGE];
   const int kind = blockIdx.y;
   if (!a.out[kind]) return;  // uniform over the work-group
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  // fragment f = (k-step s, row tile T), lane i: Pi^T[out_coord(T, i % 32)][16 s + 8 (i / 32) + e], e < 8
+  // fragment f = (k-step s, row tile T), lane i: Pi^T[out_coord(T, i % 32)][64 (i / 32) + 8 s + e], e < 8
   for (int idx = tid; idx < DQ_FRAG; idx += DQ_WAVES * 64) {
     const int f = idx >> 6, i = idx & 63, s = f >> 2, T = f & 3;
-    const float4* src = reinterpret_cast<const float4*>(a.pit + out_coord(T, i & 31) * D + 16 * s + 8 * (i >> 5));
+    const float4* src = reinterpret_cast<const float4*>(a.pit + out_coord(T, i & 31) * D + 64 * (i >> 5) + 8 * s);
     const float4 x0 = src[0], x1 = src[1];
     const float xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
     uint16_t h[8], l[8];
@@ -87,8 +96,8 @@ __global__ void __launch_bounds__(DQ_WAVES * 64, 2) decompress_kernel(Decompress
     s_fh[idx] = make_uint4(pack2(h[0], h[1]), pack2(h[2], h[3]), pack2(h[4], h[5]), pack2(h[6], h[7]));
     s_fl[idx] = make_uint4(pack2(l[0], l[1]), pack2(l[2], l[3]), pack2(l[4], l[5]), pack2(l[6], l[7]));
   }
-  for (int idx = tid; idx < 256 * DQ_COPIES; idx += DQ_WAVES * 64) {
-    const uint32_t x = static_cast<uint32_t>(idx) / DQ_COPIES;
+  for (int idx = tid; idx < 256 * COPIES; idx += DQ_WAVES * 64) {
+    const uint32_t x = static_cast<uint32_t>(idx) / COPIES;
     constexpr int PER = 8 / BITS;  // codes per byte
     uint16_t hi[4], lo[4];
 #pragma unroll
@@ -100,126 +109,220 @@ __global__ void __launch_bounds__(DQ_WAVES * 64, 2) decompress_kernel(Decompress
           make_uint4(pack2(hi[0], hi[1]), pack2(hi[2], hi[3]), pack2(lo[0], lo[1]), pack2(lo[2], lo[3]));
   }
   __syncthreads();
-  const uint32_t copy = static_cast<uint32_t>(lane % DQ_COPIES) * EB;
+  const uint32_t copy = static_cast<uint32_t>(lane % COPIES) * EB;
 
   constexpr int CB = D * BITS / 8;  // code bytes per vector
+  constexpr int HW = CB / 8;        // 32-bit words of code per lane (its k half)
+  // Stores: per row tile T a vector's coordinates 32 T .. 32 T + 31 are RB contiguous
+  // bytes, written by LPV lanes (16 B each); one store instruction covers VPI vectors,
+  // NR instructions per T cover the tile's 32.
+  constexpr int RB = OBF16 ? 64 : 128, LPV = RB / 16, VPI = 64 / LPV, NR = DQ_VEC / VPI;
+  constexpr int ESZ = OBF16 ? 2 : 4;
   const int64_t nvec = a.ntok * a.hkv;
   const int64_t ntiles = (nvec + DQ_VEC - 1) / DQ_VEC;
   const int v = lane & 31, h = lane >> 5;  // the lane's vector in the tile; k-group / output half
-  // The lane's vector of a tile: token t, head hd (past the end: vector 0, not stored).
-  struct Vec {
-    int64_t t;
-    int hd;
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * DQ_WAVES;
+  const int64_t first = static_cast<int64_t>(blockIdx.x) * DQ_WAVES + wave;
+  // this wave's tiles: first + k stride, k < mine (past the end: its first tile again)
+  const int64_t mine = first < ntiles ? (ntiles - first + stride - 1) / stride : 0;
+  if (mine == 0) return;  // uniform over the wave; no barrier follows
+
+  // One tile's pipeline stage: the lane's vector (token, head), its slot, and its
+  // record's codes for coordinates 64 h .. 64 h + 63 plus the norm.
+  struct Stage {
+    uint32_t t, hd;
     bool valid;
+    int64_t slot;
+    uint32_t cw[HW];
+    float nrm;
   };
-  auto locate = [&](int64_t tile) {
-    Vec r;
-    const int64_t vid = tile * DQ_VEC + v;
-    r.valid = vid < nvec;
+  auto locate = [&](Stage& x, int64_t k) {
+    const int64_t vid = (first + (k < mine ? k : 0) * stride) * DQ_VEC + v;
+    x.valid = vid < nvec;
     // vectors per launch < 2^31 (checked on the host): 32-bit division
-    const uint32_t vl = r.valid ? static_cast<uint32_t>(vid) : 0u;
-    r.t = vl / static_cast<uint32_t>(a.hkv);
-    r.hd = static_cast<int>(vl - static_cast<uint32_t>(r.t) * static_cast<uint32_t>(a.hkv));
-    return r;
+    const uint32_t vl = x.valid ? static_cast<uint32_t>(vid) : 0u;
+    x.t = vl / static_cast<uint32_t>(a.hkv);
+    x.hd = vl - x.t * static_cast<uint32_t>(a.hkv);
+    x.slot = a.slots[x.t];
   };
-  // Its record's codes and norm (skipped tokens read record 0, never stored).
-  uint32_t cw[CB / 4], cwn[CB / 4];
-  float nrm = 0.f, nrmn = 0.f;
-  auto fetch = [&](const Vec& x, int64_t slot, uint32_t (&w)[CB / 4], float& nv) {
-    const int64_t sl = slot >= 0 ? slot : 0;
+  auto fetch = [&](Stage& x) {  // skipped tokens read record 0, never stored
+    const int64_t sl = x.slot >= 0 ? x.slot : 0;
     const int64_t rec = ((sl >> 4) * a.hkv + x.hd) * FQ_BLOCK + (sl & 15);
-    nv = a.norm[kind][rec];
-    const uint4* cp = reinterpret_cast<const uint4*>(a.codes[kind] + rec * CB);
+    x.nrm = a.norm[kind][rec];
+    const uint4* cp = reinterpret_cast<const uint4*>(a.codes[kind] + rec * CB + h * (CB / 2));
 #pragma unroll
-    for (int q = 0; q < CB / 16; ++q) {
+    for (int q = 0; q < HW / 4; ++q) {
       const uint4 u = cp[q];
-      w[4 * q] = u.x; w[4 * q + 1] = u.y; w[4 * q + 2] = u.z; w[4 * q + 3] = u.w;
+      x.cw[4 * q] = u.x; x.cw[4 * q + 1] = u.y; x.cw[4 * q + 2] = u.z; x.cw[4 * q + 3] = u.w;
     }
   };
-  // Two-stage pipeline: the next tile's codes and the slot of the one after are
-  // requested before the current tile's products.
-  const int64_t stride = static_cast<int64_t>(gridDim.x) * DQ_WAVES;
-  int64_t tile = static_cast<int64_t>(blockIdx.x) * DQ_WAVES + wave;
-  Vec cur = locate(tile < ntiles ? tile : 0);
-  int64_t slot = a.slots[cur.t];
-  fetch(cur, slot, cw, nrm);
-  Vec nxt = locate(tile + stride < ntiles ? tile + stride : 0);
-  int64_t slotn = a.slots[nxt.t];
-  for (; tile < ntiles; tile += stride) {
-    if (tile + stride < ntiles) fetch(nxt, slotn, cwn, nrmn);
-    const Vec nn = locate(tile + 2 * stride < ntiles ? tile + 2 * stride : 0);
-    const int64_t slotnn = a.slots[nn.t];
+  // The previous tile's output, re-ordered through this wave's LDS stage so that each
+  // store instruction writes whole RB-byte runs of rows, and stored at the start of the
+  // next tile's turn (after the first turn every turn issues the same memory
+  // operations in the same order; vectors with nothing to write use g_dq_sink rows).
+  uint8_t* const stg = s_stage + wave * DQ_STAGE;
+  u4v pend[4 * NR];
+  uint64_t prow[NR];  // global addresses
+
+  // One turn, tile k in X (codes requested a turn ago), tile k + 1's slot in Y:
+  // store tile k - 1; request tile k + 1's codes into Y and tile k + 2's slot into X;
+  // rebuild tile k. Each vector memory request is only waited for a turn later.
+  auto turn = [&](Stage& X, Stage& Y, int64_t k, auto STORE) {
+    uint8_t* vrow = reinterpret_cast<uint8_t*>(g_dq_sink) + v * 512;  // this lane's vector's row
+    if (X.valid && X.slot >= 0)
+      vrow = static_cast<uint8_t*>(a.out[kind]) +
+             (static_cast<int64_t>(X.t) * a.tstride + static_cast<int64_t>(X.hd) * a.hstride) * ESZ;
+    uint32_t cw[HW];
+#pragma unroll
+    for (int q = 0; q < HW; ++q) cw[q] = X.cw[q];
+    const float nrm = X.nrm;
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (decltype(STORE)::value) {
+#pragma unroll
+      for (int T = 0; T < 4; ++T)
+#pragma unroll
+        for (int i = 0; i < NR; ++i)
+          *reinterpret_cast<g_u4v*>(prow[i] + RB * T + 16 * (lane % LPV)) = pend[NR * T + i];
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    fetch(Y);
+    locate(X, k + 2);
     f16v acc[4];
 #pragma unroll
     for (int T = 0; T < 4; ++T) acc[T] = f16v{};
-#pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      __builtin_amdgcn_sched_barrier(0);  // one k-step's operands live at a time
-      // B: coordinates 16 s + 8 h .. + 7 of the vector, level[idx] as bf16 hi / lo
-      b8 bh, bl;
-      if constexpr (BITS == 4) {
-        const uint32_t w = cw[2 * s + h];  // code bytes of coordinates 16 s + 8 h ..
-        uint2 e[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-          e[q] = *reinterpret_cast<const uint2*>(s_tab + ((w >> (8 * q)) & 255u) * (DQ_COPIES * EB) + copy);
-        bh = __builtin_bit_cast(b8, make_uint4(e[0].x, e[1].x, e[2].x, e[3].x));
-        bl = __builtin_bit_cast(b8, make_uint4(e[0].y, e[1].y, e[2].y, e[3].y));
-      } else {
-        const uint32_t w = cw[s] >> (16 * h);  // two code bytes of coordinates 16 s + 8 h ..
-        const uint4 e0 = *reinterpret_cast<const uint4*>(s_tab + (w & 255u) * (DQ_COPIES * EB) + copy);
-        const uint4 e1 = *reinterpret_cast<const uint4*>(s_tab + ((w >> 8) & 255u) * (DQ_COPIES * EB) + copy);
-        bh = __builtin_bit_cast(b8, make_uint4(e0.x, e0.y, e1.x, e1.y));
-        bl = __builtin_bit_cast(b8, make_uint4(e0.z, e0.w, e1.z, e1.w));
-      }
-      // the four row tiles' accumulators are independent: each product of a tile is
-      // three instructions after the previous one, not waiting on it
+    // k-step s: B = coordinates 64 h + 8 s .. + 7 of the vector (level[idx] as bf16
+    // hi / lo, from the table), A = the fragments of Pi^T
+    struct Ops {
       b8 ah[4], al[4];
+      uint32_t e[8];  // the table entries: 4-bit four of (hi, lo); 2-bit two of (hi, hi, lo, lo)
+    };
+    auto load_ops = [&](auto ST, Ops& o) {
+      constexpr int st = decltype(ST)::value;
+      if constexpr (BITS == 4) {
+        const uint32_t w = cw[st];  // code bytes of coordinates 64 h + 8 st ..
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const uint2 u = *reinterpret_cast<const uint2*>(s_tab + ((w >> (8 * q)) & 255u) * (COPIES * EB) + copy);
+          o.e[2 * q] = u.x;
+          o.e[2 * q + 1] = u.y;
+        }
+      } else {
+        const uint32_t w = cw[st >> 1] >> (16 * (st & 1));  // two code bytes of coordinates 64 h + 8 st ..
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          const uint4 u = *reinterpret_cast<const uint4*>(s_tab + ((w >> (8 * q)) & 255u) * (COPIES * EB) + copy);
+          o.e[4 * q] = u.x;
+          o.e[4 * q + 1] = u.y;
+          o.e[4 * q + 2] = u.z;
+          o.e[4 * q + 3] = u.w;
+        }
+      }
 #pragma unroll
       for (int T = 0; T < 4; ++T) {
-        ah[T] = __builtin_bit_cast(b8, s_fh[(s * 4 + T) * 64 + lane]);
-        al[T] = __builtin_bit_cast(b8, s_fl[(s * 4 + T) * 64 + lane]);
+        o.ah[T] = __builtin_bit_cast(b8, s_fh[(st * 4 + T) * 64 + lane]);
+        o.al[T] = __builtin_bit_cast(b8, s_fl[(st * 4 + T) * 64 + lane]);
       }
-#pragma unroll
-      for (int T = 0; T < 4; ++T) acc[T] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah[T], bh, acc[T], 0, 0, 0);
-#pragma unroll
-      for (int T = 0; T < 4; ++T) acc[T] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah[T], bl, acc[T], 0, 0, 0);
-#pragma unroll
-      for (int T = 0; T < 4; ++T) acc[T] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al[T], bh, acc[T], 0, 0, 0);
-    }
-    // ---- acc[T][vv] = x_hat[vector v][64 h + 16 T + vv]: 64 consecutive coordinates
-    if (cur.valid && slot >= 0) {
-      const int64_t base = cur.t * a.tstride + static_cast<int64_t>(cur.hd) * a.hstride + 64 * h;
-      if (a.out_bf16) {
-        __bf16* o = static_cast<__bf16*>(a.out[kind]) + base;
-#pragma unroll
-        for (int T = 0; T < 4; ++T)
-#pragma unroll
-          for (int q = 0; q < 2; ++q) {
-            uint16_t w[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) w[e] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(acc[T][8 * q + e] * nrm));
-            *reinterpret_cast<uint4*>(o + 16 * T + 8 * q) =
-                make_uint4(pack2(w[0], w[1]), pack2(w[2], w[3]), pack2(w[4], w[5]), pack2(w[6], w[7]));
-          }
+    };
+    auto products = [&](const Ops& o) {
+      b8 bh, bl;
+      if constexpr (BITS == 4) {
+        bh = __builtin_bit_cast(b8, make_uint4(o.e[0], o.e[2], o.e[4], o.e[6]));
+        bl = __builtin_bit_cast(b8, make_uint4(o.e[1], o.e[3], o.e[5], o.e[7]));
       } else {
-        float* o = static_cast<float*>(a.out[kind]) + base;
+        bh = __builtin_bit_cast(b8, make_uint4(o.e[0], o.e[1], o.e[4], o.e[5]));
+        bl = __builtin_bit_cast(b8, make_uint4(o.e[2], o.e[3], o.e[6], o.e[7]));
+      }
 #pragma unroll
-        for (int T = 0; T < 4; ++T)
+      for (int T = 0; T < 4; ++T) acc[T] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o.ah[T], bh, acc[T], 0, 0, 0);
 #pragma unroll
-          for (int q = 0; q < 4; ++q)
-            *reinterpret_cast<float4*>(o + 16 * T + 4 * q) = make_float4(
-                acc[T][4 * q] * nrm, acc[T][4 * q + 1] * nrm, acc[T][4 * q + 2] * nrm, acc[T][4 * q + 3] * nrm);
+      for (int T = 0; T < 4; ++T) acc[T] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o.ah[T], bl, acc[T], 0, 0, 0);
+#pragma unroll
+      for (int T = 0; T < 4; ++T) acc[T] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o.al[T], bh, acc[T], 0, 0, 0);
+    };
+    // (k-steps spelled out: the code words are indexed by constants)
+    using std::integral_constant;
+    Ops o;
+    auto step = [&](auto ST) {
+      __builtin_amdgcn_sched_barrier(0);  // one k-step's operands live at a time
+      load_ops(ST, o);
+      products(o);
+    };
+    step(integral_constant<int, 0>{});
+    step(integral_constant<int, 1>{});
+    step(integral_constant<int, 2>{});
+    step(integral_constant<int, 3>{});
+    step(integral_constant<int, 4>{});
+    step(integral_constant<int, 5>{});
+    step(integral_constant<int, 6>{});
+    step(integral_constant<int, 7>{});
+    __builtin_amdgcn_sched_barrier(0);
+    // acc[T][vv] = x_hat[vector v][32 T + 16 h + vv] / n; through the stage: pend[NR T + i]
+    // = bytes 16 (lane % LPV) .. of the T slice of vector VPI i + lane / LPV. The stage
+    // holds one RB-byte row per vector; 16-byte chunk c of row r sits at chunk
+    // c ^ ((r >> SW) & (LPV - 1)) so that the writes of 16 lanes hit distinct banks.
+    constexpr int SW = OBF16 ? 2 : 1;
+    auto chunk = [&](int r, int c) { return stg + r * RB + 16 * (c ^ ((r >> SW) & (LPV - 1))); };
+#pragma unroll
+    for (int T = 0; T < 4; ++T) {
+      if constexpr (OBF16) {
+        uint16_t w[16];
+#pragma unroll
+        for (int e = 0; e < 16; ++e) w[e] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(acc[T][e] * nrm));
+        *reinterpret_cast<u4v*>(chunk(v, 2 * h)) = u4v{pack2(w[0], w[1]), pack2(w[2], w[3]), pack2(w[4], w[5]), pack2(w[6], w[7])};
+        *reinterpret_cast<u4v*>(chunk(v, 2 * h + 1)) =
+            u4v{pack2(w[8], w[9]), pack2(w[10], w[11]), pack2(w[12], w[13]), pack2(w[14], w[15])};
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int i = 0; i < NR; ++i)
+          pend[NR * T + i] = *reinterpret_cast<const u4v*>(chunk(VPI * i + lane / LPV, lane % LPV));
+        __builtin_amdgcn_wave_barrier();
+      } else {
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {  // vectors 16 r .. 16 r + 15 (2 KB of stage)
+          if ((v >> 4) == r) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+              *reinterpret_cast<u4v*>(chunk(v & 15, 4 * h + q)) =
+                  u4v{__float_as_uint(acc[T][4 * q] * nrm), __float_as_uint(acc[T][4 * q + 1] * nrm),
+                      __float_as_uint(acc[T][4 * q + 2] * nrm), __float_as_uint(acc[T][4 * q + 3] * nrm)};
+          }
+          __builtin_amdgcn_wave_barrier();
+#pragma unroll
+          for (int q = 0; q < 2; ++q)
+            pend[NR * T + 2 * r + q] = *reinterpret_cast<const u4v*>(chunk(VPI * q + lane / LPV, lane % LPV));
+          __builtin_amdgcn_wave_barrier();
+        }
       }
     }
-    cur = nxt;
-    slot = slotn;
-    nrm = nrmn;
+    // row of the vector each lane stores for (instruction i)
+    const uint64_t vr = reinterpret_cast<uint64_t>(vrow);
 #pragma unroll
-    for (int q = 0; q < CB / 4; ++q) cw[q] = cwn[q];
-    nxt = nn;
-    slotn = slotnn;
+    for (int i = 0; i < NR; ++i) {
+      const int src = (VPI * i + lane / LPV) * 4;  // lane holding that vector (h = 0), as a byte index
+      const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_ds_bpermute(src, static_cast<int>(vr)));
+      const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_ds_bpermute(src, static_cast<int>(vr >> 32)));
+      prow[i] = (static_cast<uint64_t>(hi) << 32) | lo;
+    }
+  };
+
+  using std::false_type;
+  using std::true_type;
+  Stage X, Y;
+  locate(X, 0);
+  fetch(X);
+  locate(Y, 1);
+  turn(X, Y, 0, false_type{});
+  int64_t k = 1;
+  for (; k + 1 < mine; k += 2) {
+    turn(Y, X, k, true_type{});
+    turn(X, Y, k + 1, true_type{});
   }
+  if (k < mine) turn(Y, X, k, true_type{});
+#pragma unroll
+  for (int T = 0; T < 4; ++T)
+#pragma unroll
+    for (int i = 0; i < NR; ++i)
+      *reinterpret_cast<g_u4v*>(prow[i] + RB * T + 16 * (lane % LPV)) = pend[NR * T + i];
 }
 
 }  // namespace
@@ -246,10 +349,19 @@ int launch_decompress(void* stream, const fq_quantizer& q, const fq_cache& c, co
   const int64_t want = (tiles + DQ_WAVES - 1) / DQ_WAVES;
   // two work-groups per CU and kind: one round, each stages the fragments once
   const unsigned g = static_cast<unsigned>(want < 256 ? want : 256);
-  if (q.bits == 4)
-    hipLaunchKernelGGL(decompress_kernel<4>, dim3(g, 2), dim3(DQ_WAVES * 64), 0, static_cast<hipStream_t>(stream), a);
-  else
-    hipLaunchKernelGGL(decompress_kernel<2>, dim3(g, 2), dim3(DQ_WAVES * 64), 0, static_cast<hipStream_t>(stream), a);
+  const dim3 grid(g, 2), block(DQ_WAVES * 64);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (q.bits == 4) {
+    if (a.out_bf16)
+      hipLaunchKernelGGL((decompress_kernel<4, true>), grid, block, 0, st, a);
+    else
+      hipLaunchKernelGGL((decompress_kernel<4, false>), grid, block, 0, st, a);
+  } else {
+    if (a.out_bf16)
+      hipLaunchKernelGGL((decompress_kernel<2, true>), grid, block, 0, st, a);
+    else
+      hipLaunchKernelGGL((decompress_kernel<2, false>), grid, block, 0, st, a);
+  }
   return static_cast<int>(hipGetLastError());
 }
 
