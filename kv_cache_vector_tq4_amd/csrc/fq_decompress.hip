@@ -6,14 +6,24 @@
 // products with it, not the vector itself, so they are not applied.
 //
 // One wave rebuilds a tile of 32 stored vectors as X_hat^T = Pi^T C^T on the matrix
-// cores (v_mfma_f32_32x32x16_bf16): A = Pi^T (bf16 hi + lo, staged in LDS once per
-// work-group) with its rows fed in an order that leaves coordinates 64 h + 16 T +
-// vv of one vector in accumulator register vv of row tile T of lane (h, vector),
-// B = the tile's dequantized codes (columns = vectors; levels as bf16 hi + lo read
-// from a byte-indexed LDS table: one entry per code byte, 4 copies); three products
-// per k-step (hi hi, hi lo, lo hi): about 16 significant bits, below the bf16
-// output's rounding and within 1e-5 n of the exact value for fp32 output. Each
-// lane then scales by its vector's norm and stores 64 consecutive coordinates.
+// cores. A = Pi^T, staged in LDS once per work-group, its rows fed in an order that
+// leaves coordinates 32 T + 16 h + vv of a vector in accumulator register vv of row
+// tile T of lane (h, vector); k-step s of lane half h covers coordinates 64 h + 8 s ..
+// + 7, so a lane reads only its half of each record. B = the tile's dequantized codes
+// (columns = vectors) from a byte-indexed LDS level table, one entry per code byte.
+//  * bf16 output: Pi^T and the levels rounded to fp16, one v_mfma_f32_32x32x16_f16 per
+//    row tile and k-step (about 11 significant bits per term, fp32 accumulation; the
+//    result is then rounded to bf16's 8).
+//  * fp32 output: Pi^T and the levels split into bf16 hi + lo, three
+//    v_mfma_f32_32x32x16_bf16 (hi hi, hi lo, lo hi): about 16 significant bits,
+//    within 1e-5 n of the exact value.
+// Each lane scales by its vector's norm; the tile goes through the wave's LDS stage so
+// that every store instruction writes 256-byte runs of four vectors' rows.
+//
+// Memory schedule: each wave alternates two pipeline stages (this tile's codes, the
+// next tile's slot) and waits for a request one tile after issuing it; the previous
+// tile's stores lead each turn and every turn issues the same memory operations, so
+// the waits stay exact.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -25,12 +35,13 @@ namespace fq {
 namespace {
 
 constexpr int D = FQ_HEAD_DIM;
-constexpr int DQ_WAVES = 4;           // waves per work-group (two work-groups per CU)
+constexpr int DQ_WAVES = 8;           // waves per work-group (one work-group per CU)
 constexpr int DQ_VEC = 32;            // vectors per wave tile
 constexpr int DQ_FRAG = 8 * 4 * 64;   // A fragments: 8 k-steps x 4 row tiles x 64 lanes (16 B each)
-constexpr int DQ_STAGE = 2048;        // bytes of LDS per wave for re-ordering its stores
+constexpr int DQ_STAGE = 8192;        // bytes of LDS per wave for re-ordering its stores
 
 typedef __bf16 b8 __attribute__((ext_vector_type(8)));
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 typedef float f16v __attribute__((ext_vector_type(16)));
 typedef uint32_t u4v __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(1))) u4v g_u4v;  // in global memory (not flat)
@@ -72,13 +83,17 @@ __device__ __forceinline__ int out_coord(int T, int rho) {
 // One work-group stages Pi^T's A fragments, then its waves take 32-vector tiles of
 // one kind (blockIdx.y: 0 K, 1 V) in a grid-stride loop.
 template <int BITS, bool OBF16>
-__global__ void __launch_bounds__(DQ_WAVES * 64, 2) decompress_kernel(DecompressArgs a) {
-  // level table entry of code byte x: 4-bit (hi c0 | hi c1, lo c0 | lo c1), 8 B;
-  // 2-bit (hi c0 | hi c1, hi c2 | hi c3, lo c0 | lo c1, lo c2 | lo c3), 16 B; the
-  // byte's codes c0.. in coordinate order; at (x * COPIES + copy) * EB (copy = lane % COPIES)
-  constexpr int EB = BITS == 4 ? 8 : 16;
-  constexpr int COPIES = BITS == 4 ? 4 : 2;  // 8 KB either way: 80 KB of LDS per work-group
-  __shared__ uint4 s_fh[DQ_FRAG], s_fl[DQ_FRAG];  // Pi^T fragments, bf16 hi / lo (64 KB)
+__global__ void __launch_bounds__(DQ_WAVES * 64, 1) decompress_kernel(DecompressArgs a) {
+  // ONE (bf16 output): one fp16 product per k-step, Pi^T and the levels rounded to
+  // fp16. Otherwise (fp32 output): bf16 hi + lo splits and three products.
+  constexpr bool ONE = OBF16;
+  // level table entry of code byte x, the byte's codes c0.. in coordinate order:
+  // ONE: fp16 levels, 4-bit (c0 | c1) 4 B, 2-bit (c0 | c1, c2 | c3) 8 B; else bf16,
+  // 4-bit (hi c0 | hi c1, lo c0 | lo c1) 8 B, 2-bit (hi c0 | hi c1, hi c2 | hi c3,
+  // lo c0 | lo c1, lo c2 | lo c3) 16 B; at (x * COPIES + copy) * EB, copy = lane % COPIES
+  constexpr int EB = (BITS == 4 ? 8 : 16) / (ONE ? 2 : 1);
+  constexpr int COPIES = 8192 / (256 * EB);  // an 8 KB table
+  __shared__ uint4 s_fh[DQ_FRAG], s_fl[ONE ? 1 : DQ_FRAG];  // Pi^T fragments: fp16, or bf16 hi / lo
   __shared__ __align__(16) uint8_t s_tab[256 * COPIES * EB];
   __shared__ __align__(16) uint8_t s_stage[DQ_WAVES * DQ_STAGE];
   const int kind = blockIdx.y;
@@ -92,17 +107,33 @@ __global__ void __launch_bounds__(DQ_WAVES * 64, 2) decompress_kernel(Decompress
     const float xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
     uint16_t h[8], l[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) split_bf16x(xs[e], h[e], l[e]);
+    for (int e = 0; e < 8; ++e) {
+      if constexpr (ONE)
+        h[e] = __builtin_bit_cast(uint16_t, static_cast<_Float16>(xs[e]));
+      else
+        split_bf16x(xs[e], h[e], l[e]);
+    }
     s_fh[idx] = make_uint4(pack2(h[0], h[1]), pack2(h[2], h[3]), pack2(h[4], h[5]), pack2(h[6], h[7]));
-    s_fl[idx] = make_uint4(pack2(l[0], l[1]), pack2(l[2], l[3]), pack2(l[4], l[5]), pack2(l[6], l[7]));
+    if constexpr (!ONE)
+      s_fl[idx] = make_uint4(pack2(l[0], l[1]), pack2(l[2], l[3]), pack2(l[4], l[5]), pack2(l[6], l[7]));
   }
   for (int idx = tid; idx < 256 * COPIES; idx += DQ_WAVES * 64) {
     const uint32_t x = static_cast<uint32_t>(idx) / COPIES;
     constexpr int PER = 8 / BITS;  // codes per byte
     uint16_t hi[4], lo[4];
 #pragma unroll
-    for (int c = 0; c < PER; ++c) split_bf16x(a.levels[(x >> (BITS * c)) & ((1u << BITS) - 1u)], hi[c], lo[c]);
-    if constexpr (BITS == 4)
+    for (int c = 0; c < PER; ++c) {
+      const float lv = a.levels[(x >> (BITS * c)) & ((1u << BITS) - 1u)];
+      if constexpr (ONE)
+        hi[c] = __builtin_bit_cast(uint16_t, static_cast<_Float16>(lv));
+      else
+        split_bf16x(lv, hi[c], lo[c]);
+    }
+    if constexpr (ONE && BITS == 4)
+      *reinterpret_cast<uint32_t*>(s_tab + idx * EB) = pack2(hi[0], hi[1]);
+    else if constexpr (ONE)
+      *reinterpret_cast<uint2*>(s_tab + idx * EB) = make_uint2(pack2(hi[0], hi[1]), pack2(hi[2], hi[3]));
+    else if constexpr (BITS == 4)
       *reinterpret_cast<uint2*>(s_tab + idx * EB) = make_uint2(pack2(hi[0], hi[1]), pack2(lo[0], lo[1]));
     else
       *reinterpret_cast<uint4*>(s_tab + idx * EB) =
@@ -113,11 +144,11 @@ __global__ void __launch_bounds__(DQ_WAVES * 64, 2) decompress_kernel(Decompress
 
   constexpr int CB = D * BITS / 8;  // code bytes per vector
   constexpr int HW = CB / 8;        // 32-bit words of code per lane (its k half)
-  // Stores: per row tile T a vector's coordinates 32 T .. 32 T + 31 are RB contiguous
-  // bytes, written by LPV lanes (16 B each); one store instruction covers VPI vectors,
-  // NR instructions per T cover the tile's 32.
-  constexpr int RB = OBF16 ? 64 : 128, LPV = RB / 16, VPI = 64 / LPV, NR = DQ_VEC / VPI;
+  // Stores: a round writes TPR row tiles, i.e. 256 contiguous bytes of every vector's
+  // row (all of a bf16 row, half of an fp32 one), 16 lanes per vector, 4 vectors per
+  // store instruction, 8 instructions per round.
   constexpr int ESZ = OBF16 ? 2 : 4;
+  constexpr int TPR = OBF16 ? 4 : 2, ROUNDS = 4 / TPR, NR = 8;
   const int64_t nvec = a.ntok * a.hkv;
   const int64_t ntiles = (nvec + DQ_VEC - 1) / DQ_VEC;
   const int v = lane & 31, h = lane >> 5;  // the lane's vector in the tile; k-group / output half
@@ -157,12 +188,12 @@ __global__ void __launch_bounds__(DQ_WAVES * 64, 2) decompress_kernel(Decompress
     }
   };
   // The previous tile's output, re-ordered through this wave's LDS stage so that each
-  // store instruction writes whole RB-byte runs of rows, and stored at the start of the
+  // store instruction writes 256-byte runs of four rows, and stored at the start of the
   // next tile's turn (after the first turn every turn issues the same memory
   // operations in the same order; vectors with nothing to write use g_dq_sink rows).
   uint8_t* const stg = s_stage + wave * DQ_STAGE;
-  u4v pend[4 * NR];
-  uint64_t prow[NR];  // global addresses
+  u4v pend[ROUNDS * NR];
+  uint64_t prow[NR];  // global addresses of the rows of vectors 4 i + lane / 16
 
   // One turn, tile k in X (codes requested a turn ago), tile k + 1's slot in Y:
   // store tile k - 1; request tile k + 1's codes into Y and tile k + 2's slot into X;
@@ -179,10 +210,10 @@ __global__ void __launch_bounds__(DQ_WAVES * 64, 2) decompress_kernel(Decompress
     __builtin_amdgcn_sched_barrier(0);
     if constexpr (decltype(STORE)::value) {
 #pragma unroll
-      for (int T = 0; T < 4; ++T)
+      for (int rr = 0; rr < ROUNDS; ++rr)
 #pragma unroll
         for (int i = 0; i < NR; ++i)
-          *reinterpret_cast<g_u4v*>(prow[i] + RB * T + 16 * (lane % LPV)) = pend[NR * T + i];
+          *reinterpret_cast<g_u4v*>(prow[i] + 256 * rr + 16 * (lane & 15)) = pend[NR * rr + i];
     }
     __builtin_amdgcn_sched_barrier(0);
     fetch(Y);
@@ -193,37 +224,55 @@ __global__ void __launch_bounds__(DQ_WAVES * 64, 2) decompress_kernel(Decompress
     // k-step s: B = coordinates 64 h + 8 s .. + 7 of the vector (level[idx] as bf16
     // hi / lo, from the table), A = the fragments of Pi^T
     struct Ops {
-      b8 ah[4], al[4];
-      uint32_t e[8];  // the table entries: 4-bit four of (hi, lo); 2-bit two of (hi, hi, lo, lo)
+      b8 ah[4], al[4];  // ONE: ah holds the fp16 fragments
+      uint32_t e[8];    // the table entries (ONE: e[0..3])
     };
     auto load_ops = [&](auto ST, Ops& o) {
       constexpr int st = decltype(ST)::value;
+      auto entry = [&](uint32_t byte) { return s_tab + byte * (COPIES * EB) + copy; };
       if constexpr (BITS == 4) {
         const uint32_t w = cw[st];  // code bytes of coordinates 64 h + 8 st ..
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const uint2 u = *reinterpret_cast<const uint2*>(s_tab + ((w >> (8 * q)) & 255u) * (COPIES * EB) + copy);
-          o.e[2 * q] = u.x;
-          o.e[2 * q + 1] = u.y;
+          if constexpr (ONE) {
+            o.e[q] = *reinterpret_cast<const uint32_t*>(entry((w >> (8 * q)) & 255u));
+          } else {
+            const uint2 u = *reinterpret_cast<const uint2*>(entry((w >> (8 * q)) & 255u));
+            o.e[2 * q] = u.x;
+            o.e[2 * q + 1] = u.y;
+          }
         }
       } else {
         const uint32_t w = cw[st >> 1] >> (16 * (st & 1));  // two code bytes of coordinates 64 h + 8 st ..
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
-          const uint4 u = *reinterpret_cast<const uint4*>(s_tab + ((w >> (8 * q)) & 255u) * (COPIES * EB) + copy);
-          o.e[4 * q] = u.x;
-          o.e[4 * q + 1] = u.y;
-          o.e[4 * q + 2] = u.z;
-          o.e[4 * q + 3] = u.w;
+          if constexpr (ONE) {
+            const uint2 u = *reinterpret_cast<const uint2*>(entry((w >> (8 * q)) & 255u));
+            o.e[2 * q] = u.x;
+            o.e[2 * q + 1] = u.y;
+          } else {
+            const uint4 u = *reinterpret_cast<const uint4*>(entry((w >> (8 * q)) & 255u));
+            o.e[4 * q] = u.x;
+            o.e[4 * q + 1] = u.y;
+            o.e[4 * q + 2] = u.z;
+            o.e[4 * q + 3] = u.w;
+          }
         }
       }
 #pragma unroll
       for (int T = 0; T < 4; ++T) {
         o.ah[T] = __builtin_bit_cast(b8, s_fh[(st * 4 + T) * 64 + lane]);
-        o.al[T] = __builtin_bit_cast(b8, s_fl[(st * 4 + T) * 64 + lane]);
+        if constexpr (!ONE) o.al[T] = __builtin_bit_cast(b8, s_fl[(st * 4 + T) * 64 + lane]);
       }
     };
     auto products = [&](const Ops& o) {
+      if constexpr (ONE) {
+        const h8 b = __builtin_bit_cast(h8, make_uint4(o.e[0], o.e[1], o.e[2], o.e[3]));
+#pragma unroll
+        for (int T = 0; T < 4; ++T)
+          acc[T] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(h8, o.ah[T]), b, acc[T], 0, 0, 0);
+        return;
+      }
       b8 bh, bl;
       if constexpr (BITS == 4) {
         bh = __builtin_bit_cast(b8, make_uint4(o.e[0], o.e[2], o.e[4], o.e[6]));
@@ -256,49 +305,42 @@ __global__ void __launch_bounds__(DQ_WAVES * 64, 2) decompress_kernel(Decompress
     step(integral_constant<int, 6>{});
     step(integral_constant<int, 7>{});
     __builtin_amdgcn_sched_barrier(0);
-    // acc[T][vv] = x_hat[vector v][32 T + 16 h + vv] / n; through the stage: pend[NR T + i]
-    // = bytes 16 (lane % LPV) .. of the T slice of vector VPI i + lane / LPV. The stage
-    // holds one RB-byte row per vector; 16-byte chunk c of row r sits at chunk
-    // c ^ ((r >> SW) & (LPV - 1)) so that the writes of 16 lanes hit distinct banks.
-    constexpr int SW = OBF16 ? 2 : 1;
-    auto chunk = [&](int r, int c) { return stg + r * RB + 16 * (c ^ ((r >> SW) & (LPV - 1))); };
+    // acc[T][vv] = x_hat[vector v][32 T + 16 h + vv] / n. The stage holds a 256-byte
+    // row per vector (the round's TPR row tiles in coordinate order); 16-byte chunk c
+    // of row r sits at chunk c ^ (r & 15), so the writes of 16 lanes hit distinct
+    // banks. Read back: pend[NR rr + i] = chunk lane % 16 of vector 4 i + lane / 16.
+    auto chunk = [&](int r, int c) { return stg + r * 256 + 16 * (c ^ (r & 15)); };
 #pragma unroll
-    for (int T = 0; T < 4; ++T) {
-      if constexpr (OBF16) {
-        uint16_t w[16];
+    for (int rr = 0; rr < ROUNDS; ++rr) {
 #pragma unroll
-        for (int e = 0; e < 16; ++e) w[e] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(acc[T][e] * nrm));
-        *reinterpret_cast<u4v*>(chunk(v, 2 * h)) = u4v{pack2(w[0], w[1]), pack2(w[2], w[3]), pack2(w[4], w[5]), pack2(w[6], w[7])};
-        *reinterpret_cast<u4v*>(chunk(v, 2 * h + 1)) =
-            u4v{pack2(w[8], w[9]), pack2(w[10], w[11]), pack2(w[12], w[13]), pack2(w[14], w[15])};
-        __builtin_amdgcn_wave_barrier();
+      for (int tt = 0; tt < TPR; ++tt) {
+        const int T = rr * TPR + tt;
+        if constexpr (OBF16) {  // 16 coordinates = chunks 4 tt + 2 h, + 1
+          uint16_t w[16];
 #pragma unroll
-        for (int i = 0; i < NR; ++i)
-          pend[NR * T + i] = *reinterpret_cast<const u4v*>(chunk(VPI * i + lane / LPV, lane % LPV));
-        __builtin_amdgcn_wave_barrier();
-      } else {
+          for (int e = 0; e < 16; ++e) w[e] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(acc[T][e] * nrm));
+          *reinterpret_cast<u4v*>(chunk(v, 4 * tt + 2 * h)) =
+              u4v{pack2(w[0], w[1]), pack2(w[2], w[3]), pack2(w[4], w[5]), pack2(w[6], w[7])};
+          *reinterpret_cast<u4v*>(chunk(v, 4 * tt + 2 * h + 1)) =
+              u4v{pack2(w[8], w[9]), pack2(w[10], w[11]), pack2(w[12], w[13]), pack2(w[14], w[15])};
+        } else {  // chunks 8 tt + 4 h + q
 #pragma unroll
-        for (int r = 0; r < 2; ++r) {  // vectors 16 r .. 16 r + 15 (2 KB of stage)
-          if ((v >> 4) == r) {
-#pragma unroll
-            for (int q = 0; q < 4; ++q)
-              *reinterpret_cast<u4v*>(chunk(v & 15, 4 * h + q)) =
-                  u4v{__float_as_uint(acc[T][4 * q] * nrm), __float_as_uint(acc[T][4 * q + 1] * nrm),
-                      __float_as_uint(acc[T][4 * q + 2] * nrm), __float_as_uint(acc[T][4 * q + 3] * nrm)};
-          }
-          __builtin_amdgcn_wave_barrier();
-#pragma unroll
-          for (int q = 0; q < 2; ++q)
-            pend[NR * T + 2 * r + q] = *reinterpret_cast<const u4v*>(chunk(VPI * q + lane / LPV, lane % LPV));
-          __builtin_amdgcn_wave_barrier();
+          for (int q = 0; q < 4; ++q)
+            *reinterpret_cast<u4v*>(chunk(v, 8 * tt + 4 * h + q)) =
+                u4v{__float_as_uint(acc[T][4 * q] * nrm), __float_as_uint(acc[T][4 * q + 1] * nrm),
+                    __float_as_uint(acc[T][4 * q + 2] * nrm), __float_as_uint(acc[T][4 * q + 3] * nrm)};
         }
       }
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int i = 0; i < NR; ++i) pend[NR * rr + i] = *reinterpret_cast<const u4v*>(chunk(4 * i + lane / 16, lane & 15));
+      __builtin_amdgcn_wave_barrier();
     }
     // row of the vector each lane stores for (instruction i)
     const uint64_t vr = reinterpret_cast<uint64_t>(vrow);
 #pragma unroll
     for (int i = 0; i < NR; ++i) {
-      const int src = (VPI * i + lane / LPV) * 4;  // lane holding that vector (h = 0), as a byte index
+      const int src = (4 * i + lane / 16) * 4;  // lane holding that vector (h = 0), as a byte index
       const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_ds_bpermute(src, static_cast<int>(vr)));
       const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_ds_bpermute(src, static_cast<int>(vr >> 32)));
       prow[i] = (static_cast<uint64_t>(hi) << 32) | lo;
@@ -319,10 +361,10 @@ __global__ void __launch_bounds__(DQ_WAVES * 64, 2) decompress_kernel(Decompress
   }
   if (k < mine) turn(Y, X, k, true_type{});
 #pragma unroll
-  for (int T = 0; T < 4; ++T)
+  for (int rr = 0; rr < ROUNDS; ++rr)
 #pragma unroll
     for (int i = 0; i < NR; ++i)
-      *reinterpret_cast<g_u4v*>(prow[i] + RB * T + 16 * (lane % LPV)) = pend[NR * T + i];
+      *reinterpret_cast<g_u4v*>(prow[i] + 256 * rr + 16 * (lane & 15)) = pend[NR * rr + i];
 }
 
 }  // namespace
@@ -347,8 +389,8 @@ int launch_decompress(void* stream, const fq_quantizer& q, const fq_cache& c, co
   a.out_bf16 = out_dtype == FQ_BF16 ? 1 : 0;
   const int64_t tiles = (num_tokens * c.num_kv_heads + DQ_VEC - 1) / DQ_VEC;
   const int64_t want = (tiles + DQ_WAVES - 1) / DQ_WAVES;
-  // two work-groups per CU and kind: one round, each stages the fragments once
-  const unsigned g = static_cast<unsigned>(want < 256 ? want : 256);
+  // one work-group per CU (128 per kind): one round, each stages the fragments once
+  const unsigned g = static_cast<unsigned>(want < 128 ? want : 128);
   const dim3 grid(g, 2), block(DQ_WAVES * 64);
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (q.bits == 4) {
