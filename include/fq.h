@@ -195,8 +195,11 @@ fq_status fq_compress(void* stream, const fq_quantizer* quant, const fq_cache* c
  *  k_out, v_out  device; either may be NULL to skip that side. Every vector starts
  *                on a 16-byte boundary (base pointers and both strides, in bytes,
  *                multiples of 16).
- * The products run on the matrix cores with Pi and n * level split into bf16 hi + lo
- * (about 16 significant bits): fp32 outputs are within 1e-5 * n of the exact value.
+ * The products run on the matrix cores, accumulating in fp32. FQ_F32: Pi and the
+ * levels split into bf16 hi + lo, three products (about 16 significant bits, within
+ * 1e-5 * n of the exact value). FQ_BF16: Pi and the levels rounded to fp16, one
+ * product per term (each term within 2^-10 relative), then scaled by n and rounded
+ * to bf16.
  * Errors: FQ_ERR_INVALID_ARG, FQ_ERR_UNSUPPORTED, FQ_ERR_HIP.
  */
 fq_status fq_decompress(void* stream, const fq_quantizer* quant, const fq_cache* cache,
