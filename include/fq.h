@@ -47,6 +47,7 @@ typedef enum fq_status {
 
 typedef enum fq_rotation { FQ_ROT_HAAR = 0, FQ_ROT_WHT = 1 } fq_rotation;
 typedef enum fq_dtype { FQ_F32 = 0, FQ_BF16 = 1 } fq_dtype;
+typedef enum fq_codebook_kind { FQ_CB_GAUSSIAN = 0, FQ_CB_SPHERE = 1 } fq_codebook_kind;
 
 /* Human-readable name of a status code (static string). */
 const char* fq_status_string(int status);
@@ -180,6 +181,25 @@ fq_status fq_compress(void* stream, const fq_quantizer* quant, const fq_cache* c
                       const void* k, const void* v, int dtype, int64_t num_tokens,
                       int64_t token_stride, int64_t head_stride, const int64_t* slot_mapping,
                       float* debug_y, float* debug_p);
+
+/*
+ * fq_build_levels -- host, synchronous. The scalar codebook alone, of either law a
+ * rotated coordinate can be modelled by:
+ *  FQ_CB_GAUSSIAN  the codebook of fq_build_codebook: N(0,1) Lloyd-Max levels scaled
+ *                  by 1/sqrt(d) ("FlashQuant" page, "TurboQuant" step 3);
+ *  FQ_CB_SPHERE    the exact law of one coordinate of a uniform point on the unit
+ *                  sphere in R^d ("TurboQuant" blog, "Étape 2" / "Couche 2": the
+ *                  spherical Beta law): density proportional to (1 - x^2)^((d-3)/2)
+ *                  on (-1, 1); Lloyd iterated to the float64 fixed point (largest
+ *                  level change < 1e-15), levels made exactly antisymmetric, no
+ *                  further scaling.
+ *  bits 2 or 4; head_dim d, 3 <= d <= 256 (the quantizer itself needs d = 128).
+ * Outputs (host, caller-allocated, fp32 rounded once from float64): levels
+ * [2^bits] ascending, boundaries [2^bits - 1] = midpoints. They replace the levels
+ * and boundaries of an fq_quantizer; the kernels take whatever codebook it holds.
+ * Errors: FQ_ERR_INVALID_ARG (null output, bad kind), FQ_ERR_UNSUPPORTED (bits, d).
+ */
+fq_status fq_build_levels(int bits, int head_dim, int kind, float* levels, float* boundaries);
 
 /*
  * fq_decompress -- rebuild dense K and V vectors from the paged cache ("FlashQuant"

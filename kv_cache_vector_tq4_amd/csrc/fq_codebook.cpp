@@ -81,6 +81,94 @@ void lloyd_max(int bits, std::vector<double>& lev, std::vector<double>& bnd) {
   for (int i = 0; i + 1 < L; ++i) bnd[i] = 0.5 * (lev[i] + lev[i + 1]);
 }
 
+// ---- spherical marginal ("TurboQuant" blog, "Étape 2" / "Couche 2") ----
+// A coordinate of a uniform point on the unit sphere in R^d has density
+// proportional to w(x) = (1 - x^2)^(p - 1) on (-1, 1), p = (d - 1) / 2. On a cell
+// (a, b] the first moment has the closed form ((1 - a^2)^p - (1 - b^2)^p) / (2p)
+// (same unnormalized scale as w); the mass is integrated numerically with
+// composite Gauss-Legendre (GL_N nodes on GL_PANELS equal panels).
+constexpr int GL_N = 20, GL_PANELS = 16;
+
+// Nodes / weights of the GL_N-point Gauss-Legendre rule on [-1, 1]: roots of P_n by
+// Newton's method from the Chebyshev-like guesses cos(pi (i + 3/4) / (n + 1/2)),
+// P_n and P_n' from the three-term recurrence; w_i = 2 / ((1 - x_i^2) P_n'(x_i)^2).
+void gauss_legendre(double* x, double* w) {
+  const int n = GL_N;
+  for (int i = 0; i < n; ++i) {
+    double z = std::cos(3.14159265358979323846 * (i + 0.75) / (n + 0.5));
+    double dp = 1.0;
+    for (int it = 0; it < 100; ++it) {
+      double p0 = 1.0, p1 = z;
+      for (int k = 2; k <= n; ++k) {
+        const double pk = ((2.0 * k - 1.0) * z * p1 - (k - 1.0) * p0) / k;
+        p0 = p1;
+        p1 = pk;
+      }
+      dp = n * (z * p1 - p0) / (z * z - 1.0);
+      const double dz = p1 / dp;
+      z -= dz;
+      if (std::fabs(dz) < 1e-17) break;
+    }
+    x[i] = z;
+    w[i] = 2.0 / ((1.0 - z * z) * dp * dp);
+  }
+}
+
+double sphere_weight_mass(double a, double b, double p, const double* gx, const double* gw) {
+  double sum = 0;
+  const double h = (b - a) / GL_PANELS;
+  for (int j = 0; j < GL_PANELS; ++j) {
+    const double c = a + (j + 0.5) * h, r = 0.5 * h;
+    for (int i = 0; i < GL_N; ++i) {
+      const double x = c + r * gx[i];
+      const double u = 1.0 - x * x;
+      if (u > 0) sum += gw[i] * r * std::exp((p - 1.0) * std::log(u));
+    }
+  }
+  return sum;
+}
+
+double sphere_m1(double a, double b, double p) {
+  auto t = [&](double x) {
+    const double u = 1.0 - x * x;
+    return u > 0 ? std::exp(p * std::log(u)) : 0.0;
+  };
+  return (t(a) - t(b)) / (2.0 * p);
+}
+
+// Lloyd fixed point for the spherical marginal in R^d: starts from the Gaussian
+// codebook scaled by 1/sqrt(d) (the quantizer of this log-concave law is unique,
+// so the start only sets the number of steps), iterates until the largest level
+// change is below 1e-15, then makes the levels exactly antisymmetric.
+void lloyd_max_sphere(int bits, int d, std::vector<double>& lev, std::vector<double>& bnd) {
+  const int L = 1 << bits;
+  const double p = 0.5 * (d - 1);
+  std::vector<double> g, gb;
+  lloyd_max(bits, g, gb);
+  lev.resize(L);
+  bnd.resize(L - 1);
+  for (int i = 0; i < L; ++i) lev[i] = std::fmin(0.999, std::fmax(-0.999, g[i] / std::sqrt(static_cast<double>(d))));
+  double gx[GL_N], gw[GL_N];
+  gauss_legendre(gx, gw);
+  std::vector<double> nl(L);
+  for (int it = 0; it < 200000; ++it) {
+    for (int i = 0; i + 1 < L; ++i) bnd[i] = 0.5 * (lev[i] + lev[i + 1]);
+    double delta = 0;
+    for (int i = 0; i < L; ++i) {
+      const double a = i == 0 ? -1.0 : bnd[i - 1];
+      const double b = i == L - 1 ? 1.0 : bnd[i];
+      nl[i] = sphere_m1(a, b, p) / sphere_weight_mass(a, b, p, gx, gw);
+      delta = std::fmax(delta, std::fabs(nl[i] - lev[i]));
+    }
+    lev = nl;
+    if (delta < 1e-15) break;
+  }
+  std::vector<double> sym(L);
+  for (int i = 0; i < L; ++i) sym[i] = 0.5 * (lev[i] - lev[L - 1 - i]);
+  lev = sym;
+  for (int i = 0; i + 1 < L; ++i) bnd[i] = 0.5 * (lev[i] + lev[i + 1]);
+}
+
 // Haar orthogonal matrix: Householder QR of a Gaussian matrix, Q with the
 // columns' signs flipped so that diag(R) > 0. a: d x d row-major, overwritten.
 void haar_from_gaussian(int d, std::vector<double>& a, std::vector<double>& q) {
@@ -246,5 +334,23 @@ extern "C" fq_status fq_pack_mfma_operands(const float* rotation_matrix, const f
       }
     }
   }
+  return FQ_OK;
+}
+
+extern "C" fq_status fq_build_levels(int bits, int head_dim, int kind, float* levels, float* boundaries) {
+  if (!levels || !boundaries) return FQ_ERR_INVALID_ARG;
+  if (kind != FQ_CB_GAUSSIAN && kind != FQ_CB_SPHERE) return FQ_ERR_INVALID_ARG;
+  if (bits != 2 && bits != 4) return FQ_ERR_UNSUPPORTED;
+  if (head_dim < 3 || head_dim > 256) return FQ_ERR_UNSUPPORTED;
+  std::vector<double> lev, bnd;
+  double scale = 1.0;
+  if (kind == FQ_CB_GAUSSIAN) {
+    lloyd_max(bits, lev, bnd);
+    scale = 1.0 / std::sqrt(static_cast<double>(head_dim));
+  } else {
+    lloyd_max_sphere(bits, head_dim, lev, bnd);
+  }
+  for (size_t i = 0; i < lev.size(); ++i) levels[i] = static_cast<float>(lev[i] * scale);
+  for (size_t i = 0; i < bnd.size(); ++i) boundaries[i] = static_cast<float>(bnd[i] * scale);
   return FQ_OK;
 }

@@ -16,6 +16,7 @@ LIB_PATH = os.path.join(_PKG, "libfq.so")
 FQ_OK, FQ_ERR_INVALID_ARG, FQ_ERR_UNSUPPORTED, FQ_ERR_WORKSPACE, FQ_ERR_HIP = range(5)
 ROT_HAAR, ROT_WHT = 0, 1
 F32, BF16 = 0, 1
+CB_GAUSSIAN, CB_SPHERE = 0, 1
 BLOCK = 16
 
 _lib = None
@@ -69,6 +70,7 @@ EXPORTS = {
     "fq_version": (ctypes.c_int, []),
     "fq_build_codebook": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_uint64,
                                          ctypes.c_uint64, ctypes.c_int] + [ctypes.c_void_p] * 7),
+    "fq_build_levels": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]),
     "fq_compress": (ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(QuantizerT), ctypes.POINTER(CacheT),
                                    ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int64,
                                    ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p,
@@ -161,6 +163,18 @@ def build_codebook(bits=4, head_dim=128, rotation=ROT_HAAR, rot_seed=1, qjl_seed
     return out
 
 
+def build_levels(bits=4, head_dim=128, kind=None):
+    """Host (levels, boundaries) fp32 of a scalar codebook (fq_build_levels); kind
+    CB_GAUSSIAN (default) or CB_SPHERE."""
+    kind = CB_GAUSSIAN if kind is None else kind
+    L = 1 << bits
+    lev, bnd = np.zeros(L, np.float32), np.zeros(L - 1, np.float32)
+    st = lib().fq_build_levels(bits, head_dim, kind, lev.ctypes.data_as(ctypes.c_void_p),
+                               bnd.ctypes.data_as(ctypes.c_void_p))
+    _check(st, "fq_build_levels")
+    return lev, bnd
+
+
 def pack_mfma_operands(rotation_matrix, qjl_matrix=None):
     """Host bytes of the prepared matrix-core operands (fq_pack_mfma_operands)."""
     out = np.zeros(MFMA_OPERAND_BYTES, np.uint8)
@@ -178,14 +192,19 @@ class Quantizer:
 
     prepared=True also uploads the packed matrix-core operands (fq_pack_mfma_operands);
     with prepared=False the kernels derive them from the fp32 matrices themselves.
+    codebook: CB_GAUSSIAN (fq_build_codebook's) or CB_SPHERE (fq_build_levels' exact
+    spherical marginal, replacing the levels and boundaries).
     """
 
     def __init__(self, bits=4, head_dim=128, rotation=ROT_HAAR, rot_seed=1, qjl_seed=2, qjl_dim=128,
-                 device="cuda", prepared=True):
+                 device="cuda", prepared=True, codebook=CB_GAUSSIAN):
         import torch
 
         self.host = build_codebook(bits, head_dim, rotation, rot_seed, qjl_seed, qjl_dim)
+        if codebook != CB_GAUSSIAN:
+            self.host["levels"], self.host["boundaries"] = build_levels(bits, head_dim, codebook)
         self.bits, self.head_dim, self.rotation, self.qjl_dim = bits, head_dim, rotation, qjl_dim
+        self.codebook = codebook
         keys = ("levels", "boundaries", "rotation_matrix", "rotation_t", "wht_signs", "qjl_matrix",
                 "qjl_matrix_t")
         self.dev = {k: torch.from_numpy(np.ascontiguousarray(self.host[k])).to(device) for k in keys}

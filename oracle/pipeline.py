@@ -14,13 +14,23 @@ HAAR = 0
 WHT = 1
 
 
-def build(bits, head_dim, rot=HAAR, rot_seed=1, qjl_seed=2, qjl_dim=None):
+GAUSSIAN, SPHERE = "gaussian", "sphere"
+
+
+def build(bits, head_dim, rot=HAAR, rot_seed=1, qjl_seed=2, qjl_dim=None, law=GAUSSIAN):
     """All stored parameters of one layer's quantizer.
 
     Returns levels32, boundaries32, pi (fp32 operator as float64), signs (WHT
-    only, else None), s (fp32 QJL matrix as float64, m x d).
+    only, else None), s (fp32 QJL matrix as float64, m x d). law: the codebook's
+    model of a rotated coordinate, GAUSSIAN (N(0, 1/d)) or SPHERE (the exact
+    spherical marginal).
     """
-    lev, bnd = codebook.scaled_codebook(bits, head_dim)
+    if law == GAUSSIAN:
+        lev, bnd = codebook.scaled_codebook(bits, head_dim)
+    elif law == SPHERE:
+        lev, bnd = codebook.sphere_codebook(bits, head_dim)
+    else:
+        raise ValueError(law)
     m = head_dim if qjl_dim is None else qjl_dim
     if rot == HAAR:
         pi = rotation.stored(rotation.haar_rotation(rot_seed, head_dim))
@@ -30,7 +40,7 @@ def build(bits, head_dim, rot=HAAR, rot_seed=1, qjl_seed=2, qjl_dim=None):
         pi = rotation.stored(rotation.wht_matrix(sg))
     s = rotation.stored(rotation.qjl_matrix(qjl_seed, m, head_dim))
     return {"bits": bits, "d": head_dim, "rot": rot, "levels": lev, "boundaries": bnd,
-            "pi": pi, "signs": sg, "s": s, "m": m}
+            "pi": pi, "signs": sg, "s": s, "m": m, "law": law}
 
 
 def encode_keys(x, q):

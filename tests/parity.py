@@ -36,8 +36,8 @@ def torch_inputs(inp, dtype, device="cuda"):
     }
 
 
-def oracle_quantizer(bits, rot=pipeline.HAAR, rot_seed=1, qjl_seed=2):
-    return pipeline.build(bits, 128, rot=rot, rot_seed=rot_seed, qjl_seed=qjl_seed)
+def oracle_quantizer(bits, rot=pipeline.HAAR, rot_seed=1, qjl_seed=2, law=pipeline.GAUSSIAN):
+    return pipeline.build(bits, 128, rot=rot, rot_seed=rot_seed, qjl_seed=qjl_seed, law=law)
 
 
 def valid_tokens(inp):
