@@ -333,6 +333,47 @@ fq_status fq_step_attend(void* stream, const fq_quantizer* quant, const fq_cache
                          const int32_t* seq_lens, int max_seq_len, int num_splits, float scale,
                          void* workspace, size_t workspace_bytes, float* out);
 
+/*
+ * Residual full-precision window ("TurboQuant" blog, "Couche 5" residual window and
+ * "Couche 7" a 128-token window; KIVI page, "Limitations" item 4: the newest tokens
+ * stay in 16-bit floats). Each sequence keeps its newest tokens' K and V in a bf16
+ * ring win_k / win_v [batch][win_cap][Hkv][128] (device, caller-owned, 16-byte
+ * aligned): the token at position pos lives in ring slot pos % win_cap. Older
+ * tokens live in the compressed cache.
+ *
+ * fq_window_append -- device, async. For each sequence b with positions[b] >= 0
+ * (the new token's position): the token in ring slot positions[b] % win_cap (the
+ * one at position positions[b] - win_cap, if any) is compressed into the cache at
+ * evict_slots[b] (< 0: it is dropped, e.g. while the ring is not full yet), then
+ * k_new / v_new [batch][Hkv][128] (kv_dtype FQ_F32 or FQ_BF16, contiguous, 8-byte
+ * aligned; rounded to bf16) are written into that ring slot. positions,
+ * evict_slots: device int64 [batch]. workspace: device, 256-byte aligned, at least
+ * fq_window_workspace_size bytes. 1 <= win_cap <= 4096.
+ * Errors: FQ_ERR_INVALID_ARG, FQ_ERR_WORKSPACE, FQ_ERR_HIP.
+ */
+fq_status fq_window_workspace_size(int batch, int num_kv_heads, size_t* bytes);
+fq_status fq_window_append(void* stream, const fq_quantizer* quant, const fq_cache* cache, const void* k_new,
+                           const void* v_new, int kv_dtype, int batch, const int64_t* positions,
+                           const int64_t* evict_slots, void* win_k, void* win_v, int win_cap, void* workspace,
+                           size_t workspace_bytes);
+
+/*
+ * fq_decode_attention_window -- fq_decode_attention over the compressed tokens
+ * [0, seq_lens[b]) together with the window tokens in ring slots t < win_lens[b]
+ * (device int32 [batch], clamped to [0, win_cap]): one softmax over both, the window's
+ * scores scale * <q, k_t> and values exact (fp32 arithmetic on the bf16 rows). The
+ * compressed part runs the split path (partials + merge; the window joins the
+ * merge), so the workspace is fq_decode_workspace_size's for these sizes. A caller
+ * with n tokens per sequence passes seq_lens = max(0, n - win_cap) and win_lens =
+ * min(n, win_cap). Errors: as fq_decode_attention.
+ */
+fq_status fq_decode_attention_window(void* stream, const fq_quantizer* quant, const fq_cache* cache,
+                                     const void* q, int q_dtype, int batch, int num_q_heads,
+                                     const int32_t* block_tables, int max_blocks_per_seq,
+                                     const int32_t* seq_lens, int max_seq_len, int num_splits, float scale,
+                                     void* workspace, size_t workspace_bytes, const void* win_k,
+                                     const void* win_v, int win_cap, const int32_t* win_lens, float* out);
+
 #ifdef __cplusplus
 }
 #endif

@@ -180,7 +180,7 @@ fq_status decode_checked(void* stream, const fq_quantizer* quant, const fq_cache
                          const int32_t* block_tables, int max_blocks_per_seq,
                          const int32_t* seq_lens, int max_seq_len, int num_splits, float scale,
                          void* workspace, size_t workspace_bytes, float* out,
-                         const fq::AppendIn* app, int phase) {
+                         const fq::AppendIn* app, int phase, const fq::WindowIn* win = nullptr) {
   fq_status st = check_quantizer(quant);
   if (st != FQ_OK) return st;
   st = check_cache(cache, quant);
@@ -222,9 +222,16 @@ fq_status decode_checked(void* stream, const fq_quantizer* quant, const fq_cache
     if (app->debug_y && !aligned(app->debug_y, 16)) return FQ_ERR_INVALID_ARG;
     if (app->debug_p && !aligned(app->debug_p, 16)) return FQ_ERR_INVALID_ARG;
   }
+  if (win) {
+    if (!win->k || !win->v || !win->lens || win->cap <= 0 || win->cap > FQ_MAX_WINDOW)
+      return FQ_ERR_INVALID_ARG;
+    if (!aligned(win->k, 16) || !aligned(win->v, 16) || !aligned(win->lens, 4)) return FQ_ERR_INVALID_ARG;
+    if (static_cast<int64_t>(batch) * win->cap * cache->num_kv_heads * FQ_HEAD_DIM >= (int64_t{1} << 40))
+      return FQ_ERR_UNSUPPORTED;
+  }
   int e = fq::launch_decode(stream, *quant, *cache, q, q_dtype, batch, num_q_heads, block_tables,
                             max_blocks_per_seq, seq_lens, max_seq_len, s, scale, workspace, out,
-                            app, phase);
+                            app, phase, win);
   return e == 0 ? FQ_OK : FQ_ERR_HIP;
 }
 
@@ -254,6 +261,47 @@ fq_status fq_decode_step(void* stream, const fq_quantizer* quant, const fq_cache
   return decode_checked(stream, quant, cache, q, q_dtype, batch, num_q_heads, block_tables,
                         max_blocks_per_seq, seq_lens, max_seq_len, num_splits, scale, workspace,
                         workspace_bytes, out, &app, fq::DECODE_ALL);
+}
+
+fq_status fq_decode_attention_window(void* stream, const fq_quantizer* quant, const fq_cache* cache,
+                                     const void* q, int q_dtype, int batch, int num_q_heads,
+                                     const int32_t* block_tables, int max_blocks_per_seq,
+                                     const int32_t* seq_lens, int max_seq_len, int num_splits, float scale,
+                                     void* workspace, size_t workspace_bytes, const void* win_k,
+                                     const void* win_v, int win_cap, const int32_t* win_lens, float* out) {
+  const fq::WindowIn win{win_k, win_v, win_cap, win_lens};
+  return decode_checked(stream, quant, cache, q, q_dtype, batch, num_q_heads, block_tables,
+                        max_blocks_per_seq, seq_lens, max_seq_len, num_splits, scale, workspace,
+                        workspace_bytes, out, nullptr, fq::DECODE_ALL, &win);
+}
+
+fq_status fq_window_workspace_size(int batch, int num_kv_heads, size_t* bytes) {
+  if (!bytes || batch < 0 || num_kv_heads <= 0) return FQ_ERR_INVALID_ARG;
+  *bytes = fq::window_scratch_bytes(batch, num_kv_heads);
+  return FQ_OK;
+}
+
+fq_status fq_window_append(void* stream, const fq_quantizer* quant, const fq_cache* cache, const void* k_new,
+                           const void* v_new, int kv_dtype, int batch, const int64_t* positions,
+                           const int64_t* evict_slots, void* win_k, void* win_v, int win_cap, void* workspace,
+                           size_t workspace_bytes) {
+  fq_status st = check_quantizer(quant);
+  if (st != FQ_OK) return st;
+  st = check_cache(cache, quant);
+  if (st != FQ_OK) return st;
+  if (kv_dtype != FQ_F32 && kv_dtype != FQ_BF16) return FQ_ERR_INVALID_ARG;
+  if (batch < 0 || win_cap <= 0 || win_cap > FQ_MAX_WINDOW) return FQ_ERR_INVALID_ARG;
+  if (batch == 0) return FQ_OK;
+  if (!k_new || !v_new || !positions || !evict_slots || !win_k || !win_v) return FQ_ERR_INVALID_ARG;
+  if (!aligned(k_new, 8) || !aligned(v_new, 8) || !aligned(positions, 8) || !aligned(evict_slots, 8) ||
+      !aligned(win_k, 16) || !aligned(win_v, 16))
+    return FQ_ERR_INVALID_ARG;
+  if (!workspace || !aligned(workspace, 256) ||
+      workspace_bytes < fq::window_scratch_bytes(batch, cache->num_kv_heads))
+    return FQ_ERR_WORKSPACE;
+  int e = fq::launch_window_append(stream, *quant, *cache, k_new, v_new, kv_dtype, batch, positions, evict_slots,
+                                   win_k, win_v, win_cap, workspace);
+  return e == 0 ? FQ_OK : FQ_ERR_HIP;
 }
 
 fq_status fq_step_prepare(void* stream, const fq_quantizer* quant, const fq_cache* cache,

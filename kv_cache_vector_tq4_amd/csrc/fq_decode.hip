@@ -71,6 +71,13 @@ struct DecodeArgs {
   int kv_bf16, bits;
   int batch, hq, hkv, group, splits, chunk, max_blocks, qjl_on, q_bf16;
   float scale;
+  // full-precision residual window (merge_group; null = none): bf16 K / V element
+  // (b, ring slot t, h, j) at ((b * win_cap + t) * hkv + h) * d + j, slots
+  // t < win_lens[b] valid
+  const uint16_t* win_k;
+  const uint16_t* win_v;
+  const int32_t* win_lens;
+  int win_cap;
 };
 
 // fp16 helpers shared by the matrix-core kernels.
@@ -252,12 +259,58 @@ __device__ __forceinline__ void part_dot(const float (&col)[D / KP], const float
   }
 }
 
+// The residual window's part of query head hidx (global index) in one wave: the
+// scores scale <q, k_t> of its window tokens (exact, fp32), their running max m,
+// sum l of exp(s_t - m) and o = sum_t exp(s_t - m) v_t (lane: coordinates 2 lane,
+// 2 lane + 1), in token order. m = -inf, l = 0 without tokens.
+__device__ __forceinline__ void window_partial(const DecodeArgs& a, int64_t hidx, int lane, float& m, float& l,
+                                               float& o0, float& o1) {
+  const int b = static_cast<int>(hidx / a.hq);
+  const int kvh = static_cast<int>(hidx - static_cast<int64_t>(b) * a.hq) / a.group;
+  float q0, q1;
+  if (a.q_bf16) {
+    const uint32_t w = reinterpret_cast<const uint32_t*>(a.q)[hidx * (D / 2) + lane];
+    q0 = __uint_as_float(w << 16);
+    q1 = __uint_as_float(w & 0xffff0000u);
+  } else {
+    const float2 x = reinterpret_cast<const float2*>(a.q)[hidx * (D / 2) + lane];
+    q0 = x.x;
+    q1 = x.y;
+  }
+  const int n = min(max(a.win_lens[b], 0), a.win_cap);
+  const int64_t ts = static_cast<int64_t>(a.hkv) * (D / 2);  // token stride in bf16 pairs
+  const int64_t base = (static_cast<int64_t>(b) * a.win_cap * a.hkv + kvh) * (D / 2) + lane;
+  const uint32_t* kp = reinterpret_cast<const uint32_t*>(a.win_k) + base;
+  const uint32_t* vp = reinterpret_cast<const uint32_t*>(a.win_v) + base;
+  for (int t = 0; t < n; ++t) {
+    const uint32_t kw = kp[t * ts], vw = vp[t * ts];
+    float sc = fmaf(q0, __uint_as_float(kw << 16), q1 * __uint_as_float(kw & 0xffff0000u));
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) sc += __shfl_xor(sc, off);
+    sc *= a.scale;
+    const float v0 = __uint_as_float(vw << 16), v1 = __uint_as_float(vw & 0xffff0000u);
+    if (sc > m) {
+      const float c = __expf(m - sc);
+      l = fmaf(l, c, 1.f);
+      o0 = fmaf(o0, c, v0);
+      o1 = fmaf(o1, c, v1);
+      m = sc;
+    } else {
+      const float p = __expf(sc - m);
+      l += p;
+      o0 = fmaf(p, v0, o0);
+      o1 = fmaf(p, v1, o1);
+    }
+  }
+}
+
 // Log-sum-exp merge of the splits of query heads head0 .. head0 + G - 1 (global
 // indices, G <= 16) and the output rotation, by a work-group of NT threads
-// (thread = (coordinate j, k-part kp)), with lds >= (17 + NT / D * 16) * D +
+// (thread = (coordinate j, k-part kp)), with lds >= (33 + NT / D * 16) * D +
 // 16 * FQ_MAX_SPLITS + 16 floats:
 //  1. wave w takes heads w, w + NT/64: lane sp holds split sp's (max, sum); the
-//     weights exp(m_sp - M) and 1 / sum_sp l_sp w_sp go to LDS;
+//     weights exp(m_sp - M) and 1 / sum_sp l_sp w_sp go to LDS (with a residual
+//     window, its part enters M and the sum, and its weighted values go to LDS);
 //  2. thread (j, kp) adds up coordinate j of splits sp = kp, kp + KP, ... for every
 //     head; the parts are summed;
 //  3. o = Pi^T O = sum_k Pi[k][j] o_rot[k], column j of Pi loaded first.
@@ -268,6 +321,7 @@ __device__ __forceinline__ void merge_group(const DecodeArgs& a, int64_t head0, 
   float* const s_part = s_o + FQ_MAX_GROUP * D;                 // [KP][16][D]
   float* const s_w = s_part + KP * FQ_MAX_GROUP * D;            // [16][FQ_MAX_SPLITS]
   float* const s_inv = s_w + FQ_MAX_GROUP * FQ_MAX_SPLITS;      // [16]
+  float* const s_win = s_inv + FQ_MAX_GROUP;                    // [16][D] window values (original frame)
   const int j = tid & (D - 1);
   const int kp = __builtin_amdgcn_readfirstlane(tid / D);
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
@@ -275,19 +329,27 @@ __device__ __forceinline__ void merge_group(const DecodeArgs& a, int64_t head0, 
   float pc[D / KP];
   col_part_load<KP>(a.pi, j, kp, pc);
   for (int h = wv; h < G; h += NT / 64) {
+    float mw = -INFINITY, lw = 0.f, ow0 = 0.f, ow1 = 0.f;
+    if (a.win_k) window_partial(a, head0 + h, lane, mw, lw, ow0, ow1);
     float m = -INFINITY, l = 0.f;
     if (lane < S) {
       const float2 x = reinterpret_cast<const float2*>(a.part_ml)[(head0 + h) * S + lane];
       m = x.x;
       l = x.y;
     }
-    const float M = wave_max(l > 0.f ? m : -INFINITY);
+    const float M = fmaxf(wave_max(l > 0.f ? m : -INFINITY), lw > 0.f ? mw : -INFINITY);
     const float w = (lane < S && l > 0.f) ? __expf(m - M) : 0.f;
     float L = l * w;
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) L += __shfl_xor(L, off);
+    const float ww = lw > 0.f ? __expf(mw - M) : 0.f;
+    L = fmaf(lw, ww, L);
     if (lane < S) s_w[h * FQ_MAX_SPLITS + lane] = w;
     if (lane == 0) s_inv[h] = L > 0.f ? 1.f / L : 0.f;
+    if (a.win_k) {
+      s_win[h * D + 2 * lane] = ow0 * ww;
+      s_win[h * D + 2 * lane + 1] = ow1 * ww;
+    }
   }
   __syncthreads();
   for (int h = 0; h < G; ++h) {
@@ -313,6 +375,7 @@ __device__ __forceinline__ void merge_group(const DecodeArgs& a, int64_t head0, 
     float v = 0.f;
 #pragma unroll
     for (int k = 0; k < KP; ++k) v += s_part[(k * FQ_MAX_GROUP + h) * D + j];
+    if (a.win_k) v = fmaf(s_win[h * D + j], s_inv[h], v);
     a.out[(head0 + h) * D + j] = v;
   }
 }
@@ -1701,7 +1764,7 @@ __global__ void __launch_bounds__(WAVES * 64, OCC) packed_decode_kernel(DecodeAr
 // One work-group per (KV head, sequence, part of the group, as above): merge_group
 // of those heads' splits.
 __global__ void __launch_bounds__(PQ_THREADS) merge_unrotate_kernel(DecodeArgs a) {
-  __shared__ __align__(16) float s_m[(17 + PQ_THREADS / D * 16) * D + 16 * FQ_MAX_SPLITS + 16];
+  __shared__ __align__(16) float s_m[(33 + PQ_THREADS / D * 16) * D + 16 * FQ_MAX_SPLITS + 16];
   const int hn = a.group / gridDim.z;
   merge_group<PQ_THREADS>(a, static_cast<int64_t>(blockIdx.y) * a.hq + blockIdx.x * a.group + blockIdx.z * hn, hn,
                           threadIdx.x, s_m);
@@ -1713,7 +1776,7 @@ int launch_decode(void* stream, const fq_quantizer& q, const fq_cache& c, const 
                   int q_dtype, int batch, int num_q_heads, const int32_t* block_tables,
                   int max_blocks_per_seq, const int32_t* seq_lens, int max_seq_len,
                   int num_splits, float scale, void* workspace, float* out,
-                  const AppendIn* app, int phase) {
+                  const AppendIn* app, int phase, const WindowIn* win) {
   const DecodeWorkspace ws =
       decode_workspace(batch, num_q_heads, c.num_kv_heads, D, q.qjl_dim, num_splits);
   uint8_t* wb = static_cast<uint8_t*>(workspace);
@@ -1762,6 +1825,12 @@ int launch_decode(void* stream, const fq_quantizer& q, const fq_cache& c, const 
     a.kv_hstride = app->head_stride;
     a.kv_bf16 = app->dtype == FQ_BF16 ? 1 : 0;
   }
+  if (win) {  // the window joins the merge: always the split path
+    a.win_k = static_cast<const uint16_t*>(win->k);
+    a.win_v = static_cast<const uint16_t*>(win->v);
+    a.win_lens = win->lens;
+    a.win_cap = win->cap;
+  }
   hipStream_t st = static_cast<hipStream_t>(stream);
 
   // Split kernel: packed matrix-core kernel for groups of up to 8 query heads; for
@@ -1772,7 +1841,7 @@ int launch_decode(void* stream, const fq_quantizer& q, const fq_cache& c, const 
   const bool v1 = impl && std::strcmp(impl, "mfma_v1") == 0;
   const int slots = (!valu && !v1) ? (a.group <= 4 ? 4 : a.group <= 8 ? 2 : 0) : 0;
   dim3 grid(num_splits, c.num_kv_heads, batch);
-  const bool only = slots > 0 && num_splits == 1 && std::getenv("FQ_DECODE_UNFUSED") == nullptr;
+  const bool only = slots > 0 && num_splits == 1 && !win && std::getenv("FQ_DECODE_UNFUSED") == nullptr;
   if (only && phase == DECODE_ALL) {
     // one work-group per (KV head, sequence) does everything in one launch
     // (appending the newest token first, when asked)

@@ -56,11 +56,30 @@ struct AppendIn {
 enum DecodePhase { DECODE_ALL = 0, DECODE_PREPARE = 1, DECODE_ATTEND = 2 };
 
 // app == nullptr: decode only; else append the newest tokens first (same stream).
+#define FQ_MAX_WINDOW 4096  // ring capacity limit of the residual window (tokens)
+
+// A full-precision residual window next to the compressed cache: bf16 K / V
+// [batch][cap][Hkv][d], ring slots t < lens[b] valid.
+struct WindowIn {
+  const void* k;
+  const void* v;
+  int cap;
+  const int32_t* lens;  // [batch]
+};
+
 int launch_decode(void* stream, const fq_quantizer& q, const fq_cache& c, const void* qv,
                   int q_dtype, int batch, int num_q_heads, const int32_t* block_tables,
                   int max_blocks_per_seq, const int32_t* seq_lens, int max_seq_len,
                   int num_splits, float scale, void* workspace, float* out,
-                  const AppendIn* app, int phase);
+                  const AppendIn* app, int phase, const WindowIn* win = nullptr);
+
+// The window's append: each sequence's new K / V token goes to ring slot
+// positions[b] % cap; the token it replaces is first compressed into the cache at
+// evict_slots[b] (< 0: not stored). scratch: 2 * batch * Hkv * d bf16.
+size_t window_scratch_bytes(int batch, int num_kv_heads);
+int launch_window_append(void* stream, const fq_quantizer& q, const fq_cache& c, const void* k_new,
+                         const void* v_new, int kv_dtype, int batch, const int64_t* positions,
+                         const int64_t* evict_slots, void* win_k, void* win_v, int cap, void* scratch);
 
 int launch_decompress(void* stream, const fq_quantizer& q, const fq_cache& c, const int64_t* slot_mapping,
                       int64_t num_tokens, int out_dtype, void* k_out, void* v_out, int64_t token_stride,
