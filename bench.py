@@ -255,6 +255,76 @@ def decompress_measure(qz, cache, slots, reps, stream):
             "bytes_per_vector": "codes %d + norm 4 in, %d out" % (d * cache.bits // 8, 2 * d)}
 
 
+def window_measure(qz, cache, q, bt, lens, slots_np, W, reps, stream):
+    """One decode step per layer with a W-token full-precision window (timed with events):
+    fq_window_append of each sequence's newest token (the token W positions back goes
+    from the ring into the compressed cache), then fq_decode_attention_window over the
+    compressed tokens and the ring. Runs on a copy of the cache (the append writes it)."""
+    import torch
+
+    from kv_cache_vector_tq4_amd import fq
+
+    B, Hq, d = q.shape
+    Hkv = cache.num_kv_heads
+    dev = q.device
+    cw = fq.PagedCache(cache.num_blocks, Hkv, d, cache.bits, cache.qjl_dim, device=dev)
+    for name, t in cache.fields().items():
+        cw.fields()[name].copy_(t)
+    g = torch.Generator(device=dev).manual_seed(4242)
+    wk = torch.randn((B, W, Hkv, d), generator=g, device=dev).to(torch.bfloat16)
+    wv = torch.randn((B, W, Hkv, d), generator=g, device=dev).to(torch.bfloat16)
+    kn = torch.randn((B, Hkv, d), generator=g, device=dev).to(torch.bfloat16)
+    vn = torch.randn((B, Hkv, d), generator=g, device=dev).to(torch.bfloat16)
+    offs = np.concatenate([[0], np.cumsum(lens)[:-1]])
+    pos = torch.from_numpy((lens - 1).astype(np.int64)).to(dev)
+    ev = torch.from_numpy(np.array([slots_np[offs[b] + lens[b] - 1 - W] for b in range(B)], np.int64)).to(dev)
+    lens_c = torch.from_numpy((lens - W).astype(np.int32)).to(dev)
+    win_lens = torch.full((B,), W, dtype=torch.int32, device=dev)
+    max_len = int(lens.max())
+    out = torch.empty((B, Hq, d), dtype=torch.float32, device=dev)
+    wsa = torch.empty(1 << 20, dtype=torch.uint8, device=dev)
+    app = lambda: fq.window_append(qz, cw, kn, vn, pos, ev, wk, wv, workspace=wsa)
+    def graph_us(fn, n=8):
+        """Mean GPU time of fn() from HIP-graph replays of n calls (no host gaps)."""
+        fn()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(side):
+            with torch.cuda.graph(g, stream=side):
+                for _ in range(n):
+                    fn()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / (reps * n)
+
+    per_split = {}
+    for sp in (1, 2, 4):
+        ws = torch.empty(fq.workspace_bytes(B, Hq, Hkv, d, qz.qjl_dim, max_len, sp), dtype=torch.uint8, device=dev)
+        per_split[sp] = graph_us(lambda: fq.decode_window(qz, cw, q, bt, lens_c, max_len, wk, wv, win_lens,
+                                                          num_splits=sp, workspace=ws, out=out))
+    ws1 = torch.empty(fq.workspace_bytes(B, Hq, Hkv, d, qz.qjl_dim, max_len, 1), dtype=torch.uint8, device=dev)
+    no_win = torch.zeros((B,), dtype=torch.int32, device=dev)
+    empty_us = graph_us(lambda: fq.decode_window(qz, cw, q, bt, lens_c, max_len, wk, wv, no_win, num_splits=1,
+                                                 workspace=ws1, out=out))
+    plain_us = graph_us(lambda: fq.decode(qz, cw, q, bt, lens_c, max_len, num_splits=1, workspace=ws1, out=out))
+    append_us = graph_us(app)
+    del cw
+    return {"what": "per layer, batch 32: fq_window_append + fq_decode_attention_window, %d-token bf16 window, "
+                    "the rest of each context compressed" % W,
+            "timing": "HIP-graph replays (8 calls per graph)",
+            "window": W, "append_us": append_us, "decode_us_by_splits": per_split,
+            "decode_us_empty_window_1_split": empty_us, "plain_decode_us_same_lengths": plain_us}
+
+
 def attention_cosines(q, k, v, lens, kv_rows, out, seqs):
     """Cosine of the decode outputs against exact softmax attention over the
     uncompressed (bf16) K and V, per (sequence, query head), for sampled sequences.
@@ -363,6 +433,7 @@ def main():
         del k, v
     torch.cuda.synchronize()
     decomp = decompress_measure(qz, caches[0], slots_all[slots_all >= 0].contiguous(), 5, stream)
+    win = window_measure(qz, caches[0], qs[0], bt, lens, slots_np, 128, 10, stream)
     ws_bytes = fq.workspace_bytes(B, Hq, Hkv, d, 128, max_len, splits)
     # one workspace per layer: each keeps its layer's prepared queries, so the
     # attention launches can also be replayed on their own
@@ -573,6 +644,7 @@ def main():
             "mfma_util": measured_mfma_util(),
         },
         "decompress": decomp,
+        "residual_window": win,
         "accuracy": dict(accuracy, what="cosine of decode outputs vs exact fp32 softmax attention over the "
                          "uncompressed bf16 K/V, layer 0, sequences 0 / 7 / 15 / 31, all 32 query heads"),
     }

@@ -260,9 +260,14 @@ __device__ __forceinline__ void part_dot(const float (&col)[D / KP], const float
 }
 
 // The residual window's part of query head hidx (global index) in one wave: the
-// scores scale <q, k_t> of its window tokens (exact, fp32), their running max m,
-// sum l of exp(s_t - m) and o = sum_t exp(s_t - m) v_t (lane: coordinates 2 lane,
-// 2 lane + 1), in token order. m = -inf, l = 0 without tokens.
+// scores scale <q, k_t> of its window tokens (exact, fp32), their max m, the sum l
+// of exp(s_t - m) and o = sum_t exp(s_t - m) v_t (lane: coordinates 2 lane,
+// 2 lane + 1). Rounds of 64 tokens: lane t scores token t0 + t against its whole K
+// row (the query's coordinates broadcast from the lane holding them), the round's
+// max and sum come from fixed-order lane reductions, then the lanes turn to
+// coordinates and add up the round's weighted V rows in token order. Each round
+// requests all its K and V rows before using any.
+// m = -inf, l = 0 without tokens.
 __device__ __forceinline__ void window_partial(const DecodeArgs& a, int64_t hidx, int lane, float& m, float& l,
                                                float& o0, float& o1) {
   const int b = static_cast<int>(hidx / a.hq);
@@ -279,28 +284,46 @@ __device__ __forceinline__ void window_partial(const DecodeArgs& a, int64_t hidx
   }
   const int n = min(max(a.win_lens[b], 0), a.win_cap);
   const int64_t ts = static_cast<int64_t>(a.hkv) * (D / 2);  // token stride in bf16 pairs
-  const int64_t base = (static_cast<int64_t>(b) * a.win_cap * a.hkv + kvh) * (D / 2) + lane;
-  const uint32_t* kp = reinterpret_cast<const uint32_t*>(a.win_k) + base;
-  const uint32_t* vp = reinterpret_cast<const uint32_t*>(a.win_v) + base;
-  for (int t = 0; t < n; ++t) {
-    const uint32_t kw = kp[t * ts], vw = vp[t * ts];
-    float sc = fmaf(q0, __uint_as_float(kw << 16), q1 * __uint_as_float(kw & 0xffff0000u));
+  const int64_t base = (static_cast<int64_t>(b) * a.win_cap * a.hkv + kvh) * (D / 2);
+  const uint32_t* kb = reinterpret_cast<const uint32_t*>(a.win_k) + base;
+  const uint32_t* vb = reinterpret_cast<const uint32_t*>(a.win_v) + base;
+  for (int t0 = 0; t0 < n; t0 += 64) {
+    const int t = t0 + lane;
+    const uint4* kr = reinterpret_cast<const uint4*>(kb + static_cast<int64_t>(min(t, n - 1)) * ts);
+    uint4 kw[16];
 #pragma unroll
-    for (int off = 32; off > 0; off >>= 1) sc += __shfl_xor(sc, off);
-    sc *= a.scale;
-    const float v0 = __uint_as_float(vw << 16), v1 = __uint_as_float(vw & 0xffff0000u);
-    if (sc > m) {
-      const float c = __expf(m - sc);
-      l = fmaf(l, c, 1.f);
-      o0 = fmaf(o0, c, v0);
-      o1 = fmaf(o1, c, v1);
-      m = sc;
-    } else {
-      const float p = __expf(sc - m);
-      l += p;
-      o0 = fmaf(p, v0, o0);
-      o1 = fmaf(p, v1, o1);
+    for (int i = 0; i < 16; ++i) kw[i] = kr[i];
+    // the round's V rows too, all requested before any is used (rows past n reread
+    // row n - 1 and get weight 0)
+    uint32_t vw[64];
+#pragma unroll
+    for (int u = 0; u < 64; ++u) vw[u] = vb[static_cast<int64_t>(min(t0 + u, n - 1)) * ts + lane];
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const uint32_t w4[4] = {kw[i].x, kw[i].y, kw[i].z, kw[i].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {  // bf16 pair dd = coordinates 2 dd, 2 dd + 1
+        const int dd = 4 * i + e;
+        const float qa = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(q0), dd));
+        const float qb = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(q1), dd));
+        s = fmaf(qa, __uint_as_float(w4[e] << 16), fmaf(qb, __uint_as_float(w4[e] & 0xffff0000u), s));
+      }
     }
+    s = t < n ? s * a.scale : -INFINITY;
+    const float mn = fmaxf(m, wave_max_dpp(s));  // lane 0's token is live
+    const float c = __expf(m - mn);              // 0 before the first round
+    const float p = __expf(s - mn);              // 0 for lanes past n
+    l = fmaf(l, c, wave_sum_dpp(p));
+    o0 *= c;
+    o1 *= c;
+#pragma unroll
+    for (int u = 0; u < 64; ++u) {
+      const float pu = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(p), u));
+      o0 = fmaf(pu, __uint_as_float(vw[u] << 16), o0);
+      o1 = fmaf(pu, __uint_as_float(vw[u] & 0xffff0000u), o1);
+    }
+    m = mn;
   }
 }
 
@@ -1704,13 +1727,27 @@ __global__ void __launch_bounds__(WAVES * 64, OCC) packed_decode_kernel(DecodeAr
     // the only split: o_rot = O / L per head, then out = Pi^T o_rot
     float* const s_or = s_ml + WAVES * HP * 2;  // [G][D]
     float* const s_pp = s_or + PK_PREP_GM * D;  // [4][PK_PREP_GM][D]
-    static_assert((WAVES * HP * (D + 2) + 5 * PK_PREP_GM * D) * 4 <= PK_LDS_BYTES, "epilogue fits the LDS");
+    float* const s_fw = s_pp + 4 * PK_PREP_GM * D;  // [G] weight of the residual window's values
+    static_assert((WAVES * HP * (D + 2) + 5 * PK_PREP_GM * D + PK_PREP_GM) * 4 <= PK_LDS_BYTES,
+                  "epilogue fits the LDS");
+    const int64_t head0 = static_cast<int64_t>(b) * a.hq + kvh * G;
+    constexpr float LOG2E = 1.4426950408889634f;
     for (int idx = tid; idx < G * D; idx += WAVES * 64) {
       const int hh = idx / D, j = idx % D;
       float M = -INFINITY;
 #pragma unroll
       for (int w = 0; w < WAVES; ++w)
         if (s_ml[(w * HP + hh) * 2 + 1] > 0.f) M = fmaxf(M, s_ml[(w * HP + hh) * 2]);
+      // a residual window's part (window_kernel, natural-log max) joins the softmax
+      float mw = -INFINITY, lwin = 0.f;
+      if (a.win_k) {
+        const float2 x = reinterpret_cast<const float2*>(a.part_ml)[head0 + hh];
+        lwin = x.y;
+        if (lwin > 0.f) {
+          mw = x.x * LOG2E;
+          M = fmaxf(M, mw);
+        }
+      }
       float o = 0.f, L = 0.f;
 #pragma unroll
       for (int w = 0; w < WAVES; ++w) {
@@ -1721,16 +1758,21 @@ __global__ void __launch_bounds__(WAVES * 64, OCC) packed_decode_kernel(DecodeAr
           L = fmaf(lw, f, L);
         }
       }
+      const float fw = lwin > 0.f ? exp2f(mw - M) : 0.f;
+      L = fmaf(lwin, fw, L);
       s_or[hh * D + j] = L > 0.f ? o / L : 0.f;
+      if (j == 0) s_fw[hh] = L > 0.f ? fw / L : 0.f;
     }
     __syncthreads();
     if (tid < PQ_THREADS) quarter_dot_any<PK_PREP_GM>(pc, s_or, jj, kq, G, s_pp);
     __syncthreads();
-    const int64_t head0 = static_cast<int64_t>(b) * a.hq + kvh * G;
     if (tid < PQ_THREADS) {
-      for (int h = kq; h < G; h += 4)
-        a.out[(head0 + h) * D + jj] = (s_pp[(0 * PK_PREP_GM + h) * D + jj] + s_pp[(1 * PK_PREP_GM + h) * D + jj]) +
-                                      (s_pp[(2 * PK_PREP_GM + h) * D + jj] + s_pp[(3 * PK_PREP_GM + h) * D + jj]);
+      for (int h = kq; h < G; h += 4) {
+        float v = (s_pp[(0 * PK_PREP_GM + h) * D + jj] + s_pp[(1 * PK_PREP_GM + h) * D + jj]) +
+                  (s_pp[(2 * PK_PREP_GM + h) * D + jj] + s_pp[(3 * PK_PREP_GM + h) * D + jj]);
+        if (a.win_k) v = fmaf(s_fw[h], a.part_o[(head0 + h) * D + jj], v);
+        a.out[(head0 + h) * D + jj] = v;
+      }
     }
     return;
   }
@@ -1758,6 +1800,19 @@ __global__ void __launch_bounds__(WAVES * 64, OCC) packed_decode_kernel(DecodeAr
       a.part_ml[base * 2 + 1] = L;
     }
   }
+}
+
+// One one-wave work-group per (KV head, sequence, query head of the group): the
+// residual window's part of the head (window_partial) into the workspace's
+// one-split partials, (natural-log max, sum) and the
+// unnormalized values in the original frame, for the single-launch kernel's epilogue.
+__global__ void __launch_bounds__(64) window_kernel(DecodeArgs a) {
+  const int kvh = blockIdx.x, b = blockIdx.y, hh = blockIdx.z, lane = threadIdx.x;
+  const int64_t hidx = static_cast<int64_t>(b) * a.hq + kvh * a.group + hh;
+  float m = -INFINITY, l = 0.f, o0 = 0.f, o1 = 0.f;
+  window_partial(a, hidx, lane, m, l, o0, o1);
+  reinterpret_cast<float2*>(a.part_o)[hidx * (D / 2) + lane] = make_float2(o0, o1);
+  if (lane == 0) reinterpret_cast<float2*>(a.part_ml)[hidx] = make_float2(m, l);
 }
 
 // ---------------------------------------------------------------- kernel 3
@@ -1825,7 +1880,7 @@ int launch_decode(void* stream, const fq_quantizer& q, const fq_cache& c, const 
     a.kv_hstride = app->head_stride;
     a.kv_bf16 = app->dtype == FQ_BF16 ? 1 : 0;
   }
-  if (win) {  // the window joins the merge: always the split path
+  if (win) {  // the window joins the merge (split path) or the single launch's epilogue
     a.win_k = static_cast<const uint16_t*>(win->k);
     a.win_v = static_cast<const uint16_t*>(win->v);
     a.win_lens = win->lens;
@@ -1841,8 +1896,10 @@ int launch_decode(void* stream, const fq_quantizer& q, const fq_cache& c, const 
   const bool v1 = impl && std::strcmp(impl, "mfma_v1") == 0;
   const int slots = (!valu && !v1) ? (a.group <= 4 ? 4 : a.group <= 8 ? 2 : 0) : 0;
   dim3 grid(num_splits, c.num_kv_heads, batch);
-  const bool only = slots > 0 && num_splits == 1 && !win && std::getenv("FQ_DECODE_UNFUSED") == nullptr;
+  const bool only = slots > 0 && num_splits == 1 && std::getenv("FQ_DECODE_UNFUSED") == nullptr;
   if (only && phase == DECODE_ALL) {
+    if (win)  // the window's parts first, into the (otherwise unused) one-split partials
+      hipLaunchKernelGGL(window_kernel, dim3(c.num_kv_heads, batch, a.group), dim3(64), 0, st, a);
     // one work-group per (KV head, sequence) does everything in one launch
     // (appending the newest token first, when asked)
 #define FQ_FUSED(BITS, SL, DT)                                                                                   \
