@@ -374,6 +374,24 @@ fq_status fq_decode_attention_window(void* stream, const fq_quantizer* quant, co
                                      void* workspace, size_t workspace_bytes, const void* win_k,
                                      const void* win_v, int win_cap, const int32_t* win_lens, float* out);
 
+/*
+ * fq_prefill_attention -- attention of many query tokens read straight from the
+ * compressed cache ("FlashQuant" page, "架构设计": attention with inline
+ * decompression for prefill). Query token t (q [num_queries][Hq][128]) belongs to
+ * sequence q_seq[t] (its block-table row) and attends to that sequence's cached
+ * tokens [0, q_lens[t]) -- q_lens[t] = position + 1 for causal prefill over tokens
+ * already written to the cache, the sequence length for full attention. Scores,
+ * QJL term, softmax and output exactly as fq_decode_attention (each query token is
+ * one of its batch entries); q_seq, q_lens: device int32 [num_queries], q_seq[t] a
+ * valid row of block_tables. Workspace: fq_decode_workspace_size with batch =
+ * num_queries. Output fp32 [num_queries][Hq][128]. Errors: as fq_decode_attention.
+ */
+fq_status fq_prefill_attention(void* stream, const fq_quantizer* quant, const fq_cache* cache, const void* q,
+                               int q_dtype, int num_queries, int num_q_heads, const int32_t* q_seq,
+                               const int32_t* q_lens, const int32_t* block_tables, int max_blocks_per_seq,
+                               int max_seq_len, int num_splits, float scale, void* workspace,
+                               size_t workspace_bytes, float* out);
+
 #ifdef __cplusplus
 }
 #endif

@@ -180,7 +180,8 @@ fq_status decode_checked(void* stream, const fq_quantizer* quant, const fq_cache
                          const int32_t* block_tables, int max_blocks_per_seq,
                          const int32_t* seq_lens, int max_seq_len, int num_splits, float scale,
                          void* workspace, size_t workspace_bytes, float* out,
-                         const fq::AppendIn* app, int phase, const fq::WindowIn* win = nullptr) {
+                         const fq::AppendIn* app, int phase, const fq::WindowIn* win = nullptr,
+                         const int32_t* bt_row = nullptr) {
   fq_status st = check_quantizer(quant);
   if (st != FQ_OK) return st;
   st = check_cache(cache, quant);
@@ -231,7 +232,7 @@ fq_status decode_checked(void* stream, const fq_quantizer* quant, const fq_cache
   }
   int e = fq::launch_decode(stream, *quant, *cache, q, q_dtype, batch, num_q_heads, block_tables,
                             max_blocks_per_seq, seq_lens, max_seq_len, s, scale, workspace, out,
-                            app, phase, win);
+                            app, phase, win, bt_row);
   return e == 0 ? FQ_OK : FQ_ERR_HIP;
 }
 
@@ -273,6 +274,17 @@ fq_status fq_decode_attention_window(void* stream, const fq_quantizer* quant, co
   return decode_checked(stream, quant, cache, q, q_dtype, batch, num_q_heads, block_tables,
                         max_blocks_per_seq, seq_lens, max_seq_len, num_splits, scale, workspace,
                         workspace_bytes, out, nullptr, fq::DECODE_ALL, &win);
+}
+
+fq_status fq_prefill_attention(void* stream, const fq_quantizer* quant, const fq_cache* cache, const void* q,
+                               int q_dtype, int num_queries, int num_q_heads, const int32_t* q_seq,
+                               const int32_t* q_lens, const int32_t* block_tables, int max_blocks_per_seq,
+                               int max_seq_len, int num_splits, float scale, void* workspace,
+                               size_t workspace_bytes, float* out) {
+  if (num_queries > 0 && (!q_seq || !aligned(q_seq, 4))) return FQ_ERR_INVALID_ARG;
+  return decode_checked(stream, quant, cache, q, q_dtype, num_queries, num_q_heads, block_tables,
+                        max_blocks_per_seq, q_lens, max_seq_len, num_splits, scale, workspace, workspace_bytes,
+                        out, nullptr, fq::DECODE_ALL, nullptr, q_seq);
 }
 
 fq_status fq_window_workspace_size(int batch, int num_kv_heads, size_t* bytes) {

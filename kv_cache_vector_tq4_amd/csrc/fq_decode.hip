@@ -78,7 +78,14 @@ struct DecodeArgs {
   const uint16_t* win_v;
   const int32_t* win_lens;
   int win_cap;
+  // block-table row of batch entry b (null: row b); many queries of one sequence
+  // (prefill) are batch entries sharing their sequence's row
+  const int32_t* bt_row;
 };
+
+__device__ __forceinline__ int64_t table_row(const DecodeArgs& a, int b) {
+  return a.bt_row ? static_cast<int64_t>(a.bt_row[b]) : static_cast<int64_t>(b);
+}
 
 // fp16 helpers shared by the matrix-core kernels.
 typedef _Float16 h4 __attribute__((ext_vector_type(4)));
@@ -686,7 +693,7 @@ __global__ void __launch_bounds__(256) split_attention_kernel(DecodeArgs a) {
   const int len = a.seq_lens[b];
   const int t0 = split * a.chunk;
   const int t1 = min(len, t0 + a.chunk);
-  const int32_t* bt = a.block_tables + static_cast<int64_t>(b) * a.max_blocks;
+  const int32_t* bt = a.block_tables + table_row(a, b) * a.max_blocks;
   cptr qr = uniform_ptr(a.qrot + (static_cast<int64_t>(b) * a.hq + kvh * G) * D);
   cptr qsp = uniform_ptr(a.qs + (static_cast<int64_t>(b) * a.hq + kvh * G) * D);
 
@@ -956,7 +963,7 @@ __global__ void __launch_bounds__(256, 2) split_mfma4_kernel(DecodeArgs a) {
   const int t0 = split * a.chunk;
   const int t1 = min(len, t0 + a.chunk);
   const int npages = t1 > t0 ? (t1 - t0 + FQ_BLOCK - 1) / FQ_BLOCK : 0;
-  const int32_t* bt = a.block_tables + static_cast<int64_t>(b) * a.max_blocks + t0 / FQ_BLOCK;
+  const int32_t* bt = a.block_tables + table_row(a, b) * a.max_blocks + t0 / FQ_BLOCK;
   const int tc = lane & (TAB_COPIES - 1);
   const uint32_t tc4 = static_cast<uint32_t>(tc) * 4u;
   const int sc8 = lane & (SGN_COPIES - 1);
@@ -1322,7 +1329,7 @@ __global__ void __launch_bounds__(WAVES * 64, OCC) packed_decode_kernel(DecodeAr
   };
   // The first 64 block numbers of this wave are requested together with the
   // sequence length (columns clamped to the table row).
-  const int32_t* btrow = a.block_tables + static_cast<int64_t>(b) * a.max_blocks;
+  const int32_t* btrow = a.block_tables + table_row(a, b) * a.max_blocks;
   int bt_cur = a.max_blocks > 0 ? btrow[min(t0 / FQ_BLOCK + page_of(lane), a.max_blocks - 1)] : 0;
   const int len = a.seq_lens[b];
   const int t1 = min(len, t0 + a.chunk);
@@ -1831,7 +1838,7 @@ int launch_decode(void* stream, const fq_quantizer& q, const fq_cache& c, const 
                   int q_dtype, int batch, int num_q_heads, const int32_t* block_tables,
                   int max_blocks_per_seq, const int32_t* seq_lens, int max_seq_len,
                   int num_splits, float scale, void* workspace, float* out,
-                  const AppendIn* app, int phase, const WindowIn* win) {
+                  const AppendIn* app, int phase, const WindowIn* win, const int32_t* bt_row) {
   const DecodeWorkspace ws =
       decode_workspace(batch, num_q_heads, c.num_kv_heads, D, q.qjl_dim, num_splits);
   uint8_t* wb = static_cast<uint8_t*>(workspace);
@@ -1849,6 +1856,7 @@ int launch_decode(void* stream, const fq_quantizer& q, const fq_cache& c, const 
   a.v_codes = c.v_codes;
   a.v_norm = c.v_norm;
   a.block_tables = block_tables;
+  a.bt_row = bt_row;
   a.seq_lens = seq_lens;
   a.qrot = reinterpret_cast<float*>(wb + ws.qrot);
   a.qs = reinterpret_cast<float*>(wb + ws.qs);

@@ -71,7 +71,8 @@ int launch_decode(void* stream, const fq_quantizer& q, const fq_cache& c, const 
                   int q_dtype, int batch, int num_q_heads, const int32_t* block_tables,
                   int max_blocks_per_seq, const int32_t* seq_lens, int max_seq_len,
                   int num_splits, float scale, void* workspace, float* out,
-                  const AppendIn* app, int phase, const WindowIn* win = nullptr);
+                  const AppendIn* app, int phase, const WindowIn* win = nullptr,
+                  const int32_t* bt_row = nullptr);
 
 // The window's append: each sequence's new K / V token goes to ring slot
 // positions[b] % cap; the token it replaces is first compressed into the cache at

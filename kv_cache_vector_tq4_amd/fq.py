@@ -72,6 +72,11 @@ EXPORTS = {
                                          ctypes.c_uint64, ctypes.c_int] + [ctypes.c_void_p] * 7),
     "fq_build_levels": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]),
     "fq_window_workspace_size": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, ctypes.POINTER(ctypes.c_size_t)]),
+    "fq_prefill_attention": (ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(QuantizerT), ctypes.POINTER(CacheT),
+                                            ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
+                                            ctypes.c_int, ctypes.c_int, ctypes.c_float, ctypes.c_void_p,
+                                            ctypes.c_size_t, ctypes.c_void_p]),
     "fq_window_append": (ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(QuantizerT), ctypes.POINTER(CacheT),
                                         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
                                         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
@@ -362,6 +367,30 @@ def decode_window(quant, cache, q, block_tables, seq_lens, max_seq_len, win_k, w
                                           _ptr(workspace), workspace.numel() * workspace.element_size(),
                                           _ptr(win_k), _ptr(win_v), win_k.shape[1], _ptr(win_lens), _ptr(out))
     _check(st, "fq_decode_attention_window")
+    return out
+
+
+def prefill(quant, cache, q, q_seq, q_lens, block_tables, max_seq_len, num_splits=0, scale=None, workspace=None,
+            out=None, stream=None):
+    """fq_prefill_attention: query tokens q [T, Hq, d] of sequences q_seq [T] (int32) attend to
+    their sequence's cached tokens [0, q_lens[t]) -> out fp32 [T, Hq, d]."""
+    import torch
+
+    T, Hq, d = q.shape
+    assert q.is_contiguous() and block_tables.dtype == torch.int32 and block_tables.is_contiguous()
+    for x in (q_seq, q_lens):
+        assert x.dtype == torch.int32 and x.is_contiguous() and x.numel() == T
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    need = workspace_bytes(T, Hq, cache.num_kv_heads, d, quant.qjl_dim, max_seq_len, num_splits)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    if out is None:
+        out = torch.empty((T, Hq, d), dtype=torch.float32, device=q.device)
+    st = lib().fq_prefill_attention(_stream(stream), ctypes.byref(quant.struct), ctypes.byref(cache.struct),
+                                    _ptr(q), _dtype_code(q), T, Hq, _ptr(q_seq), _ptr(q_lens), _ptr(block_tables),
+                                    block_tables.shape[1], int(max_seq_len), int(num_splits), float(scale),
+                                    _ptr(workspace), workspace.numel() * workspace.element_size(), _ptr(out))
+    _check(st, "fq_prefill_attention")
     return out
 
 
