@@ -325,6 +325,44 @@ def window_measure(qz, cache, q, bt, lens, slots_np, W, reps, stream):
             "decode_us_empty_window_1_split": empty_us, "plain_decode_us_same_lengths": plain_us}
 
 
+def prefill_measure(qz, cache, bt, lens, reps, stream):
+    """Causal prefill attention of sequence 0 of the layer over its own cached tokens:
+    one query token per position (q_lens = position + 1), fq_prefill_attention,
+    timed with events around HIP-graph replays."""
+    import torch
+
+    from kv_cache_vector_tq4_amd import fq
+
+    Hkv, d = cache.num_kv_heads, cache.head_dim
+    Hq = 4 * Hkv
+    L = int(lens[0])
+    dev = bt.device
+    g = torch.Generator(device=dev).manual_seed(777)
+    q = torch.randn((L, Hq, d), generator=g, device=dev).to(torch.bfloat16)
+    q_seq = torch.zeros(L, dtype=torch.int32, device=dev)
+    q_lens = torch.arange(1, L + 1, dtype=torch.int32, device=dev)
+    ws = torch.empty(fq.workspace_bytes(L, Hq, Hkv, d, qz.qjl_dim, L, 0), dtype=torch.uint8, device=dev)
+    out = torch.empty((L, Hq, d), dtype=torch.float32, device=dev)
+    fn = lambda: fq.prefill(qz, cache, q, q_seq, q_lens, bt, L, workspace=ws, out=out)
+    fn()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    gr = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(gr, stream=side):
+            fn()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    ms = _events_ms(lambda: gr.replay(), reps, stream)
+    attended = L * (L + 1) // 2
+    return {"what": "causal prefill attention of one %d-token sequence over its compressed cache "
+                    "(fq_prefill_attention: each query token a decode batch entry; no reuse of pages across "
+                    "queries beyond the caches)" % L,
+            "queries": L, "q_heads": Hq, "ms": ms, "queries_per_s": L / (ms * 1e-3),
+            "attended_token_heads_per_s": attended * Hkv / (ms * 1e-3),
+            "cache_bytes_read_per_query_sum": attended * Hkv * cache.bytes_per_token_head()}
+
+
 def attention_cosines(q, k, v, lens, kv_rows, out, seqs):
     """Cosine of the decode outputs against exact softmax attention over the
     uncompressed (bf16) K and V, per (sequence, query head), for sampled sequences.
@@ -434,6 +472,7 @@ def main():
     torch.cuda.synchronize()
     decomp = decompress_measure(qz, caches[0], slots_all[slots_all >= 0].contiguous(), 5, stream)
     win = window_measure(qz, caches[0], qs[0], bt, lens, slots_np, 128, 10, stream)
+    pre = prefill_measure(qz, caches[0], bt, lens, 3, stream)
     ws_bytes = fq.workspace_bytes(B, Hq, Hkv, d, 128, max_len, splits)
     # one workspace per layer: each keeps its layer's prepared queries, so the
     # attention launches can also be replayed on their own
@@ -645,6 +684,7 @@ def main():
         },
         "decompress": decomp,
         "residual_window": win,
+        "prefill": pre,
         "accuracy": dict(accuracy, what="cosine of decode outputs vs exact fp32 softmax attention over the "
                          "uncompressed bf16 K/V, layer 0, sequences 0 / 7 / 15 / 31, all 32 query heads"),
     }
