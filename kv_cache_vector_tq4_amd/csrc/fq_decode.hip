@@ -1,5 +1,5 @@
-// fq_decode_attention / fq_decode_step on gfx950: paged decode attention read
-// straight from the compressed cache.
+// fq_decode_attention / fq_decode_step (and the window and prefill variants) on
+// gfx950: paged decode attention read straight from the compressed cache.
 //
 // "FlashQuant" page, "架构设计" (paged decode with split-K FlashDecoding over
 // the compressed pages) and "QJL" (corrected key inner product); "TurboQuant"
@@ -18,6 +18,12 @@
 //    splits in split order, then o = Pi^T o_rot.
 //  * split_mfma4_kernel / split_attention_kernel: groups of 16 query heads (4-bit
 //    matrix-core / vector ALU), and the vector-ALU cross-check.
+//  * window_kernel: the residual full-precision window's part of every query head
+//    ("TurboQuant" blog, "Couche 5") for the single-launch path, whose epilogue
+//    folds it into the softmax; on the split path merge_unrotate_kernel computes
+//    it per head itself.
+// A batch entry's block-table row can be remapped (bt_row): fq_prefill_attention
+// runs many query tokens of one sequence as entries sharing its pages.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
