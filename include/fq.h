@@ -26,6 +26,15 @@
  *  - Out-of-range slot ids or block-table entries are not detected on the
  *    device: the caller guarantees 0 <= slot < num_blocks * 16 (or slot < 0 to
  *    skip) and 0 <= block_tables[b][i] < num_blocks for i < ceil(seq_lens[b]/16).
+ *    fq_validate_indices checks host copies of them before a call.
+ *  - Kernel choice depends on the shapes alone, except for three environment
+ *    variables read at each call, meant for cross-checks and measurements only:
+ *    FQ_COMPRESS_KERNEL = "direct" (small compress calls: one wave per 32-vector
+ *    tile instead of four) or "lane" (vector-ALU compress, one vector per lane);
+ *    FQ_DECODE_KERNEL = "valu" (vector-ALU split decode) or "mfma_v1" (the group-16
+ *    split kernels for every group size: matrix-core at 4 bits, vector-ALU at 2); FQ_DECODE_UNFUSED (any value:
+ *    a one-split decode runs as query preparation + attention launches). Every
+ *    choice computes the same function to the stated tolerances.
  */
 #ifndef FQ_H
 #define FQ_H
@@ -39,10 +48,11 @@ extern "C" {
 
 typedef enum fq_status {
   FQ_OK = 0,
-  FQ_ERR_INVALID_ARG = 1,  /* null / misaligned pointer, negative size, bad enum */
+  FQ_ERR_INVALID_ARG = 1,  /* null / misaligned pointer, negative size, bad enum, index out of range */
   FQ_ERR_UNSUPPORTED = 2,  /* valid but outside the supported shapes above */
   FQ_ERR_WORKSPACE = 3,    /* workspace missing or smaller than fq_decode_workspace_size */
-  FQ_ERR_HIP = 4           /* the HIP runtime reported an error at launch */
+  FQ_ERR_HIP = 4,          /* the HIP runtime reported an error at launch */
+  FQ_ERR_SCRATCH = 5       /* the call needs more than the library's static scratch holds */
 } fq_status;
 
 typedef enum fq_rotation { FQ_ROT_HAAR = 0, FQ_ROT_WHT = 1 } fq_rotation;
@@ -282,8 +292,11 @@ fq_status fq_decode_attention(void* stream, const fq_quantizer* quant, const fq_
  * within rounding of 0) may be decided differently; debug_y / debug_p expose
  * the values the codes were decided from.
  *
- * Two launches: query preparation together with the compression of the new
- * tokens, then the attention (plus a merge launch when num_splits > 1).
+ * Launches: when the call resolves to one split (num_splits = 1, or 0 with
+ * batch * Hkv >= 256) and G <= 8, one launch: each work-group appends its (sequence,
+ * KV head)'s newest K and V, prepares its queries, attends and rotates its output
+ * back. Otherwise three: query preparation together with the append, the split
+ * attention, the log-sum-exp merge with the output rotation.
  *
  *  k_new, v_new  device, element (b, h, j) of sequence b's newest token at
  *                b * token_stride + h * head_stride + j, dtype kv_dtype (FQ_F32 or
@@ -361,9 +374,12 @@ fq_status fq_window_append(void* stream, const fq_quantizer* quant, const fq_cac
  * fq_decode_attention_window -- fq_decode_attention over the compressed tokens
  * [0, seq_lens[b]) together with the window tokens in ring slots t < win_lens[b]
  * (device int32 [batch], clamped to [0, win_cap]): one softmax over both, the window's
- * scores scale * <q, k_t> and values exact (fp32 arithmetic on the bf16 rows). The
- * compressed part runs the split path (partials + merge; the window joins the
- * merge), so the workspace is fq_decode_workspace_size's for these sizes. A caller
+ * scores scale * <q, k_t> and values exact (fp32 arithmetic on the bf16 rows). When
+ * the call resolves to one split and G <= 8: a window launch (the window's maximum,
+ * sum and weighted values per query head, into the workspace) and then the
+ * single-launch decode, whose epilogue folds them into the softmax; otherwise the
+ * split path (partials, then the merge, which adds the window). The workspace is
+ * fq_decode_workspace_size's for these sizes. A caller
  * with n tokens per sequence passes seq_lens = max(0, n - win_cap) and win_lens =
  * min(n, win_cap). Errors: as fq_decode_attention.
  */
@@ -391,6 +407,28 @@ fq_status fq_prefill_attention(void* stream, const fq_quantizer* quant, const fq
                                const int32_t* q_lens, const int32_t* block_tables, int max_blocks_per_seq,
                                int max_seq_len, int num_splits, float scale, void* workspace,
                                size_t workspace_bytes, float* out);
+
+/*
+ * fq_validate_indices -- host, synchronous: the bounds check on packing and paging
+ * indices ("FlashQuant" page, "关键工程改进": an index bounds check added to the
+ * packing) for callers that hold host copies of their slot mappings, block tables
+ * and lengths (the device calls do not check them). Nothing is launched.
+ *  num_blocks     blocks of the cache the indices refer to (>= 0).
+ *  slot_mapping   host int64 [num_slots] or NULL: each entry < 0 (skip) or
+ *                 < num_blocks * 16.
+ *  block_tables   host int32 [batch][max_blocks_per_seq] or NULL; seq_lens host
+ *                 int32 [batch] (required with block_tables): 0 <= seq_lens[b] <=
+ *                 max_seq_len <= max_blocks_per_seq * 16, and block_tables[b][i] in
+ *                 [0, num_blocks) for every i < ceil(seq_lens[b] / 16).
+ *  what, where    optional outputs of the first failure: what = 1 (slot mapping),
+ *                 2 (sequence length), 3 (block table); where = its flat index
+ *                 (b * max_blocks_per_seq + i for a table entry). Both 0 on FQ_OK.
+ * Returns FQ_OK, or FQ_ERR_INVALID_ARG for the first index out of range or for
+ * inconsistent sizes.
+ */
+fq_status fq_validate_indices(int num_blocks, const int64_t* slot_mapping, int64_t num_slots,
+                              const int32_t* block_tables, int batch, int max_blocks_per_seq,
+                              const int32_t* seq_lens, int max_seq_len, int* what, int64_t* where);
 
 #ifdef __cplusplus
 }

@@ -93,11 +93,43 @@ const char* fq_status_string(int status) {
     case FQ_ERR_UNSUPPORTED: return "FQ_ERR_UNSUPPORTED";
     case FQ_ERR_WORKSPACE: return "FQ_ERR_WORKSPACE";
     case FQ_ERR_HIP: return "FQ_ERR_HIP";
+    case FQ_ERR_SCRATCH: return "FQ_ERR_SCRATCH";
     default: return "FQ_ERR_UNKNOWN";
   }
 }
 
 int fq_version(void) { return FQ_VERSION; }
+
+fq_status fq_validate_indices(int num_blocks, const int64_t* slot_mapping, int64_t num_slots,
+                              const int32_t* block_tables, int batch, int max_blocks_per_seq,
+                              const int32_t* seq_lens, int max_seq_len, int* what, int64_t* where) {
+  if (what) *what = 0;
+  if (where) *where = 0;
+  auto fail = [&](int w, int64_t i) {
+    if (what) *what = w;
+    if (where) *where = i;
+    return FQ_ERR_INVALID_ARG;
+  };
+  if (num_blocks < 0 || num_slots < 0) return FQ_ERR_INVALID_ARG;
+  if (num_slots > 0 && !slot_mapping) return FQ_ERR_INVALID_ARG;
+  const int64_t nslots = static_cast<int64_t>(num_blocks) * FQ_BLOCK;
+  for (int64_t i = 0; i < num_slots; ++i)
+    if (slot_mapping[i] >= nslots) return fail(1, i);
+  if (!block_tables) return FQ_OK;
+  if (!seq_lens || batch < 0 || max_blocks_per_seq < 0 || max_seq_len < 0) return FQ_ERR_INVALID_ARG;
+  if (static_cast<int64_t>(max_seq_len) > static_cast<int64_t>(max_blocks_per_seq) * FQ_BLOCK)
+    return FQ_ERR_INVALID_ARG;
+  for (int b = 0; b < batch; ++b) {
+    const int len = seq_lens[b];
+    if (len < 0 || len > max_seq_len) return fail(2, b);
+    const int64_t row = static_cast<int64_t>(b) * max_blocks_per_seq;
+    for (int i = 0; i < (len + FQ_BLOCK - 1) / FQ_BLOCK; ++i) {
+      const int32_t blk = block_tables[row + i];
+      if (blk < 0 || blk >= num_blocks) return fail(3, row + i);
+    }
+  }
+  return FQ_OK;
+}
 
 fq_status fq_compress(void* stream, const fq_quantizer* quant, const fq_cache* cache,
                       const void* k, const void* v, int dtype, int64_t num_tokens,

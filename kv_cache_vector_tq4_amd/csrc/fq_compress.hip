@@ -533,8 +533,14 @@ __global__ void __launch_bounds__((KEY ? 4 : CT_WAVES) * 64) compress_mfma_kerne
       s_pi[idx] = pack8(hi);
       s_pi[FRAG_U4 + idx] = pack8(lo);
       if constexpr (KEY) {
-        const float4* ss = reinterpret_cast<const float4*>(a.smat + row * D + col);
-        const float4 y0 = ss[0], y1 = ss[1];
+        // keys without QJL fields: the quantizer may hold no S at all (never read
+        // then: the tiles stop before the QJL product); zeros stand in for it
+        float4 y0 = make_float4(0.f, 0.f, 0.f, 0.f), y1 = y0;
+        if (a.qjl_on) {
+          const float4* ss = reinterpret_cast<const float4*>(a.smat + row * D + col);
+          y0 = ss[0];
+          y1 = ss[1];
+        }
         const float ys[8] = {y0.x, y0.y, y0.z, y0.w, y1.x, y1.y, y1.z, y1.w};
 #pragma unroll
         for (int e = 0; e < 8; ++e) split_f16b(ys[e], hi[e], lo[e]);

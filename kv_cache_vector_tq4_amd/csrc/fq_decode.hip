@@ -975,6 +975,10 @@ __global__ void __launch_bounds__(256, 2) split_mfma4_kernel(DecodeArgs a) {
   const int sc8 = lane & (SGN_COPIES - 1);
 
   float m_run = -INFINITY, l_run = 0.f;
+  // p * ||v|| * 2^-v_exp enters the value product in fp16 (p <= 1): v_exp (wave-
+  // uniform) rises when a page holds a value norm above 2^14 * 2^v_exp
+  int v_exp = 0;
+  float v_inv = 1.f, v_lim = 16384.f;
   f4 acc_o[8];
 #pragma unroll
   for (int t = 0; t < 8; ++t) acc_o[t] = f4{0.f, 0.f, 0.f, 0.f};
@@ -1034,15 +1038,35 @@ __global__ void __launch_bounds__(256, 2) split_mfma4_kernel(DecodeArgs a) {
         for (int e = 0; e < 4; ++e) acc_o[t][e] *= al[e];
       m_run = m_new;
     }
-    const float vnv[4] = {d.vn.x, d.vn.y, d.vn.z, d.vn.w};
+    // value norms of tokens outside the split may be anything: zero them
+    float vnv[4] = {d.vn.x, d.vn.y, d.vn.z, d.vn.w};
+    float vm = 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      vnv[e] = sc[e] != -INFINITY ? vnv[e] : 0.f;
+      vm = fmaxf(vm, vnv[e]);
+    }
+    if (__any(vm > v_lim)) {
+      vm = wave_max(vm);
+      if (vm > v_lim) {  // wave-uniform
+        int ex;
+        frexpf(vm, &ex);  // vm < 2^ex, and ex >= v_exp + 15
+        const float vf = ldexpf(1.f, v_exp - (ex - 14));
+        v_exp = ex - 14;
+        v_inv = ldexpf(1.f, -v_exp);
+        v_lim = ldexpf(16384.f, v_exp);
+#pragma unroll
+        for (int t = 0; t < 8; ++t) acc_o[t] *= vf;
+      }
+    }
     uint32_t ph[2], pl[2];
 #pragma unroll
     for (int e = 0; e < 4; e += 2) {
       const float p0 = __expf(sc[e] - m_run), p1 = __expf(sc[e + 1] - m_run);
       l_run += p0 + p1;
       _Float16 h0, l0, h1, l1;
-      split_f16(p0 * vnv[e], h0, l0);
-      split_f16(p1 * vnv[e + 1], h1, l1);
+      split_f16(p0 * (vnv[e] * v_inv), h0, l0);
+      split_f16(p1 * (vnv[e + 1] * v_inv), h1, l1);
       ph[e / 2] = h2bits(h0, h1);
       pl[e / 2] = h2bits(l0, l1);
     }
@@ -1092,7 +1116,7 @@ __global__ void __launch_bounds__(256, 2) split_mfma4_kernel(DecodeArgs a) {
     s_ml[(wave * 16 + n) * 2] = m_run;
     s_ml[(wave * 16 + n) * 2 + 1] = l_run;
   }
-  const float unscale = 1.0f / static_cast<float>(1 << LEV_SHIFT);
+  const float unscale = ldexpf(1.0f, v_exp - LEV_SHIFT);
 #pragma unroll
   for (int t = 0; t < 8; ++t)
 #pragma unroll
@@ -1541,6 +1565,11 @@ __global__ void __launch_bounds__(WAVES * 64, OCC) packed_decode_kernel(DecodeAr
     m_run[k] = -INFINITY;
     l_run[k] = 0.f;
   }
+  // The value product takes p * ||v|| * 2^-v_exp in fp16 (p < 2^8 by the lazy max):
+  // v_exp (wave-uniform) rises, like the running max, when a page holds a value norm
+  // above 2^7 * 2^v_exp, so that the operand stays below 2^15 whatever the norms.
+  int v_exp = 0;
+  float v_inv = 1.f, v_lim = 128.f;
   f4 acc_o[8];
 #pragma unroll
   for (int t = 0; t < 8; ++t) acc_o[t] = f4{0.f, 0.f, 0.f, 0.f};
@@ -1598,7 +1627,7 @@ __global__ void __launch_bounds__(WAVES * 64, OCC) packed_decode_kernel(DecodeAr
     for (int k = 0; k < HL; ++k) grow = grow || (sc[k] > m_run[k] + PK_TAU);
     return grow;
   };
-  auto rescale = [&](const float (&mx)[HL]) {  // mx: this lane's candidate maxima
+  auto rescale = [&](const float (&mx)[HL], float vc) {  // mx: this lane's candidate maxima
     float al[HL];
 #pragma unroll
     for (int k = 0; k < HL; ++k) {
@@ -1607,6 +1636,19 @@ __global__ void __launch_bounds__(WAVES * 64, OCC) packed_decode_kernel(DecodeAr
       l_run[k] *= al[k];
       m_run[k] = m_new;
     }
+    // vc: this lane's value norm (0 for a token outside the split)
+    const float vm = wave_max_dpp(vc);
+    float vf = 1.f;
+    if (vm > v_lim) {  // wave-uniform
+      int ex;
+      frexpf(vm, &ex);  // vm < 2^ex, and ex >= v_exp + 8
+      vf = ldexpf(1.f, v_exp - (ex - 7));
+      v_exp = ex - 7;
+      v_inv = ldexpf(1.f, -v_exp);
+      v_lim = ldexpf(128.f, v_exp);
+    }
+#pragma unroll
+    for (int k = 0; k < HL; ++k) al[k] *= vf;
     // acc_o rows 4g .. 4g+3 are (head HL g + k, slot) pairs
     const f4 av = HL == 1 ? f4{al[0], al[0], al[0], al[0]} : f4{al[0], al[0], al[HL - 1], al[HL - 1]};
 #pragma unroll
@@ -1620,7 +1662,7 @@ __global__ void __launch_bounds__(WAVES * 64, OCC) packed_decode_kernel(DecodeAr
       const float pr = live ? __builtin_amdgcn_exp2f(sc[k] - m_run[k]) : 0.f;
       l_run[k] += pr;
       _Float16 ph, pl;
-      split_f16(pr * vn, ph, pl);
+      split_f16(live ? pr * vn : 0.f, ph, pl);  // a norm past the sequence may be anything
       xp[k] = h2bits(ph, pl);
     }
   };
@@ -1678,9 +1720,10 @@ __global__ void __launch_bounds__(WAVES * 64, OCC) packed_decode_kernel(DecodeAr
   auto process = [&](const PkPage<BITS>& d, int p) {
     float sc[HL];
     score(d, p, true, sc);
-    if (__any(grows(sc))) rescale(sc);
+    const float vc = sc[0] != -INFINITY ? d.vn : 0.f;
+    if (__any(grows(sc) || vc > v_lim)) rescale(sc, vc);
     uint32_t xp[HL];
-    probs(sc, d.vn, xp);
+    probs(sc, d.vn * v_inv, xp);
     pv(d, xp);
   };
 
@@ -1729,7 +1772,7 @@ __global__ void __launch_bounds__(WAVES * 64, OCC) packed_decode_kernel(DecodeAr
       s_ml[(wave * HP + HL * g + k) * 2 + 1] = l_run[k];
     }
   }
-  const float unscale = 1.0f / static_cast<float>(1 << LEV_SHIFT);
+  const float unscale = ldexpf(1.0f, v_exp - LEV_SHIFT);
 #pragma unroll
   for (int t = 0; t < 8; ++t) {
     const int dim = 8 * n + (BITS == 4 ? t : (t >> 1) + 4 * (t & 1));  // 2-bit: r1, r2 byte order

@@ -13,7 +13,7 @@ import numpy as np
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libfq.so")
 
-FQ_OK, FQ_ERR_INVALID_ARG, FQ_ERR_UNSUPPORTED, FQ_ERR_WORKSPACE, FQ_ERR_HIP = range(5)
+FQ_OK, FQ_ERR_INVALID_ARG, FQ_ERR_UNSUPPORTED, FQ_ERR_WORKSPACE, FQ_ERR_HIP, FQ_ERR_SCRATCH = range(6)
 ROT_HAAR, ROT_WHT = 0, 1
 F32, BF16 = 0, 1
 CB_GAUSSIAN, CB_SPHERE = 0, 1
@@ -95,6 +95,9 @@ EXPORTS = {
     "fq_pack_mfma_operands": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p,
                                              ctypes.c_size_t]),
     "fq_decode_auto_splits": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, ctypes.c_int]),
+    "fq_validate_indices": (ctypes.c_int, [ctypes.c_int, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
+                                           ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_int,
+                                           ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_int64)]),
     "fq_decode_workspace_size": (ctypes.c_int, [ctypes.c_int] * 7 + [ctypes.POINTER(ctypes.c_size_t)]),
     "fq_decode_attention": (ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(QuantizerT), ctypes.POINTER(CacheT),
                                            ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
@@ -306,6 +309,35 @@ def compress(quant, cache, k, v, slot_mapping, debug=False, stream=None):
                            _ptr(slot_mapping), _ptr(dy), _ptr(dp))
     _check(st, "fq_compress")
     return (dy, dp) if debug else None
+
+
+def _host_array(x, dtype):
+    if x is None:
+        return None
+    if hasattr(x, "detach"):
+        x = x.detach().cpu().numpy()
+    return np.ascontiguousarray(x, dtype=dtype)
+
+
+def validate_indices(num_blocks, slot_mapping=None, block_tables=None, seq_lens=None, max_seq_len=None):
+    """fq_validate_indices on host copies of a slot mapping and / or block tables with their
+    lengths. Returns None when every index is in range; raises FQError (with .what and
+    .where: 1 slot, 2 length, 3 table entry, and its flat index) otherwise."""
+    sm = _host_array(slot_mapping, np.int64)
+    bt = _host_array(block_tables, np.int32)
+    sl = _host_array(seq_lens, np.int32)
+    p = lambda a: None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+    batch = 0 if bt is None else bt.shape[0]
+    width = 0 if bt is None else bt.shape[1]
+    if max_seq_len is None:
+        max_seq_len = 0 if sl is None or sl.size == 0 else int(sl.max())
+    what, where = ctypes.c_int(0), ctypes.c_int64(0)
+    st = lib().fq_validate_indices(int(num_blocks), p(sm), 0 if sm is None else sm.size, p(bt), batch, width,
+                                   p(sl), int(max_seq_len), ctypes.byref(what), ctypes.byref(where))
+    if st != FQ_OK:
+        err = FQError(st, "fq_validate_indices")
+        err.what, err.where = what.value, where.value
+        raise err
 
 
 def auto_splits(batch, num_kv_heads, max_seq_len):

@@ -185,3 +185,40 @@ def test_pack_mfma_operands_layout():
     rows = sorted(_perm_row(T, r) for T in range(4) for r in range(32) if (r >> 2) & 1 == 0)
     assert rows == list(range(64))
     assert fq.lib().fq_pack_mfma_operands(None, None, 128, None, 0) == fq.FQ_ERR_INVALID_ARG
+
+
+def test_validate_indices_reports_every_error():
+    """The host-side bounds check on slot ids, lengths and block-table entries
+    (FlashQuant page, section 关键工程改进: index bounds checks on packing)."""
+    nb = 10
+    ok_slots = np.array([0, 5, -1, nb * 16 - 1], np.int64)
+    fq.validate_indices(nb, slot_mapping=ok_slots)
+    fq.validate_indices(nb, slot_mapping=np.zeros(0, np.int64))
+    with pytest.raises(fq.FQError) as e:
+        fq.validate_indices(nb, slot_mapping=np.array([3, nb * 16, 2], np.int64))
+    assert (e.value.what, e.value.where, e.value.status) == (1, 1, fq.FQ_ERR_INVALID_ARG)
+    bt = np.array([[0, 9, 3, -5], [7, 8, 12, 42]], np.int32)  # entries past each length are not read
+    lens = np.array([48, 32], np.int32)
+    fq.validate_indices(nb, block_tables=bt, seq_lens=lens, max_seq_len=64)
+    fq.validate_indices(nb, slot_mapping=ok_slots, block_tables=bt, seq_lens=lens)
+    with pytest.raises(fq.FQError) as e:  # block 12 is the 3rd block of sequence 1 (length 33)
+        fq.validate_indices(nb, block_tables=bt, seq_lens=np.array([48, 33], np.int32), max_seq_len=64)
+    assert (e.value.what, e.value.where) == (3, 1 * 4 + 2)
+    with pytest.raises(fq.FQError) as e:  # negative entry within the length
+        fq.validate_indices(nb, block_tables=bt, seq_lens=np.array([64, 0], np.int32), max_seq_len=64)
+    assert (e.value.what, e.value.where) == (3, 3)
+    with pytest.raises(fq.FQError) as e:  # length above max_seq_len
+        fq.validate_indices(nb, block_tables=bt, seq_lens=np.array([16, 50], np.int32), max_seq_len=49)
+    assert (e.value.what, e.value.where) == (2, 1)
+    with pytest.raises(fq.FQError) as e:  # negative length
+        fq.validate_indices(nb, block_tables=bt, seq_lens=np.array([-1, 0], np.int32), max_seq_len=64)
+    assert (e.value.what, e.value.where) == (2, 0)
+    with pytest.raises(fq.FQError) as e:  # max_seq_len wider than the table
+        fq.validate_indices(nb, block_tables=bt, seq_lens=lens, max_seq_len=65)
+    assert e.value.what == 0
+    L = fq.lib()
+    assert L.fq_validate_indices(-1, None, 0, None, 0, 0, None, 0, None, None) == fq.FQ_ERR_INVALID_ARG
+    assert L.fq_validate_indices(nb, None, 3, None, 0, 0, None, 0, None, None) == fq.FQ_ERR_INVALID_ARG
+    assert L.fq_validate_indices(nb, None, 0, ok_slots.ctypes.data_as(ctypes.c_void_p), 1, 4, None, 0,
+                                 None, None) == fq.FQ_ERR_INVALID_ARG  # table without lengths
+    assert fq.status_string(fq.FQ_ERR_SCRATCH) == "FQ_ERR_SCRATCH"

@@ -61,7 +61,7 @@ def test_decompress_with_sphere_codebook(gpu_lib):
     k_hat, v_hat = fq.decompress(qz, cache, torch.from_numpy(slots).cuda())
     torch.cuda.synchronize()
     for name, g in (("k", k_hat), ("v", v_hat)):
-        gg = g.cpu().numpy().astype(np.float64)
+        gg = g.cpu().numpy()  # rows of skipped slots are never written: only stored rows are read
         for t_, s in enumerate(slots):
             if s < 0:
                 continue
@@ -69,4 +69,4 @@ def test_decompress_with_sphere_codebook(gpu_lib):
             idx = quantize.unpack_codes(host[name + "_codes"][blk, :, off], 4, 128)
             nrm = host[name + "_norm"][blk, :, off]
             ref = quantize.reconstruct(nrm, idx, oq["levels"], oq["pi"])
-            assert np.all(np.abs(gg[t_] - ref) <= 1e-5 * np.asarray(nrm, np.float64)[:, None]), (name, t_)
+            assert np.all(np.abs(gg[t_].astype(np.float64) - ref) <= 1e-5 * np.asarray(nrm, np.float64)[:, None]), (name, t_)

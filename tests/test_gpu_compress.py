@@ -1,6 +1,7 @@
 """GPU parity of fq_compress against the oracle (through the C ABI)."""
 import numpy as np
 import pytest
+import torch
 
 from kv_cache_vector_tq4_amd import fq, synth
 from tests import parity
@@ -128,3 +129,18 @@ def test_compress_kernels_derive_operands_without_prepared_buffer(gpu_lib, bits,
     w, inp = parity.small_workload(2, 8, 4, [300, 45], 304, dtype=dtype, bits=bits, seed=67)
     qz, cache, dy, dp, oq, _ = _run(w, inp, prepared=False)
     parity.check_compress(inp, oq, cache, dy, dp)
+
+
+@pytest.mark.parametrize("prepared", [False, True])
+def test_compress_quantizer_without_qjl_matrix(gpu_lib, prepared):
+    """A quantizer with no QJL matrix at all (qjl_dim 0) and an MSE-only cache, with
+    and without the prepared matrix-core operands: keys use the MSE encoding only,
+    checked against the oracle under the fed protocol."""
+    w, inp = parity.small_workload(2, 4, 2, [300, 77], 304, seed=91)
+    t = parity.torch_inputs(inp, w.dtype)
+    oq = parity.oracle_quantizer(4)
+    qz = fq.Quantizer(4, 128, fq.ROT_HAAR, 1, 2, 0, prepared=prepared)
+    cache = fq.PagedCache(inp["num_blocks"], 2, 128, 4, 0)
+    dy, _ = fq.compress(qz, cache, t["k"], t["v"], t["slots"], debug=True)
+    torch.cuda.synchronize()
+    print("near-tie mismatches", parity.check_compress(inp, oq, cache, dy, None))

@@ -155,3 +155,21 @@ def test_llama70b_layer_ctx32k_full_size(gpu_lib, rot):
     print("splits", splits, "max-abs", err, "cos vs exact", parity.cosine(out, parity.exact(inp)))
     assert splits == 64
     assert err <= parity.DECODE_TOL
+
+
+@pytest.mark.parametrize("vscale", [100.0, 1e4])
+@pytest.mark.parametrize("splits", [1, 3])
+@pytest.mark.parametrize("bits", [4, 2])
+@pytest.mark.parametrize("G", [4, 8, 16])
+def test_decode_large_value_norms(gpu_lib, G, bits, splits, vscale):
+    """Values scaled x100 and x1e4 (norms ~1.1e3 and ~1.1e5): the fp16 operand of the
+    value product is kept in range by a power-of-two exponent that follows the value
+    norms; the output matches the oracle within 1e-3 of the value scale."""
+    w, inp = parity.small_workload(2, 2 * G, 2, [900, 333], 912, bits=bits, seed=200 + G)
+    inp = dict(inp)
+    inp["v"] = inp["v"] * np.float32(vscale)
+    out, ref, _ = _decode_case(w, inp, num_splits=splits)
+    assert np.all(np.isfinite(out))
+    err = np.max(np.abs(out - ref)) / vscale
+    print("max-abs / scale", err)
+    assert err <= parity.DECODE_TOL
