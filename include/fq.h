@@ -430,6 +430,32 @@ fq_status fq_validate_indices(int num_blocks, const int64_t* slot_mapping, int64
                               const int32_t* block_tables, int batch, int max_blocks_per_seq,
                               const int32_t* seq_lens, int max_seq_len, int* what, int64_t* where);
 
+/*
+ * fq_decode_attention_noalloc -- fq_decode_attention for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation). Same arguments, result and kernels, except
+ * that there is no workspace argument: the decode's workspace (prepared queries and
+ * per-split partials, fq_decode_workspace_size bytes) is a static device array of
+ * the library, FQ_STATIC_SCRATCH_BYTES on each GPU it runs on, held until the
+ * process ends. Its device address is looked up on the first call on each device
+ * (with that device current). The call allocates nothing.
+ *  - Calls whose workspace would exceed FQ_STATIC_SCRATCH_BYTES return
+ *    FQ_ERR_SCRATCH and launch nothing (8 MiB holds, e.g., batch 32 x 32 query
+ *    heads at 4 splits, or batch 1 x 64 query heads at 64 splits).
+ *  - Every call on one GPU uses the same array, which keeps the last call's
+ *    contents (nothing in it needs to start at zero: each call writes every part it
+ *    reads). Calls that overlap on one GPU (different streams, or threads without
+ *    ordering) race on it and give undefined results; order them on one stream.
+ * Errors: as fq_decode_attention, plus FQ_ERR_SCRATCH (size) and FQ_ERR_HIP (the
+ * address lookup failed).
+ */
+#define FQ_STATIC_SCRATCH_BYTES (8u << 20)
+fq_status fq_decode_attention_noalloc(void* stream, const fq_quantizer* quant, const fq_cache* cache,
+                                      const void* q, int q_dtype, int batch, int num_q_heads,
+                                      const int32_t* block_tables, int max_blocks_per_seq,
+                                      const int32_t* seq_lens, int max_seq_len, int num_splits,
+                                      float scale, float* out);
+
 #ifdef __cplusplus
 }
 #endif

@@ -95,6 +95,11 @@ EXPORTS = {
     "fq_pack_mfma_operands": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p,
                                              ctypes.c_size_t]),
     "fq_decode_auto_splits": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, ctypes.c_int]),
+    "fq_decode_attention_noalloc": (ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(QuantizerT),
+                                                   ctypes.POINTER(CacheT), ctypes.c_void_p, ctypes.c_int,
+                                                   ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_int,
+                                                   ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_float,
+                                                   ctypes.c_void_p]),
     "fq_validate_indices": (ctypes.c_int, [ctypes.c_int, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
                                            ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_int,
                                            ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_int64)]),
@@ -371,6 +376,24 @@ def decode(quant, cache, q, block_tables, seq_lens, max_seq_len, num_splits=0, s
                                    _ptr(seq_lens), int(max_seq_len), int(num_splits), float(scale),
                                    _ptr(workspace), workspace.numel() * workspace.element_size(), _ptr(out))
     _check(st, "fq_decode_attention")
+    return out
+
+
+STATIC_SCRATCH_BYTES = 8 << 20
+
+
+def decode_noalloc(quant, cache, q, block_tables, seq_lens, max_seq_len, out, num_splits=0, scale=None,
+                   stream=None):
+    """fq_decode_attention_noalloc: fq_decode_attention with the library's static scratch as its
+    workspace; the caller passes the output (fp32 [B, Hq, d]); nothing is allocated."""
+    B, Hq, d = q.shape
+    assert q.is_contiguous() and block_tables.is_contiguous() and seq_lens.is_contiguous()
+    assert out.shape == (B, Hq, d) and out.is_contiguous()
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    st = lib().fq_decode_attention_noalloc(_stream(stream), ctypes.byref(quant.struct), ctypes.byref(cache.struct),
+                                           _ptr(q), _dtype_code(q), B, Hq, _ptr(block_tables), block_tables.shape[1],
+                                           _ptr(seq_lens), int(max_seq_len), int(num_splits), float(scale), _ptr(out))
+    _check(st, "fq_decode_attention_noalloc")
     return out
 
 
