@@ -25,10 +25,10 @@ def _softmax(s):
     return e / np.sum(e, axis=-1, keepdims=True)
 
 
-def head_records(cache, bt_row, seq_len, kvh, bits, d, m):
+def head_records(cache, bt_row, seq_len, kvh, bits, d, m, key_bits=None):
     rec = paged.read(cache, bt_row, seq_len, kvh)
     out = {
-        "k_idx": unpack_codes(rec["k_codes"], bits, d),
+        "k_idx": unpack_codes(rec["k_codes"], bits if key_bits is None else key_bits, d),
         "k_n": rec["k_norm"].astype(np.float64),
         "v_idx": unpack_codes(rec["v_codes"], bits, d),
         "v_n": rec["v_norm"].astype(np.float64),
@@ -51,17 +51,20 @@ def key_scores(q_rot, k_levels, rec, s):
     return sc
 
 
-def decode_rotated(q, cache, block_tables, seq_lens, levels32, pi, s, bits, scale=None):
+def decode_rotated(q, cache, block_tables, seq_lens, levels32, pi, s, bits, scale=None, key_levels32=None,
+                   key_bits=None):
     """Form 1. q: [B, Hq, d]; returns out [B, Hq, d] float64.
 
     pi, s: the stored fp32 operators promoted to float64; s may be None for
-    MSE-only keys (no QJL fields in the cache).
+    MSE-only keys (no QJL fields in the cache). key_levels32 / key_bits: the keys'
+    codebook and width when they differ from the values' (levels32, bits).
     """
     q = np.asarray(q, dtype=np.float64)
     B, Hq, d = q.shape
     Hkv = cache["k_norm"].shape[1]
     G = Hq // Hkv
     c = np.asarray(levels32, dtype=np.float64)
+    ck = c if key_levels32 is None else np.asarray(key_levels32, dtype=np.float64)
     scale = 1.0 / np.sqrt(d) if scale is None else scale
     m = s.shape[0] if s is not None else 0
     out = np.zeros((B, Hq, d))
@@ -70,8 +73,8 @@ def decode_rotated(q, cache, block_tables, seq_lens, levels32, pi, s, bits, scal
         if L == 0:
             continue
         for kvh in range(Hkv):
-            r = head_records(cache, block_tables[b], L, kvh, bits, d, m)
-            kc = c[r["k_idx"]]
+            r = head_records(cache, block_tables[b], L, kvh, bits, d, m, key_bits)
+            kc = ck[r["k_idx"]]
             vc = c[r["v_idx"]]
             for g in range(G):
                 h = kvh * G + g
@@ -82,13 +85,15 @@ def decode_rotated(q, cache, block_tables, seq_lens, levels32, pi, s, bits, scal
     return out
 
 
-def decode_reconstructed(q, cache, block_tables, seq_lens, levels32, pi, s, bits, scale=None):
+def decode_reconstructed(q, cache, block_tables, seq_lens, levels32, pi, s, bits, scale=None, key_levels32=None,
+                         key_bits=None):
     """Form 2: reconstruct k_hat, v_hat in the original frame, then plain attention."""
     q = np.asarray(q, dtype=np.float64)
     B, Hq, d = q.shape
     Hkv = cache["k_norm"].shape[1]
     G = Hq // Hkv
     c = np.asarray(levels32, dtype=np.float64)
+    ck = c if key_levels32 is None else np.asarray(key_levels32, dtype=np.float64)
     scale = 1.0 / np.sqrt(d) if scale is None else scale
     m = s.shape[0] if s is not None else 0
     s_orig = s @ pi if s is not None else None
@@ -98,8 +103,8 @@ def decode_reconstructed(q, cache, block_tables, seq_lens, levels32, pi, s, bits
         if L == 0:
             continue
         for kvh in range(Hkv):
-            r = head_records(cache, block_tables[b], L, kvh, bits, d, m)
-            k_hat = r["k_n"][:, None] * (c[r["k_idx"]] @ pi)
+            r = head_records(cache, block_tables[b], L, kvh, bits, d, m, key_bits)
+            k_hat = r["k_n"][:, None] * (ck[r["k_idx"]] @ pi)
             v_hat = r["v_n"][:, None] * (c[r["v_idx"]] @ pi)
             for g in range(G):
                 h = kvh * G + g

@@ -5,7 +5,8 @@ The "FlashQuant" page ("架构设计") decodes straight from a paged cache
 16-token block size. The field layout is this library's choice and is stated
 here as the format both sides write:
 
-  k_codes [num_blocks][Hkv][16][d*bits/8]  uint8
+  k_codes [num_blocks][Hkv][16][d*kbits/8] uint8   (kbits = key bits, = bits
+                                                    unless keys use their own width)
   k_norm  [num_blocks][Hkv][16]            fp32
   k_qjl   [num_blocks][Hkv][16][m/8]       uint8   (keys with QJL only)
   k_gamma [num_blocks][Hkv][16]            fp32    (keys with QJL only)
@@ -20,10 +21,11 @@ import numpy as np
 BLOCK = 16
 
 
-def empty_cache(num_blocks, num_kv_heads, head_dim, bits, qjl_dim=None):
+def empty_cache(num_blocks, num_kv_heads, head_dim, bits, qjl_dim=None, key_bits=None):
     cb = head_dim * bits // 8
+    kcb = head_dim * (bits if key_bits is None else key_bits) // 8
     c = {
-        "k_codes": np.zeros((num_blocks, num_kv_heads, BLOCK, cb), np.uint8),
+        "k_codes": np.zeros((num_blocks, num_kv_heads, BLOCK, kcb), np.uint8),
         "k_norm": np.zeros((num_blocks, num_kv_heads, BLOCK), np.float32),
         "v_codes": np.zeros((num_blocks, num_kv_heads, BLOCK, cb), np.uint8),
         "v_norm": np.zeros((num_blocks, num_kv_heads, BLOCK), np.float32),

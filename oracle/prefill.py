@@ -12,8 +12,10 @@ import numpy as np
 from . import attention
 
 
-def prefill_rotated(q, q_seq, q_lens, cache, block_tables, levels32, pi, s, bits, scale=None):
+def prefill_rotated(q, q_seq, q_lens, cache, block_tables, levels32, pi, s, bits, scale=None, key_levels32=None,
+                    key_bits=None):
     """q: [T, Hq, d]; q_seq, q_lens: [T]; returns out [T, Hq, d] float64."""
     q = np.asarray(q, dtype=np.float64)
     bt = np.asarray(block_tables)[np.asarray(q_seq)]
-    return attention.decode_rotated(q, cache, bt, np.asarray(q_lens), levels32, pi, s, bits, scale=scale)
+    return attention.decode_rotated(q, cache, bt, np.asarray(q_lens), levels32, pi, s, bits, scale=scale,
+                                    key_levels32=key_levels32, key_bits=key_bits)

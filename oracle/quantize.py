@@ -12,8 +12,12 @@ Readings (the pages fix none of these):
 * n = 0 gives u = 0 (so y = 0);
 * idx_j = #{i : boundary_i < y_j}, the decision taken on fp32(y_j) against the
   fp32 boundaries (a value equal to a boundary goes to the lower cell);
-* 4-bit: coordinate 2k in the low nibble of byte k, 2k+1 in the high nibble;
-  2-bit: coordinate 4k+i in bits 2i..2i+1 of byte k;
+* the indices of a vector form one little-endian bit stream: coordinate j takes
+  bits b*j .. b*j + b-1 of it, bit 8k+i of the stream being bit i of byte k. At 4
+  bits that is coordinate 2k in the low nibble of byte k and 2k+1 in the high
+  nibble; at 2 bits coordinate 4k+i in bits 2i..2i+1 of byte k; at 3 bits (the
+  codebook variant of the "TurboQuant" blog's 3-bit remark) eight coordinates fill
+  three bytes, some indices straddling two bytes;
 * QJL works in the rotated frame: r~ = y - c[idx] (unit scale), gamma = n ||r~||
   (equal to ||k - k_mse|| because the rotation is orthogonal), p = S r~ with m = d
   Gaussian rows, sigma_i = [p_i >= 0] (sign(0) = +1), bit i of byte j = sigma_{8j+i}.
@@ -48,24 +52,29 @@ def quantize_indices(y: np.ndarray, boundaries32: np.ndarray) -> np.ndarray:
 
 
 def pack_codes(idx: np.ndarray, bits: int) -> np.ndarray:
-    """Step 4: pack [N, d] indices into [N, d * bits / 8] bytes, little-endian within a byte."""
+    """Step 4: pack [N, d] indices into [N, d * bits / 8] bytes: the little-endian bit
+    stream in which coordinate j occupies bits bits*j .. bits*j + bits - 1."""
     idx = np.asarray(idx, dtype=np.int64)
-    per = 8 // bits
     n, d = idx.shape
-    grp = idx.reshape(n, d // per, per)
-    out = np.zeros((n, d // per), dtype=np.int64)
-    for i in range(per):
-        out |= grp[:, :, i] << (bits * i)
+    stream = np.zeros((n, d * bits), dtype=np.int64)  # one entry per bit of the stream
+    for i in range(bits):
+        stream[:, i::bits] = (idx >> i) & 1
+    grp = stream.reshape(n, d * bits // 8, 8)
+    out = np.zeros((n, d * bits // 8), dtype=np.int64)
+    for i in range(8):
+        out |= grp[:, :, i] << i
     return out.astype(np.uint8)
 
 
 def unpack_codes(codes: np.ndarray, bits: int, d: int) -> np.ndarray:
     """Inverse of pack_codes: bytes [N, d*bits/8] -> indices [N, d]."""
     codes = np.asarray(codes, dtype=np.int64)
-    per = 8 // bits
-    mask = (1 << bits) - 1
-    parts = [(codes >> (bits * i)) & mask for i in range(per)]
-    return np.stack(parts, axis=-1).reshape(codes.shape[0], d)
+    n = codes.shape[0]
+    stream = np.stack([(codes >> i) & 1 for i in range(8)], axis=-1).reshape(n, d * bits)
+    idx = np.zeros((n, d), dtype=np.int64)
+    for i in range(bits):
+        idx |= stream[:, i::bits] << i
+    return idx
 
 
 def pack_bits(sig: np.ndarray) -> np.ndarray:

@@ -17,7 +17,7 @@ from . import attention
 
 
 def decode_with_window(q, cache, block_tables, seq_lens, levels32, pi, s, bits, win_k, win_v, win_lens,
-                       scale=None):
+                       scale=None, key_levels32=None, key_bits=None):
     """q: [B, Hq, d]; compressed tokens [0, seq_lens[b]) in the paged cache; window
     K/V win_k, win_v: [B, W, Hkv, d] with the first win_lens[b] ring slots valid.
     Returns out [B, Hq, d] float64."""
@@ -26,6 +26,7 @@ def decode_with_window(q, cache, block_tables, seq_lens, levels32, pi, s, bits, 
     Hkv = cache["k_norm"].shape[1]
     G = Hq // Hkv
     c = np.asarray(levels32, dtype=np.float64)
+    ck = c if key_levels32 is None else np.asarray(key_levels32, dtype=np.float64)
     scale = 1.0 / np.sqrt(d) if scale is None else scale
     m = s.shape[0] if s is not None else 0
     wk = np.asarray(win_k, dtype=np.float64)
@@ -35,8 +36,8 @@ def decode_with_window(q, cache, block_tables, seq_lens, levels32, pi, s, bits, 
         L, w = int(seq_lens[b]), int(win_lens[b])
         for kvh in range(Hkv):
             if L > 0:
-                r = attention.head_records(cache, block_tables[b], L, kvh, bits, d, m)
-                kc = c[r["k_idx"]]
+                r = attention.head_records(cache, block_tables[b], L, kvh, bits, d, m, key_bits)
+                kc = ck[r["k_idx"]]
                 v_hat = r["v_n"][:, None] * (c[r["v_idx"]] @ pi)
             for g in range(G):
                 h = kvh * G + g

@@ -14,26 +14,31 @@ from kv_cache_vector_tq4_amd import synth
 from oracle import attention, paged, pipeline, quantize
 
 
-def _small_case(bits=4, T=40, Hkv=2, G=2, d=128, seed=0, qjl=True, rot=pipeline.HAAR):
-    q = pipeline.build(bits, d, rot=rot)
+def _small_case(bits=4, T=40, Hkv=2, G=2, d=128, seed=0, qjl=True, rot=pipeline.HAAR, key_bits=None):
+    q = pipeline.build(bits, d, rot=rot, key_bits=key_bits)
     rs = np.random.default_rng(seed)
     k = rs.standard_normal((T, Hkv, d)) * 2
     v = rs.standard_normal((T, Hkv, d))
     nb = (T + 15) // 16 + 3
     bt = rs.permutation(nb)[None, : (T + 15) // 16].astype(np.int32)
     slots = synth.slot_mapping_for(bt[0], T)
-    cache = paged.empty_cache(nb, Hkv, d, bits, qjl_dim=q["m"] if qjl else None)
+    cache = paged.empty_cache(nb, Hkv, d, bits, qjl_dim=q["m"] if qjl else None, key_bits=q["key_bits"])
     pipeline.compress(cache, k, v, slots, q, with_qjl=qjl)
     qq = rs.standard_normal((1, Hkv * G, d))
     return q, cache, bt, np.array([T], np.int32), qq, k, v
 
 
-@pytest.mark.parametrize("bits,qjl,rot", [(4, True, 0), (4, False, 0), (2, True, 0), (4, True, 1)])
-def test_two_forms_agree(bits, qjl, rot):
-    q, cache, bt, lens, qq, _, _ = _small_case(bits=bits, qjl=qjl, rot=rot)
+@pytest.mark.parametrize("bits,qjl,rot,kb", [(4, True, 0, None), (4, False, 0, None), (2, True, 0, None),
+                                             (4, True, 1, None), (3, True, 0, None), (4, True, 0, 3),
+                                             (3, False, 1, 2)])
+def test_two_forms_agree(bits, qjl, rot, kb):
+    """Also at 3 bits and with keys of their own width (the Prod budget: 3-bit keys +
+    QJL next to 4-bit values; 2-bit MSE-only keys next to 3-bit values)."""
+    q, cache, bt, lens, qq, _, _ = _small_case(bits=bits, qjl=qjl, rot=rot, key_bits=kb)
     s = q["s"] if qjl else None
-    a = attention.decode_rotated(qq, cache, bt, lens, q["levels"], q["pi"], s, bits)
-    b = attention.decode_reconstructed(qq, cache, bt, lens, q["levels"], q["pi"], s, bits)
+    kw = dict(key_levels32=q["key_levels"], key_bits=q["key_bits"])
+    a = attention.decode_rotated(qq, cache, bt, lens, q["levels"], q["pi"], s, bits, **kw)
+    b = attention.decode_reconstructed(qq, cache, bt, lens, q["levels"], q["pi"], s, bits, **kw)
     assert np.max(np.abs(a - b)) < 1e-10
 
 
@@ -111,12 +116,15 @@ def test_gqa_head_mapping():
     assert np.allclose(a[:, [2, 3, 0, 1]], b, atol=1e-12)
 
 
-def test_decode_scores_are_unbiased_over_qjl_matrices():
+@pytest.mark.parametrize("prod", [False, True])
+def test_decode_scores_are_unbiased_over_qjl_matrices(prod):
     """Through the whole encode -> cache -> score path, the QJL-corrected score of a key
     averages to the exact <q, k> over draws of S ("QJL" section: the estimator is
-    unbiased); MSE-only scores carry a fixed bias that the correction removes."""
+    unbiased); MSE-only scores carry a fixed bias that the correction removes. Also for
+    the Prod budget (3-bit MSE keys + the QJL bit, "架构设计": the quantizer's Prod mode)."""
     d = 128
-    base = pipeline.build(4, d)
+    base = pipeline.build_prod(4, d) if prod else pipeline.build(4, d)
+    kb = base["key_bits"]
     rs = np.random.default_rng(21)
     k = rs.standard_normal((1, 1, d)) * 2.0
     qv = rs.standard_normal(d)
@@ -126,10 +134,10 @@ def test_decode_scores_are_unbiased_over_qjl_matrices():
     with_qjl = np.empty(N)
     for i in range(N):
         qd = dict(base, s=rs.standard_normal((d, d)))
-        cache = paged.empty_cache(1, 1, d, 4, qjl_dim=d)
+        cache = paged.empty_cache(1, 1, d, 4, qjl_dim=d, key_bits=kb)
         pipeline.compress(cache, k, k, np.array([0]), qd)
-        r = attention.head_records(cache, bt[0], 1, 0, 4, d, d)
-        kc = qd["levels"].astype(np.float64)[r["k_idx"]]
+        r = attention.head_records(cache, bt[0], 1, 0, 4, d, d, key_bits=kb)
+        kc = qd["key_levels"].astype(np.float64)[r["k_idx"]]
         with_qjl[i] = attention.key_scores(qd["pi"] @ qv, kc, r, qd["s"])[0]
     mse_only = attention.key_scores(base["pi"] @ qv, kc, r, None)[0]
     n32 = float(r["k_n"][0])

@@ -33,6 +33,13 @@ def test_record_sizes(q4, q2):
     assert e4["qjl"].shape == (3, 16) and e4["gamma"].dtype == np.float32
     e2 = pipeline.encode_values(x, q2)
     assert e2["codes"].shape == (3, 32)
+    # 3 bits: 48 B of codes; the Prod key record at a 4-bit budget (3-bit MSE codes +
+    # 16 B of QJL signs + norm + gamma) is 72 B, the 4-bit value record 68 B
+    qp = pipeline.build_prod(4, 128)
+    ek, ev = pipeline.encode_keys(x, qp), pipeline.encode_values(x, qp)
+    assert ek["codes"].shape == (3, 48) and ev["codes"].shape == (3, 64)
+    assert ek["codes"].shape[1] + ek["qjl"].shape[1] + 4 + 4 == 72
+    assert ek["idx"].max() < 8 and ev["idx"].max() < 16
 
 
 def test_packing_layout_by_hand():
@@ -40,11 +47,15 @@ def test_packing_layout_by_hand():
     assert list(quantize.pack_codes(idx, 4)[0]) == [0x21, 0x0F, 0x87, 0xC3]
     idx2 = np.array([[1, 2, 3, 0, 0, 3, 2, 1]])
     assert list(quantize.pack_codes(idx2, 2)[0]) == [0b00111001, 0b01101100]
+    # 3 bits: sum_j idx_j << 3j = 0x1F58D1, little-endian bytes; coordinates 2 and 5
+    # straddle a byte boundary
+    idx3 = np.array([[1, 2, 3, 4, 5, 6, 7, 0]])
+    assert list(quantize.pack_codes(idx3, 3)[0]) == [0xD1, 0x58, 0x1F]
     sig = np.array([[1, 0, 0, 0, 0, 0, 0, 1, 0, 1, 0, 0, 0, 0, 0, 0]])
     assert list(quantize.pack_bits(sig)[0]) == [0x81, 0x02]
 
 
-@pytest.mark.parametrize("bits", [2, 4])
+@pytest.mark.parametrize("bits", [2, 3, 4])
 def test_pack_roundtrip(bits):
     rs = np.random.default_rng(bits)
     idx = rs.integers(0, 1 << bits, size=(20, 128))
@@ -74,7 +85,7 @@ def test_zero_vector(q4):
     assert e["gamma"][0] == 0
 
 
-@pytest.mark.parametrize("bits,rtol", [(4, 0.03), (2, 0.03)])
+@pytest.mark.parametrize("bits,rtol", [(4, 0.03), (3, 0.03), (2, 0.03)])
 def test_mse_bound_on_random_unit_vectors(bits, rtol):
     """Mean ||u - u_hat||^2 over 10^4 random unit vectors is below the page's
     bound (sqrt(3) pi / 2) / 4^b and close to the Gaussian Lloyd-Max MSE."""
