@@ -20,9 +20,9 @@
  *    stream) and is asynchronous; results are ready when the stream is.
  *  - Reductions run in a fixed order (no float atomics): the same inputs give
  *    bit-identical outputs run to run.
- *  - Supported shapes: head_dim = 128, bits in {2, 4}, 16-token blocks,
- *    qjl_dim in {0, 128}, 1 <= num_q_heads / num_kv_heads <= 16. Others return
- *    FQ_ERR_UNSUPPORTED.
+ *  - Supported shapes: head_dim = 128, bits in {2, 3, 4} (values; keys the same or
+ *    their own key_bits in {2, 3, 4}), 16-token blocks, qjl_dim in {0, 128},
+ *    1 <= num_q_heads / num_kv_heads <= 16. Others return FQ_ERR_UNSUPPORTED.
  *  - Out-of-range slot ids or block-table entries are not detected on the
  *    device: the caller guarantees 0 <= slot < num_blocks * 16 (or slot < 0 to
  *    skip) and 0 <= block_tables[b][i] < num_blocks for i < ceil(seq_lens[b]/16).
@@ -69,7 +69,7 @@ int fq_version(void);
  * fq_build_codebook -- host, synchronous. Builds the parameters of one layer's
  * quantizer ("FlashQuant" page, "TurboQuant" steps 2-3 and "QJL").
  *
- *  bits       2 or 4: 2^bits Lloyd-Max levels for N(0,1), iterated to the
+ *  bits       2, 3 or 4: 2^bits Lloyd-Max levels for N(0,1), iterated to the
  *             float64 fixed point (largest level change < 1e-15) from the cell
  *             quantiles, made exactly antisymmetric, then scaled by 1/sqrt(d).
  *  head_dim   d = 128.
@@ -99,9 +99,12 @@ fq_status fq_build_codebook(int bits, int head_dim, int rotation, uint64_t rot_s
                             float* rotation_matrix, float* rotation_t, float* wht_signs,
                             float* qjl_matrix, float* qjl_matrix_t);
 
-/* One layer's quantizer parameters, all device pointers (fp32, as built above). */
+/* One layer's quantizer parameters, all device pointers (fp32, as built above).
+ * Keys may use an MSE codebook of their own width (key_bits): the "Prod" budget of
+ * the quantizer ("FlashQuant" page, "架构设计": Quantizer with MSE / Prod modes)
+ * gives keys (b - 1)-bit MSE codes plus the 1-bit QJL signs next to b-bit values. */
 typedef struct fq_quantizer {
-  int32_t bits;                 /* 2 or 4 */
+  int32_t bits;                 /* 2, 3 or 4: the values' codes (and the keys' unless key_bits) */
   int32_t head_dim;             /* 128 */
   int32_t rotation;             /* fq_rotation */
   int32_t qjl_dim;              /* 0 or 128 */
@@ -114,6 +117,10 @@ typedef struct fq_quantizer {
   const float* qjl_matrix_t;    /* [d][qjl_dim] row-major S^T; required when qjl_dim > 0 */
   const void* mfma_operands;    /* optional: FQ_MFMA_OPERAND_BYTES from fq_pack_mfma_operands,
                                    16-byte aligned; NULL = the kernels derive them */
+  int32_t key_bits;             /* 0 = bits; else 2, 3 or 4: width of the keys' MSE codes */
+  const float* key_levels;      /* [2^key_bits] keys' levels; required when key_bits is set
+                                   and differs from bits (NULL otherwise: levels) */
+  const float* key_boundaries;  /* [2^key_bits - 1], as key_levels */
 } fq_quantizer;
 
 /* Size in bytes of the prepared matrix-core operands of one quantizer. */
@@ -139,13 +146,18 @@ fq_status fq_pack_mfma_operands(const float* rotation_matrix, const float* qjl_m
 /*
  * The paged compressed cache of one layer (device pointers, 16-byte aligned).
  * Token slot = block * 16 + offset. Per field:
- *   k_codes [num_blocks][Hkv][16][d*bits/8] u8   index of coordinate 2k in the low
- *                                                nibble of byte k (4-bit); coordinate
- *                                                4k+i in bits 2i..2i+1 (2-bit)
+ *   k_codes [num_blocks][Hkv][16][d*kb/8]   u8   kb = key_bits (or bits); the indices
+ *                                                of a vector as one little-endian bit
+ *                                                stream, coordinate j at bits kb*j ..
+ *                                                kb*j + kb-1 (4-bit: coordinate 2k in
+ *                                                the low nibble of byte k; 2-bit:
+ *                                                coordinate 4k+i in bits 2i..2i+1 of
+ *                                                byte k; 3-bit: 8 coordinates per 3 bytes)
  *   k_norm  [num_blocks][Hkv][16]           f32  ||k||
  *   k_qjl   [num_blocks][Hkv][16][m/8]      u8   bit i of byte j = [p_{8j+i} >= 0]
  *   k_gamma [num_blocks][Hkv][16]           f32  ||k - k_mse||
- *   v_codes, v_norm                              as k_codes, k_norm
+ *   v_codes [num_blocks][Hkv][16][d*bits/8] u8   as k_codes at the values' width
+ *   v_norm                                       as k_norm
  * k_qjl / k_gamma are used only when qjl_dim > 0 (keys in inner-product mode).
  */
 typedef struct fq_cache {
@@ -161,6 +173,7 @@ typedef struct fq_cache {
   float* k_gamma;
   uint8_t* v_codes;
   float* v_norm;
+  int32_t key_bits;     /* 0 = bits; else must equal the quantizer's key width */
 } fq_cache;
 
 /*
@@ -203,7 +216,7 @@ fq_status fq_compress(void* stream, const fq_quantizer* quant, const fq_cache* c
  *                  on (-1, 1); Lloyd iterated to the float64 fixed point (largest
  *                  level change < 1e-15), levels made exactly antisymmetric, no
  *                  further scaling.
- *  bits 2 or 4; head_dim d, 3 <= d <= 256 (the quantizer itself needs d = 128).
+ *  bits 2, 3 or 4; head_dim d, 3 <= d <= 256 (the quantizer itself needs d = 128).
  * Outputs (host, caller-allocated, fp32 rounded once from float64): levels
  * [2^bits] ascending, boundaries [2^bits - 1] = midpoints. They replace the levels
  * and boundaries of an fq_quantizer; the kernels take whatever codebook it holds.

@@ -11,7 +11,11 @@ inline bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintp
 fq_status check_quantizer(const fq_quantizer* q) {
   if (!q) return FQ_ERR_INVALID_ARG;
   if (q->rotation != FQ_ROT_HAAR && q->rotation != FQ_ROT_WHT) return FQ_ERR_INVALID_ARG;
-  if (q->bits != 2 && q->bits != 4) return FQ_ERR_UNSUPPORTED;
+  if (q->bits < 2 || q->bits > 4) return FQ_ERR_UNSUPPORTED;
+  if (q->key_bits != 0 && (q->key_bits < 2 || q->key_bits > 4)) return FQ_ERR_UNSUPPORTED;
+  if (fq::key_bits_of(*q) != q->bits &&
+      (!q->key_levels || !q->key_boundaries || !aligned(q->key_levels, 4) || !aligned(q->key_boundaries, 4)))
+    return FQ_ERR_INVALID_ARG;
   if (q->head_dim != FQ_HEAD_DIM) return FQ_ERR_UNSUPPORTED;
   if (q->qjl_dim != 0 && q->qjl_dim != FQ_HEAD_DIM) return FQ_ERR_UNSUPPORTED;
   if (!q->levels || !q->boundaries || !q->rotation_matrix || !q->rotation_t)
@@ -32,6 +36,7 @@ fq_status check_cache(const fq_cache* c, const fq_quantizer* q) {
   if (c->num_blocks < 0 || c->num_kv_heads <= 0) return FQ_ERR_INVALID_ARG;
   if (c->block_size != FQ_BLOCK || c->head_dim != FQ_HEAD_DIM) return FQ_ERR_UNSUPPORTED;
   if (c->bits != q->bits) return FQ_ERR_INVALID_ARG;
+  if ((c->key_bits != 0 ? c->key_bits : c->bits) != fq::key_bits_of(*q)) return FQ_ERR_INVALID_ARG;
   if (c->qjl_dim != 0 && c->qjl_dim != q->qjl_dim) return FQ_ERR_INVALID_ARG;
   if (!c->k_codes || !c->k_norm || !c->v_codes || !c->v_norm) return FQ_ERR_INVALID_ARG;
   if (!aligned(c->k_codes, 16) || !aligned(c->v_codes, 16) || !aligned(c->k_norm, 16) ||

@@ -220,7 +220,7 @@ extern "C" fq_status fq_build_codebook(int bits, int head_dim, int rotation, uin
                                        float* qjl_matrix_t) {
   if (!levels || !boundaries) return FQ_ERR_INVALID_ARG;
   if (rotation != FQ_ROT_HAAR && rotation != FQ_ROT_WHT) return FQ_ERR_INVALID_ARG;
-  if (bits != 2 && bits != 4) return FQ_ERR_UNSUPPORTED;
+  if (bits < 2 || bits > 4) return FQ_ERR_UNSUPPORTED;
   if (head_dim != FQ_HEAD_DIM) return FQ_ERR_UNSUPPORTED;
   if (qjl_dim != 0 && qjl_dim != FQ_HEAD_DIM) return FQ_ERR_UNSUPPORTED;
   const int d = head_dim;
@@ -340,7 +340,7 @@ extern "C" fq_status fq_pack_mfma_operands(const float* rotation_matrix, const f
 extern "C" fq_status fq_build_levels(int bits, int head_dim, int kind, float* levels, float* boundaries) {
   if (!levels || !boundaries) return FQ_ERR_INVALID_ARG;
   if (kind != FQ_CB_GAUSSIAN && kind != FQ_CB_SPHERE) return FQ_ERR_INVALID_ARG;
-  if (bits != 2 && bits != 4) return FQ_ERR_UNSUPPORTED;
+  if (bits < 2 || bits > 4) return FQ_ERR_UNSUPPORTED;
   if (head_dim < 3 || head_dim > 256) return FQ_ERR_UNSUPPORTED;
   std::vector<double> lev, bnd;
   double scale = 1.0;

@@ -20,6 +20,7 @@
 #include <cstdint>
 #include <cstdlib>
 #include <cstring>
+#include <type_traits>
 
 #include "fq_internal.h"
 
@@ -39,8 +40,10 @@ struct CompressArgs {
   float* norm[2];
   uint8_t* qjl;
   float* gamma;
-  const float* levels;
+  const float* levels;  // values' codebook (and the keys' unless they have their own)
   const float* bnd;
+  const float* klevels; // keys' codebook
+  const float* kbnd;
   const float* pit;     // Pi^T, row-major: row k = column k of Pi
   const float* pi_rows; // Pi, row-major
   const void* mfma_ops; // prepared fragments (optional)
@@ -359,11 +362,12 @@ __device__ __forceinline__ void compress_tile(const CompressArgs& a, int kind, i
         dy[4 * T + q] = make_float4(acc[T][4 * q], acc[T][4 * q + 1], acc[T][4 * q + 2], acc[T][4 * q + 3]);
   }
 
-  // ---- boundary search and packing; keys keep r = y - level[idx] in acc
-  constexpr int PER = 32 / BITS;
-  uint32_t words[64 / PER];
+  // ---- boundary search and packing; keys keep r = y - level[idx] in acc. The
+  // lane's 64 coordinates are bits 64 h BITS .. of the vector's bit stream: 2 BITS
+  // words, coordinate rel at bit BITS rel of them (3-bit codes straddle words).
+  uint32_t words[2 * BITS];
 #pragma unroll
-  for (int w = 0; w < 64 / PER; ++w) words[w] = 0;
+  for (int w = 0; w < 2 * BITS; ++w) words[w] = 0;
 #pragma unroll
   for (int T = 0; T < 4; ++T) {
     if constexpr (!FRAG_GLOBAL) __builtin_amdgcn_sched_barrier(0);  // LDS fragments: load next to use
@@ -376,14 +380,22 @@ __device__ __forceinline__ void compress_tile(const CompressArgs& a, int kind, i
       const QCell q = qt[c];
       const bool gt = q.b < y;
       const uint32_t idx = q.count + (gt ? 1u : 0u);
-      words[rel / PER] |= idx << (BITS * (rel % PER));
+      const int off = BITS * rel;
+      words[off >> 5] |= idx << (off & 31);
+      if ((off & 31) + BITS > 32) words[(off >> 5) + 1] |= idx >> (32 - (off & 31));
       if constexpr (KEY) acc[T][vv] = y - (gt ? q.c_hi : q.c_lo);
     }
   }
   if (store) {
-    uint4* cd = reinterpret_cast<uint4*>(a.codes[kind] + rec * (D * BITS / 8) + 64 * h * BITS / 8);
+    uint8_t* cd = a.codes[kind] + rec * (D * BITS / 8) + 64 * h * BITS / 8;
+    if constexpr (BITS == 3) {  // 24 bytes at an 8-byte boundary
 #pragma unroll
-    for (int w = 0; w < 64 / PER; w += 4) cd[w / 4] = make_uint4(words[w], words[w + 1], words[w + 2], words[w + 3]);
+      for (int w = 0; w < 6; w += 2) reinterpret_cast<uint2*>(cd)[w / 2] = make_uint2(words[w], words[w + 1]);
+    } else {
+#pragma unroll
+      for (int w = 0; w < 2 * BITS; w += 4)
+        reinterpret_cast<uint4*>(cd)[w / 4] = make_uint4(words[w], words[w + 1], words[w + 2], words[w + 3]);
+    }
     if (h == 0) a.norm[kind][rec] = n;
   }
 
@@ -470,12 +482,13 @@ __device__ __forceinline__ void fill_qtable(QCell* s_qt, float* s_qmap, const fl
   }
 }
 
-// Codebook value of thread tid for s_bl (boundary tid, or level tid - 32), or 0.
+// Codebook value of thread tid for s_bl (boundary tid, or level tid - 32), or 0;
+// kind 0 reads the keys' codebook, 1 the values'.
 template <int BITS>
-__device__ __forceinline__ float codebook_value(const CompressArgs& a, int tid) {
+__device__ __forceinline__ float codebook_value(const CompressArgs& a, int tid, int kind) {
   constexpr int L = 1 << BITS;
-  if (tid < L - 1) return a.bnd[tid];
-  if (tid >= 32 && tid < 32 + L) return a.levels[tid - 32];
+  if (tid < L - 1) return (kind == 0 ? a.kbnd : a.bnd)[tid];
+  if (tid >= 32 && tid < 32 + L) return (kind == 0 ? a.klevels : a.levels)[tid - 32];
   return 0.f;
 }
 template <int BITS>
@@ -488,8 +501,8 @@ __device__ __forceinline__ void stage_codebook(float* s_bl, int tid, float x) {
 // Quantization cells and codebook staging; callers synchronize afterwards.
 template <int BITS>
 __device__ __forceinline__ void build_qtable(const CompressArgs& a, QCell* s_qt, float* s_qmap, float* s_bl,
-                                             int tid, int nthreads) {
-  stage_codebook<BITS>(s_bl, tid, codebook_value<BITS>(a, tid));
+                                             int tid, int nthreads, int kind) {
+  stage_codebook<BITS>(s_bl, tid, codebook_value<BITS>(a, tid, kind));
   __syncthreads();
   fill_qtable<BITS>(s_qt, s_qmap, s_bl, tid, nthreads);
 }
@@ -549,7 +562,7 @@ __global__ void __launch_bounds__((KEY ? 4 : CT_WAVES) * 64) compress_mfma_kerne
       }
     }
   }
-  build_qtable<BITS>(a, s_qt, s_qmap, s_bl, tid, blockDim.x);
+  build_qtable<BITS>(a, s_qt, s_qmap, s_bl, tid, blockDim.x, kind);
   __syncthreads();
   const float inv_w = s_qmap[0], off = s_qmap[1];
   const int64_t nvec = a.ntok * a.hkv;
@@ -568,10 +581,10 @@ __global__ void __launch_bounds__(64) compress_direct_kernel(CompressArgs a) {
   __shared__ float s_qmap[2];
   __shared__ float s_bl[32];
   const int tid = threadIdx.x;
-  build_qtable<BITS>(a, s_qt, s_qmap, s_bl, tid, 64);
-  __syncthreads();
   const int kind = blockIdx.y;
-  if (!a.src[kind]) return;
+  if (!a.src[kind]) return;  // uniform over the work-group
+  build_qtable<BITS>(a, s_qt, s_qmap, s_bl, tid, 64, kind);
+  __syncthreads();
   const uint4* ops = static_cast<const uint4*>(a.mfma_ops);
   if (kind == 0)
     compress_tile<BITS, DT, true, true>(a, 0, blockIdx.x, tid, ops, ops + 2 * FRAG_U4, s_qt, s_qmap[0], s_qmap[1]);
@@ -696,12 +709,9 @@ __device__ __forceinline__ void compress_quarter(const CompressArgs& a, int kind
     for (int q = 0; q < 4; ++q) dy[q] = make_float4(acc[4 * q], acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]);
   }
 
-  // ---- boundary search and packing of the 16 coordinates; keys keep the residual
-  constexpr int PER = 32 / BITS;
-  constexpr int NW = 16 / PER;  // code words per lane and row tile
-  uint32_t words[NW];
-#pragma unroll
-  for (int w = 0; w < NW; ++w) words[w] = 0;
+  // ---- boundary search and packing of the 16 coordinates (16 BITS bits of the
+  // vector's bit stream from bit (64 h + 16 T) BITS); keys keep the residual
+  uint64_t packed = 0;
 #pragma unroll
   for (int vv = 0; vv < 16; ++vv) {
     const float y = acc[vv];
@@ -710,13 +720,19 @@ __device__ __forceinline__ void compress_quarter(const CompressArgs& a, int kind
     const QCell q = qt[c];
     const bool gt = q.b < y;
     const uint32_t idx = q.count + (gt ? 1u : 0u);
-    words[vv / PER] |= idx << (BITS * (vv % PER));
+    packed |= static_cast<uint64_t>(idx) << (BITS * vv);
     if constexpr (KEY) acc[vv] = y - (gt ? q.c_hi : q.c_lo);
   }
   if (store) {
     uint8_t* cd = codes_p + rec * (D * BITS / 8) + (64 * h + 16 * T) * BITS / 8;
-    if constexpr (NW == 2) *reinterpret_cast<uint2*>(cd) = make_uint2(words[0], words[1]);
-    else *reinterpret_cast<uint32_t*>(cd) = words[0];
+    if constexpr (BITS == 4) {
+      *reinterpret_cast<uint2*>(cd) = make_uint2(static_cast<uint32_t>(packed), static_cast<uint32_t>(packed >> 32));
+    } else if constexpr (BITS == 2) {
+      *reinterpret_cast<uint32_t*>(cd) = static_cast<uint32_t>(packed);
+    } else {  // 6 bytes at a 2-byte boundary
+#pragma unroll
+      for (int e = 0; e < 3; ++e) reinterpret_cast<uint16_t*>(cd)[e] = static_cast<uint16_t>(packed >> (16 * e));
+    }
     if (h == 0 && T == 0) norm_p[rec] = n;
   }
 
@@ -765,7 +781,7 @@ __device__ __forceinline__ void compress_quarter(const CompressArgs& a, int kind
   }
 }
 
-template <int BITS, int DT>
+template <int KB, int VB, int DT>
 __global__ void __launch_bounds__(256) compress_split_kernel(CompressArgs a) {
   __shared__ QCell s_qt[QT_CELLS];
   __shared__ float s_qmap[2];
@@ -777,46 +793,65 @@ __global__ void __launch_bounds__(256) compress_split_kernel(CompressArgs a) {
   if (!a.src[kind]) return;  // uniform over the work-group
   // Every global load is issued up front; the quantization cells are built from
   // the codebook while the inputs are in flight.
-  const float cbv = codebook_value<BITS>(a, tid);
-  auto table = [&]() {
-    stage_codebook<BITS>(s_bl, tid, cbv);
-    __syncthreads();
-    fill_qtable<BITS>(s_qt, s_qmap, s_bl, tid, 256);
-    __syncthreads();
+  const float cbv = kind == 0 ? codebook_value<KB>(a, tid, 0) : codebook_value<VB>(a, tid, 1);
+  auto table_of = [&](auto BB) {
+    constexpr int BITS = decltype(BB)::value;
+    return [&]() {
+      stage_codebook<BITS>(s_bl, tid, cbv);
+      __syncthreads();
+      fill_qtable<BITS>(s_qt, s_qmap, s_bl, tid, 256);
+      __syncthreads();
+    };
   };
   const uint4* ops = static_cast<const uint4*>(a.mfma_ops);
   const int T = __builtin_amdgcn_readfirstlane(tid >> 6);
   if (kind == 0)
-    compress_quarter<BITS, DT, true>(a, 0, blockIdx.x, tid & 63, T, ops, ops + 2 * FRAG_U4, s_qt, s_qmap, table,
-                                     s_rh, s_rl, s_rr);
+    compress_quarter<KB, DT, true>(a, 0, blockIdx.x, tid & 63, T, ops, ops + 2 * FRAG_U4, s_qt, s_qmap,
+                                   table_of(std::integral_constant<int, KB>{}), s_rh, s_rl, s_rr);
   else
-    compress_quarter<BITS, DT, false>(a, 1, blockIdx.x, tid & 63, T, ops, ops, s_qt, s_qmap, table, s_rh, s_rl,
-                                      s_rr);
+    compress_quarter<VB, DT, false>(a, 1, blockIdx.x, tid & 63, T, ops, ops, s_qt, s_qmap,
+                                    table_of(std::integral_constant<int, VB>{}), s_rh, s_rl, s_rr);
 }
 
-template <int BITS, int DT>
+template <int KB, int VB, int DT>
 int launch_mfma(hipStream_t st, const CompressArgs& a) {
   const int64_t nvec = a.ntok * a.hkv;
   const int64_t tiles = (nvec + CT_VEC - 1) / CT_VEC;
   if (a.mfma_ops && tiles <= 1024) {
     const char* impl = std::getenv("FQ_COMPRESS_KERNEL");
-    if (impl && std::strcmp(impl, "direct") == 0)
-      hipLaunchKernelGGL((compress_direct_kernel<BITS, DT>), dim3(static_cast<unsigned>(tiles), 2), dim3(64), 0, st, a);
+    if (KB == VB && KB != 3 && impl && std::strcmp(impl, "direct") == 0)
+      hipLaunchKernelGGL((compress_direct_kernel<KB, DT>), dim3(static_cast<unsigned>(tiles), 2), dim3(64), 0, st, a);
     else
-      hipLaunchKernelGGL((compress_split_kernel<BITS, DT>), dim3(static_cast<unsigned>(tiles), 2), dim3(256), 0, st, a);
+      hipLaunchKernelGGL((compress_split_kernel<KB, VB, DT>), dim3(static_cast<unsigned>(tiles), 2), dim3(256), 0, st,
+                         a);
     return static_cast<int>(hipGetLastError());
   }
   if (a.src[0]) {
     const int64_t want = (tiles + 3) / 4;
     const unsigned g = static_cast<unsigned>(want < 256 ? want : 256);
-    hipLaunchKernelGGL((compress_mfma_kernel<BITS, DT, true>), dim3(g), dim3(4 * 64), 0, st, a, 0);
+    hipLaunchKernelGGL((compress_mfma_kernel<KB, DT, true>), dim3(g), dim3(4 * 64), 0, st, a, 0);
   }
   if (a.src[1]) {
     const int64_t want = (tiles + CT_WAVES - 1) / CT_WAVES;
     const unsigned g = static_cast<unsigned>(want < 512 ? want : 512);
-    hipLaunchKernelGGL((compress_mfma_kernel<BITS, DT, false>), dim3(g), dim3(CT_WAVES * 64), 0, st, a, 1);
+    hipLaunchKernelGGL((compress_mfma_kernel<VB, DT, false>), dim3(g), dim3(CT_WAVES * 64), 0, st, a, 1);
   }
   return static_cast<int>(hipGetLastError());
+}
+
+// (key bits, value bits) pairs the library builds: equal widths, and keys one bit
+// narrower than values (the Prod budget)
+template <int DT>
+int launch_mfma_bits(hipStream_t st, const CompressArgs& a, int kb, int vb) {
+  if (kb == 4 && vb == 4) return launch_mfma<4, 4, DT>(st, a);
+  if (kb == 3 && vb == 3) return launch_mfma<3, 3, DT>(st, a);
+  if (kb == 2 && vb == 2) return launch_mfma<2, 2, DT>(st, a);
+  if (kb == 3 && vb == 4) return launch_mfma<3, 4, DT>(st, a);
+  if (kb == 2 && vb == 3) return launch_mfma<2, 3, DT>(st, a);
+  if (kb == 2 && vb == 4) return launch_mfma<2, 4, DT>(st, a);
+  if (kb == 4 && vb == 3) return launch_mfma<4, 3, DT>(st, a);
+  if (kb == 4 && vb == 2) return launch_mfma<4, 2, DT>(st, a);
+  return launch_mfma<3, 2, DT>(st, a);
 }
 
 template <int BITS, int DT, bool WHT>
@@ -844,6 +879,8 @@ int launch_compress(void* stream, const fq_quantizer& q, const fq_cache& c, cons
   a.gamma = c.k_gamma;
   a.levels = q.levels;
   a.bnd = q.boundaries;
+  a.klevels = key_levels_of(q);
+  a.kbnd = key_boundaries_of(q);
   a.pit = q.rotation_t;
   a.pi_rows = q.rotation_matrix;
   a.mfma_ops = q.mfma_operands;
@@ -861,11 +898,11 @@ int launch_compress(void* stream, const fq_quantizer& q, const fq_cache& c, cons
   const bool wht = q.rotation == FQ_ROT_WHT;
   const bool bf = dtype == FQ_BF16;
   const char* impl = std::getenv("FQ_COMPRESS_KERNEL");
-  const bool lane_impl = impl && std::strcmp(impl, "lane") == 0;
-  if (!lane_impl) {
-    if (q.bits == 4) return bf ? launch_mfma<4, FQ_BF16>(st, a) : launch_mfma<4, FQ_F32>(st, a);
-    return bf ? launch_mfma<2, FQ_BF16>(st, a) : launch_mfma<2, FQ_F32>(st, a);
-  }
+  const int kb = key_bits_of(q);
+  // the vector-ALU alternative exists for one shared 2- or 4-bit codebook
+  const bool lane_impl = impl && std::strcmp(impl, "lane") == 0 && kb == q.bits && q.bits != 3;
+  if (!lane_impl)
+    return bf ? launch_mfma_bits<FQ_BF16>(st, a, kb, q.bits) : launch_mfma_bits<FQ_F32>(st, a, kb, q.bits);
   if (q.bits == 4) {
     if (bf) return wht ? launch_lane<4, FQ_BF16, true>(st, a) : launch_lane<4, FQ_BF16, false>(st, a);
     return wht ? launch_lane<4, FQ_F32, true>(st, a) : launch_lane<4, FQ_F32, false>(st, a);

@@ -50,7 +50,10 @@ struct DecodeArgs {
   const float* pit;   // Pi^T row-major
   const float* smat;  // S row-major [m][d]
   const float* sit;   // S^T row-major [d][m]
-  const float* levels;
+  const float* levels;   // values' codebook (and the keys' unless they have their own)
+  const float* klevels;  // keys' codebook
+  const float* kbnd;     // keys' boundaries
+  int kbits;             // keys' code width
   const uint8_t* k_codes;
   const float* k_norm;
   const uint8_t* k_qjl;
@@ -562,29 +565,45 @@ __device__ __forceinline__ void prepare_group(const DecodeArgs& a, int kvh, int 
     const float inv = n > 0.f ? 1.0f / n : 0.f;
     const float y = ((s_part[(0 * GM + r) * D + j] + s_part[(1 * GM + r) * D + j]) +
                      (s_part[(2 * GM + r) * D + j] + s_part[(3 * GM + r) * D + j])) * inv;
-    const cptr bq = uniform_ptr(a.bnd);
-    const int nb = (1 << a.bits) - 1;
+    // the row's codebook and width (keys may have their own); kq is wave-uniform
+    const int bits = kq == 0 ? a.kbits : a.bits;
+    const cptr bq = uniform_ptr(kq == 0 ? a.kbnd : a.bnd);
+    const int nb = (1 << bits) - 1;
     uint32_t idx = 0;
 #pragma unroll
     for (int i = 0; i < 15; ++i) {
       const float bi = bq[i < nb ? i : nb - 1];  // reads stay inside the nb boundaries
       if (i < nb) idx += bi < y ? 1u : 0u;
     }
-    // 32-bit word j / per of the packed codes gathered in its first lane
-    const int per = 32 / a.bits;
-    uint32_t w = idx << (a.bits * (j % per));
+    const int cb = D * bits / 8;  // code bytes per vector
+    uint8_t* const codes = const_cast<uint8_t*>(kq == 0 ? a.k_codes : a.v_codes);
+    if (bits != 3) {
+      // 32-bit word j / per of the packed codes gathered in its first lane
+      const int per = 32 / bits;
+      uint32_t w = idx << (bits * (j % per));
 #pragma unroll
-    for (int m = 1; m < 16; m <<= 1)
-      if (m < per) w |= static_cast<uint32_t>(__shfl_xor(static_cast<int>(w), m));
+      for (int m = 1; m < 16; m <<= 1)
+        if (m < per) w |= static_cast<uint32_t>(__shfl_xor(static_cast<int>(w), m));
+      if (slot >= 0 && j % per == 0) *reinterpret_cast<uint32_t*>(codes + rec * cb + 4 * (j / per)) = w;
+    } else {
+      // 3-bit: the wave's 64 coordinates are 192 bits of the stream from bit 192 (j / 64);
+      // lane L < 6 assembles its word 32 L .. 32 L + 31 from the ballots of the index bits
+      const uint64_t bm[3] = {__ballot((idx & 1u) != 0), __ballot((idx & 2u) != 0), __ballot((idx & 4u) != 0)};
+      uint32_t w = 0;
+      if (lane < 6) {
+        for (int p = 0; p < 32; ++p) {
+          const int q = 32 * lane + p;  // bit q of the run = bit q % 3 of coordinate q / 3
+          w |= static_cast<uint32_t>((bm[q % 3] >> (q / 3)) & 1u) << p;
+        }
+        if (slot >= 0) *reinterpret_cast<uint32_t*>(codes + rec * cb + 24 * (j >> 6) + 4 * lane) = w;
+      }
+    }
     if (slot >= 0) {
       if (a.dbg_y) a.dbg_y[((static_cast<int64_t>(kq) * a.batch + b) * a.hkv + kvh) * D + j] = y;
-      const int cb = D * a.bits / 8;  // code bytes per vector
-      uint8_t* const codes = const_cast<uint8_t*>(kq == 0 ? a.k_codes : a.v_codes);
-      if (j % per == 0) *reinterpret_cast<uint32_t*>(codes + rec * cb + 4 * (j / per)) = w;
       if (j == 0) const_cast<float*>(kq == 0 ? a.k_norm : a.v_norm)[rec] = n;
     }
     if (kq == 0 && qjl) {
-      const float res = y - a.levels[idx];
+      const float res = y - a.klevels[idx];
       s_r[hn * D + j] = res;
       const float rr = wave_sum_dpp(res * res);
       if (lane == 0) s_nrm[4 + (j >> 6)] = rr;
@@ -671,17 +690,24 @@ __global__ void __launch_bounds__(PQ_THREADS) prepare_queries_kernel(DecodeArgs 
 }
 
 // ---------------------------------------------------------------- kernel 2
+// Index of coordinate j in a vector's code bit stream (BITS bits per coordinate,
+// little-endian; a 3-bit index may straddle two words). j is a constant after
+// unrolling, so the word choice and the straddle are resolved at compile time.
 template <int BITS>
 __device__ __forceinline__ uint32_t code_at(const uint32_t (&w)[D * BITS / 32], int j) {
-  constexpr int PER = 32 / BITS;
-  return (w[j / PER] >> (BITS * (j % PER))) & ((1u << BITS) - 1);
+  const int off = BITS * j, wd = off >> 5, sh = off & 31;
+  uint32_t x = w[wd] >> sh;
+  if (sh + BITS > 32) x |= w[wd + 1] << (32 - sh);
+  return x & ((1u << BITS) - 1);
 }
 
-template <int BITS>
+// Vector-ALU split attention; keys with KB-bit codes, values with VB-bit codes.
+template <int KB, int VB>
 __global__ void __launch_bounds__(256) split_attention_kernel(DecodeArgs a) {
-  constexpr int L = 1 << BITS;
-  constexpr int CW = D * BITS / 32;  // code dwords per vector
+  constexpr int L = 1 << VB, LK = 1 << KB;
+  constexpr int CW = D * KB / 32;  // key code dwords per vector
   __shared__ float s_lev[L];
+  __shared__ float s_klev[LK];
   __shared__ float s_p[FQ_MAX_GROUP][SUB];  // scores, then p * v_norm
   __shared__ float s_alpha[FQ_MAX_GROUP];
   __shared__ float s_m[FQ_MAX_GROUP];
@@ -692,6 +718,7 @@ __global__ void __launch_bounds__(256) split_attention_kernel(DecodeArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int G = a.group;
   if (tid < L) s_lev[tid] = a.levels[tid];
+  if (tid < LK) s_klev[tid] = a.klevels[tid];
   if (tid < FQ_MAX_GROUP) {
     s_m[tid] = -INFINITY;
     s_l[tid] = 0.f;
@@ -716,7 +743,7 @@ __global__ void __launch_bounds__(256) split_attention_kernel(DecodeArgs a) {
     if (t < t1) {
       const int64_t rec = (static_cast<int64_t>(bt[t >> 4]) * a.hkv + kvh) * FQ_BLOCK + (t & 15);
       uint32_t cw[CW];
-      const uint4* cp = reinterpret_cast<const uint4*>(a.k_codes + rec * (D * BITS / 8));
+      const uint4* cp = reinterpret_cast<const uint4*>(a.k_codes + rec * (D * KB / 8));
 #pragma unroll
       for (int i = 0; i < CW / 4; ++i) {
         uint4 u = cp[i];
@@ -725,7 +752,7 @@ __global__ void __launch_bounds__(256) split_attention_kernel(DecodeArgs a) {
       const float kn = a.k_norm[rec] * a.scale;
       float val[D];
 #pragma unroll
-      for (int jj = 0; jj < D; ++jj) val[jj] = s_lev[code_at<BITS>(cw, jj)];
+      for (int jj = 0; jj < D; ++jj) val[jj] = s_klev[code_at<KB>(cw, jj)];
       for (int g = 0; g < G; ++g) {
         cptr qg = qr + g * D;
         float d0 = 0.f, d1 = 0.f;
@@ -802,8 +829,13 @@ __global__ void __launch_bounds__(256) split_attention_kernel(DecodeArgs a) {
     for (int tt = par; tt < nsub; tt += 2) {
       const int t = s0 + tt;
       const int64_t rec = (static_cast<int64_t>(bt[t >> 4]) * a.hkv + kvh) * FQ_BLOCK + (t & 15);
-      const uint8_t byte = a.v_codes[rec * (D * BITS / 8) + (j * BITS) / 8];
-      const uint32_t code = (byte >> ((j * BITS) & 7)) & ((1u << BITS) - 1);
+      // coordinate j's bits VB j .. of the record's stream; a 3-bit index may reach
+      // into the next byte, which is still inside the record
+      const uint8_t* vb = a.v_codes + rec * (D * VB / 8) + (j * VB) / 8;
+      const int sh = (j * VB) & 7;
+      uint32_t x = vb[0];
+      if (sh + VB > 8) x |= static_cast<uint32_t>(vb[1]) << 8;
+      const uint32_t code = (x >> sh) & ((1u << VB) - 1);
       const float c = s_lev[code];
 #pragma unroll
       for (int g = 0; g < FQ_MAX_GROUP; ++g)
@@ -1900,6 +1932,9 @@ int launch_decode(void* stream, const fq_quantizer& q, const fq_cache& c, const 
   a.smat = q.qjl_matrix;
   a.sit = q.qjl_matrix_t;
   a.levels = q.levels;
+  a.klevels = key_levels_of(q);
+  a.kbnd = key_boundaries_of(q);
+  a.kbits = key_bits_of(q);
   a.k_codes = c.k_codes;
   a.k_norm = c.k_norm;
   a.k_qjl = c.k_qjl;
@@ -1951,7 +1986,11 @@ int launch_decode(void* stream, const fq_quantizer& q, const fq_cache& c, const 
   // larger groups the earlier matrix-core kernel (4-bit) or the vector-ALU kernel
   // (2-bit, or any width on request).
   const char* impl = std::getenv("FQ_DECODE_KERNEL");
-  const bool valu = impl && std::strcmp(impl, "valu") == 0;
+  // The matrix-core kernels dequantize keys and values through one table: one 2- or
+  // 4-bit codebook for both. 3-bit codes and keys of their own width take the
+  // vector-ALU kernel.
+  const bool shared4 = a.kbits == q.bits && key_levels_of(q) == q.levels && q.bits != 3;
+  const bool valu = !shared4 || (impl && std::strcmp(impl, "valu") == 0);
   const bool v1 = impl && std::strcmp(impl, "mfma_v1") == 0;
   const int slots = (!valu && !v1) ? (a.group <= 4 ? 4 : a.group <= 8 ? 2 : 0) : 0;
   dim3 grid(num_splits, c.num_kv_heads, batch);
@@ -2022,10 +2061,15 @@ int launch_decode(void* stream, const fq_quantizer& q, const fq_cache& c, const 
     hipLaunchKernelGGL((packed_decode_kernel<2, 2, PK2_WAVES, PK2_RING, PK2_OCC, -1>), grid, dim3(PK2_WAVES * 64), 0, st, a);
   else if (q.bits == 4 && !valu)
     hipLaunchKernelGGL(split_mfma4_kernel, grid, dim3(256), 0, st, a);
-  else if (q.bits == 4)
-    hipLaunchKernelGGL(split_attention_kernel<4>, grid, dim3(256), 0, st, a);
-  else
-    hipLaunchKernelGGL(split_attention_kernel<2>, grid, dim3(256), 0, st, a);
+  else {
+#define FQ_VALU(KB, VB)                                                         \
+  if (a.kbits == KB && q.bits == VB) {                                           \
+    hipLaunchKernelGGL((split_attention_kernel<KB, VB>), grid, dim3(256), 0, st, a); \
+  } else
+    FQ_VALU(4, 4) FQ_VALU(2, 2) FQ_VALU(3, 3) FQ_VALU(3, 4) FQ_VALU(2, 3) FQ_VALU(2, 4) FQ_VALU(4, 3)
+    FQ_VALU(4, 2) FQ_VALU(3, 2) {}
+#undef FQ_VALU
+  }
   hipLaunchKernelGGL(merge_unrotate_kernel, pgrid, dim3(PQ_THREADS), 0, st, a);
   return static_cast<int>(hipGetLastError());
 }

@@ -51,11 +51,13 @@ struct DecompressArgs {
   const uint8_t* codes[2];  // K, V code arrays of the cache
   const float* norm[2];
   void* out[2];             // K, V outputs (either may be null)
-  const float* levels;
+  const float* levels;      // values' codebook
+  const float* klevels;     // keys' codebook
   const float* pit;         // Pi^T row-major: row o = column o of Pi
   const int64_t* slots;
   int64_t ntok, tstride, hstride;
   int hkv, out_bf16;
+  int kind0;                // kind of blockIdx.y = 0 (0 K, 1 V)
 };
 
 // Target of the stores for vectors that have nothing to write (past the end, or a
@@ -91,14 +93,16 @@ __global__ void __launch_bounds__(DQ_WAVES * 64, 1) decompress_kernel(Decompress
   // level table entry of code byte x, the byte's codes c0.. in coordinate order:
   // ONE: fp16 levels, 4-bit (c0 | c1) 4 B, 2-bit (c0 | c1, c2 | c3) 8 B; else bf16,
   // 4-bit (hi c0 | hi c1, lo c0 | lo c1) 8 B, 2-bit (hi c0 | hi c1, hi c2 | hi c3,
-  // lo c0 | lo c1, lo c2 | lo c3) 16 B; at (x * COPIES + copy) * EB, copy = lane % COPIES
-  constexpr int EB = (BITS == 4 ? 8 : 16) / (ONE ? 2 : 1);
+  // lo c0 | lo c1, lo c2 | lo c3) 16 B; at (x * COPIES + copy) * EB, copy = lane % COPIES.
+  // 3-bit codes use the 4-bit entries with x = 6 bits of the stream (c0 | c1 << 3).
+  constexpr int EB = (BITS == 2 ? 16 : 8) / (ONE ? 2 : 1);
   constexpr int COPIES = 8192 / (256 * EB);  // an 8 KB table
   __shared__ uint4 s_fh[DQ_FRAG], s_fl[ONE ? 1 : DQ_FRAG];  // Pi^T fragments: fp16, or bf16 hi / lo
   __shared__ __align__(16) uint8_t s_tab[256 * COPIES * EB];
   __shared__ __align__(16) uint8_t s_stage[DQ_WAVES * DQ_STAGE];
-  const int kind = blockIdx.y;
+  const int kind = static_cast<int>(blockIdx.y) + a.kind0;
   if (!a.out[kind]) return;  // uniform over the work-group
+  const float* const lev = kind == 0 ? a.klevels : a.levels;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   // fragment f = (k-step s, row tile T), lane i: Pi^T[out_coord(T, i % 32)][64 (i / 32) + 8 s + e], e < 8
   for (int idx = tid; idx < DQ_FRAG; idx += DQ_WAVES * 64) {
@@ -120,21 +124,21 @@ __global__ void __launch_bounds__(DQ_WAVES * 64, 1) decompress_kernel(Decompress
   }
   for (int idx = tid; idx < 256 * COPIES; idx += DQ_WAVES * 64) {
     const uint32_t x = static_cast<uint32_t>(idx) / COPIES;
-    constexpr int PER = 8 / BITS;  // codes per byte
+    constexpr int PER = BITS == 2 ? 4 : 2;  // codes per entry
     uint16_t hi[4], lo[4];
 #pragma unroll
     for (int c = 0; c < PER; ++c) {
-      const float lv = a.levels[(x >> (BITS * c)) & ((1u << BITS) - 1u)];
+      const float lv = lev[(x >> (BITS * c)) & ((1u << BITS) - 1u)];
       if constexpr (ONE)
         hi[c] = __builtin_bit_cast(uint16_t, static_cast<_Float16>(lv));
       else
         split_bf16x(lv, hi[c], lo[c]);
     }
-    if constexpr (ONE && BITS == 4)
+    if constexpr (ONE && BITS != 2)
       *reinterpret_cast<uint32_t*>(s_tab + idx * EB) = pack2(hi[0], hi[1]);
     else if constexpr (ONE)
       *reinterpret_cast<uint2*>(s_tab + idx * EB) = make_uint2(pack2(hi[0], hi[1]), pack2(hi[2], hi[3]));
-    else if constexpr (BITS == 4)
+    else if constexpr (BITS != 2)
       *reinterpret_cast<uint2*>(s_tab + idx * EB) = make_uint2(pack2(hi[0], hi[1]), pack2(lo[0], lo[1]));
     else
       *reinterpret_cast<uint4*>(s_tab + idx * EB) =
@@ -181,11 +185,20 @@ __global__ void __launch_bounds__(DQ_WAVES * 64, 1) decompress_kernel(Decompress
     const int64_t sl = x.slot >= 0 ? x.slot : 0;
     const int64_t rec = ((sl >> 4) * a.hkv + x.hd) * FQ_BLOCK + (sl & 15);
     x.nrm = a.norm[kind][rec];
-    const uint4* cp = reinterpret_cast<const uint4*>(a.codes[kind] + rec * CB + h * (CB / 2));
+    if constexpr (HW % 4 == 0) {
+      const uint4* cp = reinterpret_cast<const uint4*>(a.codes[kind] + rec * CB + h * (CB / 2));
 #pragma unroll
-    for (int q = 0; q < HW / 4; ++q) {
-      const uint4 u = cp[q];
-      x.cw[4 * q] = u.x; x.cw[4 * q + 1] = u.y; x.cw[4 * q + 2] = u.z; x.cw[4 * q + 3] = u.w;
+      for (int q = 0; q < HW / 4; ++q) {
+        const uint4 u = cp[q];
+        x.cw[4 * q] = u.x; x.cw[4 * q + 1] = u.y; x.cw[4 * q + 2] = u.z; x.cw[4 * q + 3] = u.w;
+      }
+    } else {  // 3-bit: 24 bytes per lane half, at an 8-byte boundary
+      const uint2* cp = reinterpret_cast<const uint2*>(a.codes[kind] + rec * CB + h * (CB / 2));
+#pragma unroll
+      for (int q = 0; q < HW / 2; ++q) {
+        const uint2 u = cp[q];
+        x.cw[2 * q] = u.x; x.cw[2 * q + 1] = u.y;
+      }
     }
   };
   // The previous tile's output, re-ordered through this wave's LDS stage so that each
@@ -231,14 +244,25 @@ __global__ void __launch_bounds__(DQ_WAVES * 64, 1) decompress_kernel(Decompress
     auto load_ops = [&](auto ST, Ops& o) {
       constexpr int st = decltype(ST)::value;
       auto entry = [&](uint32_t byte) { return s_tab + byte * (COPIES * EB) + copy; };
-      if constexpr (BITS == 4) {
-        const uint32_t w = cw[st];  // code bytes of coordinates 64 h + 8 st ..
+      if constexpr (BITS != 2) {
+        // 4-bit: the code bytes of coordinates 64 h + 8 st ..; 3-bit: their 24 bits of
+        // the stream (from bit 24 st of the lane's words), taken 6 bits (2 codes) at a time
+        constexpr int GB = BITS == 4 ? 8 : 6;
+        uint32_t w;
+        if constexpr (BITS == 4) {
+          w = cw[st];
+        } else {
+          constexpr int off = 24 * st, wd = off >> 5, sh = off & 31;
+          w = cw[wd] >> sh;
+          if constexpr (sh > 8) w |= cw[wd + 1] << (32 - sh);
+        }
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
+          const uint32_t x = (w >> (GB * q)) & ((1u << GB) - 1u);
           if constexpr (ONE) {
-            o.e[q] = *reinterpret_cast<const uint32_t*>(entry((w >> (8 * q)) & 255u));
+            o.e[q] = *reinterpret_cast<const uint32_t*>(entry(x));
           } else {
-            const uint2 u = *reinterpret_cast<const uint2*>(entry((w >> (8 * q)) & 255u));
+            const uint2 u = *reinterpret_cast<const uint2*>(entry(x));
             o.e[2 * q] = u.x;
             o.e[2 * q + 1] = u.y;
           }
@@ -275,7 +299,7 @@ __global__ void __launch_bounds__(DQ_WAVES * 64, 1) decompress_kernel(Decompress
         return;
       }
       b8 bh, bl;
-      if constexpr (BITS == 4) {
+      if constexpr (BITS != 2) {
         bh = __builtin_bit_cast(b8, make_uint4(o.e[0], o.e[2], o.e[4], o.e[6]));
         bl = __builtin_bit_cast(b8, make_uint4(o.e[1], o.e[3], o.e[5], o.e[7]));
       } else {
@@ -381,6 +405,7 @@ int launch_decompress(void* stream, const fq_quantizer& q, const fq_cache& c, co
   a.out[0] = k_out;
   a.out[1] = v_out;
   a.levels = q.levels;
+  a.klevels = key_levels_of(q);
   a.pit = q.rotation_t;
   a.slots = slot_mapping;
   a.ntok = num_tokens;
@@ -392,18 +417,28 @@ int launch_decompress(void* stream, const fq_quantizer& q, const fq_cache& c, co
   const int64_t want = (tiles + DQ_WAVES - 1) / DQ_WAVES;
   // one work-group per CU (128 per kind): one round, each stages the fragments once
   const unsigned g = static_cast<unsigned>(want < 128 ? want : 128);
-  const dim3 grid(g, 2), block(DQ_WAVES * 64);
+  const dim3 block(DQ_WAVES * 64);
   hipStream_t st = static_cast<hipStream_t>(stream);
-  if (q.bits == 4) {
-    if (a.out_bf16)
-      hipLaunchKernelGGL((decompress_kernel<4, true>), grid, block, 0, st, a);
-    else
-      hipLaunchKernelGGL((decompress_kernel<4, false>), grid, block, 0, st, a);
+  auto launch = [&](int bits, int kind0, int kinds) {
+    const dim3 grid(g, kinds);
+    a.kind0 = kind0;
+    if (bits == 4) {
+      if (a.out_bf16) hipLaunchKernelGGL((decompress_kernel<4, true>), grid, block, 0, st, a);
+      else hipLaunchKernelGGL((decompress_kernel<4, false>), grid, block, 0, st, a);
+    } else if (bits == 3) {
+      if (a.out_bf16) hipLaunchKernelGGL((decompress_kernel<3, true>), grid, block, 0, st, a);
+      else hipLaunchKernelGGL((decompress_kernel<3, false>), grid, block, 0, st, a);
+    } else {
+      if (a.out_bf16) hipLaunchKernelGGL((decompress_kernel<2, true>), grid, block, 0, st, a);
+      else hipLaunchKernelGGL((decompress_kernel<2, false>), grid, block, 0, st, a);
+    }
+  };
+  const int kb = key_bits_of(q);
+  if (kb == q.bits) {
+    launch(q.bits, 0, 2);  // K and V in one launch
   } else {
-    if (a.out_bf16)
-      hipLaunchKernelGGL((decompress_kernel<2, true>), grid, block, 0, st, a);
-    else
-      hipLaunchKernelGGL((decompress_kernel<2, false>), grid, block, 0, st, a);
+    if (k_out) launch(kb, 0, 1);
+    if (v_out) launch(q.bits, 1, 1);
   }
   return static_cast<int>(hipGetLastError());
 }

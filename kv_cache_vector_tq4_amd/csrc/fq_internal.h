@@ -14,6 +14,16 @@
 
 namespace fq {
 
+// Width of the keys' MSE codes, and their codebook (the values' unless the keys
+// have a width of their own).
+inline int key_bits_of(const fq_quantizer& q) { return q.key_bits != 0 ? q.key_bits : q.bits; }
+inline const float* key_levels_of(const fq_quantizer& q) {
+  return key_bits_of(q) != q.bits && q.key_levels ? q.key_levels : q.levels;
+}
+inline const float* key_boundaries_of(const fq_quantizer& q) {
+  return key_bits_of(q) != q.bits && q.key_boundaries ? q.key_boundaries : q.boundaries;
+}
+
 // Workspace carve-up of fq_decode_attention (offsets in bytes, 256-aligned).
 struct DecodeWorkspace {
   size_t qrot;    // f32 [B][Hq][d]        rotated queries

@@ -42,6 +42,9 @@ class QuantizerT(ctypes.Structure):
         ("qjl_matrix", ctypes.c_void_p),
         ("qjl_matrix_t", ctypes.c_void_p),
         ("mfma_operands", ctypes.c_void_p),
+        ("key_bits", ctypes.c_int32),
+        ("key_levels", ctypes.c_void_p),
+        ("key_boundaries", ctypes.c_void_p),
     ]
 
 
@@ -62,6 +65,7 @@ class CacheT(ctypes.Structure):
         ("k_gamma", ctypes.c_void_p),
         ("v_codes", ctypes.c_void_p),
         ("v_norm", ctypes.c_void_p),
+        ("key_bits", ctypes.c_int32),
     ]
 
 
@@ -219,19 +223,24 @@ class Quantizer:
     with prepared=False the kernels derive them from the fp32 matrices themselves.
     codebook: CB_GAUSSIAN (fq_build_codebook's) or CB_SPHERE (fq_build_levels' exact
     spherical marginal, replacing the levels and boundaries).
+    key_bits: width of the keys' MSE codes when it differs from bits (their codebook is
+    then that width's); key_bits = bits - 1 with QJL keys is the Prod budget.
     """
 
     def __init__(self, bits=4, head_dim=128, rotation=ROT_HAAR, rot_seed=1, qjl_seed=2, qjl_dim=128,
-                 device="cuda", prepared=True, codebook=CB_GAUSSIAN):
+                 device="cuda", prepared=True, codebook=CB_GAUSSIAN, key_bits=None):
         import torch
 
         self.host = build_codebook(bits, head_dim, rotation, rot_seed, qjl_seed, qjl_dim)
         if codebook != CB_GAUSSIAN:
             self.host["levels"], self.host["boundaries"] = build_levels(bits, head_dim, codebook)
+        self.key_bits = bits if key_bits is None else key_bits
+        if self.key_bits != bits:
+            self.host["key_levels"], self.host["key_boundaries"] = build_levels(self.key_bits, head_dim, codebook)
         self.bits, self.head_dim, self.rotation, self.qjl_dim = bits, head_dim, rotation, qjl_dim
         self.codebook = codebook
         keys = ("levels", "boundaries", "rotation_matrix", "rotation_t", "wht_signs", "qjl_matrix",
-                "qjl_matrix_t")
+                "qjl_matrix_t") + (("key_levels", "key_boundaries") if self.key_bits != bits else ())
         self.dev = {k: torch.from_numpy(np.ascontiguousarray(self.host[k])).to(device) for k in keys}
         if prepared:
             ops = pack_mfma_operands(self.host["rotation_matrix"], self.host["qjl_matrix"] if qjl_dim else None)
@@ -242,20 +251,24 @@ class Quantizer:
                                  d["rotation_t"].data_ptr(), d["wht_signs"].data_ptr(),
                                  d["qjl_matrix"].data_ptr() if qjl_dim else None,
                                  d["qjl_matrix_t"].data_ptr() if qjl_dim else None,
-                                 d["mfma_operands"].data_ptr() if prepared else None)
+                                 d["mfma_operands"].data_ptr() if prepared else None,
+                                 0 if self.key_bits == bits else self.key_bits,
+                                 d["key_levels"].data_ptr() if self.key_bits != bits else None,
+                                 d["key_boundaries"].data_ptr() if self.key_bits != bits else None)
 
 
 class PagedCache:
     """A layer's paged compressed cache in device memory (torch tensors) plus its C struct."""
 
-    def __init__(self, num_blocks, num_kv_heads, head_dim=128, bits=4, qjl_dim=128, device="cuda"):
+    def __init__(self, num_blocks, num_kv_heads, head_dim=128, bits=4, qjl_dim=128, device="cuda", key_bits=None):
         import torch
 
         cb = head_dim * bits // 8
+        self.key_bits = bits if key_bits is None else key_bits
         self.num_blocks, self.num_kv_heads, self.head_dim = num_blocks, num_kv_heads, head_dim
         self.bits, self.qjl_dim = bits, qjl_dim
         z = lambda *shape, dt: torch.zeros(shape, dtype=dt, device=device)
-        self.k_codes = z(num_blocks, num_kv_heads, BLOCK, cb, dt=torch.uint8)
+        self.k_codes = z(num_blocks, num_kv_heads, BLOCK, head_dim * self.key_bits // 8, dt=torch.uint8)
         self.k_norm = z(num_blocks, num_kv_heads, BLOCK, dt=torch.float32)
         self.v_codes = z(num_blocks, num_kv_heads, BLOCK, cb, dt=torch.uint8)
         self.v_norm = z(num_blocks, num_kv_heads, BLOCK, dt=torch.float32)
@@ -268,7 +281,8 @@ class PagedCache:
                              self.k_codes.data_ptr(), self.k_norm.data_ptr(),
                              self.k_qjl.data_ptr() if qjl_dim else None,
                              self.k_gamma.data_ptr() if qjl_dim else None,
-                             self.v_codes.data_ptr(), self.v_norm.data_ptr())
+                             self.v_codes.data_ptr(), self.v_norm.data_ptr(),
+                             0 if self.key_bits == bits else self.key_bits)
 
     def fields(self):
         out = {"k_codes": self.k_codes, "k_norm": self.k_norm, "v_codes": self.v_codes, "v_norm": self.v_norm}
@@ -278,7 +292,8 @@ class PagedCache:
 
     def bytes_per_token_head(self):
         cb = self.head_dim * self.bits // 8
-        return 2 * (cb + 4) + ((self.qjl_dim // 8 + 4) if self.qjl_dim else 0)
+        kcb = self.head_dim * self.key_bits // 8
+        return (kcb + 4) + (cb + 4) + ((self.qjl_dim // 8 + 4) if self.qjl_dim else 0)
 
 
 def _dtype_code(t):

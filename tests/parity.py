@@ -36,8 +36,8 @@ def torch_inputs(inp, dtype, device="cuda"):
     }
 
 
-def oracle_quantizer(bits, rot=pipeline.HAAR, rot_seed=1, qjl_seed=2, law=pipeline.GAUSSIAN):
-    return pipeline.build(bits, 128, rot=rot, rot_seed=rot_seed, qjl_seed=qjl_seed, law=law)
+def oracle_quantizer(bits, rot=pipeline.HAAR, rot_seed=1, qjl_seed=2, law=pipeline.GAUSSIAN, key_bits=None):
+    return pipeline.build(bits, 128, rot=rot, rot_seed=rot_seed, qjl_seed=qjl_seed, law=law, key_bits=key_bits)
 
 
 def valid_tokens(inp):
@@ -64,14 +64,21 @@ def check_compress(inp, oq, gpu_cache, dy, dp, tokens=None, heads=None):
     host = cache_to_host(gpu_cache)
     dy = dy.cpu().numpy()
     dp = dp.cpu().numpy() if dp is not None else None
-    bits = oq["bits"]
-    lev, bnd = oq["levels"], oq["boundaries"]
     counts = {"codes_k": 0, "codes_v": 0, "bits": 0, "vectors": 0}
     blk, off = slots // 16, slots % 16
     for h in heads:
         for kind, name in ((0, "k"), (1, "v")):
+            # keys may have a codebook (and width) of their own
+            bits = oq["key_bits"] if kind == 0 else oq["bits"]
+            lev = oq["key_levels"] if kind == 0 else oq["levels"]
+            bnd = oq["key_boundaries"] if kind == 0 else oq["boundaries"]
             x = inp[name].reshape(B * cap, Hkv, d)[tok, h]
-            e = pipeline.encode_keys(x, oq) if kind == 0 else pipeline.encode_values(x, oq)
+            if kind == 1:
+                e = pipeline.encode_values(x, oq)
+            elif dp is not None:
+                e = pipeline.encode_keys(x, oq)
+            else:
+                e = pipeline.encode_keys_mse(x, oq)
             yg = dy[kind, tok, h].astype(np.float64)
             # rotated coordinates
             err = np.max(np.abs(yg - e["y"])) if len(tok) else 0.0
@@ -115,7 +122,8 @@ def check_compress(inp, oq, gpu_cache, dy, dp, tokens=None, heads=None):
 def oracle_cache(inp, oq, with_qjl=True, seqs=None):
     """The oracle's compressed cache of the given sequences (all by default)."""
     B, cap, Hkv, d = inp["k"].shape
-    cache = paged.empty_cache(inp["num_blocks"], Hkv, d, oq["bits"], qjl_dim=oq["m"] if with_qjl else None)
+    cache = paged.empty_cache(inp["num_blocks"], Hkv, d, oq["bits"], qjl_dim=oq["m"] if with_qjl else None,
+                              key_bits=oq["key_bits"])
     seqs = range(B) if seqs is None else seqs
     for b in seqs:
         L = int(inp["seq_lens"][b])
@@ -142,7 +150,8 @@ def oracle_decode(inp, host_cache, oq, with_qjl=True, seqs=None):
     seqs = list(range(B)) if seqs is None else list(seqs)
     out = attention.decode_rotated(inp["q"][seqs], host_cache, inp["block_tables"][seqs],
                                    inp["seq_lens"][seqs], oq["levels"], oq["pi"],
-                                   oq["s"] if with_qjl else None, oq["bits"])
+                                   oq["s"] if with_qjl else None, oq["bits"],
+                                   key_levels32=oq["key_levels"], key_bits=oq["key_bits"])
     return out
 
 

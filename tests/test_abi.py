@@ -39,7 +39,7 @@ def test_status_strings():
     assert fq.status_string(99) == "FQ_ERR_UNKNOWN"
 
 
-@pytest.mark.parametrize("bits", [2, 4])
+@pytest.mark.parametrize("bits", [2, 3, 4])
 @pytest.mark.parametrize("rot", [fq.ROT_HAAR, fq.ROT_WHT])
 def test_builder_matches_oracle(bits, rot):
     lib_cb = fq.build_codebook(bits, 128, rot, rot_seed=11, qjl_seed=12, qjl_dim=128)
@@ -68,7 +68,8 @@ def test_builder_errors():
     L = fq.lib()
     buf = np.zeros(128 * 128, np.float32)
     p = buf.ctypes.data_as(ctypes.c_void_p)
-    assert L.fq_build_codebook(3, 128, 0, 1, 2, 128, p, p, None, None, None, None, None) == fq.FQ_ERR_UNSUPPORTED
+    assert L.fq_build_codebook(5, 128, 0, 1, 2, 128, p, p, None, None, None, None, None) == fq.FQ_ERR_UNSUPPORTED
+    assert L.fq_build_codebook(1, 128, 0, 1, 2, 128, p, p, None, None, None, None, None) == fq.FQ_ERR_UNSUPPORTED
     assert L.fq_build_codebook(4, 64, 0, 1, 2, 128, p, p, None, None, None, None, None) == fq.FQ_ERR_UNSUPPORTED
     assert L.fq_build_codebook(4, 128, 5, 1, 2, 128, p, p, None, None, None, None, None) == fq.FQ_ERR_INVALID_ARG
     assert L.fq_build_codebook(4, 128, 0, 1, 2, 128, None, p, None, None, None, None, None) == fq.FQ_ERR_INVALID_ARG
@@ -100,8 +101,20 @@ def test_compress_argument_checks():
     assert call(qz, cz, slots=None) == fq.FQ_ERR_INVALID_ARG
     assert call(qz, cz, k=base + 2) == fq.FQ_ERR_INVALID_ARG  # vectors must be 16-byte aligned
     assert call(qz, cz, hs=4) == fq.FQ_ERR_INVALID_ARG        # 8-byte head stride
-    qb = fq.QuantizerT(3, 128, 0, 128, base, base, base, base, base, base, base, None)
+    qb = fq.QuantizerT(5, 128, 0, 128, base, base, base, base, base, base, base, None)
     assert call(qb, cz) == fq.FQ_ERR_UNSUPPORTED
+    # keys of their own width: 2..4 bits, with their own codebook, matching the cache's
+    qk = fq.QuantizerT(4, 128, 0, 128, base, base, base, base, base, base, base, None, 5, base, base)
+    assert call(qk, cz) == fq.FQ_ERR_UNSUPPORTED
+    qk = fq.QuantizerT(4, 128, 0, 128, base, base, base, base, base, base, base, None, 3, None, base)
+    assert call(qk, cz) == fq.FQ_ERR_INVALID_ARG              # key codebook required
+    qk = fq.QuantizerT(4, 128, 0, 128, base, base, base, base, base, base, base, None, 3, base, base)
+    assert call(qk, cz) == fq.FQ_ERR_INVALID_ARG              # the cache's keys are 4-bit
+    ck = fq.CacheT(4, 16, 2, 128, 4, 128, base, base, base, base, base, base, 3)
+    assert call(qk, ck, n=0) == fq.FQ_OK
+    assert call(qz, ck) == fq.FQ_ERR_INVALID_ARG              # 3-bit keys in the cache, 4-bit quantizer
+    qk4 = fq.QuantizerT(4, 128, 0, 128, base, base, base, base, base, base, base, None, 4, None, None)
+    assert call(qk4, cz, n=0) == fq.FQ_OK                     # key_bits = bits: the shared codebook
     cb = fq.CacheT(4, 8, 2, 128, 4, 128, base, base, base, base, base, base)
     assert call(qz, cb) == fq.FQ_ERR_UNSUPPORTED              # block size must be 16
     cm = fq.CacheT(4, 16, 2, 128, 2, 128, base, base, base, base, base, base)

@@ -124,7 +124,7 @@ def test_lower_mse_than_the_scaled_gaussian_codebook_and_locally_optimal(bits):
             assert _mse(l2, 0.5 * (l2[:-1] + l2[1:]), d) > best
 
 
-@pytest.mark.parametrize("bits", [2, 4])
+@pytest.mark.parametrize("bits", [2, 3, 4])
 @pytest.mark.parametrize("d", [3, 16, 128, 256])
 def test_host_builder_matches_the_oracle(bits, d):
     lev, bnd = fq.build_levels(bits, d, fq.CB_SPHERE)
@@ -132,7 +132,7 @@ def test_host_builder_matches_the_oracle(bits, d):
     assert np.array_equal(lev, ol) and np.array_equal(bnd, ob)
 
 
-@pytest.mark.parametrize("bits", [2, 4])
+@pytest.mark.parametrize("bits", [2, 3, 4])
 def test_host_gaussian_kind_is_the_quantizer_codebook(bits):
     lev, bnd = fq.build_levels(bits, 128, fq.CB_GAUSSIAN)
     h = fq.build_codebook(bits)
@@ -150,6 +150,6 @@ def test_host_builder_argument_checks():
     p = lambda a: a.ctypes.data_as(ctypes.c_void_p)
     assert lib.fq_build_levels(4, 128, 7, p(lev), p(bnd)) == 1  # bad kind
     assert lib.fq_build_levels(4, 128, fq.CB_SPHERE, None, p(bnd)) == 1
-    assert lib.fq_build_levels(3, 128, fq.CB_SPHERE, p(lev), p(bnd)) == 2
+    assert lib.fq_build_levels(5, 128, fq.CB_SPHERE, p(lev), p(bnd)) == 2
     assert lib.fq_build_levels(4, 2, fq.CB_SPHERE, p(lev), p(bnd)) == 2
     assert lib.fq_build_levels(4, 257, fq.CB_SPHERE, p(lev), p(bnd)) == 2

@@ -66,19 +66,19 @@ def _strip(host, slots):
     return out
 
 
-def _step_case(w, inp, rot=fq.ROT_HAAR, with_qjl=True, num_splits=0, kv_dtype=None, skip=()):
+def _step_case(w, inp, rot=fq.ROT_HAAR, with_qjl=True, num_splits=0, kv_dtype=None, skip=(), key_bits=None):
     kvd = w.dtype if kv_dtype is None else kv_dtype
     t = parity.torch_inputs(inp, kvd)
     q = parity.torch_inputs(inp, w.dtype)["q"]
-    oq = parity.oracle_quantizer(w.bits, rot=rot)
-    qz = fq.Quantizer(w.bits, 128, rot, 1, 2, 128)
+    oq = parity.oracle_quantizer(w.bits, rot=rot, key_bits=key_bits)
+    qz = fq.Quantizer(w.bits, 128, rot, 1, 2, 128, key_bits=key_bits)
     B, cap, Hkv, d = inp["k"].shape
     flat, slots = _newest(inp)
     slots = slots.copy()
     for b in skip:
         slots[b] = -1
     host0 = parity.oracle_cache(_without_newest(inp), oq, with_qjl=with_qjl)
-    cache = fq.PagedCache(inp["num_blocks"], Hkv, 128, w.bits, 128 if with_qjl else 0)
+    cache = fq.PagedCache(inp["num_blocks"], Hkv, 128, w.bits, 128 if with_qjl else 0, key_bits=key_bits)
     parity.upload_cache(host0, cache)
     _fill_garbage(cache, slots)
     host_g = parity.cache_to_host(cache)
