@@ -95,6 +95,8 @@ def parse():
     p.add_argument("--split-step", action="store_true",
                    help="per layer fq_step_prepare, then fq_step_attend (the two halves of fq_decode_step)")
     p.add_argument("--no-extra", action="store_true", help="skip the other workloads' measurements")
+    p.add_argument("--only", choices=ONLY, default=None,
+                   help="measure one workload alone (for profiling its kernels); prints {only, result}")
     p.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                    help="only run a plain device-to-device copy of BYTES (for scaling HBM byte counters)")
     return p.parse_args()
@@ -120,16 +122,43 @@ def cpu_baseline(w, layer_seed, budget_s):
     pipeline.compress(cache, inp["k"][0, :L], inp["v"][0, :L], inp["slot_mapping"][:L], oq)
     info = threadpoolctl.threadpool_info()
     cores = max([i.get("num_threads", 1) for i in info] + [1])
-    n = 0
-    t0 = time.perf_counter()
-    while True:
-        pipeline.compress(cache, inp["k"][0, L - 1:L], inp["v"][0, L - 1:L], inp["slot_mapping"][L - 1:L], oq)
-        attention.decode_rotated(inp["q"], cache, inp["block_tables"], inp["seq_lens"], oq["levels"],
-                                 oq["pi"], oq["s"], 4)
-        n += 1
-        if time.perf_counter() - t0 >= budget_s:
-            break
-    dt = time.perf_counter() - t0
+
+    def decode_rate(budget):
+        n = 0
+        t0 = time.perf_counter()
+        while True:
+            pipeline.compress(cache, inp["k"][0, L - 1:L], inp["v"][0, L - 1:L], inp["slot_mapping"][L - 1:L], oq)
+            attention.decode_rotated(inp["q"], cache, inp["block_tables"], inp["seq_lens"], oq["levels"],
+                                     oq["pi"], oq["s"], 4)
+            n += 1
+            if time.perf_counter() - t0 >= budget:
+                break
+        return n, time.perf_counter() - t0
+
+    def compress_rate(budget):
+        # whole-sequence compress of the sample's K and V (L tokens x 8 heads each)
+        n = 0
+        t0 = time.perf_counter()
+        while True:
+            pipeline.compress(cache, inp["k"][0, :L], inp["v"][0, :L], inp["slot_mapping"][:L], oq)
+            n += 1
+            if time.perf_counter() - t0 >= budget:
+                break
+        return n * 2 * L * w.num_kv_heads, time.perf_counter() - t0
+
+    n, dt = decode_rate(budget_s * 0.6)
+    nv, dtc = compress_rate(budget_s * 0.25)
+    with threadpoolctl.threadpool_limits(limits=1):
+        n1, dt1 = decode_rate(budget_s * 0.15)
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
     per_seq_layer = dt / n
     return {
         "value": 1.0 / (per_seq_layer * w.layers),
@@ -138,11 +167,30 @@ def cpu_baseline(w, layer_seed, budget_s):
         "kind": "oracle",
         "sample": "%d x (compress 1 new token + decode 1 sequence of %d tokens, 32 q / 8 kv heads, one layer) "
                   "in %.1f s; tokens/s = 1 / (seconds per sequence-layer x %d layers)" % (n, L, dt, w.layers),
+        "single_thread_tokens_per_s": 1.0 / (dt1 / n1 * w.layers),
+        "single_thread_sample": "%d decode samples in %.1f s with the BLAS pool limited to 1 thread" % (n1, dt1),
+        "compress_mvec_per_s": nv / dtc / 1e6,
+        "compress_sample": "%d K + V vectors (whole %d-token sequences x 8 heads) in %.1f s" % (nv, L, dtc),
+        "cpu_model": model,
+        "os_cpu_count": os.cpu_count(),
+        "blas": [{k: i.get(k) for k in ("internal_api", "num_threads")} for i in info],
     }
 
 
-def _events_ms(fn, reps, stream):
-    """Mean duration (ms) of fn() from HIP events recorded on the library's stream."""
+GB = 1 << 30
+MIN_SAMPLES = 50  # timed repetitions behind every median
+
+
+def stats_ms(samples):
+    """Median and p10 / p90 (ms) of per-call durations."""
+    x = np.asarray(samples, np.float64)
+    return {"median_ms": float(np.median(x)), "p10_ms": float(np.percentile(x, 10)),
+            "p90_ms": float(np.percentile(x, 90)), "samples": int(x.size)}
+
+
+def _events_samples(fn, reps, stream, per=1):
+    """Durations (ms) of reps calls of fn() from HIP events recorded on the library's
+    stream, each divided by per (the number of calls fn() enqueues)."""
     import torch
 
     out = []
@@ -153,12 +201,42 @@ def _events_ms(fn, reps, stream):
         e1.record(stream)
         out.append((e0, e1))
     torch.cuda.synchronize()
-    return float(np.mean([a.elapsed_time(b) for a, b in out]))
+    return [a.elapsed_time(b) / per for a, b in out]
 
 
-def decode_layer_measure(index, bits, rot, replicas, reps, stream):
+def _events_ms(fn, reps, stream):
+    """Median duration (ms) of fn() from HIP events recorded on the library's stream."""
+    return float(np.median(_events_samples(fn, reps, stream)))
+
+
+def _capture(calls):
+    """A HIP graph holding the given calls (captured on a side stream, replayed once)."""
+    import torch
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            for c in calls:
+                c()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    return g
+
+
+def graph_stats(calls, stream, reps=MIN_SAMPLES):
+    """Per-call device time: HIP events around reps replays of a graph holding the calls,
+    each replay's time divided by the number of calls; median, p10, p90."""
+    g = _capture(calls)
+    return stats_ms(_events_samples(g.replay, reps, stream, per=len(calls)))
+
+
+def decode_layer_measure(index, bits, rot, stream, key_bits=None):
     """One decode layer of a workload, rotating through distinct cache replicas so that
-    the reads come from HBM (replicas x cache bytes > the 256 MB last-level cache)."""
+    the reads come from HBM: at least 1 GiB of caches (4x the 256 MB last-level cache)."""
     import torch
 
     from kv_cache_vector_tq4_amd import fq, synth
@@ -169,14 +247,16 @@ def decode_layer_measure(index, bits, rot, replicas, reps, stream):
     bt_np, nblocks = synth.block_tables(77 + index, w.seq_lens, w.capacity_tokens)
     slots = torch.from_numpy(np.concatenate([synth.slot_mapping_for(bt_np[b], int(lens[b]))
                                              for b in range(B)])).cuda()
-    qz = fq.Quantizer(bits, d, rot, 1, 2, 128)
+    qz = fq.Quantizer(bits, d, rot, 1, 2, 128, key_bits=key_bits)
+    per_cache = fq.PagedCache(1, Hkv, d, bits, 128, key_bits=key_bits).bytes_per_token_head() * int(lens.sum()) * Hkv
+    replicas = int(min(256, max(2, math.ceil(GB / per_cache))))
     caches = []
+    k, v = synth.kv_device(6000 + 17 * index, int(lens.sum()), Hkv, d)
     for r in range(replicas):
-        c = fq.PagedCache(nblocks, Hkv, d, bits, 128)
-        k, v = synth.kv_device(6000 + 17 * index + r, int(lens.sum()), Hkv, d)
+        c = fq.PagedCache(nblocks, Hkv, d, bits, 128, key_bits=key_bits)
         fq.compress(qz, c, k, v, slots)
-        del k, v
         caches.append(c)
+    del k, v
     bt = torch.from_numpy(bt_np).cuda()
     lt = torch.from_numpy(lens).cuda()
     q = torch.randn((B, Hq, d), device="cuda").to(torch.bfloat16)
@@ -189,31 +269,25 @@ def decode_layer_measure(index, bits, rot, replicas, reps, stream):
 
     for _ in range(3):
         call()
-    ms_eager = _events_ms(call, reps, stream)
+    ms_eager = _events_ms(call, MIN_SAMPLES, stream)
     # device time of a call: HIP events around replays of a graph holding one call per
     # replica (as for the stack's decode roofline; eager calls add host launch gaps)
-    side = torch.cuda.Stream()
-    side.wait_stream(torch.cuda.current_stream())
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.stream(side):
-        with torch.cuda.graph(g, stream=side):
-            for r in range(replicas):
-                fq.decode(qz, caches[r], q, bt, lt, int(lens.max()), workspace=ws, out=out)
-    torch.cuda.current_stream().wait_stream(side)
-    torch.cuda.synchronize()
-    g.replay()
-    torch.cuda.synchronize()
-    ms = _events_ms(g.replay, max(5, reps // replicas), stream) / replicas
+    st = graph_stats([lambda c=c: fq.decode(qz, c, q, bt, lt, int(lens.max()), workspace=ws, out=out)
+                      for c in caches], stream)
+    ms = st["median_ms"]
     nbytes = int(lens.sum()) * Hkv * caches[0].bytes_per_token_head()
-    return {"workload": w.name, "bits": bits, "rotation": "wht" if rot else "haar",
+    return {"workload": w.name, "bits": bits, "key_bits": caches[0].key_bits, "rotation": "wht" if rot else "haar",
             "splits": fq.auto_splits(B, Hkv, int(lens.max())), "decode_ms": ms, "decode_ms_eager": ms_eager,
-            "timing": "HIP events around graph replays of one call per cache replica",
+            "p10_ms": st["p10_ms"], "p90_ms": st["p90_ms"], "samples": st["samples"],
+            "timing": "HIP events around graph replays of one call per cache replica (median over replays)",
             "achieved_gbs": nbytes / (ms * 1e-3) / 1e9, "frac_hbm": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-            "algorithmic_bytes": nbytes, "cache_replicas": replicas}
+            "algorithmic_bytes": nbytes, "cache_replicas": replicas,
+            "rotated_bytes": replicas * nbytes}
 
 
-def compress_layer_measure(index, rot, reps, stream):
-    """Prefill compress of one layer's whole context (K and V) of a workload."""
+def compress_layer_measure(index, rot, stream, bits=4, key_bits=None):
+    """Prefill compress of one layer's whole context (K and V) of a workload; inputs and
+    output caches rotate over at least 1 GiB so that neither sits in the last-level cache."""
     import torch
 
     from kv_cache_vector_tq4_amd import fq, synth
@@ -221,35 +295,51 @@ def compress_layer_measure(index, rot, reps, stream):
     w = synth.workload(index)
     Hkv, d = w.num_kv_heads, w.head_dim
     T = int(np.sum(w.seq_lens))
-    qz = fq.Quantizer(4, d, rot, 1, 2, 128)
-    cache = fq.PagedCache((T + 15) // 16, Hkv, d, 4, 128)
+    qz = fq.Quantizer(bits, d, rot, 1, 2, 128, key_bits=key_bits)
     slots = torch.arange(T, dtype=torch.int64, device="cuda")
-    k, v = synth.kv_device(8000 + index, T, Hkv, d)
-    fq.compress(qz, cache, k, v, slots)
-    ms = _events_ms(lambda: fq.compress(qz, cache, k, v, slots), reps, stream)
     nvec = 2 * T * Hkv
-    nbytes = nvec * d * 2 + T * 8 + T * Hkv * cache.bytes_per_token_head()
-    return {"workload": w.name, "rotation": "wht" if rot else "haar", "vectors": nvec, "ms": ms,
+    probe = fq.PagedCache(1, Hkv, d, bits, 128, key_bits=key_bits)
+    nbytes = nvec * d * 2 + T * 8 + T * Hkv * probe.bytes_per_token_head()
+    reps = int(min(64, max(2, math.ceil(GB / nbytes))))
+    pool = []
+    for r in range(reps):
+        k, v = synth.kv_device(8000 + index + 101 * r, T, Hkv, d)
+        pool.append((k, v, fq.PagedCache((T + 15) // 16, Hkv, d, bits, 128, key_bits=key_bits)))
+    st = graph_stats([lambda x=x: fq.compress(qz, x[2], x[0], x[1], slots) for x in pool], stream)
+    ms = st["median_ms"]
+    return {"workload": w.name, "rotation": "wht" if rot else "haar", "bits": bits, "key_bits": probe.key_bits,
+            "vectors": nvec, "ms": ms, "p10_ms": st["p10_ms"], "p90_ms": st["p90_ms"], "samples": st["samples"],
+            "timing": "HIP events around graph replays of one call per input / cache replica (median)",
+            "replicas": reps, "rotated_bytes": reps * nbytes,
             "mvec_per_s": nvec / (ms * 1e-3) / 1e6, "achieved_gbs": nbytes / (ms * 1e-3) / 1e9,
-            "frac_hbm": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+            "frac_hbm": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "algorithmic_bytes": nbytes}
 
 
-def decompress_measure(qz, cache, slots, reps, stream):
-    """fq_decompress of a layer's stored tokens (K and V, bf16 out), timed with events."""
+def decompress_measure(qz, caches, slots, stream):
+    """fq_decompress of a layer's stored tokens (K and V, bf16 out): one call per layer
+    cache (each 144 MB of input) into three rotating output pairs (474 MB each), so the
+    reads and writes of a call are not in the last-level cache; graph replays."""
     import torch
 
     from kv_cache_vector_tq4_amd import fq
 
-    T, Hkv, d = slots.numel(), cache.num_kv_heads, cache.head_dim
-    ko = torch.empty((T, Hkv, d), dtype=torch.bfloat16, device=slots.device)
-    vo = torch.empty_like(ko)
-    fq.decompress(qz, cache, slots, k_out=ko, v_out=vo)
-    ms = _events_ms(lambda: fq.decompress(qz, cache, slots, k_out=ko, v_out=vo), reps, stream)
+    T, Hkv, d = slots.numel(), caches[0].num_kv_heads, caches[0].head_dim
+    outs = [(torch.empty((T, Hkv, d), dtype=torch.bfloat16, device=slots.device),
+             torch.empty((T, Hkv, d), dtype=torch.bfloat16, device=slots.device)) for _ in range(3)]
+    calls = [lambda i=i, c=c: fq.decompress(qz, c, slots, k_out=outs[i % 3][0], v_out=outs[i % 3][1])
+             for i, c in enumerate(caches)]
+    st = graph_stats(calls, stream, reps=max(2, MIN_SAMPLES // 8))
+    ms = st["median_ms"]
+    cache = caches[0]
     nvec = 2 * int((slots >= 0).sum().item()) * Hkv
     nbytes = nvec * (d * cache.bits // 8 + 4 + 2 * d) + 8 * T
-    del ko, vo
+    del outs
     return {"what": "fq_decompress of one layer's stored tokens, K and V, bf16 out (MSE reconstruction n Pi^T c)",
-            "vectors": nvec, "ms": ms, "mvec_per_s": nvec / (ms * 1e-3) / 1e6,
+            "vectors": nvec, "ms": ms, "p10_ms": st["p10_ms"], "p90_ms": st["p90_ms"],
+            "samples": st["samples"] * len(caches),
+            "timing": "HIP events around graph replays of one call per layer cache (%d calls, median of replays)"
+                      % len(caches),
+            "mvec_per_s": nvec / (ms * 1e-3) / 1e6,
             "algorithmic_bytes": nbytes, "achieved_gbs": nbytes / (ms * 1e-3) / 1e9,
             "frac_hbm": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
             "bytes_per_vector": "codes %d + norm 4 in, %d out" % (d * cache.bits // 8, 2 * d)}
@@ -285,26 +375,9 @@ def window_measure(qz, cache, q, bt, lens, slots_np, W, reps, stream):
     wsa = torch.empty(1 << 20, dtype=torch.uint8, device=dev)
     app = lambda: fq.window_append(qz, cw, kn, vn, pos, ev, wk, wv, workspace=wsa)
     def graph_us(fn, n=8):
-        """Mean GPU time of fn() from HIP-graph replays of n calls (no host gaps)."""
+        """Median GPU time (us) of fn() over replays of a HIP graph of n calls (no host gaps)."""
         fn()
-        side = torch.cuda.Stream()
-        side.wait_stream(torch.cuda.current_stream())
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.stream(side):
-            with torch.cuda.graph(g, stream=side):
-                for _ in range(n):
-                    fn()
-        torch.cuda.current_stream().wait_stream(side)
-        torch.cuda.synchronize()
-        g.replay()
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(reps):
-            g.replay()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) * 1e3 / (reps * n)
+        return graph_stats([fn] * n, stream)["median_ms"] * 1e3
 
     per_split = {}
     for sp in (1, 2, 4):
@@ -320,7 +393,7 @@ def window_measure(qz, cache, q, bt, lens, slots_np, W, reps, stream):
     del cw
     return {"what": "per layer, batch 32: fq_window_append + fq_decode_attention_window, %d-token bf16 window, "
                     "the rest of each context compressed" % W,
-            "timing": "HIP-graph replays (8 calls per graph)",
+            "timing": "HIP-graph replays (8 calls per graph; median of %d replays)" % MIN_SAMPLES,
             "window": W, "append_us": append_us, "decode_us_by_splits": per_split,
             "decode_us_empty_window_1_split": empty_us, "plain_decode_us_same_lengths": plain_us}
 
@@ -345,20 +418,14 @@ def prefill_measure(qz, cache, bt, lens, reps, stream):
     out = torch.empty((L, Hq, d), dtype=torch.float32, device=dev)
     fn = lambda: fq.prefill(qz, cache, q, q_seq, q_lens, bt, L, workspace=ws, out=out)
     fn()
-    side = torch.cuda.Stream()
-    side.wait_stream(torch.cuda.current_stream())
-    gr = torch.cuda.CUDAGraph()
-    with torch.cuda.stream(side):
-        with torch.cuda.graph(gr, stream=side):
-            fn()
-    torch.cuda.current_stream().wait_stream(side)
-    torch.cuda.synchronize()
-    ms = _events_ms(lambda: gr.replay(), reps, stream)
+    st = graph_stats([fn], stream, reps=reps)
+    ms = st["median_ms"]
     attended = L * (L + 1) // 2
     return {"what": "causal prefill attention of one %d-token sequence over its compressed cache "
-                    "(fq_prefill_attention: each query token a decode batch entry; no reuse of pages across "
-                    "queries beyond the caches)" % L,
-            "queries": L, "q_heads": Hq, "ms": ms, "queries_per_s": L / (ms * 1e-3),
+                    "(fq_prefill_attention, tiled: a wave per 16 query-head rows shares each page of its rows' "
+                    "prefixes; query and output rotations as row GEMMs on the matrix cores)" % L,
+            "queries": L, "q_heads": Hq, "ms": ms, "p10_ms": st["p10_ms"], "p90_ms": st["p90_ms"],
+            "samples": st["samples"], "queries_per_s": L / (ms * 1e-3),
             "attended_token_heads_per_s": attended * Hkv / (ms * 1e-3),
             "cache_bytes_read_per_query_sum": attended * Hkv * cache.bytes_per_token_head()}
 
@@ -385,29 +452,57 @@ def attention_cosines(q, k, v, lens, kv_rows, out, seqs):
     return {"mean": float(c.mean()), "min": float(c.min()), "pairs": int(c.size)}
 
 
+def variants_measure(stream):
+    """The codebook variants on the batch-32 8B-shaped layer: 3-bit keys (+ QJL) and values,
+    and the Prod budget at 4 bits (3-bit keys + QJL, 4-bit values): decode (the library's
+    split choice) and prefill compress, each rotating over >= 1 GiB."""
+    from kv_cache_vector_tq4_amd import fq
+
+    out = {}
+    for name, bits, kb in (("bits3", 3, 3), ("prod", 4, 3)):
+        out[name] = {"decode": decode_layer_measure(2, bits, fq.ROT_HAAR, stream, key_bits=kb),
+                     "compress": compress_layer_measure(2, fq.ROT_HAAR, stream, bits=bits, key_bits=kb)}
+    return out
+
+
 def stream_compress_measure(bits, layers, stream):
-    """The 80-layer 70B-shaped prefill stream: every layer's 8 x 32768 K and V vectors
-    (bf16, generated on the device) compressed with that layer's quantizer."""
+    """The 80-layer 70B-shaped prefill stream: every layer's 32768 tokens x 8 KV heads of K
+    and V (bf16, generated on the device beforehand) compressed with that layer's
+    quantizer. Inputs come from a pool of 8 layers' K/V (1.07 GB) and outputs go to a
+    ring of caches of at least 1 GiB, both cycled, so that no layer finds its inputs or
+    its outputs in the last-level cache; the 80 calls are one graph."""
     import torch
 
     from kv_cache_vector_tq4_amd import fq, synth
 
     T, Hkv, d = 32768, 8, 128
     slots = torch.arange(T, dtype=torch.int64, device="cuda")
-    cache = fq.PagedCache(T // 16, Hkv, d, bits, 128)
-    total_ms = 0.0
-    for layer in range(layers):
-        qz = fq.Quantizer(bits, d, fq.ROT_HAAR, 1 + layer, 2 + layer, 128)
-        k, v = synth.kv_device(7000 + layer, T, Hkv, d)
-        total_ms += _events_ms(lambda: fq.compress(qz, cache, k, v, slots), 1, stream)
-        del k, v
+    pool = [synth.kv_device(7000 + i, T, Hkv, d) for i in range(8)]
+    per_out = fq.PagedCache(1, Hkv, d, bits, 128).bytes_per_token_head() * T * Hkv
+    nc = int(math.ceil(GB / per_out))
+    caches = [fq.PagedCache(T // 16, Hkv, d, bits, 128) for _ in range(nc)]
+    quants = [fq.Quantizer(bits, d, fq.ROT_HAAR, 1 + layer, 2 + layer, 128) for layer in range(layers)]
+    calls = [lambda l=l: fq.compress(quants[l], caches[l % nc], pool[l % 8][0], pool[l % 8][1], slots)
+             for l in range(layers)]
+    g = _capture(calls)
+    tot = _events_samples(g.replay, 5, stream)
+    total_ms = float(np.median(tot))
     nvec = 2 * layers * T * Hkv
-    out_b = cache.bytes_per_token_head() * T * Hkv * layers
+    out_b = caches[0].bytes_per_token_head() * T * Hkv * layers
     in_b = 2 * layers * T * Hkv * d * 2 + layers * T * 8
+    del pool, caches
     return {"layers": layers, "bits": bits, "vectors": nvec, "ms": total_ms,
+            "ms_per_layer": total_ms / layers, "replays": len(tot),
+            "p10_ms": float(np.percentile(tot, 10)), "p90_ms": float(np.percentile(tot, 90)),
+            "timing": "HIP events around replays of a graph of the %d layers' fq_compress calls (median)" % layers,
             "mvec_per_s": nvec / (total_ms * 1e-3) / 1e6,
             "achieved_gbs": (in_b + out_b) / (total_ms * 1e-3) / 1e9,
-            "frac_hbm": (in_b + out_b) / (total_ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+            "frac_hbm": (in_b + out_b) / (total_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "algorithmic_bytes": in_b + out_b}
+
+
+ONLY = ("step", "step4", "c2", "c4_haar", "c4_wht", "c4_compress_haar", "c4_compress_wht", "c5_decode",
+        "stream4", "stream2", "decompress", "window", "prefill", "bits3", "prod")
 
 
 def main():
@@ -432,12 +527,31 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"calibrate_copy_bytes_read": 4 * n, "calibrate_copy_bytes_written": 4 * n, "launches": 3}))
         return
+    stream = torch.cuda.current_stream()
+    if args.only and args.only not in ("step", "step4", "decompress", "window", "prefill"):
+        # one other workload alone (for profiling its kernels)
+        log("measuring %s alone..." % args.only)
+        f = {"c2": lambda: decode_layer_measure(1, 4, fq.ROT_HAAR, stream),
+             "c4_haar": lambda: decode_layer_measure(3, 4, fq.ROT_HAAR, stream),
+             "c4_wht": lambda: decode_layer_measure(3, 4, fq.ROT_WHT, stream),
+             "c4_compress_haar": lambda: compress_layer_measure(3, fq.ROT_HAAR, stream),
+             "c4_compress_wht": lambda: compress_layer_measure(3, fq.ROT_WHT, stream),
+             "c5_decode": lambda: decode_layer_measure(4, 2, fq.ROT_HAAR, stream),
+             "stream4": lambda: stream_compress_measure(4, 80, stream),
+             "stream2": lambda: stream_compress_measure(2, 80, stream),
+             "bits3": lambda: variants_measure(stream)["bits3"],
+             "prod": lambda: variants_measure(stream)["prod"]}[args.only]
+        print(json.dumps({"only": args.only, "result": f()}), flush=True)
+        return
+
     w = synth.workload(2)
     w.layers = args.layers
     B, Hq, Hkv, d = w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim
     lens = np.asarray(w.seq_lens, np.int32)
     max_len = int(lens.max())
     splits = args.splits if args.splits > 0 else fq.auto_splits(B, Hkv, max_len)
+    if args.only == "step4":
+        splits = 4
 
     qz = fq.Quantizer(4, d, fq.ROT_HAAR, 1, 2, 128, device=dev)
     bt_np, nblocks = synth.block_tables(1234, w.seq_lens, w.capacity_tokens)
@@ -449,7 +563,6 @@ def main():
                                            for b in range(B)], np.int64)).to(dev)
     ntok = int(lens.sum())
 
-    stream = torch.cuda.current_stream()
     caches, qs, knew, vnew = [], [], [], []
     comp_ms = []
     log("filling %d layer caches (%d tokens x %d heads each)..." % (w.layers, ntok, Hkv))
@@ -470,9 +583,19 @@ def main():
         caches.append(cache)
         del k, v
     torch.cuda.synchronize()
-    decomp = decompress_measure(qz, caches[0], slots_all[slots_all >= 0].contiguous(), 5, stream)
-    win = window_measure(qz, caches[0], qs[0], bt, lens, slots_np, 128, 10, stream)
-    pre = prefill_measure(qz, caches[0], bt, lens, 3, stream)
+    if args.only in ("decompress", "window", "prefill"):
+        log("measuring %s alone..." % args.only)
+        f = {"decompress": lambda: decompress_measure(qz, caches, slots_all[slots_all >= 0].contiguous(), stream),
+             "window": lambda: window_measure(qz, caches[0], qs[0], bt, lens, slots_np, 128, MIN_SAMPLES, stream),
+             "prefill": lambda: prefill_measure(qz, caches[0], bt, lens, 10, stream)}[args.only]
+        print(json.dumps({"only": args.only, "result": f()}), flush=True)
+        return
+    measure_parts = not args.only
+    if measure_parts:
+        log("decompress, residual window, prefill...")
+        decomp = decompress_measure(qz, caches, slots_all[slots_all >= 0].contiguous(), stream)
+        win = window_measure(qz, caches[0], qs[0], bt, lens, slots_np, 128, MIN_SAMPLES, stream)
+        pre = prefill_measure(qz, caches[0], bt, lens, 10, stream)
     ws_bytes = fq.workspace_bytes(B, Hq, Hkv, d, 128, max_len, splits)
     # one workspace per layer: each keeps its layer's prepared queries, so the
     # attention launches can also be replayed on their own
@@ -482,16 +605,17 @@ def main():
     ev = []  # (start, end) events around each timed call (the attention part) in the timed steps
     mode = "separate" if args.separate else "split" if args.split_step else "step"
 
-    def attend(layer):
+    def attend(layer, sp=None):
+        sp = splits if sp is None else sp
         if mode == "separate":
-            fq.decode(qz, caches[layer], qs[layer], bt, lens_t, max_len, num_splits=splits, workspace=wss[layer],
+            fq.decode(qz, caches[layer], qs[layer], bt, lens_t, max_len, num_splits=sp, workspace=wss[layer],
                       out=outs[layer])
         elif mode == "split":
-            fq.step_attend(qz, caches[layer], B, Hq, bt, lens_t, max_len, wss[layer], num_splits=splits,
+            fq.step_attend(qz, caches[layer], B, Hq, bt, lens_t, max_len, wss[layer], num_splits=sp,
                            out=outs[layer])
         else:
             fq.decode_step(qz, caches[layer], knew[layer], vnew[layer], new_slots, qs[layer], bt, lens_t, max_len,
-                           num_splits=splits, workspace=wss[layer], out=outs[layer])
+                           num_splits=sp, workspace=wss[layer], out=outs[layer])
 
     def prepare(layer):
         if mode == "separate":
@@ -518,7 +642,7 @@ def main():
     graph = None
     graph_check = None
     if not args.no_graph:
-        # The step is launch-bound (two launches per layer): capture it once, replay it.
+        # The step is launch-bound (one or two launches per layer): capture it once, replay it.
         ref = [o.clone() for o in outs]
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())
@@ -557,40 +681,37 @@ def main():
         step(True)
     torch.cuda.synchronize()
     ms_eager = (time.perf_counter() - t1) * 1000.0 / args.steps
-    dec_ms_eager = float(np.mean([a.elapsed_time(b) for a, b in ev]))
-    # ... and from HIP events around replays of a graph holding only the layers'
-    # attention launches (device time of the launch as the stack runs it), and one
-    # holding only the preparation launches
+    dec_ms_eager = float(np.median([a.elapsed_time(b) for a, b in ev]))
+    # ... and from HIP events around >= 50 replays of a graph holding only the layers'
+    # attention launches (device time of the launch as the stack runs it; median and
+    # p10 / p90 over replays), and one holding only the preparation launches
     dec_ms = dec_ms_eager
+    dec_stats = None
     prep_ms = None
     if graph is not None:
-        def graph_ms(fn):
-            side = torch.cuda.Stream()
-            side.wait_stream(torch.cuda.current_stream())
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.stream(side):
-                with torch.cuda.graph(g, stream=side):
-                    for layer in range(w.layers):
-                        fn(layer)
-            torch.cuda.current_stream().wait_stream(side)
-            torch.cuda.synchronize()
-            g.replay()
-            torch.cuda.synchronize()
-            pairs = []
-            for _ in range(args.steps):
-                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                e0.record(stream)
-                g.replay()
-                e1.record(stream)
-                pairs.append((e0, e1))
-            torch.cuda.synchronize()
-            return float(np.mean([a.elapsed_time(b) for a, b in pairs])) / w.layers
-
         ref = [o.clone() for o in outs]
-        dec_ms = graph_ms(attend)
+        dec_stats = graph_stats([lambda l=l: attend(l) for l in range(w.layers)], stream)
+        dec_ms = dec_stats["median_ms"]
         assert all(torch.equal(o, r) for o, r in zip(outs, ref)), "attention replays differ from the step"
         if mode != "step":
-            prep_ms = graph_ms(prepare)
+            prep_ms = graph_stats([lambda l=l: prepare(l) for l in range(w.layers)], stream)["median_ms"]
+    four = None
+    if mode == "step" and splits != 4 and graph is not None and measure_parts:
+        # the batch-32 configuration's own 4-way split, next to the library's choice
+        ws4 = [torch.empty(fq.workspace_bytes(B, Hq, Hkv, d, 128, max_len, 4), dtype=torch.uint8, device=dev)
+               for _ in range(w.layers)]
+        o4 = [torch.empty_like(o) for o in outs]
+        st4 = graph_stats([lambda l=l: fq.decode_step(qz, caches[l], knew[l], vnew[l], new_slots, qs[l], bt, lens_t,
+                                                      max_len, num_splits=4, workspace=ws4[l], out=o4[l])
+                           for l in range(w.layers)], stream)
+        diff4 = max(float((a - b).abs().max()) for a, b in zip(o4, outs))
+        lb4 = ntok * Hkv * caches[0].bytes_per_token_head() + B * Hkv * (2 * d * 2 + caches[0].bytes_per_token_head())
+        four = dict(st4, what="fq_decode_step at 4 splits (prepare_queries + packed split attention + merge), "
+                              "per layer", tokens_per_s=B / (w.layers * st4["median_ms"] * 1e-3),
+                    achieved_gbs=lb4 / (st4["median_ms"] * 1e-3) / 1e9,
+                    frac_hbm=lb4 / (st4["median_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                    max_abs_vs_one_split=diff4)
+        del ws4, o4
 
     # accuracy: layer 0's outputs against exact attention over its uncompressed K / V
     # (the newest token of sequence b holds knew[0][b] / vnew[0][b], written by the step)
@@ -661,11 +782,15 @@ def main():
             "traffic": measured_traffic(mode),
             "algorithmic_bytes_per_launch": launch_bytes,
             "avg_launch_ms": dec_ms,
-            "timing": "HIP events around graph replays of the %d layers' %s calls" % (
-                w.layers, "fq_decode_step" if mode == "step" else "attention")
-                      if graph is not None else "HIP events around eager calls",
+            "launch_ms_p10": dec_stats["p10_ms"] if dec_stats else None,
+            "launch_ms_p90": dec_stats["p90_ms"] if dec_stats else None,
+            "launch_samples": dec_stats["samples"] if dec_stats else None,
+            "timing": "median over %d replays of a graph of the %d layers' %s calls, HIP events on the library's "
+                      "stream, per call" % (MIN_SAMPLES, w.layers, "fq_decode_step" if mode == "step" else "attention")
+                      if graph is not None else "HIP events around eager calls (median)",
             "avg_launch_ms_eager": dec_ms_eager,
         },
+        "step_4_splits": four,
         "step_parts": None if mode == "step" else {
             "prepare_ms": prep_ms,
             "prepare": ("fq_compress of the newest 32 x 8 K and V" if mode == "separate" else
@@ -677,33 +802,34 @@ def main():
             "mvec_per_s": comp_vec / (comp_med_ms * 1e-3) / 1e6,
             "vectors_per_launch": comp_vec,
             "avg_launch_ms": comp_med_ms,
+            "timing": "HIP events around each layer's fill (median of the layers after the first)",
             "achieved_gbs": comp_bytes / (comp_med_ms * 1e-3) / 1e9,
             "frac_hbm": comp_bytes / (comp_med_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
             "algorithmic_bytes_per_launch": comp_bytes,
             "mfma_util": measured_mfma_util(),
         },
-        "decompress": decomp,
-        "residual_window": win,
-        "prefill": pre,
         "accuracy": dict(accuracy, what="cosine of decode outputs vs exact fp32 softmax attention over the "
                          "uncompressed bf16 K/V, layer 0, sequences 0 / 7 / 15 / 31, all 32 query heads"),
     }
-    if not args.no_extra:
-        del caches, knew, vnew, qs, outs
+    if measure_parts:
+        result.update(decompress=decomp, residual_window=win, prefill=pre)
+    if not args.no_extra and not args.only:
+        del caches, knew, vnew, qs, outs, wss
         torch.cuda.empty_cache()
         log("other workloads: 70B-shape 32K decode and compress, 80-layer compress stream, batch-4 2-bit "
-            "decode, batch-1 8B decode...")
+            "decode, batch-1 8B decode, 3-bit and Prod variants...")
         extra = {}
-        extra["llama70b_b1_ctx32k_haar"] = decode_layer_measure(3, 4, fq.ROT_HAAR, 8, 20, stream)
-        extra["llama70b_b1_ctx32k_wht"] = decode_layer_measure(3, 4, fq.ROT_WHT, 8, 20, stream)
+        extra["llama70b_b1_ctx32k_haar"] = decode_layer_measure(3, 4, fq.ROT_HAAR, stream)
+        extra["llama70b_b1_ctx32k_wht"] = decode_layer_measure(3, 4, fq.ROT_WHT, stream)
         extra["stream_80layer_compress_4bit"] = stream_compress_measure(4, 80, stream)
         extra["stream_80layer_compress_2bit"] = stream_compress_measure(2, 80, stream)
-        extra["b4_ctx32k_decode_2bit"] = decode_layer_measure(4, 2, fq.ROT_HAAR, 4, 10, stream)
-        extra["llama8b_b1_ctx4k"] = decode_layer_measure(1, 4, fq.ROT_HAAR, 32, 64, stream)
-        extra["llama70b_b1_ctx32k_compress_haar"] = compress_layer_measure(3, fq.ROT_HAAR, 10, stream)
-        extra["llama70b_b1_ctx32k_compress_wht"] = compress_layer_measure(3, fq.ROT_WHT, 10, stream)
+        extra["b4_ctx32k_decode_2bit"] = decode_layer_measure(4, 2, fq.ROT_HAAR, stream)
+        extra["llama8b_b1_ctx4k"] = decode_layer_measure(1, 4, fq.ROT_HAAR, stream)
+        extra["llama70b_b1_ctx32k_compress_haar"] = compress_layer_measure(3, fq.ROT_HAAR, stream)
+        extra["llama70b_b1_ctx32k_compress_wht"] = compress_layer_measure(3, fq.ROT_WHT, stream)
+        extra.update(variants_measure(stream))
         result["other_workloads"] = extra
-    if not args.no_cpu:
+    if not args.no_cpu and not args.only:
         log("timing the CPU oracle (~%.0f s)..." % args.cpu_seconds)
         result["cpu_baseline"] = cpu_baseline(w, 77, args.cpu_seconds)
     print(json.dumps(result), flush=True)

@@ -1,5 +1,6 @@
 // C-ABI entry points: host-side argument checks, then the HIP launchers.
 #include <cstdint>
+#include <cstdlib>
 
 #include "fq.h"
 #include "fq_internal.h"
@@ -218,7 +219,7 @@ fq_status decode_checked(void* stream, const fq_quantizer* quant, const fq_cache
                          const int32_t* seq_lens, int max_seq_len, int num_splits, float scale,
                          void* workspace, size_t workspace_bytes, float* out,
                          const fq::AppendIn* app, int phase, const fq::WindowIn* win = nullptr,
-                         const int32_t* bt_row = nullptr) {
+                         const int32_t* bt_row = nullptr, bool tiled = false) {
   fq_status st = check_quantizer(quant);
   if (st != FQ_OK) return st;
   st = check_cache(cache, quant);
@@ -267,9 +268,11 @@ fq_status decode_checked(void* stream, const fq_quantizer* quant, const fq_cache
     if (static_cast<int64_t>(batch) * win->cap * cache->num_kv_heads * FQ_HEAD_DIM >= (int64_t{1} << 40))
       return FQ_ERR_UNSUPPORTED;
   }
-  int e = fq::launch_decode(stream, *quant, *cache, q, q_dtype, batch, num_q_heads, block_tables,
-                            max_blocks_per_seq, seq_lens, max_seq_len, s, scale, workspace, out,
-                            app, phase, win, bt_row);
+  int e = tiled ? fq::launch_prefill_tiled(stream, *quant, *cache, q, q_dtype, batch, num_q_heads, bt_row, seq_lens,
+                                           block_tables, max_blocks_per_seq, max_seq_len, scale, workspace, s, out)
+                : fq::launch_decode(stream, *quant, *cache, q, q_dtype, batch, num_q_heads, block_tables,
+                                    max_blocks_per_seq, seq_lens, max_seq_len, s, scale, workspace, out,
+                                    app, phase, win, bt_row);
   return e == 0 ? FQ_OK : FQ_ERR_HIP;
 }
 
@@ -319,9 +322,15 @@ fq_status fq_prefill_attention(void* stream, const fq_quantizer* quant, const fq
                                int max_seq_len, int num_splits, float scale, void* workspace,
                                size_t workspace_bytes, float* out) {
   if (num_queries > 0 && (!q_seq || !aligned(q_seq, 4))) return FQ_ERR_INVALID_ARG;
+  // query tiles sharing each page (4-bit, one codebook, groups dividing 16) unless a
+  // split count is asked for; otherwise every query token is a decode of its prefix
+  const bool tiled = (num_splits == 0 || num_splits == 1) && quant && cache && cache->num_kv_heads > 0 &&
+                     num_q_heads > 0 && num_q_heads % cache->num_kv_heads == 0 &&
+                     fq::prefill_tiled_supported(*quant, *cache, num_q_heads) &&
+                     std::getenv("FQ_PREFILL_UNTILED") == nullptr;
   return decode_checked(stream, quant, cache, q, q_dtype, num_queries, num_q_heads, block_tables,
                         max_blocks_per_seq, q_lens, max_seq_len, num_splits, scale, workspace, workspace_bytes,
-                        out, nullptr, fq::DECODE_ALL, nullptr, q_seq);
+                        out, nullptr, fq::DECODE_ALL, nullptr, q_seq, tiled);
 }
 
 fq_status fq_window_workspace_size(int batch, int num_kv_heads, size_t* bytes) {

@@ -92,6 +92,15 @@ int launch_window_append(void* stream, const fq_quantizer& q, const fq_cache& c,
                          const void* v_new, int kv_dtype, int batch, const int64_t* positions,
                          const int64_t* evict_slots, void* win_k, void* win_v, int cap, void* scratch);
 
+// Tiled prefill attention (fq_prefill_attention with num_splits 0 or 1): 4-bit codes of
+// one shared codebook and groups dividing 16. num_splits_ws: the split count the
+// workspace was sized for (its carve-up).
+bool prefill_tiled_supported(const fq_quantizer& q, const fq_cache& c, int num_q_heads);
+int launch_prefill_tiled(void* stream, const fq_quantizer& q, const fq_cache& c, const void* qv, int q_dtype,
+                         int num_queries, int num_q_heads, const int32_t* q_seq, const int32_t* q_lens,
+                         const int32_t* block_tables, int max_blocks_per_seq, int max_seq_len, float scale,
+                         void* workspace, int num_splits_ws, float* out);
+
 int launch_decompress(void* stream, const fq_quantizer& q, const fq_cache& c, const int64_t* slot_mapping,
                       int64_t num_tokens, int out_dtype, void* k_out, void* v_out, int64_t token_stride,
                       int64_t head_stride);
