@@ -212,10 +212,10 @@ struct TPage {
 // Scores are computed transposed, C[token][row] = K^[token][.] . q~[row][.], so that
 // lane (row n, g) ends up holding row n's scores of tokens 4 g .. 4 g + 3: exactly the
 // A operand of the value product C[row][dim] += P[row][token] V^[token][dim] (no data
-// moves between the two). K positions 8 g + e of a k-step: e < 4 the hi parts of 4
-// dims (or tokens), e >= 4 their lo parts; the A operand of the keys is [hi | lo] from
-// the table, the query operands are [hi | hi] and [lo | lo] (four products, the lo*lo
-// one negligible but free).
+// moves between the two). K positions 8 g + e of a k-step follow the table entries
+// as loaded (no register moves): (hi, hi, lo, lo) of dims (or tokens) 0, 1, then of
+// 2, 3; the query (probability) operands are the matching (hi, hi, hi, hi) and (lo,
+// lo, lo, lo) arrangements (four products, the lo * lo one negligible but free).
 template <int G>
 __global__ void __launch_bounds__(PT_WAVES * 64, 2) prefill_tile_kernel(PrefillArgs a) {
   constexpr int Q = 16 / G;  // query tokens per wave
@@ -312,8 +312,8 @@ __global__ void __launch_bounds__(PT_WAVES * 64, 2) prefill_tile_kernel(PrefillA
       hw[k] = h2bits(h0, h1);
       lw[k] = h2bits(l0, l1);
     }
-    bqh[s] = as_h8(hw[0], hw[1], hw[0], hw[1]);
-    bql[s] = as_h8(lw[0], lw[1], lw[0], lw[1]);
+    bqh[s] = as_h8(hw[0], hw[0], hw[1], hw[1]);
+    bql[s] = as_h8(lw[0], lw[0], lw[1], lw[1]);
   }
 #pragma unroll
   for (int s = 0; s < 4; ++s) {  // dims 32 g + 8 s .. + 7
@@ -365,7 +365,7 @@ __global__ void __launch_bounds__(PT_WAVES * 64, 2) prefill_tile_kernel(PrefillA
       const uint32_t w = d.kc[s >> 1];
       const uint2 e0 = lds_u2(s_code, tab_off(w, copy8, 2 * (s & 1)));
       const uint2 e1 = lds_u2(s_code, tab_off(w, copy8, 2 * (s & 1) + 1));
-      const h8 ak = as_h8(e0.x, e1.x, e0.y, e1.y);
+      const h8 ak = as_h8(e0.x, e0.y, e1.x, e1.y);
       accM = mfma32(ak, bqh[s], accM);
       accM = mfma32(ak, bql[s], accM);
     }
@@ -434,8 +434,8 @@ __global__ void __launch_bounds__(PT_WAVES * 64, 2) prefill_tile_kernel(PrefillA
       ph[i / 2] = h2bits(hx[0], hx[1]);
       pl[i / 2] = h2bits(lx[0], lx[1]);
     }
-    const h8 a1 = as_h8(ph[0], ph[1], ph[0], ph[1]);
-    const h8 a2 = as_h8(pl[0], pl[1], pl[0], pl[1]);
+    const h8 a1 = as_h8(ph[0], ph[0], ph[1], ph[1]);
+    const h8 a2 = as_h8(pl[0], pl[0], pl[1], pl[1]);
     // ---- values: dims 8 n + t; code bytes pair tokens (4 g, 4 g + 1) and (4 g + 2, 4 g + 3)
     const uint32_t x01 = (d.vc[0] & 0x0F0F0F0Fu) | ((d.vc[1] << 4) & 0xF0F0F0F0u);
     const uint32_t z01 = ((d.vc[0] >> 4) & 0x0F0F0F0Fu) | (d.vc[1] & 0xF0F0F0F0u);
@@ -446,7 +446,7 @@ __global__ void __launch_bounds__(PT_WAVES * 64, 2) prefill_tile_kernel(PrefillA
       const uint32_t w01 = (t & 1) ? z01 : x01, w23 = (t & 1) ? z23 : x23;
       const uint2 e01 = lds_u2(s_code, tab_off(w01, copy8, t >> 1));
       const uint2 e23 = lds_u2(s_code, tab_off(w23, copy8, t >> 1));
-      const h8 bv = as_h8(e01.x, e23.x, e01.y, e23.y);
+      const h8 bv = as_h8(e01.x, e01.y, e23.x, e23.y);
       acc_o[t] = mfma32(a1, bv, acc_o[t]);
       acc_o[t] = mfma32(a2, bv, acc_o[t]);
     }
