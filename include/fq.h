@@ -372,9 +372,12 @@ fq_status fq_step_attend(void* stream, const fq_quantizer* quant, const fq_cache
  * one at position positions[b] - win_cap, if any) is compressed into the cache at
  * evict_slots[b] (< 0: it is dropped, e.g. while the ring is not full yet), then
  * k_new / v_new [batch][Hkv][128] (kv_dtype FQ_F32 or FQ_BF16, contiguous, 8-byte
- * aligned; rounded to bf16) are written into that ring slot. positions,
+ * aligned; rounded to bf16) are written into that ring slot. One launch (a
+ * work-group per sequence and KV head: the compression of the replaced row is the
+ * single-vector form fq_decode_step uses for its newest token). positions,
  * evict_slots: device int64 [batch]. workspace: device, 256-byte aligned, at least
- * fq_window_workspace_size bytes. 1 <= win_cap <= 4096.
+ * fq_window_workspace_size bytes; that size is 0 in this version, and with 0 the
+ * workspace may be NULL. 1 <= win_cap <= 4096.
  * Errors: FQ_ERR_INVALID_ARG, FQ_ERR_WORKSPACE, FQ_ERR_HIP.
  */
 fq_status fq_window_workspace_size(int batch, int num_kv_heads, size_t* bytes);
@@ -388,10 +391,11 @@ fq_status fq_window_append(void* stream, const fq_quantizer* quant, const fq_cac
  * [0, seq_lens[b]) together with the window tokens in ring slots t < win_lens[b]
  * (device int32 [batch], clamped to [0, win_cap]): one softmax over both, the window's
  * scores scale * <q, k_t> and values exact (fp32 arithmetic on the bf16 rows). When
- * the call resolves to one split and G <= 8: a window launch (the window's maximum,
- * sum and weighted values per query head, into the workspace) and then the
- * single-launch decode, whose epilogue folds them into the softmax; otherwise the
- * split path (partials, then the merge, which adds the window). The workspace is
+ * the call resolves to one split and G <= 8: one launch, whose waves compute the
+ * window's maximum, sum and weighted values (each query head's window tokens
+ * shared out over the work-group's waves) after their pages and whose epilogue
+ * folds them into the softmax; otherwise the split path (partials, then the merge,
+ * which adds the window). The workspace is
  * fq_decode_workspace_size's for these sizes. A caller
  * with n tokens per sequence passes seq_lens = max(0, n - win_cap) and win_lens =
  * min(n, win_cap). Errors: as fq_decode_attention.

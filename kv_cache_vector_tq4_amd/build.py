@@ -15,7 +15,7 @@ LIB = os.path.join(PKG, "libfq.so")
 OBJ_DIR = os.path.join(PKG, "_build")
 ARCH = os.environ.get("FQ_OFFLOAD_ARCH", "gfx950")
 
-SOURCES = ["fq_api.cpp", "fq_codebook.cpp", "fq_compress.hip", "fq_decode.hip", "fq_decompress.hip", "fq_window.hip", "fq_noalloc.hip", "fq_prefill.hip"]
+SOURCES = ["fq_api.cpp", "fq_codebook.cpp", "fq_compress.hip", "fq_decode.hip", "fq_decompress.hip", "fq_noalloc.hip", "fq_prefill.hip"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-I" + INCLUDE, "-I" + CSRC]
 # Packed fp32 instructions are left to no one: hipcc must not form them.
 DEVICE = ["--offload-arch=" + ARCH, "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]

@@ -354,9 +354,8 @@ fq_status fq_window_append(void* stream, const fq_quantizer* quant, const fq_cac
   if (!aligned(k_new, 8) || !aligned(v_new, 8) || !aligned(positions, 8) || !aligned(evict_slots, 8) ||
       !aligned(win_k, 16) || !aligned(win_v, 16))
     return FQ_ERR_INVALID_ARG;
-  if (!workspace || !aligned(workspace, 256) ||
-      workspace_bytes < fq::window_scratch_bytes(batch, cache->num_kv_heads))
-    return FQ_ERR_WORKSPACE;
+  const size_t need = fq::window_scratch_bytes(batch, cache->num_kv_heads);
+  if (need > 0 && (!workspace || !aligned(workspace, 256) || workspace_bytes < need)) return FQ_ERR_WORKSPACE;
   int e = fq::launch_window_append(stream, *quant, *cache, k_new, v_new, kv_dtype, batch, positions, evict_slots,
                                    win_k, win_v, win_cap, workspace);
   return e == 0 ? FQ_OK : FQ_ERR_HIP;

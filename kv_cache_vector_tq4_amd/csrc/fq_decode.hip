@@ -18,10 +18,10 @@
 //    splits in split order, then o = Pi^T o_rot.
 //  * split_mfma4_kernel / split_attention_kernel: groups of 16 query heads (4-bit
 //    matrix-core / vector ALU), and the vector-ALU cross-check.
-//  * window_kernel: the residual full-precision window's part of every query head
-//    ("TurboQuant" blog, "Couche 5") for the single-launch path, whose epilogue
-//    folds it into the softmax; on the split path merge_unrotate_kernel computes
-//    it per head itself.
+//  * the residual full-precision window ("TurboQuant" blog, "Couche 5"): in the
+//    single-launch kernel the first G waves compute their query head's part of it
+//    after their pages, and the epilogue folds it into the softmax; on the split
+//    path merge_unrotate_kernel computes it per head itself.
 // A batch entry's block-table row can be remapped (bt_row): fq_prefill_attention
 // runs many query tokens of one sequence as entries sharing its pages.
 #include <hip/hip_runtime.h>
@@ -90,6 +90,9 @@ struct DecodeArgs {
   // block-table row of batch entry b (null: row b); many queries of one sequence
   // (prefill) are batch entries sharing their sequence's row
   const int32_t* bt_row;
+  // the window's append: sequence b's new position (< 0: none); the vector it
+  // compresses is ring row b * win_cap + pos % win_cap of knew / vnew
+  const int64_t* ring_pos;
 };
 
 __device__ __forceinline__ int64_t table_row(const DecodeArgs& a, int b) {
@@ -275,19 +278,43 @@ __device__ __forceinline__ void part_dot(const float (&col)[D / KP], const float
   }
 }
 
+// One stage of a reduce-scatter over the 16 lanes of a row: C values per lane in,
+// C / 2 out; after the stages M = 8, 4, 2, 1, lane r holds the row's sum of value r.
+template <int M, int C>
+__device__ __forceinline__ void row_reduce_scatter_stage(float (&v)[16], int r) {
+  // lanes r and r ^ M: the one with bit M set keeps the upper half of its C values,
+  // the other the lower half, and each adds the half the partner sent
+  const bool up = (r & M) != 0;
+#pragma unroll
+  for (int k = 0; k < C / 2; ++k) {
+    const float keep = up ? v[C / 2 + k] : v[k];
+    const float send = up ? v[k] : v[C / 2 + k];
+    float recv;
+    if constexpr (M == 8) recv = dpp_f<DPP_ROR8>(send);
+    else if constexpr (M == 4) recv = __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(send), 0x101F));
+    else if constexpr (M == 2) recv = dpp_f<DPP_XOR2>(send);
+    else recv = dpp_f<DPP_XOR1>(send);
+    v[k] = keep + recv;
+  }
+}
+
 // The residual window's part of query head hidx (global index) in one wave: the
 // scores scale <q, k_t> of its window tokens (exact, fp32), their max m, the sum l
 // of exp(s_t - m) and o = sum_t exp(s_t - m) v_t (lane: coordinates 2 lane,
-// 2 lane + 1). Rounds of 64 tokens: lane t scores token t0 + t against its whole K
-// row (the query's coordinates broadcast from the lane holding them), the round's
-// max and sum come from fixed-order lane reductions, then the lanes turn to
-// coordinates and add up the round's weighted V rows in token order. Each round
-// requests all its K and V rows before using any.
+// 2 lane + 1). Rounds of 64 tokens: lane (g, r) = (lane / 16, lane % 16) takes
+// coordinates 8r .. 8r + 7 of tokens 4i + g, i < 16 (each load instruction reads
+// four whole K rows), and a reduce-scatter over the 16 lanes of a row leaves the
+// score of token 4r + g in lane (g, r); the round's max and sum come from
+// fixed-order lane reductions, then the lanes turn to coordinates and add up the
+// round's weighted V rows in token order. Each round requests all its K and V rows
+// before using any.
 // m = -inf, l = 0 without tokens.
+// Rounds r0, r0 + rstride, ... of the head's window tokens only (by default all).
 __device__ __forceinline__ void window_partial(const DecodeArgs& a, int64_t hidx, int lane, float& m, float& l,
-                                               float& o0, float& o1) {
+                                               float& o0, float& o1, int r0 = 0, int rstride = 1) {
   const int b = static_cast<int>(hidx / a.hq);
   const int kvh = static_cast<int>(hidx - static_cast<int64_t>(b) * a.hq) / a.group;
+  const int g = lane >> 4, r = lane & 15;
   float q0, q1;
   if (a.q_bf16) {
     const uint32_t w = reinterpret_cast<const uint32_t*>(a.q)[hidx * (D / 2) + lane];
@@ -298,35 +325,44 @@ __device__ __forceinline__ void window_partial(const DecodeArgs& a, int64_t hidx
     q0 = x.x;
     q1 = x.y;
   }
+  // the query's coordinates 8r .. 8r + 7 (held by lanes 4r .. 4r + 3)
+  float qd[8];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    qd[2 * e] = __int_as_float(__builtin_amdgcn_ds_bpermute((4 * r + e) * 4, __float_as_int(q0)));
+    qd[2 * e + 1] = __int_as_float(__builtin_amdgcn_ds_bpermute((4 * r + e) * 4, __float_as_int(q1)));
+  }
   const int n = min(max(a.win_lens[b], 0), a.win_cap);
   const int64_t ts = static_cast<int64_t>(a.hkv) * (D / 2);  // token stride in bf16 pairs
+  const int64_t ts4 = static_cast<int64_t>(a.hkv) * (D / 8);  // and in 16-byte units
   const int64_t base = (static_cast<int64_t>(b) * a.win_cap * a.hkv + kvh) * (D / 2);
-  const uint32_t* kb = reinterpret_cast<const uint32_t*>(a.win_k) + base;
+  const uint4* kb = reinterpret_cast<const uint4*>(a.win_k) + base / 4;
   const uint32_t* vb = reinterpret_cast<const uint32_t*>(a.win_v) + base;
-  for (int t0 = 0; t0 < n; t0 += 64) {
-    const int t = t0 + lane;
-    const uint4* kr = reinterpret_cast<const uint4*>(kb + static_cast<int64_t>(min(t, n - 1)) * ts);
+  for (int t0 = 64 * r0; t0 < n; t0 += 64 * rstride) {
     uint4 kw[16];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) kw[i] = kr[i];
+    for (int i = 0; i < 16; ++i) kw[i] = kb[static_cast<int64_t>(min(t0 + 4 * i + g, n - 1)) * ts4 + r];
     // the round's V rows too, all requested before any is used (rows past n reread
     // row n - 1 and get weight 0)
     uint32_t vw[64];
 #pragma unroll
     for (int u = 0; u < 64; ++u) vw[u] = vb[static_cast<int64_t>(min(t0 + u, n - 1)) * ts + lane];
-    float s = 0.f;
+    float ps[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const uint32_t w4[4] = {kw[i].x, kw[i].y, kw[i].z, kw[i].w};
+      float s = 0.f;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {  // bf16 pair dd = coordinates 2 dd, 2 dd + 1
-        const int dd = 4 * i + e;
-        const float qa = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(q0), dd));
-        const float qb = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(q1), dd));
-        s = fmaf(qa, __uint_as_float(w4[e] << 16), fmaf(qb, __uint_as_float(w4[e] & 0xffff0000u), s));
-      }
+      for (int e = 0; e < 4; ++e)
+        s = fmaf(qd[2 * e], __uint_as_float(w4[e] << 16), fmaf(qd[2 * e + 1], __uint_as_float(w4[e] & 0xffff0000u), s));
+      ps[i] = s;
     }
-    s = t < n ? s * a.scale : -INFINITY;
+    row_reduce_scatter_stage<8, 16>(ps, r);
+    row_reduce_scatter_stage<4, 8>(ps, r);
+    row_reduce_scatter_stage<2, 4>(ps, r);
+    row_reduce_scatter_stage<1, 2>(ps, r);
+    const int u_own = 4 * r + g;  // this lane's token of the round
+    const float s = t0 + u_own < n ? ps[0] * a.scale : -INFINITY;
     const float mn = fmaxf(m, wave_max_dpp(s));  // lane 0's token is live
     const float c = __expf(m - mn);              // 0 before the first round
     const float p = __expf(s - mn);              // 0 for lanes past n
@@ -335,7 +371,7 @@ __device__ __forceinline__ void window_partial(const DecodeArgs& a, int64_t hidx
     o1 *= c;
 #pragma unroll
     for (int u = 0; u < 64; ++u) {
-      const float pu = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(p), u));
+      const float pu = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(p), 16 * (u & 3) + (u >> 2)));
       o0 = fmaf(pu, __uint_as_float(vw[u] << 16), o0);
       o1 = fmaf(pu, __uint_as_float(vw[u] & 0xffff0000u), o1);
     }
@@ -460,7 +496,8 @@ struct PrepIn {
   float xv;  // newest K / V coordinate (APP)
 };
 
-template <int DT, int GM, bool APP>
+// RING: no queries; the appended vectors are the window ring's rows (ring_pos).
+template <int DT, int GM, bool APP, bool RING = false>
 __device__ __forceinline__ void prep_issue(const DecodeArgs& a, int kvh, int b, int hb, int hn, int tid,
                                            PrepIn<GM>& in) {
   const int j = tid & (D - 1);
@@ -469,6 +506,8 @@ __device__ __forceinline__ void prep_issue(const DecodeArgs& a, int kvh, int b, 
   // in the order of use: loads complete in issue order
 #pragma unroll
   for (int i = 0; i < GM / 4; ++i) {
+    in.qv[i] = 0.f;
+    if constexpr (RING) continue;
     const int h = kq + 4 * i;
     const int64_t off = row0 + (h < hn ? h : 0) * D + j;
     if constexpr (DT == FQ_BF16)
@@ -479,7 +518,12 @@ __device__ __forceinline__ void prep_issue(const DecodeArgs& a, int kvh, int b, 
   in.xv = 0.f;
   if constexpr (APP) {
     if (kq < 2) {
-      const int64_t off = static_cast<int64_t>(b) * a.kv_tstride + static_cast<int64_t>(kvh) * a.kv_hstride + j;
+      int64_t tok = b;
+      if constexpr (RING) {
+        const int64_t pos = a.ring_pos[b];
+        tok = static_cast<int64_t>(b) * a.win_cap + (pos >= 0 ? pos % a.win_cap : 0);
+      }
+      const int64_t off = tok * a.kv_tstride + static_cast<int64_t>(kvh) * a.kv_hstride + j;
       const void* src = kq == 0 ? a.knew : a.vnew;
       in.xv = a.kv_bf16 ? __uint_as_float(static_cast<uint32_t>(static_cast<const uint16_t*>(src)[off]) << 16)
                         : static_cast<const float*>(src)[off];
@@ -505,7 +549,7 @@ __device__ __forceinline__ void prep_issue(const DecodeArgs& a, int kvh, int b, 
 // the Pi product give y = (Pi x) / n (0 when n = 0), idx_j = #{i : boundary_i <
 // y_j}; the key residual r = y - level[idx] is row hn of the S product, p = S r,
 // bit j = [p_j >= 0], gamma = n ||r||. Nothing is stored when the slot is negative.
-template <int SLOTS, int GM, bool APP>
+template <int SLOTS, int GM, bool APP, bool RING = false>
 __device__ __forceinline__ void prepare_group(const DecodeArgs& a, int kvh, int b, int hb, int hn, int tid,
                                               float* lds, uint4* ops, bool write_vec, const PrepIn<GM>& in) {
   static_assert(!APP || GM >= 3, "room for the appended rows");
@@ -534,6 +578,9 @@ __device__ __forceinline__ void prepare_group(const DecodeArgs& a, int kvh, int 
   int64_t slot = -1, rec = 0;
   if constexpr (APP) {
     slot = a.slots[b];
+    if constexpr (RING) {
+      if (a.ring_pos[b] < 0) slot = -1;  // no new token: nothing leaves the ring
+    }
     rec = ((slot >> 4) * a.hkv + kvh) * FQ_BLOCK + (slot & 15);
   }
 #pragma unroll
@@ -686,6 +733,37 @@ __global__ void __launch_bounds__(PQ_THREADS) prepare_queries_kernel(DecodeArgs 
   } else {
     prep_issue<DT, GM, false>(a, kvh, b, hb, hn, threadIdx.x, in);
     prepare_group<SLOTS, GM, false>(a, kvh, b, hb, hn, threadIdx.x, s_p, ops, SLOTS == 0, in);
+  }
+}
+
+// fq_window_append in one launch, one work-group per (KV head, sequence): the ring
+// row that the sequence's new token replaces is compressed into the cache at its
+// eviction slot by prepare_group's append rows (no query heads), then the new K and
+// V rows, rounded to bf16, take that ring slot. Each thread stores the coordinate
+// it loaded for the compression, after that load's value went to LDS.
+template <int KVDT>
+__global__ void __launch_bounds__(PQ_THREADS) window_append_kernel(DecodeArgs a, const void* k_new, const void* v_new,
+                                                                   uint16_t* ring_k, uint16_t* ring_v) {
+  constexpr int GM = 4;
+  __shared__ __align__(16) float s_p[prep_lds_floats<GM>()];
+  const int kvh = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  const int j = tid & (D - 1), kq = tid >> 7;
+  const int64_t pos = a.ring_pos[b];
+  float xn = 0.f;
+  if (kq < 2) {
+    const int64_t src = (static_cast<int64_t>(b) * a.hkv + kvh) * D + j;
+    const void* p = kq == 0 ? k_new : v_new;
+    if constexpr (KVDT == FQ_BF16)
+      xn = __uint_as_float(static_cast<uint32_t>(static_cast<const uint16_t*>(p)[src]) << 16);
+    else
+      xn = static_cast<const float*>(p)[src];
+  }
+  PrepIn<GM> in;
+  prep_issue<FQ_BF16, GM, true, true>(a, kvh, b, 0, 0, tid, in);
+  prepare_group<0, GM, true, true>(a, kvh, b, 0, 0, tid, s_p, nullptr, false, in);
+  if (pos >= 0 && kq < 2) {
+    const int64_t dst = ((static_cast<int64_t>(b) * a.win_cap + pos % a.win_cap) * a.hkv + kvh) * D + j;
+    (kq == 0 ? ring_k : ring_v)[dst] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(xn));
   }
 }
 
@@ -1790,6 +1868,17 @@ __global__ void __launch_bounds__(WAVES * 64, OCC) packed_decode_kernel(DecodeAr
     }
   }
 
+  // ---- the residual window (the only split): wave w computes part w / G of query
+  // head w % G's window (rounds of 64 tokens w / G, w / G + C, ..., C = WAVES / G parts
+  // per head; exact scores and values, natural-log max, original frame) once its
+  // pages are done, so the window fills the waves' end spread instead of a launch
+  const int wparts = WAVES / G;  // >= 1 (G <= 8 <= WAVES)
+  float wm = -INFINITY, wl = 0.f, wo0 = 0.f, wo1 = 0.f;
+  if constexpr (ONLY) {
+    if (a.win_k && wave < wparts * G)
+      window_partial(a, static_cast<int64_t>(b) * a.hq + kvh * G + wave % G, lane, wm, wl, wo0, wo1, wave / G,
+                     wparts);
+  }
   // ---- per-wave totals, then merge the waves in LDS
 #pragma unroll
   for (int k = 0; k < HL; ++k) l_run[k] = row_sum(l_run[k]);
@@ -1812,14 +1901,30 @@ __global__ void __launch_bounds__(WAVES * 64, OCC) packed_decode_kernel(DecodeAr
     for (int k = 0; k < HL; ++k)
       s_o[(wave * HP + HL * g + k) * D + dim] = (acc_o[t][2 * k] + acc_o[t][2 * k + 1]) * unscale;
   }
+  // the window's parts: (max, sum) and values per wave (part w / G of head w % G)
+  float* const s_wml = reinterpret_cast<float*>(s_lds) + WAVES * HP * (D + 2) + 5 * PK_PREP_GM * D + PK_PREP_GM;
+  float* const s_wo = s_wml + 2 * WAVES;  // [WAVES][D]
+  static_assert(!ONLY || (WAVES * HP * (D + 2) + 5 * PK_PREP_GM * D + PK_PREP_GM + WAVES * (D + 2)) * 4 <=
+                             static_cast<int>(sizeof(s_lds)), "epilogue fits the LDS");
+  if constexpr (ONLY) {
+    if (a.win_k && wave < wparts * G) {
+      if (lane == 0) {
+        s_wml[2 * wave] = wm;
+        s_wml[2 * wave + 1] = wl;
+      }
+      s_wo[wave * D + 2 * lane] = wo0;
+      s_wo[wave * D + 2 * lane + 1] = wo1;
+    }
+  }
   __syncthreads();
   if constexpr (ONLY) {
     // the only split: o_rot = O / L per head, then out = Pi^T o_rot
     float* const s_or = s_ml + WAVES * HP * 2;  // [G][D]
     float* const s_pp = s_or + PK_PREP_GM * D;  // [4][PK_PREP_GM][D]
     float* const s_fw = s_pp + 4 * PK_PREP_GM * D;  // [G] weight of the residual window's values
-    static_assert((WAVES * HP * (D + 2) + 5 * PK_PREP_GM * D + PK_PREP_GM) * 4 <= PK_LDS_BYTES,
-                  "epilogue fits the LDS");
+    float* const s_win_v = s_wo + WAVES * D;        // [G][D] the window's merged values
+    static_assert((WAVES * HP * (D + 2) + 5 * PK_PREP_GM * D + PK_PREP_GM + WAVES * (D + 2) + PK_PREP_GM * D) * 4 <=
+                      static_cast<int>(sizeof(s_lds)), "epilogue fits the LDS");
     const int64_t head0 = static_cast<int64_t>(b) * a.hq + kvh * G;
     constexpr float LOG2E = 1.4426950408889634f;
     for (int idx = tid; idx < G * D; idx += WAVES * 64) {
@@ -1828,15 +1933,23 @@ __global__ void __launch_bounds__(WAVES * 64, OCC) packed_decode_kernel(DecodeAr
 #pragma unroll
       for (int w = 0; w < WAVES; ++w)
         if (s_ml[(w * HP + hh) * 2 + 1] > 0.f) M = fmaxf(M, s_ml[(w * HP + hh) * 2]);
-      // a residual window's part (window_kernel, natural-log max) joins the softmax
+      // a residual window's parts (natural-log maxima) join the softmax: merged here
+      // into one (max, sum) in log2 units and the head's values in s_wo row hh
       float mw = -INFINITY, lwin = 0.f;
       if (a.win_k) {
-        const float2 x = reinterpret_cast<const float2*>(a.part_ml)[head0 + hh];
-        lwin = x.y;
-        if (lwin > 0.f) {
-          mw = x.x * LOG2E;
-          M = fmaxf(M, mw);
+        for (int c = 0; c < wparts; ++c)
+          if (s_wml[2 * (c * G + hh) + 1] > 0.f) mw = fmaxf(mw, s_wml[2 * (c * G + hh)] * LOG2E);
+        float ow = 0.f;
+        for (int c = 0; c < wparts; ++c) {
+          const float lc = s_wml[2 * (c * G + hh) + 1];
+          if (lc > 0.f) {
+            const float f = exp2f(s_wml[2 * (c * G + hh)] * LOG2E - mw);
+            lwin = fmaf(lc, f, lwin);
+            ow = fmaf(s_wo[(c * G + hh) * D + j], f, ow);
+          }
         }
+        if (lwin > 0.f) M = fmaxf(M, mw);
+        s_win_v[hh * D + j] = ow;  // own (hh, j) entry only: no other thread reads it before the barrier
       }
       float o = 0.f, L = 0.f;
 #pragma unroll
@@ -1860,7 +1973,7 @@ __global__ void __launch_bounds__(WAVES * 64, OCC) packed_decode_kernel(DecodeAr
       for (int h = kq; h < G; h += 4) {
         float v = (s_pp[(0 * PK_PREP_GM + h) * D + jj] + s_pp[(1 * PK_PREP_GM + h) * D + jj]) +
                   (s_pp[(2 * PK_PREP_GM + h) * D + jj] + s_pp[(3 * PK_PREP_GM + h) * D + jj]);
-        if (a.win_k) v = fmaf(s_fw[h], a.part_o[(head0 + h) * D + jj], v);
+        if (a.win_k) v = fmaf(s_fw[h], s_win_v[h * D + jj], v);
         a.out[(head0 + h) * D + jj] = v;
       }
     }
@@ -1890,19 +2003,6 @@ __global__ void __launch_bounds__(WAVES * 64, OCC) packed_decode_kernel(DecodeAr
       a.part_ml[base * 2 + 1] = L;
     }
   }
-}
-
-// One one-wave work-group per (KV head, sequence, query head of the group): the
-// residual window's part of the head (window_partial) into the workspace's
-// one-split partials, (natural-log max, sum) and the
-// unnormalized values in the original frame, for the single-launch kernel's epilogue.
-__global__ void __launch_bounds__(64) window_kernel(DecodeArgs a) {
-  const int kvh = blockIdx.x, b = blockIdx.y, hh = blockIdx.z, lane = threadIdx.x;
-  const int64_t hidx = static_cast<int64_t>(b) * a.hq + kvh * a.group + hh;
-  float m = -INFINITY, l = 0.f, o0 = 0.f, o1 = 0.f;
-  window_partial(a, hidx, lane, m, l, o0, o1);
-  reinterpret_cast<float2*>(a.part_o)[hidx * (D / 2) + lane] = make_float2(o0, o1);
-  if (lane == 0) reinterpret_cast<float2*>(a.part_ml)[hidx] = make_float2(m, l);
 }
 
 // ---------------------------------------------------------------- kernel 3
@@ -1996,8 +2096,6 @@ int launch_decode(void* stream, const fq_quantizer& q, const fq_cache& c, const 
   dim3 grid(num_splits, c.num_kv_heads, batch);
   const bool only = slots > 0 && num_splits == 1 && std::getenv("FQ_DECODE_UNFUSED") == nullptr;
   if (only && phase == DECODE_ALL) {
-    if (win)  // the window's parts first, into the (otherwise unused) one-split partials
-      hipLaunchKernelGGL(window_kernel, dim3(c.num_kv_heads, batch, a.group), dim3(64), 0, st, a);
     // one work-group per (KV head, sequence) does everything in one launch
     // (appending the newest token first, when asked)
 #define FQ_FUSED(BITS, SL, DT)                                                                                   \
@@ -2071,6 +2169,51 @@ int launch_decode(void* stream, const fq_quantizer& q, const fq_cache& c, const 
 #undef FQ_VALU
   }
   hipLaunchKernelGGL(merge_unrotate_kernel, pgrid, dim3(PQ_THREADS), 0, st, a);
+  return static_cast<int>(hipGetLastError());
+}
+
+size_t window_scratch_bytes(int, int) { return 0; }
+
+int launch_window_append(void* stream, const fq_quantizer& q, const fq_cache& c, const void* k_new,
+                         const void* v_new, int kv_dtype, int batch, const int64_t* positions,
+                         const int64_t* evict_slots, void* win_k, void* win_v, int cap, void*) {
+  DecodeArgs a{};
+  a.pit = q.rotation_t;
+  a.sit = q.qjl_matrix_t;
+  a.levels = q.levels;
+  a.klevels = key_levels_of(q);
+  a.kbnd = key_boundaries_of(q);
+  a.kbits = key_bits_of(q);
+  a.bits = q.bits;
+  a.bnd = q.boundaries;
+  a.k_codes = c.k_codes;
+  a.k_norm = c.k_norm;
+  a.k_qjl = c.k_qjl;
+  a.k_gamma = c.k_gamma;
+  a.v_codes = c.v_codes;
+  a.v_norm = c.v_norm;
+  a.batch = batch;
+  a.hkv = c.num_kv_heads;
+  a.hq = c.num_kv_heads;
+  a.group = 1;
+  a.qjl_on = c.qjl_dim > 0 ? 1 : 0;
+  // the vectors compressed are the ring's rows: [batch][cap][Hkv][d] bf16
+  a.knew = win_k;
+  a.vnew = win_v;
+  a.kv_bf16 = 1;
+  a.kv_tstride = static_cast<int64_t>(c.num_kv_heads) * D;
+  a.kv_hstride = D;
+  a.win_cap = cap;
+  a.slots = evict_slots;
+  a.ring_pos = positions;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const dim3 grid(static_cast<unsigned>(c.num_kv_heads), static_cast<unsigned>(batch));
+  uint16_t* rk = static_cast<uint16_t*>(win_k);
+  uint16_t* rv = static_cast<uint16_t*>(win_v);
+  if (kv_dtype == FQ_BF16)
+    hipLaunchKernelGGL(window_append_kernel<FQ_BF16>, grid, dim3(PQ_THREADS), 0, st, a, k_new, v_new, rk, rv);
+  else
+    hipLaunchKernelGGL(window_append_kernel<FQ_F32>, grid, dim3(PQ_THREADS), 0, st, a, k_new, v_new, rk, rv);
   return static_cast<int>(hipGetLastError());
 }
 

@@ -84,9 +84,9 @@ int launch_decode(void* stream, const fq_quantizer& q, const fq_cache& c, const 
                   const AppendIn* app, int phase, const WindowIn* win = nullptr,
                   const int32_t* bt_row = nullptr);
 
-// The window's append: each sequence's new K / V token goes to ring slot
-// positions[b] % cap; the token it replaces is first compressed into the cache at
-// evict_slots[b] (< 0: not stored). scratch: 2 * batch * Hkv * d bf16.
+// The window's append (one launch): each sequence's new K / V token goes to ring
+// slot positions[b] % cap; the token it replaces is first compressed into the cache
+// at evict_slots[b] (< 0: not stored). It needs no scratch (0 bytes).
 size_t window_scratch_bytes(int batch, int num_kv_heads);
 int launch_window_append(void* stream, const fq_quantizer& q, const fq_cache& c, const void* k_new,
                          const void* v_new, int kv_dtype, int batch, const int64_t* positions,

@@ -6,16 +6,20 @@ fq_window_append) against oracle/window.py (through the C ABI).
   kernels and the merge (1, 3 and automatic splits; groups 4, 8 and 16), with empty
   windows, windows only, and empty sequences.
 * Append: a run of decode steps. The ring after each append holds exactly the bf16
-  of the tokens of the last W positions; the records the append path compresses are
-  bit-identical to fq_compress of the same bf16 tokens into a mirror cache; the final
-  decode of the GPU-written cache and ring matches the oracle.
+  of the tokens of the last W positions; the records the append compresses are
+  bit-identical to fq_decode_step's append of the same bf16 tokens into a mirror
+  cache (the same single-vector arithmetic, itself checked against the oracle in
+  the step tests), and match the oracle's encoding of those tokens directly (codes
+  and QJL bits up to near-ties, norms and gamma to rounding); nothing else in the
+  cache changes; the final decode of the GPU-written cache and ring matches the
+  oracle.
 """
 import numpy as np
 import pytest
 import torch
 
 from kv_cache_vector_tq4_amd import fq
-from oracle import window
+from oracle import pipeline, quantize, window
 from tests import parity
 
 pytestmark = pytest.mark.gpu
@@ -75,6 +79,34 @@ def test_window_only_sequences(gpu_lib):
     assert float(np.max(np.abs(out.cpu().numpy() - ref))) <= 1e-5
 
 
+def _check_evicted(host, evicted, bk, bv, oq):
+    """The records of the evicted tokens against the oracle's encoding of their bf16
+    rows: codes differ only where the oracle's y is within rounding of a boundary,
+    QJL bits only where its projection is within rounding of 0 or a code changed,
+    norms to fp32 rounding, gamma to rounding where no code changed."""
+    for h in range(bk.shape[2]):
+        blk = np.array([s // 16 for _, _, s in evicted])
+        off = np.array([s % 16 for _, _, s in evicted])
+        for name, src in (("k", bk), ("v", bv)):
+            x = np.stack([src[b, p, h].float().cpu().numpy() for b, p, _ in evicted]).astype(np.float64)
+            e = pipeline.encode_keys(x, oq) if name == "k" else pipeline.encode_values(x, oq)
+            bits = oq["key_bits"] if name == "k" else oq["bits"]
+            bnd = oq["key_boundaries"] if name == "k" else oq["boundaries"]
+            idx = quantize.unpack_codes(host[name + "_codes"][blk, h, off], bits, 128)
+            diff = idx != e["idx"]
+            if diff.any():
+                gap = np.min(np.abs(e["y"][diff][:, None] - bnd.astype(np.float64)[None]), axis=1)
+                assert np.all(gap <= parity.Y_TOL), (name, h, gap.max())
+            assert np.allclose(host[name + "_norm"][blk, h, off], e["n"], rtol=1e-6, atol=0), (name, h)
+            if name == "k":
+                sig = quantize.unpack_bits(host["k_qjl"][blk, h, off], 128)
+                sc = np.linalg.norm(oq["s"], axis=1)[None] * np.linalg.norm(e["r"], axis=1)[:, None]
+                allowed = (np.abs(e["p"]) <= 2 * parity.Y_TOL * sc) | diff.any(axis=1)[:, None]
+                assert np.all(allowed[sig != e["sig"]]), ("bits", h)
+                same = ~diff.any(axis=1)
+                assert np.allclose(host["k_gamma"][blk, h, off][same], e["gamma"][same], rtol=1e-5, atol=1e-30)
+
+
 @pytest.mark.parametrize("kv", ["bf16", "f32"])
 def test_append_steps_then_decode(gpu_lib, kv):
     B, Hkv, G, W, steps = 3, 2, 4, 16, 21
@@ -88,6 +120,11 @@ def test_append_steps_then_decode(gpu_lib, kv):
     oq = parity.oracle_quantizer(4)
     cache = fq.PagedCache(B * nblk, Hkv, 128, 4, 128)
     mirror = fq.PagedCache(B * nblk, Hkv, 128, 4, 128)
+    # the mirror's appends go through fq_decode_step, whose decode part has nothing to read
+    q0 = torch.zeros((B, Hkv * G, 128), dtype=torch.bfloat16, device="cuda")
+    bt_t = torch.from_numpy(bt).cuda()
+    no_len = torch.zeros(B, dtype=torch.int32, device="cuda")
+    evicted = []  # (b, position, slot) of every record the append compressed
     dt = torch.bfloat16 if kv == "bf16" else torch.float32
     toks_k = torch.randn((B, cap, Hkv, 128), device="cuda").to(dt)
     toks_v = torch.randn((B, cap, Hkv, 128), device="cuda").to(dt)
@@ -110,10 +147,11 @@ def test_append_steps_then_decode(gpu_lib, kv):
         pos = torch.tensor(n, dtype=torch.int64, device="cuda")
         ev = [slot(b, int(n[b]) - W) if n[b] >= W else -1 for b in range(B)]
         evt = torch.tensor(ev, dtype=torch.int64, device="cuda")
-        # mirror: fq_compress of the same bf16 tokens, same launch shape
+        # mirror: the step's append of the same bf16 tokens
         ek = torch.stack([bk[b, max(int(n[b]) - W, 0)] for b in range(B)]).contiguous()
         evv = torch.stack([bv[b, max(int(n[b]) - W, 0)] for b in range(B)]).contiguous()
-        fq.compress(qz, mirror, ek, evv, evt)
+        fq.decode_step(qz, mirror, ek, evv, evt, q0, bt_t, no_len, 1)
+        evicted += [(b, int(n[b]) - W, ev[b]) for b in range(B) if ev[b] >= 0]
         kn = torch.stack([toks_k[b, int(n[b])] for b in range(B)]).contiguous()
         vn = torch.stack([toks_v[b, int(n[b])] for b in range(B)]).contiguous()
         fq.window_append(qz, cache, kn, vn, pos, evt, wk, wv)
@@ -125,6 +163,8 @@ def test_append_steps_then_decode(gpu_lib, kv):
     got, want = parity.cache_to_host(cache), parity.cache_to_host(mirror)
     for name in got:
         assert np.array_equal(got[name], want[name]), name
+    assert len(evicted) > 0
+    _check_evicted(got, evicted, bk, bv, oq)
     # final decode over the GPU-written cache and ring
     q = torch.randn((B, Hkv * G, 128), device="cuda").to(torch.bfloat16)
     seq_lens = np.maximum(n - W, 0).astype(np.int32)
