@@ -278,12 +278,10 @@ __device__ __forceinline__ void part_dot(const float (&col)[D / KP], const float
   }
 }
 
-// One stage of a reduce-scatter over the 16 lanes of a row: C values per lane in,
-// C / 2 out; after the stages M = 8, 4, 2, 1, lane r holds the row's sum of value r.
-template <int M, int C>
-__device__ __forceinline__ void row_reduce_scatter_stage(float (&v)[16], int r) {
-  // lanes r and r ^ M: the one with bit M set keeps the upper half of its C values,
-  // the other the lower half, and each adds the half the partner sent
+// One stage of a reduce-scatter over the 16 lanes of a row: lanes r and r ^ M swap
+// halves of their C values and add, the one with bit M set keeping the upper half.
+template <int M, int C, int N>
+__device__ __forceinline__ void row_reduce_scatter_stage(float (&v)[N], int r) {
   const bool up = (r & M) != 0;
 #pragma unroll
   for (int k = 0; k < C / 2; ++k) {
@@ -301,17 +299,18 @@ __device__ __forceinline__ void row_reduce_scatter_stage(float (&v)[16], int r) 
 // The residual window's part of query head hidx (global index) in one wave: the
 // scores scale <q, k_t> of its window tokens (exact, fp32), their max m, the sum l
 // of exp(s_t - m) and o = sum_t exp(s_t - m) v_t (lane: coordinates 2 lane,
-// 2 lane + 1). Rounds of 64 tokens: lane (g, r) = (lane / 16, lane % 16) takes
-// coordinates 8r .. 8r + 7 of tokens 4i + g, i < 16 (each load instruction reads
-// four whole K rows), and a reduce-scatter over the 16 lanes of a row leaves the
-// score of token 4r + g in lane (g, r); the round's max and sum come from
-// fixed-order lane reductions, then the lanes turn to coordinates and add up the
-// round's weighted V rows in token order. Each round requests all its K and V rows
-// before using any.
+// 2 lane + 1). Rounds of 32 tokens: lane (g, r) = (lane / 16, lane % 16) takes
+// coordinates 8r .. 8r + 7 of tokens 4i + g, i < 8 (each K load instruction reads
+// four whole rows); a reduce-scatter over the row's 16 lanes, then a pair sum,
+// leaves the score of token 4 (r / 2) + g in lanes (g, r) and (g, r ^ 1) (the odd
+// one stands aside); the round's max and sum come from fixed-order lane
+// reductions, then the lanes turn to coordinates and add up the round's weighted V
+// rows in token order. Each round requests all its K and V rows before using any.
 // m = -inf, l = 0 without tokens.
 // Rounds r0, r0 + rstride, ... of the head's window tokens only (by default all).
 __device__ __forceinline__ void window_partial(const DecodeArgs& a, int64_t hidx, int lane, float& m, float& l,
                                                float& o0, float& o1, int r0 = 0, int rstride = 1) {
+  constexpr int RT = 32;  // tokens per round
   const int b = static_cast<int>(hidx / a.hq);
   const int kvh = static_cast<int>(hidx - static_cast<int64_t>(b) * a.hq) / a.group;
   const int g = lane >> 4, r = lane & 15;
@@ -338,40 +337,41 @@ __device__ __forceinline__ void window_partial(const DecodeArgs& a, int64_t hidx
   const int64_t base = (static_cast<int64_t>(b) * a.win_cap * a.hkv + kvh) * (D / 2);
   const uint4* kb = reinterpret_cast<const uint4*>(a.win_k) + base / 4;
   const uint32_t* vb = reinterpret_cast<const uint32_t*>(a.win_v) + base;
-  for (int t0 = 64 * r0; t0 < n; t0 += 64 * rstride) {
-    uint4 kw[16];
+  const int u_own = 4 * (r >> 1) + g;  // this lane's token of the round
+  for (int t0 = RT * r0; t0 < n; t0 += RT * rstride) {
+    uint4 kw[RT / 4];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) kw[i] = kb[static_cast<int64_t>(min(t0 + 4 * i + g, n - 1)) * ts4 + r];
+    for (int i = 0; i < RT / 4; ++i) kw[i] = kb[static_cast<int64_t>(min(t0 + 4 * i + g, n - 1)) * ts4 + r];
     // the round's V rows too, all requested before any is used (rows past n reread
     // row n - 1 and get weight 0)
-    uint32_t vw[64];
+    uint32_t vw[RT];
 #pragma unroll
-    for (int u = 0; u < 64; ++u) vw[u] = vb[static_cast<int64_t>(min(t0 + u, n - 1)) * ts + lane];
-    float ps[16];
+    for (int u = 0; u < RT; ++u) vw[u] = vb[static_cast<int64_t>(min(t0 + u, n - 1)) * ts + lane];
+    float ps[RT / 4];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
+    for (int i = 0; i < RT / 4; ++i) {
       const uint32_t w4[4] = {kw[i].x, kw[i].y, kw[i].z, kw[i].w};
-      float s = 0.f;
+      float sacc = 0.f;
 #pragma unroll
       for (int e = 0; e < 4; ++e)
-        s = fmaf(qd[2 * e], __uint_as_float(w4[e] << 16), fmaf(qd[2 * e + 1], __uint_as_float(w4[e] & 0xffff0000u), s));
-      ps[i] = s;
+        sacc = fmaf(qd[2 * e], __uint_as_float(w4[e] << 16),
+                    fmaf(qd[2 * e + 1], __uint_as_float(w4[e] & 0xffff0000u), sacc));
+      ps[i] = sacc;
     }
-    row_reduce_scatter_stage<8, 16>(ps, r);
-    row_reduce_scatter_stage<4, 8>(ps, r);
-    row_reduce_scatter_stage<2, 4>(ps, r);
-    row_reduce_scatter_stage<1, 2>(ps, r);
-    const int u_own = 4 * r + g;  // this lane's token of the round
-    const float s = t0 + u_own < n ? ps[0] * a.scale : -INFINITY;
+    row_reduce_scatter_stage<8, 8>(ps, r);
+    row_reduce_scatter_stage<4, 4>(ps, r);
+    row_reduce_scatter_stage<2, 2>(ps, r);
+    const float tot = ps[0] + dpp_f<DPP_XOR1>(ps[0]);  // lanes r, r ^ 1: the same sum
+    const float s = ((r & 1) == 0 && t0 + u_own < n) ? tot * a.scale : -INFINITY;
     const float mn = fmaxf(m, wave_max_dpp(s));  // lane 0's token is live
     const float c = __expf(m - mn);              // 0 before the first round
-    const float p = __expf(s - mn);              // 0 for lanes past n
+    const float p = __expf(s - mn);              // 0 for lanes past n and odd lanes
     l = fmaf(l, c, wave_sum_dpp(p));
     o0 *= c;
     o1 *= c;
 #pragma unroll
-    for (int u = 0; u < 64; ++u) {
-      const float pu = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(p), 16 * (u & 3) + (u >> 2)));
+    for (int u = 0; u < RT; ++u) {
+      const float pu = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(p), 16 * (u & 3) + 2 * (u >> 2)));
       o0 = fmaf(pu, __uint_as_float(vw[u] << 16), o0);
       o1 = fmaf(pu, __uint_as_float(vw[u] & 0xffff0000u), o1);
     }
@@ -1869,7 +1869,7 @@ __global__ void __launch_bounds__(WAVES * 64, OCC) packed_decode_kernel(DecodeAr
   }
 
   // ---- the residual window (the only split): wave w computes part w / G of query
-  // head w % G's window (rounds of 64 tokens w / G, w / G + C, ..., C = WAVES / G parts
+  // head w % G's window (rounds of 32 tokens w / G, w / G + C, ..., C = WAVES / G parts
   // per head; exact scores and values, natural-log max, original frame) once its
   // pages are done, so the window fills the waves' end spread instead of a launch
   const int wparts = WAVES / G;  // >= 1 (G <= 8 <= WAVES)
