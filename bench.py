@@ -227,9 +227,19 @@ def _capture(calls):
     return g
 
 
+EAGER = False  # --no-graph: time the call sequences eagerly (e.g. under a counter profiler)
+
+
 def graph_stats(calls, stream, reps=MIN_SAMPLES):
     """Per-call device time: HIP events around reps replays of a graph holding the calls,
-    each replay's time divided by the number of calls; median, p10, p90."""
+    each replay's time divided by the number of calls; median, p10, p90. With --no-graph
+    the same sequence of calls is launched eagerly instead."""
+    if EAGER:
+        def seq():
+            for c in calls:
+                c()
+        seq()
+        return stats_ms(_events_samples(seq, reps, stream, per=len(calls)))
     g = _capture(calls)
     return stats_ms(_events_samples(g.replay, reps, stream, per=len(calls)))
 
@@ -484,8 +494,15 @@ def stream_compress_measure(bits, layers, stream):
     quants = [fq.Quantizer(bits, d, fq.ROT_HAAR, 1 + layer, 2 + layer, 128) for layer in range(layers)]
     calls = [lambda l=l: fq.compress(quants[l], caches[l % nc], pool[l % 8][0], pool[l % 8][1], slots)
              for l in range(layers)]
-    g = _capture(calls)
-    tot = _events_samples(g.replay, 5, stream)
+    if EAGER:
+        def run_all():
+            for c in calls:
+                c()
+        run_all()
+        tot = _events_samples(run_all, 5, stream)
+    else:
+        g = _capture(calls)
+        tot = _events_samples(g.replay, 5, stream)
     total_ms = float(np.median(tot))
     nvec = 2 * layers * T * Hkv
     out_b = caches[0].bytes_per_token_head() * T * Hkv * layers
@@ -507,6 +524,8 @@ ONLY = ("step", "step4", "c2", "c4_haar", "c4_wht", "c4_compress_haar", "c4_comp
 
 def main():
     args = parse()
+    global EAGER
+    EAGER = args.no_graph
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)",
               file=sys.stderr)
