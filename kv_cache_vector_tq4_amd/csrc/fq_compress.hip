@@ -29,6 +29,8 @@ namespace {
 
 constexpr int D = FQ_HEAD_DIM;
 typedef const __attribute__((address_space(4))) float* cptr;
+typedef __bf16 bf2v __attribute__((ext_vector_type(2)));
+typedef __fp16 h2v __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ cptr uniform_ptr(const float* p) {
   return reinterpret_cast<cptr>(reinterpret_cast<uintptr_t>(p));
@@ -301,12 +303,10 @@ __device__ __forceinline__ void compress_tile(const CompressArgs& a, int kind, i
     for (int s = 0; s < 8; ++s) {
       uint4 u = reinterpret_cast<const uint4*>(base)[s];
       const uint32_t w4[4] = {u.x, u.y, u.z, u.w};
+      // the squares of a bf16 pair are exact in fp32: one dot2 per pair
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const float lo = __uint_as_float(w4[q] << 16), hi = __uint_as_float(w4[q] & 0xffff0000u);
-        ss = fmaf(lo, lo, ss);
-        ss = fmaf(hi, hi, ss);
-      }
+      for (int q = 0; q < 4; ++q) ss = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf2v, w4[q]),
+                                                                     __builtin_bit_cast(bf2v, w4[q]), ss, false);
       xb[s] = __builtin_bit_cast(b8, u);
     }
   } else {
@@ -368,23 +368,35 @@ __device__ __forceinline__ void compress_tile(const CompressArgs& a, int kind, i
   uint32_t words[2 * BITS];
 #pragma unroll
   for (int w = 0; w < 2 * BITS; ++w) words[w] = 0;
+  // cell of y in the lookup table (truncation equals floor here: arguments below 0
+  // land in cell 0 either way)
+  auto cell_of = [&](float y) {
+    const int c = static_cast<int>(fmaf(y, inv_w, off));
+    return min(max(c, 0), QT_CELLS - 1);
+  };
+  // groups of QG coordinates: the group's cells are requested together, then
+  // decided (a barrier per group keeps the compiler from holding all 64 in flight)
+  constexpr int QG = 8;
 #pragma unroll
-  for (int T = 0; T < 4; ++T) {
-    if constexpr (!FRAG_GLOBAL) __builtin_amdgcn_sched_barrier(0);  // LDS fragments: load next to use
+  for (int g = 0; g < 64 / QG; ++g) {
+    QCell q[QG];
 #pragma unroll
-    for (int vv = 0; vv < 16; ++vv) {
-      const int rel = 16 * T + vv;
-      const float y = acc[T][vv];
-      int c = static_cast<int>(floorf(fmaf(y, inv_w, off)));
-      c = min(max(c, 0), QT_CELLS - 1);
-      const QCell q = qt[c];
-      const bool gt = q.b < y;
-      const uint32_t idx = q.count + (gt ? 1u : 0u);
-      const int off = BITS * rel;
-      words[off >> 5] |= idx << (off & 31);
-      if ((off & 31) + BITS > 32) words[(off >> 5) + 1] |= idx >> (32 - (off & 31));
-      if constexpr (KEY) acc[T][vv] = y - (gt ? q.c_hi : q.c_lo);
+    for (int k = 0; k < QG; ++k) {
+      const int rel = QG * g + k;
+      q[k] = qt[cell_of(acc[rel >> 4][rel & 15])];
     }
+#pragma unroll
+    for (int k = 0; k < QG; ++k) {
+      const int rel = QG * g + k;
+      const float y = acc[rel >> 4][rel & 15];
+      const bool gt = q[k].b < y;
+      const uint32_t idx = q[k].count + (gt ? 1u : 0u);
+      const int bo = BITS * rel;
+      words[bo >> 5] |= idx << (bo & 31);
+      if ((bo & 31) + BITS > 32) words[(bo >> 5) + 1] |= idx >> (32 - (bo & 31));
+      if constexpr (KEY) acc[rel >> 4][rel & 15] = y - (gt ? q[k].c_hi : q[k].c_lo);
+    }
+    __builtin_amdgcn_sched_barrier(0);
   }
   if (store) {
     uint8_t* cd = a.codes[kind] + rec * (D * BITS / 8) + 64 * h * BITS / 8;
@@ -407,48 +419,64 @@ __device__ __forceinline__ void compress_tile(const CompressArgs& a, int kind, i
 #pragma unroll
       for (int vv = 0; vv < 16; ++vv) rr = fmaf(acc[T][vv], acc[T][vv], rr);
     rr += __shfl_xor(rr, 32);
-    // B fragments of r, converted per k-step: step s covers coordinates
-    // 64h + 8s + e = acc[s/2][8(s%2) + e]
-    f16v pacc[4];
-#pragma unroll
-    for (int T = 0; T < 4; ++T) pacc[T] = f16v{};
+    // B fragments of r: k-step s covers coordinates 64h + 8s + e = acc[s/2][8(s%2) + e],
+    // as fp16 hi / lo pairs (truncating conversions; the lo part carries the hi
+    // part's error, r - hi being exact in fp32)
+    uint4 rfh[8], rfl[8];
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
-      if constexpr (!FRAG_GLOBAL) __builtin_amdgcn_sched_barrier(0);  // LDS fragments: load next to use
-      uint32_t hi[8], lo[8];
+      uint32_t hw[4], lw[4];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) split_f16b(acc[s >> 1][8 * (s & 1) + e], hi[e], lo[e]);
-      const hh8 rh = __builtin_bit_cast(hh8, make_uint4(hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16), hi[4] | (hi[5] << 16), hi[6] | (hi[7] << 16)));
-      const hh8 rl = __builtin_bit_cast(hh8, make_uint4(lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16), lo[4] | (lo[5] << 16), lo[6] | (lo[7] << 16)));
+      for (int e = 0; e < 4; ++e) {
+        const float r0 = acc[s >> 1][8 * (s & 1) + 2 * e], r1 = acc[s >> 1][8 * (s & 1) + 2 * e + 1];
+        const h2v hv = __builtin_amdgcn_cvt_pkrtz(r0, r1);
+        const h2v lv = __builtin_amdgcn_cvt_pkrtz(r0 - static_cast<float>(hv[0]), r1 - static_cast<float>(hv[1]));
+        hw[e] = __builtin_bit_cast(uint32_t, hv);
+        lw[e] = __builtin_bit_cast(uint32_t, lv);
+      }
+      rfh[s] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+      rfl[s] = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+    }
+    // p = S r in two halves of output rows (row tiles 2 hf, 2 hf + 1: coordinates
+    // 64h + 32 hf .., sign word hf); sigma = [p >= 0] is the clear sign bit (an
+    // accumulation from +0 never ends at -0)
+    uint32_t sg[2];
 #pragma unroll
-      for (int T = 0; T < 4; ++T) {
-        const hh8 ah = __builtin_bit_cast(hh8, fsm[(T * 8 + s) * 64 + lane]);
-        const hh8 al = __builtin_bit_cast(hh8, fsm[(32 + T * 8 + s) * 64 + lane]);
-        pacc[T] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah, rh, pacc[T], 0, 0, 0);
-        pacc[T] = __builtin_amdgcn_mfma_f32_32x32x16_f16(al, rh, pacc[T], 0, 0, 0);
-        pacc[T] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah, rl, pacc[T], 0, 0, 0);
+    for (int hf = 0; hf < 2; ++hf) {
+      f16v pacc[2] = {f16v{}, f16v{}};
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        if constexpr (!FRAG_GLOBAL) __builtin_amdgcn_sched_barrier(0);  // LDS fragments: load next to use
+        const hh8 rh = __builtin_bit_cast(hh8, rfh[s]);
+        const hh8 rl = __builtin_bit_cast(hh8, rfl[s]);
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int T = 2 * hf + u;
+          const hh8 ah = __builtin_bit_cast(hh8, fsm[(T * 8 + s) * 64 + lane]);
+          const hh8 al = __builtin_bit_cast(hh8, fsm[(32 + T * 8 + s) * 64 + lane]);
+          pacc[u] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah, rh, pacc[u], 0, 0, 0);
+          pacc[u] = __builtin_amdgcn_mfma_f32_32x32x16_f16(al, rh, pacc[u], 0, 0, 0);
+          pacc[u] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah, rl, pacc[u], 0, 0, 0);
+        }
+      }
+      uint32_t ng = 0;
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int vv = 0; vv < 16; ++vv) ng |= (__float_as_uint(pacc[u][vv]) >> 31) << (16 * u + vv);
+      sg[hf] = ~ng;
+      if (store && a.dbg_p) {
+        float4* dp = reinterpret_cast<float4*>(a.dbg_p + (t * a.hkv + hd) * D + 64 * h + 32 * hf);
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            dp[4 * u + q] = make_float4(pacc[u][4 * q], pacc[u][4 * q + 1], pacc[u][4 * q + 2], pacc[u][4 * q + 3]);
       }
     }
-    // pacc[T][vv] = p[64h + 16T + vv]
-    uint32_t sg[2] = {0u, 0u};
-#pragma unroll
-    for (int T = 0; T < 4; ++T)
-#pragma unroll
-      for (int vv = 0; vv < 16; ++vv) {
-        const int rel = 16 * T + vv;
-        sg[rel >> 5] |= (pacc[T][vv] >= 0.f ? 1u : 0u) << (rel & 31);
-      }
     if (store) {
       *reinterpret_cast<uint2*>(a.qjl + rec * (D / 8) + 8 * h) = make_uint2(sg[0], sg[1]);
       if (h == 0) a.gamma[rec] = n * sqrtf(rr);
-      if (a.dbg_p) {
-        float4* dp = reinterpret_cast<float4*>(a.dbg_p + (t * a.hkv + hd) * D + 64 * h);
-#pragma unroll
-        for (int T = 0; T < 4; ++T)
-#pragma unroll
-          for (int q = 0; q < 4; ++q)
-            dp[4 * T + q] = make_float4(pacc[T][4 * q], pacc[T][4 * q + 1], pacc[T][4 * q + 2], pacc[T][4 * q + 3]);
-      }
     }
   }
 }
@@ -514,8 +542,8 @@ __device__ __forceinline__ uint4 pack8(const uint32_t (&u)[8]) {
 // Large inputs: work-groups of 8 waves loop over tiles with the fragments in LDS
 // (copied from the prepared operand buffer, or built from the fp32 matrices).
 // Keys run 4 waves per work-group (their 128 KB of fragments allow one work-group
-// per CU anyway), which leaves each wave enough registers for the QJL product;
-// values run 8.
+// per CU anyway), which leaves each wave the registers of the QJL product: at 8
+// waves (256 registers each) the key tile spills and runs 1.4x slower.
 template <int BITS, int DT, bool KEY>
 __global__ void __launch_bounds__((KEY ? 4 : CT_WAVES) * 64) compress_mfma_kernel(CompressArgs a, int kind) {
   constexpr int WAVES = KEY ? 4 : CT_WAVES;
