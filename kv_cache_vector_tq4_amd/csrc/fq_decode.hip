@@ -1323,6 +1323,8 @@ constexpr int PK_LDS_BYTES = PK_QOPS_BASE + 8 * 64 * 16;  // 80 KB: two work-gro
 // table: 256 entries of eight fp16 +-1, 16 copies (copy = lane % 16), so one
 // 16-byte lookup per sign byte.
 constexpr int PK_BSIGN_BASE = PK_LDS_BYTES;
+constexpr int PK_KTAB_BASE = PK_LDS_BYTES;       // 3-bit keys: 64 pair entries x 32 copies x 8 B
+constexpr int PK_KTAB_BYTES = 64 * 32 * 8;
 constexpr int PK_LDS_BYTES_F = PK_BSIGN_BASE + 256 * 16 * 16;
 // In-kernel query preparation (groups of up to 8 heads) uses the code-table area
 // before the table is built: its scratch, then the FQ_QOPS x 64 operands.
@@ -1358,19 +1360,39 @@ struct PkPage {
 // Per-lane byte offsets of a page's fields (constant over pages).
 struct PkLane {
   uint32_t kc, sg, vc;
+  // 3-bit values: dims 8n .. 8n+7 start at bit vsh of the dword at vc and run into
+  // the one at vc2 (the same dword at the end of the record, where they do not)
+  uint32_t vc2, vsh;
 };
+
+// 3-bit codes widened for the 4-bit matrix-core path. Eight 3-bit codes (24 bits,
+// the stream of dims 8j .. 8j+7) become four bytes, byte k = code 2k + 8 x code 2k+1
+// (pair index of a 64-entry table), or with nibbles_of four bytes of two 4-bit
+// nibbles (byte k = code 2k + 16 x code 2k+1, the 4-bit table's byte layout).
+__device__ __forceinline__ uint32_t pairs_of3(uint32_t x) {
+  uint32_t t = (x & 0xFFFu) | ((x & 0xFFF000u) << 4);
+  return (t & 0x003F003Fu) | ((t & 0x0FC00FC0u) << 2);
+}
+__device__ __forceinline__ uint32_t nibbles_of3(uint32_t x) {
+  const uint32_t t = pairs_of3(x);
+  return (t & 0x07070707u) | ((t & 0x38383838u) << 1);
+}
 
 // Loads one page; rec0 = first record of the page (wave-uniform), so every
 // address is a uniform base plus a fixed 32-bit lane offset.
-template <int BITS>
+// K3 = 1: 3-bit key codes (kc as 6-bit pair bytes); K3 = 2: 3-bit values as well
+// (vc as 4-bit nibbles). The 4-bit path's layouts otherwise.
+template <int BITS, int K3 = 0>
 __device__ __forceinline__ void pk_load(const DecodeArgs& a, int64_t rec0, int n, const PkLane& o,
                                         const float* gptr, const uint8_t* sgn_base, PkPage<BITS>& d) {
-  constexpr int CB = D * BITS / 8;  // code bytes per vector
+  static_assert(K3 == 0 || BITS == 4, "3-bit codes take the 4-bit layouts");
+  constexpr int CBK = K3 ? 48 : D * BITS / 8;   // key code bytes per vector
+  constexpr int CB = K3 == 2 ? 48 : D * BITS / 8;  // value code bytes per vector
   // The page's field bases are uniform: pinned in scalar registers, every load is a
   // scalar base plus the lane's 32-bit offset (no 64-bit vector address adds).
   typedef const __attribute__((address_space(1))) uint8_t* gb8;
   typedef const __attribute__((address_space(1))) float* gf32;
-  gb8 kcb = (gb8)(a.k_codes + rec0 * CB);
+  gb8 kcb = (gb8)(a.k_codes + rec0 * CBK);
   gb8 sgb = (gb8)(sgn_base + rec0 * 16);
   gf32 knb = (gf32)(a.k_norm + rec0);
   gf32 gmb = (gf32)(gptr + rec0);
@@ -1381,7 +1403,15 @@ __device__ __forceinline__ void pk_load(const DecodeArgs& a, int64_t rec0, int n
   asm volatile("" : "+v"(okc), "+v"(osg), "+v"(ovc));
   // the 4-bit codes and sign words are read once per step: non-temporal loads
   // (3 % faster at the batch-32 shape, same bits)
-  if constexpr (BITS == 4) {
+  if constexpr (K3 != 0) {
+    // dims 32g .. 32g+31: 96 bits, four 24-bit runs of eight codes
+    typedef uint32_t u32x3 __attribute__((ext_vector_type(3)));
+    const u32x3 k = __builtin_nontemporal_load(reinterpret_cast<const __attribute__((address_space(1))) u32x3*>(kcb + okc));
+    d.kc[0] = pairs_of3(k.x & 0xFFFFFFu);
+    d.kc[1] = pairs_of3(__builtin_amdgcn_alignbit(k.y, k.x, 24) & 0xFFFFFFu);
+    d.kc[2] = pairs_of3(__builtin_amdgcn_alignbit(k.z, k.y, 16) & 0xFFFFFFu);
+    d.kc[3] = pairs_of3(k.z >> 8);
+  } else if constexpr (BITS == 4) {
     typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
     const u32x4 k = __builtin_nontemporal_load(reinterpret_cast<const __attribute__((address_space(1))) u32x4*>(kcb + okc));
     d.kc[0] = k.x;
@@ -1400,10 +1430,18 @@ __device__ __forceinline__ void pk_load(const DecodeArgs& a, int64_t rec0, int n
   d.vn = vnb[n];
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
-    if constexpr (BITS == 4)
+    if constexpr (K3 == 2) {
+      // dims 8n .. 8n+7 at bit 24n of the record: the dword at ovc and the next one
+      // (kept inside the 48-byte record: it is needed only when the run crosses it)
+      typedef const __attribute__((address_space(1))) uint32_t* gu32;
+      const uint32_t w0 = __builtin_nontemporal_load(reinterpret_cast<gu32>(vcb + ovc + CB * e));
+      const uint32_t w1 = __builtin_nontemporal_load(reinterpret_cast<gu32>(vcb + o.vc2 + CB * e));
+      d.vc[e] = nibbles_of3(__builtin_amdgcn_alignbit(w1, w0, o.vsh) & 0xFFFFFFu);
+    } else if constexpr (BITS == 4) {
       d.vc[e] = __builtin_nontemporal_load(reinterpret_cast<const __attribute__((address_space(1))) uint32_t*>(vcb + ovc + CB * e));
-    else
+    } else {
       d.vc[e] = *reinterpret_cast<const __attribute__((address_space(1))) uint16_t*>(vcb + ovc + CB * e);
+    }
   }
 }
 
@@ -1430,7 +1468,7 @@ __device__ __forceinline__ void xcd_pair_map(int hkv, int batch, int& kvh, int& 
 // work-group normalizes and un-rotates its output itself. PREP = the query
 // dtype (>= 0): as -2, and the work-group prepares its own query operands too
 // (prepare_group, in the LDS the code table takes later).
-template <int BITS, int SLOTS, int WAVES, int RING, int OCC, int PREP, bool APP = false>
+template <int BITS, int SLOTS, int WAVES, int RING, int OCC, int PREP, bool APP = false, int K3 = 0>
 __global__ void __launch_bounds__(WAVES * 64, OCC) packed_decode_kernel(DecodeArgs a) {
   static_assert(BITS == 4 || BITS == 2, "4- or 2-bit codes");
   constexpr bool INPREP = PREP >= 0;  // query operands prepared in-kernel
@@ -1439,10 +1477,14 @@ __global__ void __launch_bounds__(WAVES * 64, OCC) packed_decode_kernel(DecodeAr
   static_assert(!APP || INPREP, "the append runs in the in-kernel query preparation");
   static_assert(WAVES * 64 >= 256, "the table stage takes 256 threads");
   constexpr int CB = D * BITS / 8;  // code bytes per vector
-  constexpr bool BSIGN = ONLY;  // byte-indexed sign table (one work-group per CU)
+  // K3 = 1: 3-bit keys (their own 64-entry pair table), 4-bit values; K3 = 2: 3-bit
+  // keys and values (the values widened to the 4-bit table's layout)
+  static_assert(K3 == 0 || BITS == 4, "3-bit codes take the 4-bit path");
+  constexpr bool BSIGN = ONLY && K3 == 0;  // byte-indexed sign table (one work-group per CU)
   constexpr int PRO = RING - 1;  // pages requested ahead of the loop
-  __shared__ __align__(16) uint8_t s_lds[BSIGN ? PK_LDS_BYTES_F : PK_LDS_BYTES];
+  __shared__ __align__(16) uint8_t s_lds[BSIGN ? PK_LDS_BYTES_F : K3 ? PK_KTAB_BASE + PK_KTAB_BYTES : PK_LDS_BYTES];
   const uint8_t* const s_code = s_lds + PK_CODE_BASE;
+  const uint8_t* const s_ktab = K3 ? s_lds + PK_KTAB_BASE : s_code;  // key code table
   const uint8_t* const s_sign = s_lds + PK_SIGN_BASE;
   constexpr int HL = 4 / SLOTS;  // heads per lane in the score layout (1 or 2)
   const int split = blockIdx.x;
@@ -1497,9 +1539,11 @@ __global__ void __launch_bounds__(WAVES * 64, OCC) packed_decode_kernel(DecodeAr
     return (static_cast<int64_t>(blk) * a.hkv + kvh) * FQ_BLOCK;
   };
   PkLane lo;
-  lo.kc = static_cast<uint32_t>(n * CB + 4 * BITS * g);
+  lo.kc = static_cast<uint32_t>(K3 ? n * 48 + 12 * g : n * CB + 4 * BITS * g);
   lo.sg = static_cast<uint32_t>(n * 16 + 4 * g);
-  lo.vc = static_cast<uint32_t>(4 * g * CB + BITS * n);
+  lo.vc = static_cast<uint32_t>(K3 == 2 ? 4 * g * 48 + ((3 * n) & ~3) : 4 * g * CB + BITS * n);
+  lo.vc2 = static_cast<uint32_t>(4 * g * 48 + min(((3 * n) & ~3) + 4, 44));
+  lo.vsh = static_cast<uint32_t>(((3 * n) & 3) * 8);
 
   // ---- the query loads (in-kernel preparation) and the wave's first RING - 1
   // pages are requested before any set-up work, in the order they are needed
@@ -1509,13 +1553,23 @@ __global__ void __launch_bounds__(WAVES * 64, OCC) packed_decode_kernel(DecodeAr
   }
   // codebook levels of the table entry this thread stages (threads < 256)
   float lv[BITS == 4 ? 2 : 4] = {};
+  float klv[2] = {0.f, 0.f};  // 3-bit keys: levels of pair entry tid < 64
   if (tid < 256) {
-    if constexpr (BITS == 4) {
+    if constexpr (K3 == 2) {  // 3-bit values: nibbles 8 .. 15 never occur
+      lv[0] = (tid & 15) < 8 ? a.levels[tid & 7] : 0.f;
+      lv[1] = (tid >> 4) < 8 ? a.levels[(tid >> 4) & 7] : 0.f;
+    } else if constexpr (BITS == 4) {
       lv[0] = a.levels[tid & 15];
       lv[1] = a.levels[tid >> 4];
     } else {
 #pragma unroll
       for (int k = 0; k < 4; ++k) lv[k] = a.levels[(tid >> (2 * k)) & 3];
+    }
+  }
+  if constexpr (K3 != 0) {
+    if (tid < 64) {
+      klv[0] = a.klevels[tid & 7];
+      klv[1] = a.klevels[tid >> 3];
     }
   }
   // ---- query operands. With two heads per lane (SLOTS 2) registers are short, so
@@ -1555,7 +1609,7 @@ __global__ void __launch_bounds__(WAVES * 64, OCC) packed_decode_kernel(DecodeAr
   if (my_pages > 0) {
 #pragma unroll
     for (int k = 0; k < PRO; ++k)
-      pk_load(a, rec_of(bt_cur, min(k, min(64, my_pages) - 1)), n, lo, gptr, sgn_base, ring[k]);
+      pk_load<BITS, K3>(a, rec_of(bt_cur, min(k, min(64, my_pages) - 1)), n, lo, gptr, sgn_base, ring[k]);
   }
 
   // the byte-indexed sign table needs no input: built while the loads are in flight
@@ -1588,7 +1642,7 @@ __global__ void __launch_bounds__(WAVES * 64, OCC) packed_decode_kernel(DecodeAr
 #pragma unroll
       for (int k = 0; k < PRO; ++k)
         if (k < my_pages && nslot >= 0 && __builtin_amdgcn_readlane(bt_cur, k) == static_cast<int>(nslot >> 4))
-          pk_load(a, rec_of(bt_cur, k), n, lo, gptr, sgn_base, ring[k]);
+          pk_load<BITS, K3>(a, rec_of(bt_cur, k), n, lo, gptr, sgn_base, ring[k]);
     }
   } else if constexpr (ONLY) {
 #pragma unroll
@@ -1610,6 +1664,13 @@ __global__ void __launch_bounds__(WAVES * 64, OCC) packed_decode_kernel(DecodeAr
         split_f16(c0, h0, l0);
         split_f16(c1, h1, l1);
         stage[tid] = make_uint2(h2bits(h0, h1), h2bits(l0, l1));
+        if constexpr (K3 != 0) {
+          if (tid < 64) {
+            split_f16(klv[0] * static_cast<float>(1 << LEV_SHIFT), h0, l0);
+            split_f16(klv[1] * static_cast<float>(1 << LEV_SHIFT), h1, l1);
+            stage[256 + tid] = make_uint2(h2bits(h0, h1), h2bits(l0, l1));
+          }
+        }
       } else {
         constexpr float SC = static_cast<float>(1 << LEV_SHIFT);
         _Float16 h0, l0, h1, l1, h2, l2, h3, l3;
@@ -1633,6 +1694,10 @@ __global__ void __launch_bounds__(WAVES * 64, OCC) packed_decode_kernel(DecodeAr
       *reinterpret_cast<uint2*>(s_lds + PK_SIGN_BASE + idx * 8) = make_uint2(w[0], w[1]);
     }
     __syncthreads();
+    if constexpr (K3 != 0) {  // the 3-bit keys' pair table: 64 entries x 32 copies
+      for (int idx = tid; idx < 64 * 32; idx += NT)
+        *reinterpret_cast<uint2*>(s_lds + PK_KTAB_BASE + idx * 8) = stage[256 + (idx >> 5)];
+    }
     // 8192 (4096) entries; four per thread and round, reads issued before writes
     if constexpr (BITS == 4 && (256 * 32) % (4 * NT) != 0) {
       for (int idx = tid; idx < 256 * 32; idx += NT)
@@ -1695,8 +1760,8 @@ __global__ void __launch_bounds__(WAVES * 64, OCC) packed_decode_kernel(DecodeAr
     for (int i = 0; i < 8; ++i) {
       h8 kop;
       if constexpr (BITS == 4) {
-        const uint2 e0 = lds_u2(s_code, tab_off(d.kc[i >> 1], copy8, (2 * i) & 3));
-        const uint2 e1 = lds_u2(s_code, tab_off(d.kc[i >> 1], copy8, (2 * i + 1) & 3));
+        const uint2 e0 = lds_u2(s_ktab, tab_off(d.kc[i >> 1], copy8, (2 * i) & 3));
+        const uint2 e1 = lds_u2(s_ktab, tab_off(d.kc[i >> 1], copy8, (2 * i + 1) & 3));
         kop = h8_of(e0, e1);
       } else {
         const uint4 e = lds_u4(s_code, tab_off(d.kc[i >> 2], copy16, i & 3));
@@ -1856,13 +1921,13 @@ __global__ void __launch_bounds__(WAVES * 64, OCC) packed_decode_kernel(DecodeAr
       pg_cur = page_of(chunk_lane(c0));
       bt_cur = bt[pg_cur];
 #pragma unroll
-      for (int k = 0; k < PRO; ++k) pk_load(a, rec_of(bt_cur, min(k, cn - 1)), n, lo, gptr, sgn_base, ring[k]);
+      for (int k = 0; k < PRO; ++k) pk_load<BITS, K3>(a, rec_of(bt_cur, min(k, cn - 1)), n, lo, gptr, sgn_base, ring[k]);
     }
     for (int i = 0; i < cn; i += RING) {
 #pragma unroll
       for (int k = 0; k < RING; ++k) {
         const int ik = i + k;
-        pk_load(a, rec_of(bt_cur, min(ik + RING - 1, cn - 1)), n, lo, gptr, sgn_base, ring[(k + RING - 1) % RING]);
+        pk_load<BITS, K3>(a, rec_of(bt_cur, min(ik + RING - 1, cn - 1)), n, lo, gptr, sgn_base, ring[(k + RING - 1) % RING]);
         if (ik < cn) process(ring[k], __builtin_amdgcn_readlane(pg_cur, ik));
       }
     }
@@ -2090,28 +2155,42 @@ int launch_decode(void* stream, const fq_quantizer& q, const fq_cache& c, const 
   // 4-bit codebook for both. 3-bit codes and keys of their own width take the
   // vector-ALU kernel.
   const bool shared4 = a.kbits == q.bits && key_levels_of(q) == q.levels && q.bits != 3;
-  const bool valu = !shared4 || (impl && std::strcmp(impl, "valu") == 0);
+  // 3-bit keys with 4-bit values (k3 = 1), or 3-bit keys and values of one codebook
+  // (k3 = 2): the matrix-core kernel on the single-launch path (one split, G <= 8),
+  // widened to its 4-bit layouts; otherwise the vector-ALU kernel
+  const int k3 = a.kbits == 3 && q.bits == 4 ? 1 : a.kbits == 3 && q.bits == 3 && key_levels_of(q) == q.levels ? 2 : 0;
+  const bool force_valu = impl && std::strcmp(impl, "valu") == 0;
   const bool v1 = impl && std::strcmp(impl, "mfma_v1") == 0;
+  const bool unfused = std::getenv("FQ_DECODE_UNFUSED") != nullptr;
+  const bool k3_mfma = k3 > 0 && !v1 && num_splits == 1 && !unfused && a.group <= 8;
+  const bool valu = (!shared4 && !k3_mfma) || force_valu;
   const int slots = (!valu && !v1) ? (a.group <= 4 ? 4 : a.group <= 8 ? 2 : 0) : 0;
   dim3 grid(num_splits, c.num_kv_heads, batch);
-  const bool only = slots > 0 && num_splits == 1 && std::getenv("FQ_DECODE_UNFUSED") == nullptr;
+  const bool only = slots > 0 && num_splits == 1 && !unfused;
   if (only && phase == DECODE_ALL) {
     // one work-group per (KV head, sequence) does everything in one launch
     // (appending the newest token first, when asked)
-#define FQ_FUSED(BITS, SL, DT)                                                                                   \
-  do {                                                                                                           \
-    if (app)                                                                                                     \
-      hipLaunchKernelGGL((packed_decode_kernel<BITS, SL, pkf_waves(BITS), PKF_RING, PKF_OCC, DT, true>), grid,   \
-                         dim3(pkf_waves(BITS) * 64), 0, st, a);                                                  \
-    else                                                                                                         \
-      hipLaunchKernelGGL((packed_decode_kernel<BITS, SL, pkf_waves(BITS), PKF_RING, PKF_OCC, DT, false>), grid,  \
-                         dim3(pkf_waves(BITS) * 64), 0, st, a);                                                  \
+#define FQ_FUSED(BITS, SL, DT, K3)                                                                                   \
+  do {                                                                                                               \
+    if (app)                                                                                                         \
+      hipLaunchKernelGGL((packed_decode_kernel<BITS, SL, pkf_waves(BITS), PKF_RING, PKF_OCC, DT, true, K3>), grid,   \
+                         dim3(pkf_waves(BITS) * 64), 0, st, a);                                                      \
+    else                                                                                                             \
+      hipLaunchKernelGGL((packed_decode_kernel<BITS, SL, pkf_waves(BITS), PKF_RING, PKF_OCC, DT, false, K3>), grid,  \
+                         dim3(pkf_waves(BITS) * 64), 0, st, a);                                                      \
   } while (0)
-    const bool bf = q_dtype == FQ_BF16;
-    if (q.bits == 4 && slots == 4) { if (bf) FQ_FUSED(4, 4, FQ_BF16); else FQ_FUSED(4, 4, FQ_F32); }
-    else if (q.bits == 4) { if (bf) FQ_FUSED(4, 2, FQ_BF16); else FQ_FUSED(4, 2, FQ_F32); }
-    else if (slots == 4) { if (bf) FQ_FUSED(2, 4, FQ_BF16); else FQ_FUSED(2, 4, FQ_F32); }
-    else { if (bf) FQ_FUSED(2, 2, FQ_BF16); else FQ_FUSED(2, 2, FQ_F32); }
+#define FQ_FUSED_DT(BITS, SL, K3)                           \
+  do {                                                      \
+    if (q_dtype == FQ_BF16) FQ_FUSED(BITS, SL, FQ_BF16, K3); \
+    else FQ_FUSED(BITS, SL, FQ_F32, K3);                     \
+  } while (0)
+    if (k3 == 1) { if (slots == 4) FQ_FUSED_DT(4, 4, 1); else FQ_FUSED_DT(4, 2, 1); }
+    else if (k3 == 2) { if (slots == 4) FQ_FUSED_DT(4, 4, 2); else FQ_FUSED_DT(4, 2, 2); }
+    else if (q.bits == 4 && slots == 4) FQ_FUSED_DT(4, 4, 0);
+    else if (q.bits == 4) FQ_FUSED_DT(4, 2, 0);
+    else if (slots == 4) FQ_FUSED_DT(2, 4, 0);
+    else FQ_FUSED_DT(2, 2, 0);
+#undef FQ_FUSED_DT
 #undef FQ_FUSED
     return static_cast<int>(hipGetLastError());
   }
@@ -2139,13 +2218,15 @@ int launch_decode(void* stream, const fq_quantizer& q, const fq_cache& c, const 
   if (phase == DECODE_PREPARE) return static_cast<int>(hipGetLastError());
   if (only) {
     // the only split, query operands from the preparation launch
-#define FQ_ONLY(BITS, SL)                                                                                       \
-  hipLaunchKernelGGL((packed_decode_kernel<BITS, SL, pkf_waves(BITS), PKF_RING, PKF_OCC, -2>), grid,            \
+#define FQ_ONLY(BITS, SL, K3)                                                                                   \
+  hipLaunchKernelGGL((packed_decode_kernel<BITS, SL, pkf_waves(BITS), PKF_RING, PKF_OCC, -2, false, K3>), grid, \
                      dim3(pkf_waves(BITS) * 64), 0, st, a)
-    if (q.bits == 4 && slots == 4) FQ_ONLY(4, 4);
-    else if (q.bits == 4) FQ_ONLY(4, 2);
-    else if (slots == 4) FQ_ONLY(2, 4);
-    else FQ_ONLY(2, 2);
+    if (k3 == 1) { if (slots == 4) FQ_ONLY(4, 4, 1); else FQ_ONLY(4, 2, 1); }
+    else if (k3 == 2) { if (slots == 4) FQ_ONLY(4, 4, 2); else FQ_ONLY(4, 2, 2); }
+    else if (q.bits == 4 && slots == 4) FQ_ONLY(4, 4, 0);
+    else if (q.bits == 4) FQ_ONLY(4, 2, 0);
+    else if (slots == 4) FQ_ONLY(2, 4, 0);
+    else FQ_ONLY(2, 2, 0);
 #undef FQ_ONLY
     return static_cast<int>(hipGetLastError());
   }

@@ -8,7 +8,8 @@
   MSE + QJL, values 3-bit).
 Compress under the fed protocol (both compress kernels: the many-tile one without
 prepared operands, the small-input one with them), decode of the oracle's bytes
-(one and three splits, groups 4 / 8 / 16, Haar and WHT), the decode step (the
+(one and three splits, groups 4 / 8 / 16, Haar and WHT; the matrix-core kernel at
+one split against the vector-ALU one for groups 1 to 8), the decode step (the
 newest token appended by the GPU), and decompress (fp32 within 1e-5 n of the
 oracle's reconstruction; bf16 within the bf16 rounding of it plus 1e-3 n)."""
 import numpy as np
@@ -74,6 +75,30 @@ def test_decode(gpu_lib, vb, kb, G, splits):
     err = float(np.max(np.abs(out - ref)))
     print("max-abs", err, "cos vs exact", parity.cosine(out, parity.exact(inp)))
     assert err <= parity.DECODE_TOL
+
+
+@pytest.mark.parametrize("G", [1, 2, 4, 8])
+@pytest.mark.parametrize("vb,kb", [(3, 3), (4, 3)])
+def test_decode_matrix_core_matches_vector_alu(gpu_lib, monkeypatch, vb, kb, G):
+    """3-bit keys (with 3- or 4-bit values) decode on the matrix cores at one split and
+    G <= 8 (the codes widened to the 4-bit kernel's layouts); the vector-ALU kernel
+    (FQ_DECODE_KERNEL=valu) computes the same function. Both against the oracle and
+    within 1e-4 of each other, on ragged lengths over many pages."""
+    w, inp = parity.small_workload(3, 2 * G, 2, [1, 600, 1500], 1504, bits=vb, seed=350 + G + vb)
+    t = parity.torch_inputs(inp, w.dtype)
+    oq = parity.oracle_quantizer(vb, key_bits=kb)
+    qz = fq.Quantizer(vb, 128, fq.ROT_HAAR, 1, 2, 128, key_bits=kb)
+    host = parity.oracle_cache(inp, oq)
+    cache = _cache(inp, w, kb)
+    parity.upload_cache(host, cache)
+    out_m = fq.decode(qz, cache, t["q"], t["bt"], t["lens"], 1500, num_splits=1).cpu().numpy()
+    monkeypatch.setenv("FQ_DECODE_KERNEL", "valu")
+    out_v = fq.decode(qz, cache, t["q"], t["bt"], t["lens"], 1500, num_splits=1).cpu().numpy()
+    monkeypatch.delenv("FQ_DECODE_KERNEL")
+    ref = parity.oracle_decode(inp, host, oq)
+    assert np.max(np.abs(out_m - ref)) <= parity.DECODE_TOL
+    assert np.max(np.abs(out_v - ref)) <= parity.DECODE_TOL
+    assert np.max(np.abs(out_m - out_v)) <= 1e-4
 
 
 @pytest.mark.parametrize("vb,kb", WIDTHS)
