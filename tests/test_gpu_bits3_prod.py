@@ -101,6 +101,39 @@ def test_decode_matrix_core_matches_vector_alu(gpu_lib, monkeypatch, vb, kb, G):
     assert np.max(np.abs(out_m - out_v)) <= 1e-4
 
 
+@pytest.mark.parametrize("vb,kb", [(3, 3), (4, 3)])
+def test_window_and_prefill(gpu_lib, vb, kb):
+    """The residual window's decode (a 32-token bf16 window) and a causal prefill (every
+    query token a decode of its prefix: 3-bit codes take the per-query path) on 3-bit
+    keys, against oracle/window.py and oracle/prefill.py."""
+    from oracle import prefill, window
+    w, inp = parity.small_workload(2, 8, 2, [300, 77], 304, bits=vb, seed=360 + vb)
+    t = parity.torch_inputs(inp, w.dtype)
+    oq = parity.oracle_quantizer(vb, key_bits=kb)
+    qz = fq.Quantizer(vb, 128, fq.ROT_HAAR, 1, 2, 128, key_bits=kb)
+    host = parity.oracle_cache(inp, oq)
+    cache = _cache(inp, w, kb)
+    parity.upload_cache(host, cache)
+    g = torch.Generator(device="cuda").manual_seed(vb)
+    wk = torch.randn((2, 32, 2, 128), generator=g, device="cuda").to(torch.bfloat16)
+    wv = torch.randn((2, 32, 2, 128), generator=g, device="cuda").to(torch.bfloat16)
+    wl = [32, 9]
+    out = fq.decode_window(qz, cache, t["q"], t["bt"], t["lens"], 300, wk, wv,
+                           torch.tensor(wl, dtype=torch.int32, device="cuda")).cpu().numpy()
+    ref = window.decode_with_window(inp["q"], host, inp["block_tables"], inp["seq_lens"], oq["levels"], oq["pi"],
+                                    oq["s"], vb, wk.float().cpu().numpy(), wv.float().cpu().numpy(), wl,
+                                    key_levels32=oq["key_levels"], key_bits=kb)
+    assert np.max(np.abs(out - ref)) <= parity.DECODE_TOL
+    L = 300
+    q = torch.randn((L, 8, 128), generator=g, device="cuda").to(torch.bfloat16)
+    seq, lens = [0] * L, list(range(1, L + 1))
+    outp = fq.prefill(qz, cache, q, torch.tensor(seq, dtype=torch.int32, device="cuda"),
+                      torch.tensor(lens, dtype=torch.int32, device="cuda"), t["bt"], L).cpu().numpy()
+    refp = prefill.prefill_rotated(q.float().cpu().numpy(), seq, lens, host, inp["block_tables"], oq["levels"],
+                                   oq["pi"], oq["s"], vb, key_levels32=oq["key_levels"], key_bits=kb)
+    assert np.max(np.abs(outp - refp)) <= parity.DECODE_TOL
+
+
 @pytest.mark.parametrize("vb,kb", WIDTHS)
 def test_decode_wht_and_mse_only_keys(gpu_lib, vb, kb):
     w, inp = parity.small_workload(2, 8, 2, [700, 64], 704, bits=vb, seed=330 + vb + kb)
