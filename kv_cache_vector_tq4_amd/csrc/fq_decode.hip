@@ -2156,13 +2156,13 @@ int launch_decode(void* stream, const fq_quantizer& q, const fq_cache& c, const 
   // vector-ALU kernel.
   const bool shared4 = a.kbits == q.bits && key_levels_of(q) == q.levels && q.bits != 3;
   // 3-bit keys with 4-bit values (k3 = 1), or 3-bit keys and values of one codebook
-  // (k3 = 2): the matrix-core kernel on the single-launch path (one split, G <= 8),
-  // widened to its 4-bit layouts; otherwise the vector-ALU kernel
+  // (k3 = 2): the matrix-core kernels (G <= 8), widened to their 4-bit layouts;
+  // otherwise the vector-ALU kernel
   const int k3 = a.kbits == 3 && q.bits == 4 ? 1 : a.kbits == 3 && q.bits == 3 && key_levels_of(q) == q.levels ? 2 : 0;
   const bool force_valu = impl && std::strcmp(impl, "valu") == 0;
   const bool v1 = impl && std::strcmp(impl, "mfma_v1") == 0;
   const bool unfused = std::getenv("FQ_DECODE_UNFUSED") != nullptr;
-  const bool k3_mfma = k3 > 0 && !v1 && num_splits == 1 && !unfused && a.group <= 8;
+  const bool k3_mfma = k3 > 0 && !v1 && a.group <= 8;
   const bool valu = (!shared4 && !k3_mfma) || force_valu;
   const int slots = (!valu && !v1) ? (a.group <= 4 ? 4 : a.group <= 8 ? 2 : 0) : 0;
   dim3 grid(num_splits, c.num_kv_heads, batch);
@@ -2230,7 +2230,16 @@ int launch_decode(void* stream, const fq_quantizer& q, const fq_cache& c, const 
 #undef FQ_ONLY
     return static_cast<int>(hipGetLastError());
   }
-  if (slots == 4 && q.bits == 4)
+  // 3-bit keys: the key pair table makes 96 KB of LDS, one work-group per CU
+  if (k3 == 1 && slots == 4)
+    hipLaunchKernelGGL((packed_decode_kernel<4, 4, PK4_WAVES, PK4_RING, 1, -1, false, 1>), grid, dim3(PK4_WAVES * 64), 0, st, a);
+  else if (k3 == 1 && slots == 2)
+    hipLaunchKernelGGL((packed_decode_kernel<4, 2, PK2_WAVES, PK2_RING, 2, -1, false, 1>), grid, dim3(PK2_WAVES * 64), 0, st, a);
+  else if (k3 == 2 && slots == 4)
+    hipLaunchKernelGGL((packed_decode_kernel<4, 4, PK4_WAVES, PK4_RING, 1, -1, false, 2>), grid, dim3(PK4_WAVES * 64), 0, st, a);
+  else if (k3 == 2 && slots == 2)
+    hipLaunchKernelGGL((packed_decode_kernel<4, 2, PK2_WAVES, PK2_RING, 2, -1, false, 2>), grid, dim3(PK2_WAVES * 64), 0, st, a);
+  else if (slots == 4 && q.bits == 4)
     hipLaunchKernelGGL((packed_decode_kernel<4, 4, PK4_WAVES, PK4_RING, PK4_OCC, -1>), grid, dim3(PK4_WAVES * 64), 0, st, a);
   else if (slots == 2 && q.bits == 4)
     hipLaunchKernelGGL((packed_decode_kernel<4, 2, PK2_WAVES, PK2_RING, PK2_OCC, -1>), grid, dim3(PK2_WAVES * 64), 0, st, a);
