@@ -277,8 +277,9 @@ fq_status fq_decode_workspace_size(int batch, int num_q_heads, int num_kv_heads,
  * The context is cut into num_splits chunks of whole 16-token blocks; each
  * chunk keeps a running max / sum / weighted sum, merged by log-sum-exp.
  * Kernels: with G <= 8 the matrix cores take 2- or 4-bit codes of one shared
- * codebook, 3-bit keys with 4-bit values, and 3-bit keys and values of one
- * codebook; every other case runs the vector-ALU split kernel.
+ * codebook and every width pair with 3-bit codes (3-bit keys with 3- or 4-bit
+ * values, 2-bit keys with 3-bit values); groups of 16 with 3-bit codes run the
+ * vector-ALU split kernel.
  *
  *  q             device [batch][num_q_heads][d], FQ_F32 or FQ_BF16.
  *  block_tables  device int32 [batch][max_blocks_per_seq].

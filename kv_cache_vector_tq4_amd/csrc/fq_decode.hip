@@ -1377,17 +1377,27 @@ __device__ __forceinline__ uint32_t nibbles_of3(uint32_t x) {
   const uint32_t t = pairs_of3(x);
   return (t & 0x07070707u) | ((t & 0x38383838u) << 1);
 }
+// Eight 2-bit codes (16 bits) as the same pair bytes (code 2k + 8 x code 2k+1).
+__device__ __forceinline__ uint32_t pairs_of2(uint32_t x) {
+  const uint32_t t = (x & 0xFu) | ((x & 0xF0u) << 4) | ((x & 0xF00u) << 8) | ((x & 0xF000u) << 12);
+  return (t & 0x03030303u) | ((t & 0x0C0C0C0Cu) << 1);
+}
 
 // Loads one page; rec0 = first record of the page (wave-uniform), so every
 // address is a uniform base plus a fixed 32-bit lane offset.
-// K3 = 1: 3-bit key codes (kc as 6-bit pair bytes); K3 = 2: 3-bit values as well
-// (vc as 4-bit nibbles). The 4-bit path's layouts otherwise.
+// Key / value widths of the widened forms of the 4-bit path: K3 = 1 3-bit keys,
+// 4-bit values; K3 = 2 3-bit keys and values; K3 = 3 2-bit keys, 3-bit values.
+constexpr int k3_key_bits(int k3) { return k3 == 3 ? 2 : 3; }
+constexpr bool k3_values3(int k3) { return k3 >= 2; }
+
+// K3 != 0: key codes as 6-bit pair bytes (a table of their own), 3-bit values as
+// 4-bit nibbles. The 4-bit path's layouts otherwise.
 template <int BITS, int K3 = 0>
 __device__ __forceinline__ void pk_load(const DecodeArgs& a, int64_t rec0, int n, const PkLane& o,
                                         const float* gptr, const uint8_t* sgn_base, PkPage<BITS>& d) {
-  static_assert(K3 == 0 || BITS == 4, "3-bit codes take the 4-bit layouts");
-  constexpr int CBK = K3 ? 48 : D * BITS / 8;   // key code bytes per vector
-  constexpr int CB = K3 == 2 ? 48 : D * BITS / 8;  // value code bytes per vector
+  static_assert(K3 == 0 || BITS == 4, "widened codes take the 4-bit layouts");
+  constexpr int CBK = K3 ? 16 * k3_key_bits(K3) : D * BITS / 8;     // key code bytes per vector
+  constexpr int CB = k3_values3(K3) ? 48 : D * BITS / 8;           // value code bytes per vector
   // The page's field bases are uniform: pinned in scalar registers, every load is a
   // scalar base plus the lane's 32-bit offset (no 64-bit vector address adds).
   typedef const __attribute__((address_space(1))) uint8_t* gb8;
@@ -1403,7 +1413,15 @@ __device__ __forceinline__ void pk_load(const DecodeArgs& a, int64_t rec0, int n
   asm volatile("" : "+v"(okc), "+v"(osg), "+v"(ovc));
   // the 4-bit codes and sign words are read once per step: non-temporal loads
   // (3 % faster at the batch-32 shape, same bits)
-  if constexpr (K3 != 0) {
+  if constexpr (K3 == 3) {
+    // dims 32g .. 32g+31: 64 bits, four 16-bit runs of eight 2-bit codes
+    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+    const u32x2 k = __builtin_nontemporal_load(reinterpret_cast<const __attribute__((address_space(1))) u32x2*>(kcb + okc));
+    d.kc[0] = pairs_of2(k.x & 0xFFFFu);
+    d.kc[1] = pairs_of2(k.x >> 16);
+    d.kc[2] = pairs_of2(k.y & 0xFFFFu);
+    d.kc[3] = pairs_of2(k.y >> 16);
+  } else if constexpr (K3 != 0) {
     // dims 32g .. 32g+31: 96 bits, four 24-bit runs of eight codes
     typedef uint32_t u32x3 __attribute__((ext_vector_type(3)));
     const u32x3 k = __builtin_nontemporal_load(reinterpret_cast<const __attribute__((address_space(1))) u32x3*>(kcb + okc));
@@ -1430,7 +1448,7 @@ __device__ __forceinline__ void pk_load(const DecodeArgs& a, int64_t rec0, int n
   d.vn = vnb[n];
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
-    if constexpr (K3 == 2) {
+    if constexpr (k3_values3(K3)) {
       // dims 8n .. 8n+7 at bit 24n of the record: the dword at ovc and the next one
       // (kept inside the 48-byte record: it is needed only when the run crosses it)
       typedef const __attribute__((address_space(1))) uint32_t* gu32;
@@ -1478,8 +1496,10 @@ __global__ void __launch_bounds__(WAVES * 64, OCC) packed_decode_kernel(DecodeAr
   static_assert(WAVES * 64 >= 256, "the table stage takes 256 threads");
   constexpr int CB = D * BITS / 8;  // code bytes per vector
   // K3 = 1: 3-bit keys (their own 64-entry pair table), 4-bit values; K3 = 2: 3-bit
-  // keys and values (the values widened to the 4-bit table's layout)
-  static_assert(K3 == 0 || BITS == 4, "3-bit codes take the 4-bit path");
+  // keys and values (the values widened to the 4-bit table's layout); K3 = 3: 2-bit
+  // keys (the pair table), 3-bit values
+  static_assert(K3 == 0 || BITS == 4, "widened codes take the 4-bit path");
+  constexpr int KW = K3 ? k3_key_bits(K3) : BITS;  // key code width
   constexpr bool BSIGN = ONLY && K3 == 0;  // byte-indexed sign table (one work-group per CU)
   constexpr int PRO = RING - 1;  // pages requested ahead of the loop
   __shared__ __align__(16) uint8_t s_lds[BSIGN ? PK_LDS_BYTES_F : K3 ? PK_KTAB_BASE + PK_KTAB_BYTES : PK_LDS_BYTES];
@@ -1539,9 +1559,9 @@ __global__ void __launch_bounds__(WAVES * 64, OCC) packed_decode_kernel(DecodeAr
     return (static_cast<int64_t>(blk) * a.hkv + kvh) * FQ_BLOCK;
   };
   PkLane lo;
-  lo.kc = static_cast<uint32_t>(K3 ? n * 48 + 12 * g : n * CB + 4 * BITS * g);
+  lo.kc = static_cast<uint32_t>(K3 ? n * 16 * KW + 4 * KW * g : n * CB + 4 * BITS * g);
   lo.sg = static_cast<uint32_t>(n * 16 + 4 * g);
-  lo.vc = static_cast<uint32_t>(K3 == 2 ? 4 * g * 48 + ((3 * n) & ~3) : 4 * g * CB + BITS * n);
+  lo.vc = static_cast<uint32_t>(k3_values3(K3) ? 4 * g * 48 + ((3 * n) & ~3) : 4 * g * CB + BITS * n);
   lo.vc2 = static_cast<uint32_t>(4 * g * 48 + min(((3 * n) & ~3) + 4, 44));
   lo.vsh = static_cast<uint32_t>(((3 * n) & 3) * 8);
 
@@ -1555,7 +1575,7 @@ __global__ void __launch_bounds__(WAVES * 64, OCC) packed_decode_kernel(DecodeAr
   float lv[BITS == 4 ? 2 : 4] = {};
   float klv[2] = {0.f, 0.f};  // 3-bit keys: levels of pair entry tid < 64
   if (tid < 256) {
-    if constexpr (K3 == 2) {  // 3-bit values: nibbles 8 .. 15 never occur
+    if constexpr (k3_values3(K3)) {  // 3-bit values: nibbles 8 .. 15 never occur
       lv[0] = (tid & 15) < 8 ? a.levels[tid & 7] : 0.f;
       lv[1] = (tid >> 4) < 8 ? a.levels[(tid >> 4) & 7] : 0.f;
     } else if constexpr (BITS == 4) {
@@ -1567,9 +1587,10 @@ __global__ void __launch_bounds__(WAVES * 64, OCC) packed_decode_kernel(DecodeAr
     }
   }
   if constexpr (K3 != 0) {
-    if (tid < 64) {
-      klv[0] = a.klevels[tid & 7];
-      klv[1] = a.klevels[tid >> 3];
+    if (tid < 64) {  // pair entry (c0, c1) = (tid % 8, tid / 8); 2-bit keys use c < 4
+      constexpr int NL = 1 << KW;
+      klv[0] = (tid & 7) < NL ? a.klevels[(tid & 7) & (NL - 1)] : 0.f;
+      klv[1] = (tid >> 3) < NL ? a.klevels[(tid >> 3) & (NL - 1)] : 0.f;
     }
   }
   // ---- query operands. With two heads per lane (SLOTS 2) registers are short, so
@@ -1694,7 +1715,7 @@ __global__ void __launch_bounds__(WAVES * 64, OCC) packed_decode_kernel(DecodeAr
       *reinterpret_cast<uint2*>(s_lds + PK_SIGN_BASE + idx * 8) = make_uint2(w[0], w[1]);
     }
     __syncthreads();
-    if constexpr (K3 != 0) {  // the 3-bit keys' pair table: 64 entries x 32 copies
+    if constexpr (K3 != 0) {  // the keys' pair table: 64 entries x 32 copies
       for (int idx = tid; idx < 64 * 32; idx += NT)
         *reinterpret_cast<uint2*>(s_lds + PK_KTAB_BASE + idx * 8) = stage[256 + (idx >> 5)];
     }
@@ -2155,10 +2176,10 @@ int launch_decode(void* stream, const fq_quantizer& q, const fq_cache& c, const 
   // 4-bit codebook for both. 3-bit codes and keys of their own width take the
   // vector-ALU kernel.
   const bool shared4 = a.kbits == q.bits && key_levels_of(q) == q.levels && q.bits != 3;
-  // 3-bit keys with 4-bit values (k3 = 1), or 3-bit keys and values of one codebook
-  // (k3 = 2): the matrix-core kernels (G <= 8), widened to their 4-bit layouts;
-  // otherwise the vector-ALU kernel
-  const int k3 = a.kbits == 3 && q.bits == 4 ? 1 : a.kbits == 3 && q.bits == 3 && key_levels_of(q) == q.levels ? 2 : 0;
+  // 3-bit keys with 4-bit values (k3 = 1), 3-bit keys and values (k3 = 2), 2-bit keys
+  // with 3-bit values (k3 = 3): the matrix-core kernels (G <= 8), widened to their
+  // 4-bit layouts (keys through a pair table of their own codebook)
+  const int k3 = a.kbits == 3 && q.bits == 4 ? 1 : a.kbits == 3 && q.bits == 3 ? 2 : a.kbits == 2 && q.bits == 3 ? 3 : 0;
   const bool force_valu = impl && std::strcmp(impl, "valu") == 0;
   const bool v1 = impl && std::strcmp(impl, "mfma_v1") == 0;
   const bool unfused = std::getenv("FQ_DECODE_UNFUSED") != nullptr;
@@ -2186,6 +2207,7 @@ int launch_decode(void* stream, const fq_quantizer& q, const fq_cache& c, const 
   } while (0)
     if (k3 == 1) { if (slots == 4) FQ_FUSED_DT(4, 4, 1); else FQ_FUSED_DT(4, 2, 1); }
     else if (k3 == 2) { if (slots == 4) FQ_FUSED_DT(4, 4, 2); else FQ_FUSED_DT(4, 2, 2); }
+    else if (k3 == 3) { if (slots == 4) FQ_FUSED_DT(4, 4, 3); else FQ_FUSED_DT(4, 2, 3); }
     else if (q.bits == 4 && slots == 4) FQ_FUSED_DT(4, 4, 0);
     else if (q.bits == 4) FQ_FUSED_DT(4, 2, 0);
     else if (slots == 4) FQ_FUSED_DT(2, 4, 0);
@@ -2223,6 +2245,7 @@ int launch_decode(void* stream, const fq_quantizer& q, const fq_cache& c, const 
                      dim3(pkf_waves(BITS) * 64), 0, st, a)
     if (k3 == 1) { if (slots == 4) FQ_ONLY(4, 4, 1); else FQ_ONLY(4, 2, 1); }
     else if (k3 == 2) { if (slots == 4) FQ_ONLY(4, 4, 2); else FQ_ONLY(4, 2, 2); }
+    else if (k3 == 3) { if (slots == 4) FQ_ONLY(4, 4, 3); else FQ_ONLY(4, 2, 3); }
     else if (q.bits == 4 && slots == 4) FQ_ONLY(4, 4, 0);
     else if (q.bits == 4) FQ_ONLY(4, 2, 0);
     else if (slots == 4) FQ_ONLY(2, 4, 0);
@@ -2230,7 +2253,7 @@ int launch_decode(void* stream, const fq_quantizer& q, const fq_cache& c, const 
 #undef FQ_ONLY
     return static_cast<int>(hipGetLastError());
   }
-  // 3-bit keys: the key pair table makes 96 KB of LDS, one work-group per CU
+  // widened keys: the key pair table makes 96 KB of LDS, one work-group per CU
   if (k3 == 1 && slots == 4)
     hipLaunchKernelGGL((packed_decode_kernel<4, 4, PK4_WAVES, PK4_RING, 1, -1, false, 1>), grid, dim3(PK4_WAVES * 64), 0, st, a);
   else if (k3 == 1 && slots == 2)
@@ -2239,6 +2262,10 @@ int launch_decode(void* stream, const fq_quantizer& q, const fq_cache& c, const 
     hipLaunchKernelGGL((packed_decode_kernel<4, 4, PK4_WAVES, PK4_RING, 1, -1, false, 2>), grid, dim3(PK4_WAVES * 64), 0, st, a);
   else if (k3 == 2 && slots == 2)
     hipLaunchKernelGGL((packed_decode_kernel<4, 2, PK2_WAVES, PK2_RING, 2, -1, false, 2>), grid, dim3(PK2_WAVES * 64), 0, st, a);
+  else if (k3 == 3 && slots == 4)
+    hipLaunchKernelGGL((packed_decode_kernel<4, 4, PK4_WAVES, PK4_RING, 1, -1, false, 3>), grid, dim3(PK4_WAVES * 64), 0, st, a);
+  else if (k3 == 3 && slots == 2)
+    hipLaunchKernelGGL((packed_decode_kernel<4, 2, PK2_WAVES, PK2_RING, 2, -1, false, 3>), grid, dim3(PK2_WAVES * 64), 0, st, a);
   else if (slots == 4 && q.bits == 4)
     hipLaunchKernelGGL((packed_decode_kernel<4, 4, PK4_WAVES, PK4_RING, PK4_OCC, -1>), grid, dim3(PK4_WAVES * 64), 0, st, a);
   else if (slots == 2 && q.bits == 4)

@@ -78,10 +78,10 @@ def test_decode(gpu_lib, vb, kb, G, splits):
 
 
 @pytest.mark.parametrize("G", [1, 2, 4, 8])
-@pytest.mark.parametrize("vb,kb", [(3, 3), (4, 3)])
+@pytest.mark.parametrize("vb,kb", WIDTHS)
 def test_decode_matrix_core_matches_vector_alu(gpu_lib, monkeypatch, vb, kb, G):
-    """3-bit keys (with 3- or 4-bit values) decode on the matrix cores at one split and
-    G <= 8 (the codes widened to the 4-bit kernel's layouts); the vector-ALU kernel
+    """3-bit keys (with 3- or 4-bit values) and 2-bit keys with 3-bit values decode on
+    the matrix cores at G <= 8 (the codes widened to the 4-bit kernel's layouts); the vector-ALU kernel
     (FQ_DECODE_KERNEL=valu) computes the same function. Both against the oracle and
     within 1e-4 of each other, on ragged lengths over many pages."""
     w, inp = parity.small_workload(3, 2 * G, 2, [1, 600, 1500], 1504, bits=vb, seed=350 + G + vb)
@@ -101,7 +101,7 @@ def test_decode_matrix_core_matches_vector_alu(gpu_lib, monkeypatch, vb, kb, G):
     assert np.max(np.abs(out_m - out_v)) <= 1e-4
 
 
-@pytest.mark.parametrize("vb,kb", [(3, 3), (4, 3)])
+@pytest.mark.parametrize("vb,kb", WIDTHS)
 def test_window_and_prefill(gpu_lib, vb, kb):
     """The residual window's decode (a 32-token bf16 window) and a causal prefill (every
     query token a decode of its prefix: 3-bit codes take the per-query path) on 3-bit
