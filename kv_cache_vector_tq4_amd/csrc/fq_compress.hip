@@ -5,12 +5,15 @@
 // "TurboQuant" blog, "Couche 1" (randomized Walsh-Hadamard).
 //
 // Kernels:
-//  * compress_mfma_kernel (large inputs) / compress_split_kernel (up to 1024 tiles):
-//    32 vectors per wave tile; the rotation Y^T = Pi X^T and the QJL projection
-//    P^T = S R^T run on the matrix cores (Pi as bf16 hi + lo, S and the residual as
-//    fp16 hi + lo), with Pi's rows fed in an order that leaves 64 consecutive
-//    coordinates of one vector in each lane, so the norm, the boundary search, the
-//    packing, gamma and the sign packing are lane-local.
+//  * compress16_kernel (large inputs): 16 vectors per wave tile on 16x16x32
+//    matrix-core products, two waves per SIMD; the rotation Y^T = Pi X^T and the
+//    QJL projection P^T = S R^T run on the matrix cores (Pi as bf16 hi + lo, S and
+//    the residual as fp16 hi + lo), with Pi's rows fed in an order that leaves 32
+//    consecutive coordinates of one vector in each lane, so the norm, the boundary
+//    search, the packing, gamma and the sign packing are lane-local.
+//  * compress_split_kernel (up to 1024 tiles, prepared operands) and
+//    compress_mfma_kernel (FQ_COMPRESS_KERNEL=tile32): the same steps on 32-vector
+//    tiles of 32x32x16 products, 64 coordinates per lane.
 //  * compress_direct_kernel, compress_lane_kernel (FQ_COMPRESS_KERNEL=direct /
 //    lane): one wave per tile straight from the prepared fragments, and one
 //    vector per lane on the vector ALU (dense rotation as an outer product over
@@ -539,11 +542,282 @@ __device__ __forceinline__ uint4 pack8(const uint32_t (&u)[8]) {
   return make_uint4(u[0] | (u[1] << 16), u[2] | (u[3] << 16), u[4] | (u[5] << 16), u[6] | (u[7] << 16));
 }
 
+// ---- 16-vector tiles on v_mfma_f32_16x16x32: half a 32-vector tile's registers,
+// so that two waves share each SIMD and overlap one another's vector-ALU and
+// matrix-core phases. Lane l = (q, v) = (l / 16, l % 16) holds coordinates 32q ..
+// 32q + 31 of the tile's vector v. A fragment (T, s) of a 128 x 128 matrix M (row
+// tile T < 8, k-step s < 4): lane (q', r) holds M[row16(T, r)][32q' + 8s + e], e < 8.
+// Row tile T's accumulator then holds coordinates 32q + 4T + i (i < 4) of lane (q,
+// v)'s vector, and k-step s of a B operand takes coordinates 32q' + 8s + e of the
+// lane's own vector: the lane's own 32 coordinates, for the input and the residual.
+constexpr int F16_U4 = 8 * 4 * 64;  // uint4 per matrix (32 KB)
+typedef float f4v __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ int row16(int T, int r) { return 32 * (r >> 2) + 4 * T + (r & 3); }
+
+// Fragments of M (fp32, row-major 128 x 128; null: zeros) as hi / lo halves into
+// dst[0 .. F16_U4) / dst[F16_U4 .. 2 F16_U4): bf16 (BF) or fp16.
+template <bool BF>
+__device__ __forceinline__ void build_frag16(const float* m, uint4* dst, int tid, int nthreads) {
+  for (int idx = tid; idx < F16_U4; idx += nthreads) {
+    const int f = idx >> 6, l = idx & 63;
+    const int T = f >> 2, sk = f & 3, r = l & 15, qp = l >> 4;
+    float xs[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    if (m) {
+      const float4* src = reinterpret_cast<const float4*>(m + row16(T, r) * D + 32 * qp + 8 * sk);
+      const float4 x0 = src[0], x1 = src[1];
+      xs[0] = x0.x; xs[1] = x0.y; xs[2] = x0.z; xs[3] = x0.w;
+      xs[4] = x1.x; xs[5] = x1.y; xs[6] = x1.z; xs[7] = x1.w;
+    }
+    uint32_t hi[8], lo[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      if constexpr (BF) split_bf16(xs[e], hi[e], lo[e]);
+      else split_f16b(xs[e], hi[e], lo[e]);
+    }
+    dst[idx] = make_uint4(hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16), hi[4] | (hi[5] << 16), hi[6] | (hi[7] << 16));
+    dst[F16_U4 + idx] = make_uint4(lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16), lo[4] | (lo[5] << 16), lo[6] | (lo[7] << 16));
+  }
+}
+
+// The input of one 16-vector tile as lane (q, v) loads it: coordinates 32q .. 32q + 31
+// of vector v (bf16: 4 uint4, fp32: 8), and the vector's token, head and slot (-1:
+// not stored). Lanes past the last vector load vector 0 (loads stay unconditional);
+// they store nothing.
+template <int DT>
+struct Tile16In {
+  uint4 raw[DT == FQ_BF16 ? 4 : 8];
+  int64_t t, slot;
+  int hd;
+};
+
+template <int DT>
+__device__ __forceinline__ Tile16In<DT> load_tile16(const CompressArgs& a, int kind, int64_t tile, int lane) {
+  constexpr int esz = DT == FQ_BF16 ? 2 : 4;
+  const int v = lane & 15, q = lane >> 4;
+  const int64_t nvec = a.ntok * a.hkv;
+  const int64_t vid = tile * 16 + v;
+  const bool valid = vid < nvec;
+  const int64_t vl = valid ? vid : 0;
+  Tile16In<DT> in;
+  in.t = static_cast<uint32_t>(vl) / static_cast<uint32_t>(a.hkv);  // vectors per launch < 2^31
+  in.hd = static_cast<int>(vl - in.t * a.hkv);
+  const int64_t slot_t = a.slots[in.t];
+  in.slot = valid ? slot_t : -1;
+  const uint4* base = reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(a.src[kind]) +
+                                                     (in.t * a.tstride + in.hd * a.hstride) * esz + 32 * q * esz);
+#pragma unroll
+  for (int w = 0; w < (DT == FQ_BF16 ? 4 : 8); ++w) in.raw[w] = base[w];
+  return in;
+}
+
+// One wave compresses one tile of 16 vectors of one kind (fpi: Pi fragments, fsm: S
+// fragments for keys): the steps of compress_tile in the 16-vector layout, with half
+// its registers (the key tile fits 256 registers: two waves per SIMD).
+template <int BITS, int DT, bool KEY>
+__device__ __forceinline__ void compress_tile16(const CompressArgs& a, int kind, const Tile16In<DT>& in, int lane,
+                                                const uint4* __restrict__ fpi, const uint4* __restrict__ fsm,
+                                                const QCell* __restrict__ qt, float inv_w, float off) {
+  const int q = lane >> 4;
+  const int64_t t = in.t, slot = in.slot;
+  const int hd = in.hd;
+
+  // ---- coordinates 32q .. 32q+31: k-step s takes 32q + 8s .. +7
+  b8 xb[4];
+  b8 xl[DT == FQ_BF16 ? 1 : 4];
+  float ss = 0.f;
+  if constexpr (DT == FQ_BF16) {
+#pragma unroll
+    for (int sk = 0; sk < 4; ++sk) {
+      const uint4 u = in.raw[sk];
+      const uint32_t w4[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) ss = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf2v, w4[e]),
+                                                                     __builtin_bit_cast(bf2v, w4[e]), ss, false);
+      xb[sk] = __builtin_bit_cast(b8, u);
+    }
+  } else {
+#pragma unroll
+    for (int sk = 0; sk < 4; ++sk) {
+      const float4 f0 = __builtin_bit_cast(float4, in.raw[2 * sk]);
+      const float4 f1 = __builtin_bit_cast(float4, in.raw[2 * sk + 1]);
+      const float xs[8] = {f0.x, f0.y, f0.z, f0.w, f1.x, f1.y, f1.z, f1.w};
+      uint32_t hi[8], lo[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        ss = fmaf(xs[e], xs[e], ss);
+        split_bf16(xs[e], hi[e], lo[e]);
+      }
+      xb[sk] = __builtin_bit_cast(b8, pack8(hi));
+      xl[sk] = __builtin_bit_cast(b8, pack8(lo));
+    }
+  }
+  ss += __shfl_xor(ss, 16);
+  ss += __shfl_xor(ss, 32);
+  const float n = sqrtf(ss);
+  const float inv = n > 0.f ? 1.0f / n : 0.f;
+
+  // ---- rotation: acc[T][i] = (Pi x)[32q + 4T + i]
+  f4v acc[8];
+#pragma unroll
+  for (int T = 0; T < 8; ++T) acc[T] = f4v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int sk = 0; sk < 4; ++sk) {
+#pragma unroll
+    for (int T = 0; T < 8; ++T) {
+      if (T % 4 == 0) __builtin_amdgcn_sched_barrier(0);  // LDS fragments: load next to use
+      const b8 ah = __builtin_bit_cast(b8, fpi[(T * 4 + sk) * 64 + lane]);
+      const b8 al = __builtin_bit_cast(b8, fpi[F16_U4 + (T * 4 + sk) * 64 + lane]);
+      acc[T] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, xb[sk], acc[T], 0, 0, 0);
+      acc[T] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, xb[sk], acc[T], 0, 0, 0);
+      if constexpr (DT != FQ_BF16) acc[T] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, xl[sk], acc[T], 0, 0, 0);
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int T = 0; T < 8; ++T) acc[T] *= inv;
+
+  const int64_t rec = ((slot >> 4) * a.hkv + hd) * FQ_BLOCK + (slot & 15);
+  const bool store = slot >= 0;
+  if (a.dbg_y && store) {
+    float4* dy = reinterpret_cast<float4*>(a.dbg_y + ((kind * a.ntok + t) * a.hkv + hd) * D + 32 * q);
+#pragma unroll
+    for (int T = 0; T < 8; ++T) dy[T] = make_float4(acc[T][0], acc[T][1], acc[T][2], acc[T][3]);
+  }
+
+  // ---- boundary search and packing (coordinate rel = 4T + i of the lane at bit
+  // BITS rel of its BITS dwords); keys keep r = y - level[idx] in acc
+  uint32_t words[BITS];
+#pragma unroll
+  for (int w = 0; w < BITS; ++w) words[w] = 0;
+  auto cell_of = [&](float y) {  // truncation equals floor here (below 0: cell 0 either way)
+    const int c = static_cast<int>(fmaf(y, inv_w, off));
+    return min(max(c, 0), QT_CELLS - 1);
+  };
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {  // groups of 8 coordinates (row tiles 2g, 2g + 1)
+    QCell cq[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) cq[k] = qt[cell_of(acc[2 * g + (k >> 2)][k & 3])];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int T = 2 * g + (k >> 2), i = k & 3, rel = 4 * T + i;
+      const float y = acc[T][i];
+      const bool gt = cq[k].b < y;
+      const uint32_t idx = cq[k].count + (gt ? 1u : 0u);
+      const int bo = BITS * rel;
+      words[bo >> 5] |= idx << (bo & 31);
+      if ((bo & 31) + BITS > 32) words[(bo >> 5) + 1] |= idx >> (32 - (bo & 31));
+      if constexpr (KEY) acc[T][i] = y - (gt ? cq[k].c_hi : cq[k].c_lo);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  if (store) {
+    uint32_t* cd = reinterpret_cast<uint32_t*>(a.codes[kind] + rec * (D * BITS / 8) + 4 * BITS * q);
+    if constexpr (BITS == 4) *reinterpret_cast<uint4*>(cd) = make_uint4(words[0], words[1], words[2], words[3]);
+    else if constexpr (BITS == 2) *reinterpret_cast<uint2*>(cd) = make_uint2(words[0], words[1]);
+    else {
+#pragma unroll
+      for (int w = 0; w < BITS; ++w) cd[w] = words[w];
+    }
+    if (q == 0) a.norm[kind][rec] = n;
+  }
+
+  if constexpr (KEY) {
+    if (!a.qjl_on) return;
+    float rr = 0.f;
+#pragma unroll
+    for (int T = 0; T < 8; ++T)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) rr = fmaf(acc[T][i], acc[T][i], rr);
+    rr += __shfl_xor(rr, 16);
+    rr += __shfl_xor(rr, 32);
+    // B fragments of r: k-step s = coordinates 32q + 8s + e = acc[2s + e / 4][e % 4],
+    // as fp16 hi / lo pairs (truncating conversions; the lo part carries the hi part's
+    // error, r - hi being exact in fp32)
+    uint4 rfh[4], rfl[4];
+#pragma unroll
+    for (int sk = 0; sk < 4; ++sk) {
+      uint32_t hw[4], lw[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float r0 = acc[2 * sk + (e >> 1)][2 * (e & 1)], r1 = acc[2 * sk + (e >> 1)][2 * (e & 1) + 1];
+        const h2v hv = __builtin_amdgcn_cvt_pkrtz(r0, r1);
+        const h2v lv = __builtin_amdgcn_cvt_pkrtz(r0 - static_cast<float>(hv[0]), r1 - static_cast<float>(hv[1]));
+        hw[e] = __builtin_bit_cast(uint32_t, hv);
+        lw[e] = __builtin_bit_cast(uint32_t, lv);
+      }
+      rfh[sk] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+      rfl[sk] = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // p = S r in two halves of row tiles (4 hf .. 4 hf + 3: coordinates 32q + 16 hf ..);
+    // sigma = [p >= 0] is the clear sign bit (an accumulation from +0 never ends at -0)
+    uint32_t ng = 0;
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      f4v pacc[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) pacc[u] = f4v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int sk = 0; sk < 4; ++sk) {
+        __builtin_amdgcn_sched_barrier(0);  // LDS fragments: load next to use
+        const hh8 rh = __builtin_bit_cast(hh8, rfh[sk]);
+        const hh8 rl = __builtin_bit_cast(hh8, rfl[sk]);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int T = 4 * hf + u;
+          const hh8 ah = __builtin_bit_cast(hh8, fsm[(T * 4 + sk) * 64 + lane]);
+          const hh8 al = __builtin_bit_cast(hh8, fsm[F16_U4 + (T * 4 + sk) * 64 + lane]);
+          pacc[u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, rh, pacc[u], 0, 0, 0);
+          pacc[u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, rh, pacc[u], 0, 0, 0);
+          pacc[u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, rl, pacc[u], 0, 0, 0);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ng |= (__float_as_uint(pacc[u][i]) >> 31) << (16 * hf + 4 * u + i);
+      if (store && a.dbg_p) {
+        float4* dp = reinterpret_cast<float4*>(a.dbg_p + (t * a.hkv + hd) * D + 32 * q + 16 * hf);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) dp[u] = make_float4(pacc[u][0], pacc[u][1], pacc[u][2], pacc[u][3]);
+      }
+    }
+    if (store) {
+      *reinterpret_cast<uint32_t*>(a.qjl + rec * (D / 8) + 4 * q) = ~ng;
+      if (q == 0) a.gamma[rec] = n * sqrtf(rr);
+    }
+  }
+}
+
+// Large inputs, 16-vector tiles: work-groups of 8 waves (two per SIMD) loop over
+// tiles with the fragments built in LDS from the fp32 matrices (keys: Pi and S, 128
+// KB, one work-group per CU; values: Pi, 64 KB, two).
+template <int BITS, int DT, bool KEY>
+__global__ void __launch_bounds__(CT_WAVES * 64, 2) compress16_kernel(CompressArgs a, int kind) {
+  __shared__ uint4 s_pi[2 * F16_U4];
+  __shared__ uint4 s_sm[KEY ? 2 * F16_U4 : 1];
+  __shared__ QCell s_qt[QT_CELLS];
+  __shared__ float s_qmap[2];
+  __shared__ float s_bl[32];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  build_frag16<true>(a.pi_rows, s_pi, tid, blockDim.x);
+  if constexpr (KEY) build_frag16<false>(a.qjl_on ? a.smat : nullptr, s_sm, tid, blockDim.x);
+  build_qtable<BITS>(a, s_qt, s_qmap, s_bl, tid, blockDim.x, kind);
+  __syncthreads();
+  const float inv_w = s_qmap[0], off = s_qmap[1];
+  const int64_t ntiles = (a.ntok * a.hkv + 15) / 16;
+  for (int64_t tile = static_cast<int64_t>(blockIdx.x) * CT_WAVES + wave; tile < ntiles;
+       tile += static_cast<int64_t>(gridDim.x) * CT_WAVES)
+    compress_tile16<BITS, DT, KEY>(a, kind, load_tile16<DT>(a, kind, tile, lane), lane, s_pi, s_sm, s_qt, inv_w, off);
+}
+
 // Large inputs: work-groups of 8 waves loop over tiles with the fragments in LDS
 // (copied from the prepared operand buffer, or built from the fp32 matrices).
-// Keys run 4 waves per work-group (their 128 KB of fragments allow one work-group
-// per CU anyway), which leaves each wave the registers of the QJL product: at 8
-// waves (256 registers each) the key tile spills and runs 1.4x slower.
+// 32-vector tiles. Keys run 4 waves per work-group (their 128 KB of fragments allow
+// one work-group per CU anyway), which leaves each wave the registers of the QJL
+// product: at 8 waves (256 registers each) the key tile spills and runs 1.4x slower.
 template <int BITS, int DT, bool KEY>
 __global__ void __launch_bounds__((KEY ? 4 : CT_WAVES) * 64) compress_mfma_kernel(CompressArgs a, int kind) {
   constexpr int WAVES = KEY ? 4 : CT_WAVES;
@@ -845,8 +1119,8 @@ template <int KB, int VB, int DT>
 int launch_mfma(hipStream_t st, const CompressArgs& a) {
   const int64_t nvec = a.ntok * a.hkv;
   const int64_t tiles = (nvec + CT_VEC - 1) / CT_VEC;
+  const char* impl = std::getenv("FQ_COMPRESS_KERNEL");
   if (a.mfma_ops && tiles <= 1024) {
-    const char* impl = std::getenv("FQ_COMPRESS_KERNEL");
     if (KB == VB && KB != 3 && impl && std::strcmp(impl, "direct") == 0)
       hipLaunchKernelGGL((compress_direct_kernel<KB, DT>), dim3(static_cast<unsigned>(tiles), 2), dim3(64), 0, st, a);
     else
@@ -854,16 +1128,27 @@ int launch_mfma(hipStream_t st, const CompressArgs& a) {
                          a);
     return static_cast<int>(hipGetLastError());
   }
-  if (a.src[0]) {
-    const int64_t want = (tiles + 3) / 4;
-    const unsigned g = static_cast<unsigned>(want < 256 ? want : 256);
-    hipLaunchKernelGGL((compress_mfma_kernel<KB, DT, true>), dim3(g), dim3(4 * 64), 0, st, a, 0);
+  if (impl && std::strcmp(impl, "tile32") == 0) {  // the 32-vector tile kernel
+    if (a.src[0]) {
+      const int64_t want = (tiles + 3) / 4;
+      const unsigned g = static_cast<unsigned>(want < 256 ? want : 256);
+      hipLaunchKernelGGL((compress_mfma_kernel<KB, DT, true>), dim3(g), dim3(4 * 64), 0, st, a, 0);
+    }
+    if (a.src[1]) {
+      const int64_t want = (tiles + CT_WAVES - 1) / CT_WAVES;
+      const unsigned g = static_cast<unsigned>(want < 512 ? want : 512);
+      hipLaunchKernelGGL((compress_mfma_kernel<VB, DT, false>), dim3(g), dim3(CT_WAVES * 64), 0, st, a, 1);
+    }
+    return static_cast<int>(hipGetLastError());
   }
-  if (a.src[1]) {
-    const int64_t want = (tiles + CT_WAVES - 1) / CT_WAVES;
-    const unsigned g = static_cast<unsigned>(want < 512 ? want : 512);
-    hipLaunchKernelGGL((compress_mfma_kernel<VB, DT, false>), dim3(g), dim3(CT_WAVES * 64), 0, st, a, 1);
-  }
+  // 16-vector tiles: keys one work-group per CU (LDS), values two
+  const int64_t want = ((nvec + 15) / 16 + CT_WAVES - 1) / CT_WAVES;
+  if (a.src[0])
+    hipLaunchKernelGGL((compress16_kernel<KB, DT, true>), dim3(static_cast<unsigned>(want < 256 ? want : 256)),
+                       dim3(CT_WAVES * 64), 0, st, a, 0);
+  if (a.src[1])
+    hipLaunchKernelGGL((compress16_kernel<VB, DT, false>), dim3(static_cast<unsigned>(want < 512 ? want : 512)),
+                       dim3(CT_WAVES * 64), 0, st, a, 1);
   return static_cast<int>(hipGetLastError());
 }
 

@@ -144,3 +144,49 @@ def test_compress_quantizer_without_qjl_matrix(gpu_lib, prepared):
     dy, _ = fq.compress(qz, cache, t["k"], t["v"], t["slots"], debug=True)
     torch.cuda.synchronize()
     print("near-tie mismatches", parity.check_compress(inp, oq, cache, dy, None))
+
+
+@pytest.mark.parametrize("impl", [None, "tile32"])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("vb,kb", [(4, 4), (3, 3), (2, 2), (4, 3), (3, 2)])
+def test_compress_many_tile_kernels(gpu_lib, monkeypatch, vb, kb, dtype, impl):
+    """The kernels of large inputs (the path without the prepared operand buffer):
+    16-vector tiles on 16x16x32 matrix-core products, two waves per SIMD (default),
+    and 32-vector tiles (FQ_COMPRESS_KERNEL=tile32), on every width pair, bf16 and
+    fp32 inputs, Haar and WHT, ragged lengths spanning several tiles and work-groups,
+    against the oracle."""
+    if impl:
+        monkeypatch.setenv("FQ_COMPRESS_KERNEL", impl)
+    else:
+        monkeypatch.delenv("FQ_COMPRESS_KERNEL", raising=False)
+    w, inp = parity.small_workload(3, 8, 4, [300, 45, 1], 304, dtype=dtype, bits=vb, seed=400 + 10 * vb + kb)
+    t = parity.torch_inputs(inp, w.dtype)
+    for rot in (fq.ROT_HAAR, fq.ROT_WHT):
+        qz = fq.Quantizer(vb, 128, rot, 1, 2, 128, key_bits=kb, prepared=False)
+        oq = parity.oracle_quantizer(vb, rot=rot, key_bits=kb)
+        cache = fq.PagedCache(inp["num_blocks"], 4, 128, vb, 128, key_bits=kb)
+        dy, dp = fq.compress(qz, cache, t["k"], t["v"], t["slots"], debug=True)
+        torch.cuda.synchronize()
+        print(rot, "near-tie mismatches", parity.check_compress(inp, oq, cache, dy, dp))
+
+
+@pytest.mark.parametrize("impl", [None, "tile32"])
+def test_compress_many_tile_kernels_mse_only_and_full_size(gpu_lib, monkeypatch, impl):
+    """The same kernels without QJL fields, and on the whole 4096-token 8B-shaped
+    layer (32768 vectors per kind; sampled tokens of every head)."""
+    if impl:
+        monkeypatch.setenv("FQ_COMPRESS_KERNEL", impl)
+    else:
+        monkeypatch.delenv("FQ_COMPRESS_KERNEL", raising=False)
+    w, inp = parity.small_workload(2, 4, 2, [300, 77], 304, seed=93)
+    t = parity.torch_inputs(inp, w.dtype)
+    qz = fq.Quantizer(4, 128, fq.ROT_HAAR, 1, 2, 0, prepared=False)
+    cache = fq.PagedCache(inp["num_blocks"], 2, 128, 4, 0)
+    dy, _ = fq.compress(qz, cache, t["k"], t["v"], t["slots"], debug=True)
+    torch.cuda.synchronize()
+    parity.check_compress(inp, parity.oracle_quantizer(4), cache, dy, None)
+    w = synth.workload(1)
+    inp = synth.layer_inputs(w)
+    qz, cache, dy, dp, oq, _ = _run(w, inp, prepared=False)
+    tok = np.sort(np.random.default_rng(1).choice(4096, size=256, replace=False))
+    print("near-tie mismatches", parity.check_compress(inp, oq, cache, dy, dp, tokens=tok))
