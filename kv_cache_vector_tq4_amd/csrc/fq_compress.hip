@@ -621,6 +621,16 @@ __device__ __forceinline__ void compress_tile16(const CompressArgs& a, int kind,
   const int q = lane >> 4;
   const int64_t t = in.t, slot = in.slot;
   const int hd = in.hd;
+  // the first rotation fragments are requested before the input is waited for
+  constexpr int RD = 6, QD = 4;  // fragment pairs in flight (rotation, QJL product)
+  uint4 ring[RD][2];
+#pragma unroll
+  for (int d = 0; d < RD; ++d) {
+    const int f = (d % 8) * 4 + d / 8;
+    ring[d][0] = fpi[f * 64 + lane];
+    ring[d][1] = fpi[F16_U4 + f * 64 + lane];
+  }
+  __builtin_amdgcn_sched_barrier(0);
 
   // ---- coordinates 32q .. 32q+31: k-step s takes 32q + 8s .. +7
   b8 xb[4];
@@ -657,23 +667,26 @@ __device__ __forceinline__ void compress_tile16(const CompressArgs& a, int kind,
   const float n = sqrtf(ss);
   const float inv = n > 0.f ? 1.0f / n : 0.f;
 
-  // ---- rotation: acc[T][i] = (Pi x)[32q + 4T + i]
+  // ---- rotation: acc[T][i] = (Pi x)[32q + 4T + i], 32 steps (k-step sk = st / 8, row
+  // tile T = st % 8), each fragment pair read RD steps before its products
   f4v acc[8];
 #pragma unroll
   for (int T = 0; T < 8; ++T) acc[T] = f4v{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int sk = 0; sk < 4; ++sk) {
-#pragma unroll
-    for (int T = 0; T < 8; ++T) {
-      if (T % 4 == 0) __builtin_amdgcn_sched_barrier(0);  // LDS fragments: load next to use
-      const b8 ah = __builtin_bit_cast(b8, fpi[(T * 4 + sk) * 64 + lane]);
-      const b8 al = __builtin_bit_cast(b8, fpi[F16_U4 + (T * 4 + sk) * 64 + lane]);
-      acc[T] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, xb[sk], acc[T], 0, 0, 0);
-      acc[T] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, xb[sk], acc[T], 0, 0, 0);
-      if constexpr (DT != FQ_BF16) acc[T] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, xl[sk], acc[T], 0, 0, 0);
+  for (int st = 0; st < 32; ++st) {
+    const int T = st % 8, sk = st / 8;
+    const b8 ah = __builtin_bit_cast(b8, ring[st % RD][0]);
+    const b8 al = __builtin_bit_cast(b8, ring[st % RD][1]);
+    if (st + RD < 32) {
+      const int f = ((st + RD) % 8) * 4 + (st + RD) / 8;
+      ring[st % RD][0] = fpi[f * 64 + lane];
+      ring[st % RD][1] = fpi[F16_U4 + f * 64 + lane];
     }
+    acc[T] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, xb[sk], acc[T], 0, 0, 0);
+    acc[T] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, xb[sk], acc[T], 0, 0, 0);
+    if constexpr (DT != FQ_BF16) acc[T] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, xl[sk], acc[T], 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
   }
-  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int T = 0; T < 8; ++T) acc[T] *= inv;
 
@@ -725,6 +738,15 @@ __device__ __forceinline__ void compress_tile16(const CompressArgs& a, int kind,
 
   if constexpr (KEY) {
     if (!a.qjl_on) return;
+    // the first QJL fragments are requested before the residual's conversions
+    uint4 qring[QD][2];
+#pragma unroll
+    for (int d = 0; d < QD; ++d) {
+      const int f = (4 * (d / 16) + d % 4) * 4 + d / 4 % 4;
+      qring[d][0] = fsm[f * 64 + lane];
+      qring[d][1] = fsm[F16_U4 + f * 64 + lane];
+    }
+    __builtin_amdgcn_sched_barrier(0);
     float rr = 0.f;
 #pragma unroll
     for (int T = 0; T < 8; ++T)
@@ -751,37 +773,42 @@ __device__ __forceinline__ void compress_tile16(const CompressArgs& a, int kind,
       rfl[sk] = make_uint4(lw[0], lw[1], lw[2], lw[3]);
     }
     __builtin_amdgcn_sched_barrier(0);
-    // p = S r in two halves of row tiles (4 hf .. 4 hf + 3: coordinates 32q + 16 hf ..);
-    // sigma = [p >= 0] is the clear sign bit (an accumulation from +0 never ends at -0)
+    // p = S r in two halves of row tiles (4 hf .. 4 hf + 3: coordinates 32q + 16 hf ..),
+    // 32 steps (hf = st / 16, k-step sk = st / 4 % 4, u = st % 4), each fragment pair
+    // read QD steps before its products; sigma = [p >= 0] is the clear sign bit (an
+    // accumulation from +0 never ends at -0)
     uint32_t ng = 0;
+    f4v pacc[4];
 #pragma unroll
-    for (int hf = 0; hf < 2; ++hf) {
-      f4v pacc[4];
+    for (int st = 0; st < 32; ++st) {
+      const int hf = st / 16, sk = st / 4 % 4, u = st % 4;
+      if (st % 16 == 0)
 #pragma unroll
-      for (int u = 0; u < 4; ++u) pacc[u] = f4v{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int sk = 0; sk < 4; ++sk) {
-        __builtin_amdgcn_sched_barrier(0);  // LDS fragments: load next to use
-        const hh8 rh = __builtin_bit_cast(hh8, rfh[sk]);
-        const hh8 rl = __builtin_bit_cast(hh8, rfl[sk]);
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int T = 4 * hf + u;
-          const hh8 ah = __builtin_bit_cast(hh8, fsm[(T * 4 + sk) * 64 + lane]);
-          const hh8 al = __builtin_bit_cast(hh8, fsm[F16_U4 + (T * 4 + sk) * 64 + lane]);
-          pacc[u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, rh, pacc[u], 0, 0, 0);
-          pacc[u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, rh, pacc[u], 0, 0, 0);
-          pacc[u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, rl, pacc[u], 0, 0, 0);
-        }
+        for (int uu = 0; uu < 4; ++uu) pacc[uu] = f4v{0.f, 0.f, 0.f, 0.f};
+      const hh8 ah = __builtin_bit_cast(hh8, qring[st % QD][0]);
+      const hh8 al = __builtin_bit_cast(hh8, qring[st % QD][1]);
+      if (st + QD < 32) {
+        const int s2 = st + QD;
+        const int f = (4 * (s2 / 16) + s2 % 4) * 4 + s2 / 4 % 4;
+        qring[st % QD][0] = fsm[f * 64 + lane];
+        qring[st % QD][1] = fsm[F16_U4 + f * 64 + lane];
       }
+      const hh8 rh = __builtin_bit_cast(hh8, rfh[sk]);
+      const hh8 rl = __builtin_bit_cast(hh8, rfl[sk]);
+      pacc[u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, rh, pacc[u], 0, 0, 0);
+      pacc[u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, rh, pacc[u], 0, 0, 0);
+      pacc[u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, rl, pacc[u], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      if (st % 16 == 15) {
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
+        for (int uu = 0; uu < 4; ++uu)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) ng |= (__float_as_uint(pacc[u][i]) >> 31) << (16 * hf + 4 * u + i);
-      if (store && a.dbg_p) {
-        float4* dp = reinterpret_cast<float4*>(a.dbg_p + (t * a.hkv + hd) * D + 32 * q + 16 * hf);
+          for (int i = 0; i < 4; ++i) ng |= (__float_as_uint(pacc[uu][i]) >> 31) << (16 * hf + 4 * uu + i);
+        if (store && a.dbg_p) {
+          float4* dp = reinterpret_cast<float4*>(a.dbg_p + (t * a.hkv + hd) * D + 32 * q + 16 * hf);
 #pragma unroll
-        for (int u = 0; u < 4; ++u) dp[u] = make_float4(pacc[u][0], pacc[u][1], pacc[u][2], pacc[u][3]);
+          for (int uu = 0; uu < 4; ++uu) dp[uu] = make_float4(pacc[uu][0], pacc[uu][1], pacc[uu][2], pacc[uu][3]);
+        }
       }
     }
     if (store) {
@@ -815,26 +842,17 @@ __global__ void __launch_bounds__(CT_WAVES * 64, 2) compress16_kernel(CompressAr
 
 // Large inputs: work-groups of 8 waves loop over tiles with the fragments in LDS
 // (copied from the prepared operand buffer, or built from the fp32 matrices).
-// 32-vector tiles. Keys run 4 waves per work-group (their 128 KB of fragments allow
-// one work-group per CU anyway), which leaves each wave the registers of the QJL
-// product: at 8 waves (256 registers each) the key tile spills and runs 1.4x slower.
-template <int BITS, int DT, bool KEY>
-__global__ void __launch_bounds__((KEY ? 4 : CT_WAVES) * 64) compress_mfma_kernel(CompressArgs a, int kind) {
-  constexpr int WAVES = KEY ? 4 : CT_WAVES;
-  __shared__ uint4 s_pi[2 * FRAG_U4];                       // Pi fragments, bf16 hi / lo (64 KB)
-  __shared__ uint4 s_sm[KEY ? 2 * FRAG_U4 : 1];             // S fragments, fp16 hi / lo (64 KB, keys)
-  __shared__ QCell s_qt[QT_CELLS];
-  __shared__ float s_qmap[2];
-  __shared__ float s_bl[32];                                // boundaries [0, 15), levels at [16, 32)
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+// Pi (and for keys S) fragments of 32-vector tiles into LDS: copied from the prepared
+// operand buffer, or built from the fp32 matrices; callers synchronize afterwards.
+template <bool KEY>
+__device__ __forceinline__ void stage_frag32(const CompressArgs& a, uint4* s_pi, uint4* s_sm, int tid, int nthreads) {
   if (a.mfma_ops) {
     const uint4* ops = static_cast<const uint4*>(a.mfma_ops);
-    for (int i = tid; i < 2 * FRAG_U4; i += blockDim.x) s_pi[i] = ops[i];
+    for (int i = tid; i < 2 * FRAG_U4; i += nthreads) s_pi[i] = ops[i];
     if constexpr (KEY)
-      for (int i = tid; i < 2 * FRAG_U4; i += blockDim.x) s_sm[i] = ops[2 * FRAG_U4 + i];
+      for (int i = tid; i < 2 * FRAG_U4; i += nthreads) s_sm[i] = ops[2 * FRAG_U4 + i];
   } else {
-    for (int idx = tid; idx < FRAG_U4; idx += blockDim.x) {
+    for (int idx = tid; idx < FRAG_U4; idx += nthreads) {
       const int f = idx >> 6, l = idx & 63;
       const int T = f >> 3, s = f & 7, r = l & 31, hk = l >> 5;
       const int row = perm_row(T, r);
@@ -864,6 +882,22 @@ __global__ void __launch_bounds__((KEY ? 4 : CT_WAVES) * 64) compress_mfma_kerne
       }
     }
   }
+}
+
+// 32-vector tiles. Keys run 4 waves per work-group (their 128 KB of fragments allow
+// one work-group per CU anyway), which leaves each wave the registers of the QJL
+// product: at 8 waves (256 registers each) the key tile spills and runs 1.4x slower.
+template <int BITS, int DT, bool KEY>
+__global__ void __launch_bounds__((KEY ? 4 : CT_WAVES) * 64) compress_mfma_kernel(CompressArgs a, int kind) {
+  constexpr int WAVES = KEY ? 4 : CT_WAVES;
+  __shared__ uint4 s_pi[2 * FRAG_U4];                       // Pi fragments, bf16 hi / lo (64 KB)
+  __shared__ uint4 s_sm[KEY ? 2 * FRAG_U4 : 1];             // S fragments, fp16 hi / lo (64 KB, keys)
+  __shared__ QCell s_qt[QT_CELLS];
+  __shared__ float s_qmap[2];
+  __shared__ float s_bl[32];                                // boundaries [0, 15), levels at [16, 32)
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  stage_frag32<KEY>(a, s_pi, s_sm, tid, blockDim.x);
   build_qtable<BITS>(a, s_qt, s_qmap, s_bl, tid, blockDim.x, kind);
   __syncthreads();
   const float inv_w = s_qmap[0], off = s_qmap[1];
