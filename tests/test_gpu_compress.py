@@ -51,8 +51,10 @@ def test_compress_mse_only_keys(gpu_lib):
     parity.check_compress(inp, oq, cache, dy, None)
 
 
-def test_compress_zero_and_extreme_vectors(gpu_lib):
-    """n = 0 gives y = 0 (all codes = #{boundaries < 0}); a huge-norm and a one-hot vector."""
+@pytest.mark.parametrize("prepared", [True, False])
+def test_compress_zero_and_extreme_vectors(gpu_lib, prepared):
+    """n = 0 gives y = 0 (all codes = #{boundaries < 0}); a huge-norm and a one-hot vector;
+    through the small-input kernel (prepared operands) and the large-input one."""
     import torch
 
     w, inp = parity.small_workload(1, 2, 2, [16], 16, dtype="f32", seed=5)
@@ -61,7 +63,7 @@ def test_compress_zero_and_extreme_vectors(gpu_lib):
     inp["k"][0, 2, 1] = 0.0
     inp["k"][0, 2, 1, 5] = 3.0
     inp["v"][0, 3, 0] *= 1e6
-    qz, cache, dy, dp, oq, _ = _run(w, inp)
+    qz, cache, dy, dp, oq, _ = _run(w, inp, prepared=prepared)
     parity.check_compress(inp, oq, cache, dy, dp)
     host = parity.cache_to_host(cache)
     s0 = inp["slot_mapping"][0]
