@@ -30,7 +30,9 @@
  *  - Kernel choice depends on the shapes alone, except for three environment
  *    variables read at each call, meant for cross-checks and measurements only:
  *    FQ_COMPRESS_KERNEL = "direct" (small compress calls: one wave per 32-vector
- *    tile instead of four) or "lane" (vector-ALU compress, one vector per lane);
+ *    tile instead of four), "tile32" (large compress calls on 32-vector tiles of
+ *    32x32x16 products instead of 16-vector tiles of 16x16x32) or "lane"
+ *    (vector-ALU compress, one vector per lane);
  *    FQ_DECODE_KERNEL = "valu" (vector-ALU split decode) or "mfma_v1" (the group-16
  *    split kernels for every group size: matrix-core at 4 bits, vector-ALU at 2); FQ_DECODE_UNFUSED (any value:
  *    a one-split decode runs as query preparation + attention launches). Every
