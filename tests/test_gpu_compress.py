@@ -192,3 +192,28 @@ def test_compress_many_tile_kernels_mse_only_and_full_size(gpu_lib, monkeypatch,
     qz, cache, dy, dp, oq, _ = _run(w, inp, prepared=False)
     tok = np.sort(np.random.default_rng(1).choice(4096, size=256, replace=False))
     print("near-tie mismatches", parity.check_compress(inp, oq, cache, dy, dp, tokens=tok))
+
+
+@pytest.mark.parametrize("case", range(4))
+def test_compress_many_tile_random_shapes(gpu_lib, case):
+    """The large-input kernel on seeded random shapes: 1, 2, 3 or 8 KV heads, ragged
+    lengths (tiles straddle tokens and sequences), K and V as strided views of one
+    fused buffer, tokens past each length skipped, every width pair, bf16 or fp32."""
+    rs = np.random.default_rng(700 + case)
+    hkv = [1, 2, 3, 8][case]
+    B = int(rs.integers(1, 4))
+    lens = [int(x) for x in rs.integers(1, 200, size=B)]
+    cap = (max(lens) + 15) // 16 * 16 + 16
+    vb, kb = [(4, 4), (3, 3), (2, 2), (4, 3), (3, 2)][int(rs.integers(0, 5))]
+    dtype = ["bf16", "f32"][case % 2]
+    w, inp = parity.small_workload(B, 2 * hkv, hkv, lens, cap, dtype=dtype, bits=vb, seed=710 + case)
+    t = parity.torch_inputs(inp, dtype)
+    fused = torch.zeros((t["k"].shape[0], 3, hkv, 128), dtype=t["k"].dtype, device="cuda")
+    fused[:, 0] = t["k"]
+    fused[:, 2] = t["v"]
+    qz = fq.Quantizer(vb, 128, fq.ROT_HAAR, 1, 2, 128, key_bits=kb, prepared=False)
+    oq = parity.oracle_quantizer(vb, key_bits=kb)
+    cache = fq.PagedCache(inp["num_blocks"], hkv, 128, vb, 128, key_bits=kb)
+    dy, dp = fq.compress(qz, cache, fused[:, 0], fused[:, 2], t["slots"], debug=True)
+    torch.cuda.synchronize()
+    print(hkv, B, lens, vb, kb, dtype, "near-tie mismatches", parity.check_compress(inp, oq, cache, dy, dp))
