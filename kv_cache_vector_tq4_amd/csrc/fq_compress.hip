@@ -719,8 +719,14 @@ __device__ __forceinline__ void compress_tile16(const CompressArgs& a, int kind,
       const bool gt = cq[k].b < y;
       const uint32_t idx = cq[k].count + (gt ? 1u : 0u);
       const int bo = BITS * rel;
-      words[bo >> 5] |= idx << (bo & 31);
-      if ((bo & 31) + BITS > 32) words[(bo >> 5) + 1] |= idx >> (32 - (bo & 31));
+      if constexpr (BITS == 3) {
+        words[bo >> 5] |= idx << (bo & 31);
+        if ((bo & 31) + BITS > 32) words[(bo >> 5) + 1] |= idx >> (32 - (bo & 31));
+      } else {
+        // codes enter a word from the top in coordinate order, so the first lands in
+        // its lowest bits: w = (w >> BITS) | (idx << (32 - BITS)), one v_alignbit
+        words[bo >> 5] = __builtin_amdgcn_alignbit(idx, words[bo >> 5], BITS);
+      }
       if constexpr (KEY) acc[T][i] = y - (gt ? cq[k].c_hi : cq[k].c_lo);
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -803,7 +809,8 @@ __device__ __forceinline__ void compress_tile16(const CompressArgs& a, int kind,
 #pragma unroll
         for (int uu = 0; uu < 4; ++uu)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) ng |= (__float_as_uint(pacc[uu][i]) >> 31) << (16 * hf + 4 * uu + i);
+          for (int i = 0; i < 4; ++i)  // (ng << 1) | sign, one v_alignbit: bit order reversed below
+            ng = __builtin_amdgcn_alignbit(ng, __float_as_uint(pacc[uu][i]), 31);
         if (store && a.dbg_p) {
           float4* dp = reinterpret_cast<float4*>(a.dbg_p + (t * a.hkv + hd) * D + 32 * q + 16 * hf);
 #pragma unroll
@@ -811,6 +818,7 @@ __device__ __forceinline__ void compress_tile16(const CompressArgs& a, int kind,
         }
       }
     }
+    ng = __builtin_bitreverse32(ng);  // the first coordinate's sign to bit 0
     if (store) {
       *reinterpret_cast<uint32_t*>(a.qjl + rec * (D / 8) + 4 * q) = ~ng;
       if (q == 0) a.gamma[rec] = n * sqrtf(rr);
