@@ -543,10 +543,11 @@ __device__ __forceinline__ uint4 pack8(const uint32_t (&u)[8]) {
 }
 
 // ---- 16-vector tiles on v_mfma_f32_16x16x32: half a 32-vector tile's registers,
-// so that two waves share each SIMD and overlap one another's vector-ALU and
-// matrix-core phases. Lane l = (q, v) = (l / 16, l % 16) holds coordinates 32q ..
-// 32q + 31 of the tile's vector v. A fragment (T, s) of a 128 x 128 matrix M (row
-// tile T < 8, k-step s < 4): lane (q', r) holds M[row16(T, r)][32q' + 8s + e], e < 8.
+// so that two waves share each SIMD and one issues while the other waits on its
+// loads (a SIMD's matrix-core and vector-ALU issue do not overlap). Lane l = (q, v) =
+// (l / 16, l % 16) holds coordinates 32q .. 32q + 31 of the tile's vector v. A fragment
+// (T, s) of a 128 x 128 matrix M (row tile T < 8, k-step s < 4): lane (q', r) holds
+// M[row16(T, r)][32q' + 8s + e], e < 8.
 // Row tile T's accumulator then holds coordinates 32q + 4T + i (i < 4) of lane (q,
 // v)'s vector, and k-step s of a B operand takes coordinates 32q' + 8s + e of the
 // lane's own vector: the lane's own 32 coordinates, for the input and the residual.
