@@ -581,6 +581,23 @@ __device__ __forceinline__ void build_frag16(const float* m, uint4* dst, int tid
   }
 }
 
+// The same fragments gathered from the prepared operand buffer, whose 32-vector
+// layout holds every 8-column run of a row as one uint4 too: row R = 64 a + 16 T' +
+// 4 b + c is row r' = 8 b + 4 a + c of row tile T' there (perm_row), columns 64 h' +
+// 8 s' .. at fragment 8 T' + s', lane 32 h' + r'. ops32 -> hi fragments, the lo ones
+// FRAG_U4 further.
+__device__ __forceinline__ void gather_frag16(const uint4* __restrict__ ops32, uint4* dst, int tid, int nthreads) {
+  for (int idx = tid; idx < F16_U4; idx += nthreads) {
+    const int f = idx >> 6, l = idx & 63;
+    const int T = f >> 2, sk = f & 3, r = l & 15, qp = l >> 4;
+    const int row = row16(T, r), col = 32 * qp + 8 * sk;
+    const int a = row >> 6, t32 = (row >> 4) & 3, b = (row >> 2) & 3, c = row & 3;
+    const int src = (t32 * 8 + ((col >> 3) & 7)) * 64 + (col >> 6) * 32 + (8 * b + 4 * a + c);
+    dst[idx] = ops32[src];
+    dst[F16_U4 + idx] = ops32[FRAG_U4 + src];
+  }
+}
+
 // The input of one 16-vector tile as lane (q, v) loads it: coordinates 32q .. 32q + 31
 // of vector v (bf16: 4 uint4, fp32: 8), and the vector's token, head and slot (-1:
 // not stored). Lanes past the last vector load vector 0 (loads stay unconditional);
@@ -838,8 +855,14 @@ __global__ void __launch_bounds__(CT_WAVES * 64, 2) compress16_kernel(CompressAr
   __shared__ float s_qmap[2];
   __shared__ float s_bl[32];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  build_frag16<true>(a.pi_rows, s_pi, tid, blockDim.x);
-  if constexpr (KEY) build_frag16<false>(a.qjl_on ? a.smat : nullptr, s_sm, tid, blockDim.x);
+  if (a.mfma_ops) {  // prepared: a gather of the operand buffer (Pi, then S: zeros without QJL)
+    const uint4* ops = static_cast<const uint4*>(a.mfma_ops);
+    gather_frag16(ops, s_pi, tid, blockDim.x);
+    if constexpr (KEY) gather_frag16(ops + 2 * FRAG_U4, s_sm, tid, blockDim.x);
+  } else {
+    build_frag16<true>(a.pi_rows, s_pi, tid, blockDim.x);
+    if constexpr (KEY) build_frag16<false>(a.qjl_on ? a.smat : nullptr, s_sm, tid, blockDim.x);
+  }
   build_qtable<BITS>(a, s_qt, s_qmap, s_bl, tid, blockDim.x, kind);
   __syncthreads();
   const float inv_w = s_qmap[0], off = s_qmap[1];

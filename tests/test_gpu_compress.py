@@ -217,3 +217,25 @@ def test_compress_many_tile_random_shapes(gpu_lib, case):
     dy, dp = fq.compress(qz, cache, fused[:, 0], fused[:, 2], t["slots"], debug=True)
     torch.cuda.synchronize()
     print(hkv, B, lens, vb, kb, dtype, "near-tie mismatches", parity.check_compress(inp, oq, cache, dy, dp))
+
+
+@pytest.mark.parametrize("vb,kb,qjl", [(4, 4, 128), (4, 3, 128), (2, 2, 0)])
+def test_compress_large_prepared_equals_derived(gpu_lib, vb, kb, qjl):
+    """Past 1024 tiles of 32 vectors the 16-vector kernel takes its fragments from the
+    prepared operand buffer (a gather) or derives them from the fp32 matrices: both
+    must write the same bytes, and sampled tokens match the oracle. 4200 tokens x 8
+    KV heads (33 600 vectors per kind)."""
+    w, inp = parity.small_workload(1, 32, 8, [4200], 4208, bits=vb, seed=800 + vb + kb)
+    t = parity.torch_inputs(inp, w.dtype)
+    hosts = []
+    for prepared in (True, False):
+        qz = fq.Quantizer(vb, 128, fq.ROT_HAAR, 1, 2, qjl, key_bits=kb, prepared=prepared)
+        cache = fq.PagedCache(inp["num_blocks"], 8, 128, vb, qjl, key_bits=kb)
+        dy, dp = fq.compress(qz, cache, t["k"], t["v"], t["slots"], debug=True)
+        torch.cuda.synchronize()
+        hosts.append(parity.cache_to_host(cache))
+    for name in hosts[0]:
+        assert np.array_equal(hosts[0][name], hosts[1][name]), name
+    oq = parity.oracle_quantizer(vb, key_bits=kb)
+    tok = np.sort(np.random.default_rng(3).choice(4200, size=128, replace=False))
+    print("near-tie mismatches", parity.check_compress(inp, oq, cache, dy, dp if qjl else None, tokens=tok))
