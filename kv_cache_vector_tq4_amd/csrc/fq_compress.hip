@@ -721,10 +721,13 @@ __device__ __forceinline__ void compress_tile16(const CompressArgs& a, int kind,
   uint32_t words[BITS];
 #pragma unroll
   for (int w = 0; w < BITS; ++w) words[w] = 0;
-  auto cell_of = [&](float y) {  // truncation equals floor here (below 0: cell 0 either way)
-    const int c = static_cast<int>(fmaf(y, inv_w, off));
-    return min(max(c, 0), QT_CELLS - 1);
-  };
+  // cell of y: the position y inv_w + off rounded after subtracting half a cell, and
+  // saturated to [0, 255], in one v_cvt_pk_u8_f32 (round to nearest even): floor of
+  // the position, or one less exactly at an integer position, which the table's
+  // half-cell margins cover (a boundary within half a cell below is the uncertain one)
+  const float off_h = off - 0.5f;
+  auto cell_of = [&](float y) { return __builtin_amdgcn_cvt_pk_u8_f32(fmaf(y, inv_w, off_h), 0, 0u); };
+  static_assert(QT_CELLS == 256, "cells are bytes");
 #pragma unroll
   for (int g = 0; g < 4; ++g) {  // groups of 8 coordinates (row tiles 2g, 2g + 1)
     QCell cq[8];
