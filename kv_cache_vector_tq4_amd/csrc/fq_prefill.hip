@@ -29,6 +29,7 @@ typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 typedef float f4 __attribute__((ext_vector_type(4)));
 typedef __bf16 b8 __attribute__((ext_vector_type(8)));
 typedef float f16v __attribute__((ext_vector_type(16)));
+typedef __fp16 h2v __attribute__((ext_vector_type(2)));
 
 // ------------------------------------------------------------ rows x matrix
 // Y[r][i] = sum_k X[r][k] M[i][k] (Y = X M^T) for R rows of 128, on
@@ -423,16 +424,20 @@ __global__ void __launch_bounds__(PT_WAVES * 64, 2) prefill_tile_kernel(PrefillA
     uint32_t ph[2], pl[2];
 #pragma unroll
     for (int i = 0; i < 4; i += 2) {
-      _Float16 hx[2], lx[2];
+      float xv[2];
 #pragma unroll
       for (int k = 0; k < 2; ++k) {
         const bool live_t = sc[i + k] != -INFINITY;
         const float pr = live_t ? __builtin_amdgcn_exp2f(sc[i + k] - m_run) : 0.f;
         l_run += pr;
-        split_f16(live_t ? pr * (vnv[i + k] * v_inv) : 0.f, hx[k], lx[k]);
+        xv[k] = live_t ? pr * (vnv[i + k] * v_inv) : 0.f;
       }
-      ph[i / 2] = h2bits(hx[0], hx[1]);
-      pl[i / 2] = h2bits(lx[0], lx[1]);
+      // fp16 (hi, lo) pairs of the two tokens, each half packed by one conversion
+      // (truncating; the lo part carries the hi part's error, x - hi being exact)
+      const h2v hv = __builtin_amdgcn_cvt_pkrtz(xv[0], xv[1]);
+      const h2v lv = __builtin_amdgcn_cvt_pkrtz(xv[0] - static_cast<float>(hv[0]), xv[1] - static_cast<float>(hv[1]));
+      ph[i / 2] = __builtin_bit_cast(uint32_t, hv);
+      pl[i / 2] = __builtin_bit_cast(uint32_t, lv);
     }
     const h8 a1 = as_h8(ph[0], ph[0], ph[1], ph[1]);
     const h8 a2 = as_h8(pl[0], pl[0], pl[1], pl[1]);
