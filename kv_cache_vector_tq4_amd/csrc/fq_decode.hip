@@ -102,6 +102,7 @@ __device__ __forceinline__ int64_t table_row(const DecodeArgs& a, int b) {
 // fp16 helpers shared by the matrix-core kernels.
 typedef _Float16 h4 __attribute__((ext_vector_type(4)));
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef __fp16 h2v __attribute__((ext_vector_type(2)));
 typedef float f4 __attribute__((ext_vector_type(4)));
 
 constexpr int LEV_SHIFT = 8;        // levels are stored x 2^8 in the tables
@@ -1773,6 +1774,7 @@ __global__ void __launch_bounds__(WAVES * 64, OCC) packed_decode_kernel(DecodeAr
 
   // ---- one page: scores (16 tokens x this lane's heads, -inf where the token is
   // past the split or the page is a stand-in), then softmax, then the value product
+  const int vlim = t1 - t0 - n;  // token n of page p is in the split when 16 p < vlim
   auto score = [&](const PkPage<BITS>& d, int p, bool real, float (&sc)[HL]) {
     // ---- scores: C[(head, slot)][token]; product i covers dims 32g + 4i .. 4i+3
     f4 accM = {0.f, 0.f, 0.f, 0.f}, accQ = {0.f, 0.f, 0.f, 0.f};
@@ -1804,7 +1806,7 @@ __global__ void __launch_bounds__(WAVES * 64, OCC) packed_decode_kernel(DecodeAr
         else accQ = mfma32(qs[i], sop, accQ);
       }
     }
-    const bool valid = real && t0 + p * FQ_BLOCK + n < t1;
+    const bool valid = real && p * FQ_BLOCK < vlim;
     if constexpr (SLOTS == 4) {
       sc[0] = fmaf(accQ[2] + accQ[3], d.gm, (accM[0] + accM[1]) * d.kn) * cf[0];
     } else {
@@ -1857,9 +1859,11 @@ __global__ void __launch_bounds__(WAVES * 64, OCC) packed_decode_kernel(DecodeAr
       const bool live = sc[k] != -INFINITY;
       const float pr = live ? __builtin_amdgcn_exp2f(sc[k] - m_run[k]) : 0.f;
       l_run[k] += pr;
-      _Float16 ph, pl;
-      split_f16(live ? pr * vn : 0.f, ph, pl);  // a norm past the sequence may be anything
-      xp[k] = h2bits(ph, pl);
+      const float x = live ? pr * vn : 0.f;  // a norm past the sequence may be anything
+      // (hi, lo) fp16 pair in two truncating conversions: hi = x rounded toward zero,
+      // lo = the rest (x - hi is exact)
+      const h2v hh = __builtin_amdgcn_cvt_pkrtz(x, 0.f);
+      xp[k] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(x, x - static_cast<float>(hh[0])));
     }
   };
   auto pv = [&](const PkPage<BITS>& d, const uint32_t (&xp)[HL]) {
