@@ -400,11 +400,15 @@ def window_measure(qz, cache, q, bt, lens, slots_np, W, reps, stream):
                                                  workspace=ws1, out=out))
     plain_us = graph_us(lambda: fq.decode(qz, cw, q, bt, lens_c, max_len, num_splits=1, workspace=ws1, out=out))
     append_us = graph_us(app)
+    # the window step: the append and the one-split decode in one call (one launch)
+    step_us = graph_us(lambda: fq.decode_step_window(qz, cw, kn, vn, pos, ev, wk, wv, win_lens, q, bt, lens_c,
+                                                     max_len, num_splits=1, workspace=ws1, out=out))
     del cw
     return {"what": "per layer, batch 32: fq_window_append + fq_decode_attention_window, %d-token bf16 window, "
-                    "the rest of each context compressed" % W,
+                    "the rest of each context compressed; step_us: both as one fq_decode_step_window call" % W,
             "timing": "HIP-graph replays (8 calls per graph; median of %d replays)" % MIN_SAMPLES,
             "window": W, "append_us": append_us, "decode_us_by_splits": per_split,
+            "step_us": step_us, "append_plus_decode_us": append_us + per_split[1],
             "decode_us_empty_window_1_split": empty_us, "plain_decode_us_same_lengths": plain_us}
 
 

@@ -414,6 +414,31 @@ fq_status fq_decode_attention_window(void* stream, const fq_quantizer* quant, co
                                      const void* win_v, int win_cap, const int32_t* win_lens, float* out);
 
 /*
+ * fq_decode_step_window -- one decode step of one layer with the residual window
+ * ("TurboQuant" blog, "Couche 5": the residual window; "FlashQuant" page, "架构设计":
+ * the paged decode): fq_window_append(k_new, v_new, kv_dtype,
+ * positions, evict_slots, win_k, win_v, win_cap) followed by
+ * fq_decode_attention_window over the updated cache and ring, with the same
+ * arguments and results as those two calls in that order (bit-identical; the
+ * caller passes seq_lens and win_lens of the state after the append, e.g. with n
+ * tokens per sequence after it: seq_lens = max(0, n - win_cap), win_lens =
+ * min(n, win_cap)). When the decode resolves to one split, G <= 8 and one 2- or
+ * 4-bit codebook for keys and values: one launch, whose query preparation also
+ * compresses the ring row the new token replaces (the single-vector compression
+ * fq_decode_step uses for its newest token) and then stores the new row in its
+ * ring slot; otherwise the append's launch, then the window decode's launches.
+ * positions, evict_slots: device int64 [batch] as fq_window_append; k_new, v_new
+ * [batch][Hkv][128] contiguous, 8-byte aligned. Workspace: fq_decode_workspace_size
+ * for these sizes. Errors: as fq_window_append and fq_decode_attention_window.
+ */
+fq_status fq_decode_step_window(void* stream, const fq_quantizer* quant, const fq_cache* cache, const void* k_new,
+                                const void* v_new, int kv_dtype, const int64_t* positions, const int64_t* evict_slots,
+                                void* win_k, void* win_v, int win_cap, const int32_t* win_lens, const void* q,
+                                int q_dtype, int batch, int num_q_heads, const int32_t* block_tables,
+                                int max_blocks_per_seq, const int32_t* seq_lens, int max_seq_len, int num_splits,
+                                float scale, void* workspace, size_t workspace_bytes, float* out);
+
+/*
  * fq_prefill_attention -- attention of many query tokens read straight from the
  * compressed cache ("FlashQuant" page, "架构设计": attention with inline
  * decompression for prefill). Query token t (q [num_queries][Hq][128]) belongs to

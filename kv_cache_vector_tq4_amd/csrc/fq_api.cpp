@@ -267,6 +267,13 @@ fq_status decode_checked(void* stream, const fq_quantizer* quant, const fq_cache
     if (!aligned(win->k, 16) || !aligned(win->v, 16) || !aligned(win->lens, 4)) return FQ_ERR_INVALID_ARG;
     if (static_cast<int64_t>(batch) * win->cap * cache->num_kv_heads * FQ_HEAD_DIM >= (int64_t{1} << 40))
       return FQ_ERR_UNSUPPORTED;
+    if (win->positions) {  // the window step's append
+      if (win->new_dtype != FQ_F32 && win->new_dtype != FQ_BF16) return FQ_ERR_INVALID_ARG;
+      if (!win->new_k || !win->new_v || !win->evict_slots) return FQ_ERR_INVALID_ARG;
+      if (!aligned(win->new_k, 8) || !aligned(win->new_v, 8) || !aligned(win->positions, 8) ||
+          !aligned(win->evict_slots, 8))
+        return FQ_ERR_INVALID_ARG;
+    }
   }
   int e = tiled ? fq::launch_prefill_tiled(stream, *quant, *cache, q, q_dtype, batch, num_q_heads, bt_row, seq_lens,
                                            block_tables, max_blocks_per_seq, max_seq_len, scale, workspace, s, out)
@@ -311,6 +318,24 @@ fq_status fq_decode_attention_window(void* stream, const fq_quantizer* quant, co
                                      void* workspace, size_t workspace_bytes, const void* win_k,
                                      const void* win_v, int win_cap, const int32_t* win_lens, float* out) {
   const fq::WindowIn win{win_k, win_v, win_cap, win_lens};
+  return decode_checked(stream, quant, cache, q, q_dtype, batch, num_q_heads, block_tables,
+                        max_blocks_per_seq, seq_lens, max_seq_len, num_splits, scale, workspace,
+                        workspace_bytes, out, nullptr, fq::DECODE_ALL, &win);
+}
+
+fq_status fq_decode_step_window(void* stream, const fq_quantizer* quant, const fq_cache* cache, const void* k_new,
+                                const void* v_new, int kv_dtype, const int64_t* positions, const int64_t* evict_slots,
+                                void* win_k, void* win_v, int win_cap, const int32_t* win_lens, const void* q,
+                                int q_dtype, int batch, int num_q_heads, const int32_t* block_tables,
+                                int max_blocks_per_seq, const int32_t* seq_lens, int max_seq_len, int num_splits,
+                                float scale, void* workspace, size_t workspace_bytes, float* out) {
+  if (!positions) return FQ_ERR_INVALID_ARG;
+  fq::WindowIn win{win_k, win_v, win_cap, win_lens};
+  win.new_k = k_new;
+  win.new_v = v_new;
+  win.new_dtype = kv_dtype;
+  win.positions = positions;
+  win.evict_slots = evict_slots;
   return decode_checked(stream, quant, cache, q, q_dtype, batch, num_q_heads, block_tables,
                         max_blocks_per_seq, seq_lens, max_seq_len, num_splits, scale, workspace,
                         workspace_bytes, out, nullptr, fq::DECODE_ALL, &win);

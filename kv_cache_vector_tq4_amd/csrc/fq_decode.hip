@@ -93,6 +93,12 @@ struct DecodeArgs {
   // the window's append: sequence b's new position (< 0: none); the vector it
   // compresses is ring row b * win_cap + pos % win_cap of knew / vnew
   const int64_t* ring_pos;
+  // the window step (append and decode in one launch): the new K / V rows
+  // [B][Hkv][d] (fp32, or bf16 when wnew_bf16) that take the ring slot pos % win_cap
+  // of win_k / win_v once the row there has been compressed
+  const void* wnew_k;
+  const void* wnew_v;
+  int wnew_bf16;
 };
 
 __device__ __forceinline__ int64_t table_row(const DecodeArgs& a, int b) {
@@ -497,7 +503,8 @@ struct PrepIn {
   float xv;  // newest K / V coordinate (APP)
 };
 
-// RING: no queries; the appended vectors are the window ring's rows (ring_pos).
+// RING: the appended vectors are the window ring's rows (ring_pos); with hn = 0
+// no queries are read.
 template <int DT, int GM, bool APP, bool RING = false>
 __device__ __forceinline__ void prep_issue(const DecodeArgs& a, int kvh, int b, int hb, int hn, int tid,
                                            PrepIn<GM>& in) {
@@ -508,7 +515,7 @@ __device__ __forceinline__ void prep_issue(const DecodeArgs& a, int kvh, int b, 
 #pragma unroll
   for (int i = 0; i < GM / 4; ++i) {
     in.qv[i] = 0.f;
-    if constexpr (RING) continue;
+    if (RING && hn == 0) continue;  // the append alone: no queries
     const int h = kq + 4 * i;
     const int64_t off = row0 + (h < hn ? h : 0) * D + j;
     if constexpr (DT == FQ_BF16)
@@ -1487,7 +1494,10 @@ __device__ __forceinline__ void xcd_pair_map(int hkv, int batch, int& kvh, int& 
 // work-group normalizes and un-rotates its output itself. PREP = the query
 // dtype (>= 0): as -2, and the work-group prepares its own query operands too
 // (prepare_group, in the LDS the code table takes later).
-template <int BITS, int SLOTS, int WAVES, int RING, int OCC, int PREP, bool APP = false, int K3 = 0>
+// APP: 0 nothing appended; 1 each sequence's newest K / V token compressed into its
+// slot (fq_decode_step); 2 the window step: the ring row the new token replaces is
+// compressed into its eviction slot, then the new token takes that ring slot.
+template <int BITS, int SLOTS, int WAVES, int RING, int OCC, int PREP, int APP = 0, int K3 = 0>
 __global__ void __launch_bounds__(WAVES * 64, OCC) packed_decode_kernel(DecodeArgs a) {
   static_assert(BITS == 4 || BITS == 2, "4- or 2-bit codes");
   constexpr bool INPREP = PREP >= 0;  // query operands prepared in-kernel
@@ -1569,8 +1579,17 @@ __global__ void __launch_bounds__(WAVES * 64, OCC) packed_decode_kernel(DecodeAr
   // ---- the query loads (in-kernel preparation) and the wave's first RING - 1
   // pages are requested before any set-up work, in the order they are needed
   PrepIn<PK_PREP_GM> pin;
+  float wnew = 0.f;  // window step: coordinate tid % 128 of the new K (tid < 128) or V row
   if constexpr (INPREP) {
-    if (tid < PQ_THREADS) prep_issue<(PREP >= 0 ? PREP : 0), PK_PREP_GM, APP>(a, kvh, b, 0, G, tid, pin);
+    if (tid < PQ_THREADS) prep_issue<(PREP >= 0 ? PREP : 0), PK_PREP_GM, APP != 0, APP == 2>(a, kvh, b, 0, G, tid, pin);
+    if constexpr (APP == 2) {
+      if (tid < 2 * D) {
+        const int64_t src = (static_cast<int64_t>(b) * a.hkv + kvh) * D + (tid & (D - 1));
+        const void* p = tid < D ? a.wnew_k : a.wnew_v;
+        wnew = a.wnew_bf16 ? __uint_as_float(static_cast<uint32_t>(static_cast<const uint16_t*>(p)[src]) << 16)
+                           : static_cast<const float*>(p)[src];
+      }
+    }
   }
   // codebook levels of the table entry this thread stages (threads < 256)
   float lv[BITS == 4 ? 2 : 4] = {};
@@ -1653,14 +1672,26 @@ __global__ void __launch_bounds__(WAVES * 64, OCC) packed_decode_kernel(DecodeAr
 
   if constexpr (INPREP) {
     uint4* const s_ops = reinterpret_cast<uint4*>(s_lds + PK_PREP_OPS);
-    prepare_group<SLOTS, PK_PREP_GM, APP>(a, kvh, b, 0, G, tid, reinterpret_cast<float*>(s_lds + PK_CODE_BASE),
-                                          s_ops, false, pin);
+    prepare_group<SLOTS, PK_PREP_GM, APP != 0, APP == 2>(a, kvh, b, 0, G, tid,
+                                                         reinterpret_cast<float*>(s_lds + PK_CODE_BASE), s_ops, false,
+                                                         pin);
+    if constexpr (APP == 2) {
+      // The new row takes the ring slot whose row was just compressed: each thread
+      // stores the coordinate it loaded the replaced one of (that load's value went
+      // to LDS inside prepare_group). The window rounds after the page loop read
+      // the ring behind the barriers in between.
+      const int64_t pos = a.ring_pos[b];
+      if (pos >= 0 && tid < 2 * D) {
+        const int64_t dst = ((static_cast<int64_t>(b) * a.win_cap + pos % a.win_cap) * a.hkv + kvh) * D + (tid & (D - 1));
+        const_cast<uint16_t*>(tid < D ? a.win_k : a.win_v)[dst] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(wnew));
+      }
+    }
     __syncthreads();
     operands(s_ops, true);
-    if constexpr (APP) {
+    if constexpr (APP != 0) {
       // A page requested before the append wrote the new token's record is
       // requested again (the barrier above made those stores visible).
-      const int64_t nslot = a.slots[b];
+      const int64_t nslot = APP == 2 && a.ring_pos[b] < 0 ? -1 : a.slots[b];
 #pragma unroll
       for (int k = 0; k < PRO; ++k)
         if (k < my_pages && nslot >= 0 && __builtin_amdgcn_readlane(bt_cur, k) == static_cast<int>(nslot >> 4))
@@ -2192,16 +2223,52 @@ int launch_decode(void* stream, const fq_quantizer& q, const fq_cache& c, const 
   const int slots = (!valu && !v1) ? (a.group <= 4 ? 4 : a.group <= 8 ? 2 : 0) : 0;
   dim3 grid(num_splits, c.num_kv_heads, batch);
   const bool only = slots > 0 && num_splits == 1 && !unfused;
+  const bool wstep = win && win->positions;  // the window step: its append first
+  if (wstep && !(only && phase == DECODE_ALL && !app && k3 == 0)) {
+    // not the single launch: the append's own launch, then the decode with the window
+    int e = launch_window_append(stream, q, c, win->new_k, win->new_v, win->new_dtype, batch, win->positions,
+                                 win->evict_slots, const_cast<void*>(win->k), const_cast<void*>(win->v), win->cap,
+                                 nullptr);
+    if (e != 0) return e;
+  }
   if (only && phase == DECODE_ALL) {
     // one work-group per (KV head, sequence) does everything in one launch
-    // (appending the newest token first, when asked)
+    // (appending the newest token first, or the window step's ring row, when asked)
+    if (wstep && !app && k3 == 0) {
+      // the ring row leaving the window is the appended vector (bf16 rows of the ring)
+      a.knew = win->k;
+      a.vnew = win->v;
+      a.kv_bf16 = 1;
+      a.kv_tstride = static_cast<int64_t>(c.num_kv_heads) * D;
+      a.kv_hstride = D;
+      a.slots = win->evict_slots;
+      a.ring_pos = win->positions;
+      a.wnew_k = win->new_k;
+      a.wnew_v = win->new_v;
+      a.wnew_bf16 = win->new_dtype == FQ_BF16 ? 1 : 0;
+#define FQ_WSTEP(BITS, SL, DT)                                                                                 \
+  hipLaunchKernelGGL((packed_decode_kernel<BITS, SL, pkf_waves(BITS), PKF_RING, PKF_OCC, DT, 2, 0>), grid,     \
+                     dim3(pkf_waves(BITS) * 64), 0, st, a)
+#define FQ_WSTEP_DT(BITS, SL)                     \
+  do {                                            \
+    if (q_dtype == FQ_BF16) FQ_WSTEP(BITS, SL, FQ_BF16); \
+    else FQ_WSTEP(BITS, SL, FQ_F32);              \
+  } while (0)
+      if (q.bits == 4 && slots == 4) FQ_WSTEP_DT(4, 4);
+      else if (q.bits == 4) FQ_WSTEP_DT(4, 2);
+      else if (slots == 4) FQ_WSTEP_DT(2, 4);
+      else FQ_WSTEP_DT(2, 2);
+#undef FQ_WSTEP_DT
+#undef FQ_WSTEP
+      return static_cast<int>(hipGetLastError());
+    }
 #define FQ_FUSED(BITS, SL, DT, K3)                                                                                   \
   do {                                                                                                               \
     if (app)                                                                                                         \
-      hipLaunchKernelGGL((packed_decode_kernel<BITS, SL, pkf_waves(BITS), PKF_RING, PKF_OCC, DT, true, K3>), grid,   \
+      hipLaunchKernelGGL((packed_decode_kernel<BITS, SL, pkf_waves(BITS), PKF_RING, PKF_OCC, DT, 1, K3>), grid,      \
                          dim3(pkf_waves(BITS) * 64), 0, st, a);                                                      \
     else                                                                                                             \
-      hipLaunchKernelGGL((packed_decode_kernel<BITS, SL, pkf_waves(BITS), PKF_RING, PKF_OCC, DT, false, K3>), grid,  \
+      hipLaunchKernelGGL((packed_decode_kernel<BITS, SL, pkf_waves(BITS), PKF_RING, PKF_OCC, DT, 0, K3>), grid,      \
                          dim3(pkf_waves(BITS) * 64), 0, st, a);                                                      \
   } while (0)
 #define FQ_FUSED_DT(BITS, SL, K3)                           \
@@ -2245,7 +2312,7 @@ int launch_decode(void* stream, const fq_quantizer& q, const fq_cache& c, const 
   if (only) {
     // the only split, query operands from the preparation launch
 #define FQ_ONLY(BITS, SL, K3)                                                                                   \
-  hipLaunchKernelGGL((packed_decode_kernel<BITS, SL, pkf_waves(BITS), PKF_RING, PKF_OCC, -2, false, K3>), grid, \
+  hipLaunchKernelGGL((packed_decode_kernel<BITS, SL, pkf_waves(BITS), PKF_RING, PKF_OCC, -2, 0, K3>), grid,     \
                      dim3(pkf_waves(BITS) * 64), 0, st, a)
     if (k3 == 1) { if (slots == 4) FQ_ONLY(4, 4, 1); else FQ_ONLY(4, 2, 1); }
     else if (k3 == 2) { if (slots == 4) FQ_ONLY(4, 4, 2); else FQ_ONLY(4, 2, 2); }

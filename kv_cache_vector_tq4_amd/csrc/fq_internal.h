@@ -75,6 +75,14 @@ struct WindowIn {
   const void* v;
   int cap;
   const int32_t* lens;  // [batch]
+  // the window step (positions non-null): fq_window_append of new_k / new_v
+  // [batch][Hkv][d] (new_dtype) at positions / evict_slots first, in the same launch
+  // when the decode is the single-split one
+  const void* new_k = nullptr;
+  const void* new_v = nullptr;
+  int new_dtype = 0;
+  const int64_t* positions = nullptr;
+  const int64_t* evict_slots = nullptr;
 };
 
 int launch_decode(void* stream, const fq_quantizer& q, const fq_cache& c, const void* qv,

@@ -92,6 +92,13 @@ EXPORTS = {
                                                   ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
                                                   ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p,
                                                   ctypes.c_void_p]),
+    "fq_decode_step_window": (ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(QuantizerT), ctypes.POINTER(CacheT),
+                                             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p,
+                                             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
+                                             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                                             ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p,
+                                             ctypes.c_int, ctypes.c_int, ctypes.c_float, ctypes.c_void_p,
+                                             ctypes.c_size_t, ctypes.c_void_p]),
     "fq_compress": (ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(QuantizerT), ctypes.POINTER(CacheT),
                                    ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int64,
                                    ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p,
@@ -486,6 +493,40 @@ def window_append(quant, cache, k_new, v_new, positions, evict_slots, win_k, win
                                 _ptr(evict_slots), _ptr(win_k), _ptr(win_v), win_k.shape[1], _ptr(workspace),
                                 workspace.numel() * workspace.element_size())
     _check(st, "fq_window_append")
+
+
+def decode_step_window(quant, cache, k_new, v_new, positions, evict_slots, win_k, win_v, win_lens, q, block_tables,
+                       seq_lens, max_seq_len, num_splits=0, scale=None, workspace=None, out=None, stream=None):
+    """fq_decode_step_window: window_append(k_new, v_new, positions, evict_slots, win_k, win_v)
+    then decode_window(q, ...) over the updated cache and ring, as one call (seq_lens and
+    win_lens (int32 [B]) describe the state after the append)."""
+    import torch
+
+    B, Hq, d = q.shape
+    assert q.is_contiguous() and block_tables.dtype == torch.int32 and seq_lens.dtype == torch.int32
+    assert block_tables.is_contiguous() and seq_lens.is_contiguous()
+    for x in (k_new, v_new):
+        assert x.is_contiguous() and x.shape == (B, cache.num_kv_heads, d) and x.dtype == k_new.dtype
+    for x in (positions, evict_slots):
+        assert x.dtype == torch.int64 and x.is_contiguous() and x.numel() == B
+    for x in (win_k, win_v):
+        assert x.dtype == torch.bfloat16 and x.is_contiguous() and x.shape == win_k.shape
+        assert x.shape[0] == B and x.shape[2:] == (cache.num_kv_heads, d)
+    assert win_lens.dtype == torch.int32 and win_lens.is_contiguous() and win_lens.numel() == B
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    need = workspace_bytes(B, Hq, cache.num_kv_heads, d, quant.qjl_dim, max_seq_len, num_splits)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    if out is None:
+        out = torch.empty((B, Hq, d), dtype=torch.float32, device=q.device)
+    st = lib().fq_decode_step_window(_stream(stream), ctypes.byref(quant.struct), ctypes.byref(cache.struct),
+                                     _ptr(k_new), _ptr(v_new), _dtype_code(k_new), _ptr(positions),
+                                     _ptr(evict_slots), _ptr(win_k), _ptr(win_v), win_k.shape[1], _ptr(win_lens),
+                                     _ptr(q), _dtype_code(q), B, Hq, _ptr(block_tables), block_tables.shape[1],
+                                     _ptr(seq_lens), int(max_seq_len), int(num_splits), float(scale),
+                                     _ptr(workspace), workspace.numel() * workspace.element_size(), _ptr(out))
+    _check(st, "fq_decode_step_window")
+    return out
 
 
 def decode_step(quant, cache, k_new, v_new, slot_mapping, q, block_tables, seq_lens, max_seq_len, num_splits=0,

@@ -153,6 +153,30 @@ def test_decode_argument_checks_and_workspace():
     assert call(B=0) == fq.FQ_OK
 
 
+def test_step_window_argument_checks():
+    """fq_decode_step_window: the append's arguments are checked before anything is launched."""
+    L = fq.lib()
+    store, base, qz, cz = _fake_structs(hkv=2)
+    n = fq.workspace_bytes(3, 8, 2, 128, 128, 1000, 1)
+
+    def call(**kw):
+        return L.fq_decode_step_window(None, ctypes.byref(qz), ctypes.byref(cz), kw.get("kn", base),
+                                       kw.get("vn", base), kw.get("kdt", fq.BF16), kw.get("pos", base),
+                                       kw.get("ev", base), kw.get("wk", base), kw.get("wv", base),
+                                       kw.get("cap", 16), base, base, fq.F32, kw.get("B", 3), 8, base, 63, base,
+                                       1000, 1, 0.088, base, n, base)
+    assert call(pos=None) == fq.FQ_ERR_INVALID_ARG
+    assert call(ev=None) == fq.FQ_ERR_INVALID_ARG
+    assert call(kn=None) == fq.FQ_ERR_INVALID_ARG
+    assert call(kdt=7) == fq.FQ_ERR_INVALID_ARG
+    assert call(kn=base + 4) == fq.FQ_ERR_INVALID_ARG   # new rows 8-byte aligned
+    assert call(pos=base + 4) == fq.FQ_ERR_INVALID_ARG  # int64 positions
+    assert call(wk=None) == fq.FQ_ERR_INVALID_ARG
+    assert call(cap=0) == fq.FQ_ERR_INVALID_ARG
+    assert call(cap=4097) == fq.FQ_ERR_INVALID_ARG
+    assert call(B=0) == fq.FQ_OK
+
+
 def test_auto_splits():
     assert fq.auto_splits(1, 8, 4096) == 16
     assert fq.auto_splits(1, 8, 32768) == 64
