@@ -1471,6 +1471,106 @@ __device__ __forceinline__ void pk_load(const DecodeArgs& a, int64_t rec0, int n
   }
 }
 
+// The residual window inside the only split's work-group: wave w takes ring tokens
+// t0 = 16 (w + k WAVES) .. t0 + 15, k = 0, 1, ..., for every query head of the group,
+// so that each window row is read once per work-group. Lane (g, r) = (lane / 16,
+// lane % 16) holds coordinates 8r .. 8r + 7 of K rows t0 + 4i + g (i < 4: each load
+// instruction reads four whole rows) and coordinates 2 lane, 2 lane + 1 of the 16 V
+// rows. Rows at or past the window length n reread row n - 1 and get weight 0.
+struct WinRows {
+  uint4 k[4];
+  uint32_t v[16];
+};
+
+__device__ __forceinline__ void win_rows_load(const DecodeArgs& a, int b, int kvh, int t0, int n, int lane,
+                                              WinRows& w) {
+  const int g = lane >> 4, r = lane & 15;
+  const int64_t row0 = static_cast<int64_t>(b) * a.win_cap;
+  const uint4* kb = reinterpret_cast<const uint4*>(a.win_k);
+  const uint32_t* vb = reinterpret_cast<const uint32_t*>(a.win_v);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int64_t t = row0 + min(t0 + 4 * i + g, n - 1);
+    w.k[i] = kb[(t * a.hkv + kvh) * (D / 8) + r];
+  }
+#pragma unroll
+  for (int u = 0; u < 16; ++u) {
+    const int64_t t = row0 + min(t0 + u, n - 1);
+    w.v[u] = vb[(t * a.hkv + kvh) * (D / 2) + lane];
+  }
+}
+
+// One 16-token round of the window for heads HB .. HB + 3 (those < G): exact fp32
+// scores scale <q_h, k_t> (q_h: fp32 row h of s_q in LDS), a reduce-scatter over the
+// 16 lanes of each row that leaves the (head, token i) entry 4 (h - HB) + i = r in
+// lane (g, r) (token t0 + 4i + g), then per head the round's maximum and sum over its
+// 16 lanes (16 g + 4 (h - HB) + i) by fixed-order butterflies (every lane of a head
+// gets the same bits), the online update of the head's (max m, sum l) -- natural-log
+// units, m = -inf and l = 0 while the head has no token -- and o[h] += p_t v_t in
+// token order. m_lane: running max of this lane's own head.
+template <int HB, int GP>
+__device__ __forceinline__ void win_round(const DecodeArgs& a, const WinRows& w, const float* s_q, int G, int t0, int n,
+                                          int lane, float (&m)[GP], float (&l)[GP], float (&o)[GP][2],
+                                          float& m_lane) {
+  static_assert(HB + 4 <= GP, "four heads per round");
+  const int g = lane >> 4, r = lane & 15;
+  float ps[16];
+#pragma unroll
+  for (int h = 0; h < 4; ++h) {
+    if (HB + h >= G) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ps[h * 4 + i] = 0.f;
+      continue;
+    }
+    const float4 qa = *reinterpret_cast<const float4*>(s_q + (HB + h) * D + 8 * r);
+    const float4 qb = *reinterpret_cast<const float4*>(s_q + (HB + h) * D + 8 * r + 4);
+    const float qv[8] = {qa.x, qa.y, qa.z, qa.w, qb.x, qb.y, qb.z, qb.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t w4[4] = {w.k[i].x, w.k[i].y, w.k[i].z, w.k[i].w};
+      float acc = 0.f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        acc = fmaf(qv[2 * e + 1], __uint_as_float(w4[e] & 0xffff0000u), fmaf(qv[2 * e], __uint_as_float(w4[e] << 16), acc));
+      ps[h * 4 + i] = acc;
+    }
+  }
+  row_reduce_scatter_stage<8, 16>(ps, r);
+  row_reduce_scatter_stage<4, 8>(ps, r);
+  row_reduce_scatter_stage<2, 4>(ps, r);
+  row_reduce_scatter_stage<1, 2>(ps, r);
+  const int hl = HB + (r >> 2), il = r & 3;  // this lane's head and token
+  const float sc = hl < G && t0 + 4 * il + g < n ? ps[0] * a.scale : -INFINITY;
+  float mx = fmaxf(sc, dpp_f<DPP_XOR1>(sc));
+  mx = fmaxf(mx, dpp_f<DPP_XOR2>(mx));
+  mx = fmaxf(mx, __shfl_xor(mx, 16));
+  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  const float mn = fmaxf(m_lane, mx);
+  const float p = sc == -INFINITY ? 0.f : __expf(sc - mn);
+  float ls = p + dpp_f<DPP_XOR1>(p);
+  ls += dpp_f<DPP_XOR2>(ls);
+  ls += __shfl_xor(ls, 16);
+  ls += __shfl_xor(ls, 32);
+  m_lane = mn;
+#pragma unroll
+  for (int h = 0; h < 4; ++h) {
+    if (HB + h >= G) continue;
+    const float m_new = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mn), 4 * h));
+    const float sum = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ls), 4 * h));
+    const float c = m[HB + h] == -INFINITY ? 0.f : __expf(m[HB + h] - m_new);
+    l[HB + h] = fmaf(l[HB + h], c, sum);
+    m[HB + h] = m_new;
+    o[HB + h][0] *= c;
+    o[HB + h][1] *= c;
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {  // token t0 + u = t0 + 4 i + gg, its p in lane 16 gg + 4 h + i
+      const float pu = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(p), 16 * (u & 3) + 4 * h + (u >> 2)));
+      o[HB + h][0] = fmaf(pu, __uint_as_float(w.v[u] << 16), o[HB + h][0]);
+      o[HB + h][1] = fmaf(pu, __uint_as_float(w.v[u] & 0xffff0000u), o[HB + h][1]);
+    }
+  }
+}
+
 // (KV head, sequence) of a work-group of a one-split grid (1, Hkv, B). Work-groups
 // go to the 8 XCDs round-robin by linear id, each XCD with its own L2; this order
 // puts KV heads 2k and 2k+1 of a sequence on the same XCD, one right after the
@@ -1513,7 +1613,12 @@ __global__ void __launch_bounds__(WAVES * 64, OCC) packed_decode_kernel(DecodeAr
   constexpr int KW = K3 ? k3_key_bits(K3) : BITS;  // key code width
   constexpr bool BSIGN = ONLY && K3 == 0;  // byte-indexed sign table (one work-group per CU)
   constexpr int PRO = RING - 1;  // pages requested ahead of the loop
-  __shared__ __align__(16) uint8_t s_lds[BSIGN ? PK_LDS_BYTES_F : K3 ? PK_KTAB_BASE + PK_KTAB_BYTES : PK_LDS_BYTES];
+  // the only split also keeps the residual window's merged part ([8][D] values, [8]
+  // (max, sum)) in a region of its own past the tables
+  constexpr int LDS_MAIN = BSIGN ? PK_LDS_BYTES_F : K3 ? PK_KTAB_BASE + PK_KTAB_BYTES : PK_LDS_BYTES;
+  constexpr int LDS_WIN = ONLY ? 8 * (D + 2) * 4 : 0;
+  __shared__ __align__(16) uint8_t s_lds[LDS_MAIN + LDS_WIN];
+  static_assert(LDS_MAIN + LDS_WIN <= 160 * 1024, "LDS of one CU");
   const uint8_t* const s_code = s_lds + PK_CODE_BASE;
   const uint8_t* const s_ktab = K3 ? s_lds + PK_KTAB_BASE : s_code;  // key code table
   const uint8_t* const s_sign = s_lds + PK_SIGN_BASE;
@@ -1652,6 +1757,18 @@ __global__ void __launch_bounds__(WAVES * 64, OCC) packed_decode_kernel(DecodeAr
     for (int k = 0; k < PRO; ++k)
       pk_load<BITS, K3>(a, rec_of(bt_cur, min(k, min(64, my_pages) - 1)), n, lo, gptr, sgn_base, ring[k]);
   }
+  // The residual window's first round of rows (the only split with in-kernel query
+  // preparation): requested behind the query and page loads, so they arrive during
+  // the preparation and are used right after it.
+  constexpr bool WIN = ONLY && INPREP;
+  constexpr int GPW = 4 * HL;  // heads per wave (>= G)
+  const int nwin = WIN && a.win_k ? min(max(a.win_lens[b], 0), a.win_cap) : 0;
+  // (12-wave work-groups, at 168 registers, request them after the preparation)
+  constexpr bool WPF = WIN && WAVES <= 8;
+  WinRows wr;
+  if constexpr (WPF) {
+    if (16 * wave < nwin) win_rows_load(a, b, kvh, 16 * wave, nwin, lane, wr);
+  }
 
   // the byte-indexed sign table needs no input: built while the loads are in flight
   // (its LDS is not the one in-kernel query preparation uses)
@@ -1681,10 +1798,16 @@ __global__ void __launch_bounds__(WAVES * 64, OCC) packed_decode_kernel(DecodeAr
       // to LDS inside prepare_group). The window rounds after the page loop read
       // the ring behind the barriers in between.
       const int64_t pos = a.ring_pos[b];
+      const uint16_t wb16 = __builtin_bit_cast(uint16_t, static_cast<__bf16>(wnew));
       if (pos >= 0 && tid < 2 * D) {
         const int64_t dst = ((static_cast<int64_t>(b) * a.win_cap + pos % a.win_cap) * a.hkv + kvh) * D + (tid & (D - 1));
-        const_cast<uint16_t*>(tid < D ? a.win_k : a.win_v)[dst] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(wnew));
+        const_cast<uint16_t*>(tid < D ? a.win_k : a.win_v)[dst] = wb16;
       }
+      // and to rows G (K) and G + 1 (V) of the preparation's query rows in LDS (their
+      // readers are done), from where the window rounds take the new token's row
+      if (tid < 2 * D)
+        reinterpret_cast<float*>(s_lds + PK_CODE_BASE)[(G + (tid >= D ? 1 : 0)) * D + (tid & (D - 1))] =
+            __uint_as_float(static_cast<uint32_t>(wb16) << 16);
     }
     __syncthreads();
     operands(s_ops, true);
@@ -1703,6 +1826,94 @@ __global__ void __launch_bounds__(WAVES * 64, OCC) packed_decode_kernel(DecodeAr
       if (tid + k * NT < 8 * 64) reinterpret_cast<uint4*>(s_lds + PK_QOPS_BASE)[tid + k * NT] = qcp[k];
   } else {
     operands(gops, true);
+  }
+
+  // ---- the residual window (rounds of 16 tokens per wave, all heads; the fp32 query
+  // rows are still in LDS): per wave and head its max, sum and weighted values, then
+  // merged over the waves through the code-table area (before the tables take it)
+  // into the window region: values [G][D] and per head (max (natural log), sum)
+  float* const s_wv = reinterpret_cast<float*>(s_lds + LDS_MAIN);  // [G][D]
+  float* const s_wml = s_wv + 8 * D;                                 // [G][2]
+  if constexpr (WIN) {
+    float wm[GPW], wl[GPW], wo[GPW][2];
+#pragma unroll
+    for (int h = 0; h < GPW; ++h) {
+      wm[h] = -INFINITY;
+      wl[h] = 0.f;
+      wo[h][0] = wo[h][1] = 0.f;
+    }
+    if (16 * wave < nwin) {
+      const float* const s_qf = reinterpret_cast<const float*>(s_lds + PK_CODE_BASE);
+      float m_lane[GPW / 4];
+#pragma unroll
+      for (int c = 0; c < GPW / 4; ++c) m_lane[c] = -INFINITY;
+      for (int t0 = 16 * wave; t0 < nwin; t0 += 16 * WAVES) {
+        if (!WPF || t0 != 16 * wave) win_rows_load(a, b, kvh, t0, nwin, lane, wr);
+        if constexpr (APP == 2) {
+          // rows requested before the append stored the new token take its row from LDS
+          const int64_t pos = a.ring_pos[b];
+          const int sl = pos >= 0 ? static_cast<int>(pos % a.win_cap) : -1;
+          if (sl >= t0 && sl < t0 + 16) {
+            const int u = sl - t0, gl = lane >> 4, rl = lane & 15;
+            const float* const nk = s_qf + G * D + 8 * rl;
+            const float* const nv = s_qf + (G + 1) * D + 2 * lane;
+            uint32_t kw[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              kw[e] = (__float_as_uint(nk[2 * e]) >> 16) | (__float_as_uint(nk[2 * e + 1]) & 0xffff0000u);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              if (i == (u >> 2) && gl == (u & 3)) wr.k[i] = make_uint4(kw[0], kw[1], kw[2], kw[3]);
+            const uint32_t vw = (__float_as_uint(nv[0]) >> 16) | (__float_as_uint(nv[1]) & 0xffff0000u);
+#pragma unroll
+            for (int uu = 0; uu < 16; ++uu)
+              if (uu == u) wr.v[uu] = vw;
+          }
+        }
+        win_round<0, GPW>(a, wr, s_qf, G, t0, nwin, lane, wm, wl, wo, m_lane[0]);
+        if constexpr (GPW == 8) win_round<4, GPW>(a, wr, s_qf, G, t0, nwin, lane, wm, wl, wo, m_lane[GPW / 4 - 1]);
+      }
+    }
+    if (nwin > 0) {  // the same for the whole work-group
+      __syncthreads();  // every wave's rounds have read the query rows
+      float* const s_wp = reinterpret_cast<float*>(s_lds + PK_CODE_BASE);  // [WAVES][G][D]
+      float* const s_wq = s_wp + WAVES * G * D;                             // [WAVES][G][2]
+      static_assert(PK_CODE_BASE + WAVES * 8 * (D + 2) * 4 <= PK_STAGE_BASE, "window parts fit the code-table area");
+#pragma unroll
+      for (int h = 0; h < GPW; ++h) {
+        if (h >= G) continue;
+        s_wp[(wave * G + h) * D + 2 * lane] = wo[h][0];
+        s_wp[(wave * G + h) * D + 2 * lane + 1] = wo[h][1];
+        if (lane == 0) {
+          s_wq[2 * (wave * G + h)] = wm[h];
+          s_wq[2 * (wave * G + h) + 1] = wl[h];
+        }
+      }
+      __syncthreads();
+      for (int idx = tid; idx < G * D; idx += NT) {
+        {
+          const int h = idx / D, j = idx % D;
+          float M = -INFINITY;
+          for (int w = 0; w < WAVES; ++w)
+            if (s_wq[2 * (w * G + h) + 1] > 0.f) M = fmaxf(M, s_wq[2 * (w * G + h)]);
+          float o = 0.f, L = 0.f;
+          for (int w = 0; w < WAVES; ++w) {
+            const float lw = s_wq[2 * (w * G + h) + 1];
+            if (lw > 0.f) {
+              const float f = __expf(s_wq[2 * (w * G + h)] - M);
+              o = fmaf(s_wp[(w * G + h) * D + j], f, o);
+              L = fmaf(lw, f, L);
+            }
+          }
+          s_wv[idx] = o;
+          if (j == 0) {
+            s_wml[2 * h] = M;
+            s_wml[2 * h + 1] = L;
+          }
+        }
+      }
+      // the table build below writes the code-table area only behind its own barrier
+    }
   }
 
   // ---- tables: stage the 256 entries once, then fan out conflict-free copies
@@ -1989,17 +2200,6 @@ __global__ void __launch_bounds__(WAVES * 64, OCC) packed_decode_kernel(DecodeAr
     }
   }
 
-  // ---- the residual window (the only split): wave w computes part w / G of query
-  // head w % G's window (rounds of 32 tokens w / G, w / G + C, ..., C = WAVES / G parts
-  // per head; exact scores and values, natural-log max, original frame) once its
-  // pages are done, so the window fills the waves' end spread instead of a launch
-  const int wparts = WAVES / G;  // >= 1 (G <= 8 <= WAVES)
-  float wm = -INFINITY, wl = 0.f, wo0 = 0.f, wo1 = 0.f;
-  if constexpr (ONLY) {
-    if (a.win_k && wave < wparts * G)
-      window_partial(a, static_cast<int64_t>(b) * a.hq + kvh * G + wave % G, lane, wm, wl, wo0, wo1, wave / G,
-                     wparts);
-  }
   // ---- per-wave totals, then merge the waves in LDS
 #pragma unroll
   for (int k = 0; k < HL; ++k) l_run[k] = row_sum(l_run[k]);
@@ -2022,30 +2222,14 @@ __global__ void __launch_bounds__(WAVES * 64, OCC) packed_decode_kernel(DecodeAr
     for (int k = 0; k < HL; ++k)
       s_o[(wave * HP + HL * g + k) * D + dim] = (acc_o[t][2 * k] + acc_o[t][2 * k + 1]) * unscale;
   }
-  // the window's parts: (max, sum) and values per wave (part w / G of head w % G)
-  float* const s_wml = reinterpret_cast<float*>(s_lds) + WAVES * HP * (D + 2) + 5 * PK_PREP_GM * D + PK_PREP_GM;
-  float* const s_wo = s_wml + 2 * WAVES;  // [WAVES][D]
-  static_assert(!ONLY || (WAVES * HP * (D + 2) + 5 * PK_PREP_GM * D + PK_PREP_GM + WAVES * (D + 2)) * 4 <=
-                             static_cast<int>(sizeof(s_lds)), "epilogue fits the LDS");
-  if constexpr (ONLY) {
-    if (a.win_k && wave < wparts * G) {
-      if (lane == 0) {
-        s_wml[2 * wave] = wm;
-        s_wml[2 * wave + 1] = wl;
-      }
-      s_wo[wave * D + 2 * lane] = wo0;
-      s_wo[wave * D + 2 * lane + 1] = wo1;
-    }
-  }
+  static_assert(!ONLY || (WAVES * HP * (D + 2) + 5 * PK_PREP_GM * D + PK_PREP_GM) * 4 <= LDS_MAIN,
+                "epilogue fits the LDS before the window region");
   __syncthreads();
   if constexpr (ONLY) {
     // the only split: o_rot = O / L per head, then out = Pi^T o_rot
     float* const s_or = s_ml + WAVES * HP * 2;  // [G][D]
     float* const s_pp = s_or + PK_PREP_GM * D;  // [4][PK_PREP_GM][D]
     float* const s_fw = s_pp + 4 * PK_PREP_GM * D;  // [G] weight of the residual window's values
-    float* const s_win_v = s_wo + WAVES * D;        // [G][D] the window's merged values
-    static_assert((WAVES * HP * (D + 2) + 5 * PK_PREP_GM * D + PK_PREP_GM + WAVES * (D + 2) + PK_PREP_GM * D) * 4 <=
-                      static_cast<int>(sizeof(s_lds)), "epilogue fits the LDS");
     const int64_t head0 = static_cast<int64_t>(b) * a.hq + kvh * G;
     constexpr float LOG2E = 1.4426950408889634f;
     for (int idx = tid; idx < G * D; idx += WAVES * 64) {
@@ -2054,23 +2238,15 @@ __global__ void __launch_bounds__(WAVES * 64, OCC) packed_decode_kernel(DecodeAr
 #pragma unroll
       for (int w = 0; w < WAVES; ++w)
         if (s_ml[(w * HP + hh) * 2 + 1] > 0.f) M = fmaxf(M, s_ml[(w * HP + hh) * 2]);
-      // a residual window's parts (natural-log maxima) join the softmax: merged here
-      // into one (max, sum) in log2 units and the head's values in s_wo row hh
+      // the residual window's merged part (natural-log max, sum, values) joins the
+      // softmax, its max in log2 units
       float mw = -INFINITY, lwin = 0.f;
-      if (a.win_k) {
-        for (int c = 0; c < wparts; ++c)
-          if (s_wml[2 * (c * G + hh) + 1] > 0.f) mw = fmaxf(mw, s_wml[2 * (c * G + hh)] * LOG2E);
-        float ow = 0.f;
-        for (int c = 0; c < wparts; ++c) {
-          const float lc = s_wml[2 * (c * G + hh) + 1];
-          if (lc > 0.f) {
-            const float f = exp2f(s_wml[2 * (c * G + hh)] * LOG2E - mw);
-            lwin = fmaf(lc, f, lwin);
-            ow = fmaf(s_wo[(c * G + hh) * D + j], f, ow);
-          }
+      if (nwin > 0) {
+        lwin = s_wml[2 * hh + 1];
+        if (lwin > 0.f) {
+          mw = s_wml[2 * hh] * LOG2E;
+          M = fmaxf(M, mw);
         }
-        if (lwin > 0.f) M = fmaxf(M, mw);
-        s_win_v[hh * D + j] = ow;  // own (hh, j) entry only: no other thread reads it before the barrier
       }
       float o = 0.f, L = 0.f;
 #pragma unroll
@@ -2094,7 +2270,7 @@ __global__ void __launch_bounds__(WAVES * 64, OCC) packed_decode_kernel(DecodeAr
       for (int h = kq; h < G; h += 4) {
         float v = (s_pp[(0 * PK_PREP_GM + h) * D + jj] + s_pp[(1 * PK_PREP_GM + h) * D + jj]) +
                   (s_pp[(2 * PK_PREP_GM + h) * D + jj] + s_pp[(3 * PK_PREP_GM + h) * D + jj]);
-        if (a.win_k) v = fmaf(s_fw[h], s_win_v[h * D + jj], v);
+        if (nwin > 0) v = fmaf(s_fw[h], s_wv[h * D + jj], v);
         a.out[(head0 + h) * D + jj] = v;
       }
     }
