@@ -398,10 +398,10 @@ fq_status fq_window_append(void* stream, const fq_quantizer* quant, const fq_cac
  * (device int32 [batch], clamped to [0, win_cap]): one softmax over both, the window's
  * scores scale * <q, k_t> and values exact (fp32 arithmetic on the bf16 rows). When
  * the call resolves to one split and G <= 8: one launch, whose waves compute the
- * window's maximum, sum and weighted values (each query head's window tokens
- * shared out over the work-group's waves) after their pages and whose epilogue
- * folds them into the softmax; otherwise the split path (partials, then the merge,
- * which adds the window). The workspace is
+ * window's maximum, sum and weighted values before their pages (each wave 16 of the
+ * window tokens for every query head of the group; the parts merged in LDS) and
+ * whose epilogue folds them into the softmax; otherwise the split path (partials,
+ * then the merge, which adds the window). The workspace is
  * fq_decode_workspace_size's for these sizes. A caller
  * with n tokens per sequence passes seq_lens = max(0, n - win_cap) and win_lens =
  * min(n, win_cap). Errors: as fq_decode_attention.

@@ -19,9 +19,12 @@
 //  * split_mfma4_kernel / split_attention_kernel: groups of 16 query heads (4-bit
 //    matrix-core / vector ALU), and the vector-ALU cross-check.
 //  * the residual full-precision window ("TurboQuant" blog, "Couche 5"): in the
-//    single-launch kernel the first G waves compute their query head's part of it
-//    after their pages, and the epilogue folds it into the softmax; on the split
-//    path merge_unrotate_kernel computes it per head itself.
+//    single-launch kernel each wave computes 16 of its tokens for every query head
+//    before the page loop (rows requested during the query preparation), the parts
+//    are merged in LDS and the epilogue folds them into the softmax; on the split
+//    path merge_unrotate_kernel computes it per head itself. With the window step
+//    (APP = 2) the same launch first appends: the ring row the new token replaces
+//    is compressed into the cache, then the new row takes its ring slot.
 // A batch entry's block-table row can be remapped (bt_row): fq_prefill_attention
 // runs many query tokens of one sequence as entries sharing its pages.
 #include <hip/hip_runtime.h>
@@ -314,9 +317,8 @@ __device__ __forceinline__ void row_reduce_scatter_stage(float (&v)[N], int r) {
 // reductions, then the lanes turn to coordinates and add up the round's weighted V
 // rows in token order. Each round requests all its K and V rows before using any.
 // m = -inf, l = 0 without tokens.
-// Rounds r0, r0 + rstride, ... of the head's window tokens only (by default all).
 __device__ __forceinline__ void window_partial(const DecodeArgs& a, int64_t hidx, int lane, float& m, float& l,
-                                               float& o0, float& o1, int r0 = 0, int rstride = 1) {
+                                               float& o0, float& o1) {
   constexpr int RT = 32;  // tokens per round
   const int b = static_cast<int>(hidx / a.hq);
   const int kvh = static_cast<int>(hidx - static_cast<int64_t>(b) * a.hq) / a.group;
@@ -345,7 +347,7 @@ __device__ __forceinline__ void window_partial(const DecodeArgs& a, int64_t hidx
   const uint4* kb = reinterpret_cast<const uint4*>(a.win_k) + base / 4;
   const uint32_t* vb = reinterpret_cast<const uint32_t*>(a.win_v) + base;
   const int u_own = 4 * (r >> 1) + g;  // this lane's token of the round
-  for (int t0 = RT * r0; t0 < n; t0 += RT * rstride) {
+  for (int t0 = 0; t0 < n; t0 += RT) {
     uint4 kw[RT / 4];
 #pragma unroll
     for (int i = 0; i < RT / 4; ++i) kw[i] = kb[static_cast<int64_t>(min(t0 + 4 * i + g, n - 1)) * ts4 + r];
