@@ -4,7 +4,8 @@ fq_window_append) against oracle/window.py (through the C ABI).
 * Decode: the oracle's compressed bytes plus a bf16 window; one softmax over both,
   against the oracle to the decode tolerance (1e-3 max-abs), through the split
   kernels and the merge (1, 3 and automatic splits; groups 4, 8 and 16), with empty
-  windows, windows only, and empty sequences.
+  windows, windows only, and empty sequences; a 300-slot ring in the single launch
+  (several 16-token rounds per wave, 4- and 2-bit codes, groups 4 and 8).
 * Append: a run of decode steps. The ring after each append holds exactly the bf16
   of the tokens of the last W positions; the records the append compresses are
   bit-identical to fq_decode_step's append of the same bf16 tokens into a mirror
@@ -174,6 +175,31 @@ def test_append_steps_then_decode(gpu_lib, kv):
     torch.cuda.synchronize()
     inp = {"q": q.float().cpu().numpy(), "block_tables": bt, "seq_lens": seq_lens}
     ref = _oracle(inp, got, oq, wk, wv, wl)
+    err = float(np.max(np.abs(out.cpu().numpy() - ref)))
+    print("max-abs", err)
+    assert err <= parity.DECODE_TOL
+
+
+@pytest.mark.parametrize("G,bits", [(4, 4), (8, 4), (4, 2), (8, 2)])
+def test_long_window_single_launch(gpu_lib, G, bits):
+    """A 300-slot ring at one split: several 16-token rounds per wave in the single launch
+    (8 waves at 4-bit, 12 at 2-bit), windows of 300, 129, 17 and 0 tokens."""
+    w, inp = parity.small_workload(4, 2 * G, 2, [40, 333, 7, 100], 352, bits=bits, seed=230 + G + bits)
+    t = parity.torch_inputs(inp, w.dtype)
+    oq = parity.oracle_quantizer(bits)
+    qz = fq.Quantizer(bits, 128, fq.ROT_HAAR, 1, 2, 128)
+    host = parity.oracle_cache(inp, oq)
+    cache = fq.PagedCache(inp["num_blocks"], 2, 128, bits, 128)
+    parity.upload_cache(host, cache)
+    W = 300
+    g = torch.Generator(device="cuda").manual_seed(19 + G)
+    wk = torch.randn((4, W, 2, 128), generator=g, device="cuda").to(torch.bfloat16)
+    wv = torch.randn((4, W, 2, 128), generator=g, device="cuda").to(torch.bfloat16)
+    wl = [300, 129, 17, 0]
+    out = fq.decode_window(qz, cache, t["q"], t["bt"], t["lens"], 352, wk, wv,
+                           torch.tensor(wl, dtype=torch.int32, device="cuda"), num_splits=1)
+    torch.cuda.synchronize()
+    ref = _oracle(inp, host, oq, wk, wv, wl)
     err = float(np.max(np.abs(out.cpu().numpy() - ref)))
     print("max-abs", err)
     assert err <= parity.DECODE_TOL

@@ -12,6 +12,8 @@ append and the decode over the compressed cache plus the window in one call.
 * The batch-32 8B-shaped layer with a 128-token window in the launch configuration
   the benchmark times (one split): bit-identical to the two calls, three sequences
   against the oracle.
+* A 300-slot ring at one split, the new token's slot in a wave's first 16-token round
+  (rows requested before the append) or in a later one (requested after it).
 """
 import numpy as np
 import pytest
@@ -150,5 +152,57 @@ def test_step_window_full_size_b32(gpu_lib):
     want = _oracle(t["q"][seqs], host, oq, bt[seqs], (lens - W).astype(np.int32)[seqs], wk[seqs], wv[seqs],
                    np.full(len(seqs), W, np.int32))
     err = float(np.max(np.abs(out.cpu().numpy()[seqs] - want)))
+    print("max-abs vs oracle", err)
+    assert err <= parity.DECODE_TOL
+
+
+def test_step_window_long_ring(gpu_lib):
+    """A 300-slot ring, one split: the new token's slot lies in a later 16-token round of
+    its wave (rows requested after the append), bit-identical to the two calls."""
+    B, Hkv, G, W = 2, 2, 4, 300
+    n0 = np.array([310, 290])  # full ring; filling ring
+    cap = int(n0.max()) + 1
+    rng = np.random.default_rng(77)
+    nblk = (cap + 15) // 16
+    bt = np.ascontiguousarray(np.arange(B * nblk, dtype=np.int32).reshape(B, nblk)[:, rng.permutation(nblk)])
+    slot = lambda b, p: int(bt[b, p // 16]) * 16 + p % 16
+    qz = fq.Quantizer(4, 128, fq.ROT_HAAR, 1, 2, 128)
+    oq = parity.oracle_quantizer(4)
+    cache = fq.PagedCache(B * nblk, Hkv, 128, 4, 128)
+    g = torch.Generator(device="cuda").manual_seed(5)
+    toks_k = torch.randn((B, cap, Hkv, 128), generator=g, device="cuda").to(torch.bfloat16)
+    toks_v = torch.randn((B, cap, Hkv, 128), generator=g, device="cuda").to(torch.bfloat16)
+    wk = torch.zeros((B, W, Hkv, 128), dtype=torch.bfloat16, device="cuda")
+    wv = torch.zeros_like(wk)
+    for b in range(B):
+        n = int(n0[b])
+        c_end = max(0, n - W)
+        if c_end:
+            sl = torch.tensor([slot(b, p) for p in range(c_end)], dtype=torch.int64, device="cuda")
+            fq.compress(qz, cache, toks_k[b, :c_end].contiguous(), toks_v[b, :c_end].contiguous(), sl)
+        for p in range(c_end, n):
+            wk[b, p % W] = toks_k[b, p]
+            wv[b, p % W] = toks_v[b, p]
+    mirror, mk, mv = _clone_cache(cache), wk.clone(), wv.clone()
+    pos = torch.from_numpy(n0.astype(np.int64)).cuda()
+    evt = torch.tensor([slot(b, int(n0[b]) - W) if n0[b] >= W else -1 for b in range(B)], dtype=torch.int64,
+                       device="cuda")
+    kn = torch.stack([toks_k[b, int(n0[b])] for b in range(B)]).contiguous()
+    vn = torch.stack([toks_v[b, int(n0[b])] for b in range(B)]).contiguous()
+    n1 = n0 + 1
+    sl_t = torch.from_numpy(np.maximum(n1 - W, 0).astype(np.int32)).cuda()
+    wl = np.minimum(n1, W).astype(np.int32)
+    wl_t = torch.from_numpy(wl).cuda()
+    bt_t = torch.from_numpy(bt).cuda()
+    q = torch.randn((B, Hkv * G, 128), generator=g, device="cuda").to(torch.bfloat16)
+    out = fq.decode_step_window(qz, cache, kn, vn, pos, evt, wk, wv, wl_t, q, bt_t, sl_t, cap, num_splits=1)
+    fq.window_append(qz, mirror, kn, vn, pos, evt, mk, mv)
+    ref = fq.decode_window(qz, mirror, q, bt_t, sl_t, cap, mk, mv, wl_t, num_splits=1)
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref), float((out - ref).abs().max())
+    assert torch.equal(wk, mk) and torch.equal(wv, mv)
+    _same_cache(cache, mirror)
+    want = _oracle(q, parity.cache_to_host(cache), oq, bt, np.maximum(n1 - W, 0).astype(np.int32), wk, wv, wl)
+    err = float(np.max(np.abs(out.cpu().numpy() - want)))
     print("max-abs vs oracle", err)
     assert err <= parity.DECODE_TOL
