@@ -412,11 +412,29 @@ __device__ __forceinline__ void merge_group(const DecodeArgs& a, int64_t head0, 
   const int S = a.splits;
   float pc[D / KP];
   col_part_load<KP>(a.pi, j, kp, pc);
+  // one head of up to 32 splits (the small-batch grids): its splits' (max, sum) and
+  // then their outputs are requested now, before the weights the outputs are summed
+  // with are known (one memory round trip instead of two; loads complete in issue
+  // order). 8B-shaped batch-1 layer, 16 splits: 18.1 -> 17.2 us per call; at 64
+  // splits the early outputs measured 0.5 % slower and are not requested early.
+  constexpr int SP = (32 + KP - 1) / KP;
+  const bool early = G == 1 && S <= 32;
+  float pre[SP];
+  float2 ml1 = make_float2(-INFINITY, 0.f);
+  if (early) {
+    if (wv == 0 && lane < S) ml1 = reinterpret_cast<const float2*>(a.part_ml)[head0 * S + lane];
+    const float* po = a.part_o + head0 * S * D + j;
+#pragma unroll
+    for (int i = 0; i < SP; ++i) pre[i] = kp + i * KP < S ? po[(kp + i * KP) * D] : 0.f;
+  }
   for (int h = wv; h < G; h += NT / 64) {
     float mw = -INFINITY, lw = 0.f, ow0 = 0.f, ow1 = 0.f;
     if (a.win_k) window_partial(a, head0 + h, lane, mw, lw, ow0, ow1);
     float m = -INFINITY, l = 0.f;
-    if (lane < S) {
+    if (early) {
+      m = ml1.x;
+      l = ml1.y;
+    } else if (lane < S) {
       const float2 x = reinterpret_cast<const float2*>(a.part_ml)[(head0 + h) * S + lane];
       m = x.x;
       l = x.y;
@@ -436,12 +454,20 @@ __device__ __forceinline__ void merge_group(const DecodeArgs& a, int64_t head0, 
     }
   }
   __syncthreads();
-  for (int h = 0; h < G; ++h) {
-    const float* po = a.part_o + (head0 + h) * S * D + j;
+  if (early) {
     float acc = 0.f;
+#pragma unroll
+    for (int i = 0; i < SP; ++i)
+      if (kp + i * KP < S) acc = fmaf(pre[i], s_w[kp + i * KP], acc);
+    s_part[kp * FQ_MAX_GROUP * D + j] = acc;
+  } else {
+    for (int h = 0; h < G; ++h) {
+      const float* po = a.part_o + (head0 + h) * S * D + j;
+      float acc = 0.f;
 #pragma unroll 16
-    for (int sp = kp; sp < S; sp += KP) acc = fmaf(po[sp * D], s_w[h * FQ_MAX_SPLITS + sp], acc);
-    s_part[(kp * FQ_MAX_GROUP + h) * D + j] = acc;
+      for (int sp = kp; sp < S; sp += KP) acc = fmaf(po[sp * D], s_w[h * FQ_MAX_SPLITS + sp], acc);
+      s_part[(kp * FQ_MAX_GROUP + h) * D + j] = acc;
+    }
   }
   __syncthreads();
   for (int h = kp; h < G; h += KP) {
