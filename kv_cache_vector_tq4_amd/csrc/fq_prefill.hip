@@ -341,24 +341,44 @@ __global__ void __launch_bounds__(PT_WAVES * 64, 2) prefill_tile_kernel(PrefillA
 #pragma unroll
   for (int t = 0; t < 8; ++t) acc_o[t] = f4{0.f, 0.f, 0.f, 0.f};
 
+  // A page's field bases are uniform (pinned in scalar registers) and every lane
+  // reads at a fixed 32-bit byte offset from them, so no address is formed per lane
+  // and page. Without QJL fields the sign and gamma loads read the codes and norms
+  // instead (the results are not used).
+  typedef const __attribute__((address_space(1))) uint8_t* gb8;
+  const uint32_t o_kc = static_cast<uint32_t>(n * 64 + 16 * g), o_sg = static_cast<uint32_t>(n * 16 + 4 * g);
+  const uint32_t o_n = static_cast<uint32_t>(16 * g), o_vc = static_cast<uint32_t>(4 * g * 64 + 4 * n);
+  const uint8_t* const sg_src = qjl ? a.k_qjl : a.k_codes;
+  const float* const gm_src = qjl ? a.k_gamma : a.k_norm;
   auto load = [&](int blk, TPage& d) {
     const int64_t rec0 = (static_cast<int64_t>(blk) * a.hkv + kvh) * FQ_BLOCK;
-    const uint4 k = *reinterpret_cast<const uint4*>(a.k_codes + (rec0 + n) * 64 + 16 * g);
+    gb8 kcb = (gb8)(a.k_codes + rec0 * 64);
+    gb8 sgb = (gb8)(sg_src + rec0 * 16);
+    gb8 knb = (gb8)(a.k_norm + rec0);
+    gb8 gmb = (gb8)(gm_src + rec0);
+    gb8 vnb = (gb8)(a.v_norm + rec0);
+    gb8 vcb = (gb8)(a.v_codes + rec0 * 64);
+    asm volatile("" : "+s"(kcb), "+s"(sgb), "+s"(knb), "+s"(gmb), "+s"(vnb), "+s"(vcb));
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    typedef float f32x4 __attribute__((ext_vector_type(4)));
+    typedef const __attribute__((address_space(1))) u32x4* gu4;
+    typedef const __attribute__((address_space(1))) f32x4* gf4;
+    typedef const __attribute__((address_space(1))) uint32_t* gu32;
+    const u32x4 k = *reinterpret_cast<gu4>(kcb + o_kc);
     d.kc[0] = k.x; d.kc[1] = k.y; d.kc[2] = k.z; d.kc[3] = k.w;
-    d.kn = *reinterpret_cast<const float4*>(a.k_norm + rec0 + 4 * g);
-    d.vn = *reinterpret_cast<const float4*>(a.v_norm + rec0 + 4 * g);
-    if (qjl) {
-      d.sg = *reinterpret_cast<const uint32_t*>(a.k_qjl + (rec0 + n) * 16 + 4 * g);
-      d.gm = *reinterpret_cast<const float4*>(a.k_gamma + rec0 + 4 * g);
-    } else {
-      d.sg = 0u;
-      d.gm = make_float4(0.f, 0.f, 0.f, 0.f);
-    }
+    const f32x4 kn = *reinterpret_cast<gf4>(knb + o_n), vn = *reinterpret_cast<gf4>(vnb + o_n);
+    const f32x4 gm = *reinterpret_cast<gf4>(gmb + o_n);
+    d.kn = make_float4(kn.x, kn.y, kn.z, kn.w);
+    d.vn = make_float4(vn.x, vn.y, vn.z, vn.w);
+    d.gm = make_float4(gm.x, gm.y, gm.z, gm.w);
+    d.sg = *reinterpret_cast<gu32>(sgb + o_sg);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) d.vc[e] = *reinterpret_cast<const uint32_t*>(a.v_codes + (rec0 + 4 * g + e) * 64 + 4 * n);
+    for (int e = 0; e < 4; ++e) d.vc[e] = *reinterpret_cast<gu32>(vcb + o_vc + 64 * e);
   };
 
-  auto process = [&](const TPage& d, int p, bool act) {
+  // lim: this lane's row's token count in the sequence being walked (0 when the row
+  // belongs to another one), so token validity is one compare
+  auto process = [&](const TPage& d, int p, int lim) {
     // ---- scores C[token 4 g + i][row n]
     f4 accM = {0.f, 0.f, 0.f, 0.f}, accQ = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -389,7 +409,7 @@ __global__ void __launch_bounds__(PT_WAVES * 64, 2) prefill_tile_kernel(PrefillA
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int tok = p * FQ_BLOCK + 4 * g + i;
-      const bool valid = act && tok < my_len;
+      const bool valid = tok < lim;
       sc[i] = valid ? fmaf(accQ[i], gmv[i], accM[i] * knv[i]) * cf : -INFINITY;
       mx = fmaxf(mx, sc[i]);
       vm = fmaxf(vm, valid ? vnv[i] : 0.f);
@@ -463,7 +483,8 @@ __global__ void __launch_bounds__(PT_WAVES * 64, 2) prefill_tile_kernel(PrefillA
     const int s_cur = wave_min_i(done ? INT_MAX : my_seq);
     if (s_cur == INT_MAX) break;
     const bool act = !done && my_seq == s_cur;
-    const int lmax = wave_max_i(act ? my_len : 0);
+    const int lim = act ? my_len : 0;
+    const int lmax = wave_max_i(lim);
     const int npg = (lmax + FQ_BLOCK - 1) / FQ_BLOCK;
     const int32_t* btrow = a.block_tables + static_cast<int64_t>(s_cur) * a.max_blocks;
     for (int c0 = 0; c0 < npg; c0 += 64) {
@@ -474,10 +495,10 @@ __global__ void __launch_bounds__(PT_WAVES * 64, 2) prefill_tile_kernel(PrefillA
       load(blk(0), pa);
       for (int i = 0; i < cn; i += 2) {
         load(blk(i + 1), pb);
-        process(pa, c0 + i, act);
+        process(pa, c0 + i, lim);
         if (i + 1 >= cn) break;
         load(blk(i + 2), pa);
-        process(pb, c0 + i + 1, act);
+        process(pb, c0 + i + 1, lim);
       }
     }
     done = done || act;
