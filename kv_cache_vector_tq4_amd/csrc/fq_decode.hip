@@ -1479,9 +1479,10 @@ __device__ __forceinline__ void pk_load(const DecodeArgs& a, int64_t rec0, int n
     d.kc[1] = k.y;
   }
   d.sg = __builtin_nontemporal_load(reinterpret_cast<const __attribute__((address_space(1))) uint32_t*>(sgb + osg));
-  d.kn = knb[n];
-  d.gm = gmb[n];
-  d.vn = vnb[n];
+  // the norm runs too (same-process step runs: +0.6 to +2.9 % tokens/s)
+  d.kn = __builtin_nontemporal_load(knb + n);
+  d.gm = __builtin_nontemporal_load(gmb + n);
+  d.vn = __builtin_nontemporal_load(vnb + n);
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     if constexpr (k3_values3(K3)) {
