@@ -254,7 +254,7 @@ fq_status fq_decompress(void* stream, const fq_quantizer* quant, const fq_cache*
 /*
  * Split count the decode chooses when called with num_splits = 0: enough
  * (batch, KV head, split) work-groups to fill the GPU, each covering at least
- * 256 tokens, at most 64 splits. Host only.
+ * 128 tokens, at most 32 splits. Host only.
  */
 int fq_decode_auto_splits(int batch, int num_kv_heads, int max_seq_len);
 

@@ -178,8 +178,10 @@ def test_step_window_argument_checks():
 
 
 def test_auto_splits():
-    assert fq.auto_splits(1, 8, 4096) == 16
-    assert fq.auto_splits(1, 8, 32768) == 64
+    assert fq.auto_splits(1, 8, 4096) == 32
+    assert fq.auto_splits(1, 8, 32768) == 32
+    assert fq.auto_splits(4, 8, 32768) == 16
+    assert fq.auto_splits(1, 8, 1000) == 7
     assert fq.auto_splits(32, 8, 4096) == 1
     assert fq.auto_splits(16, 8, 4096) == 4
     assert fq.auto_splits(64, 8, 4096) == 1
