@@ -215,8 +215,11 @@ struct TPage {
 // A operand of the value product C[row][dim] += P[row][token] V^[token][dim] (no data
 // moves between the two). K positions 8 g + e of a k-step follow the table entries
 // as loaded (no register moves): (hi, hi, lo, lo) of dims (or tokens) 0, 1, then of
-// 2, 3; the query (probability) operands are the matching (hi, hi, hi, hi) and (lo,
-// lo, lo, lo) arrangements (four products, the lo * lo one negligible but free).
+// 2, 3. Scores: the query's hi part against those (hi k + lo k), and its lo part in
+// one product per two k-steps against the hi halves of their four entries (8 dims),
+// 12 products per page instead of 16 (the lo x lo term, below the fp16 rounding of
+// the sum, is left out). Values: the probability's (hi, hi, hi, hi) and (lo, lo, lo,
+// lo) arrangements against the value entries (four products, lo x lo included).
 template <int G>
 __global__ void __launch_bounds__(PT_WAVES * 64, 2) prefill_tile_kernel(PrefillArgs a) {
   constexpr int Q = 16 / G;  // query tokens per wave
@@ -301,21 +304,26 @@ __global__ void __launch_bounds__(PT_WAVES * 64, 2) prefill_tile_kernel(PrefillA
     qscale = ldexpf(1.f, e_use);
   }
   const float cf = a.scale * LOG2E_F / (qscale * static_cast<float>(1 << LEV_SHIFT));
-  h8 bqh[8], bql[8], bsh[4], bsl[4];
+  // bqh[s]: q~ hi of dims 32 g + 4 s .. + 3 against the (hi, hi, lo, lo) table
+  // entries; bql[t]: q~ lo of dims 32 g + 8 t .. + 7 against the hi parts of two
+  // k-steps' entries (the lo x lo product is left out: below fp16 rounding of the sum)
+  h8 bqh[8], bql[4], bsh[4], bsl[4];
+  uint32_t qlw[16];
 #pragma unroll
   for (int s = 0; s < 8; ++s) {  // dims 32 g + 4 s .. + 3
-    uint32_t hw[2], lw[2];
+    uint32_t hw[2];
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
       _Float16 h0, l0, h1, l1;
       split_f16(qv[4 * s + 2 * k] * qscale, h0, l0);
       split_f16(qv[4 * s + 2 * k + 1] * qscale, h1, l1);
       hw[k] = h2bits(h0, h1);
-      lw[k] = h2bits(l0, l1);
+      qlw[2 * s + k] = h2bits(l0, l1);
     }
     bqh[s] = as_h8(hw[0], hw[0], hw[1], hw[1]);
-    bql[s] = as_h8(lw[0], lw[0], lw[1], lw[1]);
   }
+#pragma unroll
+  for (int t = 0; t < 4; ++t) bql[t] = as_h8(qlw[4 * t], qlw[4 * t + 1], qlw[4 * t + 2], qlw[4 * t + 3]);
 #pragma unroll
   for (int s = 0; s < 4; ++s) {  // dims 32 g + 8 s .. + 7
     uint32_t hw[4], lw[4];
@@ -382,13 +390,15 @@ __global__ void __launch_bounds__(PT_WAVES * 64, 2) prefill_tile_kernel(PrefillA
     // ---- scores C[token 4 g + i][row n]
     f4 accM = {0.f, 0.f, 0.f, 0.f}, accQ = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      const uint32_t w = d.kc[s >> 1];
-      const uint2 e0 = lds_u2(s_code, tab_off(w, copy8, 2 * (s & 1)));
-      const uint2 e1 = lds_u2(s_code, tab_off(w, copy8, 2 * (s & 1) + 1));
-      const h8 ak = as_h8(e0.x, e0.y, e1.x, e1.y);
-      accM = mfma32(ak, bqh[s], accM);
-      accM = mfma32(ak, bql[s], accM);
+    for (int t = 0; t < 4; ++t) {  // k-steps 2t, 2t + 1: code bytes 0, 1 and 2, 3 of word t
+      const uint32_t w = d.kc[t];
+      const uint2 e0 = lds_u2(s_code, tab_off(w, copy8, 0));
+      const uint2 e1 = lds_u2(s_code, tab_off(w, copy8, 1));
+      const uint2 e2 = lds_u2(s_code, tab_off(w, copy8, 2));
+      const uint2 e3 = lds_u2(s_code, tab_off(w, copy8, 3));
+      accM = mfma32(as_h8(e0.x, e0.y, e1.x, e1.y), bqh[2 * t], accM);
+      accM = mfma32(as_h8(e2.x, e2.y, e3.x, e3.y), bqh[2 * t + 1], accM);
+      accM = mfma32(as_h8(e0.x, e1.x, e2.x, e3.x), bql[t], accM);
     }
     if (qjl) {
       const uint32_t sgl = d.sg & 0x0F0F0F0Fu, sgh = (d.sg >> 4) & 0x0F0F0F0Fu;
